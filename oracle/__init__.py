@@ -1,0 +1,197 @@
+"""Plain CPU oracle of the LLM.int8() mixed-precision decomposition matmul.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg are the only callers.  The HIP library never imports, links or
+runs anything here, and this package never imports the HIP library.
+
+The arithmetic lives in ``llmint8_oracle.c`` (plain C, one output element at
+a time); this module only marshals numpy arrays through ctypes.  fp16 data is
+passed as raw binary16 bit patterns (``uint16``); ``np.float16`` arrays are
+accepted and reinterpreted.
+
+Parity status: every function here is pinned by the CPU tests in
+``tests/test_oracle_*.py`` (worked examples printed on the pages, closed
+forms, special cases and brute force).  The one part without a pin to an
+independent value is the fp64 summation order of the fp16 outlier product,
+which sits far below the fp16 output tolerance.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "llmint8_oracle.c")
+_SO = os.path.join(_HERE, "libllmint8_oracle.so")
+
+_lib = None
+
+
+def build():
+    """Compile the oracle shared library with gcc (IEEE arithmetic, OpenMP)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fno-fast-math",
+           "-ffp-contract=off", "-shared", "-fPIC", _SRC, "-o", _SO + ".tmp",
+           "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(_SO + ".tmp", _SO)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_SO):
+        build()
+    lib = ctypes.CDLL(_SO)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_half_to_double_n.argtypes = [P, I64, P]
+    lib.oracle_double_to_half_n.argtypes = [P, I64, P]
+    lib.oracle_round_127x_over_a_n.argtypes = [P, P, I64, P]
+    lib.oracle_dequant_weight_n.argtypes = [P, P, I64, P]
+    lib.oracle_quantize_weight.argtypes = [P, I64, I64, P, P]
+    lib.oracle_outlier_columns.argtypes = [P, I64, I64, ctypes.c_float, P]
+    lib.oracle_outlier_columns.restype = I64
+    lib.oracle_quantize_rows.argtypes = [P, I64, I64, P, I64, P, I64, P, P]
+    lib.oracle_int_gemm.argtypes = [P, P, I64, I64, I64, P]
+    lib.oracle_int_gemm.restype = I64
+    lib.oracle_matmul.argtypes = [P, I64, I64, I64, P, P, P, ctypes.c_float,
+                                  P, I64, P, I64, P, P, P, P]
+    lib.oracle_matmul.restype = I64
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _bits(a):
+    """Binary16 bit patterns of an fp16 (or already uint16) array."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError("expected float16 or uint16 bit patterns, got %s" % a.dtype)
+    return a
+
+
+def num_threads():
+    return int(_load().oracle_num_threads())
+
+
+def half_to_double(h):
+    h = _bits(h)
+    out = np.empty(h.shape, np.float64)
+    _load().oracle_half_to_double_n(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+def double_to_half(v):
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, np.uint16)
+    _load().oracle_double_to_half_n(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def round_127x_over_a(x, a):
+    """Nearest integer (ties to even) to 127*x/a for binary16 x, a."""
+    x, a = np.broadcast_arrays(_bits(x), _bits(a))
+    x = np.ascontiguousarray(x)
+    a = np.ascontiguousarray(a)
+    out = np.empty(x.shape, np.int32)
+    _load().oracle_round_127x_over_a_n(_ptr(x), _ptr(a), x.size, _ptr(out))
+    return out
+
+
+def dequant_weight(cb, scb):
+    """Binary16 value nearest to cb*scb/127, element-wise."""
+    cb, scb = np.broadcast_arrays(np.asarray(cb, np.int8), np.asarray(scb, np.float32))
+    cb = np.ascontiguousarray(cb)
+    scb = np.ascontiguousarray(scb)
+    out = np.empty(cb.shape, np.uint16)
+    _load().oracle_dequant_weight_n(_ptr(cb), _ptr(scb), cb.size, _ptr(out))
+    return out
+
+
+def quantize_weight(W_t):
+    """W_t: [N,K] fp16 (row n = output column n).  Returns (CB [N,K] int8, SCB [N] f32)."""
+    W_t = _bits(W_t)
+    N, K = W_t.shape
+    CB = np.empty((N, K), np.int8)
+    SCB = np.empty((N,), np.float32)
+    _load().oracle_quantize_weight(_ptr(W_t), K, N, _ptr(CB), _ptr(SCB))
+    return CB, SCB
+
+
+def outlier_columns(X, threshold):
+    """Ascending int32 array of the columns whose max |x| exceeds threshold."""
+    X = _bits(X)
+    T, K = X.shape
+    O = np.empty((max(K, 1),), np.int32)
+    n = _load().oracle_outlier_columns(_ptr(X), T, K, float(threshold), _ptr(O))
+    return O[:n].copy()
+
+
+def quantize_rows(X, O, rows=None):
+    """Returns (Xq [nrows,K] int8, a [nrows] f32) for the listed rows (all by default)."""
+    X = _bits(X)
+    T, K = X.shape
+    O = np.ascontiguousarray(O, np.int32)
+    if rows is None:
+        nrows = T
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, np.int64)
+        nrows = rows_arr.size
+    Xq = np.empty((nrows, K), np.int8)
+    a = np.empty((nrows,), np.float32)
+    _load().oracle_quantize_rows(_ptr(X), T, K, _ptr(O), O.size, _ptr(rows_arr),
+                                 nrows, _ptr(Xq), _ptr(a))
+    return Xq, a
+
+
+def int_gemm(Xq, CB):
+    """C[i,n] = sum_k Xq[i,k]*CB[n,k] (int64 sums, returned as int32)."""
+    Xq = np.ascontiguousarray(Xq, np.int8)
+    CB = np.ascontiguousarray(CB, np.int8)
+    M, K = Xq.shape
+    N, K2 = CB.shape
+    assert K == K2
+    C = np.empty((M, N), np.int32)
+    bad = _load().oracle_int_gemm(_ptr(Xq), _ptr(CB), M, K, N, _ptr(C))
+    if bad:
+        raise OverflowError("%d int32 overflows in the integer product" % bad)
+    return C
+
+
+def matmul(X, CB, SCB, threshold=6.0, bias=None, rows=None, cols=None):
+    """The decomposition for the listed output rows/columns.
+
+    Returns (out [nrows,ncols] uint16 binary16 bits, O int32, a [nrows] f32).
+    O is always found from all rows of X.
+    """
+    X = _bits(X)
+    T, K = X.shape
+    CB = np.ascontiguousarray(CB, np.int8)
+    SCB = np.ascontiguousarray(SCB, np.float32)
+    N = CB.shape[0]
+    assert CB.shape == (N, K) and SCB.shape == (N,)
+    b = _bits(bias) if bias is not None else None
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    cols_arr = None if cols is None else np.ascontiguousarray(cols, np.int64)
+    nrows = T if rows_arr is None else rows_arr.size
+    ncols = N if cols_arr is None else cols_arr.size
+    out = np.empty((nrows, ncols), np.uint16)
+    O = np.empty((max(K, 1),), np.int32)
+    n = np.zeros((1,), np.int64)
+    a = np.empty((max(nrows, 1),), np.float32)
+    bad = _load().oracle_matmul(_ptr(X), T, K, N, _ptr(CB), _ptr(SCB), _ptr(b),
+                                float(threshold), _ptr(rows_arr), nrows,
+                                _ptr(cols_arr), ncols, _ptr(out), _ptr(O),
+                                _ptr(n), _ptr(a))
+    if bad:
+        raise OverflowError("%d int32 overflows in the integer product" % bad)
+    return out, O[: int(n[0])].copy(), a[:nrows].copy()

@@ -1,0 +1,394 @@
+/*
+ * llmint8_oracle.c -- plain CPU oracle of the LLM.int8() mixed-precision
+ * decomposition matmul.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no source, header, table or helper with the
+ * HIP library.
+ *
+ * Every function is the definition written out, one output element at a
+ * time, with no blocking, fusion or reordering.  Sources (the web pages this
+ * follows):
+ *   [HF]   agentlenshq.com, "Hugging Face, LLM.int8() 8-bit matrix
+ *          multiplication integrated into Transformers and Accelerate":
+ *          the three-step method, the absmax example, the Int8Params note
+ *          that the fp16 weight is recovered as CB*SCB/127.
+ *   [SUM]  kurtkim.github.io, "LLM.int8()" paper summary: the absmax
+ *          equation (section "8-bit Data Types and Quantization"), the int32
+ *          accumulation (section "Int8 Matrix Multiplication with 16-bit Float
+ *          Inputs and Outputs"), vector-wise quantization (section
+ *          "Vector-wise Quantization"), and the decomposition over the outlier
+ *          set O with alpha = 6.0 (section "The Core of LLM.int8():
+ *          Mixed-precision Decomposition").
+ *   [QB]   techblog.paldyn.com, quantization basics: the binary16 layout
+ *          (1 sign, 5 exponent, 10 fraction bits; largest finite 65504).
+ *
+ * Readings where the pages leave a step open (each one is listed, with its
+ * reason, in the design notes):
+ *   - rounding is to nearest with ties to even, of the exact rational value;
+ *   - a column is an outlier when its largest |x| is strictly greater than
+ *     the threshold;
+ *   - the row absmax runs over the non-outlier columns only, and the int8
+ *     matrix keeps outlier columns as zeros;
+ *   - the weight absmax runs over all of K;
+ *   - the outlier product uses the weight dequantized to fp16 from CB and
+ *     SCB, because only CB and SCB exist once the weight is quantized;
+ *   - the output is one rounding to fp16 of the exact-as-possible (fp64)
+ *     sum of the dequantized int8 part, the outlier part and the bias.
+ *
+ * fp16 values cross this interface as raw IEEE binary16 bit patterns
+ * (uint16_t); the codec below is written from the bit layout.
+ * Build: gcc -O2 -fopenmp -fno-fast-math -ffp-contract=off -shared -fPIC.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* binary16 codec ([QB] floating-point formats: 1 sign bit, 5 exponent bits  */
+/* with bias 15, 10 fraction bits).                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Exact value of a binary16 bit pattern. */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);              /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);  /* (1 + f/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest binary16 value, ties to even, in one step.
+ * Magnitudes from 65520 (halfway between 65504 and 2^16) upward become inf. */
+uint16_t oracle_double_to_half(double v)
+{
+    if (isnan(v))
+        return 0x7e00;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return sign | 0x7c00;
+    int e2;
+    frexp(a, &e2);          /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;         /* binade exponent of a */
+    if (E < -14)
+        E = -14;            /* subnormals share the spacing of the lowest binade */
+    if (E > 15)
+        return sign | 0x7c00;
+    double ulp = ldexp(1.0, E - 10);    /* spacing of binary16 values in [2^E, 2^(E+1)) */
+    double q = a / ulp;                 /* exact: scaling by a power of two */
+    double r = floor(q);
+    double frac = q - r;                /* exact */
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0))
+        r += 1.0;
+    if (r >= 2048.0) {                  /* rounded up into the next binade */
+        r = 1024.0;
+        E += 1;
+    }
+    if (E > 15)
+        return sign | 0x7c00;
+    if (r < 1024.0)                     /* only possible for E == -14: subnormal */
+        return sign | (uint16_t)r;
+    return sign | (uint16_t)(((E + 15) << 10) | ((int)r - 1024));
+}
+
+/* |x| of a binary16 bit pattern, as a bit pattern (clear the sign bit).  For
+ * finite values the unsigned order of these patterns is the order of the
+ * magnitudes, so the max of patterns is the pattern of the max. */
+static uint16_t half_abs_bits(uint16_t h) { return (uint16_t)(h & 0x7fff); }
+
+/* Split a finite non-negative binary16 value into integer mantissa m and
+ * exponent p with value = m * 2^p. */
+static void half_split(uint16_t h, int64_t *m, int *p)
+{
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    if (e == 0) {
+        *m = f;
+        *p = -24;
+    } else {
+        *m = 1024 + f;
+        *p = e - 25;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Absmax quantization ([SUM] "8-bit Data Types and Quantization": the int8   */
+/* value is 127*x / max|X| rounded to the nearest integer).                  */
+/* ------------------------------------------------------------------------ */
+
+/* Nearest integer to the exact rational 127*x/a, ties to even, for binary16
+ * values x and a with 0 < a and |x| <= a.  Written with integers so that no
+ * floating-point rounding enters: 127*x/a = 127*mx*2^px / (ma*2^pa). */
+int oracle_round_127x_over_a(uint16_t xh, uint16_t ah)
+{
+    uint16_t xa = half_abs_bits(xh);
+    int64_t mx, ma;
+    int px, pa;
+    half_split(xa, &mx, &px);
+    half_split(half_abs_bits(ah), &ma, &pa);
+    if (ma == 0 || mx == 0)
+        return 0;
+    int d = px - pa;
+    int64_t num, den;
+    if (d >= 0) {            /* |x| <= a bounds num by 127*ma, so no overflow */
+        num = (127 * mx) << d;
+        den = ma;
+    } else {                 /* -d <= 29 and ma < 2^11: den < 2^40 */
+        num = 127 * mx;
+        den = ma << (-d);
+    }
+    int64_t q = num / den;
+    int64_t rem = num - q * den;
+    if (2 * rem > den || (2 * rem == den && (q & 1)))
+        q += 1;
+    return (xh & 0x8000) ? (int)-q : (int)q;
+}
+
+/* Dequantized fp16 weight: the binary16 value nearest to CB*SCB/127 ([HF]
+ * Int8Params note).  The product is exact in fp64 and the quotient is
+ * correctly rounded in fp64; a rational with odd denominator 127 and
+ * numerator on a grid no finer than SCB's lies at least 2^-18 of its binade
+ * away from any binary16 midpoint, far more than the fp64 rounding error, so
+ * this single conversion equals rounding the exact rational once. */
+uint16_t oracle_dequant_weight(int8_t cb, float scb)
+{
+    return oracle_double_to_half(((double)cb * (double)scb) / 127.0);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step: weight quantization ([HF] Int8Params: CB int8 in [-127,127] plus     */
+/* SCB with W ~= CB*SCB/127; vector-wise means one scale per output column   */
+/* of W, i.e. per row of the stored [N,K] weight).                           */
+/* ------------------------------------------------------------------------ */
+
+/* W_t: [N,K] binary16, row n holds output column n of W.  CB: [N,K] int8,
+ * SCB: [N] float (the absmax, an fp16 value widened exactly). */
+void oracle_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N,
+                            int8_t *CB, float *SCB)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint16_t *row = W_t + n * K;
+        uint16_t amax = 0;
+        for (int64_t k = 0; k < K; ++k)
+            if (half_abs_bits(row[k]) > amax)
+                amax = half_abs_bits(row[k]);
+        SCB[n] = (float)oracle_half_to_double(amax);
+        for (int64_t k = 0; k < K; ++k)
+            CB[n * K + k] = (int8_t)oracle_round_127x_over_a(row[k], amax);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step: outlier feature columns ([HF] step 1; [SUM] mixed-precision          */
+/* decomposition: O holds the hidden dimensions h with a value above alpha). */
+/* ------------------------------------------------------------------------ */
+
+/* colmax[k] = max_t |X[t,k]|; O = { k : colmax[k] > threshold } in ascending
+ * order.  Returns n = |O|.  O needs room for K entries. */
+int64_t oracle_outlier_columns(const uint16_t *X, int64_t T, int64_t K,
+                               float threshold, int32_t *O)
+{
+    int64_t n = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        uint16_t cmax = 0;
+        for (int64_t t = 0; t < T; ++t)
+            if (half_abs_bits(X[t * K + k]) > cmax)
+                cmax = half_abs_bits(X[t * K + k]);
+        if (oracle_half_to_double(cmax) > (double)threshold)
+            O[n++] = (int32_t)k;
+    }
+    return n;
+}
+
+/* Membership table of O over 0..K-1 (1 = outlier column). */
+static unsigned char *outlier_mask(const int32_t *O, int64_t n, int64_t K)
+{
+    unsigned char *m = (unsigned char *)calloc((size_t)K, 1);
+    for (int64_t j = 0; j < n; ++j)
+        m[O[j]] = 1;
+    return m;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step: row-wise absmax quantization of the non-outlier part ([HF] step 2:  */
+/* activations row-wise; [SUM] the int8 sum runs over h not in O).           */
+/* ------------------------------------------------------------------------ */
+
+/* For each listed row t: a[t] = max_{k not in O} |X[t,k]| (0 if none);
+ * Xq[t,k] = 0 for k in O, else nearest integer to 127*X[t,k]/a[t] (0 when
+ * a[t] = 0).  rows == NULL means all T rows; Xq/a are indexed by position i
+ * in the row list (Xq: [nrows,K], a: [nrows]). */
+void oracle_quantize_rows(const uint16_t *X, int64_t T, int64_t K,
+                          const int32_t *O, int64_t n,
+                          const int64_t *rows, int64_t nrows,
+                          int8_t *Xq, float *a)
+{
+    unsigned char *isout = outlier_mask(O, n, K);
+    if (rows == NULL)
+        nrows = T;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t t = rows ? rows[i] : i;
+        const uint16_t *xr = X + t * K;
+        uint16_t amax = 0;
+        for (int64_t k = 0; k < K; ++k)
+            if (!isout[k] && half_abs_bits(xr[k]) > amax)
+                amax = half_abs_bits(xr[k]);
+        a[i] = (float)oracle_half_to_double(amax);
+        for (int64_t k = 0; k < K; ++k)
+            Xq[i * K + k] = isout[k] ? 0 : (int8_t)oracle_round_127x_over_a(xr[k], amax);
+    }
+    free(isout);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step: int8 matrix product with 32-bit integer result ([SUM] "Int8 Matrix  */
+/* Multiplication with 16-bit Float Inputs and Outputs": C_i32 = A_i8 B_i8). */
+/* ------------------------------------------------------------------------ */
+
+/* C[i,n] = sum_k Xq[i,k] * CB[n,k], summed in int64.  Xq: [M,K], CB: [N,K],
+ * C: [M,N].  Returns the number of sums that do not fit in int32 (those are
+ * stored clamped); 0 is the expected result for K <= 133144. */
+int64_t oracle_int_gemm(const int8_t *Xq, const int8_t *CB, int64_t M,
+                        int64_t K, int64_t N, int32_t *C)
+{
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (int64_t)Xq[i * K + k] * (int64_t)CB[n * K + k];
+            if (s > INT32_MAX) {
+                s = INT32_MAX;
+                ++bad;
+            } else if (s < INT32_MIN) {
+                s = INT32_MIN;
+                ++bad;
+            }
+            C[i * N + n] = (int32_t)s;
+        }
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The whole decomposition for a list of output rows ([SUM] mixed-precision  */
+/* decomposition: C ~= sum_{h in O} X^h W^h + S * sum_{h not in O} Xi8 Wi8,   */
+/* with S the outer product of the row and column scales over 127^2; [HF]    */
+/* step 3: dequantize the int8 result and add the fp16 outlier result).      */
+/* ------------------------------------------------------------------------ */
+
+/* out[i,c] = fp16( C[t,c]*a[t]*SCB[c]/127^2
+ *                  + sum_{k in O} X[t,k] * Wdq(CB[c,k], SCB[c])  [+ bias[c]] )
+ * for t = rows[i] (all rows when rows == NULL) and c = cols[j] (all N
+ * columns when cols == NULL).  O is found from all T rows of X.
+ * out: [nrows, ncols]; bias: [N] binary16 or NULL.  If O_out / n_out are
+ * given they receive O and n; a_out ([nrows]) receives the row scales.
+ * Returns the number of int32 overflows in C (0 expected). */
+int64_t oracle_matmul(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                      const int8_t *CB, const float *SCB, const uint16_t *bias,
+                      float threshold, const int64_t *rows, int64_t nrows,
+                      const int64_t *cols, int64_t ncols, uint16_t *out,
+                      int32_t *O_out, int64_t *n_out, float *a_out)
+{
+    if (rows == NULL)
+        nrows = T;
+    if (cols == NULL)
+        ncols = N;
+    int32_t *O = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
+    int64_t n = oracle_outlier_columns(X, T, K, threshold, O);
+    int8_t *Xq = (int8_t *)malloc((size_t)(nrows * K > 0 ? nrows * K : 1));
+    float *a = (float *)malloc(sizeof(float) * (size_t)(nrows > 0 ? nrows : 1));
+    oracle_quantize_rows(X, T, K, O, n, rows, nrows, Xq, a);
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t t = rows ? rows[i] : i;
+        for (int64_t j = 0; j < ncols; ++j) {
+            int64_t c = cols ? cols[j] : j;
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (int64_t)Xq[i * K + k] * (int64_t)CB[c * K + k];
+            if (s > INT32_MAX || s < INT32_MIN)
+                ++bad;
+            /* dequantized int8 part: C * a[t] * SCB[c] / 127^2 */
+            double acc = (double)s * (double)a[i] * (double)SCB[c] / 16129.0;
+            /* fp16 outlier part, over O in ascending order */
+            for (int64_t jj = 0; jj < n; ++jj) {
+                int64_t k = O[jj];
+                acc += oracle_half_to_double(X[t * K + k]) *
+                       oracle_half_to_double(oracle_dequant_weight(CB[c * K + k], SCB[c]));
+            }
+            if (bias)
+                acc += oracle_half_to_double(bias[c]);
+            out[i * ncols + j] = oracle_double_to_half(acc);
+        }
+    }
+    if (O_out)
+        memcpy(O_out, O, sizeof(int32_t) * (size_t)n);
+    if (n_out)
+        *n_out = n;
+    if (a_out)
+        memcpy(a_out, a, sizeof(float) * (size_t)nrows);
+    free(O);
+    free(Xq);
+    free(a);
+    return bad;
+}
+
+/* Number of threads the parallel loops use (for reporting the CPU baseline). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* Element-wise array forms of the scalar helpers above (for the tests).     */
+/* ------------------------------------------------------------------------ */
+
+void oracle_half_to_double_n(const uint16_t *h, int64_t len, double *out)
+{
+    for (int64_t i = 0; i < len; ++i)
+        out[i] = oracle_half_to_double(h[i]);
+}
+
+void oracle_double_to_half_n(const double *v, int64_t len, uint16_t *out)
+{
+    for (int64_t i = 0; i < len; ++i)
+        out[i] = oracle_double_to_half(v[i]);
+}
+
+void oracle_round_127x_over_a_n(const uint16_t *x, const uint16_t *a,
+                                int64_t len, int32_t *out)
+{
+    for (int64_t i = 0; i < len; ++i)
+        out[i] = oracle_round_127x_over_a(x[i], a[i]);
+}
+
+void oracle_dequant_weight_n(const int8_t *cb, const float *scb, int64_t len,
+                             uint16_t *out)
+{
+    for (int64_t i = 0; i < len; ++i)
+        out[i] = oracle_dequant_weight(cb[i], scb[i]);
+}
