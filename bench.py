@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the LLM.int8() decomposition matmul on one MI355X.
+
+A step is one llmint8_matmul call (outlier detection, row quantization, the
+int8 MFMA GEMM with the fused dequantize + fp16 outlier epilogue) on the
+6.7B-style FFN fc1 shape: X [4096,4096] fp16 with 6 outlier feature dims
+holding +-U(20,60) in 75 % of rows, W [4096,16384] as int8 CB + SCB (quantized
+once before timing, as the method does when the weight is loaded),
+threshold 6.0.  Inputs are seeded and synthetic and resident in HBM before the
+timed region.
+
+The JSON line also carries:
+  roofline      the GEMM kernel's own duration (HIP events recorded around its
+                launch on the stream it runs on) against the dense int8 MFMA peak;
+  cpu_baseline  the plain CPU oracle timed on a bounded sample of the same work;
+  decode        the weight-streaming kernel at T in {1,4,16}, K=12288, N=49152
+                (604 MB of CB, two copies rotated), against HBM bandwidth.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch has already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self):
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError("hipEventCreate failed: %d" % rc)
+        self.made.append(e.value)
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(ms.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.made = []
+
+
+def timed_steps(torch, L, X, CBs, SCB, thr, out, ws, steps, warmup, ev):
+    """warmup untimed steps, then `steps` timed ones; returns (ms/step, mean main-kernel ms)."""
+    for i in range(warmup):
+        L.llmint8_matmul(X, CBs[i % len(CBs)], SCB, thr, out=out, ws=ws)
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        L.llmint8_matmul_path(X, CBs[i % len(CBs)], SCB, thr, out=out, ws=ws, path=L.PATH_AUTO,
+                              main_start=pairs[i][0], main_stop=pairs[i][1])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = [ev.elapsed_ms(a, b) for a, b in pairs]
+    return (t1 - t0) * 1e3 / steps, float(np.mean(kern)), kern
+
+
+def cpu_baseline(X, W_t, thr, rows):
+    import oracle
+    CBh, SCBh = oracle.quantize_weight(W_t)
+    sel = np.arange(rows)
+    t0 = time.perf_counter()
+    oracle.matmul(X, CBh, SCBh, thr, rows=sel)
+    dt = time.perf_counter() - t0
+    T, K = X.shape
+    N = W_t.shape[0]
+    return {"value": 2.0 * rows * K * N / dt / 1e12, "unit": "TOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "rows 0..%d of X (%d of %d) against all %d output columns; the outlier set is "
+                      "found from all rows; %.1f s wall" % (rows - 1, rows, T, N, dt)}
+
+
+def decode_bench(torch, L, workloads, steps, warmup, ev, dev):
+    log("decode: generating W [12288,49152] ...")
+    d1 = workloads.decode_175b(1, with_weight=True)
+    W = torch.from_numpy(d1.pop("W_t")).to(dev)
+    CB, SCB = L.llmint8_quantize_weight(W)
+    del W
+    CB2 = CB.clone()                 # rotate two copies: 2 x 604 MB, beyond the 256 MB MALL
+    torch.cuda.synchronize()
+    K, N = CB.shape[1], CB.shape[0]
+    res = {}
+    for T in (1, 4, 16):
+        d = d1 if T == 1 else workloads.decode_175b(T, with_weight=False)
+        X = torch.from_numpy(d["X"]).to(dev)
+        out = torch.empty((T, N), dtype=torch.float16, device=dev)
+        ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=dev)
+        ms, kms, _ = timed_steps(torch, L, X, [CB, CB2], SCB, 6.0, out, ws, steps, warmup, ev)
+        alg = K * N + 4 * N + T * K + 4 * T + 2 * T * N
+        res["T%d" % T] = {"kernel_us": round(kms * 1e3, 2), "step_us": round(ms * 1e3, 2),
+                          "kernel_GBs": round(alg / (kms * 1e-3) / 1e9, 1),
+                          "step_GBs": round(alg / (ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(alg / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "alg_bytes": alg}
+        log("decode T=%d: kernel %.1f us (%.0f GB/s), step %.1f us" % (T, kms * 1e3, alg / kms / 1e6, ms * 1e3))
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the CPU-oracle sample (4096 = the whole workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from int8_quantized_matmul_02_amd import llmint8 as L
+    from int8_quantized_matmul_02_amd import workloads
+
+    dev = torch.device("cuda", 0)
+    ev = HipEvents()
+    log("fc1 workload: generating inputs ...")
+    d = workloads.ffn_6p7b(with_fc2=False)
+    X_h, W_h, thr = d["X"], d["W_t"], d["threshold"]
+    X = torch.from_numpy(X_h).to(dev)
+    W = torch.from_numpy(W_h).to(dev)
+    CB, SCB = L.llmint8_quantize_weight(W)
+    del W
+    T, K = X.shape
+    N = CB.shape[0]
+    out = torch.empty((T, N), dtype=torch.float16, device=dev)
+    ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=dev)
+    _, _, _, n_out = L.llmint8_quantize_act(X, thr)
+    n_outliers = int(n_out.cpu()[0])
+
+    ms, gemm_ms, _ = timed_steps(torch, L, X, [CB], SCB, thr, out, ws, args.steps, args.warmup, ev)
+    ops = 2.0 * T * K * N
+    value = ops / (ms * 1e-3) / 1e12
+    achieved = ops / (gemm_ms * 1e-3) / 1e12
+    log("fc1: %.1f us/step (%.0f TOP/s), GEMM kernel %.1f us (%.0f TOP/s, %.1f%% of int8 peak)"
+        % (ms * 1e3, value, gemm_ms * 1e3, achieved, 100 * achieved / INT8_PEAK_TOPS))
+
+    result = {
+        "metric": "int8-decomp matmul TOPS (% int8 MFMA peak) prefill; GB/s (% HBM) decode",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded fp16 activations with planted outlier dims; random N(0,0.02) weights)",
+        "config": {"workload": "6.7B-style FFN fc1: X[4096,4096] fp16, 6 outlier dims +-U(20,60) in 75% "
+                               "of rows, W[4096,16384] int8 CB+SCB, threshold 6.0",
+                   "T": T, "K": K, "N": N, "threshold": thr, "n_outliers": n_outliers},
+        "roofline": {"bound": "mfma", "kernel": "k_gemm (int8 MFMA GEMM + fused epilogue)",
+                     "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "kernel_us": round(gemm_ms * 1e3, 2), "ops_per_launch": ops},
+    }
+    if not args.no_decode:
+        result["decode"] = decode_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on %d rows ..." % args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(X_h, W_h, thr, args.cpu_rows)
+    ev.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

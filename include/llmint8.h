@@ -1,0 +1,176 @@
+/*
+ * llmint8.h -- C ABI of the MI355X (gfx950) LLM.int8() mixed-precision
+ * decomposition matmul.
+ *
+ * The operation (kurtkim.github.io, "LLM.int8()" paper summary, section
+ * "The Core of LLM.int8(): Mixed-precision Decomposition", equation for
+ * C_f16; agentlenshq.com, "Hugging Face, LLM.int8() 8-bit matrix
+ * multiplication integrated into Transformers and Accelerate", section "Core
+ * idea", steps 1-3):
+ *
+ *   out[t,n] = fp16( sum_{k in O} X[t,k] * Wdq[n,k]
+ *                    + C[t,n] * a[t] * SCB[n] / 127^2  [+ bias[n]] )
+ *   O        = { k : max_t |X[t,k]| > threshold }            (outlier columns)
+ *   a[t]     = max_{k not in O} |X[t,k]|                      (row absmax)
+ *   Xq[t,k]  = k in O ? 0 : round(127 * X[t,k] / a[t])        (int8)
+ *   C[t,n]   = sum_k Xq[t,k] * CB[n,k]                        (exact int32)
+ *   Wdq[n,k] = fp16(CB[n,k] * SCB[n] / 127)
+ *
+ * "round" is to nearest with ties to even, of the exact quotient; the int8
+ * values lie in [-127, 127].
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    row-major and contiguous, owned by the caller, 16-byte aligned.  Outputs
+ *    must not alias inputs.  fp16 data is passed as raw IEEE binary16 bit
+ *    patterns (uint16_t).
+ *  - Shapes: T >= 1 (any value; a ragged last tile is handled), K and N
+ *    multiples of 64, K <= 133144 (so K * 127^2 fits in int32).
+ *  - Every call only enqueues work on `stream` (NULL = the default stream)
+ *    and returns; it never allocates, frees or synchronizes.  The library
+ *    keeps no mutable state, so concurrent calls on different streams with
+ *    separate outputs and workspaces are safe.
+ *  - Status codes: arguments are checked on the host before anything is
+ *    enqueued, in this order: null pointers, non-positive sizes or a NaN /
+ *    negative threshold -> LLMINT8_ERR_INVALID_ARG; K or N not a multiple of
+ *    64 or K > 133144 -> LLMINT8_ERR_UNSUPPORTED_SHAPE; workspace smaller than
+ *    the query -> LLMINT8_ERR_WORKSPACE.  A failed launch -> LLMINT8_ERR_HIP.
+ *    On an error status nothing has been enqueued (for LLMINT8_ERR_HIP, the
+ *    launches before the failing one may have been).  Faults inside kernels
+ *    surface at the caller's next synchronization, as for any HIP work.
+ *  - Inputs must be finite (not checked).
+ */
+#ifndef LLMINT8_H
+#define LLMINT8_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifndef LLMINT8_API
+#define LLMINT8_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LLMINT8_OK = 0,
+    LLMINT8_ERR_INVALID_ARG = 1,
+    LLMINT8_ERR_UNSUPPORTED_SHAPE = 2,
+    LLMINT8_ERR_WORKSPACE = 3,
+    LLMINT8_ERR_HIP = 4
+} llmint8_status_t;
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+LLMINT8_API const char *llmint8_status_string(int status);
+
+/* Bytes of workspace llmint8_matmul needs for a [T,K] x [K,N] call (the
+ * worst case over all outlier counts: the fp16 outlier operands may cover
+ * every column when the threshold is 0).  Pure host function; returns 0 for
+ * invalid sizes. */
+LLMINT8_API size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N);
+
+/* Bytes of workspace llmint8_quantize_act needs for K columns. */
+LLMINT8_API size_t llmint8_quantize_act_workspace_bytes(int64_t K);
+
+/*
+ * Weight quantization (agentlenshq.com write-up, section "Integration into
+ * transformers": the weight is quantized once, when it is moved to the GPU,
+ * into int8 CB in [-127, 127] plus SCB, with W ~= CB * SCB / 127; vector-wise,
+ * one scale per output column -- LLM.int8() summary, section "Vector-wise
+ * Quantization").
+ *
+ *   W_t  in : fp16 [N,K]  -- W transposed (row n = output column n), the
+ *                            nn.Linear weight layout
+ *   CB   out: int8 [N,K]  -- CB[n,k] = round(127 * W_t[n,k] / SCB[n]), 0 if SCB[n] = 0
+ *   SCB  out: f32  [N]    -- SCB[n] = max_k |W_t[n,k]| (an fp16 value)
+ *
+ * Call it once per weight; quantizing an already dequantized weight again is
+ * not an identity in general.
+ */
+LLMINT8_API llmint8_status_t llmint8_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N,
+                                         int8_t *CB, float *SCB, hipStream_t stream);
+
+/*
+ * Activation quantization: outlier-column detection and row-wise absmax
+ * quantization of the remaining columns (agentlenshq.com write-up, "Core
+ * idea" steps 1-2; LLM.int8() summary, sections "8-bit Data Types and
+ * Quantization" and "The Core of LLM.int8()").
+ *
+ *   X            in : fp16 [T,K]
+ *   threshold    in : outliers are columns with some |x| > threshold
+ *                     (strict; 6.0 is the pages' value; +inf = no outliers,
+ *                     0 = every column holding a nonzero)
+ *   Xq           out: int8 [T,K], outlier columns stored as 0
+ *   row_absmax   out: f32  [T], a[t] over the non-outlier columns (0 if none)
+ *   outlier_idx  out: int32 [K] capacity; entries [0, n) are O ascending,
+ *                     later entries are unspecified
+ *   n_outliers   out: int32 [1] (device), n = |O|
+ *   ws, ws_bytes    : scratch of at least
+ *                     llmint8_quantize_act_workspace_bytes(K) bytes
+ */
+LLMINT8_API llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                                      int8_t *Xq, float *row_absmax, int32_t *outlier_idx,
+                                      int32_t *n_outliers, void *ws, size_t ws_bytes,
+                                      hipStream_t stream);
+
+/*
+ * The decomposition matmul (LLM.int8() summary, section "The Core of
+ * LLM.int8(): Mixed-precision Decomposition"; agentlenshq.com write-up,
+ * "Core idea" step 3: dequantize the int8 result and add the fp16 outlier
+ * result).  Runs activation quantization, the int8 product with int32
+ * accumulation, vector-wise dequantization by a[t] * SCB[n] / 127^2, the
+ * fp16 product of the outlier columns with the dequantized weight rows, and
+ * the optional bias, with a single rounding to fp16 at the end.
+ *
+ *   X          in : fp16 [T,K]
+ *   CB, SCB    in : from llmint8_quantize_weight, [N,K] int8 and [N] f32
+ *   bias       in : fp16 [N] or NULL
+ *   threshold  in : as for llmint8_quantize_act
+ *   out        out: fp16 [T,N] (overflow rounds to +-inf)
+ *   ws, ws_bytes  : scratch of at least llmint8_workspace_bytes(T, K, N)
+ *
+ * T <= 16 runs a weight-streaming kernel (the decode regime), larger T a
+ * tiled MFMA GEMM; both give results that meet the same tolerance.
+ */
+LLMINT8_API llmint8_status_t llmint8_matmul(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                const int8_t *CB, const float *SCB, const uint16_t *bias,
+                                float threshold, uint16_t *out, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/*
+ * llmint8_matmul with the kernel choice forced and optional timing events,
+ * for tests and benchmarks: path 0 = automatic, 1 = tiled GEMM, 2 =
+ * weight-streaming kernel (requires T <= 16, else
+ * LLMINT8_ERR_UNSUPPORTED_SHAPE).  When main_start / main_stop are non-NULL
+ * they are recorded on `stream` immediately before and after the launch of
+ * the main kernel (the GEMM or weight-streaming kernel), so their elapsed
+ * time is that kernel's duration.  The events are created and owned by the
+ * caller.
+ */
+LLMINT8_API llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                     const int8_t *CB, const float *SCB, const uint16_t *bias,
+                                     float threshold, uint16_t *out, void *ws, size_t ws_bytes,
+                                     int path, hipEvent_t main_start, hipEvent_t main_stop,
+                                     hipStream_t stream);
+
+/*
+ * The int8 product alone, C[t,n] = sum_k Xq[t,k] * CB[n,k] in int32 (LLM.int8()
+ * summary, section "Int8 Matrix Multiplication with 16-bit Float Inputs and
+ * Outputs"), through the same main loops as llmint8_matmul with the epilogue
+ * storing the raw accumulators.  For exact checks of the accumulators.
+ *
+ *   Xq in: int8 [T,K];  CB in: int8 [N,K];  C out: int32 [T,N]
+ *   path: 0 = automatic, 1 = tiled GEMM, 2 = weight-streaming (T <= 16)
+ */
+LLMINT8_API llmint8_status_t llmint8_igemm_i32(const int8_t *Xq, int64_t T, int64_t K, int64_t N,
+                                   const int8_t *CB, int32_t *C, int path, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLMINT8_H */

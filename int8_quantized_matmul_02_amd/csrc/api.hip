@@ -1,0 +1,186 @@
+// api.hip -- the C ABI: argument checks, workspace layout, kernel dispatch.
+// The operations and their sources are documented in include/llmint8.h.
+
+#include <math.h>
+
+#include "../../include/llmint8.h"
+#include "internal.h"
+
+namespace llmint8 {
+
+namespace {
+constexpr int64_t kMaxK = 133144;   // floor((2^31 - 1) / 127^2): K * 127^2 fits in int32
+constexpr int64_t kDecodeMaxT = 16;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+llmint8_status_t check_shape(int64_t T, int64_t K, int64_t N)
+{
+    if (T <= 0 || K <= 0 || N <= 0)
+        return LLMINT8_ERR_INVALID_ARG;
+    if (K % 64 != 0 || N % 64 != 0 || K > kMaxK)
+        return LLMINT8_ERR_UNSUPPORTED_SHAPE;
+    return LLMINT8_OK;
+}
+
+bool bad_threshold(float thr) { return isnan(thr) || thr < 0.0f; }
+}  // namespace
+
+MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N)
+{
+    MatmulWorkspace L;
+    size_t off = 0;
+    const size_t t = (size_t)T, k = (size_t)K, n = (size_t)N;
+    L.flags = off;       off += align256(k);
+    L.colmap = off;      off += align256(4 * k);
+    L.outlier_idx = off; off += align256(4 * k);
+    L.n_outliers = off;  off += 256;
+    L.row_absmax = off;  off += align256(4 * t);
+    L.xq = off;          off += align256(t * k);
+    L.x_out = off;       off += align256(2 * t * k);
+    L.w_out = off;       off += align256(2 * n * k);
+    L.total = off;
+    return L;
+}
+
+size_t act_workspace_bytes(int64_t K) { return align256((size_t)K) + align256(4 * (size_t)K); }
+
+}  // namespace llmint8
+
+using namespace llmint8;
+
+extern "C" {
+
+const char *llmint8_status_string(int status)
+{
+    switch (status) {
+    case LLMINT8_OK: return "LLMINT8_OK";
+    case LLMINT8_ERR_INVALID_ARG: return "LLMINT8_ERR_INVALID_ARG: null/misaligned pointer, non-positive size or NaN/negative threshold";
+    case LLMINT8_ERR_UNSUPPORTED_SHAPE: return "LLMINT8_ERR_UNSUPPORTED_SHAPE: K and N must be multiples of 64, K <= 133144 (and T <= 16 for the weight-streaming path)";
+    case LLMINT8_ERR_WORKSPACE: return "LLMINT8_ERR_WORKSPACE: workspace smaller than the size query";
+    case LLMINT8_ERR_HIP: return "LLMINT8_ERR_HIP: a kernel launch failed";
+    default: return "LLMINT8: unknown status";
+    }
+}
+
+size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N)
+{
+    if (T <= 0 || K <= 0 || N <= 0)
+        return 0;
+    return matmul_workspace_layout(T, K, N).total;
+}
+
+size_t llmint8_quantize_act_workspace_bytes(int64_t K)
+{
+    if (K <= 0)
+        return 0;
+    return act_workspace_bytes(K);
+}
+
+llmint8_status_t llmint8_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N, int8_t *CB,
+                                         float *SCB, hipStream_t stream)
+{
+    if (!W_t || !CB || !SCB || !aligned16(W_t) || !aligned16(CB))
+        return LLMINT8_ERR_INVALID_ARG;
+    llmint8_status_t st = check_shape(1, K, N);
+    if (st != LLMINT8_OK)
+        return st;
+    return launch_quantize_weight(W_t, K, N, CB, SCB, stream) == hipSuccess ? LLMINT8_OK
+                                                                            : LLMINT8_ERR_HIP;
+}
+
+llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                                      int8_t *Xq, float *row_absmax, int32_t *outlier_idx,
+                                      int32_t *n_outliers, void *ws, size_t ws_bytes,
+                                      hipStream_t stream)
+{
+    if (!X || !Xq || !row_absmax || !outlier_idx || !n_outliers || !ws || !aligned16(X) ||
+        !aligned16(Xq) || !aligned16(ws) || bad_threshold(threshold))
+        return LLMINT8_ERR_INVALID_ARG;
+    llmint8_status_t st = check_shape(T, K, 64);
+    if (st != LLMINT8_OK)
+        return st;
+    if (ws_bytes < act_workspace_bytes(K))
+        return LLMINT8_ERR_WORKSPACE;
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    uint8_t *flags = base;
+    int32_t *colmap = reinterpret_cast<int32_t *>(base + align256((size_t)K));
+    hipError_t e = launch_quantize_act(X, T, K, threshold, Xq, row_absmax, outlier_idx,
+                                       n_outliers, flags, colmap, nullptr, stream);
+    return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
+}
+
+llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                     const int8_t *CB, const float *SCB, const uint16_t *bias,
+                                     float threshold, uint16_t *out, void *ws, size_t ws_bytes,
+                                     int path, hipEvent_t main_start, hipEvent_t main_stop,
+                                     hipStream_t stream)
+{
+    if (!X || !CB || !SCB || !out || !ws || !aligned16(X) || !aligned16(CB) ||
+        !aligned16(out) || !aligned16(ws) || bad_threshold(threshold) || path < 0 || path > 2)
+        return LLMINT8_ERR_INVALID_ARG;
+    llmint8_status_t st = check_shape(T, K, N);
+    if (st != LLMINT8_OK)
+        return st;
+    if (path == 2 && T > kDecodeMaxT)
+        return LLMINT8_ERR_UNSUPPORTED_SHAPE;
+    const MatmulWorkspace L = matmul_workspace_layout(T, K, N);
+    if (ws_bytes < L.total)
+        return LLMINT8_ERR_WORKSPACE;
+    const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
+
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    uint8_t *flags = base + L.flags;
+    int32_t *colmap = reinterpret_cast<int32_t *>(base + L.colmap);
+    int32_t *O = reinterpret_cast<int32_t *>(base + L.outlier_idx);
+    int32_t *n_out = reinterpret_cast<int32_t *>(base + L.n_outliers);
+    float *a = reinterpret_cast<float *>(base + L.row_absmax);
+    int8_t *Xq = reinterpret_cast<int8_t *>(base + L.xq);
+    uint16_t *x_out = reinterpret_cast<uint16_t *>(base + L.x_out);
+    uint16_t *w_out = reinterpret_cast<uint16_t *>(base + L.w_out);
+
+    if (launch_quantize_act(X, T, K, threshold, Xq, a, O, n_out, flags, colmap, x_out, stream) !=
+        hipSuccess)
+        return LLMINT8_ERR_HIP;
+    EpilogueArgs ep{a, SCB, x_out, w_out, O, n_out, bias, out, nullptr};
+    hipError_t e = hipSuccess;
+    if (!decode)
+        e = launch_gather_outlier_weights(CB, SCB, O, n_out, K, N, w_out, stream);
+    if (e == hipSuccess && main_start)
+        e = hipEventRecord(main_start, stream);
+    if (e == hipSuccess)
+        e = decode ? launch_decode(Xq, CB, T, K, N, ep, stream)
+                   : launch_gemm(Xq, CB, T, K, N, ep, stream);
+    if (e == hipSuccess && main_stop)
+        e = hipEventRecord(main_stop, stream);
+    return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
+}
+
+llmint8_status_t llmint8_matmul(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                const int8_t *CB, const float *SCB, const uint16_t *bias,
+                                float threshold, uint16_t *out, void *ws, size_t ws_bytes,
+                                hipStream_t stream)
+{
+    return llmint8_matmul_path(X, T, K, N, CB, SCB, bias, threshold, out, ws, ws_bytes, 0,
+                               nullptr, nullptr, stream);
+}
+
+llmint8_status_t llmint8_igemm_i32(const int8_t *Xq, int64_t T, int64_t K, int64_t N,
+                                   const int8_t *CB, int32_t *C, int path, hipStream_t stream)
+{
+    if (!Xq || !CB || !C || !aligned16(Xq) || !aligned16(CB) || path < 0 || path > 2)
+        return LLMINT8_ERR_INVALID_ARG;
+    llmint8_status_t st = check_shape(T, K, N);
+    if (st != LLMINT8_OK)
+        return st;
+    if (path == 2 && T > kDecodeMaxT)
+        return LLMINT8_ERR_UNSUPPORTED_SHAPE;
+    const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
+    EpilogueArgs ep{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, C};
+    hipError_t e = decode ? launch_decode(Xq, CB, T, K, N, ep, stream)
+                          : launch_gemm(Xq, CB, T, K, N, ep, stream);
+    return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// internal.h -- device helpers and launcher declarations shared by the
+// library's translation units (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llmint8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kOutlierPad = 32;   // outlier operands are zero-padded to a multiple of this
+
+__device__ __forceinline__ float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default mode); overflow -> inf.
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// round(127 * x / a) to nearest, ties to even, for fp16 values x and a with
+// |x| <= a and a > 0.  127*x is exact in fp32 (7 + 11 bits) and the quotient
+// is one IEEE-correct fp32 division (the library is built with
+// -fhip-fp32-correctly-rounded-divide-sqrt): such a quotient of binary16
+// values never lands on the wrong side of, or onto, a half-integer, so this
+// is the exact-rational rounding.
+__device__ __forceinline__ int quant127(float x, float a)
+{
+    return (int)__builtin_rintf((127.0f * x) / a);
+}
+
+// fp16 nearest to cb * scb / 127: the product is exact in fp32 and the fp32
+// quotient of a rational with odd denominator 127 cannot sit on or across a
+// binary16 midpoint, so the two roundings give the singly rounded value.
+__device__ __forceinline__ uint16_t dequant_w(int cb, float scb)
+{
+    return f2h(((float)cb * scb) / 127.0f);
+}
+
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        unsigned o = __shfl_xor(v, off, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Workspace segments of one llmint8_matmul call (byte offsets from the base).
+struct MatmulWorkspace {
+    size_t flags, colmap, outlier_idx, n_outliers, row_absmax, xq, x_out, w_out, total;
+};
+MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N);
+size_t act_workspace_bytes(int64_t K);
+
+// ---- launchers (each enqueues on `s`; return hipGetLastError()) ----
+hipError_t launch_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N, int8_t *CB,
+                                  float *SCB, hipStream_t s);
+
+// Outlier detection + compaction + row quantization.  x_out (fp16 [T, ldo],
+// ldo = K) receives the gathered outlier columns when non-null.
+hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                               int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
+                               uint8_t *flags, int32_t *colmap, uint16_t *x_out,
+                               hipStream_t s);
+
+// Dequantized outlier weight rows: w_out[n, j] = fp16(CB[n,O[j]]*SCB[n]/127),
+// zero for n_outliers <= j < pad32(n_outliers); row stride ldo = K.
+hipError_t launch_gather_outlier_weights(const int8_t *CB, const float *SCB, const int32_t *O,
+                                         const int32_t *n_out, int64_t K, int64_t N,
+                                         uint16_t *w_out, hipStream_t s);
+
+struct EpilogueArgs {
+    const float *a;          // [T] row absmax
+    const float *scb;        // [N]
+    const uint16_t *x_out;   // [T, ldo] gathered outlier activations (fp16)
+    const uint16_t *w_out;   // [N, ldo] dequantized outlier weights (fp16), GEMM path
+    const int32_t *O;        // [n] outlier column indices (weight-streaming path)
+    const int32_t *n_out;    // device scalar n
+    const uint16_t *bias;    // [N] or null
+    uint16_t *out;           // [T, N] fp16
+    int32_t *c_i32;          // [T, N] raw accumulators (debug epilogue) or null
+};
+
+hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
+                       const EpilogueArgs &ep, hipStream_t s);
+hipError_t launch_decode(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
+                         const EpilogueArgs &ep, hipStream_t s);
+
+}  // namespace llmint8

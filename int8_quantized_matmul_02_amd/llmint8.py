@@ -1,0 +1,209 @@
+"""Python binding of libllmint8.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls (see
+include/llmint8.h for the operation, layouts, ownership and errors).  Every
+step of the computation runs in the library's HIP kernels; torch only
+provides device memory (outputs and workspace, allocated here when the caller
+passes none) and the current stream.  There is no fallback: if the library is
+not built, or a call returns an error status, these functions raise.
+"""
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllmint8.so")
+_lib = None
+
+LLMINT8_OK = 0
+PATH_AUTO, PATH_GEMM, PATH_DECODE = 0, 1, 2
+
+EXPORTS = (
+    "llmint8_status_string",
+    "llmint8_workspace_bytes",
+    "llmint8_quantize_act_workspace_bytes",
+    "llmint8_quantize_weight",
+    "llmint8_quantize_act",
+    "llmint8_matmul",
+    "llmint8_matmul_path",
+    "llmint8_igemm_i32",
+)
+
+
+class LLMInt8Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %s" % (fn, _load().llmint8_status_string(status).decode()))
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            "libllmint8.so is not built (expected at %s); run "
+            "`python -m int8_quantized_matmul_02_amd.build` or __graft_entry__.build()" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, F, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_int
+    lib.llmint8_status_string.argtypes = [I]
+    lib.llmint8_status_string.restype = ctypes.c_char_p
+    lib.llmint8_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.llmint8_workspace_bytes.restype = SZ
+    lib.llmint8_quantize_act_workspace_bytes.argtypes = [I64]
+    lib.llmint8_quantize_act_workspace_bytes.restype = SZ
+    lib.llmint8_quantize_weight.argtypes = [P, I64, I64, P, P, P]
+    lib.llmint8_quantize_act.argtypes = [P, I64, I64, F, P, P, P, P, P, SZ, P]
+    lib.llmint8_matmul.argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ, P]
+    lib.llmint8_matmul_path.argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ, I, P, P, P]
+    lib.llmint8_igemm_i32.argtypes = [P, I64, I64, I64, P, P, I, P]
+    for fn in ("llmint8_quantize_weight", "llmint8_quantize_act", "llmint8_matmul",
+               "llmint8_matmul_path", "llmint8_igemm_i32"):
+        getattr(lib, fn).restype = I
+    _lib = lib
+    return lib
+
+
+def _check(fn, rc):
+    if rc != LLMINT8_OK:
+        raise LLMInt8Error(fn, rc)
+
+
+def _dev(t, name, dtypes):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device (cuda) tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+_H = (torch.float16, torch.int16)
+
+
+def llmint8_status_string(status):
+    return _load().llmint8_status_string(int(status)).decode()
+
+
+def llmint8_workspace_bytes(T, K, N):
+    return int(_load().llmint8_workspace_bytes(T, K, N))
+
+
+def llmint8_quantize_act_workspace_bytes(K):
+    return int(_load().llmint8_quantize_act_workspace_bytes(K))
+
+
+def llmint8_quantize_weight(W_t, CB=None, SCB=None):
+    """W_t: fp16 [N,K] (the nn.Linear weight layout).  Returns (CB int8 [N,K], SCB f32 [N])."""
+    lib = _load()
+    _dev(W_t, "W_t", _H)
+    N, K = W_t.shape
+    CB = torch.empty((N, K), dtype=torch.int8, device=W_t.device) if CB is None else _dev(CB, "CB", (torch.int8,))
+    SCB = torch.empty((N,), dtype=torch.float32, device=W_t.device) if SCB is None else _dev(SCB, "SCB", (torch.float32,))
+    _check("llmint8_quantize_weight",
+           lib.llmint8_quantize_weight(W_t.data_ptr(), K, N, CB.data_ptr(), SCB.data_ptr(), _stream(W_t)))
+    return CB, SCB
+
+
+def llmint8_quantize_act(X, threshold=6.0, Xq=None, row_absmax=None, outlier_idx=None,
+                         n_outliers=None, ws=None):
+    """X: fp16 [T,K].  Returns (Xq int8 [T,K], row_absmax f32 [T], outlier_idx int32 [K],
+    n_outliers int32 [1]); outlier_idx[:n] is the ascending outlier column list."""
+    lib = _load()
+    _dev(X, "X", _H)
+    T, K = X.shape
+    d = X.device
+    Xq = torch.empty((T, K), dtype=torch.int8, device=d) if Xq is None else _dev(Xq, "Xq", (torch.int8,))
+    row_absmax = torch.empty((T,), dtype=torch.float32, device=d) if row_absmax is None else row_absmax
+    outlier_idx = torch.empty((K,), dtype=torch.int32, device=d) if outlier_idx is None else outlier_idx
+    n_outliers = torch.empty((1,), dtype=torch.int32, device=d) if n_outliers is None else n_outliers
+    need = llmint8_quantize_act_workspace_bytes(K)
+    ws = torch.empty((need,), dtype=torch.uint8, device=d) if ws is None else ws
+    _check("llmint8_quantize_act",
+           lib.llmint8_quantize_act(X.data_ptr(), T, K, float(threshold), Xq.data_ptr(),
+                                    row_absmax.data_ptr(), outlier_idx.data_ptr(),
+                                    n_outliers.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                    _stream(X)))
+    return Xq, row_absmax, outlier_idx, n_outliers
+
+
+def llmint8_matmul_path(X, CB, SCB, threshold=6.0, bias=None, out=None, ws=None, path=PATH_AUTO,
+                        main_start=None, main_stop=None):
+    """X fp16 [T,K], CB int8 [N,K], SCB f32 [N], bias fp16 [N] or None -> out fp16 [T,N].
+
+    main_start / main_stop: optional raw hipEvent_t handles (ints) recorded
+    around the main kernel's launch."""
+    lib = _load()
+    _dev(X, "X", _H)
+    _dev(CB, "CB", (torch.int8,))
+    _dev(SCB, "SCB", (torch.float32,))
+    T, K = X.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K or SCB.shape != (N,):
+        raise ValueError("shape mismatch: X %s, CB %s, SCB %s" % (tuple(X.shape), tuple(CB.shape), tuple(SCB.shape)))
+    if bias is not None:
+        _dev(bias, "bias", _H)
+        if bias.shape != (N,):
+            raise ValueError("bias must have shape (%d,)" % N)
+    out = torch.empty((T, N), dtype=torch.float16, device=X.device) if out is None else _dev(out, "out", _H)
+    if ws is None:
+        ws = torch.empty((llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=X.device)
+    _check("llmint8_matmul_path",
+           lib.llmint8_matmul_path(X.data_ptr(), T, K, N, CB.data_ptr(), SCB.data_ptr(),
+                                   bias.data_ptr() if bias is not None else None,
+                                   float(threshold), out.data_ptr(), ws.data_ptr(),
+                                   ws.numel() * ws.element_size(), int(path),
+                                   ctypes.c_void_p(main_start) if main_start else None,
+                                   ctypes.c_void_p(main_stop) if main_stop else None,
+                                   _stream(X)))
+    return out
+
+
+def llmint8_matmul(X, CB, SCB, threshold=6.0, bias=None, out=None, ws=None):
+    """The LLM.int8() decomposition matmul; see llmint8_matmul_path."""
+    lib = _load()
+    _dev(X, "X", _H)
+    _dev(CB, "CB", (torch.int8,))
+    _dev(SCB, "SCB", (torch.float32,))
+    T, K = X.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K or SCB.shape != (N,):
+        raise ValueError("shape mismatch: X %s, CB %s, SCB %s" % (tuple(X.shape), tuple(CB.shape), tuple(SCB.shape)))
+    if bias is not None:
+        _dev(bias, "bias", _H)
+    out = torch.empty((T, N), dtype=torch.float16, device=X.device) if out is None else _dev(out, "out", _H)
+    if ws is None:
+        ws = torch.empty((llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=X.device)
+    _check("llmint8_matmul",
+           lib.llmint8_matmul(X.data_ptr(), T, K, N, CB.data_ptr(), SCB.data_ptr(),
+                              bias.data_ptr() if bias is not None else None, float(threshold),
+                              out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                              _stream(X)))
+    return out
+
+
+def llmint8_igemm_i32(Xq, CB, C=None, path=PATH_AUTO):
+    """C int32 [T,N] = Xq int8 [T,K] @ CB int8 [N,K]^T, exact."""
+    lib = _load()
+    _dev(Xq, "Xq", (torch.int8,))
+    _dev(CB, "CB", (torch.int8,))
+    T, K = Xq.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K:
+        raise ValueError("shape mismatch: Xq %s, CB %s" % (tuple(Xq.shape), tuple(CB.shape)))
+    C = torch.empty((T, N), dtype=torch.int32, device=Xq.device) if C is None else _dev(C, "C", (torch.int32,))
+    _check("llmint8_igemm_i32",
+           lib.llmint8_igemm_i32(Xq.data_ptr(), T, K, N, CB.data_ptr(), C.data_ptr(), int(path),
+                                 _stream(Xq)))
+    return C

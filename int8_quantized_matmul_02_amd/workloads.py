@@ -114,6 +114,26 @@ def ffn_6p7b(seed=0, with_fc2=True):
     return d
 
 
+def ffn_6p7b_fc2_input(seed=0):
+    """A stand-in for the ReLU'd fc1 output that feeds fc2: [4096,16384] fp16.
+
+    fc1 of the 6.7B-style FFN maps rows holding the outlier dims to outputs of
+    standard deviation about 2.41 and the other rows to about 1.28 (from the
+    fc1 inputs and the N(0,0.02) weights); the stand-in draws ReLU(N(0, s_t^2))
+    with s_t = 2.41 in a seeded 75 % of rows and 1.28 elsewhere.  It is used
+    where an input must come from the generator rather than from a kernel."""
+    ss = np.random.SeedSequence([seed, 2])
+    r = np.random.Generator(np.random.PCG64(ss))
+    T, K = 4096, 16384
+    rows = r.random(T) < 0.75
+    std = np.where(rows, np.float32(2.41), np.float32(1.28)).astype(np.float32)
+    x = np.empty((T, K), np.float16)
+    for r0 in range(0, T, 512):
+        z = r.standard_normal((min(T, r0 + 512) - r0, K), dtype=np.float32) * std[r0:r0 + 512, None]
+        x[r0:r0 + 512] = np.maximum(z, 0.0).astype(np.float16)
+    return dict(X=x, threshold=6.0)
+
+
 def decode_175b(T, seed=0, with_weight=True):
     """X [T,12288], 6 dims +-U(20,60) in every row; W [12288,49152] (604 MB as int8)."""
     rx, rw = _streams(seed)
