@@ -1,0 +1,536 @@
+// gemm_kernel.h -- the tiled int8 MFMA GEMM with the fused LLM.int8() epilogue.
+//
+// C[t,n] = sum_k Xq[t,k] * CB[n,k] accumulates exactly in int32 (LLM.int8()
+// summary, kurtkim.github.io, section "Int8 Matrix Multiplication with 16-bit
+// Float Inputs and Outputs").  The epilogue dequantizes by the outer product
+// of the row and column scales, a[t] * SCB[n] / 127^2 (section "Vector-wise
+// Quantization"), adds the fp16 product of the outlier columns of X with the
+// matching dequantized weight rows and the bias, and rounds once to fp16
+// (section "The Core of LLM.int8(): Mixed-precision Decomposition"; the
+// agentlenshq.com write-up, "Core idea" step 3).
+//
+// Design (gfx950):
+//  * Block tile BM x BN, 64 bytes of K per pipeline stage, STAGES stages in
+//    LDS filled by direct global->LDS 16-byte loads (no VGPR staging): each
+//    wavefront load instruction fills 1 KB = 16 staged rows of 64 bytes.
+//  * Both operands are K-contiguous ([T,K] and [N,K]), so A and B fragments
+//    have the same shape: a lane reads 16 consecutive bytes of one row.  The
+//    16-byte chunks of staged row r are XOR-swizzled (chunk c in slot
+//    c ^ swz(r)) so the 16-byte fragment reads of consecutive rows spread
+//    over all LDS banks.
+//  * Wavefronts are WM x WN over the block tile, each owning FM x FN
+//    accumulator tiles of 32x32 (v_mfma_i32_32x32x32_i8; the k order inside
+//    an MFMA is irrelevant for an exact integer sum because A and B use the
+//    same lane -> k mapping).
+//  * The fp16 outlier product (K' = number of outlier columns, padded to 32)
+//    runs through the same pipeline on the gathered fp16 operands with
+//    v_mfma_f32_32x32x16_f16, accumulating onto the dequantized fp32 values.
+//  * Tiles are numbered XCD-aware: workgroup ids are dealt round-robin over
+//    the 8 XCDs, so each XCD gets a contiguous run of tile ids, and tile ids
+//    walk a grouped raster (GROUP tile rows at a time) for L2 reuse.
+#pragma once
+
+#include "internal.h"
+
+namespace llmint8 {
+namespace gemm {
+namespace {   // internal linkage: nothing here is exported from the library
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kRowBytes = 64;   // bytes of each operand row staged per pipeline stage
+constexpr int kXcds = 8;
+
+// Measured on gfx950: 16-lane groups of ds_read_b128 hit 64 banks; rows of
+// 64 bytes put rows r, r+4, r+8, r+12 on the same banks, which this spreads.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int GROUP_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_, GROUP = GROUP_;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
+    static constexpr int kAInstr = BM / 16 / kWaves;   // 1 KB load instructions per wave per stage
+    static constexpr int kBInstr = BN / 16 / kWaves;
+    static constexpr int kLoads = kAInstr + kBInstr;
+    static constexpr int kStageBytes = (BM + BN) * kRowBytes;
+    static constexpr int kLdsBytes = STAGES * kStageBytes;
+    static_assert(BM % (16 * kWaves) == 0 && BN % (16 * kWaves) == 0, "load split");
+    static_assert(FM >= 1 && FN >= 1, "wave tile");
+    static_assert(STAGES >= 2, "pipeline depth");
+};
+
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left alone (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void tile_coords(int bid, int nblk, int ntm, int ntn, int group, int &tm,
+                                            int &tn)
+{
+    const int q = nblk / kXcds, r = nblk % kXcds;
+    const int x = bid % kXcds, loc = bid / kXcds;
+    const int t = x < r ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
+    const int per_group = group * ntn;
+    const int g = t / per_group, first = g * group;
+    const int gs = ntm - first < group ? ntm - first : group;
+    const int w = t - g * per_group;
+    tm = first + w % gs;
+    tn = w / gs;
+}
+
+// One operand pair streamed through the LDS ring: per-lane DMA source offsets
+// (bytes, relative to the tile's first row) for each of this wave's load
+// instructions.
+template <class C>
+struct Streams {
+    const char *a, *b;              // first row of the tile (row-major, K-contiguous)
+    uint32_t offA[C::kAInstr], offB[C::kBInstr];
+
+    __device__ __forceinline__ void init(const char *abase, int64_t lda, int64_t m0, int64_t mrows,
+                                         const char *bbase, int64_t ldb, int64_t n0, int64_t nrows,
+                                         int wave, int lane)
+    {
+        a = abase + m0 * lda;
+        b = bbase + n0 * ldb;
+#pragma unroll
+        for (int j = 0; j < C::kAInstr; ++j) {
+            const int r = (wave * C::kAInstr + j) * 16 + lane / 4;
+            const int64_t row = m0 + r < mrows ? r : mrows - 1 - m0;   // ragged: clamp
+            offA[j] = (uint32_t)(row * lda + (((lane & 3) ^ swz(r)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < C::kBInstr; ++j) {
+            const int r = (wave * C::kBInstr + j) * 16 + lane / 4;
+            const int64_t row = n0 + r < nrows ? r : nrows - 1 - n0;
+            offB[j] = (uint32_t)(row * ldb + (((lane & 3) ^ swz(r)) << 4));
+        }
+    }
+
+    // The j-th of this wave's kLoads load instructions for a stage (A first).
+    __device__ __forceinline__ void issue_one(char *smem, int stage, int64_t kbyte, int wave,
+                                              int j) const
+    {
+        char *sa = smem + stage * C::kStageBytes;
+        char *sb = sa + C::BM * kRowBytes;
+        if (j < C::kAInstr)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(a + kbyte + offA[j]),
+                (lds_void *)(sa + (wave * C::kAInstr + j) * 16 * kRowBytes), 16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(b + kbyte + offB[j - C::kAInstr]),
+                (lds_void *)(sb + (wave * C::kBInstr + j - C::kAInstr) * 16 * kRowBytes), 16,
+                0, 0);
+    }
+
+    __device__ __forceinline__ void issue(char *smem, int stage, int64_t kbyte, int wave) const
+    {
+        char *sa = smem + stage * C::kStageBytes;
+        char *sb = sa + C::BM * kRowBytes;
+#pragma unroll
+        for (int j = 0; j < C::kAInstr; ++j)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(a + kbyte + offA[j]),
+                (lds_void *)(sa + (wave * C::kAInstr + j) * 16 * kRowBytes), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < C::kBInstr; ++j)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(b + kbyte + offB[j]),
+                (lds_void *)(sb + (wave * C::kBInstr + j) * 16 * kRowBytes), 16, 0, 0);
+    }
+};
+
+struct MfmaI8 {
+    typedef v16i acc_t;
+    __device__ __forceinline__ static acc_t op(v4i a, v4i b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+    }
+};
+
+// fp16 MFMA on accumulators that hold fp32 bit patterns in the same
+// registers as the int32 sums (the epilogue converts them in place).
+struct MfmaF16 {
+    typedef v16i acc_t;
+    __device__ __forceinline__ static acc_t op(v4i a, v4i b, acc_t c)
+    {
+        return __builtin_bit_cast(
+            v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a),
+                                                         __builtin_bit_cast(v8h, b),
+                                                         __builtin_bit_cast(v16f, c), 0, 0, 0));
+    }
+};
+
+// Fragments of one 32-deep k-step: FM A-fragments and FN B-fragments.
+template <class C>
+struct Frags {
+    v4i a[C::FM], b[C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ void read_frags(Frags<C> &f, const char *sa, const char *sb, int fo)
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+        f.a[i] = *reinterpret_cast<const v4i *>(sa + i * 32 * kRowBytes + fo);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+        f.b[j] = *reinterpret_cast<const v4i *>(sb + j * 32 * kRowBytes + fo);
+}
+
+template <class C, class M>
+__device__ __forceinline__ void mfmas(const Frags<C> &f, typename M::acc_t (&acc)[C::FM][C::FN])
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = M::op(f.a[i], f.b[j], acc[i][j]);
+}
+
+template <class C>
+__device__ __forceinline__ void read_one(Frags<C> &f, const char *sa, const char *sb, int fo, int g)
+{
+    if (g < C::FM)
+        f.a[g] = *reinterpret_cast<const v4i *>(sa + g * 32 * kRowBytes + fo);
+    else
+        f.b[g - C::FM] = *reinterpret_cast<const v4i *>(sb + (g - C::FM) * 32 * kRowBytes + fo);
+}
+
+// One half-stage in a fixed issue order: groups of (one global->LDS load,
+// one fragment read of the next k-step, FM*FN/groups MFMAs of this k-step),
+// pinned with scheduling barriers so the loads and reads always sit between
+// MFMAs and the matrix core never waits on their issue.
+template <class C, class M, bool kWithLoads>
+__device__ __forceinline__ void half_stage(const Frags<C> &cur, Frags<C> &nxt, const char *sa,
+                                           const char *sb, int fo,
+                                           typename M::acc_t (&acc)[C::FM][C::FN],
+                                           const Streams<C> &st, char *smem, int stage,
+                                           int64_t kbyte, int wave)
+{
+    constexpr int kReads = C::FM + C::FN, kMfma = C::FM * C::FN;
+    constexpr int kGroups = kReads > C::kLoads ? kReads : C::kLoads;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+        if (kWithLoads && g < C::kLoads)
+            st.issue_one(smem, stage, kbyte, wave, g);
+        if (g < kReads)
+            read_one<C>(nxt, sa, sb, fo, g);
+#pragma unroll
+        for (int idx = g * kMfma / kGroups; idx < (g + 1) * kMfma / kGroups; ++idx) {
+            const int i = idx / C::FN, j = idx % C::FN;
+            acc[i][j] = M::op(cur.b[j], cur.a[i], acc[i][j]);   // D[n][t]: see k_gemm
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// fp16 MFMA on fp32 accumulators.
+struct MfmaF16F {
+    typedef v16f acc_t;
+    __device__ __forceinline__ static acc_t op(v4i a, v4i b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a),
+                                                      __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+    }
+};
+
+// Runs numK stages (64 bytes of K = two 32-deep k-steps each) of the
+// pipelined main loop.  Stage s is loaded into LDS buffer s % STAGES.  Every
+// trip loads exactly one stage (stages past the end reload the last one into
+// a buffer nobody reads), so the number of loads in flight at each wait is a
+// constant and the loop body has no branches for the scheduler to stop at.
+// The barrier sits between the two k-steps of a stage, so the MFMAs issued
+// before it keep the matrix cores busy while the wavefronts synchronize.
+template <class C, class M>
+__device__ __forceinline__ void mainloop(char *smem, const Streams<C> &st, int numK,
+                                         typename M::acc_t (&acc)[C::FM][C::FN], int wm, int wn,
+                                         int wave, int lane)
+{
+    static_assert(C::STAGES >= 3, "mid-stage barrier needs at least 3 stages");
+    // fragment read offsets: row (lane&31) of each 32-row tile, chunk 2s + lane/32
+    const int frow = (lane & 31) * kRowBytes;
+    const int fo0 = frow + ((((lane >> 5)) ^ swz(lane & 31)) << 4);
+    const int fo1 = frow + (((2 + (lane >> 5)) ^ swz(lane & 31)) << 4);
+    const int aoff = wm * (C::BM / C::WM) * kRowBytes;
+    const int boff = C::BM * kRowBytes + wn * (C::BN / C::WN) * kRowBytes;
+    const int64_t klast = (int64_t)(numK - 1) * kRowBytes;
+    auto kb = [&](int s) -> int64_t {
+        const int64_t k = (int64_t)s * kRowBytes;
+        return k < klast ? k : klast;
+    };
+
+#pragma unroll
+    for (int s = 0; s < C::STAGES - 1; ++s)
+        st.issue(smem, s, kb(s), wave);
+    wait_vm<(C::STAGES - 2) * C::kLoads>();   // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+
+    Frags<C> f0, f1;
+    read_frags<C>(f0, smem + aoff, smem + boff, fo0);
+    for (int kt = 0; kt < numK; ++kt) {
+        const char *sa = smem + (kt % C::STAGES) * C::kStageBytes + aoff;
+        const char *sb = smem + (kt % C::STAGES) * C::kStageBytes + boff;
+        // first half: reads of k-step 1 under the MFMAs of k-step 0
+        half_stage<C, M, false>(f0, f1, sa, sb, fo1, acc, st, smem, 0, 0, wave);
+        wait_vm<(C::STAGES - 3) * C::kLoads>();   // stage kt+1 landed
+        __builtin_amdgcn_s_barrier();
+        // second half: every wavefront is past stage kt-1, so refill its buffer,
+        // and read the next stage's k-step 0, under k-step 1's MFMAs
+        const int nk = kt + 1 < numK ? kt + 1 : kt;
+        half_stage<C, M, true>(f1, f0, smem + (nk % C::STAGES) * C::kStageBytes + aoff,
+                               smem + (nk % C::STAGES) * C::kStageBytes + boff, fo0, acc, st,
+                               smem, (kt + C::STAGES - 1) % C::STAGES, kb(kt + C::STAGES - 1),
+                               wave);
+    }
+    wait_vm<0>();   // the tail loads land before anyone reuses the buffers
+}
+
+// Bias, one rounding to fp16 and 8-byte stores for one transposed 32x32
+// accumulator tile: row t, columns n0 + 8g + {0..3} in registers 4g..4g+3.
+template <class C>
+__device__ __forceinline__ void store_tile(const EpilogueArgs &ep, v16f d, int64_t t, int64_t n0,
+                                           int64_t T, int64_t N)
+{
+    if (t >= T)
+        return;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + 8 * g;
+        if (n >= N)
+            continue;
+        float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (ep.bias) {
+            const uint2 bb = *reinterpret_cast<const uint2 *>(ep.bias + n);
+            b[0] = h2f((uint16_t)(bb.x & 0xffffu));
+            b[1] = h2f((uint16_t)(bb.x >> 16));
+            b[2] = h2f((uint16_t)(bb.y & 0xffffu));
+            b[3] = h2f((uint16_t)(bb.y >> 16));
+        }
+        uint16_t h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            h[q] = f2h(d[4 * g + q] + b[q]);
+        *reinterpret_cast<uint2 *>(ep.out + t * N + n) =
+            make_uint2((unsigned)h[0] | ((unsigned)h[1] << 16), (unsigned)h[2] | ((unsigned)h[3] << 16));
+    }
+}
+
+template <class C, bool kRawI32>
+__global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__ A,
+                                                      const int8_t *__restrict__ B, int64_t T,
+                                                      int64_t K, int64_t N, EpilogueArgs ep)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int ntm = (int)((T + C::BM - 1) / C::BM), ntn = (int)((N + C::BN - 1) / C::BN);
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, ntm, ntn, C::GROUP, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+
+    v16i acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0;
+
+    {
+        Streams<C> st;
+        st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
+                n0, N, wave, lane);
+        mainloop<C, MfmaI8>(smem, st, (int)(K / kRowBytes), acc, wm, wn, wave, lane);
+    }
+
+    // The MFMAs compute D = CB_tile * Xq_tile^T, so a 32x32 accumulator holds
+    // C transposed: lane l has output row t = lane%32 of the sub-tile and, in
+    // registers 4g..4g+3, the four consecutive output columns
+    // n = 8g + 4*(lane/32) + {0,1,2,3}.  Each lane therefore needs one row
+    // scale per sub-tile row and writes 4 adjacent outputs with one store.
+    const int tl = lane & 31, nl = 4 * (lane >> 5);
+    const int64_t tw = m0 + wm * (C::BM / C::WM), nw = n0 + wn * (C::BN / C::WN);
+    if constexpr (kRawI32) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            const int64_t t = tw + i * 32 + tl;
+            if (t >= T)
+                continue;
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t n = nw + j * 32 + 8 * g + nl;
+                    if (n < N)
+                        *reinterpret_cast<v4i *>(ep.c_i32 + t * N + n) =
+                            v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                acc[i][j][4 * g + 3]};
+                }
+        }
+    } else {
+        const int nout = *ep.n_out;
+        float at[C::FM];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            const int64_t t = tw + i * 32 + tl;
+            at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
+        }
+        if (nout <= kOutlierPad) {
+            // Up to 32 outlier columns: their fp16 fragments come straight from
+            // L2, and each 32x32 tile is finished on its own (dequantize, fp16
+            // MFMA over the outlier columns, bias, round, store) in a few VGPRs.
+            v4i xo[C::FM][2], wo[C::FN][2];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i) {
+                int64_t t = tw + i * 32 + tl;
+                t = t < T ? t : T - 1;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    xo[i][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.x_out + t * K + 16 * s2 + nl * 2)
+                                         : v4i{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                int64_t n = nw + j * 32 + tl;
+                n = n < N ? n : N - 1;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    wo[j][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.w_out + n * K + 16 * s2 + nl * 2)
+                                         : v4i{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                v4f sn[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    int64_t n = nw + j * 32 + 8 * g + nl;
+                    sn[g] = *reinterpret_cast<const v4f *>(ep.scb + (n < N ? n : N - 4));
+                }
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i) {
+                    v16f d;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        d[r] = (float)acc[i][j][r] * (at[i] * sn[r / 4][r % 4]);
+                    if (nout > 0) {
+                        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wo[j][0]),
+                                                                 __builtin_bit_cast(v8h, xo[i][0]), d, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wo[j][1]),
+                                                                 __builtin_bit_cast(v8h, xo[i][1]), d, 0, 0, 0);
+                    }
+                    store_tile<C>(ep, d, tw + i * 32 + tl, nw + j * 32 + nl, T, N);
+                }
+            }
+        } else {
+            // Many outlier columns: park the dequantized int8 part of the tile
+            // in the fp32 workspace; k_gemm_outliers adds the fp16 product.
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                v4f sn[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    int64_t n = nw + j * 32 + 8 * g + nl;
+                    sn[g] = *reinterpret_cast<const v4f *>(ep.scb + (n < N ? n : N - 4));
+                }
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i) {
+                    const int64_t t = tw + i * 32 + tl;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int64_t n = nw + j * 32 + 8 * g + nl;
+                        v4f d;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            d[q] = (float)acc[i][j][4 * g + q] * (at[i] * sn[g][q]);
+                        if (t < T && n < N)
+                            *reinterpret_cast<v4f *>(ep.d_part + t * N + n) = d;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// The fp16 product over more than 32 outlier columns, as its own GEMM
+// through the same LDS pipeline (K' = outlier count padded to 32), added to
+// the dequantized int8 part that k_gemm parked in d_part.  With 32 or fewer
+// outlier columns k_gemm has already finished the output and every block
+// returns at once.
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void k_gemm_outliers(int64_t T, int64_t K, int64_t N,
+                                                               EpilogueArgs ep)
+{
+    const int nout = *ep.n_out;
+    if (nout <= kOutlierPad)
+        return;
+    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int ntm = (int)((T + C::BM - 1) / C::BM), ntn = (int)((N + C::BN - 1) / C::BN);
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, ntm, ntn, C::GROUP, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+
+    v16f acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.0f;
+    {
+        Streams<C> st;
+        st.init(reinterpret_cast<const char *>(ep.x_out), 2 * K, m0, T,
+                reinterpret_cast<const char *>(ep.w_out), 2 * K, n0, N, wave, lane);
+        const int stages = (nout + kOutlierPad - 1) / kOutlierPad;   // 32 halves = 64 bytes each
+        mainloop<C, MfmaF16F>(smem, st, stages, acc, wm, wn, wave, lane);
+    }
+    const int tl = lane & 31, nl = 4 * (lane >> 5);
+    const int64_t tw = m0 + wm * (C::BM / C::WM), nw = n0 + wn * (C::BN / C::WN);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const int64_t t = tw + i * 32 + tl;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            v16f d = acc[i][j];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t n = nw + j * 32 + 8 * g + nl;
+                if (t < T && n < N) {
+                    const v4f p = *reinterpret_cast<const v4f *>(ep.d_part + t * N + n);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        d[4 * g + q] += p[q];
+                }
+            }
+            store_tile<C>(ep, d, t, nw + j * 32 + nl, T, N);
+        }
+    }
+}
+
+template <class C>
+hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
+                  const EpilogueArgs &ep, hipStream_t s)
+{
+    const int64_t ntm = (T + C::BM - 1) / C::BM, ntn = (N + C::BN - 1) / C::BN;
+    const dim3 grid((unsigned)(ntm * ntn));
+    if (ep.c_i32) {
+        hipLaunchKernelGGL((k_gemm<C, true>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K, N, ep);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((k_gemm<C, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K, N, ep);
+    hipLaunchKernelGGL((k_gemm_outliers<C>), grid, dim3(C::kThreads), 0, s, T, K, N, ep);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace gemm
+}  // namespace llmint8

@@ -51,7 +51,7 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
 
 // Workspace segments of one llmint8_matmul call (byte offsets from the base).
 struct MatmulWorkspace {
-    size_t flags, colmap, outlier_idx, n_outliers, row_absmax, xq, x_out, w_out, total;
+    size_t flags, colmap, outlier_idx, n_outliers, row_absmax, xq, x_out, w_out, d_part, total;
 };
 MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N);
 size_t act_workspace_bytes(int64_t K);
@@ -83,6 +83,8 @@ struct EpilogueArgs {
     const uint16_t *bias;    // [N] or null
     uint16_t *out;           // [T, N] fp16
     int32_t *c_i32;          // [T, N] raw accumulators (debug epilogue) or null
+    float *d_part;           // [T, N] fp32 scratch for the dequantized int8 part (GEMM path,
+                             // used when more than 32 columns are outliers)
 };
 
 hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
