@@ -37,6 +37,33 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def profiled_traffic(summary):
+    """HBM bytes per launch from a committed rocprofv3 counter summary in profiles/.
+
+    The summary records a hash of the kernel's sources; when the sources have
+    changed since the counters were taken the figure no longer describes the
+    kernel and None is returned."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        want, files = fields["kernel_sources_sha256_16"].split(None, 1)
+        h = hashlib.sha256()
+        for f in files.strip("()").split():
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest()[:16] != want:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError, OSError):
+        return None
+
+
 class HipEvents:
     """hipEvent_t handles through the HIP runtime torch has already loaded."""
 
@@ -120,7 +147,8 @@ def decode_bench(torch, L, workloads, steps, warmup, ev, dev):
                           "kernel_GBs": round(alg / (kms * 1e-3) / 1e9, 1),
                           "step_GBs": round(alg / (ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(alg / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                          "alg_bytes": alg}
+                          "alg_bytes": alg,
+                          "traffic": profiled_traffic("k_decode_175b_fc1.txt")}
         log("decode T=%d: kernel %.1f us (%.0f GB/s), step %.1f us" % (T, kms * 1e3, alg / kms / 1e6, ms * 1e3))
     return res
 
@@ -133,6 +161,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the CPU-oracle sample (4096 = the whole workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run one 256 MiB device-to-device copy first (a kernel of known traffic, "
+                         "for scaling hardware byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -146,6 +177,13 @@ def main():
 
     dev = torch.device("cuda", 0)
     ev = HipEvents()
+    if args.copy_calib:
+        src = torch.ones((256 << 20,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log("fc1 workload: generating inputs ...")
     d = workloads.ffn_6p7b(with_fc2=False)
     X_h, W_h, thr = d["X"], d["W_t"], d["threshold"]
@@ -185,7 +223,9 @@ def main():
                    "T": T, "K": K, "N": N, "threshold": thr, "n_outliers": n_outliers},
         "roofline": {"bound": "mfma", "kernel": "k_gemm (int8 MFMA GEMM + fused epilogue)",
                      "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                     "traffic": profiled_traffic("k_gemm_ffn_6p7b_fc1.txt"),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                      "kernel_us": round(gemm_ms * 1e3, 2), "ops_per_launch": ops},
     }
     if not args.no_decode:
