@@ -32,7 +32,8 @@ MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N)
     MatmulWorkspace L;
     size_t off = 0;
     const size_t t = (size_t)T, k = (size_t)K, n = (size_t)N;
-    L.flags = off;       off += align256(k);
+    L.partial = off;     off += align256((size_t)kMaxDetectSplits * (k / 8));
+    L.mask = off;        off += align256(k / 8);
     L.colmap = off;      off += align256(4 * k);
     L.outlier_idx = off; off += align256(4 * k);
     L.n_outliers = off;  off += 256;
@@ -45,7 +46,11 @@ MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N)
     return L;
 }
 
-size_t act_workspace_bytes(int64_t K) { return align256((size_t)K) + align256(4 * (size_t)K); }
+size_t act_workspace_bytes(int64_t K)
+{
+    const size_t k = (size_t)K;
+    return align256((size_t)kMaxDetectSplits * (k / 8)) + align256(k / 8) + align256(4 * k);
+}
 
 }  // namespace llmint8
 
@@ -105,10 +110,12 @@ llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, int64_t K, f
     if (ws_bytes < act_workspace_bytes(K))
         return LLMINT8_ERR_WORKSPACE;
     uint8_t *base = static_cast<uint8_t *>(ws);
-    uint8_t *flags = base;
-    int32_t *colmap = reinterpret_cast<int32_t *>(base + align256((size_t)K));
+    uint8_t *partial = base;
+    uint8_t *mask = base + align256((size_t)kMaxDetectSplits * ((size_t)K / 8));
+    int32_t *colmap = reinterpret_cast<int32_t *>(mask + align256((size_t)K / 8));
+    const GatherArgs none{nullptr, nullptr, 0, nullptr};
     hipError_t e = launch_quantize_act(X, T, K, threshold, Xq, row_absmax, outlier_idx,
-                                       n_outliers, flags, colmap, nullptr, stream);
+                                       n_outliers, partial, mask, colmap, nullptr, none, stream);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 
@@ -132,7 +139,8 @@ llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, in
     const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
 
     uint8_t *base = static_cast<uint8_t *>(ws);
-    uint8_t *flags = base + L.flags;
+    uint8_t *partial = base + L.partial;
+    uint8_t *mask = base + L.mask;
     int32_t *colmap = reinterpret_cast<int32_t *>(base + L.colmap);
     int32_t *O = reinterpret_cast<int32_t *>(base + L.outlier_idx);
     int32_t *n_out = reinterpret_cast<int32_t *>(base + L.n_outliers);
@@ -142,20 +150,14 @@ llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, in
     uint16_t *w_out = reinterpret_cast<uint16_t *>(base + L.w_out);
     float *d_part = reinterpret_cast<float *>(base + L.d_part);
 
-    if (launch_quantize_act(X, T, K, threshold, Xq, a, O, n_out, flags, colmap, x_out, stream) !=
-        hipSuccess)
+    // the GEMM path also needs the dequantized outlier weight rows
+    const GatherArgs g{CB, SCB, N, decode ? nullptr : w_out};
+    if (launch_quantize_act(X, T, K, threshold, Xq, a, O, n_out, partial, mask, colmap, x_out, g,
+                            stream) != hipSuccess)
         return LLMINT8_ERR_HIP;
     EpilogueArgs ep{a, SCB, x_out, w_out, O, n_out, bias, out, nullptr, d_part};
-    hipError_t e = hipSuccess;
-    if (!decode)
-        e = launch_gather_outlier_weights(CB, SCB, O, n_out, K, N, w_out, stream);
-    if (e == hipSuccess && main_start)
-        e = hipEventRecord(main_start, stream);
-    if (e == hipSuccess)
-        e = decode ? launch_decode(Xq, CB, T, K, N, ep, stream)
-                   : launch_gemm(Xq, CB, T, K, N, ep, stream);
-    if (e == hipSuccess && main_stop)
-        e = hipEventRecord(main_stop, stream);
+    const hipError_t e = decode ? launch_decode(Xq, CB, T, K, N, ep, stream, main_start, main_stop)
+                                : launch_gemm(Xq, CB, T, K, N, ep, stream, main_start, main_stop);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 

@@ -9,9 +9,9 @@ namespace llmint8 {
 using GemmMain = gemm::Cfg<256, 256, 2, 2, 4, 4>;
 
 hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
-                       const EpilogueArgs &ep, hipStream_t s)
+                       const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1)
 {
-    return gemm::launch<GemmMain>(Xq, CB, T, K, N, ep, s);
+    return gemm::launch<GemmMain>(Xq, CB, T, K, N, ep, s, ev0, ev1);
 }
 
 }  // namespace llmint8

@@ -40,6 +40,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRowBytes = 64;   // bytes of each operand row staged per pipeline stage
 constexpr int kXcds = 8;
+constexpr int kPersistentBlocks = 256;   // one per CU
 
 // Measured on gfx950: 16-lane groups of ds_read_b128 hit 64 banks; rows of
 // 64 bytes put rows r, r+4, r+8, r+12 on the same banks, which this spreads.
@@ -464,18 +465,13 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
 // outlier columns k_gemm has already finished the output and every block
 // returns at once.
 template <class C>
-__global__ __launch_bounds__(C::kThreads) void k_gemm_outliers(int64_t T, int64_t K, int64_t N,
-                                                               EpilogueArgs ep)
+__device__ __forceinline__ void outlier_tile(char *smem, int tile, int ntiles, int ntm, int ntn,
+                                             int64_t T, int64_t K, int64_t N, int nout,
+                                             const EpilogueArgs &ep, int wm, int wn, int wave,
+                                             int lane)
 {
-    const int nout = *ep.n_out;
-    if (nout <= kOutlierPad)
-        return;
-    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / C::WN, wn = wave % C::WN;
-    const int ntm = (int)((T + C::BM - 1) / C::BM), ntn = (int)((N + C::BN - 1) / C::BN);
     int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, ntm, ntn, C::GROUP, tm, tn);
+    tile_coords(tile, ntiles, ntm, ntn, C::GROUP, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
 
     v16f acc[C::FM][C::FN];
@@ -517,17 +513,50 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_outliers(int64_t T, int64_
 }
 
 template <class C>
+__global__ __launch_bounds__(C::kThreads) void k_gemm_outliers(int64_t T, int64_t K, int64_t N,
+                                                               EpilogueArgs ep)
+{
+    const int nout = *ep.n_out;
+    if (nout <= kOutlierPad)
+        return;
+    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int ntm = (int)((T + C::BM - 1) / C::BM), ntn = (int)((N + C::BN - 1) / C::BN);
+    // persistent blocks walk the tiles (the grid is small so that the common
+    // case, an early return, costs little)
+    for (int tile = blockIdx.x; tile < ntm * ntn; tile += gridDim.x) {
+        __builtin_amdgcn_s_barrier();   // the previous tile's LDS reads are done
+        outlier_tile<C>(smem, tile, ntm * ntn, ntm, ntn, T, K, N, nout, ep, wm, wn, wave, lane);
+    }
+}
+
+template <class C>
 hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
-                  const EpilogueArgs &ep, hipStream_t s)
+                  const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
+                  hipEvent_t ev1 = nullptr)
 {
     const int64_t ntm = (T + C::BM - 1) / C::BM, ntn = (N + C::BN - 1) / C::BN;
     const dim3 grid((unsigned)(ntm * ntn));
-    if (ep.c_i32) {
-        hipLaunchKernelGGL((k_gemm<C, true>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K, N, ep);
-        return hipGetLastError();
+    if (ev0) {
+        const hipError_t e = hipEventRecord(ev0, s);
+        if (e != hipSuccess)
+            return e;
     }
-    hipLaunchKernelGGL((k_gemm<C, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K, N, ep);
-    hipLaunchKernelGGL((k_gemm_outliers<C>), grid, dim3(C::kThreads), 0, s, T, K, N, ep);
+    if (ep.c_i32)
+        hipLaunchKernelGGL((k_gemm<C, true>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K, N, ep);
+    else
+        hipLaunchKernelGGL((k_gemm<C, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K, N, ep);
+    if (ev1) {
+        const hipError_t e = hipEventRecord(ev1, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    if (!ep.c_i32) {
+        const int64_t blocks = ntm * ntn < kPersistentBlocks ? ntm * ntn : kPersistentBlocks;
+        hipLaunchKernelGGL((k_gemm_outliers<C>), dim3((unsigned)blocks), dim3(C::kThreads), 0, s,
+                           T, K, N, ep);
+    }
     return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
 
 // Workspace segments of one llmint8_matmul call (byte offsets from the base).
 struct MatmulWorkspace {
-    size_t flags, colmap, outlier_idx, n_outliers, row_absmax, xq, x_out, w_out, d_part, total;
+    size_t partial, mask, colmap, outlier_idx, n_outliers, row_absmax, xq, x_out, w_out, d_part, total;
 };
 MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N);
 size_t act_workspace_bytes(int64_t K);
@@ -60,18 +60,29 @@ size_t act_workspace_bytes(int64_t K);
 hipError_t launch_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N, int8_t *CB,
                                   float *SCB, hipStream_t s);
 
-// Outlier detection + compaction + row quantization.  x_out (fp16 [T, ldo],
-// ldo = K) receives the gathered outlier columns when non-null.
+// What the row-quantization launch needs to also produce the dequantized
+// outlier weight rows for the GEMM: w_out[n, j] = fp16(CB[n,O[j]]*SCB[n]/127),
+// zero for n_outliers <= j < pad32(n_outliers), row stride K.  w_out == null
+// skips it.
+struct GatherArgs {
+    const int8_t *CB;
+    const float *SCB;
+    int64_t N;
+    uint16_t *w_out;
+};
+
+// Row splits k_detect uses for a [T,K] input (the partial-flag buffer holds
+// splits * K/8 bytes, at most kMaxDetectSplits * K/8).
+constexpr int kMaxDetectSplits = 64;
+int detect_row_splits(int64_t T, int64_t K);
+
+// Outlier detection + compaction + row quantization (+ the optional outlier
+// weight gather).  x_out (fp16 [T, K]) receives the gathered outlier columns
+// when non-null.
 hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
                                int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
-                               uint8_t *flags, int32_t *colmap, uint16_t *x_out,
-                               hipStream_t s);
-
-// Dequantized outlier weight rows: w_out[n, j] = fp16(CB[n,O[j]]*SCB[n]/127),
-// zero for n_outliers <= j < pad32(n_outliers); row stride ldo = K.
-hipError_t launch_gather_outlier_weights(const int8_t *CB, const float *SCB, const int32_t *O,
-                                         const int32_t *n_out, int64_t K, int64_t N,
-                                         uint16_t *w_out, hipStream_t s);
+                               uint8_t *partial, uint8_t *mask, int32_t *colmap,
+                               uint16_t *x_out, const GatherArgs &g, hipStream_t s);
 
 struct EpilogueArgs {
     const float *a;          // [T] row absmax
@@ -87,9 +98,12 @@ struct EpilogueArgs {
                              // used when more than 32 columns are outliers)
 };
 
+// ev0/ev1 (optional) are recorded on s right before and after the main kernel.
 hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
-                       const EpilogueArgs &ep, hipStream_t s);
+                       const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr);
 hipError_t launch_decode(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
-                         const EpilogueArgs &ep, hipStream_t s);
+                         const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
+                         hipEvent_t ev1 = nullptr);
 
 }  // namespace llmint8

@@ -77,91 +77,130 @@ __global__ __launch_bounds__(kBlock) void k_quantize_weight(const uint16_t *__re
 }
 
 // ---------------------------------------------------------------------------
-// Outlier-column detection.
+// Outlier-column detection, in two launches and without atomics or a
+// clearing pass: k_detect ORs "some |x| > threshold" over a range of rows
+// for 8 columns per lane and writes one bit per column for its row range
+// (every partial byte is written); k_compact ORs the row ranges together.
+// The comparison |x| > threshold is done on binary16 bit patterns against the
+// largest binary16 value not above the threshold (computed on the host), which
+// is the same test as comparing the exact values.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_clear_flags(uint32_t *flags32, int64_t words)
-{
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < words;
-         i += (int64_t)gridDim.x * kBlock)
-        flags32[i] = 0u;
-}
+constexpr int kDetectRowGroups = kBlock / 32; // row groups per block
 
-constexpr int kDetectRows = 32;   // rows per block; each wavefront takes every 4th
-
-// Block (x, y): columns [512x, 512x+512) (8 per lane), rows [32y, 32y+32).
-// A column's flag is set to 1 when some |x| in it exceeds the threshold; many
-// blocks may store the same 1, which is benign.
 __global__ __launch_bounds__(kBlock) void k_detect(const uint16_t *__restrict__ X, int64_t T,
-                                                   int64_t K, float threshold,
-                                                   uint8_t *__restrict__ flags)
+                                                   int64_t K, unsigned thr_bits, int rows_per,
+                                                   uint8_t *__restrict__ partial)
 {
-    const int lane = threadIdx.x % kWave;
-    const int wy = threadIdx.x / kWave;
-    const int64_t c8 = (int64_t)blockIdx.x * kWave + lane;   // 8-column chunk
-    if (c8 * 8 >= K)
-        return;
-    unsigned m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    // grid.y is capped, so row groups are taken in a grid-stride loop
-    for (int64_t t0 = (int64_t)blockIdx.y * kDetectRows; t0 < T;
-         t0 += (int64_t)gridDim.y * kDetectRows) {
-        const int64_t t1 = t0 + kDetectRows < T ? t0 + kDetectRows : T;
-        for (int64_t t = t0 + wy; t < t1; t += kWavesPerBlock) {
-            uint4 v = *reinterpret_cast<const uint4 *>(X + t * K + c8 * 8);
-            m[0] = umax(m[0], abs_lo(v.x));
-            m[1] = umax(m[1], abs_hi(v.x));
-            m[2] = umax(m[2], abs_lo(v.y));
-            m[3] = umax(m[3], abs_hi(v.y));
-            m[4] = umax(m[4], abs_lo(v.z));
-            m[5] = umax(m[5], abs_hi(v.z));
-            m[6] = umax(m[6], abs_lo(v.w));
-            m[7] = umax(m[7], abs_hi(v.w));
+    __shared__ uint8_t s_bits[kDetectRowGroups][32];
+    const int c = threadIdx.x & 31, rg = threadIdx.x >> 5;
+    const int64_t col8 = (int64_t)blockIdx.x * 32 + c;    // 8-column chunk
+    const int64_t nchunk = K / 8;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per;
+    const int64_t r1 = r0 + rows_per < T ? r0 + rows_per : T;
+    unsigned bits = 0;
+    if (col8 < nchunk) {
+        for (int64_t t = r0 + rg; t < r1; t += kDetectRowGroups) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(X + t * K + col8 * 8);
+            const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bits |= (abs_lo(w[i]) > thr_bits ? 1u : 0u) << (2 * i);
+                bits |= (abs_hi(w[i]) > thr_bits ? 1u : 0u) << (2 * i + 1);
+            }
         }
     }
+    s_bits[rg][c] = (uint8_t)bits;
+    __syncthreads();
+    if (rg == 0 && col8 < nchunk) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        if (h2f((uint16_t)m[i]) > threshold)
-            flags[c8 * 8 + i] = 1;
+        for (int g = 1; g < kDetectRowGroups; ++g)
+            bits |= s_bits[g][c];
+        partial[blockIdx.y * nchunk + col8] = (uint8_t)bits;
+    }
 }
 
 constexpr int kCompactThreads = 1024;
+constexpr int kMaxMaskWords = 133144 / 32 + 1;   // K/32 words of mask bits for the largest K
 
-// One block turns the flags into the ascending index list O, the count n and
-// the column -> position map (colmap[k] = j for k = O[j], -1 otherwise).
-__global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__restrict__ flags,
-                                                             int64_t K, int32_t *__restrict__ O,
+// One block.  First every thread loads a share of the row-range partials (8
+// bytes at a time, all independent) and ORs the nonzero ones into an LDS
+// bitmask; then mask[b] = OR over row ranges for 8-column chunk b, the
+// ascending outlier list O, its length n, and colmap[k] = position of k in O
+// (or -1).  Each thread owns a contiguous run of chunks so a block-wide
+// exclusive scan of the per-thread counts gives the positions.
+__global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__restrict__ partial,
+                                                             int splits, int64_t K,
+                                                             uint8_t *__restrict__ mask,
+                                                             int32_t *__restrict__ O,
                                                              int32_t *__restrict__ n_out,
                                                              int32_t *__restrict__ colmap)
 {
+    __shared__ unsigned s_mask[kMaxMaskWords];
     __shared__ int wave_tot[kCompactThreads / kWave];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int64_t per = (K + kCompactThreads - 1) / kCompactThreads;
-    const int64_t k0 = tid * per < K ? tid * per : K;
-    const int64_t k1 = k0 + per < K ? k0 + per : K;
+    // 32-bit indexing: K <= 133144 keeps every count here far below 2^31
+    const int nchunk = (int)(K / 8);         // mask bytes; a multiple of 8 since K % 64 == 0
+    const int nvec = nchunk / 8;             // 8-byte vectors per row range
+    const int nwords = nchunk / 4;
+    for (int w = tid; w < nwords; w += kCompactThreads)
+        s_mask[w] = 0u;
+    __syncthreads();
+    const int items = nvec * splits;
+    constexpr int kBatch = 8;   // independent loads in flight per thread
+    for (int base = tid; base < items; base += kBatch * kCompactThreads) {
+        uint2 x[kBatch];
+        int vv[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int it = base + u * kCompactThreads;
+            const int r = it / nvec;
+            vv[u] = it - r * nvec;
+            x[u] = it < items ? *reinterpret_cast<const uint2 *>(partial + r * nchunk + vv[u] * 8)
+                              : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (x[u].x)
+                atomicOr(&s_mask[2 * vv[u]], x[u].x);
+            if (x[u].y)
+                atomicOr(&s_mask[2 * vv[u] + 1], x[u].y);
+        }
+    }
+    __syncthreads();
+    const int per = (nchunk + kCompactThreads - 1) / kCompactThreads;
+    const int b0 = tid * per < nchunk ? tid * per : nchunk;
+    const int b1 = b0 + per < nchunk ? b0 + per : nchunk;
     int cnt = 0;
-    for (int64_t k = k0; k < k1; ++k)
-        cnt += flags[k] != 0;
-    // inclusive scan within the wavefront
+    for (int b = b0; b < b1; ++b) {
+        const unsigned m = (s_mask[b / 4] >> (8 * (b % 4))) & 0xffu;
+        mask[b] = (uint8_t)m;
+        cnt += __builtin_popcount(m);
+    }
     int inc = cnt;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
-        int o = __shfl_up(inc, off, kWave);
+        const int o = __shfl_up(inc, off, kWave);
         if (lane >= off)
             inc += o;
     }
     if (lane == kWave - 1)
         wave_tot[wave] = inc;
     __syncthreads();
-    int base = inc - cnt;
+    int j = inc - cnt;
     for (int w = 0; w < wave; ++w)
-        base += wave_tot[w];
-    int j = base;
-    for (int64_t k = k0; k < k1; ++k) {
-        if (flags[k]) {
-            O[j] = (int32_t)k;
-            colmap[k] = j;
-            ++j;
-        } else {
-            colmap[k] = -1;
+        j += wave_tot[w];
+    for (int b = b0; b < b1; ++b) {
+        const unsigned m = (s_mask[b / 4] >> (8 * (b % 4))) & 0xffu;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = b * 8 + i;
+            if ((m >> i) & 1u) {
+                O[j] = (int32_t)k;
+                colmap[k] = j;
+                ++j;
+            } else {
+                colmap[k] = -1;
+            }
         }
     }
     if (tid == kCompactThreads - 1)
@@ -169,85 +208,164 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__re
 }
 
 // ---------------------------------------------------------------------------
-// Row quantization: one wavefront per row t.  Pass 1 takes the absmax over
-// the non-outlier columns, pass 2 (re-reading the row from cache) writes the
-// int8 row with outlier columns as 0, and gathers the outlier values into the
-// compact fp16 row x_out[t, colmap[k]] padded with zeros to a multiple of 32.
+// Row quantization: one 256-thread block per row t (so that even a handful of
+// rows keeps many lanes busy).  The row is read once into registers (NC
+// 16-byte chunks per thread; NC = 0 re-reads it from cache for very long
+// rows), its absmax over the non-outlier columns is reduced with shuffles and
+// LDS, then the int8 row is packed with outlier columns as 0, and the outlier
+// values are gathered into the compact fp16 row x_out[t, colmap[k]],
+// zero-padded to a multiple of 32.  Chunks without outlier columns (nearly
+// all of them) take a branch-free path.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint2 quant8(uint4 v, float amax)
+{
+    // amax > 0 here; every value is a non-outlier
+    unsigned packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int q = quant127(h2f(half_at(v, i)), amax);
+        packed[i >> 2] |= ((unsigned)q & 0xffu) << (8 * (i & 3));
+    }
+    return make_uint2(packed[0], packed[1]);
+}
+
+__device__ __forceinline__ uint2 quant8_masked(uint4 v, unsigned fl, float amax, int64_t t,
+                                              int64_t K, int64_t c,
+                                              const int32_t *__restrict__ colmap,
+                                              uint16_t *__restrict__ x_out)
+{
+    unsigned packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint16_t h = half_at(v, i);
+        int q = 0;
+        if ((fl >> i) & 1u) {
+            if (x_out)
+                x_out[t * K + colmap[c * 8 + i]] = h;
+        } else if (amax > 0.0f) {
+            q = quant127(h2f(h), amax);
+        }
+        packed[i >> 2] |= ((unsigned)q & 0xffu) << (8 * (i & 3));
+    }
+    return make_uint2(packed[0], packed[1]);
+}
+
+__device__ __forceinline__ void quant_chunk(uint4 v, unsigned fl, float amax, int64_t t, int64_t K,
+                                           int64_t c, const int32_t *__restrict__ colmap,
+                                           uint16_t *__restrict__ x_out, uint2 *dst)
+{
+    if (fl == 0u && amax > 0.0f)
+        *dst = quant8(v, amax);
+    else
+        *dst = quant8_masked(v, fl, amax, t, K, c, colmap, x_out);
+}
+
+__device__ __forceinline__ unsigned chunk_absmax_masked(uint4 v, unsigned fl)
+{
+    if (fl == 0u)
+        return chunk_absmax(v);
+    unsigned m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (!((fl >> i) & 1u))
+            m = umax(m, half_at(v, i) & 0x7fffu);
+    return m;
+}
+
+template <int NC>
 __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict__ X, int64_t T,
-                                                     int64_t K, const uint8_t *__restrict__ flags,
+                                                     int64_t K, const uint8_t *__restrict__ mask,
                                                      const int32_t *__restrict__ colmap,
                                                      const int32_t *__restrict__ n_out,
                                                      int8_t *__restrict__ Xq,
                                                      float *__restrict__ a,
-                                                     uint16_t *__restrict__ x_out)
+                                                     uint16_t *__restrict__ x_out,
+                                                     const int8_t *__restrict__ CB,
+                                                     const float *__restrict__ SCB,
+                                                     const int32_t *__restrict__ O, int64_t N,
+                                                     uint16_t *__restrict__ w_out)
 {
-    const int lane = threadIdx.x % kWave;
-    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    if (t >= T)
+    __shared__ unsigned s_max[kWavesPerBlock];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    if ((int64_t)blockIdx.x >= T) {
+        // Extra blocks: dequantized outlier weight rows for the GEMM,
+        // w_out[r, j] = fp16(CB[r, O[j]] * SCB[r] / 127), zero up to a multiple of 32.
+        const int n = *n_out;
+        const int npad = (n + kOutlierPad - 1) / kOutlierPad * kOutlierPad;
+        const int64_t gb = (int64_t)blockIdx.x - T, nb = (int64_t)gridDim.x - T;
+        for (int64_t r = gb * kWavesPerBlock + wave; r < N; r += nb * kWavesPerBlock) {
+            const float sc = SCB[r];
+            for (int j = lane; j < npad; j += kWave)
+                w_out[r * K + j] = j < n ? dequant_w(CB[r * K + O[j]], sc) : (uint16_t)0;
+        }
         return;
+    }
+    const int64_t t = blockIdx.x;
     const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
-    const uint2 *fr = reinterpret_cast<const uint2 *>(flags);
+    uint2 *dst = reinterpret_cast<uint2 *>(Xq + t * K);
     const int64_t nchunk = K / 8;
     unsigned m = 0;
-    for (int64_t c = lane; c < nchunk; c += kWave) {
-        uint4 v = xr[c];
-        uint2 f = fr[c];
+    uint4 v[NC > 0 ? NC : 1];
+    unsigned fl[NC > 0 ? NC : 1];
+    if constexpr (NC > 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            unsigned fl = ((i < 4 ? f.x : f.y) >> (8 * (i & 3))) & 0xffu;
-            if (!fl)
-                m = umax(m, half_at(v, i) & 0x7fffu);
+        for (int i = 0; i < NC; ++i) {
+            const int64_t c = tid + (int64_t)i * kBlock;
+            v[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
+            fl[i] = c < nchunk ? mask[c] : 0u;
         }
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+            m = umax(m, chunk_absmax_masked(v[i], fl[i]));
+    } else {
+        for (int64_t c = tid; c < nchunk; c += kBlock)
+            m = umax(m, chunk_absmax_masked(xr[c], mask[c]));
     }
     m = wave_max_u32(m);
-    const float amax = h2f((uint16_t)m);
-    uint2 *dst = reinterpret_cast<uint2 *>(Xq + t * K);
-    for (int64_t c = lane; c < nchunk; c += kWave) {
-        uint4 v = xr[c];
-        uint2 f = fr[c];
-        unsigned packed[2] = {0u, 0u};
+    if (lane == 0)
+        s_max[wave] = m;
+    __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            unsigned fl = ((i < 4 ? f.x : f.y) >> (8 * (i & 3))) & 0xffu;
-            uint16_t h = half_at(v, i);
-            int q = 0;
-            if (fl) {
-                if (x_out)
-                    x_out[t * K + colmap[c * 8 + i]] = h;
-            } else if (amax > 0.0f) {
-                q = quant127(h2f(h), amax);
-            }
-            packed[i >> 2] |= ((unsigned)q & 0xffu) << (8 * (i & 3));
+    for (int w = 0; w < kWavesPerBlock; ++w)
+        m = umax(m, s_max[w]);
+    const float amax = h2f((uint16_t)m);
+    if constexpr (NC > 0) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int64_t c = tid + (int64_t)i * kBlock;
+            if (c < nchunk)
+                quant_chunk(v[i], fl[i], amax, t, K, c, colmap, x_out, dst + c);
         }
-        dst[c] = make_uint2(packed[0], packed[1]);
+    } else {
+        for (int64_t c = tid; c < nchunk; c += kBlock)
+            quant_chunk(xr[c], mask[c], amax, t, K, c, colmap, x_out, dst + c);
     }
     if (x_out) {
         const int n = *n_out;
         const int npad = (n + kOutlierPad - 1) / kOutlierPad * kOutlierPad;
-        for (int j = n + lane; j < npad; j += kWave)
+        for (int j = n + tid; j < npad; j += kBlock)
             x_out[t * K + j] = 0;
     }
-    if (lane == 0)
+    if (tid == 0)
         a[t] = amax;
 }
 
-// ---------------------------------------------------------------------------
-// Dequantized outlier weight rows for the GEMM epilogue.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_gather_outlier_weights(
-    const int8_t *__restrict__ CB, const float *__restrict__ SCB, const int32_t *__restrict__ O,
-    const int32_t *__restrict__ n_out, int64_t K, int64_t N, uint16_t *__restrict__ w_out)
+// Largest binary16 bit pattern whose value is <= thr (thr >= 0, not NaN);
+// 0x7c00 (inf) when thr >= 65504 so that no finite value exceeds it.
+unsigned threshold_bits(float thr)
 {
-    const int lane = threadIdx.x % kWave;
-    const int n = *n_out;
-    const int npad = (n + kOutlierPad - 1) / kOutlierPad * kOutlierPad;
-    for (int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; r < N;
-         r += (int64_t)gridDim.x * kWavesPerBlock) {
-        const float s = SCB[r];
-        for (int j = lane; j < npad; j += kWave)
-            w_out[r * K + j] = j < n ? dequant_w(CB[r * K + O[j]], s) : (uint16_t)0;
+    if (!(thr < 65504.0f))
+        return 0x7c00u;
+    unsigned lo = 0, hi = 0x7bffu;   // invariant: value(lo) <= thr
+    while (lo < hi) {
+        const unsigned mid = (lo + hi + 1) / 2;
+        _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)mid);
+        if ((float)h <= thr)
+            lo = mid;
+        else
+            hi = mid - 1;
     }
+    return lo;
 }
 
 }  // namespace
@@ -261,37 +379,54 @@ hipError_t launch_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N, int
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
-                               int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
-                               uint8_t *flags, int32_t *colmap, uint16_t *x_out,
-                               hipStream_t s)
+int detect_row_splits(int64_t T, int64_t K)
 {
-    const int64_t words = K / 4;
-    const int64_t clear_blocks = (words + kBlock - 1) / kBlock;
-    hipLaunchKernelGGL(k_clear_flags, dim3((unsigned)clear_blocks), dim3(kBlock), 0, s,
-                       reinterpret_cast<uint32_t *>(flags), words);
-    int64_t det_y = (T + kDetectRows - 1) / kDetectRows;
-    if (det_y > 65535)
-        det_y = 65535;
-    const dim3 det_grid((unsigned)((K / 8 + kWave - 1) / kWave), (unsigned)det_y);
-    hipLaunchKernelGGL(k_detect, det_grid, dim3(kBlock), 0, s, X, T, K, threshold, flags);
-    hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, flags, K, O, n_out,
-                       colmap);
-    const int64_t rq_blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(k_rowquant, dim3((unsigned)rq_blocks), dim3(kBlock), 0, s, X, T, K, flags,
-                       colmap, n_out, Xq, a, x_out);
-    return hipGetLastError();
+    const int64_t col_blocks = (K / 8 + 31) / 32;
+    int64_t r = (2048 + col_blocks - 1) / col_blocks;
+    const int64_t by_rows = (T + kDetectRowGroups - 1) / kDetectRowGroups;
+    if (r > by_rows)
+        r = by_rows;
+    if (r > kMaxDetectSplits)
+        r = kMaxDetectSplits;
+    return r < 1 ? 1 : (int)r;
 }
 
-hipError_t launch_gather_outlier_weights(const int8_t *CB, const float *SCB, const int32_t *O,
-                                         const int32_t *n_out, int64_t K, int64_t N,
-                                         uint16_t *w_out, hipStream_t s)
+hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                               int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
+                               uint8_t *partial, uint8_t *mask, int32_t *colmap,
+                               uint16_t *x_out, const GatherArgs &g, hipStream_t s)
 {
-    int64_t blocks = (N + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (blocks > 4096)
-        blocks = 4096;
-    hipLaunchKernelGGL(k_gather_outlier_weights, dim3((unsigned)blocks), dim3(kBlock), 0, s, CB,
-                       SCB, O, n_out, K, N, w_out);
+    const int splits = detect_row_splits(T, K);
+    const int rows_per = (int)((T + splits - 1) / splits);
+    const dim3 det_grid((unsigned)((K / 8 + 31) / 32), (unsigned)splits);
+    hipLaunchKernelGGL(k_detect, det_grid, dim3(kBlock), 0, s, X, T, K, threshold_bits(threshold),
+                       rows_per, partial);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, partial, splits, K, mask, O,
+                       n_out, colmap);
+    int64_t gather_blocks = 0;
+    if (g.w_out) {
+        gather_blocks = (g.N + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (gather_blocks > 2048)
+            gather_blocks = 2048;
+    }
+    const dim3 grid((unsigned)(T + gather_blocks));
+    const int64_t chunks_per_thread = (K / 8 + kBlock - 1) / kBlock;
+#define LLMINT8_ROWQUANT(NCV)                                                                   \
+    hipLaunchKernelGGL(k_rowquant<NCV>, grid, dim3(kBlock), 0, s, X, T, K, mask, colmap, n_out, \
+                       Xq, a, x_out, g.CB, g.SCB, O, g.N, g.w_out)
+    if (chunks_per_thread <= 1)
+        LLMINT8_ROWQUANT(1);
+    else if (chunks_per_thread <= 2)
+        LLMINT8_ROWQUANT(2);
+    else if (chunks_per_thread <= 4)
+        LLMINT8_ROWQUANT(4);
+    else if (chunks_per_thread <= 8)
+        LLMINT8_ROWQUANT(8);
+    else if (chunks_per_thread <= 16)
+        LLMINT8_ROWQUANT(16);
+    else
+        LLMINT8_ROWQUANT(0);
+#undef LLMINT8_ROWQUANT
     return hipGetLastError();
 }
 
