@@ -19,7 +19,7 @@ SOURCES = ["api.hip", "quant.hip", "gemm.hip", "decode.hip"]
 ARCH = os.environ.get("LLMINT8_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=" + ARCH,
+    "-O3", "-std=c++20", "-fPIC", "-shared", "--offload-arch=" + ARCH,
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function",

@@ -38,7 +38,7 @@ MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N)
     L.outlier_idx = off; off += align256(4 * k);
     L.n_outliers = off;  off += 256;
     L.row_absmax = off;  off += align256(4 * t);
-    L.xq = off;          off += align256(t * k);
+    L.xq = off;          off += align256((t > 16 ? t : 16) * k);   // decode: 16-row fragment order
     L.x_out = off;       off += align256(2 * t * k);
     L.w_out = off;       off += align256(2 * n * k);
     L.d_part = off;      off += align256(4 * t * n);
@@ -115,7 +115,8 @@ llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, int64_t K, f
     int32_t *colmap = reinterpret_cast<int32_t *>(mask + align256((size_t)K / 8));
     const GatherArgs none{nullptr, nullptr, 0, nullptr};
     hipError_t e = launch_quantize_act(X, T, K, threshold, Xq, row_absmax, outlier_idx,
-                                       n_outliers, partial, mask, colmap, nullptr, none, stream);
+                                       n_outliers, partial, mask, colmap, nullptr, none, false,
+                                       stream);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 
@@ -150,14 +151,17 @@ llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, in
     uint16_t *w_out = reinterpret_cast<uint16_t *>(base + L.w_out);
     float *d_part = reinterpret_cast<float *>(base + L.d_part);
 
-    // the GEMM path also needs the dequantized outlier weight rows
+    // the GEMM path also needs the dequantized outlier weight rows; the
+    // decode path takes more than a few activation rows in fragment order
     const GatherArgs g{CB, SCB, N, decode ? nullptr : w_out};
+    const bool packed = decode && T >= kDecodePackedMinT;
     if (launch_quantize_act(X, T, K, threshold, Xq, a, O, n_out, partial, mask, colmap, x_out, g,
-                            stream) != hipSuccess)
+                            packed, stream) != hipSuccess)
         return LLMINT8_ERR_HIP;
     EpilogueArgs ep{a, SCB, x_out, w_out, O, n_out, bias, out, nullptr, d_part};
-    const hipError_t e = decode ? launch_decode(Xq, CB, T, K, N, ep, stream, main_start, main_stop)
-                                : launch_gemm(Xq, CB, T, K, N, ep, stream, main_start, main_stop);
+    const hipError_t e =
+        decode ? launch_decode(Xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
+               : launch_gemm(Xq, CB, T, K, N, ep, stream, main_start, main_stop);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 
@@ -182,7 +186,7 @@ llmint8_status_t llmint8_igemm_i32(const int8_t *Xq, int64_t T, int64_t K, int64
         return LLMINT8_ERR_UNSUPPORTED_SHAPE;
     const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
     EpilogueArgs ep{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, C, nullptr};
-    hipError_t e = decode ? launch_decode(Xq, CB, T, K, N, ep, stream)
+    hipError_t e = decode ? launch_decode(Xq, CB, T, K, N, ep, false, stream)
                           : launch_gemm(Xq, CB, T, K, N, ep, stream);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }

@@ -4,14 +4,20 @@
 
 namespace llmint8 {
 
-// Each wavefront streams 16 weight rows, 1 KB of each per stage, through two
-// LDS stages; four wavefronts per block.
-using DecodeMain = decode::CfgLds<2, 1024, 4>;
+// Each wavefront streams 16 weight rows, 512 bytes of each per stage, with
+// three register buffers (two stages in flight); four wavefronts per block.
+// With more than a few activation rows the fragments come from the packed
+// layout (one contiguous KB per k-step instead of 16 row pieces).
+using DecodeRows = decode::CfgRs<512, 4, 3, false>;
+using DecodePacked = decode::CfgRs<512, 4, 3, true>;
 
 hipError_t launch_decode(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
-                         const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1)
+                         const EpilogueArgs &ep, bool xq_packed, hipStream_t s, hipEvent_t ev0,
+                         hipEvent_t ev1)
 {
-    return decode::launch_lds<DecodeMain>(Xq, CB, T, K, N, ep, s, ev0, ev1);
+    if (xq_packed)
+        return decode::launch_rs<DecodePacked>(Xq, CB, T, K, N, ep, s, ev0, ev1);
+    return decode::launch_rs<DecodeRows>(Xq, CB, T, K, N, ep, s, ev0, ev1);
 }
 
 }  // namespace llmint8

@@ -1,13 +1,25 @@
-// decode_kernel.h -- weight-streaming kernel for T <= 16 rows (the decode regime).
+// decode_kernel.h -- weight-streaming kernels for T <= 16 rows (the decode regime).
 //
 // With at most 16 activation rows the product is bound by reading CB once
 // from HBM (K*N bytes against at most 16*K*N*2 int8 ops), so there is no
-// output tiling to reuse.  Each wavefront owns 16*NT output columns and
-// streams their CB rows with 16-byte non-temporal loads, UNROLL 64-byte
-// k-steps in flight, feeding the 16x16x64 int8 MFMA with the zero-padded
-// activation rows as the other operand (one activation fragment serves NT
-// MFMAs).  The k order inside an MFMA is irrelevant for the exact integer sum
-// because both operands use the same lane -> k mapping.
+// output tiling to reuse: every wavefront owns 16 consecutive CB rows (16
+// output columns) and streams them once, feeding the 16x16x64 int8 MFMA with
+// the zero-padded activation rows as the other operand.  The k order inside
+// an MFMA is irrelevant for the exact integer sum because both operands use
+// the same lane -> k mapping.
+//
+// What decides the speed is the HBM access pattern.  A load instruction whose
+// 64 lanes fetch 16 bytes from 16 different rows scatters 64-byte requests
+// over 16 DRAM pages; here every load instruction fetches 1 KB contiguous
+// from one CB row.  The MFMA, however, needs the 16 rows spread across lanes,
+// so each stage is transposed through a wavefront-private LDS buffer.  Two
+// ways to fill it:
+//   k_decode_rs   16-byte register loads, double-buffered, then ds_write
+//   k_decode_lds  direct global->LDS loads (global_load_lds)
+// The 16-byte chunks of staged row r are XOR-swizzled by r, which makes both
+// the 1 KB writes and the fragment reads (16 rows, one chunk each) hit
+// distinct LDS banks.  Every wavefront synchronizes with nothing but its own
+// loads (s_waitcnt).
 //
 // The epilogue is the decomposition of the LLM.int8() summary
 // (kurtkim.github.io, sections "Vector-wise Quantization" and "The Core of
@@ -17,140 +29,14 @@
 // the bias, round once to fp16.
 #pragma once
 
+#include <utility>
+
 #include "internal.h"
 
 namespace llmint8 {
 namespace decode {
 namespace {   // internal linkage: nothing here is exported from the library
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-
-template <int NT_, int UNROLL_>
-struct Cfg {
-    static constexpr int NT = NT_, UNROLL = UNROLL_;
-    static constexpr int kCols = 16 * NT;   // output columns per wavefront
-};
-
-template <class C, bool kRawI32>
-__global__ __launch_bounds__(kThreads) void k_decode(const int8_t *__restrict__ A,
-                                                     const int8_t *__restrict__ B, int64_t T,
-                                                     int64_t K, int64_t N, EpilogueArgs ep)
-{
-    const int lane = threadIdx.x % kWave;
-    const int64_t n0 = ((int64_t)blockIdx.x * kWaves + threadIdx.x / kWave) * C::kCols;
-    if (n0 >= N)
-        return;
-    const int r = lane % 16, kb = (lane / 16) * 16;
-    const bool arow = r < T;
-    const int8_t *pa = A + (arow ? r : 0) * K + kb;
-    const int8_t *pb[C::NT];
-#pragma unroll
-    for (int j = 0; j < C::NT; ++j) {
-        int64_t row = n0 + j * 16 + r;
-        row = row < N ? row : N - 1;   // a partial last group (N % kCols) reads row N-1, stores masked
-        pb[j] = B + row * K + kb;
-    }
-    v4i acc[C::NT];
-#pragma unroll
-    for (int j = 0; j < C::NT; ++j)
-        acc[j] = v4i{0, 0, 0, 0};
-    const v4i zero = v4i{0, 0, 0, 0};
-    int64_t k = 0;
-    for (; k + 64 * C::UNROLL <= K; k += 64 * C::UNROLL) {
-        v4i b[C::UNROLL][C::NT], a[C::UNROLL];
-#pragma unroll
-        for (int u = 0; u < C::UNROLL; ++u)
-#pragma unroll
-            for (int j = 0; j < C::NT; ++j)
-                b[u][j] = __builtin_nontemporal_load(
-                    reinterpret_cast<const v4i *>(pb[j] + k + 64 * u));
-#pragma unroll
-        for (int u = 0; u < C::UNROLL; ++u)
-            a[u] = arow ? *reinterpret_cast<const v4i *>(pa + k + 64 * u) : zero;
-#pragma unroll
-        for (int u = 0; u < C::UNROLL; ++u)
-#pragma unroll
-            for (int j = 0; j < C::NT; ++j)
-                acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u][j], acc[j], 0, 0, 0);
-    }
-    for (; k < K; k += 64) {
-        const v4i a = arow ? *reinterpret_cast<const v4i *>(pa + k) : zero;
-#pragma unroll
-        for (int j = 0; j < C::NT; ++j) {
-            const v4i b = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(pb[j] + k));
-            acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[j], 0, 0, 0);
-        }
-    }
-
-    // 16x16 accumulator layout: lane holds column lane%16, rows 4*(lane/16) + q.
-#pragma unroll
-    for (int j = 0; j < C::NT; ++j) {
-        const int64_t n = n0 + j * 16 + lane % 16;
-        if (n >= N)
-            continue;
-        if constexpr (kRawI32) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t t = 4 * (lane / 16) + q;
-                if (t < T)
-                    ep.c_i32[t * N + n] = acc[j][q];
-            }
-        } else {
-            const float sn = ep.scb[n];
-            const float sn_d = sn * (1.0f / 16129.0f);
-            const int nout = *ep.n_out;
-            const float bias = ep.bias ? h2f(ep.bias[n]) : 0.0f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t t = 4 * (lane / 16) + q;
-                if (t >= T)
-                    continue;
-                float v = (float)acc[j][q] * (ep.a[t] * sn_d);
-                for (int o = 0; o < nout; ++o)
-                    v += h2f(ep.x_out[t * K + o]) * h2f(dequant_w(B[n * K + ep.O[o]], sn));
-                ep.out[t * N + n] = f2h(v + bias);
-            }
-        }
-    }
-}
-
-template <class C>
-hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
-                  const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
-                  hipEvent_t ev1 = nullptr)
-{
-    const int64_t blocks = (N + kWaves * C::kCols - 1) / (kWaves * C::kCols);
-    if (ev0) {
-        const hipError_t e = hipEventRecord(ev0, s);
-        if (e != hipSuccess)
-            return e;
-    }
-    if (ep.c_i32)
-        hipLaunchKernelGGL((k_decode<C, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, Xq,
-                           CB, T, K, N, ep);
-    else
-        hipLaunchKernelGGL((k_decode<C, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, Xq,
-                           CB, T, K, N, ep);
-    if (ev1) {
-        const hipError_t e = hipEventRecord(ev1, s);
-        if (e != hipSuccess)
-            return e;
-    }
-    return hipGetLastError();
-}
-
-
-// ---------------------------------------------------------------------------
-// LDS-staged variant.  A load instruction whose 64 lanes fetch 16 bytes of
-// 16 different rows turns into 64-byte requests scattered over 16 DRAM pages;
-// here every load instruction instead fetches 1 KB contiguous from one CB row
-// straight into LDS (global_load_lds), and the MFMA fragments are read back
-// from LDS.  Each wavefront stages only its own 16 rows (16 KB per stage), so
-// it synchronizes with nothing but its own loads (s_waitcnt).  The 16-byte
-// chunks of staged row r are XOR-swizzled by r, which makes the fragment
-// reads (16 rows, one chunk each) hit distinct LDS banks.
-// ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int n>
@@ -160,13 +46,292 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// ROWBYTES of each of a wavefront's 16 CB rows per stage, STAGES stages per
-// wavefront, WAVES wavefronts per block.
+constexpr int kPrefetchOutliers = 8;
+
+// Outlier weight bytes CB[n, O[j]] for the first kPrefetchOutliers outlier
+// columns, fetched before the weight stream so their latency is hidden.
+struct OutlierPrefetch {
+    int nout;
+    int8_t w[kPrefetchOutliers];
+};
+
+template <bool kRawI32>
+__device__ __forceinline__ OutlierPrefetch prefetch_outliers(const int8_t *B, int64_t n, int64_t K,
+                                                             const EpilogueArgs &ep)
+{
+    OutlierPrefetch p{};
+    if constexpr (!kRawI32) {
+        p.nout = *ep.n_out;
+        // unconditional loads (O holds K >= 64 entries; unused ones read column 0)
+#pragma unroll
+        for (int j = 0; j < kPrefetchOutliers; ++j) {
+            const int o = ep.O[j];
+            p.w[j] = B[n * K + (j < p.nout ? o : 0)];
+        }
+    }
+    return p;
+}
+
+// 16x16 accumulator layout: lane holds column n = n0 + lane%16 and rows
+// t = 4*(lane/16) + q.
+template <bool kRawI32>
+__device__ __forceinline__ void epilogue(const v4i acc, int lane, int64_t n, int64_t T, int64_t K,
+                                         int64_t N, const int8_t *B, const EpilogueArgs &ep,
+                                         const OutlierPrefetch &pre)
+{
+    const int t0 = 4 * (lane / 16);
+    if constexpr (kRawI32) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (t0 + q < T)
+                ep.c_i32[(t0 + q) * N + n] = acc[q];
+    } else {
+        const float sn = ep.scb[n];
+        const float sn_d = sn * (1.0f / 16129.0f);
+        const float bias = ep.bias ? h2f(ep.bias[n]) : 0.0f;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t t = t0 + q < T ? t0 + q : T - 1;
+            v[q] = (float)acc[q] * (ep.a[t] * sn_d);
+        }
+        // Outlier columns in ascending order, kPrefetchOutliers at a time.  All
+        // loads are unconditional so that none waits on its own: x_out rows
+        // are zero-padded to a multiple of 32 >= o0 + kPrefetchOutliers, and
+        // an unused slot gets weight 0.
+        for (int o0 = 0; o0 < pre.nout; o0 += kPrefetchOutliers) {
+            float w[kPrefetchOutliers];
+#pragma unroll
+            for (int j = 0; j < kPrefetchOutliers; ++j) {
+                int cb = pre.w[j];
+                if (o0 > 0) {
+                    const int o = o0 + j < pre.nout ? ep.O[o0 + j] : 0;
+                    cb = B[n * K + o];
+                }
+                w[j] = o0 + j < pre.nout ? h2f(dequant_w(cb, sn)) : 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t t = t0 + q < T ? t0 + q : T - 1;
+                const uint16_t *xo = ep.x_out + t * K + o0;
+#pragma unroll
+                for (int j = 0; j < kPrefetchOutliers; ++j)
+                    v[q] += h2f(xo[j]) * w[j];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (t0 + q < T)
+                ep.out[(t0 + q) * N + n] = f2h(v[q] + bias);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged: per stage a wavefront loads ROWB bytes of each of its 16
+// rows (16*ROWB/1024 load instructions of 1 KB, 1024/ROWB rows each) into one
+// of NB register buffers, writes the oldest buffer to its LDS stage and runs
+// the MFMAs from there, then refills that buffer with stage c+NB.  NB-1
+// stages stay in flight while one is consumed.  The activation fragments of
+// a stage are issued NB-1 stages ahead too (NB-1 fragment buffers), right
+// before the weights of the stage after it, so that one s_waitcnt per stage
+// covers both without waiting for anything newer.
+//
+// Addresses: a load's base (weight block + stage + its first row) is
+// wavefront-uniform and lives in scalar registers; each lane adds one fixed
+// 32-bit offset.  The last stage is shifted back to end exactly at K and the
+// k-steps it shares with the previous stage are left out of its MFMAs, so no
+// load ever needs a per-lane bound.  Stages past the end (issued while the last
+// ones are consumed) re-read the last stage's addresses and are never used:
+// every pass issues the same loads, which keeps the compiler's own s_waitcnt
+// placement exact.
+// ---------------------------------------------------------------------------
+template <int ROWB_, int WAVES_, int NB_ = 2, bool PACKED_A_ = false, int READ_GROUP_ = 8>
+struct CfgRs {
+    static constexpr int ROWB = ROWB_, WAVES = WAVES_, NB = NB_;
+    // activations packed as [K/64][4][16][16]: k-step, 16-byte chunk, row, byte
+    static constexpr bool kPackedA = PACKED_A_;
+    static constexpr int kThreads = 64 * WAVES;
+    static constexpr int kStage = 16 * ROWB;            // bytes per wavefront stage
+    static constexpr int kRowsPerLoad = 1024 / ROWB;    // rows one 1 KB load instruction covers
+    static constexpr int kLoads = 16 / kRowsPerLoad;    // load instructions per stage
+    static constexpr int kSteps = ROWB / 64;            // 16x16x64 MFMA k-steps per stage
+    static constexpr int kReadGroup = READ_GROUP_ < kSteps ? READ_GROUP_ : kSteps;
+    static constexpr int NA = NB - 1;                   // activation fragment buffers
+    static constexpr int kUnroll = NB * NA;             // lcm(NB, NB-1): buffer rotation period
+    // loads younger than stage c's weights and activations when it is consumed
+    static constexpr int kWait = (NB - 1) * kLoads + (NA - 1) * kSteps;
+    static constexpr int kLdsBytes = WAVES * kStage;
+    static_assert(NB >= 2 && NB <= 4, "register buffers");
+    static_assert(ROWB >= 64 && 1024 % ROWB == 0, "stage shape");
+    static_assert(kSteps % kReadGroup == 0, "read groups");
+    static_assert(kWait < 64, "vmcnt range");
+};
+
+template <class C, bool kRawI32>
+__global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restrict__ A,
+                                                           const int8_t *__restrict__ B,
+                                                           int64_t T, int64_t K, int64_t N,
+                                                           EpilogueArgs ep)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t n0 = ((int64_t)blockIdx.x * C::WAVES + wave) * 16;
+    if (n0 >= N)
+        return;   // whole wavefront: N is a multiple of 16
+    const OutlierPrefetch pre = prefetch_outliers<kRawI32>(B, n0 + lane % 16, K, ep);
+    char *wl = smem + wave * C::kStage;
+    const int8_t *bw = B + n0 * K;
+    const int r = lane % 16, g = lane / 16;
+    const int8_t *pa = A + (r < T ? r : T - 1) * K + 16 * g;
+    const int kk = (int)K;   // K <= 133144: every in-block offset fits 32 bits
+    const int nch = (kk + C::ROWB - 1) / C::ROWB;
+
+    // Piece m of a stage (one load instruction): lane l holds row
+    // m*kRowsPerLoad + lrow, bytes [lcol, lcol+16) of the stage's k range;
+    // in LDS, row i keeps its 16-byte chunk q at i*ROWB + 16*(q ^ (i & 15)).
+    const int lrow = (16 * lane) / C::ROWB, lcol = (16 * lane) % C::ROWB;
+    const int lane_off = lrow * kk + lcol;
+    auto lds_off = [&](int m) {
+        const int row = m * C::kRowsPerLoad + lrow;
+        return row * C::ROWB + 16 * ((lcol / 16) ^ (row & 15));
+    };
+    // first k of stage c: the last stage (and any past it) ends at K (K >= ROWB)
+    auto stage_k = [&](int c) { return min(c * C::ROWB, kk - C::ROWB); };
+
+    const v4i zero = v4i{0, 0, 0, 0};
+    auto load_b = [&](v4i(&R)[C::kLoads], int c) {
+        const int kc = stage_k(c);
+#pragma unroll
+        for (int m = 0; m < C::kLoads; ++m) {
+            const int8_t *sp = bw + (int64_t)(m * C::kRowsPerLoad) * K + kc;
+            R[m] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(sp + lane_off));
+        }
+    };
+    auto store_b = [&](const v4i(&R)[C::kLoads]) {
+#pragma unroll
+        for (int m = 0; m < C::kLoads; ++m)
+            *reinterpret_cast<v4i *>(wl + lds_off(m)) = R[m];
+    };
+    // Activation fragments: lane (r, g) holds row r, chunk g of each 64-byte
+    // k-step.  Rows r >= T read row T-1: an MFMA output row depends only on
+    // its own activation row, and rows >= T are never stored.  No value is
+    // masked after its load, so no load waits on its own.
+    auto load_a = [&](v4i(&a)[C::kSteps], int c) {
+        const int kc = stage_k(c);
+#pragma unroll
+        for (int s2 = 0; s2 < C::kSteps; ++s2) {
+            if constexpr (C::kPackedA)
+                a[s2] = *reinterpret_cast<const v4i *>(A + (kc + 64 * s2) * 16 + 16 * lane);
+            else
+                a[s2] = *reinterpret_cast<const v4i *>(pa + kc + 64 * s2);
+        }
+    };
+    v4i acc = v4i{0, 0, 0, 0};
+    // Fragment reads in groups of kReadGroup, each group issued before its
+    // MFMAs (each MFMA waits only for its own read).  The first `skip` bytes
+    // of the last stage were already summed by the previous stage: their
+    // k-steps (skip is a multiple of 64) are left out by a uniform test.
+    auto compute = [&](const v4i(&a)[C::kSteps], int skip) {
+        const char *src = wl + r * C::ROWB;
+#pragma unroll
+        for (int s0 = 0; s0 < C::kSteps; s0 += C::kReadGroup) {
+            v4i b[C::kReadGroup];
+#pragma unroll
+            for (int i = 0; i < C::kReadGroup; ++i)
+                b[i] = *reinterpret_cast<const v4i *>(src + (((4 * (s0 + i) + g) ^ r) * 16));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < C::kReadGroup; ++i)
+                if (64 * (s0 + i) >= skip)
+                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[s0 + i], b[i], acc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    v4i R[C::NB][C::kLoads];
+    v4i a[C::NA][C::kSteps];
+    if (nch == 1) {
+        // K <= ROWB: bytes past K come from column 0 of the row and are
+        // stored as zeros; activation addresses past K are clamped likewise
+#pragma unroll
+        for (int m = 0; m < C::kLoads; ++m) {
+            const int8_t *sp = bw + (int64_t)(m * C::kRowsPerLoad) * K;
+            R[0][m] = *reinterpret_cast<const v4i *>(sp + lrow * kk + (lcol < kk ? lcol : 0));
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < C::kSteps; ++s2) {
+            const int k = 64 * s2 < kk ? 64 * s2 : 0;
+            if constexpr (C::kPackedA)
+                a[0][s2] = *reinterpret_cast<const v4i *>(A + k * 16 + 16 * lane);
+            else
+                a[0][s2] = *reinterpret_cast<const v4i *>(pa + k);
+        }
+        wait_vm<0>();
+#pragma unroll
+        for (int m = 0; m < C::kLoads; ++m)
+            *reinterpret_cast<v4i *>(wl + lds_off(m)) = lcol < kk ? R[0][m] : zero;
+        compute(a[0], 0);
+    } else {
+        // Issue order, oldest first, when stage c is consumed:
+        //   R(c) a(c) R(c+1) a(c+1) ... R(c+NB-2) a(c+NB-2) R(c+NB-1)
+        // Step c waits for R(c) and a(c), stores and consumes them, then
+        // issues a(c+NB-1) into a(c)'s buffer and R(c+NB) into R(c)'s.
+        // The phases stay in this order (sched_barrier): hoisting the next
+        // loads above the LDS stores would need another set of registers.
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j) {
+            load_b(R[j], j);
+            if (j < C::NA)
+                load_a(a[j], j);
+        }
+        // step u of a rotation period (buffer indices are compile-time); only
+        // the final stage can overlap the one before it
+        auto step = [&]<int u, bool kLast>(std::integral_constant<int, u>,
+                                           std::bool_constant<kLast>, int cc) {
+            wait_vm<C::kWait>();
+            store_b(R[u % C::NB]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(a[u % C::NA], kLast ? cc * C::ROWB - stage_k(cc) : 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!kLast) {
+                load_a(a[u % C::NA], cc + C::NA);
+                load_b(R[u % C::NB], cc + C::NB);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto steps = [&]<int... U>(std::integer_sequence<int, U...>, int c0, auto last) {
+            constexpr int n = sizeof...(U);
+            (step(std::integral_constant<int, U>{},
+                  std::bool_constant<decltype(last)::value && U + 1 == n>{}, c0 + U),
+             ...);
+        };
+        // Whole rotation periods in a single-exit loop that leaves 1 to
+        // kUnroll stages, then those as one straight-line sequence picked by
+        // their count: every block is entered with the same loads in flight,
+        // which keeps the compiler's own s_waitcnt placement exact.
+        int c = 0;
+        for (; c + C::kUnroll < nch; c += C::kUnroll)
+            steps(std::make_integer_sequence<int, C::kUnroll>{}, c, std::false_type{});
+        const int rem = nch - c;
+        [&]<int... Q>(std::integer_sequence<int, Q...>) {
+            ((rem == Q + 1
+                  ? (steps(std::make_integer_sequence<int, Q + 1>{}, c, std::true_type{}), 0)
+                  : 0),
+             ...);
+        }(std::make_integer_sequence<int, C::kUnroll>{});
+    }
+    epilogue<kRawI32>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-staged with direct loads: ROWBYTES of each of a wavefront's 16 CB rows
+// per stage, STAGES stages per wavefront, WAVES wavefronts per block.
+// ---------------------------------------------------------------------------
 template <int STAGES_, int ROWBYTES_, int WAVES_>
 struct CfgLds {
     static constexpr int STAGES = STAGES_, ROWBYTES = ROWBYTES_, WAVES = WAVES_;
     static constexpr int kThreads = 64 * WAVES;
-    static constexpr int kCols = 16;
     static constexpr int kStageWave = 16 * ROWBYTES;
     static constexpr int kLoads = kStageWave / 1024;    // 1 KB load instructions per stage
     static constexpr int kSteps = ROWBYTES / 64;        // 16x16x64 MFMA k-steps per stage
@@ -186,6 +351,7 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_lds(const int8_t *__rest
     const int64_t n0 = ((int64_t)blockIdx.x * C::WAVES + wave) * 16;
     if (n0 >= N)
         return;   // whole wavefront: N is a multiple of 16
+    const OutlierPrefetch pre = prefetch_outliers<kRawI32>(B, n0 + lane % 16, K, ep);
     char *wl = smem + wave * C::STAGES * C::kStageWave;
     const int r = lane % 16, g = lane / 16;
     const bool arow = r < T;
@@ -243,37 +409,22 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_lds(const int8_t *__rest
             }
         }
     }
-
-    const int64_t n = n0 + lane % 16;
-    if constexpr (kRawI32) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t t = 4 * (lane / 16) + q;
-            if (t < T)
-                ep.c_i32[t * N + n] = acc[q];
-        }
-    } else {
-        const float sn = ep.scb[n];
-        const float sn_d = sn * (1.0f / 16129.0f);
-        const int nout = *ep.n_out;
-        const float bias = ep.bias ? h2f(ep.bias[n]) : 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t t = 4 * (lane / 16) + q;
-            if (t >= T)
-                continue;
-            float v = (float)acc[q] * (ep.a[t] * sn_d);
-            for (int o = 0; o < nout; ++o)
-                v += h2f(ep.x_out[t * K + o]) * h2f(dequant_w(B[n * K + ep.O[o]], sn));
-            ep.out[t * N + n] = f2h(v + bias);
-        }
-    }
+    epilogue<kRawI32>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
 }
 
-template <class C>
-hipError_t launch_lds(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
-                      const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
-                      hipEvent_t ev1 = nullptr)
+template <class C, bool R>
+struct RsKernel {
+    static constexpr auto fn = k_decode_rs<C, R>;
+};
+template <class C, bool R>
+struct LdsKernel {
+    static constexpr auto fn = k_decode_lds<C, R>;
+};
+
+// One block per C::WAVES * 16 output columns.
+template <class C, template <class, bool> class Kernel>
+hipError_t launch_kernel(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
+                         const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1)
 {
     const int64_t blocks = (N + C::WAVES * 16 - 1) / (C::WAVES * 16);
     if (ev0) {
@@ -282,10 +433,10 @@ hipError_t launch_lds(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, 
             return e;
     }
     if (ep.c_i32)
-        hipLaunchKernelGGL((k_decode_lds<C, true>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
-                           s, Xq, CB, T, K, N, ep);
+        hipLaunchKernelGGL((Kernel<C, true>::fn), dim3((unsigned)blocks), dim3(C::kThreads), 0, s,
+                           Xq, CB, T, K, N, ep);
     else
-        hipLaunchKernelGGL((k_decode_lds<C, false>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
+        hipLaunchKernelGGL((Kernel<C, false>::fn), dim3((unsigned)blocks), dim3(C::kThreads), 0,
                            s, Xq, CB, T, K, N, ep);
     if (ev1) {
         const hipError_t e = hipEventRecord(ev1, s);
@@ -293,6 +444,22 @@ hipError_t launch_lds(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, 
             return e;
     }
     return hipGetLastError();
+}
+
+template <class C>
+hipError_t launch_rs(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
+                     const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
+                     hipEvent_t ev1 = nullptr)
+{
+    return launch_kernel<C, RsKernel>(Xq, CB, T, K, N, ep, s, ev0, ev1);
+}
+
+template <class C>
+hipError_t launch_lds(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
+                      const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
+                      hipEvent_t ev1 = nullptr)
+{
+    return launch_kernel<C, LdsKernel>(Xq, CB, T, K, N, ep, s, ev0, ev1);
 }
 
 }  // namespace

@@ -78,11 +78,14 @@ int detect_row_splits(int64_t T, int64_t K);
 
 // Outlier detection + compaction + row quantization (+ the optional outlier
 // weight gather).  x_out (fp16 [T, K]) receives the gathered outlier columns
-// when non-null.
+// when non-null.  xq_packed (T <= 16 only) writes Xq in the decode kernel's
+// fragment order [K/64][4][16][16] (16*K bytes; rows >= T are left as they
+// are) instead of row-major [T, K].
 hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
                                int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
                                uint8_t *partial, uint8_t *mask, int32_t *colmap,
-                               uint16_t *x_out, const GatherArgs &g, hipStream_t s);
+                               uint16_t *x_out, const GatherArgs &g, bool xq_packed,
+                               hipStream_t s);
 
 struct EpilogueArgs {
     const float *a;          // [T] row absmax
@@ -102,8 +105,11 @@ struct EpilogueArgs {
 hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
                        const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr);
+// Activation rows above which the decode path takes Xq in fragment order.
+constexpr int64_t kDecodePackedMinT = 9;
+// xq_packed: Xq is in the fragment order written by launch_quantize_act.
 hipError_t launch_decode(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
-                         const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
-                         hipEvent_t ev1 = nullptr);
+                         const EpilogueArgs &ep, bool xq_packed, hipStream_t s,
+                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 }  // namespace llmint8

@@ -272,6 +272,17 @@ __device__ __forceinline__ unsigned chunk_absmax_masked(uint4 v, unsigned fl)
     return m;
 }
 
+// Destination of the 8 int8 values k = 8c .. 8c+7 of row t.  Row-major
+// [T, K], or (decode path, T <= 16) the MFMA fragment order
+// [K/64][4][16][16]: 64-byte k-step, 16-byte chunk, row, byte.
+__device__ __forceinline__ uint2 *xq_chunk(int8_t *Xq, int64_t t, int64_t K, int64_t c,
+                                           bool packed)
+{
+    const int64_t off =
+        packed ? (c / 8) * 1024 + ((c % 8) / 2) * 256 + t * 16 + (c % 2) * 8 : t * K + 8 * c;
+    return reinterpret_cast<uint2 *>(Xq + off);
+}
+
 template <int NC>
 __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict__ X, int64_t T,
                                                      int64_t K, const uint8_t *__restrict__ mask,
@@ -283,7 +294,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
                                                      const int8_t *__restrict__ CB,
                                                      const float *__restrict__ SCB,
                                                      const int32_t *__restrict__ O, int64_t N,
-                                                     uint16_t *__restrict__ w_out)
+                                                     uint16_t *__restrict__ w_out, bool packed)
 {
     __shared__ unsigned s_max[kWavesPerBlock];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -302,7 +313,6 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     }
     const int64_t t = blockIdx.x;
     const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
-    uint2 *dst = reinterpret_cast<uint2 *>(Xq + t * K);
     const int64_t nchunk = K / 8;
     unsigned m = 0;
     uint4 v[NC > 0 ? NC : 1];
@@ -334,11 +344,13 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
         for (int i = 0; i < NC; ++i) {
             const int64_t c = tid + (int64_t)i * kBlock;
             if (c < nchunk)
-                quant_chunk(v[i], fl[i], amax, t, K, c, colmap, x_out, dst + c);
+                quant_chunk(v[i], fl[i], amax, t, K, c, colmap, x_out,
+                            xq_chunk(Xq, t, K, c, packed));
         }
     } else {
         for (int64_t c = tid; c < nchunk; c += kBlock)
-            quant_chunk(xr[c], mask[c], amax, t, K, c, colmap, x_out, dst + c);
+            quant_chunk(xr[c], mask[c], amax, t, K, c, colmap, x_out,
+                        xq_chunk(Xq, t, K, c, packed));
     }
     if (x_out) {
         const int n = *n_out;
@@ -394,7 +406,8 @@ int detect_row_splits(int64_t T, int64_t K)
 hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
                                int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
                                uint8_t *partial, uint8_t *mask, int32_t *colmap,
-                               uint16_t *x_out, const GatherArgs &g, hipStream_t s)
+                               uint16_t *x_out, const GatherArgs &g, bool xq_packed,
+                               hipStream_t s)
 {
     const int splits = detect_row_splits(T, K);
     const int rows_per = (int)((T + splits - 1) / splits);
@@ -413,7 +426,7 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
     const int64_t chunks_per_thread = (K / 8 + kBlock - 1) / kBlock;
 #define LLMINT8_ROWQUANT(NCV)                                                                   \
     hipLaunchKernelGGL(k_rowquant<NCV>, grid, dim3(kBlock), 0, s, X, T, K, mask, colmap, n_out, \
-                       Xq, a, x_out, g.CB, g.SCB, O, g.N, g.w_out)
+                       Xq, a, x_out, g.CB, g.SCB, O, g.N, g.w_out, xq_packed)
     if (chunks_per_thread <= 1)
         LLMINT8_ROWQUANT(1);
     else if (chunks_per_thread <= 2)

@@ -96,6 +96,32 @@ def test_matmul_parity(T, K, N, thr, use_bias):
         assert_fp16_close(d2h(out), ref, "out path=%d" % p)
 
 
+# K values for the weight-streaming kernel (512 bytes of each weight row per
+# stage, rotation period 6): one stage shorter than, equal to and just over a
+# stage; every remainder length 1..6 after whole periods; a partial last
+# stage overlapping the one before it.
+DECODE_K = [64, 448, 512, 576, 1024, 1536, 2048, 2560, 3072, 3584, 4160, 6656]
+
+
+@pytest.mark.parametrize("T", [1, 8, 9, 16])
+@pytest.mark.parametrize("K", DECODE_K)
+def test_decode_path_shapes(T, K):
+    """Weight-streaming path across its stage counts; T = 8/9 crosses from
+    row-major to fragment-ordered activations."""
+    N = 192
+    say("decode shapes T=%d K=%d N=%d" % (T, K, N))
+    X, W_t, _ = workloads.case(T, K, N, n_dims=min(6, K // 16), lo=8, hi=60, p=0.5, seed=K + T)
+    CBr, SCBr = oracle.quantize_weight(W_t)
+    ref, _, _ = oracle.matmul(X, CBr, SCBr, 6.0)
+    CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
+    out = L.llmint8_matmul_path(h2d(X), CB, SCB, 6.0, path=L.PATH_DECODE)
+    assert_fp16_close(d2h(out), ref, "out")
+    rng = np.random.default_rng(K * 17 + T)
+    A = rng.integers(-127, 128, (T, K)).astype(np.int8)
+    C = L.llmint8_igemm_i32(h2d(A), CB, path=L.PATH_DECODE)
+    assert_equal_exact(d2h(C), oracle.int_gemm(A, CBr), "C")
+
+
 def test_matmul_entry_point_matches_path_auto():
     X, W_t, _ = workloads.case(200, 256, 192, n_dims=3, seed=3)
     CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
