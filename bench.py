@@ -37,7 +37,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def profiled_traffic(summary):
+def profiled_traffic(summary, key="traffic_bytes_per_launch"):
     """HBM bytes per launch from a committed rocprofv3 counter summary in profiles/.
 
     The summary records a hash of the kernel's sources; when the sources have
@@ -59,7 +59,7 @@ def profiled_traffic(summary):
             h.update(open(os.path.join(ROOT, f), "rb").read())
         if h.hexdigest()[:16] != want:
             return None
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields[key])
     except (KeyError, ValueError, OSError):
         return None
 
@@ -148,7 +148,8 @@ def decode_bench(torch, L, workloads, steps, warmup, ev, dev):
                           "step_GBs": round(alg / (ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(alg / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "alg_bytes": alg,
-                          "traffic": profiled_traffic("k_decode_175b_fc1.txt")}
+                          "traffic": profiled_traffic("k_decode_175b_fc1.txt",
+                                                      "traffic_bytes_per_launch_T%d" % T)}
         log("decode T=%d: kernel %.1f us (%.0f GB/s), step %.1f us" % (T, kms * 1e3, alg / kms / 1e6, ms * 1e3))
     return res
 
