@@ -99,6 +99,7 @@ __device__ __forceinline__ void epilogue(const v4i acc, int lane, int64_t n, int
         // loads are unconditional so that none waits on its own: x_out rows
         // are zero-padded to a multiple of 32 >= o0 + kPrefetchOutliers, and
         // an unused slot gets weight 0.
+        const int64_t ldo = outlier_ld(pre.nout);
         for (int o0 = 0; o0 < pre.nout; o0 += kPrefetchOutliers) {
             float w[kPrefetchOutliers];
 #pragma unroll
@@ -113,7 +114,7 @@ __device__ __forceinline__ void epilogue(const v4i acc, int lane, int64_t n, int
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int64_t t = t0 + q < T ? t0 + q : T - 1;
-                const uint16_t *xo = ep.x_out + t * K + o0;
+                const uint16_t *xo = ep.x_out + t * ldo + o0;
 #pragma unroll
                 for (int j = 0; j < kPrefetchOutliers; ++j)
                     v[q] += h2f(xo[j]) * w[j];

@@ -1,17 +1,23 @@
-// gemm.hip -- instantiation of the tiled int8 MFMA GEMM (gemm_kernel.h) used
+// gemm.hip -- instantiations of the tiled int8 MFMA GEMM (gemm_kernel.h) used
 // by llmint8_matmul for T > 16 and by llmint8_igemm_i32.
 #include "gemm_kernel.h"
 
 namespace llmint8 {
 
-// 256 x 256 block tile, 2 x 2 wavefronts of 128 x 128, 4-stage LDS ring
-// (4 x 32 KB), groups of 4 tile rows.
-using GemmMain = gemm::Cfg<256, 256, 2, 2, 4, 4>;
+// 256 x 256 block tile, 2 x 2 wavefronts of 128 x 128, groups of 4 tile
+// rows.  With K a multiple of 128 the ring holds two stages of 128 bytes per
+// row (every load instruction then fetches whole 128-byte lines), otherwise
+// four stages of 64 bytes; 128 KB of LDS either way.  The fp16 pass over
+// more than 32 outlier columns always takes 64-byte stages.
+using Gemm128 = gemm::Cfg<256, 256, 2, 2, 2, 4, 128>;
+using Gemm64 = gemm::Cfg<256, 256, 2, 2, 4, 4, 64>;
 
 hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
                        const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1)
 {
-    return gemm::launch<GemmMain>(Xq, CB, T, K, N, ep, s, ev0, ev1);
+    if (K % Gemm128::ROWB == 0)
+        return gemm::launch<Gemm128, Gemm64>(Xq, CB, T, K, N, ep, s, ev0, ev1);
+    return gemm::launch<Gemm64, Gemm64>(Xq, CB, T, K, N, ep, s, ev0, ev1);
 }
 
 }  // namespace llmint8

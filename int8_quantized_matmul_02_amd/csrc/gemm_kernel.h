@@ -38,28 +38,38 @@ namespace {   // internal linkage: nothing here is exported from the library
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kRowBytes = 64;   // bytes of each operand row staged per pipeline stage
 constexpr int kXcds = 8;
 constexpr int kPersistentBlocks = 256;   // one per CU
 
-// Measured on gfx950: 16-lane groups of ds_read_b128 hit 64 banks; rows of
-// 64 bytes put rows r, r+4, r+8, r+12 on the same banks, which this spreads.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
-
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int GROUP_>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int GROUP_, int ROWB_ = 64>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_, GROUP = GROUP_;
+    static constexpr int ROWB = ROWB_;                  // bytes of each operand row per stage
+    static constexpr int kKSteps = ROWB / 32;           // 32-deep MFMA k-steps per stage
+    static constexpr int kChunks = ROWB / 16;           // 16-byte chunks per staged row
+    static constexpr int kRowsPerInstr = 1024 / ROWB;   // rows one 1 KB load instruction fills
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = kWaves * 64;
     static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
-    static constexpr int kAInstr = BM / 16 / kWaves;   // 1 KB load instructions per wave per stage
-    static constexpr int kBInstr = BN / 16 / kWaves;
+    static constexpr int kAInstr = BM / kRowsPerInstr / kWaves;   // load instructions per wave per stage
+    static constexpr int kBInstr = BN / kRowsPerInstr / kWaves;
     static constexpr int kLoads = kAInstr + kBInstr;
-    static constexpr int kStageBytes = (BM + BN) * kRowBytes;
+    static constexpr int kStageBytes = (BM + BN) * ROWB;
     static constexpr int kLdsBytes = STAGES * kStageBytes;
-    static_assert(BM % (16 * kWaves) == 0 && BN % (16 * kWaves) == 0, "load split");
+    static_assert(ROWB == 64 || ROWB == 128, "stage depth");
+    static_assert(BM % (kRowsPerInstr * kWaves) == 0 && BN % (kRowsPerInstr * kWaves) == 0,
+                  "load split");
     static_assert(FM >= 1 && FN >= 1, "wave tile");
     static_assert(STAGES >= 2, "pipeline depth");
+    static_assert((STAGES - 1) * kLoads < 64, "vmcnt range");
+
+    // Slot swizzle of staged row r, measured on gfx950: 16-lane groups of
+    // ds_read_b128 cover all 64 banks.  64-byte rows put rows r, r+4, r+8,
+    // r+12 on the same banks, 128-byte rows put every other row there.
+    __device__ __forceinline__ static int swz(int r)
+    {
+        return ROWB == 64 ? (r >> 2) & 3 : (r >> 1) & 7;
+    }
 };
 
 // s_waitcnt vmcnt(n) with expcnt/lgkmcnt left alone (gfx9 encoding).
@@ -98,17 +108,20 @@ struct Streams {
     {
         a = abase + m0 * lda;
         b = bbase + n0 * ldb;
+        // lane l fills LDS bytes [16l, 16l+16) of its instruction's KB: row
+        // l / kChunks, slot l % kChunks, which holds chunk slot ^ swz(row)
+        const int lr = lane / C::kChunks, ls = lane % C::kChunks;
 #pragma unroll
         for (int j = 0; j < C::kAInstr; ++j) {
-            const int r = (wave * C::kAInstr + j) * 16 + lane / 4;
+            const int r = (wave * C::kAInstr + j) * C::kRowsPerInstr + lr;
             const int64_t row = m0 + r < mrows ? r : mrows - 1 - m0;   // ragged: clamp
-            offA[j] = (uint32_t)(row * lda + (((lane & 3) ^ swz(r)) << 4));
+            offA[j] = (uint32_t)(row * lda + ((ls ^ C::swz(r)) << 4));
         }
 #pragma unroll
         for (int j = 0; j < C::kBInstr; ++j) {
-            const int r = (wave * C::kBInstr + j) * 16 + lane / 4;
+            const int r = (wave * C::kBInstr + j) * C::kRowsPerInstr + lr;
             const int64_t row = n0 + r < nrows ? r : nrows - 1 - n0;
-            offB[j] = (uint32_t)(row * ldb + (((lane & 3) ^ swz(r)) << 4));
+            offB[j] = (uint32_t)(row * ldb + ((ls ^ C::swz(r)) << 4));
         }
     }
 
@@ -117,32 +130,22 @@ struct Streams {
                                               int j) const
     {
         char *sa = smem + stage * C::kStageBytes;
-        char *sb = sa + C::BM * kRowBytes;
+        char *sb = sa + C::BM * C::ROWB;
         if (j < C::kAInstr)
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(a + kbyte + offA[j]),
-                (lds_void *)(sa + (wave * C::kAInstr + j) * 16 * kRowBytes), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(a + kbyte + offA[j]),
+                                             (lds_void *)(sa + (wave * C::kAInstr + j) * 1024), 16,
+                                             0, 0);
         else
             __builtin_amdgcn_global_load_lds(
                 (const void *)(b + kbyte + offB[j - C::kAInstr]),
-                (lds_void *)(sb + (wave * C::kBInstr + j - C::kAInstr) * 16 * kRowBytes), 16,
-                0, 0);
+                (lds_void *)(sb + (wave * C::kBInstr + j - C::kAInstr) * 1024), 16, 0, 0);
     }
 
     __device__ __forceinline__ void issue(char *smem, int stage, int64_t kbyte, int wave) const
     {
-        char *sa = smem + stage * C::kStageBytes;
-        char *sb = sa + C::BM * kRowBytes;
 #pragma unroll
-        for (int j = 0; j < C::kAInstr; ++j)
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(a + kbyte + offA[j]),
-                (lds_void *)(sa + (wave * C::kAInstr + j) * 16 * kRowBytes), 16, 0, 0);
-#pragma unroll
-        for (int j = 0; j < C::kBInstr; ++j)
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(b + kbyte + offB[j]),
-                (lds_void *)(sb + (wave * C::kBInstr + j) * 16 * kRowBytes), 16, 0, 0);
+        for (int j = 0; j < C::kLoads; ++j)
+            issue_one(smem, stage, kbyte, wave, j);
     }
 };
 
@@ -178,10 +181,10 @@ __device__ __forceinline__ void read_frags(Frags<C> &f, const char *sa, const ch
 {
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
-        f.a[i] = *reinterpret_cast<const v4i *>(sa + i * 32 * kRowBytes + fo);
+        f.a[i] = *reinterpret_cast<const v4i *>(sa + i * 32 * C::ROWB + fo);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
-        f.b[j] = *reinterpret_cast<const v4i *>(sb + j * 32 * kRowBytes + fo);
+        f.b[j] = *reinterpret_cast<const v4i *>(sb + j * 32 * C::ROWB + fo);
 }
 
 template <class C, class M>
@@ -194,13 +197,18 @@ __device__ __forceinline__ void mfmas(const Frags<C> &f, typename M::acc_t (&acc
             acc[i][j] = M::op(f.a[i], f.b[j], acc[i][j]);
 }
 
+// The g-th fragment read of a k-step, in the order the MFMAs (row-major over
+// (i, j)) first need them: a0, b0 .. b(FN-1), a1 .. a(FM-1).  The last read
+// then has FN*(FM-1) MFMAs of the next k-step to land.
 template <class C>
 __device__ __forceinline__ void read_one(Frags<C> &f, const char *sa, const char *sb, int fo, int g)
 {
-    if (g < C::FM)
-        f.a[g] = *reinterpret_cast<const v4i *>(sa + g * 32 * kRowBytes + fo);
+    if (g == 0)
+        f.a[0] = *reinterpret_cast<const v4i *>(sa + fo);
+    else if (g <= C::FN)
+        f.b[g - 1] = *reinterpret_cast<const v4i *>(sb + (g - 1) * 32 * C::ROWB + fo);
     else
-        f.b[g - C::FM] = *reinterpret_cast<const v4i *>(sb + (g - C::FM) * 32 * kRowBytes + fo);
+        f.a[g - C::FN] = *reinterpret_cast<const v4i *>(sa + (g - C::FN) * 32 * C::ROWB + fo);
 }
 
 // One half-stage in a fixed issue order: groups of (one global->LDS load,
@@ -241,53 +249,69 @@ struct MfmaF16F {
     }
 };
 
-// Runs numK stages (64 bytes of K = two 32-deep k-steps each) of the
-// pipelined main loop.  Stage s is loaded into LDS buffer s % STAGES.  Every
-// trip loads exactly one stage (stages past the end reload the last one into
-// a buffer nobody reads), so the number of loads in flight at each wait is a
-// constant and the loop body has no branches for the scheduler to stop at.
-// The barrier sits between the two k-steps of a stage, so the MFMAs issued
-// before it keep the matrix cores busy while the wavefronts synchronize.
+// Runs numK stages (ROWB bytes of K = ROWB/32 32-deep k-steps each) of the
+// pipelined main loop.  Stage s is loaded into LDS buffer s % STAGES.  A
+// buffer is free once every wavefront has read its stage's last k-step,
+// which the barrier before the stage's last k-step of MFMAs establishes; the
+// stage STAGES ahead is issued into it right there, so all STAGES buffers
+// are busy and a stage's loads have STAGES-1 trips to land.  Every trip
+// loads exactly one stage (stages past the end reload the last one into a
+// buffer nobody reads again), so the number of loads in flight at each wait
+// is a constant and the loop body has no branches for the scheduler to stop
+// at.  The barrier sits before the last k-step of a stage, so the MFMAs
+// issued before it keep the matrix cores busy while the wavefronts meet.
+// Fragments of the next k-step are read from LDS under the current one's
+// MFMAs.
 template <class C, class M>
 __device__ __forceinline__ void mainloop(char *smem, const Streams<C> &st, int numK,
                                          typename M::acc_t (&acc)[C::FM][C::FN], int wm, int wn,
                                          int wave, int lane)
 {
-    static_assert(C::STAGES >= 3, "mid-stage barrier needs at least 3 stages");
-    // fragment read offsets: row (lane&31) of each 32-row tile, chunk 2s + lane/32
-    const int frow = (lane & 31) * kRowBytes;
-    const int fo0 = frow + ((((lane >> 5)) ^ swz(lane & 31)) << 4);
-    const int fo1 = frow + (((2 + (lane >> 5)) ^ swz(lane & 31)) << 4);
-    const int aoff = wm * (C::BM / C::WM) * kRowBytes;
-    const int boff = C::BM * kRowBytes + wn * (C::BN / C::WN) * kRowBytes;
-    const int64_t klast = (int64_t)(numK - 1) * kRowBytes;
+    // fragment read offsets: row (lane&31) of each 32-row tile, chunk
+    // 2s + lane/32 for k-step s of the stage
+    const int frow = (lane & 31) * C::ROWB;
+    int fo[C::kKSteps];
+#pragma unroll
+    for (int s = 0; s < C::kKSteps; ++s)
+        fo[s] = frow + (((2 * s + (lane >> 5)) ^ C::swz(lane & 31)) << 4);
+    const int aoff = wm * (C::BM / C::WM) * C::ROWB;
+    const int boff = C::BM * C::ROWB + wn * (C::BN / C::WN) * C::ROWB;
+    const int64_t klast = (int64_t)(numK - 1) * C::ROWB;
     auto kb = [&](int s) -> int64_t {
-        const int64_t k = (int64_t)s * kRowBytes;
+        const int64_t k = (int64_t)s * C::ROWB;
         return k < klast ? k : klast;
     };
+    auto stage_a = [&](int s) { return smem + (s % C::STAGES) * C::kStageBytes + aoff; };
+    auto stage_b = [&](int s) { return smem + (s % C::STAGES) * C::kStageBytes + boff; };
 
 #pragma unroll
-    for (int s = 0; s < C::STAGES - 1; ++s)
+    for (int s = 0; s < C::STAGES; ++s)
         st.issue(smem, s, kb(s), wave);
-    wait_vm<(C::STAGES - 2) * C::kLoads>();   // stage 0 landed
+    wait_vm<(C::STAGES - 1) * C::kLoads>();   // stage 0 landed
     __builtin_amdgcn_s_barrier();
 
     Frags<C> f0, f1;
-    read_frags<C>(f0, smem + aoff, smem + boff, fo0);
+    read_frags<C>(f0, stage_a(0), stage_b(0), fo[0]);
     for (int kt = 0; kt < numK; ++kt) {
-        const char *sa = smem + (kt % C::STAGES) * C::kStageBytes + aoff;
-        const char *sb = smem + (kt % C::STAGES) * C::kStageBytes + boff;
-        // first half: reads of k-step 1 under the MFMAs of k-step 0
-        half_stage<C, M, false>(f0, f1, sa, sb, fo1, acc, st, smem, 0, 0, wave);
-        wait_vm<(C::STAGES - 3) * C::kLoads>();   // stage kt+1 landed
-        __builtin_amdgcn_s_barrier();
-        // second half: every wavefront is past stage kt-1, so refill its buffer,
-        // and read the next stage's k-step 0, under k-step 1's MFMAs
-        const int nk = kt + 1 < numK ? kt + 1 : kt;
-        half_stage<C, M, true>(f1, f0, smem + (nk % C::STAGES) * C::kStageBytes + aoff,
-                               smem + (nk % C::STAGES) * C::kStageBytes + boff, fo0, acc, st,
-                               smem, (kt + C::STAGES - 1) % C::STAGES, kb(kt + C::STAGES - 1),
-                               wave);
+#pragma unroll
+        for (int s = 0; s < C::kKSteps; ++s) {
+            Frags<C> &cur = s % 2 == 0 ? f0 : f1;
+            Frags<C> &nxt = s % 2 == 0 ? f1 : f0;
+            if (s + 1 < C::kKSteps) {
+                // reads of k-step s+1 under the MFMAs of k-step s
+                half_stage<C, M, false>(cur, nxt, stage_a(kt), stage_b(kt), fo[s + 1], acc, st,
+                                        smem, 0, 0, wave);
+            } else {
+                wait_vm<(C::STAGES - 2) * C::kLoads>();   // stage kt+1 landed
+                __builtin_amdgcn_s_barrier();
+                // every wavefront has read all of stage kt: refill its buffer
+                // with stage kt+STAGES, and read the next stage's k-step 0,
+                // under the last k-step's MFMAs
+                const int nk = kt + 1 < numK ? kt + 1 : kt;
+                half_stage<C, M, true>(cur, nxt, stage_a(nk), stage_b(nk), fo[0], acc, st, smem,
+                                       kt % C::STAGES, kb(kt + C::STAGES), wave);
+            }
+        }
     }
     wait_vm<0>();   // the tail loads land before anyone reuses the buffers
 }
@@ -322,6 +346,129 @@ __device__ __forceinline__ void store_tile(const EpilogueArgs &ep, v16f d, int64
     }
 }
 
+// The finished fp16 block tile is staged in LDS (BM rows of BN*2 bytes) and
+// written out row by row in 16-byte pieces, so that every store instruction
+// fills whole 128-byte lines; straight from the accumulator layout each
+// store would touch 32 rows.  8-byte unit u of tile row r sits in slot
+// u ^ (r % 32): the 32 rows of an accumulator tile write one unit each
+// without bank conflicts, and a 16-byte read of units 2k, 2k+1 finds them in
+// slot k ^ ((r % 32) / 2), halves swapped when r is odd.
+template <class C>
+__device__ __forceinline__ void write_tile(const char *smem, const EpilogueArgs &ep, int64_t m0,
+                                           int64_t n0, int64_t T, int64_t N, int tid)
+{
+    constexpr int kPieces = C::BN / 8;                 // 16-byte pieces per tile row
+    constexpr int kRowsPerPass = C::kThreads / kPieces;
+    const int k = tid % kPieces;
+#pragma unroll 4
+    for (int r = tid / kPieces; r < C::BM; r += kRowsPerPass) {
+        const int64_t t = m0 + r, n = n0 + 8 * k;
+        uint4 v = *reinterpret_cast<const uint4 *>(smem + r * (C::BN * 2) +
+                                                   16 * (k ^ ((r & 31) >> 1)));
+        if (r & 1)
+            v = make_uint4(v.z, v.w, v.x, v.y);
+        if (t < T && n < N)
+            *reinterpret_cast<uint4 *>(ep.out + t * N + n) = v;
+    }
+}
+
+// Up to 32 outlier columns: their fp16 fragments come straight from L2
+// (rows of 32 halves), and each 32x32 accumulator tile is finished on its
+// own (dequantize, fp16 MFMA over the outlier columns, bias, round) in a few
+// VGPRs and staged in LDS, which every wavefront has stopped reading; then
+// the whole block tile is written out.  Operands come from clamped
+// addresses, the outlier fragments all first and the column scales one
+// column group ahead, so the latency is not paid per tile.
+template <class C, bool kBias>
+__device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], const float (&at)[C::FM],
+                                            char *smem, const EpilogueArgs &ep, int64_t m0,
+                                            int64_t n0, int64_t T, int64_t N, int nout, int wm,
+                                            int wn, int lane, int tid)
+{
+    static_assert(C::BM * C::BN * 2 <= C::kLdsBytes, "output tile fits the LDS ring");
+    const int tl = lane & 31, nl = 4 * (lane >> 5);
+    const int64_t tw = m0 + wm * (C::BM / C::WM), nw = n0 + wn * (C::BN / C::WN);
+    v4i xo[C::FM][2], wo[C::FN][2];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        int64_t t = tw + i * 32 + tl;
+        t = t < T ? t : T - 1;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+            xo[i][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.x_out + t * kOutlierPad + 16 * s2 + nl * 2)
+                                 : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+        int64_t n = nw + j * 32 + tl;
+        n = n < N ? n : N - 1;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+            wo[j][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.w_out + n * kOutlierPad + 16 * s2 + nl * 2)
+                                 : v4i{0, 0, 0, 0};
+    }
+    // column scales and bias of column group j, fetched one group ahead
+    v4f sn[2][4];
+    uint2 bias[2][4];
+    auto load_cols = [&](int j, int buf) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            int64_t nc = nw + j * 32 + 8 * g + nl;
+            nc = nc < N ? nc : N - 4;
+            sn[buf][g] = *reinterpret_cast<const v4f *>(ep.scb + nc);
+            if constexpr (kBias)
+                bias[buf][g] = *reinterpret_cast<const uint2 *>(ep.bias + nc);
+        }
+    };
+    load_cols(0, 0);
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+        if (j + 1 < C::FN)
+            load_cols(j + 1, (j + 1) % 2);
+        const int cb = j % 2;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            v16f d;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                d[r] = (float)acc[i][j][r] * (at[i] * sn[cb][r / 4][r % 4]);
+            if (nout > 0) {
+                d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wo[j][0]),
+                                                         __builtin_bit_cast(v8h, xo[i][0]), d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wo[j][1]),
+                                                         __builtin_bit_cast(v8h, xo[i][1]), d, 0, 0, 0);
+            }
+            // bias, one rounding, staged: registers 4g..4g+3 hold tile columns
+            // nc + 8g .. nc + 8g + 3 of tile row tr
+            const int tr = wm * (C::BM / C::WM) + i * 32 + tl;
+            const int nc = wn * (C::BN / C::WN) + j * 32 + nl;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint16_t h[4];
+                if constexpr (kBias) {
+                    const uint2 bb = bias[cb][g];
+                    const float bv[4] = {h2f((uint16_t)(bb.x & 0xffffu)), h2f((uint16_t)(bb.x >> 16)),
+                                         h2f((uint16_t)(bb.y & 0xffffu)), h2f((uint16_t)(bb.y >> 16))};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        h[q] = f2h(d[4 * g + q] + bv[q]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        h[q] = f2h(d[4 * g + q]);
+                }
+                const int u = (nc + 8 * g) / 4;
+                *reinterpret_cast<uint2 *>(smem + tr * (C::BN * 2) + 8 * (u ^ (tr & 31))) =
+                    make_uint2((unsigned)h[0] | ((unsigned)h[1] << 16),
+                               (unsigned)h[2] | ((unsigned)h[3] << 16));
+            }
+        }
+    }
+    __syncthreads();
+    write_tile<C>(smem, ep, m0, n0, T, N, tid);
+}
+
 template <class C, bool kRawI32>
 __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__ A,
                                                       const int8_t *__restrict__ B, int64_t T,
@@ -348,7 +495,7 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
         Streams<C> st;
         st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
                 n0, N, wave, lane);
-        mainloop<C, MfmaI8>(smem, st, (int)(K / kRowBytes), acc, wm, wn, wave, lane);
+        mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
     }
 
     // The MFMAs compute D = CB_tile * Xq_tile^T, so a 32x32 accumulator holds
@@ -384,51 +531,10 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
             at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
         }
         if (nout <= kOutlierPad) {
-            // Up to 32 outlier columns: their fp16 fragments come straight from
-            // L2, and each 32x32 tile is finished on its own (dequantize, fp16
-            // MFMA over the outlier columns, bias, round, store) in a few VGPRs.
-            v4i xo[C::FM][2], wo[C::FN][2];
-#pragma unroll
-            for (int i = 0; i < C::FM; ++i) {
-                int64_t t = tw + i * 32 + tl;
-                t = t < T ? t : T - 1;
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-                    xo[i][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.x_out + t * K + 16 * s2 + nl * 2)
-                                         : v4i{0, 0, 0, 0};
-            }
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-                int64_t n = nw + j * 32 + tl;
-                n = n < N ? n : N - 1;
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-                    wo[j][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.w_out + n * K + 16 * s2 + nl * 2)
-                                         : v4i{0, 0, 0, 0};
-            }
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-                v4f sn[4];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    int64_t n = nw + j * 32 + 8 * g + nl;
-                    sn[g] = *reinterpret_cast<const v4f *>(ep.scb + (n < N ? n : N - 4));
-                }
-#pragma unroll
-                for (int i = 0; i < C::FM; ++i) {
-                    v16f d;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        d[r] = (float)acc[i][j][r] * (at[i] * sn[r / 4][r % 4]);
-                    if (nout > 0) {
-                        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wo[j][0]),
-                                                                 __builtin_bit_cast(v8h, xo[i][0]), d, 0, 0, 0);
-                        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wo[j][1]),
-                                                                 __builtin_bit_cast(v8h, xo[i][1]), d, 0, 0, 0);
-                    }
-                    store_tile<C>(ep, d, tw + i * 32 + tl, nw + j * 32 + nl, T, N);
-                }
-            }
+            if (ep.bias)
+                finish_tile<C, true>(acc, at, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
+            else
+                finish_tile<C, false>(acc, at, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
         } else {
             // Many outlier columns: park the dequantized int8 part of the tile
             // in the fp32 workspace; k_gemm_outliers adds the fp16 product.
@@ -484,9 +590,12 @@ __device__ __forceinline__ void outlier_tile(char *smem, int tile, int ntiles, i
                 acc[i][j][r] = 0.0f;
     {
         Streams<C> st;
-        st.init(reinterpret_cast<const char *>(ep.x_out), 2 * K, m0, T,
-                reinterpret_cast<const char *>(ep.w_out), 2 * K, n0, N, wave, lane);
-        const int stages = (nout + kOutlierPad - 1) / kOutlierPad;   // 32 halves = 64 bytes each
+        const int64_t ldo = outlier_ld(nout);   // x_out / w_out row stride in halves
+        st.init(reinterpret_cast<const char *>(ep.x_out), 2 * ldo, m0, T,
+                reinterpret_cast<const char *>(ep.w_out), 2 * ldo, n0, N, wave, lane);
+        // the outlier count padded to 32 halves = one 64-byte stage each
+        static_assert(C::ROWB == 64, "outlier rows are padded to 64 bytes");
+        const int stages = (nout + kOutlierPad - 1) / kOutlierPad;
         mainloop<C, MfmaF16F>(smem, st, stages, acc, wm, wn, wave, lane);
     }
     const int tl = lane & 31, nl = 4 * (lane >> 5);
@@ -531,11 +640,17 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_outliers(int64_t T, int64_
     }
 }
 
-template <class C>
+// C: the int8 GEMM (K must be a multiple of C::ROWB); CO: the fp16 pass over
+// more than 32 outlier columns (outlier rows are padded to 64 bytes, so
+// CO::ROWB must be 64).
+template <class C, class CO = C>
 hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
                   const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
                   hipEvent_t ev1 = nullptr)
 {
+    static_assert(CO::ROWB == 64 && CO::BM == C::BM && CO::BN == C::BN, "outlier pass tiling");
+    if (K % C::ROWB != 0)
+        return hipErrorInvalidValue;
     const int64_t ntm = (T + C::BM - 1) / C::BM, ntn = (N + C::BN - 1) / C::BN;
     const dim3 grid((unsigned)(ntm * ntn));
     if (ev0) {
@@ -554,7 +669,7 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
     }
     if (!ep.c_i32) {
         const int64_t blocks = ntm * ntn < kPersistentBlocks ? ntm * ntn : kPersistentBlocks;
-        hipLaunchKernelGGL((k_gemm_outliers<C>), dim3((unsigned)blocks), dim3(C::kThreads), 0, s,
+        hipLaunchKernelGGL((k_gemm_outliers<CO>), dim3((unsigned)blocks), dim3(CO::kThreads), 0, s,
                            T, K, N, ep);
     }
     return hipGetLastError();

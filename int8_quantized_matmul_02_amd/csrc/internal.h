@@ -16,6 +16,14 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 constexpr int kWave = 64;
 constexpr int kOutlierPad = 32;   // outlier operands are zero-padded to a multiple of this
 
+// Row stride, in halves, of the gathered outlier operands x_out [T, ld] and
+// w_out [N, ld]: the outlier count n padded to a multiple of kOutlierPad
+// (rows stay short and dense; every reader knows n).
+__host__ __device__ __forceinline__ int64_t outlier_ld(int n)
+{
+    return (int64_t)(n + kOutlierPad - 1) / kOutlierPad * kOutlierPad;
+}
+
 __device__ __forceinline__ float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 // fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default mode); overflow -> inf.
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
@@ -62,8 +70,8 @@ hipError_t launch_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N, int
 
 // What the row-quantization launch needs to also produce the dequantized
 // outlier weight rows for the GEMM: w_out[n, j] = fp16(CB[n,O[j]]*SCB[n]/127),
-// zero for n_outliers <= j < pad32(n_outliers), row stride K.  w_out == null
-// skips it.
+// zero for n_outliers <= j < outlier_ld(n_outliers), which is also the row
+// stride.  w_out == null skips it.
 struct GatherArgs {
     const int8_t *CB;
     const float *SCB;
@@ -77,8 +85,8 @@ constexpr int kMaxDetectSplits = 64;
 int detect_row_splits(int64_t T, int64_t K);
 
 // Outlier detection + compaction + row quantization (+ the optional outlier
-// weight gather).  x_out (fp16 [T, K]) receives the gathered outlier columns
-// when non-null.  xq_packed (T <= 16 only) writes Xq in the decode kernel's
+// weight gather).  x_out (fp16 [T, outlier_ld(n)]) receives the gathered
+// outlier columns, zero-padded, when non-null.  xq_packed (T <= 16 only) writes Xq in the decode kernel's
 // fragment order [K/64][4][16][16] (16*K bytes; rows >= T are left as they
 // are) instead of row-major [T, K].
 hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
@@ -90,8 +98,8 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
 struct EpilogueArgs {
     const float *a;          // [T] row absmax
     const float *scb;        // [N]
-    const uint16_t *x_out;   // [T, ldo] gathered outlier activations (fp16)
-    const uint16_t *w_out;   // [N, ldo] dequantized outlier weights (fp16), GEMM path
+    const uint16_t *x_out;   // [T, outlier_ld(n)] gathered outlier activations (fp16)
+    const uint16_t *w_out;   // [N, outlier_ld(n)] dequantized outlier weights (fp16), GEMM path
     const int32_t *O;        // [n] outlier column indices (weight-streaming path)
     const int32_t *n_out;    // device scalar n
     const uint16_t *bias;    // [N] or null

@@ -213,8 +213,8 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__re
 // 16-byte chunks per thread; NC = 0 re-reads it from cache for very long
 // rows), its absmax over the non-outlier columns is reduced with shuffles and
 // LDS, then the int8 row is packed with outlier columns as 0, and the outlier
-// values are gathered into the compact fp16 row x_out[t, colmap[k]],
-// zero-padded to a multiple of 32.  Chunks without outlier columns (nearly
+// values are gathered into the compact fp16 row x_out[t, colmap[k]] (row
+// stride outlier_ld(n)), zero-padded to a multiple of 32.  Chunks without outlier columns (nearly
 // all of them) take a branch-free path.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint2 quant8(uint4 v, float amax)
@@ -232,7 +232,7 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float amax)
 __device__ __forceinline__ uint2 quant8_masked(uint4 v, unsigned fl, float amax, int64_t t,
                                               int64_t K, int64_t c,
                                               const int32_t *__restrict__ colmap,
-                                              uint16_t *__restrict__ x_out)
+                                              uint16_t *__restrict__ x_out, int64_t ldo)
 {
     unsigned packed[2] = {0u, 0u};
 #pragma unroll
@@ -241,7 +241,7 @@ __device__ __forceinline__ uint2 quant8_masked(uint4 v, unsigned fl, float amax,
         int q = 0;
         if ((fl >> i) & 1u) {
             if (x_out)
-                x_out[t * K + colmap[c * 8 + i]] = h;
+                x_out[t * ldo + colmap[c * 8 + i]] = h;
         } else if (amax > 0.0f) {
             q = quant127(h2f(h), amax);
         }
@@ -252,12 +252,12 @@ __device__ __forceinline__ uint2 quant8_masked(uint4 v, unsigned fl, float amax,
 
 __device__ __forceinline__ void quant_chunk(uint4 v, unsigned fl, float amax, int64_t t, int64_t K,
                                            int64_t c, const int32_t *__restrict__ colmap,
-                                           uint16_t *__restrict__ x_out, uint2 *dst)
+                                           uint16_t *__restrict__ x_out, int64_t ldo, uint2 *dst)
 {
     if (fl == 0u && amax > 0.0f)
         *dst = quant8(v, amax);
     else
-        *dst = quant8_masked(v, fl, amax, t, K, c, colmap, x_out);
+        *dst = quant8_masked(v, fl, amax, t, K, c, colmap, x_out, ldo);
 }
 
 __device__ __forceinline__ unsigned chunk_absmax_masked(uint4 v, unsigned fl)
@@ -302,17 +302,19 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
         // Extra blocks: dequantized outlier weight rows for the GEMM,
         // w_out[r, j] = fp16(CB[r, O[j]] * SCB[r] / 127), zero up to a multiple of 32.
         const int n = *n_out;
-        const int npad = (n + kOutlierPad - 1) / kOutlierPad * kOutlierPad;
+        const int64_t ldo = outlier_ld(n);
         const int64_t gb = (int64_t)blockIdx.x - T, nb = (int64_t)gridDim.x - T;
         for (int64_t r = gb * kWavesPerBlock + wave; r < N; r += nb * kWavesPerBlock) {
             const float sc = SCB[r];
-            for (int j = lane; j < npad; j += kWave)
-                w_out[r * K + j] = j < n ? dequant_w(CB[r * K + O[j]], sc) : (uint16_t)0;
+            for (int j = lane; j < ldo; j += kWave)
+                w_out[r * ldo + j] = j < n ? dequant_w(CB[r * K + O[j]], sc) : (uint16_t)0;
         }
         return;
     }
     const int64_t t = blockIdx.x;
     const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
+    const int nout = x_out ? *n_out : 0;
+    const int64_t ldo = outlier_ld(nout);
     const int64_t nchunk = K / 8;
     unsigned m = 0;
     uint4 v[NC > 0 ? NC : 1];
@@ -344,19 +346,17 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
         for (int i = 0; i < NC; ++i) {
             const int64_t c = tid + (int64_t)i * kBlock;
             if (c < nchunk)
-                quant_chunk(v[i], fl[i], amax, t, K, c, colmap, x_out,
+                quant_chunk(v[i], fl[i], amax, t, K, c, colmap, x_out, ldo,
                             xq_chunk(Xq, t, K, c, packed));
         }
     } else {
         for (int64_t c = tid; c < nchunk; c += kBlock)
-            quant_chunk(xr[c], mask[c], amax, t, K, c, colmap, x_out,
+            quant_chunk(xr[c], mask[c], amax, t, K, c, colmap, x_out, ldo,
                         xq_chunk(Xq, t, K, c, packed));
     }
     if (x_out) {
-        const int n = *n_out;
-        const int npad = (n + kOutlierPad - 1) / kOutlierPad * kOutlierPad;
-        for (int j = n + tid; j < npad; j += kBlock)
-            x_out[t * K + j] = 0;
+        for (int j = nout + tid; j < ldo; j += kBlock)
+            x_out[t * ldo + j] = 0;
     }
     if (tid == 0)
         a[t] = amax;
