@@ -114,9 +114,12 @@ llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, int64_t K, f
     uint8_t *mask = base + align256((size_t)kMaxDetectSplits * ((size_t)K / 8));
     int32_t *colmap = reinterpret_cast<int32_t *>(mask + align256((size_t)K / 8));
     const GatherArgs none{nullptr, nullptr, 0, nullptr};
-    hipError_t e = launch_quantize_act(X, T, K, threshold, Xq, row_absmax, outlier_idx,
-                                       n_outliers, partial, mask, colmap, nullptr, none, false,
-                                       stream);
+    hipError_t e =
+        quantize_act_fits_one_block(T, K)
+            ? launch_quantize_act_one_block(X, T, K, threshold, Xq, row_absmax, outlier_idx,
+                                            n_outliers, nullptr, false, stream)
+            : launch_quantize_act(X, T, K, threshold, Xq, row_absmax, outlier_idx, n_outliers,
+                                  partial, mask, colmap, nullptr, none, false, stream);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 
@@ -155,8 +158,13 @@ llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, in
     // decode path takes more than a few activation rows in fragment order
     const GatherArgs g{CB, SCB, N, decode ? nullptr : w_out};
     const bool packed = decode && T >= kDecodePackedMinT;
-    if (launch_quantize_act(X, T, K, threshold, Xq, a, O, n_out, partial, mask, colmap, x_out, g,
-                            packed, stream) != hipSuccess)
+    const hipError_t eq =
+        decode && quantize_act_fits_one_block(T, K)
+            ? launch_quantize_act_one_block(X, T, K, threshold, Xq, a, O, n_out, x_out, packed,
+                                            stream)
+            : launch_quantize_act(X, T, K, threshold, Xq, a, O, n_out, partial, mask, colmap,
+                                  x_out, g, packed, stream);
+    if (eq != hipSuccess)
         return LLMINT8_ERR_HIP;
     EpilogueArgs ep{a, SCB, x_out, w_out, O, n_out, bias, out, nullptr, d_part};
     const hipError_t e =

@@ -95,6 +95,17 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
                                uint16_t *x_out, const GatherArgs &g, bool xq_packed,
                                hipStream_t s);
 
+// The same quantization for few rows in one block and one launch (no
+// workspace): T <= 4 and T*K <= kQuantOneBlockMaxElems, where one compute
+// unit (reading X twice, one correctly rounded division per value) beats
+// three dependent launches.  Results are identical to launch_quantize_act's.
+constexpr int64_t kQuantOneBlockMaxElems = 4 * 16384;
+bool quantize_act_fits_one_block(int64_t T, int64_t K);
+hipError_t launch_quantize_act_one_block(const uint16_t *X, int64_t T, int64_t K,
+                                         float threshold, int8_t *Xq, float *a, int32_t *O,
+                                         int32_t *n_out, uint16_t *x_out, bool xq_packed,
+                                         hipStream_t s);
+
 struct EpilogueArgs {
     const float *a;          // [T] row absmax
     const float *scb;        // [N]

@@ -362,6 +362,184 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
         a[t] = amax;
 }
 
+// ---------------------------------------------------------------------------
+// Few rows (T <= 4, the decode regime): the whole quantization in one block,
+// one launch.  Each thread owns 8-column chunks c = tid, tid + 512, ...:
+//   1. it loads its chunks' rows (as many at once as 32 16-byte registers
+//      hold), flags the columns with some |x| above the threshold and keeps
+//      per-row maxima of |x| over the unflagged columns;
+//   2. an LDS tree gives a[t], and a block scan over the chunk flags in
+//      column order gives the ascending outlier list, n and, per chunk, the
+//      number of outlier columns before it;
+//   3. it reloads its chunks (now cache hits), packs the int8 values and
+//      gathers the outlier values into x_out.
+// TB >= T bounds the rows in registers.  The tests and the arithmetic are the
+// same as in k_detect / k_compact / k_rowquant, so the results are identical
+// bit for bit.
+// ---------------------------------------------------------------------------
+constexpr int kSmallThreads = 512;
+constexpr int kSmallMaxT = 4;
+constexpr int kSmallMaxChunks = 133144 / 8;
+
+template <int TB>
+__global__ __launch_bounds__(kSmallThreads) void k_quant_small(
+    const uint16_t *__restrict__ X, int T, int K, unsigned thr_bits, int8_t *__restrict__ Xq,
+    float *__restrict__ a, int32_t *__restrict__ O, int32_t *__restrict__ n_out,
+    uint16_t *__restrict__ x_out, bool packed)
+{
+    constexpr int G = TB == 1 ? 16 : 32 / TB;   // chunks loaded at once
+    __shared__ uint8_t s_flags[kSmallMaxChunks];
+    __shared__ int s_pre[kSmallMaxChunks];
+    __shared__ unsigned s_red[TB][kSmallThreads];
+    __shared__ int s_wave_tot[kSmallThreads / kWave];
+    __shared__ int s_n;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int nchunk = K / 8;
+
+    // 1. outlier flags and per-row maxima over the remaining columns
+    unsigned rmax[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+        rmax[t] = 0u;
+    for (int c0 = tid; c0 < nchunk; c0 += G * kSmallThreads) {
+        uint4 v[G][TB];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int c = c0 + g * kSmallThreads;
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                v[g][t] = (t < T && c < nchunk)
+                              ? *reinterpret_cast<const uint4 *>(X + (int64_t)t * K + 8 * c)
+                              : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int c = c0 + g * kSmallThreads;
+            unsigned fl = 0;
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                const unsigned w[4] = {v[g][t].x, v[g][t].y, v[g][t].z, v[g][t].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    fl |= (abs_lo(w[i]) > thr_bits ? 1u : 0u) << (2 * i);
+                    fl |= (abs_hi(w[i]) > thr_bits ? 1u : 0u) << (2 * i + 1);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                rmax[t] = umax(rmax[t], chunk_absmax_masked(v[g][t], fl));
+            if (c < nchunk)
+                s_flags[c] = (uint8_t)fl;
+        }
+    }
+
+    // 2. row scales (LDS tree); outlier list in column order (block scan)
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+        s_red[t][tid] = rmax[t];
+    __syncthreads();
+#pragma unroll
+    for (int stride = kSmallThreads / 2; stride > 0; stride >>= 1) {
+        if (tid < stride) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                s_red[t][tid] = umax(s_red[t][tid], s_red[t][tid + stride]);
+        }
+        __syncthreads();
+    }
+    if (tid < T)
+        a[tid] = h2f((uint16_t)s_red[tid][0]);
+    const int per = (nchunk + kSmallThreads - 1) / kSmallThreads;
+    const int b0 = tid * per < nchunk ? tid * per : nchunk;
+    const int b1 = b0 + per < nchunk ? b0 + per : nchunk;
+    int cnt = 0;
+    for (int b = b0; b < b1; ++b)
+        cnt += __builtin_popcount(s_flags[b]);
+    int inc = cnt;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(inc, off, kWave);
+        if (lane >= off)
+            inc += o;
+    }
+    if (lane == kWave - 1)
+        s_wave_tot[wave] = inc;
+    __syncthreads();
+    int j = inc - cnt;
+    for (int w = 0; w < wave; ++w)
+        j += s_wave_tot[w];
+    for (int b = b0; b < b1; ++b) {
+        const unsigned m = s_flags[b];
+        s_pre[b] = j;
+        for (int i = 0; i < 8; ++i)
+            if ((m >> i) & 1u)
+                O[j++] = 8 * b + i;
+    }
+    if (tid == kSmallThreads - 1) {
+        *n_out = j;
+        s_n = j;
+    }
+    __syncthreads();
+
+    // 3. int8 rows and the gathered outlier values
+    const int n = s_n;
+    const int64_t ldo = outlier_ld(n);
+    float amax[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+        amax[t] = h2f((uint16_t)s_red[t][0]);
+    for (int c0 = tid; c0 < nchunk; c0 += G * kSmallThreads) {
+        uint4 v[G][TB];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int c = c0 + g * kSmallThreads;
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                v[g][t] = (t < T && c < nchunk)
+                              ? *reinterpret_cast<const uint4 *>(X + (int64_t)t * K + 8 * c)
+                              : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int c = c0 + g * kSmallThreads;
+            if (c >= nchunk)
+                continue;
+            const unsigned fl = s_flags[c];
+            const int pre = s_pre[c];
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                if (t >= T)
+                    continue;
+                uint2 q;
+                if (fl == 0u && amax[t] > 0.0f) {
+                    q = quant8(v[g][t], amax[t]);
+                } else {
+                    unsigned packed8[2] = {0u, 0u};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint16_t h = half_at(v[g][t], i);
+                        int qi = 0;
+                        if ((fl >> i) & 1u) {
+                            if (x_out)
+                                x_out[t * ldo + pre + __builtin_popcount(fl & ((1u << i) - 1u))] = h;
+                        } else if (amax[t] > 0.0f) {
+                            qi = quant127(h2f(h), amax[t]);
+                        }
+                        packed8[i >> 2] |= ((unsigned)qi & 0xffu) << (8 * (i & 3));
+                    }
+                    q = make_uint2(packed8[0], packed8[1]);
+                }
+                *xq_chunk(Xq, t, K, c, packed) = q;
+            }
+        }
+    }
+    if (x_out) {
+        const int padw = (int)ldo - n;
+        for (int idx = tid; idx < T * padw; idx += kSmallThreads)
+            x_out[(idx / padw) * ldo + n + idx % padw] = 0;
+    }
+}
+
 // Largest binary16 bit pattern whose value is <= thr (thr >= 0, not NaN);
 // 0x7c00 (inf) when thr >= 65504 so that no finite value exceeds it.
 unsigned threshold_bits(float thr)
@@ -401,6 +579,26 @@ int detect_row_splits(int64_t T, int64_t K)
     if (r > kMaxDetectSplits)
         r = kMaxDetectSplits;
     return r < 1 ? 1 : (int)r;
+}
+
+bool quantize_act_fits_one_block(int64_t T, int64_t K)
+{
+    return T <= kSmallMaxT && T * K <= kQuantOneBlockMaxElems;
+}
+
+hipError_t launch_quantize_act_one_block(const uint16_t *X, int64_t T, int64_t K,
+                                         float threshold, int8_t *Xq, float *a, int32_t *O,
+                                         int32_t *n_out, uint16_t *x_out, bool xq_packed,
+                                         hipStream_t s)
+{
+    const unsigned tb = threshold_bits(threshold);
+    if (T <= 1)
+        hipLaunchKernelGGL(k_quant_small<1>, dim3(1), dim3(kSmallThreads), 0, s, X, (int)T,
+                           (int)K, tb, Xq, a, O, n_out, x_out, xq_packed);
+    else
+        hipLaunchKernelGGL(k_quant_small<kSmallMaxT>, dim3(1), dim3(kSmallThreads), 0, s, X,
+                           (int)T, (int)K, tb, Xq, a, O, n_out, x_out, xq_packed);
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,

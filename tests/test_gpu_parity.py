@@ -40,7 +40,11 @@ def test_quantize_weight_exact(N, K):
     assert_equal_exact(d2h(SCB), SCBr, "SCB")
 
 
-@pytest.mark.parametrize("T,K", [(1, 64), (16, 256), (100, 320), (513, 1024), (2000, 2048)])
+# Few rows take the one-block kernel (T <= 4 and T*K <= 4*16384, (4, 16384)
+# at the limit); the rest, (4, 16448) just past it, the three-kernel chain.
+@pytest.mark.parametrize("T,K", [(1, 64), (16, 256), (100, 320), (513, 1024), (2000, 2048),
+                                 (1, 133120), (2, 12288), (3, 1088), (4, 16384), (4, 16448),
+                                 (9, 12288), (16, 16384)])
 @pytest.mark.parametrize("thr", [6.0, 0.0, np.inf, 2.5])
 def test_quantize_act_exact(T, K, thr):
     say("quantize_act T=%d K=%d thr=%s" % (T, K, thr))
