@@ -111,6 +111,13 @@ def timed_steps(torch, L, X, CBs, SCB, thr, out, ws, steps, warmup, ev):
     return (t1 - t0) * 1e3 / steps, float(np.mean(kern)), kern
 
 
+def spread_us(kern_ms):
+    """Median and p10/p90 of per-launch kernel times, in microseconds."""
+    q = np.percentile(np.asarray(kern_ms) * 1e3, [50, 10, 90])
+    return {"kernel_us_median": round(float(q[0]), 2), "kernel_us_p10": round(float(q[1]), 2),
+            "kernel_us_p90": round(float(q[2]), 2)}
+
+
 def cpu_baseline(X, W_t, thr, rows):
     import oracle
     CBh, SCBh = oracle.quantize_weight(W_t)
@@ -141,7 +148,7 @@ def decode_bench(torch, L, workloads, steps, warmup, ev, dev):
         X = torch.from_numpy(d["X"]).to(dev)
         out = torch.empty((T, N), dtype=torch.float16, device=dev)
         ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=dev)
-        ms, kms, _ = timed_steps(torch, L, X, [CB, CB2], SCB, 6.0, out, ws, steps, warmup, ev)
+        ms, kms, kern = timed_steps(torch, L, X, [CB, CB2], SCB, 6.0, out, ws, steps, warmup, ev)
         alg = K * N + 4 * N + T * K + 4 * T + 2 * T * N
         res["T%d" % T] = {"kernel_us": round(kms * 1e3, 2), "step_us": round(ms * 1e3, 2),
                           "kernel_GBs": round(alg / (kms * 1e-3) / 1e9, 1),
@@ -150,6 +157,7 @@ def decode_bench(torch, L, workloads, steps, warmup, ev, dev):
                           "alg_bytes": alg,
                           "traffic": profiled_traffic("k_decode_175b_fc1.txt",
                                                       "traffic_bytes_per_launch_T%d" % T)}
+        res["T%d" % T].update(spread_us(kern))
         log("decode T=%d: kernel %.1f us (%.0f GB/s), step %.1f us" % (T, kms * 1e3, alg / kms / 1e6, ms * 1e3))
     return res
 
@@ -199,7 +207,8 @@ def main():
     _, _, _, n_out = L.llmint8_quantize_act(X, thr)
     n_outliers = int(n_out.cpu()[0])
 
-    ms, gemm_ms, _ = timed_steps(torch, L, X, [CB], SCB, thr, out, ws, args.steps, args.warmup, ev)
+    ms, gemm_ms, gemm_kern = timed_steps(torch, L, X, [CB], SCB, thr, out, ws, args.steps,
+                                         args.warmup, ev)
     ops = 2.0 * T * K * N
     value = ops / (ms * 1e-3) / 1e12
     achieved = ops / (gemm_ms * 1e-3) / 1e12
@@ -229,6 +238,7 @@ def main():
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                      "kernel_us": round(gemm_ms * 1e3, 2), "ops_per_launch": ops},
     }
+    result["roofline"].update(spread_us(gemm_kern))
     if not args.no_decode:
         result["decode"] = decode_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
     if not args.no_cpu_baseline:
