@@ -316,36 +316,6 @@ __device__ __forceinline__ void mainloop(char *smem, const Streams<C> &st, int n
     wait_vm<0>();   // the tail loads land before anyone reuses the buffers
 }
 
-// Bias, one rounding to fp16 and 8-byte stores for one transposed 32x32
-// accumulator tile: row t, columns n0 + 8g + {0..3} in registers 4g..4g+3.
-template <class C>
-__device__ __forceinline__ void store_tile(const EpilogueArgs &ep, v16f d, int64_t t, int64_t n0,
-                                           int64_t T, int64_t N)
-{
-    if (t >= T)
-        return;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + 8 * g;
-        if (n >= N)
-            continue;
-        float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (ep.bias) {
-            const uint2 bb = *reinterpret_cast<const uint2 *>(ep.bias + n);
-            b[0] = h2f((uint16_t)(bb.x & 0xffffu));
-            b[1] = h2f((uint16_t)(bb.x >> 16));
-            b[2] = h2f((uint16_t)(bb.y & 0xffffu));
-            b[3] = h2f((uint16_t)(bb.y >> 16));
-        }
-        uint16_t h[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            h[q] = f2h(d[4 * g + q] + b[q]);
-        *reinterpret_cast<uint2 *>(ep.out + t * N + n) =
-            make_uint2((unsigned)h[0] | ((unsigned)h[1] << 16), (unsigned)h[2] | ((unsigned)h[3] << 16));
-    }
-}
-
 // The finished fp16 block tile is staged in LDS (BM rows of BN*2 bytes) and
 // written out row by row in 16-byte pieces, so that every store instruction
 // fills whole 128-byte lines; straight from the accumulator layout each
@@ -482,6 +452,11 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
     tile_coords(blockIdx.x, gridDim.x, ntm, ntn, C::GROUP, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
 
+    // Every column an outlier (n == K, e.g. threshold 0): Xq is all zeros and
+    // the int8 part vanishes; k_gemm_outliers computes the whole output.
+    if (!kRawI32 && *ep.n_out >= K)
+        return;
+
     v16i acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -593,32 +568,50 @@ __device__ __forceinline__ void outlier_tile(char *smem, int tile, int ntiles, i
         const int64_t ldo = outlier_ld(nout);   // x_out / w_out row stride in halves
         st.init(reinterpret_cast<const char *>(ep.x_out), 2 * ldo, m0, T,
                 reinterpret_cast<const char *>(ep.w_out), 2 * ldo, n0, N, wave, lane);
-        // the outlier count padded to 32 halves = one 64-byte stage each
-        static_assert(C::ROWB == 64, "outlier rows are padded to 64 bytes");
-        const int stages = (nout + kOutlierPad - 1) / kOutlierPad;
+        // more than 32 outliers: rows padded to a multiple of 64 halves = 128 bytes
+        static_assert(128 % C::ROWB == 0, "outlier rows hold whole stages");
+        const int stages = (int)(ldo * 2 / C::ROWB);
         mainloop<C, MfmaF16F>(smem, st, stages, acc, wm, wn, wave, lane);
     }
+    // Add the parked int8 part (none when every column is an outlier), the
+    // bias, round once, stage the tile in the LDS ring (every wavefront is past
+    // its main loop) and write it out in whole lines.
+    static_assert(C::BM * C::BN * 2 <= C::kLdsBytes, "output tile fits the LDS ring");
     const int tl = lane & 31, nl = 4 * (lane >> 5);
     const int64_t tw = m0 + wm * (C::BM / C::WM), nw = n0 + wn * (C::BN / C::WN);
+    const bool int8_part = nout < K;
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        const int64_t t = tw + i * 32 + tl;
+    for (int j = 0; j < C::FN; ++j) {
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-            v16f d = acc[i][j];
+        for (int i = 0; i < C::FM; ++i) {
+            int64_t t = tw + i * 32 + tl;
+            t = t < T ? t : T - 1;
+            const int tr = wm * (C::BM / C::WM) + i * 32 + tl;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int64_t n = nw + j * 32 + 8 * g + nl;
-                if (t < T && n < N) {
-                    const v4f p = *reinterpret_cast<const v4f *>(ep.d_part + t * N + n);
+                int64_t n = nw + j * 32 + 8 * g + nl;
+                n = n < N ? n : N - 4;
+                v4f p = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                if (int8_part)
+                    p = *reinterpret_cast<const v4f *>(ep.d_part + t * N + n);
+                const uint2 bb = ep.bias ? *reinterpret_cast<const uint2 *>(ep.bias + n)
+                                         : make_uint2(0u, 0u);
+                const float bv[4] = {h2f((uint16_t)(bb.x & 0xffffu)), h2f((uint16_t)(bb.x >> 16)),
+                                     h2f((uint16_t)(bb.y & 0xffffu)), h2f((uint16_t)(bb.y >> 16))};
+                uint16_t h[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        d[4 * g + q] += p[q];
-                }
+                for (int q = 0; q < 4; ++q)
+                    h[q] = f2h(acc[i][j][4 * g + q] + p[q] + bv[q]);
+                const int u = (wn * (C::BN / C::WN) + j * 32 + 8 * g + nl) / 4;
+                *reinterpret_cast<uint2 *>(smem + tr * (C::BN * 2) + 8 * (u ^ (tr & 31))) =
+                    make_uint2((unsigned)h[0] | ((unsigned)h[1] << 16),
+                               (unsigned)h[2] | ((unsigned)h[3] << 16));
             }
-            store_tile<C>(ep, d, t, nw + j * 32 + nl, T, N);
         }
     }
+    __syncthreads();
+    write_tile<C>(smem, ep, m0, n0, T, N, threadIdx.x);
 }
 
 template <class C>
@@ -641,14 +634,13 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_outliers(int64_t T, int64_
 }
 
 // C: the int8 GEMM (K must be a multiple of C::ROWB); CO: the fp16 pass over
-// more than 32 outlier columns (outlier rows are padded to 64 bytes, so
-// CO::ROWB must be 64).
+// more than 32 outlier columns (whose rows are padded to 128 bytes).
 template <class C, class CO = C>
 hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
                   const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
                   hipEvent_t ev1 = nullptr)
 {
-    static_assert(CO::ROWB == 64 && CO::BM == C::BM && CO::BN == C::BN, "outlier pass tiling");
+    static_assert(CO::BM == C::BM && CO::BN == C::BN, "outlier pass tiling");
     if (K % C::ROWB != 0)
         return hipErrorInvalidValue;
     const int64_t ntm = (T + C::BM - 1) / C::BM, ntn = (N + C::BN - 1) / C::BN;

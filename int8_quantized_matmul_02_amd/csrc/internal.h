@@ -14,14 +14,16 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
-constexpr int kOutlierPad = 32;   // outlier operands are zero-padded to a multiple of this
+constexpr int kOutlierPad = 32;   // outlier rows of up to 32 columns are padded to this length
 
 // Row stride, in halves, of the gathered outlier operands x_out [T, ld] and
-// w_out [N, ld]: the outlier count n padded to a multiple of kOutlierPad
-// (rows stay short and dense; every reader knows n).
+// w_out [N, ld]; the rows are zero-padded up to it.  Up to 32 outliers: 32
+// (the GEMM epilogue's two 16-deep fp16 MFMA steps); more: a multiple of 64
+// halves, the 128-byte stages of the fp16 GEMM pass.  Rows stay short and
+// dense, and every reader derives ld from n.
 __host__ __device__ __forceinline__ int64_t outlier_ld(int n)
 {
-    return (int64_t)(n + kOutlierPad - 1) / kOutlierPad * kOutlierPad;
+    return n == 0 ? 0 : n <= kOutlierPad ? kOutlierPad : (int64_t)(n + 63) / 64 * 64;
 }
 
 __device__ __forceinline__ float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }

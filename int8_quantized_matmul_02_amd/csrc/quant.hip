@@ -229,11 +229,29 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float amax)
     return make_uint2(packed[0], packed[1]);
 }
 
+// The 8 values of a chunk whose columns are all outliers: they sit at
+// consecutive positions p0 .. p0+7 of the compact row.
+__device__ __forceinline__ void copy8(uint16_t *__restrict__ dst, uint4 v)
+{
+    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0u) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            dst[i] = half_at(v, i);
+    }
+}
+
 __device__ __forceinline__ uint2 quant8_masked(uint4 v, unsigned fl, float amax, int64_t t,
                                               int64_t K, int64_t c,
                                               const int32_t *__restrict__ colmap,
                                               uint16_t *__restrict__ x_out, int64_t ldo)
 {
+    if (fl == 0xffu) {
+        if (x_out)
+            copy8(x_out + t * ldo + colmap[c * 8], v);
+        return make_uint2(0u, 0u);
+    }
     unsigned packed[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -297,17 +315,42 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
                                                      uint16_t *__restrict__ w_out, bool packed)
 {
     __shared__ unsigned s_max[kWavesPerBlock];
+    __shared__ uint16_t s_tab[kWavesPerBlock][256];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     if ((int64_t)blockIdx.x >= T) {
         // Extra blocks: dequantized outlier weight rows for the GEMM,
-        // w_out[r, j] = fp16(CB[r, O[j]] * SCB[r] / 127), zero up to a multiple of 32.
+        // w_out[r, j] = fp16(CB[r, O[j]] * SCB[r] / 127), zero up to a multiple
+        // of 32; one wavefront per weight row.  A row has only 255 possible
+        // values, so the wavefront first tabulates them in LDS; each lane then
+        // gathers 8 consecutive outlier columns and stores them at once.  (LDS
+        // operations of one wavefront complete in order, so the table is
+        // complete before any lane reads it, and the reads of one row are done
+        // before the next row's table overwrites it.)
         const int n = *n_out;
         const int64_t ldo = outlier_ld(n);
         const int64_t gb = (int64_t)blockIdx.x - T, nb = (int64_t)gridDim.x - T;
+        uint16_t *tab = s_tab[wave];
         for (int64_t r = gb * kWavesPerBlock + wave; r < N; r += nb * kWavesPerBlock) {
             const float sc = SCB[r];
-            for (int j = lane; j < ldo; j += kWave)
-                w_out[r * ldo + j] = j < n ? dequant_w(CB[r * K + O[j]], sc) : (uint16_t)0;
+            for (int i = lane; i < 255; i += kWave)
+                tab[i] = dequant_w(i - 127, sc);
+            const int8_t *cbr = CB + r * K;
+            for (int64_t j0 = 8 * lane; j0 < ldo; j0 += 8 * kWave) {
+                const int4 o0 = *reinterpret_cast<const int4 *>(O + j0);
+                const int4 o1 = *reinterpret_cast<const int4 *>(O + j0 + 4);
+                const int o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+                unsigned h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    // entries of O at or past n are stale: read column 0 instead
+                    const int oc = j0 + e < n ? o[e] : 0;
+                    const unsigned v = tab[(cbr[oc] + 127) & 255];
+                    h[e] = j0 + e < n ? v : 0u;
+                }
+                *reinterpret_cast<uint4 *>(w_out + r * ldo + j0) =
+                    make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                               h[6] | (h[7] << 16));
+            }
         }
         return;
     }
@@ -513,6 +556,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_small(
                 uint2 q;
                 if (fl == 0u && amax[t] > 0.0f) {
                     q = quant8(v[g][t], amax[t]);
+                } else if (fl == 0xffu) {
+                    if (x_out)
+                        copy8(x_out + t * ldo + pre, v[g][t]);
+                    q = make_uint2(0u, 0u);
                 } else {
                     unsigned packed8[2] = {0u, 0u};
 #pragma unroll
