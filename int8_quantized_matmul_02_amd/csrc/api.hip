@@ -41,7 +41,6 @@ MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N)
     L.xq = off;          off += align256((t > 16 ? t : 16) * k);   // decode: 16-row fragment order
     L.x_out = off;       off += align256(2 * t * k);
     L.w_out = off;       off += align256(2 * n * k);
-    L.d_part = off;      off += align256(4 * t * n);
     L.total = off;
     return L;
 }
@@ -152,7 +151,6 @@ llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, in
     int8_t *Xq = reinterpret_cast<int8_t *>(base + L.xq);
     uint16_t *x_out = reinterpret_cast<uint16_t *>(base + L.x_out);
     uint16_t *w_out = reinterpret_cast<uint16_t *>(base + L.w_out);
-    float *d_part = reinterpret_cast<float *>(base + L.d_part);
 
     // the GEMM path also needs the dequantized outlier weight rows; the
     // decode path takes more than a few activation rows in fragment order
@@ -166,7 +164,7 @@ llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, in
                                   x_out, g, packed, stream);
     if (eq != hipSuccess)
         return LLMINT8_ERR_HIP;
-    EpilogueArgs ep{a, SCB, x_out, w_out, O, n_out, bias, out, nullptr, d_part};
+    EpilogueArgs ep{a, SCB, x_out, w_out, O, n_out, bias, out, nullptr};
     const hipError_t e =
         decode ? launch_decode(Xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
                : launch_gemm(Xq, CB, T, K, N, ep, stream, main_start, main_stop);
@@ -193,7 +191,7 @@ llmint8_status_t llmint8_igemm_i32(const int8_t *Xq, int64_t T, int64_t K, int64
     if (path == 2 && T > kDecodeMaxT)
         return LLMINT8_ERR_UNSUPPORTED_SHAPE;
     const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
-    EpilogueArgs ep{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, C, nullptr};
+    EpilogueArgs ep{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, C};
     hipError_t e = decode ? launch_decode(Xq, CB, T, K, N, ep, false, stream)
                           : launch_gemm(Xq, CB, T, K, N, ep, stream);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;

@@ -8,8 +8,8 @@ namespace llmint8 {
 // rows.  With K a multiple of 128 the ring holds two stages of 128 bytes per
 // row (every load instruction then fetches whole 128-byte lines), otherwise
 // four stages of 64 bytes; 128 KB of LDS either way.  The fp16 pass over
-// more than 32 outlier columns (rows padded to 128 bytes) takes 128-byte
-// stages.
+// more than 32 outlier columns (rows padded to 128 bytes) runs through the
+// same ring.
 using Gemm128 = gemm::Cfg<256, 256, 2, 2, 2, 4, 128>;
 using Gemm64 = gemm::Cfg<256, 256, 2, 2, 4, 4, 64>;
 
@@ -17,8 +17,8 @@ hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K,
                        const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1)
 {
     if (K % Gemm128::ROWB == 0)
-        return gemm::launch<Gemm128, Gemm128>(Xq, CB, T, K, N, ep, s, ev0, ev1);
-    return gemm::launch<Gemm64, Gemm128>(Xq, CB, T, K, N, ep, s, ev0, ev1);
+        return gemm::launch<Gemm128>(Xq, CB, T, K, N, ep, s, ev0, ev1);
+    return gemm::launch<Gemm64>(Xq, CB, T, K, N, ep, s, ev0, ev1);
 }
 
 }  // namespace llmint8

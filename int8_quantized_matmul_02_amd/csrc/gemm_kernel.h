@@ -10,9 +10,10 @@
 // agentlenshq.com write-up, "Core idea" step 3).
 //
 // Design (gfx950):
-//  * Block tile BM x BN, 64 bytes of K per pipeline stage, STAGES stages in
-//    LDS filled by direct global->LDS 16-byte loads (no VGPR staging): each
-//    wavefront load instruction fills 1 KB = 16 staged rows of 64 bytes.
+//  * Block tile BM x BN, ROWB (64 or 128) bytes of K per pipeline stage,
+//    STAGES stages in LDS filled by direct global->LDS 16-byte loads (no
+//    VGPR staging): each wavefront load instruction fills 1 KB = 1024/ROWB
+//    staged rows.
 //  * Both operands are K-contiguous ([T,K] and [N,K]), so A and B fragments
 //    have the same shape: a lane reads 16 consecutive bytes of one row.  The
 //    16-byte chunks of staged row r are XOR-swizzled (chunk c in slot
@@ -22,9 +23,11 @@
 //    accumulator tiles of 32x32 (v_mfma_i32_32x32x32_i8; the k order inside
 //    an MFMA is irrelevant for an exact integer sum because A and B use the
 //    same lane -> k mapping).
-//  * The fp16 outlier product (K' = number of outlier columns, padded to 32)
-//    runs through the same pipeline on the gathered fp16 operands with
-//    v_mfma_f32_32x32x16_f16, accumulating onto the dequantized fp32 values.
+//  * The fp16 outlier product, with v_mfma_f32_32x32x16_f16 accumulating
+//    onto the dequantized fp32 values: up to 32 outlier columns as two MFMAs
+//    per accumulator tile in k_gemm's epilogue; more in k_gemm_many, which
+//    runs it as a second pass through the same pipeline over the gathered
+//    fp16 operands (K' = n padded to a multiple of 64).
 //  * Tiles are numbered XCD-aware: workgroup ids are dealt round-robin over
 //    the 8 XCDs, so each XCD gets a contiguous run of tile ids, and tile ids
 //    walk a grouped raster (GROUP tile rows at a time) for L2 reuse.
@@ -39,7 +42,6 @@ namespace {   // internal linkage: nothing here is exported from the library
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kXcds = 8;
-constexpr int kPersistentBlocks = 256;   // one per CU
 
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int GROUP_, int ROWB_ = 64>
 struct Cfg {
@@ -170,6 +172,16 @@ struct MfmaF16 {
     }
 };
 
+// fp16 MFMA on fp32 accumulators (the many-outlier pass).
+struct MfmaF16F {
+    typedef v16f acc_t;
+    __device__ __forceinline__ static acc_t op(v4i a, v4i b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a),
+                                                      __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+    }
+};
+
 // Fragments of one 32-deep k-step: FM A-fragments and FN B-fragments.
 template <class C>
 struct Frags {
@@ -238,16 +250,6 @@ __device__ __forceinline__ void half_stage(const Frags<C> &cur, Frags<C> &nxt, c
         __builtin_amdgcn_sched_barrier(0);
     }
 }
-
-// fp16 MFMA on fp32 accumulators.
-struct MfmaF16F {
-    typedef v16f acc_t;
-    __device__ __forceinline__ static acc_t op(v4i a, v4i b, acc_t c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a),
-                                                      __builtin_bit_cast(v8h, b), c, 0, 0, 0);
-    }
-};
 
 // Runs numK stages (ROWB bytes of K = ROWB/32 32-deep k-steps each) of the
 // pipelined main loop.  Stage s is loaded into LDS buffer s % STAGES.  A
@@ -439,6 +441,86 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
     write_tile<C>(smem, ep, m0, n0, T, N, tid);
 }
 
+// More than 32 outlier columns: the fp16 product runs as a second GEMM on
+// the same tile, through the same LDS pipeline, over the gathered operands
+// (x_out and w_out rows, K' = n padded to a multiple of 64 halves).  The int8
+// sums are first dequantized into fp32 accumulators (the int32 ones die
+// there, so the two share registers) onto which the fp16 MFMAs add; then
+// the bias, one rounding, and the tile goes out through LDS like
+// finish_tile's.
+template <class C>
+__device__ __forceinline__ void outlier_pass(const v16i (&acc)[C::FM][C::FN],
+                                             const float (&at)[C::FM], char *smem,
+                                             const EpilogueArgs &ep, int64_t m0, int64_t n0,
+                                             int64_t T, int64_t K, int64_t N, int nout, int wm,
+                                             int wn, int wave, int lane, int tid)
+{
+    const int tl = lane & 31, nl = 4 * (lane >> 5);
+    const int64_t nw = n0 + wn * (C::BN / C::WN);
+    v16f accf[C::FM][C::FN];
+    if (nout < K) {
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            v4f sn[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t n = nw + j * 32 + 8 * g + nl;
+                sn[g] = *reinterpret_cast<const v4f *>(ep.scb + (n < N ? n : N - 4));
+            }
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    accf[i][j][r] = (float)acc[i][j][r] * (at[i] * sn[r / 4][r % 4]);
+        }
+    } else {   // the int8 part is all zeros
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    accf[i][j][r] = 0.0f;
+    }
+    __builtin_amdgcn_s_barrier();   // every wavefront is done reading the LDS ring
+    {
+        Streams<C> st;
+        const int64_t ldo = outlier_ld(nout);   // x_out / w_out row stride in halves
+        st.init(reinterpret_cast<const char *>(ep.x_out), 2 * ldo, m0, T,
+                reinterpret_cast<const char *>(ep.w_out), 2 * ldo, n0, N, wave, lane);
+        static_assert(128 % C::ROWB == 0, "outlier rows (multiples of 128 bytes) hold whole stages");
+        mainloop<C, MfmaF16F>(smem, st, (int)(ldo * 2 / C::ROWB), accf, wm, wn, wave, lane);
+    }
+    static_assert(C::BM * C::BN * 2 <= C::kLdsBytes, "output tile fits the LDS ring");
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            const int tr = wm * (C::BM / C::WM) + i * 32 + tl;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                int64_t n = nw + j * 32 + 8 * g + nl;
+                n = n < N ? n : N - 4;
+                const uint2 bb = ep.bias ? *reinterpret_cast<const uint2 *>(ep.bias + n)
+                                         : make_uint2(0u, 0u);
+                const float bv[4] = {h2f((uint16_t)(bb.x & 0xffffu)), h2f((uint16_t)(bb.x >> 16)),
+                                     h2f((uint16_t)(bb.y & 0xffffu)), h2f((uint16_t)(bb.y >> 16))};
+                uint16_t h[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    h[q] = f2h(accf[i][j][4 * g + q] + bv[q]);
+                const int u = (wn * (C::BN / C::WN) + j * 32 + 8 * g + nl) / 4;
+                *reinterpret_cast<uint2 *>(smem + tr * (C::BN * 2) + 8 * (u ^ (tr & 31))) =
+                    make_uint2((unsigned)h[0] | ((unsigned)h[1] << 16),
+                               (unsigned)h[2] | ((unsigned)h[3] << 16));
+            }
+        }
+    }
+    __syncthreads();
+    write_tile<C>(smem, ep, m0, n0, T, N, tid);
+}
+
 template <class C, bool kRawI32>
 __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__ A,
                                                       const int8_t *__restrict__ B, int64_t T,
@@ -452,9 +534,8 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
     tile_coords(blockIdx.x, gridDim.x, ntm, ntn, C::GROUP, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
 
-    // Every column an outlier (n == K, e.g. threshold 0): Xq is all zeros and
-    // the int8 part vanishes; k_gemm_outliers computes the whole output.
-    if (!kRawI32 && *ep.n_out >= K)
+    // More than 32 outlier columns: k_gemm_many computes this output.
+    if (!kRawI32 && *ep.n_out > kOutlierPad)
         return;
 
     v16i acc[C::FM][C::FN];
@@ -505,118 +586,24 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
             const int64_t t = tw + i * 32 + tl;
             at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
         }
-        if (nout <= kOutlierPad) {
-            if (ep.bias)
-                finish_tile<C, true>(acc, at, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
-            else
-                finish_tile<C, false>(acc, at, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
-        } else {
-            // Many outlier columns: park the dequantized int8 part of the tile
-            // in the fp32 workspace; k_gemm_outliers adds the fp16 product.
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-                v4f sn[4];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    int64_t n = nw + j * 32 + 8 * g + nl;
-                    sn[g] = *reinterpret_cast<const v4f *>(ep.scb + (n < N ? n : N - 4));
-                }
-#pragma unroll
-                for (int i = 0; i < C::FM; ++i) {
-                    const int64_t t = tw + i * 32 + tl;
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int64_t n = nw + j * 32 + 8 * g + nl;
-                        v4f d;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            d[q] = (float)acc[i][j][4 * g + q] * (at[i] * sn[g][q]);
-                        if (t < T && n < N)
-                            *reinterpret_cast<v4f *>(ep.d_part + t * N + n) = d;
-                    }
-                }
-            }
-        }
+        if (ep.bias)
+            finish_tile<C, true>(acc, at, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
+        else
+            finish_tile<C, false>(acc, at, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
     }
 }
 
-// The fp16 product over more than 32 outlier columns, as its own GEMM
-// through the same LDS pipeline (K' = outlier count padded to 32), added to
-// the dequantized int8 part that k_gemm parked in d_part.  With 32 or fewer
-// outlier columns k_gemm has already finished the output and every block
-// returns at once.
+// More than 32 outlier columns (k_gemm returns at once then, and this kernel
+// does otherwise): per tile the int8 GEMM (skipped when every column is an
+// outlier, e.g. threshold 0, since Xq is then all zeros), then the fused
+// fp16 pass over the outlier columns.  A kernel of its own so that the
+// registers this path needs do not cost k_gemm's epilogue; one tile per
+// block (a persistent tile loop makes the compiler spill around it).
 template <class C>
-__device__ __forceinline__ void outlier_tile(char *smem, int tile, int ntiles, int ntm, int ntn,
-                                             int64_t T, int64_t K, int64_t N, int nout,
-                                             const EpilogueArgs &ep, int wm, int wn, int wave,
-                                             int lane)
-{
-    int tm, tn;
-    tile_coords(tile, ntiles, ntm, ntn, C::GROUP, tm, tn);
-    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-
-    v16f acc[C::FM][C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[i][j][r] = 0.0f;
-    {
-        Streams<C> st;
-        const int64_t ldo = outlier_ld(nout);   // x_out / w_out row stride in halves
-        st.init(reinterpret_cast<const char *>(ep.x_out), 2 * ldo, m0, T,
-                reinterpret_cast<const char *>(ep.w_out), 2 * ldo, n0, N, wave, lane);
-        // more than 32 outliers: rows padded to a multiple of 64 halves = 128 bytes
-        static_assert(128 % C::ROWB == 0, "outlier rows hold whole stages");
-        const int stages = (int)(ldo * 2 / C::ROWB);
-        mainloop<C, MfmaF16F>(smem, st, stages, acc, wm, wn, wave, lane);
-    }
-    // Add the parked int8 part (none when every column is an outlier), the
-    // bias, round once, stage the tile in the LDS ring (every wavefront is past
-    // its main loop) and write it out in whole lines.
-    static_assert(C::BM * C::BN * 2 <= C::kLdsBytes, "output tile fits the LDS ring");
-    const int tl = lane & 31, nl = 4 * (lane >> 5);
-    const int64_t tw = m0 + wm * (C::BM / C::WM), nw = n0 + wn * (C::BN / C::WN);
-    const bool int8_part = nout < K;
-    __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-            int64_t t = tw + i * 32 + tl;
-            t = t < T ? t : T - 1;
-            const int tr = wm * (C::BM / C::WM) + i * 32 + tl;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                int64_t n = nw + j * 32 + 8 * g + nl;
-                n = n < N ? n : N - 4;
-                v4f p = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-                if (int8_part)
-                    p = *reinterpret_cast<const v4f *>(ep.d_part + t * N + n);
-                const uint2 bb = ep.bias ? *reinterpret_cast<const uint2 *>(ep.bias + n)
-                                         : make_uint2(0u, 0u);
-                const float bv[4] = {h2f((uint16_t)(bb.x & 0xffffu)), h2f((uint16_t)(bb.x >> 16)),
-                                     h2f((uint16_t)(bb.y & 0xffffu)), h2f((uint16_t)(bb.y >> 16))};
-                uint16_t h[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    h[q] = f2h(acc[i][j][4 * g + q] + p[q] + bv[q]);
-                const int u = (wn * (C::BN / C::WN) + j * 32 + 8 * g + nl) / 4;
-                *reinterpret_cast<uint2 *>(smem + tr * (C::BN * 2) + 8 * (u ^ (tr & 31))) =
-                    make_uint2((unsigned)h[0] | ((unsigned)h[1] << 16),
-                               (unsigned)h[2] | ((unsigned)h[3] << 16));
-            }
-        }
-    }
-    __syncthreads();
-    write_tile<C>(smem, ep, m0, n0, T, N, threadIdx.x);
-}
-
-template <class C>
-__global__ __launch_bounds__(C::kThreads) void k_gemm_outliers(int64_t T, int64_t K, int64_t N,
-                                                               EpilogueArgs ep)
+__global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restrict__ A,
+                                                           const int8_t *__restrict__ B,
+                                                           int64_t T, int64_t K, int64_t N,
+                                                           EpilogueArgs ep)
 {
     const int nout = *ep.n_out;
     if (nout <= kOutlierPad)
@@ -625,22 +612,42 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_outliers(int64_t T, int64_
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int ntm = (int)((T + C::BM - 1) / C::BM), ntn = (int)((N + C::BN - 1) / C::BN);
-    // persistent blocks walk the tiles (the grid is small so that the common
-    // case, an early return, costs little)
-    for (int tile = blockIdx.x; tile < ntm * ntn; tile += gridDim.x) {
-        __builtin_amdgcn_s_barrier();   // the previous tile's LDS reads are done
-        outlier_tile<C>(smem, tile, ntm * ntn, ntm, ntn, T, K, N, nout, ep, wm, wn, wave, lane);
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, ntm, ntn, C::GROUP, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+
+    v16i acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0;
+    if (nout < K) {
+        Streams<C> st;
+        st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
+                n0, N, wave, lane);
+        mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
     }
+    float at[C::FM];
+    const int64_t tw = m0 + wm * (C::BM / C::WM) + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const int64_t t = tw + i * 32;
+        at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
+    }
+    outlier_pass<C>(acc, at, smem, ep, m0, n0, T, K, N, nout, wm, wn, wave, lane, tid);
 }
 
-// C: the int8 GEMM (K must be a multiple of C::ROWB); CO: the fp16 pass over
-// more than 32 outlier columns (whose rows are padded to 128 bytes).
-template <class C, class CO = C>
+// The int8 GEMM (K must be a multiple of C::ROWB) with its fused epilogue;
+// for the output (not the raw int32 sums) also k_gemm_many, of which only
+// one does work, depending on the outlier count on the device.
+template <class C>
 hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
                   const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
                   hipEvent_t ev1 = nullptr)
 {
-    static_assert(CO::BM == C::BM && CO::BN == C::BN, "outlier pass tiling");
     if (K % C::ROWB != 0)
         return hipErrorInvalidValue;
     const int64_t ntm = (T + C::BM - 1) / C::BM, ntn = (N + C::BN - 1) / C::BN;
@@ -659,11 +666,8 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
         if (e != hipSuccess)
             return e;
     }
-    if (!ep.c_i32) {
-        const int64_t blocks = ntm * ntn < kPersistentBlocks ? ntm * ntn : kPersistentBlocks;
-        hipLaunchKernelGGL((k_gemm_outliers<CO>), dim3((unsigned)blocks), dim3(CO::kThreads), 0, s,
-                           T, K, N, ep);
-    }
+    if (!ep.c_i32)
+        hipLaunchKernelGGL((k_gemm_many<C>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K, N, ep);
     return hipGetLastError();
 }
 

@@ -61,7 +61,7 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
 
 // Workspace segments of one llmint8_matmul call (byte offsets from the base).
 struct MatmulWorkspace {
-    size_t partial, mask, colmap, outlier_idx, n_outliers, row_absmax, xq, x_out, w_out, d_part, total;
+    size_t partial, mask, colmap, outlier_idx, n_outliers, row_absmax, xq, x_out, w_out, total;
 };
 MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N);
 size_t act_workspace_bytes(int64_t K);
@@ -118,8 +118,6 @@ struct EpilogueArgs {
     const uint16_t *bias;    // [N] or null
     uint16_t *out;           // [T, N] fp16
     int32_t *c_i32;          // [T, N] raw accumulators (debug epilogue) or null
-    float *d_part;           // [T, N] fp32 scratch for the dequantized int8 part (GEMM path,
-                             // used when more than 32 columns are outliers)
 };
 
 // ev0/ev1 (optional) are recorded on s right before and after the main kernel.

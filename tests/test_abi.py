@@ -61,10 +61,8 @@ def test_workspace_queries(lib, T):
     ws = L.llmint8_workspace_bytes(T, K, N)
     # partial flags (64 row splits x K/8) + mask + colmap + O + n + row scales
     # + Xq (at least 16 rows: the decode path's fragment order) + fp16 outlier
-    # operands (worst case n = K) + the fp32 int8-part buffer used when more
-    # than 32 columns are outliers
-    floor = (8 * K + K // 8 + 8 * K + 4 * T + max(T, 16) * K + 2 * T * K + 2 * N * K
-             + 4 * T * N)
+    # operands (worst case n = K)
+    floor = 8 * K + K // 8 + 8 * K + 4 * T + max(T, 16) * K + 2 * T * K + 2 * N * K
     assert floor <= ws <= floor + 16 * 256
     assert L.llmint8_workspace_bytes(0, K, N) == 0
     assert L.llmint8_quantize_act_workspace_bytes(K) >= 8 * K + K // 8 + 4 * K
