@@ -2,7 +2,9 @@
 
 Flags that matter for results:
   * -fhip-fp32-correctly-rounded-divide-sqrt: the int8 quantization takes
-    round(127*x/a) from one IEEE-correct fp32 division (never a reciprocal);
+    round(127*x/a) through r = 127/a and x*r where that is provably the same
+    rounding, and from one IEEE-correct fp32 division otherwise; both
+    divisions must be correctly rounded;
   * no fast-math;
   * -Xclang -target-feature -Xclang -packed-fp32-ops: no packed fp32 VALU
     instructions are generated.

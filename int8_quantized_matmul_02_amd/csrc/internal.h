@@ -41,6 +41,20 @@ __device__ __forceinline__ int quant127(float x, float a)
     return (int)__builtin_rintf((127.0f * x) / a);
 }
 
+// The same rounding through r = 127/a (one correctly rounded division per
+// row or column): y = x*r is within 2^-22 |z| < 2^-15 of the exact quotient
+// z = 127x/a (two roundings of relative size 2^-24 each, |z| <= 127), so
+// rint(y) is the rounding of z unless y lies within 2^-15 of a half-integer.
+// Returns false there (|y - rint(y)| >= 0.5 - 2^-15; y - rint(y) is exact);
+// the caller then takes quant127, which such values need rarely.
+__device__ __forceinline__ bool quant127_fast(float x, float r, int &q)
+{
+    const float y = x * r;
+    const float f = __builtin_rintf(y);
+    q = (int)f;
+    return __builtin_fabsf(y - f) < 0.499969482421875f;   // 0.5 - 2^-15
+}
+
 // fp16 nearest to cb * scb / 127: the product is exact in fp32 and the fp32
 // quotient of a rational with odd denominator 127 cannot sit on or across a
 // binary16 midpoint, so the two roundings give the singly rounded value.

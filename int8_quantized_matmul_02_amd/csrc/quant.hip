@@ -42,6 +42,28 @@ __device__ __forceinline__ uint16_t half_at(uint4 v, int i)
     return (uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu));
 }
 
+__device__ __forceinline__ uint2 quant8(uint4 v, float amax, float r)
+{
+    // amax > 0 here, r = 127/amax; every value is a non-outlier.  The
+    // reciprocal route settles nearly every chunk; a chunk with a value near
+    // a rounding boundary is redone with divisions.
+    int q[8];
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        ok &= quant127_fast(h2f(half_at(v, i)), r, q[i]);
+    if (!ok) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            q[i] = quant127(h2f(half_at(v, i)), amax);
+    }
+    unsigned packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        packed[i >> 2] |= ((unsigned)q[i] & 0xffu) << (8 * (i & 3));
+    return make_uint2(packed[0], packed[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Weight quantization: one wavefront per output column n (row n of W_t).
 // ---------------------------------------------------------------------------
@@ -62,15 +84,13 @@ __global__ __launch_bounds__(kBlock) void k_quantize_weight(const uint16_t *__re
     m = wave_max_u32(m);
     const float amax = h2f((uint16_t)m);
     uint2 *dst = reinterpret_cast<uint2 *>(CB + n * K);
-    for (int64_t c = lane; c < nchunk; c += kWave) {
-        uint4 v = row[c];
-        unsigned packed[2] = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int q = amax > 0.0f ? quant127(h2f(half_at(v, i)), amax) : 0;
-            packed[i >> 2] |= ((unsigned)q & 0xffu) << (8 * (i & 3));
-        }
-        dst[c] = make_uint2(packed[0], packed[1]);
+    if (amax > 0.0f) {
+        const float r = 127.0f / amax;
+        for (int64_t c = lane; c < nchunk; c += kWave)
+            dst[c] = quant8(row[c], amax, r);
+    } else {
+        for (int64_t c = lane; c < nchunk; c += kWave)
+            dst[c] = make_uint2(0u, 0u);
     }
     if (lane == 0)
         SCB[n] = amax;
@@ -99,13 +119,23 @@ __global__ __launch_bounds__(kBlock) void k_detect(const uint16_t *__restrict__ 
     const int64_t r1 = r0 + rows_per < T ? r0 + rows_per : T;
     unsigned bits = 0;
     if (col8 < nchunk) {
-        for (int64_t t = r0 + rg; t < r1; t += kDetectRowGroups) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(X + t * K + col8 * 8);
-            const unsigned w[4] = {v.x, v.y, v.z, v.w};
+        constexpr int kRowsInFlight = 8;
+        for (int64_t t0 = r0 + rg; t0 < r1; t0 += kRowsInFlight * kDetectRowGroups) {
+            uint4 v[kRowsInFlight];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bits |= (abs_lo(w[i]) > thr_bits ? 1u : 0u) << (2 * i);
-                bits |= (abs_hi(w[i]) > thr_bits ? 1u : 0u) << (2 * i + 1);
+            for (int u = 0; u < kRowsInFlight; ++u) {
+                const int64_t t = t0 + (int64_t)u * kDetectRowGroups;
+                v[u] = t < r1 ? *reinterpret_cast<const uint4 *>(X + t * K + col8 * 8)
+                              : make_uint4(0u, 0u, 0u, 0u);   // |0| is never above
+            }
+#pragma unroll
+            for (int u = 0; u < kRowsInFlight; ++u) {
+                const unsigned w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bits |= (abs_lo(w[i]) > thr_bits ? 1u : 0u) << (2 * i);
+                    bits |= (abs_hi(w[i]) > thr_bits ? 1u : 0u) << (2 * i + 1);
+                }
             }
         }
     }
@@ -217,18 +247,6 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__re
 // stride outlier_ld(n)), zero-padded to a multiple of 32.  Chunks without outlier columns (nearly
 // all of them) take a branch-free path.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint2 quant8(uint4 v, float amax)
-{
-    // amax > 0 here; every value is a non-outlier
-    unsigned packed[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int q = quant127(h2f(half_at(v, i)), amax);
-        packed[i >> 2] |= ((unsigned)q & 0xffu) << (8 * (i & 3));
-    }
-    return make_uint2(packed[0], packed[1]);
-}
-
 // The 8 values of a chunk whose columns are all outliers: they sit at
 // consecutive positions p0 .. p0+7 of the compact row.
 __device__ __forceinline__ void copy8(uint16_t *__restrict__ dst, uint4 v)
@@ -268,12 +286,13 @@ __device__ __forceinline__ uint2 quant8_masked(uint4 v, unsigned fl, float amax,
     return make_uint2(packed[0], packed[1]);
 }
 
-__device__ __forceinline__ void quant_chunk(uint4 v, unsigned fl, float amax, int64_t t, int64_t K,
+__device__ __forceinline__ void quant_chunk(uint4 v, unsigned fl, float amax, float r, int64_t t,
+                                           int64_t K,
                                            int64_t c, const int32_t *__restrict__ colmap,
                                            uint16_t *__restrict__ x_out, int64_t ldo, uint2 *dst)
 {
     if (fl == 0u && amax > 0.0f)
-        *dst = quant8(v, amax);
+        *dst = quant8(v, amax, r);
     else
         *dst = quant8_masked(v, fl, amax, t, K, c, colmap, x_out, ldo);
 }
@@ -301,6 +320,75 @@ __device__ __forceinline__ uint2 *xq_chunk(int8_t *Xq, int64_t t, int64_t K, int
     return reinterpret_cast<uint2 *>(Xq + off);
 }
 
+// Dequantized outlier weight rows for the GEMM, w_out[r, j] = fp16(CB[r, O[j]]
+// * SCB[r] / 127), zero up to outlier_ld(n): blocks gb = 0 .. nb-1 of a
+// launch share the N rows.  Up to 32 outliers (one 32-half row each) a lane
+// takes one 8-column group of one row, 16 rows per wavefront, and computes
+// its at most 8 values directly.  More outliers: one wavefront per row, which
+// first tabulates the row's 255 possible values in LDS (tab, 256 entries of
+// this wavefront); each lane then gathers 8 consecutive outlier columns and
+// stores them at once.  (LDS operations of one wavefront complete in order,
+// so the table is complete before any lane reads it, and the reads of one
+// row are done before the next row's table overwrites it.)  Entries of O at
+// or past n are stale: column 0 is read in their place and the value is 0.
+__device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
+                                             const int32_t *__restrict__ n_out,
+                                             const int8_t *__restrict__ CB,
+                                             const float *__restrict__ SCB,
+                                             const int32_t *__restrict__ O, int64_t N,
+                                             uint16_t *__restrict__ w_out, uint16_t *tab)
+{
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int n = *n_out;
+    const int64_t ldo = outlier_ld(n);
+    if (ldo == kOutlierPad) {
+        constexpr int kGroups = kOutlierPad / 8, kRowsPerWave = kWave / kGroups;
+        const int g = lane % kGroups;
+        int o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = 8 * g + e;   // < 32 <= K: in bounds of O
+            o[e] = j < n ? O[j] : 0;
+        }
+        for (int64_t r = (gb * kWavesPerBlock + wave) * kRowsPerWave + lane / kGroups; r < N;
+             r += nb * kWavesPerBlock * kRowsPerWave) {
+            const float sc = SCB[r];
+            const int8_t *cbr = CB + r * K;
+            unsigned h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const unsigned v = dequant_w(cbr[o[e]], sc);
+                h[e] = 8 * g + e < n ? v : 0u;
+            }
+            *reinterpret_cast<uint4 *>(w_out + r * kOutlierPad + 8 * g) =
+                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                           h[6] | (h[7] << 16));
+        }
+        return;
+    }
+    for (int64_t r = gb * kWavesPerBlock + wave; r < N; r += nb * kWavesPerBlock) {
+        const float sc = SCB[r];
+        for (int i = lane; i < 255; i += kWave)
+            tab[i] = dequant_w(i - 127, sc);
+        const int8_t *cbr = CB + r * K;
+        for (int64_t j0 = 8 * lane; j0 < ldo; j0 += 8 * kWave) {
+            const int4 o0 = *reinterpret_cast<const int4 *>(O + j0);
+            const int4 o1 = *reinterpret_cast<const int4 *>(O + j0 + 4);
+            const int o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+            unsigned h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int oc = j0 + e < n ? o[e] : 0;
+                const unsigned v = tab[(cbr[oc] + 127) & 255];
+                h[e] = j0 + e < n ? v : 0u;
+            }
+            *reinterpret_cast<uint4 *>(w_out + r * ldo + j0) =
+                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                           h[6] | (h[7] << 16));
+        }
+    }
+}
+
 template <int NC>
 __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict__ X, int64_t T,
                                                      int64_t K, const uint8_t *__restrict__ mask,
@@ -318,40 +406,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     __shared__ uint16_t s_tab[kWavesPerBlock][256];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     if ((int64_t)blockIdx.x >= T) {
-        // Extra blocks: dequantized outlier weight rows for the GEMM,
-        // w_out[r, j] = fp16(CB[r, O[j]] * SCB[r] / 127), zero up to a multiple
-        // of 32; one wavefront per weight row.  A row has only 255 possible
-        // values, so the wavefront first tabulates them in LDS; each lane then
-        // gathers 8 consecutive outlier columns and stores them at once.  (LDS
-        // operations of one wavefront complete in order, so the table is
-        // complete before any lane reads it, and the reads of one row are done
-        // before the next row's table overwrites it.)
-        const int n = *n_out;
-        const int64_t ldo = outlier_ld(n);
-        const int64_t gb = (int64_t)blockIdx.x - T, nb = (int64_t)gridDim.x - T;
-        uint16_t *tab = s_tab[wave];
-        for (int64_t r = gb * kWavesPerBlock + wave; r < N; r += nb * kWavesPerBlock) {
-            const float sc = SCB[r];
-            for (int i = lane; i < 255; i += kWave)
-                tab[i] = dequant_w(i - 127, sc);
-            const int8_t *cbr = CB + r * K;
-            for (int64_t j0 = 8 * lane; j0 < ldo; j0 += 8 * kWave) {
-                const int4 o0 = *reinterpret_cast<const int4 *>(O + j0);
-                const int4 o1 = *reinterpret_cast<const int4 *>(O + j0 + 4);
-                const int o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-                unsigned h[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    // entries of O at or past n are stale: read column 0 instead
-                    const int oc = j0 + e < n ? o[e] : 0;
-                    const unsigned v = tab[(cbr[oc] + 127) & 255];
-                    h[e] = j0 + e < n ? v : 0u;
-                }
-                *reinterpret_cast<uint4 *>(w_out + r * ldo + j0) =
-                    make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                               h[6] | (h[7] << 16));
-            }
-        }
+        gather_w_out(blockIdx.x - T, gridDim.x - T, K, n_out, CB, SCB, O, N, w_out, s_tab[wave]);
         return;
     }
     const int64_t t = blockIdx.x;
@@ -384,17 +439,18 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     for (int w = 0; w < kWavesPerBlock; ++w)
         m = umax(m, s_max[w]);
     const float amax = h2f((uint16_t)m);
+    const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
     if constexpr (NC > 0) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             const int64_t c = tid + (int64_t)i * kBlock;
             if (c < nchunk)
-                quant_chunk(v[i], fl[i], amax, t, K, c, colmap, x_out, ldo,
+                quant_chunk(v[i], fl[i], amax, r, t, K, c, colmap, x_out, ldo,
                             xq_chunk(Xq, t, K, c, packed));
         }
     } else {
         for (int64_t c = tid; c < nchunk; c += kBlock)
-            quant_chunk(xr[c], mask[c], amax, t, K, c, colmap, x_out, ldo,
+            quant_chunk(xr[c], mask[c], amax, r, t, K, c, colmap, x_out, ldo,
                         xq_chunk(Xq, t, K, c, packed));
     }
     if (x_out) {
@@ -555,7 +611,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_small(
                     continue;
                 uint2 q;
                 if (fl == 0u && amax[t] > 0.0f) {
-                    q = quant8(v[g][t], amax[t]);
+                    q = quant8(v[g][t], amax[t], 127.0f / amax[t]);
                 } else if (fl == 0xffu) {
                     if (x_out)
                         copy8(x_out + t * ldo + pre, v[g][t]);
@@ -661,14 +717,17 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
                        rows_per, partial);
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, partial, splits, K, mask, O,
                        n_out, colmap);
+    // w_out blocks: one wavefront per row when many columns are outliers; with
+    // up to 32 a block covers 64 rows and the rest exit at once
     int64_t gather_blocks = 0;
     if (g.w_out) {
         gather_blocks = (g.N + kWavesPerBlock - 1) / kWavesPerBlock;
         if (gather_blocks > 2048)
             gather_blocks = 2048;
     }
+    const int64_t nchunk = K / 8;
     const dim3 grid((unsigned)(T + gather_blocks));
-    const int64_t chunks_per_thread = (K / 8 + kBlock - 1) / kBlock;
+    const int64_t chunks_per_thread = (nchunk + kBlock - 1) / kBlock;
 #define LLMINT8_ROWQUANT(NCV)                                                                   \
     hipLaunchKernelGGL(k_rowquant<NCV>, grid, dim3(kBlock), 0, s, X, T, K, mask, colmap, n_out, \
                        Xq, a, x_out, g.CB, g.SCB, O, g.N, g.w_out, xq_packed)

@@ -26,6 +26,7 @@ SHAPES = [
     (129, 512, 384),
     (300, 576, 640),
     (513, 1024, 256),
+    (1030, 320, 320),   # w_out gathered both ways (threshold 6: up to 32 outliers; 0: all)
 ]
 
 
@@ -44,7 +45,8 @@ def test_quantize_weight_exact(N, K):
 # at the limit); the rest, (4, 16448) just past it, the three-kernel chain.
 @pytest.mark.parametrize("T,K", [(1, 64), (16, 256), (100, 320), (513, 1024), (2000, 2048),
                                  (1, 133120), (2, 12288), (3, 1088), (4, 16384), (4, 16448),
-                                 (9, 12288), (16, 16384)])
+                                 (9, 12288), (16, 16384), (1027, 640), (1024, 16384),
+                                 (1024, 16448)])
 @pytest.mark.parametrize("thr", [6.0, 0.0, np.inf, 2.5])
 def test_quantize_act_exact(T, K, thr):
     say("quantize_act T=%d K=%d thr=%s" % (T, K, thr))

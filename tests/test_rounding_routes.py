@@ -1,0 +1,77 @@
+"""The two fp32 routes the HIP kernels use for round(127*x/a), checked on the
+CPU against the oracle's exact rational rounding (ties to even).
+
+* the division route rint((127x)/a) with one correctly rounded fp32 division;
+* the reciprocal route r = 127/a, y = x*r, q = rint(y), taken only where
+  |y - q| < 0.5 - 2^-15 (the kernels fall back to the division elsewhere).
+
+numpy's float32 arithmetic is IEEE round-to-nearest-even, as the GPU's is, so
+these are the kernels' results.  Every binary16 x with |x| <= a is tried for
+a spread of a (special values and a seeded random sample)."""
+import numpy as np
+import pytest
+
+import oracle
+
+HALF_MARGIN = np.float32(0.5 - 2.0 ** -15)
+
+
+def all_x_up_to(a_bits):
+    """Every binary16 bit pattern x with |x| <= a (both signs)."""
+    mag = np.arange(0, int(a_bits) + 1, dtype=np.uint16)
+    return np.concatenate([mag, mag | np.uint16(0x8000)])
+
+
+def special_a():
+    vals = [6.0, 5.3984375, 1.0, 2.0, 0.5, 127.0, 254.0, 3.19921875, 65504.0, 6.1035156e-05,
+            5.9604645e-08, 1.0009766, 0.99951172, 3.0, 255.0, 100.0]
+    return np.array(vals, np.float16).view(np.uint16)
+
+
+def random_a(n, seed=11):
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(1, 0x7c00, n).astype(np.uint16)   # positive finite, nonzero
+    return bits
+
+
+def routes(xb, ab):
+    x = xb.view(np.float16).astype(np.float32)
+    a = np.float32(np.array(ab, np.uint16).view(np.float16))
+    q_div = np.rint((np.float32(127.0) * x) / a)
+    r = np.float32(127.0) / a
+    y = x * r
+    q_rec = np.rint(y)
+    ok = np.abs(y - q_rec) < HALF_MARGIN
+    return q_div.astype(np.int32), q_rec.astype(np.int32), ok
+
+
+@pytest.mark.parametrize("which", ["special", "random"])
+def test_reciprocal_and_division_routes_are_exact(which):
+    a_list = special_a() if which == "special" else random_a(1500)
+    fallback = 0
+    total = 0
+    for ab in a_list:
+        xb = all_x_up_to(ab)
+        exact = oracle.round_127x_over_a(xb, np.full(xb.shape, ab, np.uint16))
+        q_div, q_rec, ok = routes(xb, ab)
+        assert np.array_equal(q_div, exact), "division route, a bits %#x" % ab
+        assert np.array_equal(q_rec[ok], exact[ok]), "reciprocal route, a bits %#x" % ab
+        fallback += int((~ok).sum())
+        total += xb.size
+    # the fallback is rare on these inputs (ties and near-ties only)
+    assert fallback < 0.01 * total
+
+
+def test_reciprocal_route_declines_exact_ties():
+    # 127 * x / a = k + 1/2 exactly: a = 254, x = 1 (0.5), x = 3 (1.5); a = 2, x = 1/127-ish
+    # is not representable, so use a = 254 * 2^j
+    for j in range(-6, 7):
+        a = np.float16(254.0 * 2.0 ** j)
+        xs = np.array([1.0, 3.0, 5.0, 253.0], np.float16) * np.float16(2.0 ** j)
+        xb = xs.view(np.uint16)
+        ab = np.uint16(np.array(a).view(np.uint16))
+        exact = oracle.round_127x_over_a(xb, np.full(xb.shape, ab, np.uint16))
+        q_div, q_rec, ok = routes(xb, ab)
+        assert not ok.any(), "a tie must take the division route"
+        assert np.array_equal(q_div, exact)
+        assert np.array_equal(exact % 2, np.zeros_like(exact)), "ties go to even"
