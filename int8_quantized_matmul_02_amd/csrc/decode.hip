@@ -6,8 +6,9 @@ namespace llmint8 {
 
 // Each wavefront streams 16 weight rows, 512 bytes of each per stage, with
 // three register buffers (two stages in flight); four wavefronts per block.
-// With more than a few activation rows the fragments come from the packed
-// layout (one contiguous KB per k-step instead of 16 row pieces).
+// With two or more activation rows the fragments come from the packed layout
+// (one contiguous KB per k-step instead of up to 16 row pieces) and the
+// block's wavefronts keep in step so that they share each fragment in L1.
 using DecodeRows = decode::CfgRs<512, 4, 3, false>;
 using DecodePacked = decode::CfgRs<512, 4, 3, true>;
 

@@ -151,6 +151,12 @@ struct CfgRs {
     static constexpr int ROWB = ROWB_, WAVES = WAVES_, NB = NB_;
     // activations packed as [K/64][4][16][16]: k-step, 16-byte chunk, row, byte
     static constexpr bool kPackedA = PACKED_A_;
+    // With packed activations every wavefront reads the same 1 KB fragment per
+    // k-step; a barrier per stage keeps a block's wavefronts on the same stage
+    // so that all but the first read it from the L1 cache instead of L2 (at
+    // 16 rows the fragments are otherwise as much L2 traffic as the weights).
+    // Needs every wavefront of a block active: N a multiple of 16 * WAVES.
+    static constexpr bool kSync = PACKED_A_;
     static constexpr int kThreads = 64 * WAVES;
     static constexpr int kStage = 16 * ROWB;            // bytes per wavefront stage
     static constexpr int kRowsPerLoad = 1024 / ROWB;    // rows one 1 KB load instruction covers
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t n0 = ((int64_t)blockIdx.x * C::WAVES + wave) * 16;
     if (n0 >= N)
-        return;   // whole wavefront: N is a multiple of 16
+        return;   // whole wavefront: N is a multiple of 16 (never with kSync)
     const OutlierPrefetch pre = prefetch_outliers<kRawI32>(B, n0 + lane % 16, K, ep);
     char *wl = smem + wave * C::kStage;
     const int8_t *bw = B + n0 * K;
@@ -197,8 +203,19 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
         const int row = m * C::kRowsPerLoad + lrow;
         return row * C::ROWB + 16 * ((lcol / 16) ^ (row & 15));
     };
-    // first k of stage c: the last stage (and any past it) ends at K (K >= ROWB)
-    auto stage_k = [&](int c) { return min(c * C::ROWB, kk - C::ROWB); };
+    // First k of the stage consumed c-th.  Each block takes the stages before
+    // the last in a rotated order, starting at stage blockIdx % (nch - 1):
+    // when every wavefront reads the same k window of its rows (rows K bytes
+    // apart) the requests crowd a few HBM channels, rotated they spread (on
+    // the 12288 x 49152 weight: 71 % -> 80 % of the HBM peak).  The int32
+    // sums do not depend on the order.  The last stage stays last; it ends at
+    // K (K >= ROWB), and so does any stage past it.
+    const int nrot = nch > 1 ? nch - 1 : 1;
+    const int rot = (int)(blockIdx.x % (unsigned)nrot);
+    auto stage_k = [&](int c) {
+        const int p = c >= nch - 1 ? nch - 1 : c + rot < nrot ? c + rot : c + rot - nrot;
+        return min(p * C::ROWB, kk - C::ROWB);
+    };
 
     const v4i zero = v4i{0, 0, 0, 0};
     auto load_b = [&](v4i(&R)[C::kLoads], int c) {
@@ -290,6 +307,8 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
         // the final stage can overlap the one before it
         auto step = [&]<int u, bool kLast>(std::integral_constant<int, u>,
                                            std::bool_constant<kLast>, int cc) {
+            if constexpr (C::kSync)
+                __builtin_amdgcn_s_barrier();
             wait_vm<C::kWait>();
             store_b(R[u % C::NB]);
             __builtin_amdgcn_sched_barrier(0);
@@ -452,6 +471,8 @@ hipError_t launch_rs(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, i
                      const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
                      hipEvent_t ev1 = nullptr)
 {
+    if (C::kSync && N % (16 * C::WAVES) != 0)
+        return hipErrorInvalidValue;   // a block's wavefronts must all reach the barriers
     return launch_kernel<C, RsKernel>(Xq, CB, T, K, N, ep, s, ev0, ev1);
 }
 

@@ -138,8 +138,10 @@ struct EpilogueArgs {
 hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
                        const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr);
-// Activation rows above which the decode path takes Xq in fragment order.
-constexpr int64_t kDecodePackedMinT = 9;
+// Activation rows from which the decode path takes Xq in fragment order
+// (one contiguous KB per k-step, shared by a block's wavefronts through L1);
+// a single row stays row-major (one 64-byte piece per k-step).
+constexpr int64_t kDecodePackedMinT = 2;
 // xq_packed: Xq is in the fragment order written by launch_quantize_act.
 hipError_t launch_decode(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
                          const EpilogueArgs &ep, bool xq_packed, hipStream_t s,
