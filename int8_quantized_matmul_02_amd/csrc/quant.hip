@@ -463,15 +463,14 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
 
 // ---------------------------------------------------------------------------
 // Few rows (T <= 4, the decode regime): the whole quantization in one block,
-// one launch.  Each thread owns 8-column chunks c = tid, tid + 512, ...:
-//   1. it loads its chunks' rows (as many at once as 32 16-byte registers
-//      hold), flags the columns with some |x| above the threshold and keeps
-//      per-row maxima of |x| over the unflagged columns;
-//   2. an LDS tree gives a[t], and a block scan over the chunk flags in
-//      column order gives the ascending outlier list, n and, per chunk, the
-//      number of outlier columns before it;
-//   3. it reloads its chunks (now cache hits), packs the int8 values and
-//      gathers the outlier values into x_out.
+// one launch.  Each thread owns 8-column chunks c = tid, tid + 512, ... and
+// holds them in registers throughout (all of them fit: T*K <= 65536):
+//   1. it loads its chunks' rows, flags the columns with some |x| above the
+//      threshold and keeps per-row maxima of |x| over the unflagged columns;
+//   2. wave reductions and the 8 wave maxima in LDS give a[t], and a block
+//      scan over the chunk flags in column order gives the ascending outlier
+//      list, n and, per chunk, the number of outlier columns before it;
+//   3. it packs the int8 values and gathers the outlier values into x_out.
 // TB >= T bounds the rows in registers.  The tests and the arithmetic are the
 // same as in k_detect / k_compact / k_rowquant, so the results are identical
 // bit for bit.
@@ -480,16 +479,15 @@ constexpr int kSmallThreads = 512;
 constexpr int kSmallMaxT = 4;
 constexpr int kSmallMaxChunks = 133144 / 8;
 
-template <int TB>
+template <int TB, int G>
 __global__ __launch_bounds__(kSmallThreads) void k_quant_small(
     const uint16_t *__restrict__ X, int T, int K, unsigned thr_bits, int8_t *__restrict__ Xq,
     float *__restrict__ a, int32_t *__restrict__ O, int32_t *__restrict__ n_out,
     uint16_t *__restrict__ x_out, bool packed)
 {
-    constexpr int G = TB == 1 ? 16 : 32 / TB;   // chunks loaded at once
     __shared__ uint8_t s_flags[kSmallMaxChunks];
     __shared__ int s_pre[kSmallMaxChunks];
-    __shared__ unsigned s_red[TB][kSmallThreads];
+    __shared__ unsigned s_wmax[TB][kSmallThreads / kWave];
     __shared__ int s_wave_tot[kSmallThreads / kWave];
     __shared__ int s_n;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -500,54 +498,62 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_small(
 #pragma unroll
     for (int t = 0; t < TB; ++t)
         rmax[t] = 0u;
-    for (int c0 = tid; c0 < nchunk; c0 += G * kSmallThreads) {
-        uint4 v[G][TB];
+    // every chunk of the thread at once (the launch picks G with
+    // K/8 <= G * kSmallThreads); the values stay in registers until packed
+    uint4 v[G][TB];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int c = c0 + g * kSmallThreads;
+    for (int g = 0; g < G; ++g) {
+        const int c = tid + g * kSmallThreads;
 #pragma unroll
-            for (int t = 0; t < TB; ++t)
-                v[g][t] = (t < T && c < nchunk)
-                              ? *reinterpret_cast<const uint4 *>(X + (int64_t)t * K + 8 * c)
-                              : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int t = 0; t < TB; ++t)
+            v[g][t] = (t < T && c < nchunk)
+                          ? *reinterpret_cast<const uint4 *>(X + (int64_t)t * K + 8 * c)
+                          : make_uint4(0u, 0u, 0u, 0u);
+    }
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int c = c0 + g * kSmallThreads;
-            unsigned fl = 0;
+    for (int g = 0; g < G; ++g) {
+        const int c = tid + g * kSmallThreads;
+        unsigned fl = 0;
 #pragma unroll
-            for (int t = 0; t < TB; ++t) {
-                const unsigned w[4] = {v[g][t].x, v[g][t].y, v[g][t].z, v[g][t].w};
+        for (int t = 0; t < TB; ++t) {
+            const unsigned w[4] = {v[g][t].x, v[g][t].y, v[g][t].z, v[g][t].w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    fl |= (abs_lo(w[i]) > thr_bits ? 1u : 0u) << (2 * i);
-                    fl |= (abs_hi(w[i]) > thr_bits ? 1u : 0u) << (2 * i + 1);
-                }
+            for (int i = 0; i < 4; ++i) {
+                fl |= (abs_lo(w[i]) > thr_bits ? 1u : 0u) << (2 * i);
+                fl |= (abs_hi(w[i]) > thr_bits ? 1u : 0u) << (2 * i + 1);
             }
-#pragma unroll
-            for (int t = 0; t < TB; ++t)
-                rmax[t] = umax(rmax[t], chunk_absmax_masked(v[g][t], fl));
-            if (c < nchunk)
-                s_flags[c] = (uint8_t)fl;
         }
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+            rmax[t] = umax(rmax[t], chunk_absmax_masked(v[g][t], fl));
+        if (c < nchunk)
+            s_flags[c] = (uint8_t)fl;
     }
 
-    // 2. row scales (LDS tree); outlier list in column order (block scan)
+    // 2. row scales (wave reductions, then the 8 wave maxima through LDS);
+    // outlier list in column order (block scan)
 #pragma unroll
-    for (int t = 0; t < TB; ++t)
-        s_red[t][tid] = rmax[t];
-    __syncthreads();
-#pragma unroll
-    for (int stride = kSmallThreads / 2; stride > 0; stride >>= 1) {
-        if (tid < stride) {
-#pragma unroll
-            for (int t = 0; t < TB; ++t)
-                s_red[t][tid] = umax(s_red[t][tid], s_red[t][tid + stride]);
-        }
-        __syncthreads();
+    for (int t = 0; t < TB; ++t) {
+        const unsigned wm = wave_max_u32(rmax[t]);
+        if (lane == 0)
+            s_wmax[t][wave] = wm;
     }
-    if (tid < T)
-        a[tid] = h2f((uint16_t)s_red[tid][0]);
+    __syncthreads();   // also publishes s_flags
+    unsigned amax_bits[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+        unsigned m = 0;
+#pragma unroll
+        for (int w = 0; w < kSmallThreads / kWave; ++w)
+            m = umax(m, s_wmax[t][w]);
+        amax_bits[t] = m;
+    }
+    if (tid < T) {
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+            if (t == tid)
+                a[tid] = h2f((uint16_t)amax_bits[t]);
+    }
     const int per = (nchunk + kSmallThreads - 1) / kSmallThreads;
     const int b0 = tid * per < nchunk ? tid * per : nchunk;
     const int b1 = b0 + per < nchunk ? b0 + per : nchunk;
@@ -586,54 +592,42 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_small(
     float amax[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t)
-        amax[t] = h2f((uint16_t)s_red[t][0]);
-    for (int c0 = tid; c0 < nchunk; c0 += G * kSmallThreads) {
-        uint4 v[G][TB];
+        amax[t] = h2f((uint16_t)amax_bits[t]);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int c = c0 + g * kSmallThreads;
+    for (int g = 0; g < G; ++g) {
+        const int c = tid + g * kSmallThreads;
+        if (c >= nchunk)
+            continue;
+        const unsigned fl = s_flags[c];
+        const int pre = s_pre[c];
 #pragma unroll
-            for (int t = 0; t < TB; ++t)
-                v[g][t] = (t < T && c < nchunk)
-                              ? *reinterpret_cast<const uint4 *>(X + (int64_t)t * K + 8 * c)
-                              : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int c = c0 + g * kSmallThreads;
-            if (c >= nchunk)
+        for (int t = 0; t < TB; ++t) {
+            if (t >= T)
                 continue;
-            const unsigned fl = s_flags[c];
-            const int pre = s_pre[c];
+            uint2 q;
+            if (fl == 0u && amax[t] > 0.0f) {
+                q = quant8(v[g][t], amax[t], 127.0f / amax[t]);
+            } else if (fl == 0xffu) {
+                if (x_out)
+                    copy8(x_out + t * ldo + pre, v[g][t]);
+                q = make_uint2(0u, 0u);
+            } else {
+                unsigned packed8[2] = {0u, 0u};
 #pragma unroll
-            for (int t = 0; t < TB; ++t) {
-                if (t >= T)
-                    continue;
-                uint2 q;
-                if (fl == 0u && amax[t] > 0.0f) {
-                    q = quant8(v[g][t], amax[t], 127.0f / amax[t]);
-                } else if (fl == 0xffu) {
-                    if (x_out)
-                        copy8(x_out + t * ldo + pre, v[g][t]);
-                    q = make_uint2(0u, 0u);
-                } else {
-                    unsigned packed8[2] = {0u, 0u};
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const uint16_t h = half_at(v[g][t], i);
-                        int qi = 0;
-                        if ((fl >> i) & 1u) {
-                            if (x_out)
-                                x_out[t * ldo + pre + __builtin_popcount(fl & ((1u << i) - 1u))] = h;
-                        } else if (amax[t] > 0.0f) {
-                            qi = quant127(h2f(h), amax[t]);
-                        }
-                        packed8[i >> 2] |= ((unsigned)qi & 0xffu) << (8 * (i & 3));
+                for (int i = 0; i < 8; ++i) {
+                    const uint16_t h = half_at(v[g][t], i);
+                    int qi = 0;
+                    if ((fl >> i) & 1u) {
+                        if (x_out)
+                            x_out[t * ldo + pre + __builtin_popcount(fl & ((1u << i) - 1u))] = h;
+                    } else if (amax[t] > 0.0f) {
+                        qi = quant127(h2f(h), amax[t]);
                     }
-                    q = make_uint2(packed8[0], packed8[1]);
+                    packed8[i >> 2] |= ((unsigned)qi & 0xffu) << (8 * (i & 3));
                 }
-                *xq_chunk(Xq, t, K, c, packed) = q;
+                q = make_uint2(packed8[0], packed8[1]);
             }
+            *xq_chunk(Xq, t, K, c, packed) = q;
         }
     }
     if (x_out) {
@@ -694,13 +688,41 @@ hipError_t launch_quantize_act_one_block(const uint16_t *X, int64_t T, int64_t K
                                          int32_t *n_out, uint16_t *x_out, bool xq_packed,
                                          hipStream_t s)
 {
+    // each thread holds G chunks: K/8 <= G * kSmallThreads, G <= 16 for one
+    // row and <= 8 for up to four (T * K <= kQuantOneBlockMaxElems)
+    if (!quantize_act_fits_one_block(T, K))
+        return hipErrorInvalidValue;
+    const int64_t per = (K / 8 + kSmallThreads - 1) / kSmallThreads;
     const unsigned tb = threshold_bits(threshold);
-    if (T <= 1)
-        hipLaunchKernelGGL(k_quant_small<1>, dim3(1), dim3(kSmallThreads), 0, s, X, (int)T,
-                           (int)K, tb, Xq, a, O, n_out, x_out, xq_packed);
-    else
-        hipLaunchKernelGGL(k_quant_small<kSmallMaxT>, dim3(1), dim3(kSmallThreads), 0, s, X,
-                           (int)T, (int)K, tb, Xq, a, O, n_out, x_out, xq_packed);
+#define LLMINT8_QSMALL(TB, G)                                                                     \
+    hipLaunchKernelGGL((k_quant_small<TB, G>), dim3(1), dim3(kSmallThreads), 0, s, X, (int)T,    \
+                       (int)K, tb, Xq, a, O, n_out, x_out, xq_packed)
+    if (T <= 1) {
+        if (per <= 1)
+            LLMINT8_QSMALL(1, 1);
+        else if (per <= 2)
+            LLMINT8_QSMALL(1, 2);
+        else if (per <= 4)
+            LLMINT8_QSMALL(1, 4);
+        else if (per <= 8)
+            LLMINT8_QSMALL(1, 8);
+        else if (per <= 16)
+            LLMINT8_QSMALL(1, 16);
+        else
+            return hipErrorInvalidValue;
+    } else {
+        if (per <= 1)
+            LLMINT8_QSMALL(kSmallMaxT, 1);
+        else if (per <= 2)
+            LLMINT8_QSMALL(kSmallMaxT, 2);
+        else if (per <= 4)
+            LLMINT8_QSMALL(kSmallMaxT, 4);
+        else if (per <= 8)
+            LLMINT8_QSMALL(kSmallMaxT, 8);
+        else
+            return hipErrorInvalidValue;
+    }
+#undef LLMINT8_QSMALL
     return hipGetLastError();
 }
 
