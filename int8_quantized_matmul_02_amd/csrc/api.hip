@@ -114,9 +114,9 @@ llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, int64_t K, f
     int32_t *colmap = reinterpret_cast<int32_t *>(mask + align256((size_t)K / 8));
     const GatherArgs none{nullptr, nullptr, 0, nullptr};
     hipError_t e =
-        quantize_act_fits_one_block(T, K)
-            ? launch_quantize_act_one_block(X, T, K, threshold, Xq, row_absmax, outlier_idx,
-                                            n_outliers, nullptr, false, stream)
+        quantize_act_fits_rows(T, K)
+            ? launch_quantize_act_rows(X, T, K, threshold, Xq, row_absmax, outlier_idx,
+                                       n_outliers, nullptr, false, stream)
             : launch_quantize_act(X, T, K, threshold, Xq, row_absmax, outlier_idx, n_outliers,
                                   partial, mask, colmap, nullptr, none, false, stream);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
@@ -157,9 +157,8 @@ llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, in
     const GatherArgs g{CB, SCB, N, decode ? nullptr : w_out};
     const bool packed = decode && T >= kDecodePackedMinT;
     const hipError_t eq =
-        decode && quantize_act_fits_one_block(T, K)
-            ? launch_quantize_act_one_block(X, T, K, threshold, Xq, a, O, n_out, x_out, packed,
-                                            stream)
+        decode && quantize_act_fits_rows(T, K)
+            ? launch_quantize_act_rows(X, T, K, threshold, Xq, a, O, n_out, x_out, packed, stream)
             : launch_quantize_act(X, T, K, threshold, Xq, a, O, n_out, partial, mask, colmap,
                                   x_out, g, packed, stream);
     if (eq != hipSuccess)

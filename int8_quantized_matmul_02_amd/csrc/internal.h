@@ -111,16 +111,17 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
                                uint16_t *x_out, const GatherArgs &g, bool xq_packed,
                                hipStream_t s);
 
-// The same quantization for few rows in one block and one launch (no
-// workspace): T <= 4 and T*K <= kQuantOneBlockMaxElems, where one compute
-// unit (reading X twice, one correctly rounded division per value) beats
-// three dependent launches.  Results are identical to launch_quantize_act's.
-constexpr int64_t kQuantOneBlockMaxElems = 4 * 16384;
-bool quantize_act_fits_one_block(int64_t T, int64_t K);
-hipError_t launch_quantize_act_one_block(const uint16_t *X, int64_t T, int64_t K,
-                                         float threshold, int8_t *Xq, float *a, int32_t *O,
-                                         int32_t *n_out, uint16_t *x_out, bool xq_packed,
-                                         hipStream_t s);
+// The same quantization for few rows in one launch of T blocks and without
+// workspace (each block derives the outlier set from all rows itself): one
+// row with K <= kQuantRowsMaxK1, or up to kQuantRowsMaxT rows with
+// K <= kQuantRowsMaxK.  Results are identical to launch_quantize_act's.
+constexpr int64_t kQuantRowsMaxT = 16;
+constexpr int64_t kQuantRowsMaxK = 16384;
+constexpr int64_t kQuantRowsMaxK1 = 65536;
+bool quantize_act_fits_rows(int64_t T, int64_t K);
+hipError_t launch_quantize_act_rows(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                                    int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
+                                    uint16_t *x_out, bool xq_packed, hipStream_t s);
 
 struct EpilogueArgs {
     const float *a;          // [T] row absmax

@@ -462,98 +462,84 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Few rows (T <= 4, the decode regime): the whole quantization in one block,
-// one launch.  Each thread owns 8-column chunks c = tid, tid + 512, ... and
-// holds them in registers throughout (all of them fit: T*K <= 65536):
-//   1. it loads its chunks' rows, flags the columns with some |x| above the
-//      threshold and keeps per-row maxima of |x| over the unflagged columns;
-//   2. wave reductions and the 8 wave maxima in LDS give a[t], and a block
-//      scan over the chunk flags in column order gives the ascending outlier
-//      list, n and, per chunk, the number of outlier columns before it;
-//   3. it packs the int8 values and gathers the outlier values into x_out.
-// TB >= T bounds the rows in registers.  The tests and the arithmetic are the
-// same as in k_detect / k_compact / k_rowquant, so the results are identical
-// bit for bit.
+// Few rows (T <= 16, the decode regime): the whole quantization in one
+// launch of T blocks, block t quantizing row t.  The outlier set depends on
+// every row, and at these sizes each block can afford to read all of X (at
+// most 16 rows x 16384 columns): every block derives the same flags itself,
+// so no partial flags, compaction launch or workspace are needed.  A thread
+// owns the 8-column chunks c = tid, tid + 512, ... (G of them):
+//   1. it loads its chunks of every row, R rows at a time, ORs "some |x|
+//      above the threshold" per column and keeps row t's chunks in registers;
+//   2. a block scan over the chunk flags in column order gives, per chunk,
+//      the number of outlier columns before it and n (block 0 also writes
+//      the ascending outlier list and n);
+//   3. the absmax of row t over the other columns (wave reductions and the 8
+//      wave maxima through LDS), then the packed int8 row and the row's
+//      outlier values in x_out.
+// The tests and the arithmetic are those of k_detect / k_compact /
+// k_rowquant, so the results are identical bit for bit.
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 512;
-constexpr int kSmallMaxT = 4;
-constexpr int kSmallMaxChunks = 133144 / 8;
+constexpr int kSmallMaxChunks = 16 * kSmallThreads;   // G <= 16: K <= 65536
 
-template <int TB, int G>
-__global__ __launch_bounds__(kSmallThreads) void k_quant_small(
+template <int G>
+__global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
     const uint16_t *__restrict__ X, int T, int K, unsigned thr_bits, int8_t *__restrict__ Xq,
     float *__restrict__ a, int32_t *__restrict__ O, int32_t *__restrict__ n_out,
     uint16_t *__restrict__ x_out, bool packed)
 {
+    constexpr int R = G >= 16 ? 1 : 16 / G;   // rows per batch: R*G loads in flight
     __shared__ uint8_t s_flags[kSmallMaxChunks];
     __shared__ int s_pre[kSmallMaxChunks];
-    __shared__ unsigned s_wmax[TB][kSmallThreads / kWave];
+    __shared__ unsigned s_wmax[kSmallThreads / kWave];
     __shared__ int s_wave_tot[kSmallThreads / kWave];
     __shared__ int s_n;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int t = blockIdx.x;
     const int nchunk = K / 8;
 
-    // 1. outlier flags and per-row maxima over the remaining columns
-    unsigned rmax[TB];
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-        rmax[t] = 0u;
-    // every chunk of the thread at once (the launch picks G with
-    // K/8 <= G * kSmallThreads); the values stay in registers until packed
-    uint4 v[G][TB];
+    // 1. column flags over all rows; row t's chunks stay in registers
+    uint4 v[G];
+    unsigned fl[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const int c = tid + g * kSmallThreads;
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-            v[g][t] = (t < T && c < nchunk)
-                          ? *reinterpret_cast<const uint4 *>(X + (int64_t)t * K + 8 * c)
-                          : make_uint4(0u, 0u, 0u, 0u);
+        v[g] = make_uint4(0u, 0u, 0u, 0u);
+        fl[g] = 0u;
     }
+    for (int r0 = 0; r0 < T; r0 += R) {
+        uint4 w[R][G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int c = tid + g * kSmallThreads;
-        unsigned fl = 0;
+        for (int u = 0; u < R; ++u)
 #pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            const unsigned w[4] = {v[g][t].x, v[g][t].y, v[g][t].z, v[g][t].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                fl |= (abs_lo(w[i]) > thr_bits ? 1u : 0u) << (2 * i);
-                fl |= (abs_hi(w[i]) > thr_bits ? 1u : 0u) << (2 * i + 1);
+            for (int g = 0; g < G; ++g) {
+                const int r = r0 + u, c = tid + g * kSmallThreads;
+                w[u][g] = (r < T && c < nchunk)
+                              ? *reinterpret_cast<const uint4 *>(X + (int64_t)r * K + 8 * c)
+                              : make_uint4(0u, 0u, 0u, 0u);   // |0| is never above
             }
-        }
 #pragma unroll
-        for (int t = 0; t < TB; ++t)
-            rmax[t] = umax(rmax[t], chunk_absmax_masked(v[g][t], fl));
+        for (int u = 0; u < R; ++u)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const unsigned x[4] = {w[u][g].x, w[u][g].y, w[u][g].z, w[u][g].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    fl[g] |= (abs_lo(x[i]) > thr_bits ? 1u : 0u) << (2 * i);
+                    fl[g] |= (abs_hi(x[i]) > thr_bits ? 1u : 0u) << (2 * i + 1);
+                }
+                if (r0 + u == t)
+                    v[g] = w[u][g];
+            }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int c = tid + g * kSmallThreads;
         if (c < nchunk)
-            s_flags[c] = (uint8_t)fl;
+            s_flags[c] = (uint8_t)fl[g];
     }
+    __syncthreads();
 
-    // 2. row scales (wave reductions, then the 8 wave maxima through LDS);
-    // outlier list in column order (block scan)
-#pragma unroll
-    for (int t = 0; t < TB; ++t) {
-        const unsigned wm = wave_max_u32(rmax[t]);
-        if (lane == 0)
-            s_wmax[t][wave] = wm;
-    }
-    __syncthreads();   // also publishes s_flags
-    unsigned amax_bits[TB];
-#pragma unroll
-    for (int t = 0; t < TB; ++t) {
-        unsigned m = 0;
-#pragma unroll
-        for (int w = 0; w < kSmallThreads / kWave; ++w)
-            m = umax(m, s_wmax[t][w]);
-        amax_bits[t] = m;
-    }
-    if (tid < T) {
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-            if (t == tid)
-                a[tid] = h2f((uint16_t)amax_bits[t]);
-    }
+    // 2. outlier positions in column order (block scan)
     const int per = (nchunk + kSmallThreads - 1) / kSmallThreads;
     const int b0 = tid * per < nchunk ? tid * per : nchunk;
     const int b1 = b0 + per < nchunk ? b0 + per : nchunk;
@@ -569,71 +555,82 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_small(
     }
     if (lane == kWave - 1)
         s_wave_tot[wave] = inc;
+    // row t's absmax over the non-outlier columns
+    unsigned m = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        m = umax(m, chunk_absmax_masked(v[g], fl[g]));
+    m = wave_max_u32(m);
+    if (lane == 0)
+        s_wmax[wave] = m;
     __syncthreads();
     int j = inc - cnt;
     for (int w = 0; w < wave; ++w)
         j += s_wave_tot[w];
     for (int b = b0; b < b1; ++b) {
-        const unsigned m = s_flags[b];
+        const unsigned mb = s_flags[b];
         s_pre[b] = j;
-        for (int i = 0; i < 8; ++i)
-            if ((m >> i) & 1u)
-                O[j++] = 8 * b + i;
+        if (t == 0) {
+            for (int i = 0; i < 8; ++i)
+                if ((mb >> i) & 1u)
+                    O[j++] = 8 * b + i;
+        } else {
+            j += __builtin_popcount(mb);
+        }
     }
     if (tid == kSmallThreads - 1) {
-        *n_out = j;
+        if (t == 0)
+            *n_out = j;
         s_n = j;
     }
+    unsigned amax_bits = 0;
+#pragma unroll
+    for (int w = 0; w < kSmallThreads / kWave; ++w)
+        amax_bits = umax(amax_bits, s_wmax[w]);
+    const float amax = h2f((uint16_t)amax_bits);
+    if (tid == 0)
+        a[t] = amax;
     __syncthreads();
 
-    // 3. int8 rows and the gathered outlier values
+    // 3. row t: int8 values and the gathered outlier values
     const int n = s_n;
     const int64_t ldo = outlier_ld(n);
-    float amax[TB];
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-        amax[t] = h2f((uint16_t)amax_bits[t]);
+    const float r127 = amax > 0.0f ? 127.0f / amax : 0.0f;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const int c = tid + g * kSmallThreads;
         if (c >= nchunk)
             continue;
-        const unsigned fl = s_flags[c];
+        const unsigned f = fl[g];
         const int pre = s_pre[c];
+        uint2 q;
+        if (f == 0u && amax > 0.0f) {
+            q = quant8(v[g], amax, r127);
+        } else if (f == 0xffu) {
+            if (x_out)
+                copy8(x_out + t * ldo + pre, v[g]);
+            q = make_uint2(0u, 0u);
+        } else {
+            unsigned packed8[2] = {0u, 0u};
 #pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            if (t >= T)
-                continue;
-            uint2 q;
-            if (fl == 0u && amax[t] > 0.0f) {
-                q = quant8(v[g][t], amax[t], 127.0f / amax[t]);
-            } else if (fl == 0xffu) {
-                if (x_out)
-                    copy8(x_out + t * ldo + pre, v[g][t]);
-                q = make_uint2(0u, 0u);
-            } else {
-                unsigned packed8[2] = {0u, 0u};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint16_t h = half_at(v[g][t], i);
-                    int qi = 0;
-                    if ((fl >> i) & 1u) {
-                        if (x_out)
-                            x_out[t * ldo + pre + __builtin_popcount(fl & ((1u << i) - 1u))] = h;
-                    } else if (amax[t] > 0.0f) {
-                        qi = quant127(h2f(h), amax[t]);
-                    }
-                    packed8[i >> 2] |= ((unsigned)qi & 0xffu) << (8 * (i & 3));
+            for (int i = 0; i < 8; ++i) {
+                const uint16_t h = half_at(v[g], i);
+                int qi = 0;
+                if ((f >> i) & 1u) {
+                    if (x_out)
+                        x_out[t * ldo + pre + __builtin_popcount(f & ((1u << i) - 1u))] = h;
+                } else if (amax > 0.0f) {
+                    qi = quant127(h2f(h), amax);
                 }
-                q = make_uint2(packed8[0], packed8[1]);
+                packed8[i >> 2] |= ((unsigned)qi & 0xffu) << (8 * (i & 3));
             }
-            *xq_chunk(Xq, t, K, c, packed) = q;
+            q = make_uint2(packed8[0], packed8[1]);
         }
+        *xq_chunk(Xq, t, K, c, packed) = q;
     }
     if (x_out) {
-        const int padw = (int)ldo - n;
-        for (int idx = tid; idx < T * padw; idx += kSmallThreads)
-            x_out[(idx / padw) * ldo + n + idx % padw] = 0;
+        for (int64_t idx = n + tid; idx < ldo; idx += kSmallThreads)
+            x_out[t * ldo + idx] = 0;
     }
 }
 
@@ -678,51 +675,37 @@ int detect_row_splits(int64_t T, int64_t K)
     return r < 1 ? 1 : (int)r;
 }
 
-bool quantize_act_fits_one_block(int64_t T, int64_t K)
+bool quantize_act_fits_rows(int64_t T, int64_t K)
 {
-    return T <= kSmallMaxT && T * K <= kQuantOneBlockMaxElems;
+    return T == 1 ? K <= kQuantRowsMaxK1 : T <= kQuantRowsMaxT && K <= kQuantRowsMaxK;
 }
 
-hipError_t launch_quantize_act_one_block(const uint16_t *X, int64_t T, int64_t K,
-                                         float threshold, int8_t *Xq, float *a, int32_t *O,
-                                         int32_t *n_out, uint16_t *x_out, bool xq_packed,
-                                         hipStream_t s)
+hipError_t launch_quantize_act_rows(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                                    int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
+                                    uint16_t *x_out, bool xq_packed, hipStream_t s)
 {
-    // each thread holds G chunks: K/8 <= G * kSmallThreads, G <= 16 for one
-    // row and <= 8 for up to four (T * K <= kQuantOneBlockMaxElems)
-    if (!quantize_act_fits_one_block(T, K))
+    if (!quantize_act_fits_rows(T, K))
         return hipErrorInvalidValue;
+    // G chunks per thread: K/8 <= G * kSmallThreads
     const int64_t per = (K / 8 + kSmallThreads - 1) / kSmallThreads;
     const unsigned tb = threshold_bits(threshold);
-#define LLMINT8_QSMALL(TB, G)                                                                     \
-    hipLaunchKernelGGL((k_quant_small<TB, G>), dim3(1), dim3(kSmallThreads), 0, s, X, (int)T,    \
-                       (int)K, tb, Xq, a, O, n_out, x_out, xq_packed)
-    if (T <= 1) {
-        if (per <= 1)
-            LLMINT8_QSMALL(1, 1);
-        else if (per <= 2)
-            LLMINT8_QSMALL(1, 2);
-        else if (per <= 4)
-            LLMINT8_QSMALL(1, 4);
-        else if (per <= 8)
-            LLMINT8_QSMALL(1, 8);
-        else if (per <= 16)
-            LLMINT8_QSMALL(1, 16);
-        else
-            return hipErrorInvalidValue;
-    } else {
-        if (per <= 1)
-            LLMINT8_QSMALL(kSmallMaxT, 1);
-        else if (per <= 2)
-            LLMINT8_QSMALL(kSmallMaxT, 2);
-        else if (per <= 4)
-            LLMINT8_QSMALL(kSmallMaxT, 4);
-        else if (per <= 8)
-            LLMINT8_QSMALL(kSmallMaxT, 8);
-        else
-            return hipErrorInvalidValue;
-    }
-#undef LLMINT8_QSMALL
+    const dim3 grid((unsigned)T);
+#define LLMINT8_QROWS(G)                                                                          \
+    hipLaunchKernelGGL((k_quant_rows<G>), grid, dim3(kSmallThreads), 0, s, X, (int)T, (int)K, tb, \
+                       Xq, a, O, n_out, x_out, xq_packed)
+    if (per <= 1)
+        LLMINT8_QROWS(1);
+    else if (per <= 2)
+        LLMINT8_QROWS(2);
+    else if (per <= 4)
+        LLMINT8_QROWS(4);
+    else if (per <= 8)
+        LLMINT8_QROWS(8);
+    else if (per <= 16)
+        LLMINT8_QROWS(16);
+    else
+        return hipErrorInvalidValue;
+#undef LLMINT8_QROWS
     return hipGetLastError();
 }
 
