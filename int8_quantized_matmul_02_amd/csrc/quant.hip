@@ -36,6 +36,36 @@ __device__ __forceinline__ unsigned chunk_absmax(uint4 v)
     return m;
 }
 
+// Running per-column maximum of |x| over rows, two binary16 columns per
+// 32-bit word (packed 16-bit integer max on the magnitude bit patterns, which
+// order like the magnitudes); a column is an outlier iff its maximum is above
+// the threshold, so the flags are derived once from the maxima.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pk_max_abs(unsigned m, unsigned v)
+{
+    const u16x2 a = __builtin_bit_cast(u16x2, m), b = __builtin_bit_cast(u16x2, v & 0x7fff7fffu);
+    return __builtin_bit_cast(unsigned, __builtin_elementwise_max(a, b));
+}
+
+__device__ __forceinline__ uint4 colmax8(uint4 m, uint4 v)
+{
+    return make_uint4(pk_max_abs(m.x, v.x), pk_max_abs(m.y, v.y), pk_max_abs(m.z, v.z),
+                      pk_max_abs(m.w, v.w));
+}
+
+// Bit i: column i of the chunk has a magnitude above the threshold.
+__device__ __forceinline__ unsigned flags8(uint4 m, unsigned thr_bits)
+{
+    const unsigned w[4] = {m.x, m.y, m.z, m.w};
+    unsigned fl = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fl |= (abs_lo(w[i]) > thr_bits ? 1u : 0u) << (2 * i);
+        fl |= (abs_hi(w[i]) > thr_bits ? 1u : 0u) << (2 * i + 1);
+    }
+    return fl;
+}
+
 __device__ __forceinline__ uint16_t half_at(uint4 v, int i)
 {
     unsigned w = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
@@ -120,6 +150,7 @@ __global__ __launch_bounds__(kBlock) void k_detect(const uint16_t *__restrict__ 
     unsigned bits = 0;
     if (col8 < nchunk) {
         constexpr int kRowsInFlight = 8;
+        uint4 cm = make_uint4(0u, 0u, 0u, 0u);
         for (int64_t t0 = r0 + rg; t0 < r1; t0 += kRowsInFlight * kDetectRowGroups) {
             uint4 v[kRowsInFlight];
 #pragma unroll
@@ -129,15 +160,10 @@ __global__ __launch_bounds__(kBlock) void k_detect(const uint16_t *__restrict__ 
                               : make_uint4(0u, 0u, 0u, 0u);   // |0| is never above
             }
 #pragma unroll
-            for (int u = 0; u < kRowsInFlight; ++u) {
-                const unsigned w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bits |= (abs_lo(w[i]) > thr_bits ? 1u : 0u) << (2 * i);
-                    bits |= (abs_hi(w[i]) > thr_bits ? 1u : 0u) << (2 * i + 1);
-                }
-            }
+            for (int u = 0; u < kRowsInFlight; ++u)
+                cm = colmax8(cm, v[u]);
         }
+        bits = flags8(cm, thr_bits);
     }
     s_bits[rg][c] = (uint8_t)bits;
     __syncthreads();
@@ -468,8 +494,8 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
 // most 16 rows x 16384 columns): every block derives the same flags itself,
 // so no partial flags, compaction launch or workspace are needed.  A thread
 // owns the 8-column chunks c = tid, tid + 512, ... (G of them):
-//   1. it loads its chunks of every row, R rows at a time, ORs "some |x|
-//      above the threshold" per column and keeps row t's chunks in registers;
+//   1. it loads its chunks of every row, R rows at a time, keeps the column
+//      maxima of |x| (the flags follow from them) and row t's chunks;
 //   2. a block scan over the chunk flags in column order gives, per chunk,
 //      the number of outlier columns before it and n (block 0 also writes
 //      the ascending outlier list and n);
@@ -488,7 +514,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
     float *__restrict__ a, int32_t *__restrict__ O, int32_t *__restrict__ n_out,
     uint16_t *__restrict__ x_out, bool packed)
 {
-    constexpr int R = G >= 16 ? 1 : 16 / G;   // rows per batch: R*G loads in flight
+    constexpr int R = G >= 16 ? 1 : 32 / G;   // rows per batch: R*G loads in flight
     __shared__ uint8_t s_flags[kSmallMaxChunks];
     __shared__ int s_pre[kSmallMaxChunks];
     __shared__ unsigned s_wmax[kSmallThreads / kWave];
@@ -499,12 +525,11 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
     const int nchunk = K / 8;
 
     // 1. column flags over all rows; row t's chunks stay in registers
-    uint4 v[G];
-    unsigned fl[G];
+    uint4 v[G], cm[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         v[g] = make_uint4(0u, 0u, 0u, 0u);
-        fl[g] = 0u;
+        cm[g] = make_uint4(0u, 0u, 0u, 0u);
     }
     for (int r0 = 0; r0 < T; r0 += R) {
         uint4 w[R][G];
@@ -521,19 +546,16 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
         for (int u = 0; u < R; ++u)
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const unsigned x[4] = {w[u][g].x, w[u][g].y, w[u][g].z, w[u][g].w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    fl[g] |= (abs_lo(x[i]) > thr_bits ? 1u : 0u) << (2 * i);
-                    fl[g] |= (abs_hi(x[i]) > thr_bits ? 1u : 0u) << (2 * i + 1);
-                }
+                cm[g] = colmax8(cm[g], w[u][g]);
                 if (r0 + u == t)
                     v[g] = w[u][g];
             }
     }
+    unsigned fl[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const int c = tid + g * kSmallThreads;
+        fl[g] = flags8(cm[g], thr_bits);
         if (c < nchunk)
             s_flags[c] = (uint8_t)fl[g];
     }
