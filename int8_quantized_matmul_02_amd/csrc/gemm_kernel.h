@@ -344,31 +344,29 @@ __device__ __forceinline__ void write_tile(const char *smem, const EpilogueArgs 
     }
 }
 
-// Up to 32 outlier columns: their fp16 fragments come straight from L2
-// (rows of 32 halves), and each 32x32 accumulator tile is finished on its
-// own (dequantize, fp16 MFMA over the outlier columns, bias, round) in a few
-// VGPRs and staged in LDS, which every wavefront has stopped reading; then
-// the whole block tile is written out.  Operands come from clamped
-// addresses, the outlier fragments all first and the column scales one
-// column group ahead, so the latency is not paid per tile.
-template <class C, bool kBias>
-__device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], const float (&at)[C::FM],
-                                            char *smem, const EpilogueArgs &ep, int64_t m0,
-                                            int64_t n0, int64_t T, int64_t N, int nout, int wm,
-                                            int wn, int lane, int tid)
+// The fp16 outlier fragments of a tile (up to 32 outlier columns): x_out rows
+// of the tile's T rows and w_out rows of its N columns, two 16-deep k-steps.
+// They do not depend on the GEMM, so k_gemm loads them before its main loop
+// and their latency is not paid in the epilogue.
+template <class C>
+struct OutlierFrags {
+    v4i xo[C::FM][2], wo[C::FN][2];
+};
+template <class C>
+__device__ __forceinline__ void load_outlier_frags(OutlierFrags<C> &f, const EpilogueArgs &ep,
+                                                   int64_t m0, int64_t n0, int64_t T, int64_t N,
+                                                   int nout, int wm, int wn, int lane)
 {
-    static_assert(C::BM * C::BN * 2 <= C::kLdsBytes, "output tile fits the LDS ring");
     const int tl = lane & 31, nl = 4 * (lane >> 5);
     const int64_t tw = m0 + wm * (C::BM / C::WM), nw = n0 + wn * (C::BN / C::WN);
-    v4i xo[C::FM][2], wo[C::FN][2];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
         int64_t t = tw + i * 32 + tl;
         t = t < T ? t : T - 1;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
-            xo[i][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.x_out + t * kOutlierPad + 16 * s2 + nl * 2)
-                                 : v4i{0, 0, 0, 0};
+            f.xo[i][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.x_out + t * kOutlierPad + 16 * s2 + nl * 2)
+                                   : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
@@ -376,9 +374,30 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
         n = n < N ? n : N - 1;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
-            wo[j][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.w_out + n * kOutlierPad + 16 * s2 + nl * 2)
-                                 : v4i{0, 0, 0, 0};
+            f.wo[j][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.w_out + n * kOutlierPad + 16 * s2 + nl * 2)
+                                   : v4i{0, 0, 0, 0};
     }
+}
+
+// Up to 32 outlier columns: their fp16 fragments (loaded before the main
+// loop, rows of 32 halves) go straight into the MFMAs, and each 32x32
+// accumulator tile is finished on its own (dequantize, fp16 MFMA over the
+// outlier columns, bias, round) in a few VGPRs and staged in LDS, which every
+// wavefront has stopped reading; then the whole block tile is written out.
+// Operands come from clamped addresses and the column scales are loaded one
+// column group ahead, so no latency is paid per accumulator tile.
+template <class C, bool kBias>
+__device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], const float (&at)[C::FM],
+                                            const OutlierFrags<C> &of,
+                                            char *smem, const EpilogueArgs &ep, int64_t m0,
+                                            int64_t n0, int64_t T, int64_t N, int nout, int wm,
+                                            int wn, int lane, int tid)
+{
+    static_assert(C::BM * C::BN * 2 <= C::kLdsBytes, "output tile fits the LDS ring");
+    const int tl = lane & 31, nl = 4 * (lane >> 5);
+    const int64_t tw = m0 + wm * (C::BM / C::WM), nw = n0 + wn * (C::BN / C::WN);
+    const auto &xo = of.xo;
+    const auto &wo = of.wo;
     // column scales and bias of column group j, fetched one group ahead
     v4f sn[2][4];
     uint2 bias[2][4];
@@ -535,8 +554,15 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
 
     // More than 32 outlier columns: k_gemm_many computes this output.
-    if (!kRawI32 && *ep.n_out > kOutlierPad)
+    const int nout = kRawI32 ? 0 : *ep.n_out;
+    if (!kRawI32 && nout > kOutlierPad)
         return;
+    // the outlier fragments do not depend on the GEMM: loaded now, they have
+    // landed when the main loop ends (the row scales stay after it: held
+    // through the loop they cost more spills in the epilogue than they save)
+    OutlierFrags<C> of;
+    if constexpr (!kRawI32)
+        load_outlier_frags<C>(of, ep, m0, n0, T, N, nout, wm, wn, lane);
 
     v16i acc[C::FM][C::FN];
 #pragma unroll
@@ -579,7 +605,6 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
                 }
         }
     } else {
-        const int nout = *ep.n_out;
         float at[C::FM];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
@@ -587,9 +612,9 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
             at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
         }
         if (ep.bias)
-            finish_tile<C, true>(acc, at, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
+            finish_tile<C, true>(acc, at, of, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
         else
-            finish_tile<C, false>(acc, at, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
+            finish_tile<C, false>(acc, at, of, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
     }
 }
 
