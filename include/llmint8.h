@@ -30,7 +30,10 @@
  *  - Every call only enqueues work on `stream` (NULL = the default stream)
  *    and returns; it never allocates, frees or synchronizes.  The library
  *    keeps no mutable state, so concurrent calls on different streams with
- *    separate outputs and workspaces are safe.
+ *    separate outputs and workspaces are safe.  The work is kernel launches
+ *    only (no memset, copy or event; the workspace needs no clearing), so a
+ *    call made during stream capture can be replayed from a HIP graph; the
+ *    timing events of llmint8_matmul_path are the one exception.
  *  - Status codes: arguments are checked on the host before anything is
  *    enqueued, in this order: null pointers, non-positive sizes or a NaN /
  *    negative threshold -> LLMINT8_ERR_INVALID_ARG; K or N not a multiple of

@@ -1,0 +1,69 @@
+"""llmint8_matmul under HIP graph capture.
+
+A call enqueues kernels only (no memset, no event, no allocation or host
+synchronization once out and ws are given), so a caller can capture it.  Each
+replay follows eager work of the test's own and a synchronization, and must
+reproduce the eager result bit for bit (the kernels are deterministic); so
+must a replay after new input values are copied into the captured buffer.
+The eager results themselves are checked against the oracle by the parity
+tests."""
+import numpy as np
+import pytest
+import torch
+
+from int8_quantized_matmul_02_amd import llmint8 as L
+from int8_quantized_matmul_02_amd import workloads
+from tests.gpu_helpers import dev, h2d, say
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T,K,N", [(1, 1024, 512), (4, 2048, 256), (16, 1088, 320),
+                                   (300, 512, 512)])
+@pytest.mark.parametrize("thr", [6.0, 0.0])
+def test_matmul_graph_replay(T, K, N, thr):
+    say("graph replay T=%d K=%d N=%d thr=%s" % (T, K, N, thr))
+    d = dev()
+    X, W_t, _ = workloads.case(T, K, N, n_dims=min(6, K // 16), lo=8, hi=60, p=0.5,
+                               seed=11 * T + K + N)
+    X2, _, _ = workloads.case(T, K, N, n_dims=min(6, K // 16), lo=8, hi=60, p=0.5,
+                              seed=11 * T + K + N + 1)
+    CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
+    bias = h2d(np.random.default_rng(5).standard_normal(N).astype(np.float16))
+    Xd = h2d(X)
+    out = torch.empty((T, N), dtype=torch.float16, device=d)
+    ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=d)
+
+    def eager(x):
+        o = torch.empty((T, N), dtype=torch.float16, device=d)
+        w = torch.empty_like(ws)
+        L.llmint8_matmul(x, CB, SCB, thr, bias=bias, out=o, ws=w)
+        torch.cuda.synchronize()
+        return o
+
+    ref = eager(Xd)
+    ref2 = eager(h2d(X2))
+
+    # warm up on a side stream (default priority), then capture
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        L.llmint8_matmul(Xd, CB, SCB, thr, bias=bias, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.llmint8_matmul(Xd, CB, SCB, thr, bias=bias, out=out, ws=ws)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        out.fill_(float("nan"))            # eager work between the replays
+        ws.fill_(0x5a)                     # stale workspace contents must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "replay %d" % rep
+    Xd.copy_(h2d(X2))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref2.view(torch.int16)), "replay on new inputs"
