@@ -41,12 +41,14 @@ def test_quantize_weight_exact(N, K):
     assert_equal_exact(d2h(SCB), SCBr, "SCB")
 
 
-# Few rows take the one-block kernel (T <= 4 and T*K <= 4*16384, (4, 16384)
-# at the limit); the rest, (4, 16448) just past it, the three-kernel chain.
+# Few rows take the one-launch kernel (T = 1 with K <= 65536, (1, 65536) at
+# the limit; T <= 16 with K <= 16384, (4, 16384) and (16, 16384) at it); the
+# rest, (1, 65600), (4, 16448), (16, 16448) and (17, 1024) just past, the
+# three-kernel chain.
 @pytest.mark.parametrize("T,K", [(1, 64), (16, 256), (100, 320), (513, 1024), (2000, 2048),
-                                 (1, 133120), (2, 12288), (3, 1088), (4, 16384), (4, 16448),
-                                 (9, 12288), (16, 16384), (1027, 640), (1024, 16384),
-                                 (1024, 16448)])
+                                 (1, 133120), (1, 65536), (1, 65600), (2, 12288), (3, 1088),
+                                 (4, 16384), (4, 16448), (9, 12288), (16, 16384), (16, 16448),
+                                 (17, 1024), (1027, 640), (1024, 16384), (1024, 16448)])
 @pytest.mark.parametrize("thr", [6.0, 0.0, np.inf, 2.5])
 def test_quantize_act_exact(T, K, thr):
     say("quantize_act T=%d K=%d thr=%s" % (T, K, thr))
@@ -113,8 +115,8 @@ DECODE_K = [64, 448, 512, 576, 1024, 1536, 2048, 2560, 3072, 3584, 4160, 6656]
 @pytest.mark.parametrize("K", DECODE_K)
 def test_decode_path_shapes(T, K):
     """Weight-streaming path across its stage counts; T = 1/2 crosses from
-    row-major to fragment-ordered activations (and the one-launch
-    quantization serves T <= 4)."""
+    row-major to fragment-ordered activations (the one-launch quantization
+    serves all of these shapes)."""
     N = 192
     say("decode shapes T=%d K=%d N=%d" % (T, K, N))
     X, W_t, _ = workloads.case(T, K, N, n_dims=min(6, K // 16), lo=8, hi=60, p=0.5, seed=K + T)
