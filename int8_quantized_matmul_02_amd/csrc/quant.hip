@@ -402,11 +402,22 @@ __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
             const int4 o1 = *reinterpret_cast<const int4 *>(O + j0 + 4);
             const int o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
             unsigned h[8];
+            if (j0 + 8 <= n && o[7] == o[0] + 7 && (o[0] & 7) == 0) {
+                // 8 consecutive outlier columns (every column, at threshold 0):
+                // one 8-byte load of the weight row (8-byte aligned; K % 64 == 0)
+                const uint2 raw = *reinterpret_cast<const uint2 *>(cbr + o[0]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int oc = j0 + e < n ? o[e] : 0;
-                const unsigned v = tab[(cbr[oc] + 127) & 255];
-                h[e] = j0 + e < n ? v : 0u;
+                for (int e = 0; e < 8; ++e) {
+                    const int cb = (int)(int8_t)(((e < 4 ? raw.x : raw.y) >> (8 * (e & 3))) & 0xffu);
+                    h[e] = tab[(cb + 127) & 255];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int oc = j0 + e < n ? o[e] : 0;
+                    const unsigned v = tab[(cbr[oc] + 127) & 255];
+                    h[e] = j0 + e < n ? v : 0u;
+                }
             }
             *reinterpret_cast<uint4 *>(w_out + r * ldo + j0) =
                 make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
