@@ -32,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+FP16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 MFMA, TFLOP/s
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 
 
@@ -178,6 +179,56 @@ def decode_bench(torch, L, workloads, steps, warmup, ev, dev):
     return res
 
 
+def configs_bench(torch, L, workloads, steps, warmup, ev, dev):
+    """The method's other workloads (parity cases), each timed like the main one:
+    the 1.3B up-projection, the fc2-like input (every column an outlier) and
+    the attention-projection sweep (outlier dims n in {0,6,32,128}, threshold
+    0 and inf, T = 4095).  Step figures count 2*T*K*N ops for the whole call;
+    the GEMM kernel's own time is given where k_gemm does the work (up to 32
+    outlier columns)."""
+    res = {}
+
+    def run(name, X_h, W_h, thr):
+        X = torch.from_numpy(X_h).to(dev)
+        W = torch.from_numpy(W_h).to(dev)
+        CB, SCB = L.llmint8_quantize_weight(W)
+        del W
+        T, K = X.shape
+        N = CB.shape[0]
+        out = torch.empty((T, N), dtype=torch.float16, device=dev)
+        ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=dev)
+        n = int(L.llmint8_quantize_act(X, thr)[3].cpu()[0])
+        ms, kms, _ = timed_steps(torch, L, X, [CB], SCB, thr, out, ws, steps, warmup, ev)
+        ops = 2.0 * T * K * N
+        r = {"T": T, "K": K, "N": N, "threshold": thr if np.isfinite(thr) else "inf",
+             "n_outliers": n,
+             "step_us": round(ms * 1e3, 2), "step_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+             "step_frac_int8_peak": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+        if n <= 32:
+            r["gemm_kernel_us"] = round(kms * 1e3, 2)
+            r["gemm_frac_int8_peak"] = round(ops / (kms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
+        if n == K:
+            r["step_frac_fp16_peak"] = round(ops / (ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4)
+        res[name] = r
+        log("config %s: n=%d step %.1f us (%.0f TOP/s)" % (name, n, ms * 1e3, ops / ms / 1e9))
+        del CB, SCB, X, out, ws
+        torch.cuda.empty_cache()
+
+    d = workloads.up_proj_1p3b()
+    run("up_proj_1p3b", d["X"], d["W_t"], 6.0)
+    d = workloads.ffn_6p7b(with_fc2=True)
+    run("ffn_6p7b_fc2", workloads.ffn_6p7b_fc2_input()["X"], d.pop("W2_t"), 6.0)
+    del d
+    W5 = workloads.attn_proj_sweep(0)["W_t"]
+    for nd in (0, 6, 32, 128):
+        run("attn_proj_n%d" % nd, workloads.attn_proj_sweep(nd, with_weight=False)["X"], W5, 6.0)
+    X6 = workloads.attn_proj_sweep(6, with_weight=False)["X"]
+    run("attn_proj_thr0", X6, W5, 0.0)
+    run("attn_proj_thrinf", X6, W5, float("inf"))
+    run("attn_proj_T4095", workloads.attn_proj_sweep(6, T=4095, with_weight=False)["X"], W5, 6.0)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +237,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the CPU-oracle sample (4096 = the whole workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--configs", action="store_true",
+                    help="also time the other workloads (1.3B up-proj, fc2-like, attention sweep)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run one 256 MiB device-to-device copy first (a kernel of known traffic, "
                          "for scaling hardware byte counters)")
@@ -260,6 +313,8 @@ def main():
     result["roofline"].update(spread_us(gemm_kern))
     if not args.no_decode:
         result["decode"] = decode_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
+    if args.configs:
+        result["configs"] = configs_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on %d rows ..." % args.cpu_rows)
         result["cpu_baseline"] = cpu_baseline(X_h, W_h, thr, args.cpu_rows)
