@@ -34,7 +34,7 @@ MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N)
     const size_t t = (size_t)T, k = (size_t)K, n = (size_t)N;
     L.partial = off;     off += align256((size_t)kMaxDetectSplits * (k / 8));
     L.mask = off;        off += align256(k / 8);
-    L.colmap = off;      off += align256(4 * k);
+    L.chunk_pre = off;   off += align256(4 * k);   // K/8 entries used
     L.outlier_idx = off; off += align256(4 * k);
     L.n_outliers = off;  off += 256;
     L.row_absmax = off;  off += align256(4 * t);
@@ -111,14 +111,14 @@ llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, int64_t K, f
     uint8_t *base = static_cast<uint8_t *>(ws);
     uint8_t *partial = base;
     uint8_t *mask = base + align256((size_t)kMaxDetectSplits * ((size_t)K / 8));
-    int32_t *colmap = reinterpret_cast<int32_t *>(mask + align256((size_t)K / 8));
+    int32_t *chunk_pre = reinterpret_cast<int32_t *>(mask + align256((size_t)K / 8));
     const GatherArgs none{nullptr, nullptr, 0, nullptr};
     hipError_t e =
         quantize_act_fits_rows(T, K)
             ? launch_quantize_act_rows(X, T, K, threshold, Xq, row_absmax, outlier_idx,
                                        n_outliers, nullptr, false, stream)
             : launch_quantize_act(X, T, K, threshold, Xq, row_absmax, outlier_idx, n_outliers,
-                                  partial, mask, colmap, nullptr, none, false, stream);
+                                  partial, mask, chunk_pre, nullptr, none, false, stream);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 
@@ -144,7 +144,7 @@ llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, in
     uint8_t *base = static_cast<uint8_t *>(ws);
     uint8_t *partial = base + L.partial;
     uint8_t *mask = base + L.mask;
-    int32_t *colmap = reinterpret_cast<int32_t *>(base + L.colmap);
+    int32_t *chunk_pre = reinterpret_cast<int32_t *>(base + L.chunk_pre);
     int32_t *O = reinterpret_cast<int32_t *>(base + L.outlier_idx);
     int32_t *n_out = reinterpret_cast<int32_t *>(base + L.n_outliers);
     float *a = reinterpret_cast<float *>(base + L.row_absmax);
@@ -159,7 +159,7 @@ llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, in
     const hipError_t eq =
         decode && quantize_act_fits_rows(T, K)
             ? launch_quantize_act_rows(X, T, K, threshold, Xq, a, O, n_out, x_out, packed, stream)
-            : launch_quantize_act(X, T, K, threshold, Xq, a, O, n_out, partial, mask, colmap,
+            : launch_quantize_act(X, T, K, threshold, Xq, a, O, n_out, partial, mask, chunk_pre,
                                   x_out, g, packed, stream);
     if (eq != hipSuccess)
         return LLMINT8_ERR_HIP;

@@ -75,7 +75,7 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
 
 // Workspace segments of one llmint8_matmul call (byte offsets from the base).
 struct MatmulWorkspace {
-    size_t partial, mask, colmap, outlier_idx, n_outliers, row_absmax, xq, x_out, w_out, total;
+    size_t partial, mask, chunk_pre, outlier_idx, n_outliers, row_absmax, xq, x_out, w_out, total;
 };
 MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N);
 size_t act_workspace_bytes(int64_t K);
@@ -107,7 +107,7 @@ int detect_row_splits(int64_t T, int64_t K);
 // are) instead of row-major [T, K].
 hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
                                int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
-                               uint8_t *partial, uint8_t *mask, int32_t *colmap,
+                               uint8_t *partial, uint8_t *mask, int32_t *chunk_pre,
                                uint16_t *x_out, const GatherArgs &g, bool xq_packed,
                                hipStream_t s);
 

@@ -181,7 +181,8 @@ constexpr int kMaxMaskWords = 133144 / 32 + 1;   // K/32 words of mask bits for 
 // One block.  First every thread loads a share of the row-range partials (8
 // bytes at a time, all independent) and ORs the nonzero ones into an LDS
 // bitmask; then mask[b] = OR over row ranges for 8-column chunk b, the
-// ascending outlier list O, its length n, and colmap[k] = position of k in O
+// ascending outlier list O, its length n, and chunk_pre[b] = the number of
+// outlier columns before 8-column chunk b (the position of its first one in O)
 // (or -1).  Each thread owns a contiguous run of chunks so a block-wide
 // exclusive scan of the per-thread counts gives the positions.
 __global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__restrict__ partial,
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__re
                                                              uint8_t *__restrict__ mask,
                                                              int32_t *__restrict__ O,
                                                              int32_t *__restrict__ n_out,
-                                                             int32_t *__restrict__ colmap)
+                                                             int32_t *__restrict__ chunk_pre)
 {
     __shared__ unsigned s_mask[kMaxMaskWords];
     __shared__ int wave_tot[kCompactThreads / kWave];
@@ -247,17 +248,11 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__re
         j += wave_tot[w];
     for (int b = b0; b < b1; ++b) {
         const unsigned m = (s_mask[b / 4] >> (8 * (b % 4))) & 0xffu;
+        chunk_pre[b] = j;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int k = b * 8 + i;
-            if ((m >> i) & 1u) {
-                O[j] = (int32_t)k;
-                colmap[k] = j;
-                ++j;
-            } else {
-                colmap[k] = -1;
-            }
-        }
+        for (int i = 0; i < 8; ++i)
+            if ((m >> i) & 1u)
+                O[j++] = b * 8 + i;
     }
     if (tid == kCompactThreads - 1)
         *n_out = j;
@@ -269,9 +264,10 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__re
 // 16-byte chunks per thread; NC = 0 re-reads it from cache for very long
 // rows), its absmax over the non-outlier columns is reduced with shuffles and
 // LDS, then the int8 row is packed with outlier columns as 0, and the outlier
-// values are gathered into the compact fp16 row x_out[t, colmap[k]] (row
-// stride outlier_ld(n)), zero-padded to a multiple of 32.  Chunks without outlier columns (nearly
-// all of them) take a branch-free path.
+// values are gathered into the compact fp16 row x_out[t, .] (row stride
+// outlier_ld(n), zero-padded): the outlier columns of chunk c start at
+// chunk_pre[c], loaded once per such chunk while the absmax is reduced.
+// Chunks without outlier columns (nearly all of them) take a branch-free path.
 // ---------------------------------------------------------------------------
 // The 8 values of a chunk whose columns are all outliers: they sit at
 // consecutive positions p0 .. p0+7 of the compact row.
@@ -286,14 +282,15 @@ __device__ __forceinline__ void copy8(uint16_t *__restrict__ dst, uint4 v)
     }
 }
 
-__device__ __forceinline__ uint2 quant8_masked(uint4 v, unsigned fl, float amax, int64_t t,
-                                              int64_t K, int64_t c,
-                                              const int32_t *__restrict__ colmap,
-                                              uint16_t *__restrict__ x_out, int64_t ldo)
+// A chunk with outlier columns (flags fl): those are 0 in the int8 row and
+// go to the compact row xrow (null: not gathered) from position pre on, in
+// column order; the others are quantized as usual (amax > 0 then, r = 127/amax).
+__device__ __forceinline__ uint2 quant8_masked(uint4 v, unsigned fl, float amax, float r,
+                                              int pre, uint16_t *__restrict__ xrow)
 {
     if (fl == 0xffu) {
-        if (x_out)
-            copy8(x_out + t * ldo + colmap[c * 8], v);
+        if (xrow)
+            copy8(xrow + pre, v);
         return make_uint2(0u, 0u);
     }
     unsigned packed[2] = {0u, 0u};
@@ -302,25 +299,25 @@ __device__ __forceinline__ uint2 quant8_masked(uint4 v, unsigned fl, float amax,
         const uint16_t h = half_at(v, i);
         int q = 0;
         if ((fl >> i) & 1u) {
-            if (x_out)
-                x_out[t * ldo + colmap[c * 8 + i]] = h;
+            if (xrow)
+                xrow[pre + __builtin_popcount(fl & ((1u << i) - 1u))] = h;
         } else if (amax > 0.0f) {
-            q = quant127(h2f(h), amax);
+            const float x = h2f(h);
+            if (!quant127_fast(x, r, q))
+                q = quant127(x, amax);
         }
         packed[i >> 2] |= ((unsigned)q & 0xffu) << (8 * (i & 3));
     }
     return make_uint2(packed[0], packed[1]);
 }
 
-__device__ __forceinline__ void quant_chunk(uint4 v, unsigned fl, float amax, float r, int64_t t,
-                                           int64_t K,
-                                           int64_t c, const int32_t *__restrict__ colmap,
-                                           uint16_t *__restrict__ x_out, int64_t ldo, uint2 *dst)
+__device__ __forceinline__ void quant_chunk(uint4 v, unsigned fl, float amax, float r, int pre,
+                                           uint16_t *__restrict__ xrow, uint2 *dst)
 {
     if (fl == 0u && amax > 0.0f)
         *dst = quant8(v, amax, r);
     else
-        *dst = quant8_masked(v, fl, amax, t, K, c, colmap, x_out, ldo);
+        *dst = quant8_masked(v, fl, amax, r, pre, xrow);
 }
 
 __device__ __forceinline__ unsigned chunk_absmax_masked(uint4 v, unsigned fl)
@@ -429,7 +426,7 @@ __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
 template <int NC>
 __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict__ X, int64_t T,
                                                      int64_t K, const uint8_t *__restrict__ mask,
-                                                     const int32_t *__restrict__ colmap,
+                                                     const int32_t *__restrict__ chunk_pre,
                                                      const int32_t *__restrict__ n_out,
                                                      int8_t *__restrict__ Xq,
                                                      float *__restrict__ a,
@@ -451,15 +448,22 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     const int nout = x_out ? *n_out : 0;
     const int64_t ldo = outlier_ld(nout);
     const int64_t nchunk = K / 8;
+    uint16_t *xrow = x_out ? x_out + t * ldo : nullptr;
     unsigned m = 0;
     uint4 v[NC > 0 ? NC : 1];
     unsigned fl[NC > 0 ? NC : 1];
+    int pre[NC > 0 ? NC : 1];
     if constexpr (NC > 0) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             const int64_t c = tid + (int64_t)i * kBlock;
             v[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
             fl[i] = c < nchunk ? mask[c] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int64_t c = tid + (int64_t)i * kBlock;
+            pre[i] = (xrow && fl[i] != 0u) ? chunk_pre[c] : 0;   // lands during the reduction
         }
 #pragma unroll
         for (int i = 0; i < NC; ++i)
@@ -482,13 +486,14 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
         for (int i = 0; i < NC; ++i) {
             const int64_t c = tid + (int64_t)i * kBlock;
             if (c < nchunk)
-                quant_chunk(v[i], fl[i], amax, r, t, K, c, colmap, x_out, ldo,
-                            xq_chunk(Xq, t, K, c, packed));
+                quant_chunk(v[i], fl[i], amax, r, pre[i], xrow, xq_chunk(Xq, t, K, c, packed));
         }
     } else {
-        for (int64_t c = tid; c < nchunk; c += kBlock)
-            quant_chunk(xr[c], mask[c], amax, r, t, K, c, colmap, x_out, ldo,
+        for (int64_t c = tid; c < nchunk; c += kBlock) {
+            const unsigned f = mask[c];
+            quant_chunk(xr[c], f, amax, r, (xrow && f != 0u) ? chunk_pre[c] : 0, xrow,
                         xq_chunk(Xq, t, K, c, packed));
+        }
     }
     if (x_out) {
         for (int j = nout + tid; j < ldo; j += kBlock)
@@ -653,7 +658,9 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
                     if (x_out)
                         x_out[t * ldo + pre + __builtin_popcount(f & ((1u << i) - 1u))] = h;
                 } else if (amax > 0.0f) {
-                    qi = quant127(h2f(h), amax);
+                    const float x = h2f(h);
+                    if (!quant127_fast(x, r127, qi))
+                        qi = quant127(x, amax);
                 }
                 packed8[i >> 2] |= ((unsigned)qi & 0xffu) << (8 * (i & 3));
             }
@@ -744,7 +751,7 @@ hipError_t launch_quantize_act_rows(const uint16_t *X, int64_t T, int64_t K, flo
 
 hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
                                int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
-                               uint8_t *partial, uint8_t *mask, int32_t *colmap,
+                               uint8_t *partial, uint8_t *mask, int32_t *chunk_pre,
                                uint16_t *x_out, const GatherArgs &g, bool xq_packed,
                                hipStream_t s)
 {
@@ -754,7 +761,7 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
     hipLaunchKernelGGL(k_detect, det_grid, dim3(kBlock), 0, s, X, T, K, threshold_bits(threshold),
                        rows_per, partial);
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, partial, splits, K, mask, O,
-                       n_out, colmap);
+                       n_out, chunk_pre);
     // w_out blocks: one wavefront per row when many columns are outliers; with
     // up to 32 a block covers 64 rows and the rest exit at once
     int64_t gather_blocks = 0;
@@ -767,7 +774,7 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
     const dim3 grid((unsigned)(T + gather_blocks));
     const int64_t chunks_per_thread = (nchunk + kBlock - 1) / kBlock;
 #define LLMINT8_ROWQUANT(NCV)                                                                   \
-    hipLaunchKernelGGL(k_rowquant<NCV>, grid, dim3(kBlock), 0, s, X, T, K, mask, colmap, n_out, \
+    hipLaunchKernelGGL(k_rowquant<NCV>, grid, dim3(kBlock), 0, s, X, T, K, mask, chunk_pre, n_out, \
                        Xq, a, x_out, g.CB, g.SCB, O, g.N, g.w_out, xq_packed)
     if (chunks_per_thread <= 1)
         LLMINT8_ROWQUANT(1);
