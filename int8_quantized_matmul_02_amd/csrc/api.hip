@@ -32,7 +32,7 @@ MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N)
     MatmulWorkspace L;
     size_t off = 0;
     const size_t t = (size_t)T, k = (size_t)K, n = (size_t)N;
-    L.partial = off;     off += align256((size_t)kMaxDetectSplits * (k / 8));
+    L.partial = off;     off += align256((size_t)kDetectSplits * (k / 8));
     L.mask = off;        off += align256(k / 8);
     L.chunk_pre = off;   off += align256(4 * k);   // K/8 entries used
     L.outlier_idx = off; off += align256(4 * k);
@@ -48,7 +48,7 @@ MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N)
 size_t act_workspace_bytes(int64_t K)
 {
     const size_t k = (size_t)K;
-    return align256((size_t)kMaxDetectSplits * (k / 8)) + align256(k / 8) + align256(4 * k);
+    return align256((size_t)kDetectSplits * (k / 8)) + align256(k / 8) + align256(4 * k);
 }
 
 }  // namespace llmint8
@@ -110,7 +110,7 @@ llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, int64_t K, f
         return LLMINT8_ERR_WORKSPACE;
     uint8_t *base = static_cast<uint8_t *>(ws);
     uint8_t *partial = base;
-    uint8_t *mask = base + align256((size_t)kMaxDetectSplits * ((size_t)K / 8));
+    uint8_t *mask = base + align256((size_t)kDetectSplits * ((size_t)K / 8));
     int32_t *chunk_pre = reinterpret_cast<int32_t *>(mask + align256((size_t)K / 8));
     const GatherArgs none{nullptr, nullptr, 0, nullptr};
     hipError_t e =

@@ -96,20 +96,31 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int ntm, int ntn,
     tn = w / gs;
 }
 
-// One operand pair streamed through the LDS ring: per-lane DMA source offsets
-// (bytes, relative to the tile's first row) for each of this wave's load
-// instructions.
+// One operand pair streamed through the LDS ring.  Each operand is read
+// through a buffer resource based at the tile's first row, so a load
+// instruction takes a constant per-lane 32-bit offset (row * ld + swizzled
+// chunk, fixed for the whole loop) plus the stage's k byte as a scalar
+// offset, and its LDS destination in M0: no per-load address arithmetic.
 template <class C>
 struct Streams {
-    const char *a, *b;              // first row of the tile (row-major, K-contiguous)
+    __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t offA[C::kAInstr], offB[C::kBInstr];
+
+    // Buffer over [base, base + bytes): raw (stride 0) 32-bit words; the
+    // extent is capped at 4 GB - 1 (every offset used stays below it).
+    __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const char *base, int64_t bytes)
+    {
+        const uint32_t n = bytes > 0xffffffffll ? 0xffffffffu : (uint32_t)bytes;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, (int)n,
+                                                 0x00020000);
+    }
 
     __device__ __forceinline__ void init(const char *abase, int64_t lda, int64_t m0, int64_t mrows,
                                          const char *bbase, int64_t ldb, int64_t n0, int64_t nrows,
                                          int wave, int lane)
     {
-        a = abase + m0 * lda;
-        b = bbase + n0 * ldb;
+        ra = rsrc(abase + m0 * lda, (mrows - m0) * lda);
+        rb = rsrc(bbase + n0 * ldb, (nrows - n0) * ldb);
         // lane l fills LDS bytes [16l, 16l+16) of its instruction's KB: row
         // l / kChunks, slot l % kChunks, which holds chunk slot ^ swz(row)
         const int lr = lane / C::kChunks, ls = lane % C::kChunks;
@@ -134,13 +145,13 @@ struct Streams {
         char *sa = smem + stage * C::kStageBytes;
         char *sb = sa + C::BM * C::ROWB;
         if (j < C::kAInstr)
-            __builtin_amdgcn_global_load_lds((const void *)(a + kbyte + offA[j]),
-                                             (lds_void *)(sa + (wave * C::kAInstr + j) * 1024), 16,
-                                             0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_void *)(sa + (wave * C::kAInstr + j) * 1024), 16, offA[j],
+                (uint32_t)kbyte, 0, 0);
         else
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(b + kbyte + offB[j - C::kAInstr]),
-                (lds_void *)(sb + (wave * C::kBInstr + j - C::kAInstr) * 1024), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_void *)(sb + (wave * C::kBInstr + j - C::kAInstr) * 1024), 16,
+                offB[j - C::kAInstr], (uint32_t)kbyte, 0, 0);
     }
 
     __device__ __forceinline__ void issue(char *smem, int stage, int64_t kbyte, int wave) const
@@ -546,7 +557,8 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
                                                       int64_t K, int64_t N, EpilogueArgs ep)
 {
     __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int ntm = (int)((T + C::BM - 1) / C::BM), ntn = (int)((N + C::BN - 1) / C::BN);
     int tm, tn;
@@ -634,7 +646,8 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restr
     if (nout <= kOutlierPad)
         return;
     __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int ntm = (int)((T + C::BM - 1) / C::BM), ntn = (int)((N + C::BN - 1) / C::BN);
     int tm, tn;

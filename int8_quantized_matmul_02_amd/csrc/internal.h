@@ -41,20 +41,6 @@ __device__ __forceinline__ int quant127(float x, float a)
     return (int)__builtin_rintf((127.0f * x) / a);
 }
 
-// The same rounding through r = 127/a (one correctly rounded division per
-// row or column): y = x*r is within 2^-22 |z| < 2^-15 of the exact quotient
-// z = 127x/a (two roundings of relative size 2^-24 each, |z| <= 127), so
-// rint(y) is the rounding of z unless y lies within 2^-15 of a half-integer.
-// Returns false there (|y - rint(y)| >= 0.5 - 2^-15; y - rint(y) is exact);
-// the caller then takes quant127, which such values need rarely.
-__device__ __forceinline__ bool quant127_fast(float x, float r, int &q)
-{
-    const float y = x * r;
-    const float f = __builtin_rintf(y);
-    q = (int)f;
-    return __builtin_fabsf(y - f) < 0.499969482421875f;   // 0.5 - 2^-15
-}
-
 // fp16 nearest to cb * scb / 127: the product is exact in fp32 and the fp32
 // quotient of a rational with odd denominator 127 cannot sit on or across a
 // binary16 midpoint, so the two roundings give the singly rounded value.
@@ -95,10 +81,16 @@ struct GatherArgs {
     uint16_t *w_out;
 };
 
-// Row splits k_detect uses for a [T,K] input (the partial-flag buffer holds
-// splits * K/8 bytes, at most kMaxDetectSplits * K/8).
-constexpr int kMaxDetectSplits = 64;
-int detect_row_splits(int64_t T, int64_t K);
+// Row ranges of the outlier detection: the partial-flag buffer holds
+// kDetectSplits bytes per 8-column chunk (kDetectSplits * K/8 bytes).
+constexpr int kDetectSplits = 16;
+// The row quantization takes a wavefront per row from kRowQuantWaveMinT rows
+// on when the rows are at most kRowQuantWaveMaxK long (measured on MI355X:
+// 15 vs 20 us at 2048 x 2048, equal at 4096 x 4096); otherwise a block of
+// 256 threads per row, which keeps more loads in flight per row for long
+// rows (49 vs 53 us at 4096 x 12288).
+constexpr int64_t kRowQuantWaveMinT = 256;
+constexpr int64_t kRowQuantWaveMaxK = 4096;
 
 // Outlier detection + compaction + row quantization (+ the optional outlier
 // weight gather).  x_out (fp16 [T, outlier_ld(n)]) receives the gathered

@@ -72,26 +72,58 @@ __device__ __forceinline__ uint16_t half_at(uint4 v, int i)
     return (uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu));
 }
 
+// 1.5 * 2^23: for |y| <= 2^22, y + kRoundMagic lands in [2^23, 2^24), where
+// the fp32 spacing is 1, so the addition rounds y to an integer (ties to even,
+// kRoundMagic being even) held in the low mantissa bits:
+// bits(y + kRoundMagic) = bits(kRoundMagic) + rint(y), and its low byte is
+// rint(y) as an int8 in two's complement.
+constexpr float kRoundMagic = 12582912.0f;
+
 __device__ __forceinline__ uint2 quant8(uint4 v, float amax, float r)
 {
-    // amax > 0 here, r = 127/amax; every value is a non-outlier.  The
-    // reciprocal route settles nearly every chunk; a chunk with a value near
-    // a rounding boundary is redone with divisions.
-    int q[8];
-    bool ok = true;
+    // r = 127/amax (0 when amax = 0, and then every value here is 0); |x| <=
+    // amax for every value.  The reciprocal route settles nearly every chunk:
+    // r is one correctly rounded division, so y = x*r is within 2^-22 |z| <
+    // 2^-16 of the exact quotient z = 127x/amax (two roundings of relative
+    // size 2^-24, |z| <= 127), and rint(y) is the rounding of z unless y lies
+    // within 2^-15 of a half-integer (y - rint(y) is exact).  The largest
+    // |y - rint(y)| of the chunk tells; at or above 0.5 - 2^-15 the chunk is
+    // redone with correctly rounded divisions, which such values need rarely.
+    float s[8];
+    float dmax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        ok &= quant127_fast(h2f(half_at(v, i)), r, q[i]);
-    if (!ok) {
+    for (int i = 0; i < 8; ++i) {
+        const float y = h2f(half_at(v, i)) * r;
+        s[i] = y + kRoundMagic;
+        dmax = __builtin_fmaxf(dmax, __builtin_fabsf(y - (s[i] - kRoundMagic)));
+    }
+    if (!(dmax < 0.499969482421875f)) {   // 0.5 - 2^-15
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            q[i] = quant127(h2f(half_at(v, i)), amax);
+            s[i] = (float)quant127(h2f(half_at(v, i)), amax) + kRoundMagic;
     }
-    unsigned packed[2] = {0u, 0u};
+    unsigned b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        packed[i >> 2] |= ((unsigned)q[i] & 0xffu) << (8 * (i & 3));
-    return make_uint2(packed[0], packed[1]);
+        b[i] = __builtin_bit_cast(unsigned, s[i]);
+    // low bytes: perm selector 0..3 picks a byte of the second operand, 4..7
+    // of the first, 0x0c gives 0
+    const unsigned lo0 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+    const unsigned hi0 = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+    const unsigned lo1 = __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u);
+    const unsigned hi1 = __builtin_amdgcn_perm(b[7], b[6], 0x04000c0cu);
+    return make_uint2(lo0 | hi0, lo1 | hi1);
+}
+
+// v with the halves whose flag bit is set replaced by +0.
+__device__ __forceinline__ uint4 drop_flagged(uint4 v, unsigned fl)
+{
+    unsigned k[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        k[i] = (((fl >> (2 * i)) & 1u) ? 0u : 0x0000ffffu) |
+               (((fl >> (2 * i + 1)) & 1u) ? 0u : 0xffff0000u);
+    return make_uint4(v.x & k[0], v.y & k[1], v.z & k[2], v.w & k[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -128,20 +160,25 @@ __global__ __launch_bounds__(kBlock) void k_quantize_weight(const uint16_t *__re
 
 // ---------------------------------------------------------------------------
 // Outlier-column detection, in two launches and without atomics or a
-// clearing pass: k_detect ORs "some |x| > threshold" over a range of rows
-// for 8 columns per lane and writes one bit per column for its row range
-// (every partial byte is written); k_compact ORs the row ranges together.
+// clearing pass.  k_detect splits the rows into kDetectSplits ranges; a lane
+// keeps the running column maxima of |x| of 8 columns over its rows, the
+// flags "maximum above the threshold" are ORed over the block's row groups
+// and written as byte partial[chunk * kDetectSplits + split] (every byte is
+// written, also for empty ranges).  k_compact ORs the 16 bytes of a chunk.
 // The comparison |x| > threshold is done on binary16 bit patterns against the
 // largest binary16 value not above the threshold (computed on the host), which
 // is the same test as comparing the exact values.
 // ---------------------------------------------------------------------------
-constexpr int kDetectRowGroups = kBlock / 32; // row groups per block
+constexpr int kDetectThreads = 1024;
+constexpr int kDetectRowGroups = kDetectThreads / 32;   // 32 lanes (chunks) per row group
 
-__global__ __launch_bounds__(kBlock) void k_detect(const uint16_t *__restrict__ X, int64_t T,
-                                                   int64_t K, unsigned thr_bits, int rows_per,
-                                                   uint8_t *__restrict__ partial)
+__global__ __launch_bounds__(kDetectThreads) void k_detect(const uint16_t *__restrict__ X,
+                                                           int64_t T, int64_t K,
+                                                           unsigned thr_bits, int64_t rows_per,
+                                                           uint8_t *__restrict__ partial)
 {
-    __shared__ uint8_t s_bits[kDetectRowGroups][32];
+    // byte rg of chunk lane c at s_bits[c * kDetectRowGroups + rg]
+    __shared__ unsigned s_bits[32 * kDetectRowGroups / 4];
     const int c = threadIdx.x & 31, rg = threadIdx.x >> 5;
     const int64_t col8 = (int64_t)blockIdx.x * 32 + c;    // 8-column chunk
     const int64_t nchunk = K / 8;
@@ -165,62 +202,64 @@ __global__ __launch_bounds__(kBlock) void k_detect(const uint16_t *__restrict__ 
         }
         bits = flags8(cm, thr_bits);
     }
-    s_bits[rg][c] = (uint8_t)bits;
+    reinterpret_cast<uint8_t *>(s_bits)[c * kDetectRowGroups + rg] = (uint8_t)bits;
     __syncthreads();
     if (rg == 0 && col8 < nchunk) {
+        unsigned o = 0;
 #pragma unroll
-        for (int g = 1; g < kDetectRowGroups; ++g)
-            bits |= s_bits[g][c];
-        partial[blockIdx.y * nchunk + col8] = (uint8_t)bits;
+        for (int w = 0; w < kDetectRowGroups / 4; ++w)
+            o |= s_bits[c * (kDetectRowGroups / 4) + w];
+        o |= o >> 16;
+        o |= o >> 8;
+        partial[col8 * kDetectSplits + blockIdx.y] = (uint8_t)(o & 0xffu);
     }
 }
 
-constexpr int kCompactThreads = 1024;
-constexpr int kMaxMaskWords = 133144 / 32 + 1;   // K/32 words of mask bits for the largest K
+// The OR of a chunk's kDetectSplits partial bytes: its 8 outlier flags.
+__device__ __forceinline__ unsigned chunk_flags(const uint8_t *__restrict__ partial, int64_t c)
+{
+    static_assert(kDetectSplits == 16, "one 16-byte load per chunk");
+    const uint4 p = *reinterpret_cast<const uint4 *>(partial + c * kDetectSplits);
+    unsigned o = p.x | p.y | p.z | p.w;
+    o |= o >> 16;
+    o |= o >> 8;
+    return o & 0xffu;
+}
 
-// One block.  First every thread loads a share of the row-range partials (8
-// bytes at a time, all independent) and ORs the nonzero ones into an LDS
-// bitmask; then mask[b] = OR over row ranges for 8-column chunk b, the
-// ascending outlier list O, its length n, and chunk_pre[b] = the number of
-// outlier columns before 8-column chunk b (the position of its first one in O)
-// (or -1).  Each thread owns a contiguous run of chunks so a block-wide
-// exclusive scan of the per-thread counts gives the positions.
+constexpr int kCompactThreads = 1024;
+constexpr int kMaxChunks = 133144 / 8 + 1;   // K/8 for the largest K
+
+// One block.  Every thread ORs the partial bytes of its chunks (one 16-byte
+// load each, all independent) into an LDS flag byte; then mask[b] = the flags
+// of 8-column chunk b, the ascending outlier list O, its length n, and
+// chunk_pre[b] = the number of outlier columns before chunk b (the position
+// of its first one in O).  Each thread owns a contiguous run of chunks so a
+// block-wide exclusive scan of the per-thread counts gives the positions.
 __global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__restrict__ partial,
-                                                             int splits, int64_t K,
+                                                             int64_t K,
                                                              uint8_t *__restrict__ mask,
                                                              int32_t *__restrict__ O,
                                                              int32_t *__restrict__ n_out,
                                                              int32_t *__restrict__ chunk_pre)
 {
-    __shared__ unsigned s_mask[kMaxMaskWords];
+    __shared__ uint8_t s_fl[kMaxChunks];
     __shared__ int wave_tot[kCompactThreads / kWave];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     // 32-bit indexing: K <= 133144 keeps every count here far below 2^31
-    const int nchunk = (int)(K / 8);         // mask bytes; a multiple of 8 since K % 64 == 0
-    const int nvec = nchunk / 8;             // 8-byte vectors per row range
-    const int nwords = nchunk / 4;
-    for (int w = tid; w < nwords; w += kCompactThreads)
-        s_mask[w] = 0u;
-    __syncthreads();
-    const int items = nvec * splits;
-    constexpr int kBatch = 8;   // independent loads in flight per thread
-    for (int base = tid; base < items; base += kBatch * kCompactThreads) {
-        uint2 x[kBatch];
-        int vv[kBatch];
+    const int nchunk = (int)(K / 8);
+    constexpr int kBatch = 4;   // independent loads in flight per thread
+    for (int base = tid; base < nchunk; base += kBatch * kCompactThreads) {
+        unsigned f[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int it = base + u * kCompactThreads;
-            const int r = it / nvec;
-            vv[u] = it - r * nvec;
-            x[u] = it < items ? *reinterpret_cast<const uint2 *>(partial + r * nchunk + vv[u] * 8)
-                              : make_uint2(0u, 0u);
+            const int c = base + u * kCompactThreads;
+            f[u] = c < nchunk ? chunk_flags(partial, c) : 0u;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            if (x[u].x)
-                atomicOr(&s_mask[2 * vv[u]], x[u].x);
-            if (x[u].y)
-                atomicOr(&s_mask[2 * vv[u] + 1], x[u].y);
+            const int c = base + u * kCompactThreads;
+            if (c < nchunk)
+                s_fl[c] = (uint8_t)f[u];
         }
     }
     __syncthreads();
@@ -229,7 +268,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__re
     const int b1 = b0 + per < nchunk ? b0 + per : nchunk;
     int cnt = 0;
     for (int b = b0; b < b1; ++b) {
-        const unsigned m = (s_mask[b / 4] >> (8 * (b % 4))) & 0xffu;
+        const unsigned m = s_fl[b];
         mask[b] = (uint8_t)m;
         cnt += __builtin_popcount(m);
     }
@@ -247,7 +286,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__re
     for (int w = 0; w < wave; ++w)
         j += wave_tot[w];
     for (int b = b0; b < b1; ++b) {
-        const unsigned m = (s_mask[b / 4] >> (8 * (b % 4))) & 0xffu;
+        const unsigned m = s_fl[b];
         chunk_pre[b] = j;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -282,54 +321,38 @@ __device__ __forceinline__ void copy8(uint16_t *__restrict__ dst, uint4 v)
     }
 }
 
-// A chunk with outlier columns (flags fl): those are 0 in the int8 row and
-// go to the compact row xrow (null: not gathered) from position pre on, in
-// column order; the others are quantized as usual (amax > 0 then, r = 127/amax).
-__device__ __forceinline__ uint2 quant8_masked(uint4 v, unsigned fl, float amax, float r,
-                                              int pre, uint16_t *__restrict__ xrow)
+// The outlier values of one chunk (flags fl != 0) into the compact row xrow,
+// from position pre on in column order.
+__device__ __forceinline__ void scatter_outliers(uint4 v, unsigned fl, int pre,
+                                                 uint16_t *__restrict__ xrow)
 {
     if (fl == 0xffu) {
-        if (xrow)
-            copy8(xrow + pre, v);
-        return make_uint2(0u, 0u);
+        copy8(xrow + pre, v);
+        return;
     }
-    unsigned packed[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint16_t h = half_at(v, i);
-        int q = 0;
-        if ((fl >> i) & 1u) {
-            if (xrow)
-                xrow[pre + __builtin_popcount(fl & ((1u << i) - 1u))] = h;
-        } else if (amax > 0.0f) {
-            const float x = h2f(h);
-            if (!quant127_fast(x, r, q))
-                q = quant127(x, amax);
-        }
-        packed[i >> 2] |= ((unsigned)q & 0xffu) << (8 * (i & 3));
-    }
-    return make_uint2(packed[0], packed[1]);
+    for (int i = 0; i < 8; ++i)
+        if ((fl >> i) & 1u)
+            xrow[pre + __builtin_popcount(fl & ((1u << i) - 1u))] = half_at(v, i);
 }
 
+// One chunk of a row: outlier columns (flags fl) are 0 in the int8 row and go
+// to the compact row xrow (null: not gathered) from position pre on; the
+// others are quantized (r = 127/amax, or 0 when amax = 0).
 __device__ __forceinline__ void quant_chunk(uint4 v, unsigned fl, float amax, float r, int pre,
                                            uint16_t *__restrict__ xrow, uint2 *dst)
 {
-    if (fl == 0u && amax > 0.0f)
-        *dst = quant8(v, amax, r);
-    else
-        *dst = quant8_masked(v, fl, amax, r, pre, xrow);
+    if (fl) {
+        if (xrow)
+            scatter_outliers(v, fl, pre, xrow);
+        v = drop_flagged(v, fl);
+    }
+    *dst = quant8(v, amax, r);
 }
 
 __device__ __forceinline__ unsigned chunk_absmax_masked(uint4 v, unsigned fl)
 {
-    if (fl == 0u)
-        return chunk_absmax(v);
-    unsigned m = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        if (!((fl >> i) & 1u))
-            m = umax(m, half_at(v, i) & 0x7fffu);
-    return m;
+    return chunk_absmax(fl ? drop_flagged(v, fl) : v);
 }
 
 // Destination of the 8 int8 values k = 8c .. 8c+7 of row t.  Row-major
@@ -504,6 +527,108 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Row quantization for many short rows: one wavefront per row, four rows per
+// block, the row held in registers (NC 16-byte chunks per lane, chunk
+// c = lane + 64 i, so every load instruction reads 1 KB of the row).  The
+// absmax is a wave reduction (no LDS, no block barrier), outlier columns are
+// zeroed before the absmax and the pack, so chunks with and without outliers
+// take the same arithmetic, and the outlier values go to the compact row of
+// x_out at positions from a wavefront prefix count of the flags (ballots), so
+// no per-chunk position table is read.  Extra blocks build w_out as
+// k_rowquant's.
+// ---------------------------------------------------------------------------
+// Outlier columns before this lane's chunk within one 64-chunk step of a
+// wavefront (lanes below it), and in the whole step: per flag bit, a ballot
+// and its masked population count.
+__device__ __forceinline__ void step_prefix(unsigned fl, uint64_t below, int &pre, int &tot)
+{
+    pre = 0;
+    tot = 0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const uint64_t m = __ballot((fl >> b) & 1u);
+        pre += __popcll(m & below);
+        tot += __popcll(m);
+    }
+}
+
+template <int NC>
+__global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restrict__ X, int64_t T,
+                                                       int64_t K, const uint8_t *__restrict__ mask,
+                                                       const int32_t *__restrict__ n_out,
+                                                       int8_t *__restrict__ Xq,
+                                                       float *__restrict__ a,
+                                                       uint16_t *__restrict__ x_out,
+                                                       const int8_t *__restrict__ CB,
+                                                       const float *__restrict__ SCB,
+                                                       const int32_t *__restrict__ O, int64_t N,
+                                                       uint16_t *__restrict__ w_out,
+                                                       int64_t row_blocks)
+{
+    __shared__ uint16_t s_tab[kWavesPerBlock][256];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    if ((int64_t)blockIdx.x >= row_blocks) {
+        gather_w_out(blockIdx.x - row_blocks, gridDim.x - row_blocks, K, n_out, CB, SCB, O, N,
+                     w_out, s_tab[wave]);
+        return;
+    }
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (t >= T)
+        return;
+    const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
+    uint2 *qr = reinterpret_cast<uint2 *>(Xq + t * K);
+    const int64_t nchunk = K / 8;
+    const int nout = x_out ? *n_out : 0;
+    const int64_t ldo = outlier_ld(nout);
+    uint16_t *xrow = x_out ? x_out + t * ldo : nullptr;
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint4 v[NC];
+    unsigned fl[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int64_t c = lane + (int64_t)i * kWave;
+        v[i] = c < nchunk ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+        fl[i] = c < nchunk ? mask[c] : 0u;
+    }
+    // the outlier values first, then they are zeroed in place
+    if (xrow && nout > 0) {
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            if (__ballot(fl[i] != 0u) == 0ull)
+                continue;
+            int pre, tot;
+            step_prefix(fl[i], below, pre, tot);
+            if (fl[i])
+                scatter_outliers(v[i], fl[i], base + pre, xrow);
+            base += tot;
+        }
+    }
+    unsigned m = 0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        if (fl[i])
+            v[i] = drop_flagged(v[i], fl[i]);
+        m = umax(m, chunk_absmax(v[i]));
+    }
+    m = wave_max_u32(m);
+    const float amax = h2f((uint16_t)m);
+    const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int64_t c = lane + (int64_t)i * kWave;
+        if (c < nchunk)
+            qr[c] = quant8(v[i], amax, r);
+    }
+    if (xrow) {
+        for (int64_t j = nout + lane; j < ldo; j += kWave)
+            xrow[j] = 0;
+    }
+    if (lane == 0)
+        a[t] = amax;
+}
+
+// ---------------------------------------------------------------------------
 // Few rows (T <= 16, the decode regime): the whole quantization in one
 // launch of T blocks, block t quantizing row t.  The outlier set depends on
 // every row, and at these sizes each block can afford to read all of X (at
@@ -640,32 +765,13 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
         if (c >= nchunk)
             continue;
         const unsigned f = fl[g];
-        const int pre = s_pre[c];
-        uint2 q;
-        if (f == 0u && amax > 0.0f) {
-            q = quant8(v[g], amax, r127);
-        } else if (f == 0xffu) {
+        uint4 x = v[g];
+        if (f) {
             if (x_out)
-                copy8(x_out + t * ldo + pre, v[g]);
-            q = make_uint2(0u, 0u);
-        } else {
-            unsigned packed8[2] = {0u, 0u};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint16_t h = half_at(v[g], i);
-                int qi = 0;
-                if ((f >> i) & 1u) {
-                    if (x_out)
-                        x_out[t * ldo + pre + __builtin_popcount(f & ((1u << i) - 1u))] = h;
-                } else if (amax > 0.0f) {
-                    const float x = h2f(h);
-                    if (!quant127_fast(x, r127, qi))
-                        qi = quant127(x, amax);
-                }
-                packed8[i >> 2] |= ((unsigned)qi & 0xffu) << (8 * (i & 3));
-            }
-            q = make_uint2(packed8[0], packed8[1]);
+                scatter_outliers(x, f, s_pre[c], x_out + t * ldo);
+            x = drop_flagged(x, f);
         }
+        const uint2 q = quant8(x, amax, r127);
         *xq_chunk(Xq, t, K, c, packed) = q;
     }
     if (x_out) {
@@ -701,18 +807,6 @@ hipError_t launch_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N, int
     hipLaunchKernelGGL(k_quantize_weight, dim3((unsigned)blocks), dim3(kBlock), 0, s, W_t, K, N,
                        CB, SCB);
     return hipGetLastError();
-}
-
-int detect_row_splits(int64_t T, int64_t K)
-{
-    const int64_t col_blocks = (K / 8 + 31) / 32;
-    int64_t r = (2048 + col_blocks - 1) / col_blocks;
-    const int64_t by_rows = (T + kDetectRowGroups - 1) / kDetectRowGroups;
-    if (r > by_rows)
-        r = by_rows;
-    if (r > kMaxDetectSplits)
-        r = kMaxDetectSplits;
-    return r < 1 ? 1 : (int)r;
 }
 
 bool quantize_act_fits_rows(int64_t T, int64_t K)
@@ -755,13 +849,15 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
                                uint16_t *x_out, const GatherArgs &g, bool xq_packed,
                                hipStream_t s)
 {
-    const int splits = detect_row_splits(T, K);
-    const int rows_per = (int)((T + splits - 1) / splits);
-    const dim3 det_grid((unsigned)((K / 8 + 31) / 32), (unsigned)splits);
-    hipLaunchKernelGGL(k_detect, det_grid, dim3(kBlock), 0, s, X, T, K, threshold_bits(threshold),
-                       rows_per, partial);
-    hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, partial, splits, K, mask, O,
-                       n_out, chunk_pre);
+    if (xq_packed && T > 16)
+        return hipErrorInvalidValue;
+    const int64_t nchunk = K / 8;
+    const int64_t rows_per = (T + kDetectSplits - 1) / kDetectSplits;
+    const dim3 det_grid((unsigned)((nchunk + 31) / 32), (unsigned)kDetectSplits);
+    hipLaunchKernelGGL(k_detect, det_grid, dim3(kDetectThreads), 0, s, X, T, K,
+                       threshold_bits(threshold), rows_per, partial);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, partial, K, mask, O, n_out,
+                       chunk_pre);
     // w_out blocks: one wavefront per row when many columns are outliers; with
     // up to 32 a block covers 64 rows and the rest exit at once
     int64_t gather_blocks = 0;
@@ -770,7 +866,25 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
         if (gather_blocks > 2048)
             gather_blocks = 2048;
     }
-    const int64_t nchunk = K / 8;
+    if (T >= kRowQuantWaveMinT && K <= kRowQuantWaveMaxK) {
+        // a wavefront per row, the row in NC chunks per lane
+        const int64_t per = (nchunk + kWave - 1) / kWave;
+        const int64_t row_blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+        const dim3 grid((unsigned)(row_blocks + gather_blocks));
+#define LLMINT8_ROWQUANT_W(NCV)                                                                  \
+    hipLaunchKernelGGL(k_rowquant_w<NCV>, grid, dim3(kBlock), 0, s, X, T, K, mask, n_out, Xq, a, \
+                       x_out, g.CB, g.SCB, O, g.N, g.w_out, row_blocks)
+        static_assert(kRowQuantWaveMaxK / 8 <= 8 * kWave, "rows of at most 8 chunks per lane");
+        if (per <= 2)
+            LLMINT8_ROWQUANT_W(2);
+        else if (per <= 4)
+            LLMINT8_ROWQUANT_W(4);
+        else
+            LLMINT8_ROWQUANT_W(8);
+#undef LLMINT8_ROWQUANT_W
+        return hipGetLastError();
+    }
+    // fewer rows: a block per row keeps more lanes busy
     const dim3 grid((unsigned)(T + gather_blocks));
     const int64_t chunks_per_thread = (nchunk + kBlock - 1) / kBlock;
 #define LLMINT8_ROWQUANT(NCV)                                                                   \

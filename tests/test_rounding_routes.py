@@ -3,7 +3,11 @@ CPU against the oracle's exact rational rounding (ties to even).
 
 * the division route rint((127x)/a) with one correctly rounded fp32 division;
 * the reciprocal route r = 127/a, y = x*r, q = rint(y), taken only where
-  |y - q| < 0.5 - 2^-15 (the kernels fall back to the division elsewhere).
+  |y - q| < 0.5 - 2^-15 (the kernels fall back to the division elsewhere);
+* the same route with the product fused into the rounding and the residual
+  (hipcc contracts x*r + 1.5*2^23 and x*r - q into fused multiply-adds):
+  q = rint of the exact product p = x*r, accepted where fp32(p - q) is below
+  the same margin.
 
 numpy's float32 arithmetic is IEEE round-to-nearest-even, as the GPU's is, so
 these are the kernels' results.  Every binary16 x with |x| <= a is tried for
@@ -42,7 +46,12 @@ def routes(xb, ab):
     y = x * r
     q_rec = np.rint(y)
     ok = np.abs(y - q_rec) < HALF_MARGIN
-    return q_div.astype(np.int32), q_rec.astype(np.int32), ok
+    # fused: the product is exact in fp64 (11 + 24 bits), so are its rounding
+    # to an integer and the residual; only the residual is rounded to fp32
+    p = x.astype(np.float64) * np.float64(r)
+    q_fus = np.rint(p)
+    ok_fus = np.abs((p - q_fus).astype(np.float32)) < HALF_MARGIN
+    return (q_div.astype(np.int32), q_rec.astype(np.int32), ok, q_fus.astype(np.int32), ok_fus)
 
 
 @pytest.mark.parametrize("which", ["special", "random"])
@@ -53,13 +62,14 @@ def test_reciprocal_and_division_routes_are_exact(which):
     for ab in a_list:
         xb = all_x_up_to(ab)
         exact = oracle.round_127x_over_a(xb, np.full(xb.shape, ab, np.uint16))
-        q_div, q_rec, ok = routes(xb, ab)
+        q_div, q_rec, ok, q_fus, ok_fus = routes(xb, ab)
         assert np.array_equal(q_div, exact), "division route, a bits %#x" % ab
         assert np.array_equal(q_rec[ok], exact[ok]), "reciprocal route, a bits %#x" % ab
-        fallback += int((~ok).sum())
+        assert np.array_equal(q_fus[ok_fus], exact[ok_fus]), "fused route, a bits %#x" % ab
+        fallback += int((~ok).sum()) + int((~ok_fus).sum())
         total += xb.size
     # the fallback is rare on these inputs (ties and near-ties only)
-    assert fallback < 0.01 * total
+    assert fallback < 0.02 * total
 
 
 def test_reciprocal_route_declines_exact_ties():
@@ -71,7 +81,7 @@ def test_reciprocal_route_declines_exact_ties():
         xb = xs.view(np.uint16)
         ab = np.uint16(np.array(a).view(np.uint16))
         exact = oracle.round_127x_over_a(xb, np.full(xb.shape, ab, np.uint16))
-        q_div, q_rec, ok = routes(xb, ab)
-        assert not ok.any(), "a tie must take the division route"
+        q_div, q_rec, ok, q_fus, ok_fus = routes(xb, ab)
+        assert not ok.any() and not ok_fus.any(), "a tie must take the division route"
         assert np.array_equal(q_div, exact)
         assert np.array_equal(exact % 2, np.zeros_like(exact)), "ties go to even"
