@@ -33,6 +33,9 @@
 //    walk a grouped raster (GROUP tile rows at a time) for L2 reuse.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "internal.h"
 
 namespace llmint8 {
@@ -234,23 +237,24 @@ __device__ __forceinline__ void read_one(Frags<C> &f, const char *sa, const char
         f.a[g - C::FN] = *reinterpret_cast<const v4i *>(sa + (g - C::FN) * 32 * C::ROWB + fo);
 }
 
-// One half-stage in a fixed issue order: groups of (one global->LDS load,
-// one fragment read of the next k-step, FM*FN/groups MFMAs of this k-step),
+// One k-step in a fixed issue order: groups of (one global->LDS load, one
+// fragment read of a later k-step, FM*FN/groups MFMAs of this k-step),
 // pinned with scheduling barriers so the loads and reads always sit between
-// MFMAs and the matrix core never waits on their issue.
-template <class C, class M, bool kWithLoads>
-__device__ __forceinline__ void half_stage(const Frags<C> &cur, Frags<C> &nxt, const char *sa,
-                                           const char *sb, int fo,
-                                           typename M::acc_t (&acc)[C::FM][C::FN],
-                                           const Streams<C> &st, char *smem, int stage,
-                                           int64_t kbyte, int wave)
+// MFMAs and the matrix core never waits on their issue.  Loads kL0 ..
+// kL0+kNL-1 of the stage being refilled are issued here.
+template <class C, class M, int kL0, int kNL>
+__device__ __forceinline__ void kstep(const Frags<C> &cur, Frags<C> &nxt, const char *sa,
+                                      const char *sb, int fo,
+                                      typename M::acc_t (&acc)[C::FM][C::FN],
+                                      const Streams<C> &st, char *smem, int stage, int64_t kbyte,
+                                      int wave)
 {
     constexpr int kReads = C::FM + C::FN, kMfma = C::FM * C::FN;
-    constexpr int kGroups = kReads > C::kLoads ? kReads : C::kLoads;
+    constexpr int kGroups = kReads > kNL ? kReads : kNL;
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
-        if (kWithLoads && g < C::kLoads)
-            st.issue_one(smem, stage, kbyte, wave, g);
+        if (g < kNL)
+            st.issue_one(smem, stage, kbyte, wave, kL0 + g);
         if (g < kReads)
             read_one<C>(nxt, sa, sb, fo, g);
 #pragma unroll
@@ -260,6 +264,99 @@ __device__ __forceinline__ void half_stage(const Frags<C> &cur, Frags<C> &nxt, c
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+template <class C, class M, bool kWithLoads>
+__device__ __forceinline__ void half_stage(const Frags<C> &cur, Frags<C> &nxt, const char *sa,
+                                           const char *sb, int fo,
+                                           typename M::acc_t (&acc)[C::FM][C::FN],
+                                           const Streams<C> &st, char *smem, int stage,
+                                           int64_t kbyte, int wave)
+{
+    kstep<C, M, 0, kWithLoads ? C::kLoads : 0>(cur, nxt, sa, sb, fo, acc, st, smem, stage, kbyte,
+                                                wave);
+}
+
+// s_waitcnt lgkmcnt(0) with vmcnt/expcnt left alone: every LDS read issued
+// by this wavefront has returned.
+__device__ __forceinline__ void wait_lds()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+// The main loop for 128-byte stages (4 k-steps): fragments are read two
+// k-steps ahead (three fragment buffers), so every wavefront is done
+// reading a stage after its second k-step; the barrier sits there, and the
+// refill of the stage's buffer (stage kt+STAGES) is spread over its last two
+// k-steps instead of being issued in one burst, which had stalled the MFMA
+// stream behind the load issue.  Buffer use, waits and tail handling as in
+// mainloop; the fragment buffers rotate with period 3 stages (12 k-steps),
+// so the loop body is three stages long and 1 or 2 leftover stages run after
+// it.
+template <class C, class M>
+__device__ __forceinline__ void mainloop_ra2(char *smem, const Streams<C> &st, int numK,
+                                             typename M::acc_t (&acc)[C::FM][C::FN], int wm,
+                                             int wn, int wave, int lane)
+{
+    static_assert(C::kKSteps == 4 && C::kLoads % 2 == 0, "128-byte stages");
+    const int frow = (lane & 31) * C::ROWB;
+    int fo[C::kKSteps];
+#pragma unroll
+    for (int s = 0; s < C::kKSteps; ++s)
+        fo[s] = frow + (((2 * s + (lane >> 5)) ^ C::swz(lane & 31)) << 4);
+    const int aoff = wm * (C::BM / C::WM) * C::ROWB;
+    const int boff = C::BM * C::ROWB + wn * (C::BN / C::WN) * C::ROWB;
+    const int64_t klast = (int64_t)(numK - 1) * C::ROWB;
+    auto kb = [&](int s) -> int64_t {
+        const int64_t k = (int64_t)s * C::ROWB;
+        return k < klast ? k : klast;
+    };
+    auto stage_a = [&](int s) { return smem + (s % C::STAGES) * C::kStageBytes + aoff; };
+    auto stage_b = [&](int s) { return smem + (s % C::STAGES) * C::kStageBytes + boff; };
+
+#pragma unroll
+    for (int s = 0; s < C::STAGES; ++s)
+        st.issue(smem, s, kb(s), wave);
+    wait_vm<(C::STAGES - 1) * C::kLoads>();   // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+
+    Frags<C> F[3];
+    read_frags<C>(F[0], stage_a(0), stage_b(0), fo[0]);
+    read_frags<C>(F[1], stage_a(0), stage_b(0), fo[1]);
+    constexpr int kHalf = C::kLoads / 2;
+    // stage kt whose k-step 0 uses fragment buffer P (kt % 3 == P mod 3 in
+    // the unrolled period): k-step s uses F[(4P + s) % 3] and reads k-step
+    // s+2 into F[(4P + s + 2) % 3]
+    auto stage = [&]<int P>(std::integral_constant<int, P>, int kt) {
+        const int nk = kt + 1 < numK ? kt + 1 : kt;
+        const int rb = kt % C::STAGES;
+        const int64_t kr = kb(kt + C::STAGES);
+        kstep<C, M, 0, 0>(F[(4 * P) % 3], F[(4 * P + 2) % 3], stage_a(kt), stage_b(kt), fo[2], acc,
+                          st, smem, 0, 0, wave);
+        kstep<C, M, 0, 0>(F[(4 * P + 1) % 3], F[(4 * P + 3) % 3], stage_a(kt), stage_b(kt), fo[3],
+                          acc, st, smem, 0, 0, wave);
+        // every read of stage kt has been issued; once they have returned and
+        // stage kt+1 has landed, the wavefronts meet and stage kt's buffer is
+        // refilled over the next two k-steps
+        wait_lds();
+        wait_vm<(C::STAGES - 2) * C::kLoads>();
+        __builtin_amdgcn_s_barrier();
+        kstep<C, M, 0, kHalf>(F[(4 * P + 2) % 3], F[(4 * P + 4) % 3], stage_a(nk), stage_b(nk),
+                              fo[0], acc, st, smem, rb, kr, wave);
+        kstep<C, M, kHalf, kHalf>(F[(4 * P + 3) % 3], F[(4 * P + 5) % 3], stage_a(nk),
+                                  stage_b(nk), fo[1], acc, st, smem, rb, kr, wave);
+    };
+    int kt = 0;
+    for (; kt + 3 <= numK; kt += 3) {
+        stage(std::integral_constant<int, 0>{}, kt);
+        stage(std::integral_constant<int, 1>{}, kt + 1);
+        stage(std::integral_constant<int, 2>{}, kt + 2);
+    }
+    if (numK - kt >= 1)
+        stage(std::integral_constant<int, 0>{}, kt);
+    if (numK - kt >= 2)
+        stage(std::integral_constant<int, 1>{}, kt + 1);
+    wait_vm<0>();   // the tail loads land before anyone reuses the buffers
 }
 
 // Runs numK stages (ROWB bytes of K = ROWB/32 32-deep k-steps each) of the
@@ -329,6 +426,21 @@ __device__ __forceinline__ void mainloop(char *smem, const Streams<C> &st, int n
     wait_vm<0>();   // the tail loads land before anyone reuses the buffers
 }
 
+// The main loop for the stage shape: read-two-ahead for the int8 product
+// over 128-byte stages (the fp16 pass over many outlier columns keeps the
+// one-ahead loop: its fp32 accumulators leave no room for the third
+// fragment buffer).
+template <class C, class M>
+__device__ __forceinline__ void run_mainloop(char *smem, const Streams<C> &st, int numK,
+                                             typename M::acc_t (&acc)[C::FM][C::FN], int wm,
+                                             int wn, int wave, int lane)
+{
+    if constexpr (C::kKSteps == 4 && std::is_same_v<M, MfmaI8>)
+        mainloop_ra2<C, M>(smem, st, numK, acc, wm, wn, wave, lane);
+    else
+        mainloop<C, M>(smem, st, numK, acc, wm, wn, wave, lane);
+}
+
 // The finished fp16 block tile is staged in LDS (BM rows of BN*2 bytes) and
 // written out row by row in 16-byte pieces, so that every store instruction
 // fills whole 128-byte lines; straight from the accumulator layout each
@@ -355,39 +467,56 @@ __device__ __forceinline__ void write_tile(const char *smem, const EpilogueArgs 
     }
 }
 
-// The fp16 outlier fragments of a tile (up to 32 outlier columns): x_out rows
-// of the tile's T rows and w_out rows of its N columns, two 16-deep k-steps.
-// They do not depend on the GEMM, so k_gemm loads them before its main loop
-// and their latency is not paid in the epilogue.
+// The fp16 outlier operands of a tile (up to 32 outlier columns): the x_out
+// rows of its BM rows and the w_out rows of its BN columns, 32 halves (64
+// bytes) each, held in the LDS bytes after the ring (BM+BN rows; chunk q of
+// row r in slot q ^ ((r >> 2) & 3), so that the 16 rows a quarter-wave reads
+// cover all banks).  They do not depend on the GEMM: each wavefront issues a
+// quarter of them as direct global->LDS loads before its first stage, so they
+// have landed when the main loop starts and cost no registers during it.
 template <class C>
-struct OutlierFrags {
-    v4i xo[C::FM][2], wo[C::FN][2];
+struct OutlierRows {
+    static constexpr int kRowBytes = 64;
+    static constexpr int kBytes = (C::BM + C::BN) * kRowBytes;
+    static constexpr int kInstr = kBytes / 1024 / C::kWaves;   // load instructions per wave
+    static_assert(kBytes % (1024 * C::kWaves) == 0 && (C::BM / 16) % kInstr == 0,
+                  "whole instructions, each within x or w rows");
+    __device__ __forceinline__ static int slot(int r, int q) { return q ^ ((r >> 2) & 3); }
 };
+
 template <class C>
-__device__ __forceinline__ void load_outlier_frags(OutlierFrags<C> &f, const EpilogueArgs &ep,
+__device__ __forceinline__ void issue_outlier_rows(char *orows, const EpilogueArgs &ep,
                                                    int64_t m0, int64_t n0, int64_t T, int64_t N,
-                                                   int nout, int wm, int wn, int lane)
+                                                   int wave, int lane)
 {
-    const int tl = lane & 31, nl = 4 * (lane >> 5);
-    const int64_t tw = m0 + wm * (C::BM / C::WM), nw = n0 + wn * (C::BN / C::WN);
+    using R = OutlierRows<C>;
+    const char *xb = reinterpret_cast<const char *>(ep.x_out);
+    const char *wb = reinterpret_cast<const char *>(ep.w_out);
+    // every row read lies inside the workspace's x_out / w_out segments (at
+    // least 2*K >= 64 bytes per row); with n = 0 their contents are unused
+    const __amdgpu_buffer_rsrc_t rx = Streams<C>::rsrc(xb + m0 * R::kRowBytes, (T - m0) * R::kRowBytes);
+    const __amdgpu_buffer_rsrc_t rw = Streams<C>::rsrc(wb + n0 * R::kRowBytes, (N - n0) * R::kRowBytes);
+    const int lr = lane / 4, lq = lane % 4;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        int64_t t = tw + i * 32 + tl;
-        t = t < T ? t : T - 1;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-            f.xo[i][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.x_out + t * kOutlierPad + 16 * s2 + nl * 2)
-                                   : v4i{0, 0, 0, 0};
+    for (int u = 0; u < R::kInstr; ++u) {
+        const int j = wave * R::kInstr + u;          // 16 staged rows per instruction
+        const int r = 16 * j + lr;                   // staged row: x rows, then w rows
+        const bool isx = 16 * j < C::BM;
+        const int64_t rr = isx ? r : r - C::BM;      // row within the tile's rows / columns
+        const int64_t lim = isx ? T - m0 : N - n0;
+        const int64_t row = rr < lim ? rr : lim - 1;   // ragged: clamp
+        const uint32_t off = (uint32_t)(row * R::kRowBytes + 16 * R::slot(r, lq));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isx ? rx : rw, (lds_void *)(orows + j * 1024), 16,
+                                                 off, 0, 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-        int64_t n = nw + j * 32 + tl;
-        n = n < N ? n : N - 1;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-            f.wo[j][s2] = nout > 0 ? *reinterpret_cast<const v4i *>(ep.w_out + n * kOutlierPad + 16 * s2 + nl * 2)
-                                   : v4i{0, 0, 0, 0};
-    }
+}
+
+// 16 bytes of staged outlier row r: halves 8c .. 8c+7.
+template <class C>
+__device__ __forceinline__ v4i outlier_frag(const char *orows, int r, int c)
+{
+    return *reinterpret_cast<const v4i *>(orows + r * OutlierRows<C>::kRowBytes +
+                                          16 * OutlierRows<C>::slot(r, c));
 }
 
 // Up to 32 outlier columns: their fp16 fragments (loaded before the main
@@ -399,16 +528,23 @@ __device__ __forceinline__ void load_outlier_frags(OutlierFrags<C> &f, const Epi
 // column group ahead, so no latency is paid per accumulator tile.
 template <class C, bool kBias>
 __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], const float (&at)[C::FM],
-                                            const OutlierFrags<C> &of,
+                                            const char *orows,
                                             char *smem, const EpilogueArgs &ep, int64_t m0,
                                             int64_t n0, int64_t T, int64_t N, int nout, int wm,
                                             int wn, int lane, int tid)
 {
     static_assert(C::BM * C::BN * 2 <= C::kLdsBytes, "output tile fits the LDS ring");
     const int tl = lane & 31, nl = 4 * (lane >> 5);
-    const int64_t tw = m0 + wm * (C::BM / C::WM), nw = n0 + wn * (C::BN / C::WN);
-    const auto &xo = of.xo;
-    const auto &wo = of.wo;
+    const int64_t nw = n0 + wn * (C::BN / C::WN);
+    // outlier fragments from LDS: lane (tl, hi) holds halves 8*(2*s2 + hi) ..
+    // +7 of its row for the 16-deep k-step s2
+    const int hi = lane >> 5;
+    v4i xo[C::FM][2];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+            xo[i][s2] = outlier_frag<C>(orows, wm * (C::BM / C::WM) + i * 32 + tl, 2 * s2 + hi);
     // column scales and bias of column group j, fetched one group ahead
     v4f sn[2][4];
     uint2 bias[2][4];
@@ -429,6 +565,10 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
         if (j + 1 < C::FN)
             load_cols(j + 1, (j + 1) % 2);
         const int cb = j % 2;
+        v4i wo[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+            wo[s2] = outlier_frag<C>(orows, C::BM + wn * (C::BN / C::WN) + j * 32 + tl, 2 * s2 + hi);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
             v16f d;
@@ -436,9 +576,9 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
             for (int r = 0; r < 16; ++r)
                 d[r] = (float)acc[i][j][r] * (at[i] * sn[cb][r / 4][r % 4]);
             if (nout > 0) {
-                d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wo[j][0]),
+                d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wo[0]),
                                                          __builtin_bit_cast(v8h, xo[i][0]), d, 0, 0, 0);
-                d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wo[j][1]),
+                d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wo[1]),
                                                          __builtin_bit_cast(v8h, xo[i][1]), d, 0, 0, 0);
             }
             // bias, one rounding, staged: registers 4g..4g+3 hold tile columns
@@ -519,7 +659,7 @@ __device__ __forceinline__ void outlier_pass(const v16i (&acc)[C::FM][C::FN],
         st.init(reinterpret_cast<const char *>(ep.x_out), 2 * ldo, m0, T,
                 reinterpret_cast<const char *>(ep.w_out), 2 * ldo, n0, N, wave, lane);
         static_assert(128 % C::ROWB == 0, "outlier rows (multiples of 128 bytes) hold whole stages");
-        mainloop<C, MfmaF16F>(smem, st, (int)(ldo * 2 / C::ROWB), accf, wm, wn, wave, lane);
+        run_mainloop<C, MfmaF16F>(smem, st, (int)(ldo * 2 / C::ROWB), accf, wm, wn, wave, lane);
     }
     static_assert(C::BM * C::BN * 2 <= C::kLdsBytes, "output tile fits the LDS ring");
     __builtin_amdgcn_s_barrier();
@@ -556,7 +696,9 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
                                                       const int8_t *__restrict__ B, int64_t T,
                                                       int64_t K, int64_t N, EpilogueArgs ep)
 {
-    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
+    // the ring, then (output path) the tile's outlier rows
+    __shared__ __attribute__((aligned(1024)))
+    char smem[C::kLdsBytes + (kRawI32 ? 0 : OutlierRows<C>::kBytes)];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -569,12 +711,11 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
     const int nout = kRawI32 ? 0 : *ep.n_out;
     if (!kRawI32 && nout > kOutlierPad)
         return;
-    // the outlier fragments do not depend on the GEMM: loaded now, they have
-    // landed when the main loop ends (the row scales stay after it: held
-    // through the loop they cost more spills in the epilogue than they save)
-    OutlierFrags<C> of;
+    // the outlier rows do not depend on the GEMM: staged into LDS now, they
+    // have landed when the main loop starts (its first wait covers them)
+    char *orows = smem + C::kLdsBytes;
     if constexpr (!kRawI32)
-        load_outlier_frags<C>(of, ep, m0, n0, T, N, nout, wm, wn, lane);
+        issue_outlier_rows<C>(orows, ep, m0, n0, T, N, wave, lane);
 
     v16i acc[C::FM][C::FN];
 #pragma unroll
@@ -589,7 +730,7 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
         Streams<C> st;
         st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
                 n0, N, wave, lane);
-        mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+        run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
     }
 
     // The MFMAs compute D = CB_tile * Xq_tile^T, so a 32x32 accumulator holds
@@ -624,9 +765,9 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
             at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
         }
         if (ep.bias)
-            finish_tile<C, true>(acc, at, of, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
+            finish_tile<C, true>(acc, at, orows, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
         else
-            finish_tile<C, false>(acc, at, of, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
+            finish_tile<C, false>(acc, at, orows, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
     }
 }
 
@@ -666,7 +807,7 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restr
         Streams<C> st;
         st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
                 n0, N, wave, lane);
-        mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+        run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
     }
     float at[C::FM];
     const int64_t tw = m0 + wm * (C::BM / C::WM) + (lane & 31);
