@@ -179,11 +179,61 @@ def decode_bench(torch, L, workloads, steps, warmup, ev, dev):
     return res
 
 
+def ffn_pair(torch, L, d, steps, warmup, dev):
+    """The 6.7B-style FFN as one step: fc1 (X [4096,4096] -> [4096,16384]) with
+    the ReLU fused into its output, then fc2 on that output ([4096,16384] ->
+    [4096,4096]), both through the decomposition at threshold 6.  Counts
+    2*T*K*N ops per layer.  Also timed with the ReLU as a separate torch pass
+    between the layers, for the cost of the unfused chain."""
+    X = torch.from_numpy(d["X"]).to(dev)
+    CB1, SCB1 = L.llmint8_quantize_weight(torch.from_numpy(d["W_t"]).to(dev))
+    CB2, SCB2 = L.llmint8_quantize_weight(torch.from_numpy(d["W2_t"]).to(dev))
+    T, D = X.shape
+    F = CB1.shape[0]
+    h = torch.empty((T, F), dtype=torch.float16, device=dev)
+    y = torch.empty((T, D), dtype=torch.float16, device=dev)
+    ws = torch.empty((max(L.llmint8_workspace_bytes(T, D, F), L.llmint8_workspace_bytes(T, F, D)),),
+                     dtype=torch.uint8, device=dev)
+
+    def fused():
+        L.llmint8_matmul_act(X, CB1, SCB1, 6.0, L.ACT_RELU, out=h, ws=ws)
+        L.llmint8_matmul(h, CB2, SCB2, 6.0, out=y, ws=ws)
+
+    def unfused():
+        L.llmint8_matmul(X, CB1, SCB1, 6.0, out=h, ws=ws)
+        torch.relu_(h)
+        L.llmint8_matmul(h, CB2, SCB2, 6.0, out=y, ws=ws)
+
+    def per_step(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    n2 = int(L.llmint8_quantize_act(torch.relu(L.llmint8_matmul(X, CB1, SCB1, 6.0)), 6.0)[3].cpu()[0])
+    s_f = per_step(fused)
+    s_u = per_step(unfused)
+    ops = 2.0 * T * D * F * 2
+    r = {"T": T, "D": D, "F": F, "threshold": 6.0, "fc2_n_outliers": n2,
+         "step_us": round(s_f * 1e6, 2), "step_TOPS": round(ops / s_f / 1e12, 1),
+         "step_frac_int8_peak": round(ops / s_f / 1e12 / INT8_PEAK_TOPS, 4),
+         "unfused_step_us": round(s_u * 1e6, 2)}
+    log("config ffn_6p7b_pair: fc1+ReLU+fc2 %.1f us (%.0f TOP/s), ReLU as a separate pass %.1f us"
+        % (s_f * 1e6, ops / s_f / 1e12, s_u * 1e6))
+    del X, CB1, SCB1, CB2, SCB2, h, y, ws
+    torch.cuda.empty_cache()
+    return r
+
+
 def configs_bench(torch, L, workloads, steps, warmup, ev, dev):
     """The method's other workloads (parity cases), each timed like the main one:
     the 1.3B up-projection, the fc2-like input (every column an outlier) and
     the attention-projection sweep (outlier dims n in {0,6,32,128}, threshold
-    0 and inf, T = 4095).  Step figures count 2*T*K*N ops for the whole call;
+    0 and inf, T = 4095), and the FFN pair fc1 -> ReLU -> fc2.  Step figures count 2*T*K*N ops for the whole call;
     the GEMM kernel's own time is given where k_gemm does the work (up to 32
     outlier columns)."""
     res = {}
@@ -217,7 +267,8 @@ def configs_bench(torch, L, workloads, steps, warmup, ev, dev):
     d = workloads.up_proj_1p3b()
     run("up_proj_1p3b", d["X"], d["W_t"], 6.0)
     d = workloads.ffn_6p7b(with_fc2=True)
-    run("ffn_6p7b_fc2", workloads.ffn_6p7b_fc2_input()["X"], d.pop("W2_t"), 6.0)
+    run("ffn_6p7b_fc2", workloads.ffn_6p7b_fc2_input()["X"], d["W2_t"], 6.0)
+    res["ffn_6p7b_pair"] = ffn_pair(torch, L, d, steps, warmup, dev)
     del d
     W5 = workloads.attn_proj_sweep(0)["W_t"]
     for nd in (0, 6, 32, 128):

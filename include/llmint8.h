@@ -144,6 +144,28 @@ LLMINT8_API llmint8_status_t llmint8_matmul(const uint16_t *X, int64_t T, int64_
                                 float threshold, uint16_t *out, void *ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* Output activations of llmint8_matmul_act. */
+enum { LLMINT8_ACT_NONE = 0, LLMINT8_ACT_RELU = 1 };
+
+/*
+ * llmint8_matmul followed by the layer's activation, fused into the output
+ * rounding: out = fp16(act(v)) for the unrounded output v above (with
+ * LLMINT8_ACT_RELU, act(v) = max(v, 0); rounding to nearest commutes with
+ * it, so this equals max(fp16(v), 0)).  For the feed-forward layers the
+ * method targets (LLM.int8() summary, "Introduction": the feed-forward and
+ * attention projection layers), whose expansion is followed by a ReLU (the
+ * summary's "8-bit Data Types and Quantization" names ReLU outputs as the
+ * activations that feed the next layer), so that the next llmint8_matmul
+ * reads the activated values without a separate pass.  Arguments as for
+ * llmint8_matmul; an activation other than the two above ->
+ * LLMINT8_ERR_INVALID_ARG.
+ */
+LLMINT8_API llmint8_status_t llmint8_matmul_act(const uint16_t *X, int64_t T, int64_t K,
+                                                int64_t N, const int8_t *CB, const float *SCB,
+                                                const uint16_t *bias, float threshold,
+                                                int activation, uint16_t *out, void *ws,
+                                                size_t ws_bytes, hipStream_t stream);
+
 /*
  * llmint8_matmul with the kernel choice forced and optional timing events,
  * for tests and benchmarks: path 0 = automatic, 1 = tiled GEMM, 2 =

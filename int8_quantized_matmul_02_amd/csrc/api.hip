@@ -122,14 +122,15 @@ llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, int64_t K, f
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 
-llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, int64_t N,
-                                     const int8_t *CB, const float *SCB, const uint16_t *bias,
-                                     float threshold, uint16_t *out, void *ws, size_t ws_bytes,
-                                     int path, hipEvent_t main_start, hipEvent_t main_stop,
-                                     hipStream_t stream)
+namespace {
+llmint8_status_t matmul_impl(const uint16_t *X, int64_t T, int64_t K, int64_t N, const int8_t *CB,
+                             const float *SCB, const uint16_t *bias, float threshold,
+                             int activation, uint16_t *out, void *ws, size_t ws_bytes, int path,
+                             hipEvent_t main_start, hipEvent_t main_stop, hipStream_t stream)
 {
     if (!X || !CB || !SCB || !out || !ws || !aligned16(X) || !aligned16(CB) ||
-        !aligned16(out) || !aligned16(ws) || bad_threshold(threshold) || path < 0 || path > 2)
+        !aligned16(out) || !aligned16(ws) || bad_threshold(threshold) || path < 0 || path > 2 ||
+        (activation != LLMINT8_ACT_NONE && activation != LLMINT8_ACT_RELU))
         return LLMINT8_ERR_INVALID_ARG;
     llmint8_status_t st = check_shape(T, K, N);
     if (st != LLMINT8_OK)
@@ -163,11 +164,32 @@ llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, in
                                   x_out, g, packed, stream);
     if (eq != hipSuccess)
         return LLMINT8_ERR_HIP;
-    EpilogueArgs ep{a, SCB, x_out, w_out, O, n_out, bias, out, nullptr};
+    EpilogueArgs ep{a, SCB, x_out, w_out, O, n_out, bias, out, nullptr,
+                    activation == LLMINT8_ACT_RELU ? 1 : 0};
     const hipError_t e =
         decode ? launch_decode(Xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
                : launch_gemm(Xq, CB, T, K, N, ep, stream, main_start, main_stop);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
+}
+}  // namespace
+
+llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                     const int8_t *CB, const float *SCB, const uint16_t *bias,
+                                     float threshold, uint16_t *out, void *ws, size_t ws_bytes,
+                                     int path, hipEvent_t main_start, hipEvent_t main_stop,
+                                     hipStream_t stream)
+{
+    return matmul_impl(X, T, K, N, CB, SCB, bias, threshold, LLMINT8_ACT_NONE, out, ws, ws_bytes,
+                       path, main_start, main_stop, stream);
+}
+
+llmint8_status_t llmint8_matmul_act(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                    const int8_t *CB, const float *SCB, const uint16_t *bias,
+                                    float threshold, int activation, uint16_t *out, void *ws,
+                                    size_t ws_bytes, hipStream_t stream)
+{
+    return matmul_impl(X, T, K, N, CB, SCB, bias, threshold, activation, out, ws, ws_bytes, 0,
+                       nullptr, nullptr, stream);
 }
 
 llmint8_status_t llmint8_matmul(const uint16_t *X, int64_t T, int64_t K, int64_t N,

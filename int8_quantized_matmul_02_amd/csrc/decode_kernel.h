@@ -74,7 +74,7 @@ __device__ __forceinline__ OutlierPrefetch prefetch_outliers(const int8_t *B, in
 
 // 16x16 accumulator layout: lane holds column n = n0 + lane%16 and rows
 // t = 4*(lane/16) + q.
-template <bool kRawI32>
+template <bool kRawI32, bool kRelu = false>
 __device__ __forceinline__ void epilogue(const v4i acc, int lane, int64_t n, int64_t T, int64_t K,
                                          int64_t N, const int8_t *B, const EpilogueArgs &ep,
                                          const OutlierPrefetch &pre)
@@ -123,7 +123,7 @@ __device__ __forceinline__ void epilogue(const v4i acc, int lane, int64_t n, int
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             if (t0 + q < T)
-                ep.out[(t0 + q) * N + n] = f2h(v[q] + bias);
+                ep.out[(t0 + q) * N + n] = f2h_act<kRelu>(v[q] + bias);
     }
 }
 
@@ -174,7 +174,7 @@ struct CfgRs {
     static_assert(kWait < 64, "vmcnt range");
 };
 
-template <class C, bool kRawI32>
+template <class C, bool kRawI32, bool kRelu = false>
 __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restrict__ A,
                                                            const int8_t *__restrict__ B,
                                                            int64_t T, int64_t K, int64_t N,
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
              ...);
         }(std::make_integer_sequence<int, C::kUnroll>{});
     }
-    epilogue<kRawI32>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
+    epilogue<kRawI32, kRelu>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
 }
 
 // ---------------------------------------------------------------------------
@@ -432,10 +432,12 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_lds(const int8_t *__rest
     epilogue<kRawI32>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
 }
 
-template <class C, bool R>
+template <class C, bool R, bool kRelu = false>
 struct RsKernel {
-    static constexpr auto fn = k_decode_rs<C, R>;
+    static constexpr auto fn = k_decode_rs<C, R, kRelu>;
 };
+template <class C, bool R>
+using RsKernelRelu = RsKernel<C, R, true>;
 template <class C, bool R>
 struct LdsKernel {
     static constexpr auto fn = k_decode_lds<C, R>;
@@ -473,6 +475,8 @@ hipError_t launch_rs(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, i
 {
     if (C::kSync && N % (16 * C::WAVES) != 0)
         return hipErrorInvalidValue;   // a block's wavefronts must all reach the barriers
+    if (ep.act && !ep.c_i32)
+        return launch_kernel<C, RsKernelRelu>(Xq, CB, T, K, N, ep, s, ev0, ev1);
     return launch_kernel<C, RsKernel>(Xq, CB, T, K, N, ep, s, ev0, ev1);
 }
 

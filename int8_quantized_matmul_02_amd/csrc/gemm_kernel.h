@@ -526,7 +526,7 @@ __device__ __forceinline__ v4i outlier_frag(const char *orows, int r, int c)
 // wavefront has stopped reading; then the whole block tile is written out.
 // Operands come from clamped addresses and the column scales are loaded one
 // column group ahead, so no latency is paid per accumulator tile.
-template <class C, bool kBias>
+template <class C, bool kBias, bool kRelu>
 __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], const float (&at)[C::FM],
                                             const char *orows,
                                             char *smem, const EpilogueArgs &ep, int64_t m0,
@@ -594,11 +594,11 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
                                          h2f((uint16_t)(bb.y & 0xffffu)), h2f((uint16_t)(bb.y >> 16))};
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        h[q] = f2h(d[4 * g + q] + bv[q]);
+                        h[q] = f2h_act<kRelu>(d[4 * g + q] + bv[q]);
                 } else {
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        h[q] = f2h(d[4 * g + q]);
+                        h[q] = f2h_act<kRelu>(d[4 * g + q]);
                 }
                 const int u = (nc + 8 * g) / 4;
                 *reinterpret_cast<uint2 *>(smem + tr * (C::BN * 2) + 8 * (u ^ (tr & 31))) =
@@ -618,7 +618,7 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
 // there, so the two share registers) onto which the fp16 MFMAs add; then
 // the bias, one rounding, and the tile goes out through LDS like
 // finish_tile's.
-template <class C>
+template <class C, bool kRelu>
 __device__ __forceinline__ void outlier_pass(const v16i (&acc)[C::FM][C::FN],
                                              const float (&at)[C::FM], char *smem,
                                              const EpilogueArgs &ep, int64_t m0, int64_t n0,
@@ -679,7 +679,7 @@ __device__ __forceinline__ void outlier_pass(const v16i (&acc)[C::FM][C::FN],
                 uint16_t h[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    h[q] = f2h(accf[i][j][4 * g + q] + bv[q]);
+                    h[q] = f2h_act<kRelu>(accf[i][j][4 * g + q] + bv[q]);
                 const int u = (wn * (C::BN / C::WN) + j * 32 + 8 * g + nl) / 4;
                 *reinterpret_cast<uint2 *>(smem + tr * (C::BN * 2) + 8 * (u ^ (tr & 31))) =
                     make_uint2((unsigned)h[0] | ((unsigned)h[1] << 16),
@@ -691,7 +691,7 @@ __device__ __forceinline__ void outlier_pass(const v16i (&acc)[C::FM][C::FN],
     write_tile<C>(smem, ep, m0, n0, T, N, tid);
 }
 
-template <class C, bool kRawI32>
+template <class C, bool kRawI32, bool kRelu>
 __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__ A,
                                                       const int8_t *__restrict__ B, int64_t T,
                                                       int64_t K, int64_t N, EpilogueArgs ep)
@@ -765,9 +765,11 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
             at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
         }
         if (ep.bias)
-            finish_tile<C, true>(acc, at, orows, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
+            finish_tile<C, true, kRelu>(acc, at, orows, smem, ep, m0, n0, T, N, nout, wm, wn, lane,
+                                        tid);
         else
-            finish_tile<C, false>(acc, at, orows, smem, ep, m0, n0, T, N, nout, wm, wn, lane, tid);
+            finish_tile<C, false, kRelu>(acc, at, orows, smem, ep, m0, n0, T, N, nout, wm, wn, lane,
+                                         tid);
     }
 }
 
@@ -777,7 +779,7 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
 // fp16 pass over the outlier columns.  A kernel of its own so that the
 // registers this path needs do not cost k_gemm's epilogue; one tile per
 // block (a persistent tile loop makes the compiler spill around it).
-template <class C>
+template <class C, bool kRelu>
 __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restrict__ A,
                                                            const int8_t *__restrict__ B,
                                                            int64_t T, int64_t K, int64_t N,
@@ -816,12 +818,13 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restr
         const int64_t t = tw + i * 32;
         at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
     }
-    outlier_pass<C>(acc, at, smem, ep, m0, n0, T, K, N, nout, wm, wn, wave, lane, tid);
+    outlier_pass<C, kRelu>(acc, at, smem, ep, m0, n0, T, K, N, nout, wm, wn, wave, lane, tid);
 }
 
-// The int8 GEMM (K must be a multiple of C::ROWB) with its fused epilogue;
-// for the output (not the raw int32 sums) also k_gemm_many, of which only
-// one does work, depending on the outlier count on the device.
+// The int8 GEMM (K must be a multiple of C::ROWB) with its fused epilogue
+// (and the output activation, ep.act, a template parameter of the output
+// kernels); for the output (not the raw int32 sums) also k_gemm_many, of
+// which only one does work, depending on the outlier count on the device.
 template <class C>
 hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
                   const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
@@ -837,16 +840,27 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
             return e;
     }
     if (ep.c_i32)
-        hipLaunchKernelGGL((k_gemm<C, true>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K, N, ep);
+        hipLaunchKernelGGL((k_gemm<C, true, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K,
+                           N, ep);
+    else if (ep.act)
+        hipLaunchKernelGGL((k_gemm<C, false, true>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K,
+                           N, ep);
     else
-        hipLaunchKernelGGL((k_gemm<C, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K, N, ep);
+        hipLaunchKernelGGL((k_gemm<C, false, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K,
+                           N, ep);
     if (ev1) {
         const hipError_t e = hipEventRecord(ev1, s);
         if (e != hipSuccess)
             return e;
     }
-    if (!ep.c_i32)
-        hipLaunchKernelGGL((k_gemm_many<C>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K, N, ep);
+    if (!ep.c_i32) {
+        if (ep.act)
+            hipLaunchKernelGGL((k_gemm_many<C, true>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K,
+                               N, ep);
+        else
+            hipLaunchKernelGGL((k_gemm_many<C, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T,
+                               K, N, ep);
+    }
     return hipGetLastError();
 }
 

@@ -30,6 +30,14 @@ __device__ __forceinline__ float h2f(uint16_t u) { return (float)__builtin_bit_c
 // fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default mode); overflow -> inf.
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
+// The layer's activation applied to the output before its one rounding to
+// fp16 (kRelu: max(v, 0); round-to-nearest commutes with it).
+template <bool kRelu>
+__device__ __forceinline__ uint16_t f2h_act(float v)
+{
+    return f2h(kRelu ? __builtin_fmaxf(v, 0.0f) : v);
+}
+
 // round(127 * x / a) to nearest, ties to even, for fp16 values x and a with
 // |x| <= a and a > 0.  127*x is exact in fp32 (7 + 11 bits) and the quotient
 // is one IEEE-correct fp32 division (the library is built with
@@ -125,6 +133,7 @@ struct EpilogueArgs {
     const uint16_t *bias;    // [N] or null
     uint16_t *out;           // [T, N] fp16
     int32_t *c_i32;          // [T, N] raw accumulators (debug epilogue) or null
+    int act;                 // output activation: 0 none, 1 ReLU
 };
 
 // ev0/ev1 (optional) are recorded on s right before and after the main kernel.

@@ -1,0 +1,127 @@
+"""Linear8bitLt: a torch.nn.Module over the library's C ABI.
+
+The Hugging Face write-up of LLM.int8() (agentlenshq.com, "Hugging Face,
+LLM.int8() 8-bit matrix multiplication integrated into Transformers and
+Accelerate", section "Integration into transformers") describes the
+user-facing piece: a drop-in replacement for torch.nn.Linear that stores the
+weight as int8 CB plus per-output-column scales SCB when it is moved to the
+GPU (has_fp16_weights=False), runs the decomposition matmul with a
+`threshold` (6.0 by default) and adds the bias.  With has_fp16_weights=True
+the fp16 weight stays the parameter and is quantized again on every call
+(the mode for weights that still change).
+
+Everything computed runs in libllmint8's HIP kernels: weight quantization
+(llmint8_quantize_weight), the whole decomposition (llmint8_matmul_act), and
+an optional ReLU fused into its output rounding for the feed-forward
+expansion layers.  This module only holds the tensors, flattens leading
+dimensions into rows, and keeps one workspace buffer per device, grown as
+needed, so that steady-state calls allocate nothing but their output.
+"""
+import torch
+
+from . import llmint8 as L
+
+_ACTS = {None: L.ACT_NONE, "none": L.ACT_NONE, "relu": L.ACT_RELU}
+
+
+class Linear8bitLt(torch.nn.Module):
+    """y = act(x W^T + b) through the LLM.int8() decomposition.
+
+    in_features and out_features must be multiples of 64 (the library's
+    tile granularity), in_features at most 133,144.  Inputs are fp16 on a
+    HIP device with in_features as the last dimension; the output is fp16.
+    """
+
+    def __init__(self, in_features, out_features, bias=True, has_fp16_weights=False,
+                 threshold=6.0, activation=None, device=None):
+        super().__init__()
+        if in_features % 64 or out_features % 64 or in_features <= 0 or out_features <= 0:
+            raise ValueError("in_features and out_features must be positive multiples of 64, "
+                             "got %d and %d" % (in_features, out_features))
+        if in_features > 133144:
+            raise ValueError("in_features must be at most 133144 (int32-exact accumulation)")
+        if activation not in _ACTS:
+            raise ValueError("activation must be None, 'none' or 'relu', got %r" % (activation,))
+        if not threshold >= 0.0:
+            raise ValueError("threshold must be >= 0 (float('inf') disables outliers)")
+        self.in_features = in_features
+        self.out_features = out_features
+        self.has_fp16_weights = has_fp16_weights
+        self.threshold = float(threshold)
+        self.activation = activation
+        self.weight = torch.nn.Parameter(
+            torch.empty((out_features, in_features), dtype=torch.float16, device=device),
+            requires_grad=False)
+        torch.nn.init.normal_(self.weight, 0.0, 0.02)
+        if bias:
+            self.bias = torch.nn.Parameter(
+                torch.zeros((out_features,), dtype=torch.float16, device=device),
+                requires_grad=False)
+        else:
+            self.register_parameter("bias", None)
+        self.register_buffer("CB", None)
+        self.register_buffer("SCB", None)
+        self._ws = {}
+
+    @classmethod
+    def from_linear(cls, linear, has_fp16_weights=False, threshold=6.0, activation=None):
+        """A Linear8bitLt holding torch.nn.Linear `linear`'s weight and bias
+        (cast to fp16); quantized on the first forward call, or by
+        quantize_()."""
+        m = cls(linear.in_features, linear.out_features, bias=linear.bias is not None,
+                has_fp16_weights=has_fp16_weights, threshold=threshold, activation=activation,
+                device=linear.weight.device)
+        with torch.no_grad():
+            m.weight.copy_(linear.weight.to(torch.float16))
+            if linear.bias is not None:
+                m.bias.copy_(linear.bias.to(torch.float16))
+        return m
+
+    def quantize_(self):
+        """Quantize the fp16 weight into CB and SCB (on its device).  Without
+        fp16 weights the fp16 parameter is released afterwards, as the
+        write-up's Int8Params does when the weight is moved to the GPU."""
+        if self.weight is None:
+            return self
+        if self.weight.device.type != "cuda":
+            raise RuntimeError("Linear8bitLt: move the module to a HIP device before quantizing")
+        w = self.weight.detach().contiguous()
+        if self.CB is None or self.CB.device != w.device:
+            self.CB = torch.empty((self.out_features, self.in_features), dtype=torch.int8,
+                                  device=w.device)
+            self.SCB = torch.empty((self.out_features,), dtype=torch.float32, device=w.device)
+        L.llmint8_quantize_weight(w, CB=self.CB, SCB=self.SCB)
+        if not self.has_fp16_weights:
+            self.weight = None
+        return self
+
+    def _workspace(self, T, device):
+        need = L.llmint8_workspace_bytes(T, self.in_features, self.out_features)
+        ws = self._ws.get(device)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty((need,), dtype=torch.uint8, device=device)
+            self._ws[device] = ws
+        return ws
+
+    def forward(self, x):
+        if x.dtype != torch.float16:
+            raise TypeError("Linear8bitLt expects fp16 input, got %s" % x.dtype)
+        if x.shape[-1] != self.in_features:
+            raise ValueError("last dimension %d != in_features %d" % (x.shape[-1], self.in_features))
+        if self.has_fp16_weights or self.CB is None:
+            # fp16 weights are quantized on every call (they may have changed)
+            self.quantize_()
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, self.in_features).contiguous()
+        T = x2.shape[0]
+        if T == 0:
+            return x.new_empty(lead + (self.out_features,))
+        out = L.llmint8_matmul_act(x2, self.CB, self.SCB, self.threshold,
+                                   _ACTS[self.activation], bias=self.bias,
+                                   ws=self._workspace(T, x2.device))
+        return out.reshape(lead + (self.out_features,))
+
+    def extra_repr(self):
+        return ("in_features=%d, out_features=%d, bias=%s, has_fp16_weights=%s, threshold=%g, "
+                "activation=%s" % (self.in_features, self.out_features, self.bias is not None,
+                                   self.has_fp16_weights, self.threshold, self.activation))

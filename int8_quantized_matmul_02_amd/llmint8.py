@@ -17,6 +17,7 @@ _lib = None
 
 LLMINT8_OK = 0
 PATH_AUTO, PATH_GEMM, PATH_DECODE = 0, 1, 2
+ACT_NONE, ACT_RELU = 0, 1
 
 EXPORTS = (
     "llmint8_status_string",
@@ -25,6 +26,7 @@ EXPORTS = (
     "llmint8_quantize_weight",
     "llmint8_quantize_act",
     "llmint8_matmul",
+    "llmint8_matmul_act",
     "llmint8_matmul_path",
     "llmint8_igemm_i32",
 )
@@ -59,10 +61,11 @@ def _load():
     lib.llmint8_quantize_weight.argtypes = [P, I64, I64, P, P, P]
     lib.llmint8_quantize_act.argtypes = [P, I64, I64, F, P, P, P, P, P, SZ, P]
     lib.llmint8_matmul.argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ, P]
+    lib.llmint8_matmul_act.argtypes = [P, I64, I64, I64, P, P, P, F, I, P, P, SZ, P]
     lib.llmint8_matmul_path.argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ, I, P, P, P]
     lib.llmint8_igemm_i32.argtypes = [P, I64, I64, I64, P, P, I, P]
     for fn in ("llmint8_quantize_weight", "llmint8_quantize_act", "llmint8_matmul",
-               "llmint8_matmul_path", "llmint8_igemm_i32"):
+               "llmint8_matmul_act", "llmint8_matmul_path", "llmint8_igemm_i32"):
         getattr(lib, fn).restype = I
     _lib = lib
     return lib
@@ -190,6 +193,30 @@ def llmint8_matmul(X, CB, SCB, threshold=6.0, bias=None, out=None, ws=None):
                               bias.data_ptr() if bias is not None else None, float(threshold),
                               out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                               _stream(X)))
+    return out
+
+
+def llmint8_matmul_act(X, CB, SCB, threshold=6.0, activation=ACT_NONE, bias=None, out=None,
+                       ws=None):
+    """llmint8_matmul with the output activation (ACT_NONE or ACT_RELU) fused."""
+    lib = _load()
+    _dev(X, "X", _H)
+    _dev(CB, "CB", (torch.int8,))
+    _dev(SCB, "SCB", (torch.float32,))
+    T, K = X.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K or SCB.shape != (N,):
+        raise ValueError("shape mismatch: X %s, CB %s, SCB %s" % (tuple(X.shape), tuple(CB.shape), tuple(SCB.shape)))
+    if bias is not None:
+        _dev(bias, "bias", _H)
+    out = torch.empty((T, N), dtype=torch.float16, device=X.device) if out is None else _dev(out, "out", _H)
+    if ws is None:
+        ws = torch.empty((llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=X.device)
+    _check("llmint8_matmul_act",
+           lib.llmint8_matmul_act(X.data_ptr(), T, K, N, CB.data_ptr(), SCB.data_ptr(),
+                                  bias.data_ptr() if bias is not None else None, float(threshold),
+                                  int(activation), out.data_ptr(), ws.data_ptr(),
+                                  ws.numel() * ws.element_size(), _stream(X)))
     return out
 
 

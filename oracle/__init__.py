@@ -167,8 +167,19 @@ def int_gemm(Xq, CB):
     return C
 
 
-def matmul(X, CB, SCB, threshold=6.0, bias=None, rows=None, cols=None):
-    """The decomposition for the listed output rows/columns.
+def relu_half(h):
+    """ReLU on binary16 bit patterns: every value with the sign bit set
+    (negative numbers, -0, -inf) becomes +0, the rest is unchanged.  Rounding
+    to nearest is monotone and maps 0 to 0, so relu(fp16(v)) = fp16(max(v, 0))
+    for every real v: applying it to the rounded output is the ReLU of the
+    exact output, rounded once."""
+    h = np.ascontiguousarray(h).view(np.uint16)
+    return np.where(h & np.uint16(0x8000), np.uint16(0), h).astype(np.uint16)
+
+
+def matmul(X, CB, SCB, threshold=6.0, bias=None, rows=None, cols=None, relu=False):
+    """The decomposition for the listed output rows/columns (relu: followed
+    by the layer's ReLU, as the feed-forward expansion layers have it).
 
     Returns (out [nrows,ncols] uint16 binary16 bits, O int32, a [nrows] f32).
     O is always found from all rows of X.
@@ -194,4 +205,6 @@ def matmul(X, CB, SCB, threshold=6.0, bias=None, rows=None, cols=None):
                                 _ptr(n), _ptr(a))
     if bad:
         raise OverflowError("%d int32 overflows in the integer product" % bad)
+    if relu:
+        out = relu_half(out)
     return out, O[: int(n[0])].copy(), a[:nrows].copy()

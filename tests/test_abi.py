@@ -108,3 +108,10 @@ def test_other_entry_points_validate(lib):
     assert lib.llmint8_igemm_i32(P, 4, 64, 64, P, None, 0, None) == 1
     assert lib.llmint8_igemm_i32(P, 40, 64, 64, P, P, 2, None) == 2
     assert lib.llmint8_matmul(P, 4, 64, 64, P, P, None, float("nan"), P, P, 1 << 30, None) == 1
+    # the activation entry point: an unknown activation is an argument error,
+    # and it validates like llmint8_matmul otherwise
+    assert lib.llmint8_matmul_act(P, 4, 64, 64, P, P, None, 6.0, 2, P, P, 1 << 30, None) == 1
+    assert lib.llmint8_matmul_act(P, 4, 64, 64, P, P, None, 6.0, -1, P, P, 1 << 30, None) == 1
+    assert lib.llmint8_matmul_act(None, 4, 64, 64, P, P, None, 6.0, 1, P, P, 1 << 30, None) == 1
+    assert lib.llmint8_matmul_act(P, 4, 96, 64, P, P, None, 6.0, 1, P, P, 1 << 30, None) == 2
+    assert lib.llmint8_matmul_act(P, 4, 64, 64, P, P, None, 6.0, 1, P, P, 16, None) == 3

@@ -218,3 +218,38 @@ def test_row_and_column_sampling_consistent():
     part, O2, a2 = oracle.matmul(X, CB, SCB, 6.0, rows=rows, cols=cols)
     assert np.array_equal(O2, O) and np.array_equal(a2, a[rows])
     assert np.array_equal(part, full[np.ix_(rows, cols)])
+
+
+def test_relu_on_binary16_patterns():
+    """relu_half against numpy on every non-NaN binary16 value: negatives,
+    -0 and -inf become +0, the rest is unchanged."""
+    h = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = h.view(f16)
+    keep = ~np.isnan(v)
+    got = oracle.relu_half(h)[keep].view(f16).astype(np.float64)
+    want = np.maximum(v[keep].astype(np.float64), 0.0)
+    assert np.array_equal(got, want)
+    assert not np.any(oracle.relu_half(h)[keep] == np.uint16(0x8000)), "no -0 survives"
+
+
+def test_relu_commutes_with_the_output_rounding():
+    """fp16(max(v, 0)) = relu(fp16(v)) for real v, including values that round
+    to 0 or to the smallest subnormals and values past the fp16 range, so the
+    oracle may apply the ReLU to its once-rounded output."""
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.standard_normal(200000) * s for s in (1e-8, 1e-5, 1.0, 1e3, 1e5)])
+    v = np.concatenate([v, [0.0, -0.0, 2.0 ** -25, -(2.0 ** -25), 65520.0, -65520.0]])
+    a = oracle.double_to_half(np.maximum(v, 0.0))
+    b = oracle.relu_half(oracle.double_to_half(v))
+    assert np.array_equal(a, b)
+
+
+def test_matmul_relu_is_relu_of_the_output():
+    X, W_t, _ = workloads.case(40, 256, 128, n_dims=3, seed=9)
+    CB, SCB = oracle.quantize_weight(W_t)
+    bias = np.random.default_rng(3).standard_normal(128).astype(f16)
+    plain, O, a = oracle.matmul(X, CB, SCB, 6.0, bias=bias)
+    act, O2, a2 = oracle.matmul(X, CB, SCB, 6.0, bias=bias, relu=True)
+    assert np.array_equal(O, O2) and np.array_equal(a, a2)
+    assert np.array_equal(act, oracle.relu_half(plain))
+    assert (_h(act) >= 0).all() and (_h(act) > 0).any() and (_h(plain) < 0).any()
