@@ -229,11 +229,46 @@ def ffn_pair(torch, L, d, steps, warmup, dev):
     return r
 
 
+def fp16_weight_step(torch, L, d, steps, warmup, dev):
+    """fc1 with the weight kept in fp16 (has_fp16_weights=True): every step
+    quantizes W [16384,4096] (llmint8_quantize_weight) before the matmul."""
+    X = torch.from_numpy(d["X"]).to(dev)
+    W = torch.from_numpy(d["W_t"]).to(dev)
+    N, K = W.shape
+    T = X.shape[0]
+    CB = torch.empty((N, K), dtype=torch.int8, device=dev)
+    SCB = torch.empty((N,), dtype=torch.float32, device=dev)
+    out = torch.empty((T, N), dtype=torch.float16, device=dev)
+    ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=dev)
+
+    def step():
+        L.llmint8_quantize_weight(W, CB=CB, SCB=SCB)
+        L.llmint8_matmul(X, CB, SCB, 6.0, out=out, ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    s = (time.perf_counter() - t0) / steps
+    ops = 2.0 * T * K * N
+    wbytes = 3.0 * N * K + 4 * N    # quantization reads 2 B and writes 1 B per weight
+    log("config ffn_6p7b_fc1_fp16_weights: quantize W + matmul %.1f us (%.0f TOP/s)"
+        % (s * 1e6, ops / s / 1e12))
+    del X, W, CB, SCB, out, ws
+    torch.cuda.empty_cache()
+    return {"T": T, "K": K, "N": N, "threshold": 6.0, "step_us": round(s * 1e6, 2),
+            "step_TOPS": round(ops / s / 1e12, 1), "weight_quant_bytes": wbytes}
+
+
 def configs_bench(torch, L, workloads, steps, warmup, ev, dev):
     """The method's other workloads (parity cases), each timed like the main one:
     the 1.3B up-projection, the fc2-like input (every column an outlier) and
     the attention-projection sweep (outlier dims n in {0,6,32,128}, threshold
-    0 and inf, T = 4095), and the FFN pair fc1 -> ReLU -> fc2.  Step figures count 2*T*K*N ops for the whole call;
+    0 and inf, T = 4095), the FFN pair fc1 -> ReLU -> fc2, and fc1 with its
+    weight quantized in every step (fp16 weights kept).  Step figures count 2*T*K*N ops for the whole call;
     the GEMM kernel's own time is given where k_gemm does the work (up to 32
     outlier columns)."""
     res = {}
@@ -269,6 +304,7 @@ def configs_bench(torch, L, workloads, steps, warmup, ev, dev):
     d = workloads.ffn_6p7b(with_fc2=True)
     run("ffn_6p7b_fc2", workloads.ffn_6p7b_fc2_input()["X"], d["W2_t"], 6.0)
     res["ffn_6p7b_pair"] = ffn_pair(torch, L, d, steps, warmup, dev)
+    res["ffn_6p7b_fc1_fp16_weights"] = fp16_weight_step(torch, L, d, steps, warmup, dev)
     del d
     W5 = workloads.attn_proj_sweep(0)["W_t"]
     for nd in (0, 6, 32, 128):
