@@ -200,3 +200,27 @@ def test_stream_asynchrony_and_ordering():
         ev.record(s)
     ev.synchronize()
     assert_fp16_close(out.cpu().numpy(), ref, "side stream")
+
+
+# One activation row with K <= 16384: the weight-streaming kernel quantizes
+# the row in every block.  Outlier counts around the 1024 columns it lists in
+# LDS (beyond them it walks the chunk flags), every column an outlier
+# (threshold 0), none (threshold inf), and K at the 16384 limit and past it
+# (where the separate quantization launch takes over).
+@pytest.mark.parametrize("K,n_dims,thr", [(8192, 1023, 6.0), (8192, 1024, 6.0), (8192, 1025, 6.0),
+                                           (8192, 3000, 6.0), (16384, 6, 0.0), (16384, 6, np.inf),
+                                           (12288, 6, 6.0), (16448, 6, 6.0)])
+@pytest.mark.parametrize("relu", [False, True])
+def test_one_row_decode(K, n_dims, thr, relu):
+    N = 320
+    say("one-row decode K=%d n_dims=%d thr=%s relu=%s" % (K, n_dims, thr, relu))
+    X, W_t, dims = workloads.case(1, K, N, n_dims=n_dims, lo=8, hi=60, p=1.0, seed=K + n_dims)
+    bias = np.random.default_rng(K).standard_normal(N).astype(np.float16)
+    CBr, SCBr = oracle.quantize_weight(W_t)
+    ref, Or, _ = oracle.matmul(X, CBr, SCBr, thr, bias=bias, relu=relu)
+    if np.isfinite(thr) and thr > 0:
+        assert Or.size == n_dims
+    CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
+    out = L.llmint8_matmul_act(h2d(X), CB, SCB, thr, L.ACT_RELU if relu else L.ACT_NONE,
+                               bias=h2d(bias))
+    assert_fp16_close(d2h(out), ref, "one-row decode")
