@@ -62,8 +62,8 @@ def profiled_traffic(summary, key="traffic_bytes_per_launch"):
             h.update(open(os.path.join(ROOT, f), "rb").read())
         if h.hexdigest()[:16] != want:
             return None
-        return int(fields[key])
-    except (KeyError, ValueError, OSError):
+        return int(fields[key].split()[0])   # a figure may carry a note after it
+    except (KeyError, ValueError, IndexError, OSError):
         return None
 
 
