@@ -11,7 +11,8 @@ accepted and reinterpreted.
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (worked examples printed on the pages, closed
-forms, special cases and brute force).  The one part without a pin to an
+forms, special cases and brute force); the zero-point variant's functions by
+``tests/test_oracle_zeropoint.py``.  The one part without a pin to an
 independent value is the fp64 summation order of the fp16 outlier product,
 which sits far below the fp16 output tolerance.
 """
@@ -60,6 +61,12 @@ def _load():
                                   P, I64, P, I64, P, P, P, P]
     lib.oracle_matmul.restype = I64
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_dequant_weight_zp_n.argtypes = [P, P, P, I64, P]
+    lib.oracle_quantize_weight_zp.argtypes = [P, I64, I64, P, P, P]
+    lib.oracle_quantize_rows_zp.argtypes = [P, I64, I64, P, I64, P, I64, P, P, P]
+    lib.oracle_matmul_zp.argtypes = [P, I64, I64, I64, P, P, P, P, ctypes.c_float,
+                                     P, I64, P, I64, P, P, P, P, P]
+    lib.oracle_matmul_zp.restype = I64
     _lib = lib
     return lib
 
@@ -208,3 +215,76 @@ def matmul(X, CB, SCB, threshold=6.0, bias=None, rows=None, cols=None, relu=Fals
     if relu:
         out = relu_half(out)
     return out, O[: int(n[0])].copy(), a[:nrows].copy()
+
+
+# ---------------------------------------------------------------------------
+# Zero-point (asymmetric) vector-wise variant.  The readings of the page's
+# garbled zero-point formulas are stated in llmint8_oracle.c; in short, per
+# vector: range [min(min,0), max(max,0)], d = fp32(max' - min'),
+# nd = fp32(254/d), zp = RNE(nd*min') + 127, code = min(RNE(nd*x) - zp, 127),
+# and x ~= (code + zp) / nd.
+# ---------------------------------------------------------------------------
+def dequant_weight_zp(cb, zp, nd):
+    """Binary16 value of fp32((cb + zp) / nd), element-wise (0 where nd = 0)."""
+    cb, zp, nd = np.broadcast_arrays(np.asarray(cb, np.int8), np.asarray(zp, np.int32),
+                                     np.asarray(nd, np.float32))
+    cb, zp, nd = (np.ascontiguousarray(v) for v in (cb, zp, nd))
+    out = np.empty(cb.shape, np.uint16)
+    _load().oracle_dequant_weight_zp_n(_ptr(cb), _ptr(zp), _ptr(nd), cb.size, _ptr(out))
+    return out
+
+
+def quantize_weight_zp(W_t):
+    """W_t: [N,K] fp16.  Returns (CB [N,K] int8, ND [N] f32, ZP [N] int32)."""
+    W_t = _bits(W_t)
+    N, K = W_t.shape
+    CB = np.empty((N, K), np.int8)
+    ND = np.empty((N,), np.float32)
+    ZP = np.empty((N,), np.int32)
+    _load().oracle_quantize_weight_zp(_ptr(W_t), K, N, _ptr(CB), _ptr(ND), _ptr(ZP))
+    return CB, ND, ZP
+
+
+def quantize_rows_zp(X, O, rows=None):
+    """Returns (Xq [nrows,K] int8, nd [nrows] f32, zp [nrows] int32) for the
+    listed rows (all by default); outlier columns hold -zp."""
+    X = _bits(X)
+    T, K = X.shape
+    O = np.ascontiguousarray(O, np.int32)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    nrows = T if rows_arr is None else rows_arr.size
+    Xq = np.empty((nrows, K), np.int8)
+    nd = np.empty((nrows,), np.float32)
+    zp = np.empty((nrows,), np.int32)
+    _load().oracle_quantize_rows_zp(_ptr(X), T, K, _ptr(O), O.size, _ptr(rows_arr), nrows,
+                                    _ptr(Xq), _ptr(nd), _ptr(zp))
+    return Xq, nd, zp
+
+
+def matmul_zp(X, CB, ND, ZP, threshold=6.0, bias=None, rows=None, cols=None):
+    """The decomposition with zero-point quantization on both operands, for
+    the listed output rows/columns.  Returns (out [nrows,ncols] uint16
+    binary16 bits, O int32, nd [nrows] f32, zp [nrows] int32)."""
+    X = _bits(X)
+    T, K = X.shape
+    CB = np.ascontiguousarray(CB, np.int8)
+    ND = np.ascontiguousarray(ND, np.float32)
+    ZP = np.ascontiguousarray(ZP, np.int32)
+    N = CB.shape[0]
+    assert CB.shape == (N, K) and ND.shape == (N,) and ZP.shape == (N,)
+    b = _bits(bias) if bias is not None else None
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    cols_arr = None if cols is None else np.ascontiguousarray(cols, np.int64)
+    nrows = T if rows_arr is None else rows_arr.size
+    ncols = N if cols_arr is None else cols_arr.size
+    out = np.empty((nrows, ncols), np.uint16)
+    O = np.empty((max(K, 1),), np.int32)
+    n = np.zeros((1,), np.int64)
+    nd = np.empty((max(nrows, 1),), np.float32)
+    zp = np.empty((max(nrows, 1),), np.int32)
+    bad = _load().oracle_matmul_zp(_ptr(X), T, K, N, _ptr(CB), _ptr(ND), _ptr(ZP), _ptr(b),
+                                   float(threshold), _ptr(rows_arr), nrows, _ptr(cols_arr),
+                                   ncols, _ptr(out), _ptr(O), _ptr(n), _ptr(nd), _ptr(zp))
+    if bad:
+        raise OverflowError("%d int32 overflows in the integer product" % bad)
+    return out, O[: int(n[0])].copy(), nd[:nrows].copy(), zp[:nrows].copy()

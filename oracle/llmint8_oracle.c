@@ -36,6 +36,8 @@
  *     SCB, because only CB and SCB exist once the weight is quantized;
  *   - the output is one rounding to fp16 of the exact-as-possible (fp64)
  *     sum of the dequantized int8 part, the outlier part and the bias.
+ * The zero-point (asymmetric) variant near the end of this file has its own
+ * list of readings there.
  *
  * fp16 values cross this interface as raw IEEE binary16 bit patterns
  * (uint16_t); the codec below is written from the bit layout.
@@ -351,6 +353,207 @@ int64_t oracle_matmul(const uint16_t *X, int64_t T, int64_t K, int64_t N,
     free(Xq);
     free(a);
     return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Zero-point (asymmetric) vector-wise variant ([SUM] "8-bit Data Types and  */
+/* Quantization", zeropoint quantization: scale by the normalized dynamic    */
+/* range nd = 2*127/(max - min), shift by an integer zero point zp so that   */
+/* the values fill [-127, 127]; the product of two such numbers is           */
+/* (A_i8 + zp_a)(B_i8 + zp_b), accumulated in int32 and dequantized by       */
+/* dividing by nd_a*nd_b; [SUM] "Int8 Matrix Multiplication with 16-bit      */
+/* Float Inputs and Outputs" names nd_x, nd_w as the zeropoint constants).   */
+/*                                                                            */
+/* Readings (the page's zero-point formulas are garbled; these are the       */
+/* plainest consistent ones, each listed in the design notes):               */
+/*   - one (nd, zp) per vector: per row of X over its non-outlier columns,   */
+/*     per output column of W over all of K (vector-wise, like the absmax    */
+/*     variant);                                                             */
+/*   - the range always contains 0: min' = min(min, 0), max' = max(max, 0),  */
+/*     so zp fits the page's int16 (it lies in [-127, 127]), the value 0 has */
+/*     an exact code (-zp), and every |A_i8 + zp| <= 254;                    */
+/*   - d = fp32(max' - min') and nd = fp32(254 / d), each rounded once;      */
+/*     d = 0 (an all-zero vector) gives nd = 0, zp = 0 and codes 0;          */
+/*   - zp = RNE(nd * min') + 127 and A_i8 = min(RNE(nd * x) - zp, 127), both */
+/*     roundings of the exact product nd * x (ties to even); the clamp only  */
+/*     acts when fp32 rounding makes RNE(nd*max') - RNE(nd*min') = 255;      */
+/*   - outlier columns hold the code of 0, -zp, so that A_i8 + zp_a = 0      */
+/*     there and they add nothing to the integer product;                    */
+/*   - the fp16 outlier product uses the weight dequantized as               */
+/*     fp16(fp32(CB + zp) / nd) (one fp32 division, then one rounding to     */
+/*     fp16; 0 when nd = 0).                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Exact product of an fp32 scale and an fp16 value (24 + 11 significant bits
+ * fit fp64's 53), rounded to the nearest integer with ties to even (rint in
+ * the default rounding mode). */
+static int64_t rne_product(float nd, double x)
+{
+    return (int64_t)rint((double)nd * x);
+}
+
+/* The zero-point parameters of one vector from its smallest and largest
+ * value (binary16, already widened to double) with 0 added to the range. */
+static void zp_params(double vmin, double vmax, float *nd, int32_t *zp)
+{
+    if (vmin > 0.0)
+        vmin = 0.0;
+    if (vmax < 0.0)
+        vmax = 0.0;
+    float d = (float)vmax - (float)vmin;      /* one fp32 rounding */
+    if (d == 0.0f) {
+        *nd = 0.0f;
+        *zp = 0;
+        return;
+    }
+    float n = 254.0f / d;                     /* one fp32 division */
+    *nd = n;
+    *zp = (int32_t)(rne_product(n, vmin) + 127);
+}
+
+/* Code of value x in a vector with parameters (nd, zp). */
+static int8_t zp_code(float nd, int32_t zp, double x)
+{
+    if (nd == 0.0f)
+        return 0;
+    int64_t q = rne_product(nd, x) - zp;
+    if (q > 127)
+        q = 127;
+    return (int8_t)q;
+}
+
+/* Dequantized fp16 weight of code cb in a column with parameters (nd, zp). */
+uint16_t oracle_dequant_weight_zp(int8_t cb, int32_t zp, float nd)
+{
+    if (nd == 0.0f)
+        return 0;
+    float w = (float)(cb + zp) / nd;          /* exact numerator, one division */
+    return oracle_double_to_half((double)w);  /* fp32 -> fp16, one rounding */
+}
+
+/* W_t: [N,K] binary16.  CB: [N,K] int8 codes, ND: [N] nd, ZP: [N] zp. */
+void oracle_quantize_weight_zp(const uint16_t *W_t, int64_t K, int64_t N,
+                               int8_t *CB, float *ND, int32_t *ZP)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint16_t *row = W_t + n * K;
+        double vmin = 0.0, vmax = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = oracle_half_to_double(row[k]);
+            if (v < vmin)
+                vmin = v;
+            if (v > vmax)
+                vmax = v;
+        }
+        zp_params(vmin, vmax, &ND[n], &ZP[n]);
+        for (int64_t k = 0; k < K; ++k)
+            CB[n * K + k] = zp_code(ND[n], ZP[n], oracle_half_to_double(row[k]));
+    }
+}
+
+/* For each listed row t (all T when rows == NULL): (nd, zp) over the
+ * non-outlier columns, Xq[i,k] = the code of X[t,k] for k not in O and -zp
+ * (the code of 0) for k in O. */
+void oracle_quantize_rows_zp(const uint16_t *X, int64_t T, int64_t K,
+                             const int32_t *O, int64_t n,
+                             const int64_t *rows, int64_t nrows,
+                             int8_t *Xq, float *nd, int32_t *zp)
+{
+    unsigned char *isout = outlier_mask(O, n, K);
+    if (rows == NULL)
+        nrows = T;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t t = rows ? rows[i] : i;
+        const uint16_t *xr = X + t * K;
+        double vmin = 0.0, vmax = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            if (isout[k])
+                continue;
+            double v = oracle_half_to_double(xr[k]);
+            if (v < vmin)
+                vmin = v;
+            if (v > vmax)
+                vmax = v;
+        }
+        zp_params(vmin, vmax, &nd[i], &zp[i]);
+        for (int64_t k = 0; k < K; ++k)
+            Xq[i * K + k] = isout[k] ? (int8_t)(-zp[i])
+                                     : zp_code(nd[i], zp[i], oracle_half_to_double(xr[k]));
+    }
+    free(isout);
+}
+
+/* out[i,c] = fp16( sum_k (Xq[t,k] + zp_a[t]) * (CB[c,k] + ZP[c]) / (nd_a[t] * ND[c])
+ *                  + sum_{k in O} X[t,k] * Wdq_zp(CB[c,k], ZP[c], ND[c])  [+ bias[c]] )
+ * with the shifted products summed directly in int64 (the page's 16-bit
+ * multiply form, no unrolling) and the rest in fp64, rounded once.  A zero
+ * nd on either side makes the integer term 0.  Arguments as oracle_matmul;
+ * nd_out / zp_out ([nrows]) receive the row parameters.  Returns the number
+ * of integer sums outside int32 (0 expected for K <= 33286). */
+int64_t oracle_matmul_zp(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                         const int8_t *CB, const float *ND, const int32_t *ZP,
+                         const uint16_t *bias, float threshold,
+                         const int64_t *rows, int64_t nrows,
+                         const int64_t *cols, int64_t ncols, uint16_t *out,
+                         int32_t *O_out, int64_t *n_out, float *nd_out, int32_t *zp_out)
+{
+    if (rows == NULL)
+        nrows = T;
+    if (cols == NULL)
+        ncols = N;
+    int32_t *O = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
+    int64_t n = oracle_outlier_columns(X, T, K, threshold, O);
+    int8_t *Xq = (int8_t *)malloc((size_t)(nrows * K > 0 ? nrows * K : 1));
+    float *nd = (float *)malloc(sizeof(float) * (size_t)(nrows > 0 ? nrows : 1));
+    int32_t *zp = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nrows > 0 ? nrows : 1));
+    oracle_quantize_rows_zp(X, T, K, O, n, rows, nrows, Xq, nd, zp);
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t t = rows ? rows[i] : i;
+        for (int64_t j = 0; j < ncols; ++j) {
+            int64_t c = cols ? cols[j] : j;
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += ((int64_t)Xq[i * K + k] + zp[i]) * ((int64_t)CB[c * K + k] + ZP[c]);
+            if (s > INT32_MAX || s < INT32_MIN)
+                ++bad;
+            double acc = 0.0;
+            if (nd[i] != 0.0f && ND[c] != 0.0f)
+                acc = (double)s / ((double)nd[i] * (double)ND[c]);
+            for (int64_t jj = 0; jj < n; ++jj) {
+                int64_t k = O[jj];
+                acc += oracle_half_to_double(X[t * K + k]) *
+                       oracle_half_to_double(oracle_dequant_weight_zp(CB[c * K + k], ZP[c], ND[c]));
+            }
+            if (bias)
+                acc += oracle_half_to_double(bias[c]);
+            out[i * ncols + j] = oracle_double_to_half(acc);
+        }
+    }
+    if (O_out)
+        memcpy(O_out, O, sizeof(int32_t) * (size_t)n);
+    if (n_out)
+        *n_out = n;
+    if (nd_out)
+        memcpy(nd_out, nd, sizeof(float) * (size_t)nrows);
+    if (zp_out)
+        memcpy(zp_out, zp, sizeof(int32_t) * (size_t)nrows);
+    free(O);
+    free(Xq);
+    free(nd);
+    free(zp);
+    return bad;
+}
+
+/* Element-wise form of oracle_dequant_weight_zp (for the tests). */
+void oracle_dequant_weight_zp_n(const int8_t *cb, const int32_t *zp, const float *nd,
+                                int64_t len, uint16_t *out)
+{
+    for (int64_t i = 0; i < len; ++i)
+        out[i] = oracle_dequant_weight_zp(cb[i], zp[i], nd[i]);
 }
 
 /* Number of threads the parallel loops use (for reporting the CPU baseline). */
