@@ -183,6 +183,82 @@ LLMINT8_API llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, i
                                      hipStream_t stream);
 
 /*
+ * Zero-point (asymmetric) variant of the decomposition.  The LLM.int8()
+ * summary (kurtkim.github.io, "LLM.int8()", section "8-bit Data Types and
+ * Quantization", zeropoint quantization; and "Int8 Matrix Multiplication with
+ * 16-bit Float Inputs and Outputs") maps a vector's range onto [-127, 127]
+ * with the normalized dynamic range nd = 2*127/(max - min) and an integer
+ * zero point zp, multiplies the shifted values (A + zp_a)(B + zp_b) in
+ * integers and dequantizes by dividing by nd_a*nd_b.  Here, per vector (a row
+ * of X over its non-outlier columns; a row of W_t, i.e. an output column of
+ * W, over all K):
+ *
+ *   min' = min(min, 0), max' = max(max, 0)     (0 joins every range)
+ *   d    = fp32(max' - min'),  nd = fp32(254 / d)   (d = 0: nd = 0, zp = 0)
+ *   zp   = RNE(nd * min') + 127                     (in [-127, 127])
+ *   code = min(RNE(nd * x) - zp, 127)               (in [-127, 127])
+ *
+ * RNE rounds the exact product nd*x to the nearest integer, ties to even;
+ * code + zp = RNE(nd*x) is the page's shifted value and x ~= (code + zp)/nd.
+ * Outlier columns of X (as for llmint8_matmul) hold the code of 0, -zp, so
+ * they add nothing to the integer sum, and
+ *
+ *   out[t,n] = fp16( sum_k (Xq[t,k] + zp_a[t]) * (CB[n,k] + ZP[n]) / (nd_a[t] * ND[n])
+ *                    + sum_{k in O} X[t,k] * fp16(fp32(CB[n,k] + ZP[n]) / ND[n])  [+ bias[n]] )
+ *
+ * (the integer term is 0 when either nd is 0).  The integer sum is formed
+ * unrolled, as the page writes it when no 16-bit multiply exists:
+ * C + ZP[n]*(rs_a[t] + K*zp_a[t]) + zp_a[t]*RS[n] with C the int8 product and
+ * rs, RS the code sums; |code + zp| <= 254 keeps it exact in int32 for
+ * K <= 33286, the limit of these entry points (larger K ->
+ * LLMINT8_ERR_UNSUPPORTED_SHAPE).  Other conventions as above.
+ */
+
+/*
+ * Zero-point weight quantization, once per weight.
+ *   W_t in: fp16 [N,K];  CB out: int8 [N,K] codes;  ND out: fp32 [N] nd;
+ *   ZP out: int32 [N] zero points;  RS out: int32 [N], RS[n] = sum_k CB[n,k].
+ */
+LLMINT8_API llmint8_status_t llmint8_quantize_weight_zp(const uint16_t *W_t, int64_t K, int64_t N,
+                                                        int8_t *CB, float *ND, int32_t *ZP,
+                                                        int32_t *RS, hipStream_t stream);
+
+/*
+ * Zero-point activation quantization with outlier detection (as
+ * llmint8_quantize_act, same workspace query llmint8_quantize_act_workspace_bytes).
+ *   X in: fp16 [T,K];  Xq out: int8 [T,K];  nd out: fp32 [T];
+ *   row_zp out: int32 [T][2] (8-byte aligned), row_zp[t] = {zp_a[t], sum_k Xq[t,k]};
+ *   outlier_idx / n_outliers out: as llmint8_quantize_act.
+ */
+LLMINT8_API llmint8_status_t llmint8_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K,
+                                                     float threshold, int8_t *Xq, float *nd,
+                                                     int32_t *row_zp, int32_t *outlier_idx,
+                                                     int32_t *n_outliers, void *ws,
+                                                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The zero-point decomposition: out [T,N] fp16 from X [T,K] fp16 and the
+ * output of llmint8_quantize_weight_zp (CB, ND, ZP, RS; ND, ZP and RS
+ * 16-byte aligned), with optional bias and the threshold as llmint8_matmul.
+ * Workspace: llmint8_workspace_bytes(T, K, N).
+ */
+LLMINT8_API llmint8_status_t llmint8_matmul_zp(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                               const int8_t *CB, const float *ND,
+                                               const int32_t *ZP, const int32_t *RS,
+                                               const uint16_t *bias, float threshold,
+                                               uint16_t *out, void *ws, size_t ws_bytes,
+                                               hipStream_t stream);
+
+/* llmint8_matmul_zp with the path choice and timing events of llmint8_matmul_path. */
+LLMINT8_API llmint8_status_t llmint8_matmul_zp_path(const uint16_t *X, int64_t T, int64_t K,
+                                                    int64_t N, const int8_t *CB, const float *ND,
+                                                    const int32_t *ZP, const int32_t *RS,
+                                                    const uint16_t *bias, float threshold,
+                                                    uint16_t *out, void *ws, size_t ws_bytes,
+                                                    int path, hipEvent_t main_start,
+                                                    hipEvent_t main_stop, hipStream_t stream);
+
+/*
  * The int8 product alone, C[t,n] = sum_k Xq[t,k] * CB[n,k] in int32 (LLM.int8()
  * summary, section "Int8 Matrix Multiplication with 16-bit Float Inputs and
  * Outputs"), through the same main loops as llmint8_matmul with the epilogue

@@ -74,7 +74,11 @@ __device__ __forceinline__ OutlierPrefetch prefetch_outliers(const int8_t *B, in
 
 // 16x16 accumulator layout: lane holds column n = n0 + lane%16 and rows
 // t = 4*(lane/16) + q.
-template <bool kRawI32, bool kRelu = false>
+// Zero-point variant (kZp): ep.a and ep.scb hold nd of the rows and columns,
+// and the integer part is the shifted sum C + zp_b*(rs_a + K*zp_a) +
+// zp_a*rs_b, exact in wrapping 32-bit arithmetic (its true value fits int32),
+// divided by nd_a*nd_b; the outlier weights are fp16((cb + zp_b)/nd_b).
+template <bool kRawI32, bool kRelu = false, bool kZp = false>
 __device__ __forceinline__ void epilogue(const v4i acc, int lane, int64_t n, int64_t T, int64_t K,
                                          int64_t N, const int8_t *B, const EpilogueArgs &ep,
                                          const OutlierPrefetch &pre)
@@ -87,13 +91,27 @@ __device__ __forceinline__ void epilogue(const v4i acc, int lane, int64_t n, int
                 ep.c_i32[(t0 + q) * N + n] = acc[q];
     } else {
         const float sn = ep.scb[n];
-        const float sn_d = sn * (1.0f / 16129.0f);
         const float bias = ep.bias ? h2f(ep.bias[n]) : 0.0f;
+        const int zb = kZp ? ep.zp_b[n] : 0;
         float v[4];
+        if constexpr (kZp) {
+            const float ib = zp_inv(sn);
+            const unsigned rb = (unsigned)ep.rs_b[n];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t t = t0 + q < T ? t0 + q : T - 1;
-            v[q] = (float)acc[q] * (ep.a[t] * sn_d);
+            for (int q = 0; q < 4; ++q) {
+                const int64_t t = t0 + q < T ? t0 + q : T - 1;
+                const int2 z = ep.row_zp[t];
+                const unsigned ra = (unsigned)z.y + (unsigned)K * (unsigned)z.x;
+                const unsigned c = (unsigned)acc[q] + (unsigned)zb * ra + (unsigned)z.x * rb;
+                v[q] = (float)(int)c * (zp_inv(ep.a[t]) * ib);
+            }
+        } else {
+            const float sn_d = sn * (1.0f / 16129.0f);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t t = t0 + q < T ? t0 + q : T - 1;
+                v[q] = (float)acc[q] * (ep.a[t] * sn_d);
+            }
         }
         // Outlier columns in ascending order, kPrefetchOutliers at a time.  All
         // loads are unconditional so that none waits on its own: x_out rows
@@ -109,7 +127,9 @@ __device__ __forceinline__ void epilogue(const v4i acc, int lane, int64_t n, int
                     const int o = o0 + j < pre.nout ? ep.O[o0 + j] : 0;
                     cb = B[n * K + o];
                 }
-                w[j] = o0 + j < pre.nout ? h2f(dequant_w(cb, sn)) : 0.0f;
+                w[j] = o0 + j < pre.nout
+                           ? h2f(kZp ? dequant_w_zp(cb, zb, sn) : dequant_w(cb, sn))
+                           : 0.0f;
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -174,7 +194,7 @@ struct CfgRs {
     static_assert(kWait < 64, "vmcnt range");
 };
 
-template <class C, bool kRawI32, bool kRelu = false>
+template <class C, bool kRawI32, bool kRelu = false, bool kZp = false>
 __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restrict__ A,
                                                            const int8_t *__restrict__ B,
                                                            int64_t T, int64_t K, int64_t N,
@@ -341,7 +361,7 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
              ...);
         }(std::make_integer_sequence<int, C::kUnroll>{});
     }
-    epilogue<kRawI32, kRelu>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
+    epilogue<kRawI32, kRelu, kZp>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
 }
 
 // ---------------------------------------------------------------------------
@@ -432,12 +452,14 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_lds(const int8_t *__rest
     epilogue<kRawI32>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
 }
 
-template <class C, bool R, bool kRelu = false>
+template <class C, bool R, bool kRelu = false, bool kZp = false>
 struct RsKernel {
-    static constexpr auto fn = k_decode_rs<C, R, kRelu>;
+    static constexpr auto fn = k_decode_rs<C, R, kRelu, kZp>;
 };
 template <class C, bool R>
 using RsKernelRelu = RsKernel<C, R, true>;
+template <class C, bool R>
+using RsKernelZp = RsKernel<C, R, false, true>;
 template <class C, bool R>
 struct LdsKernel {
     static constexpr auto fn = k_decode_lds<C, R>;
@@ -475,6 +497,8 @@ hipError_t launch_rs(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, i
 {
     if (C::kSync && N % (16 * C::WAVES) != 0)
         return hipErrorInvalidValue;   // a block's wavefronts must all reach the barriers
+    if (ep.row_zp && !ep.c_i32)
+        return launch_kernel<C, RsKernelZp>(Xq, CB, T, K, N, ep, s, ev0, ev1);
     if (ep.act && !ep.c_i32)
         return launch_kernel<C, RsKernelRelu>(Xq, CB, T, K, N, ep, s, ev0, ev1);
     return launch_kernel<C, RsKernel>(Xq, CB, T, K, N, ep, s, ev0, ev1);

@@ -519,6 +519,29 @@ __device__ __forceinline__ v4i outlier_frag(const char *orows, int r, int c)
                                           16 * OutlierRows<C>::slot(r, c));
 }
 
+// Zero-point variant, per output row t: ia = 1/nd_a[t], za = zp_a[t] and
+// ra = rs_a[t] + K*zp_a[t] (mod 2^32), so that the shifted integer sum of
+// an output is C + zp_b[n]*ra + za*rs_b[n] -- exact in wrapping 32-bit
+// arithmetic because its true value fits int32 (K <= 33286).
+__device__ __forceinline__ void zp_row(const EpilogueArgs &ep, int64_t t, int64_t K, float &ia,
+                                       int &za, int &ra)
+{
+    ia = zp_inv(ep.a[t]);
+    const int2 z = ep.row_zp[t];
+    za = z.x;
+    ra = (int)((unsigned)z.y + (unsigned)K * (unsigned)z.x);
+}
+
+// Zero-point variant: the dequantized int8 part of one output, from the
+// int8 sum acc, the row's za and ra, the column's zp_b and rs_b, and 1/nd_a
+// (ia) and nd_b.
+__device__ __forceinline__ float zp_dequant(int acc, int za, int ra, int zb, int rb, float ia,
+                                            float ndb)
+{
+    const unsigned c = (unsigned)acc + (unsigned)zb * (unsigned)ra + (unsigned)za * (unsigned)rb;
+    return (float)(int)c * (ia * zp_inv(ndb));
+}
+
 // Up to 32 outlier columns: their fp16 fragments (loaded before the main
 // loop, rows of 32 halves) go straight into the MFMAs, and each 32x32
 // accumulator tile is finished on its own (dequantize, fp16 MFMA over the
@@ -526,8 +549,9 @@ __device__ __forceinline__ v4i outlier_frag(const char *orows, int r, int c)
 // wavefront has stopped reading; then the whole block tile is written out.
 // Operands come from clamped addresses and the column scales are loaded one
 // column group ahead, so no latency is paid per accumulator tile.
-template <class C, bool kBias, bool kRelu>
+template <class C, bool kBias, bool kRelu, bool kZp>
 __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], const float (&at)[C::FM],
+                                            const int (&za)[C::FM], const int (&ra)[C::FM],
                                             const char *orows,
                                             char *smem, const EpilogueArgs &ep, int64_t m0,
                                             int64_t n0, int64_t T, int64_t N, int nout, int wm,
@@ -545,8 +569,9 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
             xo[i][s2] = outlier_frag<C>(orows, wm * (C::BM / C::WM) + i * 32 + tl, 2 * s2 + hi);
-    // column scales and bias of column group j, fetched one group ahead
+    // column factors and bias of column group j, fetched one group ahead
     v4f sn[2][4];
+    v4i zb[2][4], rb[2][4];   // zero-point variant only
     uint2 bias[2][4];
     auto load_cols = [&](int j, int buf) {
 #pragma unroll
@@ -554,6 +579,10 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
             int64_t nc = nw + j * 32 + 8 * g + nl;
             nc = nc < N ? nc : N - 4;
             sn[buf][g] = *reinterpret_cast<const v4f *>(ep.scb + nc);
+            if constexpr (kZp) {
+                zb[buf][g] = *reinterpret_cast<const v4i *>(ep.zp_b + nc);
+                rb[buf][g] = *reinterpret_cast<const v4i *>(ep.rs_b + nc);
+            }
             if constexpr (kBias)
                 bias[buf][g] = *reinterpret_cast<const uint2 *>(ep.bias + nc);
         }
@@ -573,8 +602,13 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
         for (int i = 0; i < C::FM; ++i) {
             v16f d;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                d[r] = (float)acc[i][j][r] * (at[i] * sn[cb][r / 4][r % 4]);
+            for (int r = 0; r < 16; ++r) {
+                if constexpr (kZp)
+                    d[r] = zp_dequant(acc[i][j][r], za[i], ra[i], zb[cb][r / 4][r % 4],
+                                      rb[cb][r / 4][r % 4], at[i], sn[cb][r / 4][r % 4]);
+                else
+                    d[r] = (float)acc[i][j][r] * (at[i] * sn[cb][r / 4][r % 4]);
+            }
             if (nout > 0) {
                 d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wo[0]),
                                                          __builtin_bit_cast(v8h, xo[i][0]), d, 0, 0, 0);
@@ -618,9 +652,10 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
 // there, so the two share registers) onto which the fp16 MFMAs add; then
 // the bias, one rounding, and the tile goes out through LDS like
 // finish_tile's.
-template <class C, bool kRelu>
+template <class C, bool kRelu, bool kZp>
 __device__ __forceinline__ void outlier_pass(const v16i (&acc)[C::FM][C::FN],
-                                             const float (&at)[C::FM], char *smem,
+                                             const float (&at)[C::FM], const int (&za)[C::FM],
+                                             const int (&ra)[C::FM], char *smem,
                                              const EpilogueArgs &ep, int64_t m0, int64_t n0,
                                              int64_t T, int64_t K, int64_t N, int nout, int wm,
                                              int wn, int wave, int lane, int tid)
@@ -632,16 +667,27 @@ __device__ __forceinline__ void outlier_pass(const v16i (&acc)[C::FM][C::FN],
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
             v4f sn[4];
+            v4i zb[4], rb[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int64_t n = nw + j * 32 + 8 * g + nl;
-                sn[g] = *reinterpret_cast<const v4f *>(ep.scb + (n < N ? n : N - 4));
+                int64_t n = nw + j * 32 + 8 * g + nl;
+                n = n < N ? n : N - 4;
+                sn[g] = *reinterpret_cast<const v4f *>(ep.scb + n);
+                if constexpr (kZp) {
+                    zb[g] = *reinterpret_cast<const v4i *>(ep.zp_b + n);
+                    rb[g] = *reinterpret_cast<const v4i *>(ep.rs_b + n);
+                }
             }
 #pragma unroll
             for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    accf[i][j][r] = (float)acc[i][j][r] * (at[i] * sn[r / 4][r % 4]);
+                for (int r = 0; r < 16; ++r) {
+                    if constexpr (kZp)
+                        accf[i][j][r] = zp_dequant(acc[i][j][r], za[i], ra[i], zb[r / 4][r % 4],
+                                                   rb[r / 4][r % 4], at[i], sn[r / 4][r % 4]);
+                    else
+                        accf[i][j][r] = (float)acc[i][j][r] * (at[i] * sn[r / 4][r % 4]);
+                }
         }
     } else {   // the int8 part is all zeros
 #pragma unroll
@@ -691,7 +737,7 @@ __device__ __forceinline__ void outlier_pass(const v16i (&acc)[C::FM][C::FN],
     write_tile<C>(smem, ep, m0, n0, T, N, tid);
 }
 
-template <class C, bool kRawI32, bool kRelu>
+template <class C, bool kRawI32, bool kRelu, bool kZp = false>
 __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__ A,
                                                       const int8_t *__restrict__ B, int64_t T,
                                                       int64_t K, int64_t N, EpilogueArgs ep)
@@ -759,17 +805,21 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
         }
     } else {
         float at[C::FM];
+        int za[C::FM], ra[C::FM];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
             const int64_t t = tw + i * 32 + tl;
-            at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
+            if constexpr (kZp)
+                zp_row(ep, t < T ? t : T - 1, K, at[i], za[i], ra[i]);
+            else
+                at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
         }
         if (ep.bias)
-            finish_tile<C, true, kRelu>(acc, at, orows, smem, ep, m0, n0, T, N, nout, wm, wn, lane,
-                                        tid);
+            finish_tile<C, true, kRelu, kZp>(acc, at, za, ra, orows, smem, ep, m0, n0, T, N, nout,
+                                             wm, wn, lane, tid);
         else
-            finish_tile<C, false, kRelu>(acc, at, orows, smem, ep, m0, n0, T, N, nout, wm, wn, lane,
-                                         tid);
+            finish_tile<C, false, kRelu, kZp>(acc, at, za, ra, orows, smem, ep, m0, n0, T, N, nout,
+                                              wm, wn, lane, tid);
     }
 }
 
@@ -779,7 +829,7 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
 // fp16 pass over the outlier columns.  A kernel of its own so that the
 // registers this path needs do not cost k_gemm's epilogue; one tile per
 // block (a persistent tile loop makes the compiler spill around it).
-template <class C, bool kRelu>
+template <class C, bool kRelu, bool kZp = false>
 __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restrict__ A,
                                                            const int8_t *__restrict__ B,
                                                            int64_t T, int64_t K, int64_t N,
@@ -812,13 +862,18 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restr
         run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
     }
     float at[C::FM];
+    int za[C::FM], ra[C::FM];
     const int64_t tw = m0 + wm * (C::BM / C::WM) + (lane & 31);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
         const int64_t t = tw + i * 32;
-        at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
+        if constexpr (kZp)
+            zp_row(ep, t < T ? t : T - 1, K, at[i], za[i], ra[i]);
+        else
+            at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
     }
-    outlier_pass<C, kRelu>(acc, at, smem, ep, m0, n0, T, K, N, nout, wm, wn, wave, lane, tid);
+    outlier_pass<C, kRelu, kZp>(acc, at, za, ra, smem, ep, m0, n0, T, K, N, nout, wm, wn, wave,
+                                lane, tid);
 }
 
 // The int8 GEMM (K must be a multiple of C::ROWB) with its fused epilogue
@@ -842,6 +897,9 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
     if (ep.c_i32)
         hipLaunchKernelGGL((k_gemm<C, true, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K,
                            N, ep);
+    else if (ep.row_zp)
+        hipLaunchKernelGGL((k_gemm<C, false, false, true>), grid, dim3(C::kThreads), 0, s, Xq, CB,
+                           T, K, N, ep);
     else if (ep.act)
         hipLaunchKernelGGL((k_gemm<C, false, true>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K,
                            N, ep);
@@ -854,7 +912,10 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
             return e;
     }
     if (!ep.c_i32) {
-        if (ep.act)
+        if (ep.row_zp)
+            hipLaunchKernelGGL((k_gemm_many<C, false, true>), grid, dim3(C::kThreads), 0, s, Xq, CB,
+                               T, K, N, ep);
+        else if (ep.act)
             hipLaunchKernelGGL((k_gemm_many<C, true>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K,
                                N, ep);
         else

@@ -57,6 +57,23 @@ __device__ __forceinline__ uint16_t dequant_w(int cb, float scb)
     return f2h(((float)cb * scb) / 127.0f);
 }
 
+// Zero-point variant: the fp16 weight fp16(fp32(cb + zp) / nd) of code cb
+// in a column with parameters (nd, zp); 0 when nd = 0 (an all-zero column).
+// cb + zp is an integer of at most 9 bits, exact in fp32; one correctly
+// rounded division, then the rounding to fp16.
+__device__ __forceinline__ uint16_t dequant_w_zp(int cb, int zp, float nd)
+{
+    return nd > 0.0f ? f2h((float)(cb + zp) / nd) : (uint16_t)0;
+}
+
+// 1/nd for the zero-point dequantization (0 when nd = 0).  v_rcp_f32 is
+// within 1 ulp: the dequantized value, an fp32 product rounded to fp16 at
+// the end, moves by a few fp32 ulps at most.
+__device__ __forceinline__ float zp_inv(float nd)
+{
+    return nd > 0.0f ? __builtin_amdgcn_rcpf(nd) : 0.0f;
+}
+
 __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
 {
 #pragma unroll
@@ -69,7 +86,8 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
 
 // Workspace segments of one llmint8_matmul call (byte offsets from the base).
 struct MatmulWorkspace {
-    size_t partial, mask, chunk_pre, outlier_idx, n_outliers, row_absmax, xq, x_out, w_out, total;
+    size_t partial, mask, chunk_pre, outlier_idx, n_outliers, row_absmax, row_zp, xq, x_out, w_out,
+        total;
 };
 MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N);
 size_t act_workspace_bytes(int64_t K);
@@ -84,9 +102,10 @@ hipError_t launch_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N, int
 // stride.  w_out == null skips it.
 struct GatherArgs {
     const int8_t *CB;
-    const float *SCB;
+    const float *SCB;   // zero-point variant: nd of each column
     int64_t N;
     uint16_t *w_out;
+    const int32_t *zp = nullptr;   // zero-point variant: zp of each column (else null)
 };
 
 // Row ranges of the outlier detection: the partial-flag buffer holds
@@ -124,8 +143,8 @@ hipError_t launch_quantize_act_rows(const uint16_t *X, int64_t T, int64_t K, flo
                                     uint16_t *x_out, bool xq_packed, hipStream_t s);
 
 struct EpilogueArgs {
-    const float *a;          // [T] row absmax
-    const float *scb;        // [N]
+    const float *a;          // [T] row absmax (zero-point variant: nd of each row)
+    const float *scb;        // [N] (zero-point variant: nd of each column)
     const uint16_t *x_out;   // [T, outlier_ld(n)] gathered outlier activations (fp16)
     const uint16_t *w_out;   // [N, outlier_ld(n)] dequantized outlier weights (fp16), GEMM path
     const int32_t *O;        // [n] outlier column indices (weight-streaming path)
@@ -134,7 +153,33 @@ struct EpilogueArgs {
     uint16_t *out;           // [T, N] fp16
     int32_t *c_i32;          // [T, N] raw accumulators (debug epilogue) or null
     int act;                 // output activation: 0 none, 1 ReLU
+    // Zero-point variant (all null otherwise): per row {zp, sum of the row's
+    // codes}, per column zp and sum of the column's codes.  The integer part
+    // is then sum_k (A + zp_a)(B + zp_b) = C + zp_b*(rs_a + K*zp_a) + zp_a*rs_b.
+    const int2 *row_zp = nullptr;
+    const int32_t *zp_b = nullptr;
+    const int32_t *rs_b = nullptr;
 };
+
+// Zero-point variant (the asymmetric quantizer of the LLM.int8() summary,
+// "8-bit Data Types and Quantization"): per vector, range [min(min,0),
+// max(max,0)], d = fp32(max' - min'), nd = fp32(254/d), zp = RNE(nd*min') +
+// 127, code = min(RNE(nd*x) - zp, 127) (roundings of the exact product);
+// d = 0 gives nd = 0, zp = 0, codes 0.  Weight: per row of W_t over all K,
+// with RS[n] the sum of the row's codes.  K <= kMaxKZp keeps the shifted
+// product sum_k (A+zp_a)(B+zp_b), |A+zp| <= 254, inside int32.
+constexpr int64_t kMaxKZp = 33286;
+hipError_t launch_quantize_weight_zp(const uint16_t *W_t, int64_t K, int64_t N, int8_t *CB,
+                                     float *ND, int32_t *ZP, int32_t *RS, hipStream_t s);
+// Activations: as launch_quantize_act, but the non-outlier part of each row
+// zero-point quantized (nd[t]; row_zp[t] = {zp, sum of the row's K codes});
+// outlier columns hold the code of 0, -zp.  g.zp must be set when g.w_out
+// is (the outlier weight rows are then dequantized as fp16((cb+zp)/nd)).
+hipError_t launch_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                                  int8_t *Xq, float *nd, int2 *row_zp, int32_t *O,
+                                  int32_t *n_out, uint8_t *partial, uint8_t *mask,
+                                  int32_t *chunk_pre, uint16_t *x_out, const GatherArgs &g,
+                                  bool xq_packed, hipStream_t s);
 
 // ev0/ev1 (optional) are recorded on s right before and after the main kernel.
 hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,

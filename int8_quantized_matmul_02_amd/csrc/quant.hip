@@ -79,6 +79,22 @@ __device__ __forceinline__ uint16_t half_at(uint4 v, int i)
 // rint(y) as an int8 in two's complement.
 constexpr float kRoundMagic = 12582912.0f;
 
+// The 8 integers held as kRoundMagic + q in s[] (|q| <= 127), as int8 bytes.
+__device__ __forceinline__ uint2 pack_low_bytes(const float (&s)[8])
+{
+    unsigned b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        b[i] = __builtin_bit_cast(unsigned, s[i]);
+    // low bytes: perm selector 0..3 picks a byte of the second operand, 4..7
+    // of the first, 0x0c gives 0
+    const unsigned lo0 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+    const unsigned hi0 = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+    const unsigned lo1 = __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u);
+    const unsigned hi1 = __builtin_amdgcn_perm(b[7], b[6], 0x04000c0cu);
+    return make_uint2(lo0 | hi0, lo1 | hi1);
+}
+
 __device__ __forceinline__ uint2 quant8(uint4 v, float amax, float r)
 {
     // r = 127/amax (0 when amax = 0, and then every value here is 0); |x| <=
@@ -102,17 +118,7 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float amax, float r)
         for (int i = 0; i < 8; ++i)
             s[i] = (float)quant127(h2f(half_at(v, i)), amax) + kRoundMagic;
     }
-    unsigned b[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        b[i] = __builtin_bit_cast(unsigned, s[i]);
-    // low bytes: perm selector 0..3 picks a byte of the second operand, 4..7
-    // of the first, 0x0c gives 0
-    const unsigned lo0 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
-    const unsigned hi0 = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
-    const unsigned lo1 = __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u);
-    const unsigned hi1 = __builtin_amdgcn_perm(b[7], b[6], 0x04000c0cu);
-    return make_uint2(lo0 | hi0, lo1 | hi1);
+    return pack_low_bytes(s);
 }
 
 // v with the halves whose flag bit is set replaced by +0.
@@ -377,12 +383,22 @@ __device__ __forceinline__ uint2 *xq_chunk(int8_t *Xq, int64_t t, int64_t K, int
 // so the table is complete before any lane reads it, and the reads of one
 // row are done before the next row's table overwrites it.)  Entries of O at
 // or past n are stale: column 0 is read in their place and the value is 0.
+// Zero-point variant (kZp): SCB holds each row's nd, ZP its zp, and the
+// values are fp16((cb + zp) / nd).
+template <bool kZp>
+__device__ __forceinline__ uint16_t dequant_row(int cb, float sc, int zp)
+{
+    return kZp ? dequant_w_zp(cb, zp, sc) : dequant_w(cb, sc);
+}
+
+template <bool kZp = false>
 __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
                                              const int32_t *__restrict__ n_out,
                                              const int8_t *__restrict__ CB,
                                              const float *__restrict__ SCB,
                                              const int32_t *__restrict__ O, int64_t N,
-                                             uint16_t *__restrict__ w_out, uint16_t *tab)
+                                             uint16_t *__restrict__ w_out, uint16_t *tab,
+                                             const int32_t *__restrict__ ZP = nullptr)
 {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int n = *n_out;
@@ -399,11 +415,12 @@ __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
         for (int64_t r = (gb * kWavesPerBlock + wave) * kRowsPerWave + lane / kGroups; r < N;
              r += nb * kWavesPerBlock * kRowsPerWave) {
             const float sc = SCB[r];
+            const int zr = kZp ? ZP[r] : 0;
             const int8_t *cbr = CB + r * K;
             unsigned h[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const unsigned v = dequant_w(cbr[o[e]], sc);
+                const unsigned v = dequant_row<kZp>(cbr[o[e]], sc, zr);
                 h[e] = 8 * g + e < n ? v : 0u;
             }
             *reinterpret_cast<uint4 *>(w_out + r * kOutlierPad + 8 * g) =
@@ -414,8 +431,9 @@ __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
     }
     for (int64_t r = gb * kWavesPerBlock + wave; r < N; r += nb * kWavesPerBlock) {
         const float sc = SCB[r];
+        const int zr = kZp ? ZP[r] : 0;
         for (int i = lane; i < 255; i += kWave)
-            tab[i] = dequant_w(i - 127, sc);
+            tab[i] = dequant_row<kZp>(i - 127, sc, zr);
         const int8_t *cbr = CB + r * K;
         for (int64_t j0 = 8 * lane; j0 < ldo; j0 += 8 * kWave) {
             const int4 o0 = *reinterpret_cast<const int4 *>(O + j0);
@@ -780,6 +798,222 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Zero-point variant (the asymmetric quantizer of the LLM.int8() summary,
+// kurtkim.github.io, "8-bit Data Types and Quantization"): per vector the
+// range [min(min,0), max(max,0)] is mapped onto [-127, 127] by the
+// normalized dynamic range nd = 254/d and the integer zero point zp, and the
+// code of x is RNE(nd*x) - zp, so that code + zp is the shifted value the
+// page multiplies.  Like the absmax kernels, these are HBM-bound streams.
+// ---------------------------------------------------------------------------
+// Signed minimum and maximum of the 8 values of a chunk folded into (mn, mx).
+__device__ __forceinline__ void chunk_minmax(uint4 v, float &mn, float &mx)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float f = h2f(half_at(v, i));
+        mn = __builtin_fminf(mn, f);
+        mx = __builtin_fmaxf(mx, f);
+    }
+}
+
+__device__ __forceinline__ void wave_minmax(float &mn, float &mx)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        mn = __builtin_fminf(mn, __shfl_xor(mn, off, kWave));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, off, kWave));
+    }
+}
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// (nd, zp) of a vector whose range [mn, mx] already contains 0:
+// d = fp32(mx - mn) and nd = fp32(254/d), each rounded once (the division is
+// IEEE-correct: the library is built with correctly rounded fp32 division);
+// zp = RNE(nd*mn) + 127, the product rounded exactly once by the fused
+// multiply-add with kRoundMagic (|nd*mn| <= 254.0001, so the sum sits where
+// the fp32 spacing is 1).  d = 0 gives (0, 0).
+struct ZpParams {
+    float nd;
+    int zp;
+};
+__device__ __forceinline__ ZpParams zp_params(float mn, float mx)
+{
+    const float d = mx - mn;
+    if (!(d > 0.0f))
+        return ZpParams{0.0f, 0};
+    const float nd = 254.0f / d;
+    const float s = __builtin_fmaf(mn, nd, kRoundMagic);
+    return ZpParams{nd, (int)(s - kRoundMagic) + 127};
+}
+
+// Codes of 8 values, min(RNE(nd*x) - zp, 127): one fused multiply-add per
+// value with the addend kRoundMagic rounds the exact product to an integer
+// (ties to even, kRoundMagic being even; an odd addend such as
+// kRoundMagic - zp would send ties to odd), then zp (zpf, an integer, so the
+// subtraction is exact within [2^23, 2^24)) is subtracted, the clamp is an
+// fp32 min, and the code is the low byte.  The codes' sum is added to *sum
+// (bits(kRoundMagic + q) - bits(kRoundMagic) = q).
+__device__ __forceinline__ uint2 quant8_zp(uint4 v, float nd, float zpf, int &sum)
+{
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        s[i] = __builtin_fminf(__builtin_fmaf(h2f(half_at(v, i)), nd, kRoundMagic) - zpf,
+                               kRoundMagic + 127.0f);
+        sum += (int)(__builtin_bit_cast(unsigned, s[i]) - __builtin_bit_cast(unsigned, kRoundMagic));
+    }
+    return pack_low_bytes(s);
+}
+
+// Weight: one wavefront per row n of W_t (output column n of W), over all K.
+__global__ __launch_bounds__(kBlock) void k_quantize_weight_zp(const uint16_t *__restrict__ W_t,
+                                                               int64_t K, int64_t N,
+                                                               int8_t *__restrict__ CB,
+                                                               float *__restrict__ ND,
+                                                               int32_t *__restrict__ ZP,
+                                                               int32_t *__restrict__ RS)
+{
+    const int lane = threadIdx.x % kWave;
+    const int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    if (n >= N)
+        return;
+    const uint4 *row = reinterpret_cast<const uint4 *>(W_t + n * K);
+    const int64_t nchunk = K / 8;
+    float mn = 0.0f, mx = 0.0f;   // 0 joins the range
+    for (int64_t c = lane; c < nchunk; c += kWave)
+        chunk_minmax(row[c], mn, mx);
+    wave_minmax(mn, mx);
+    const ZpParams p = zp_params(mn, mx);
+    const float zpf = (float)p.zp;
+    uint2 *dst = reinterpret_cast<uint2 *>(CB + n * K);
+    int sum = 0;
+    for (int64_t c = lane; c < nchunk; c += kWave)
+        dst[c] = quant8_zp(row[c], p.nd, zpf, sum);
+    sum = wave_sum(sum);
+    if (lane == 0) {
+        ND[n] = p.nd;
+        ZP[n] = p.zp;
+        RS[n] = sum;
+    }
+}
+
+// Activations: one 256-thread block per row t, as k_rowquant (the row in NC
+// 16-byte chunks per thread; NC = 0 re-reads it for very long rows).  The
+// range runs over the non-outlier columns (flagged values replaced by 0,
+// which is in every range anyway); outlier columns get the code of 0, -zp
+// (quant8_zp of a dropped value), and their values go to the compact row of
+// x_out.  Extra blocks build w_out with the zero-point dequantization.
+template <int NC>
+__global__ __launch_bounds__(kBlock) void k_rowquant_zp(
+    const uint16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ mask,
+    const int32_t *__restrict__ chunk_pre, const int32_t *__restrict__ n_out,
+    int8_t *__restrict__ Xq, float *__restrict__ nd_out, int2 *__restrict__ row_zp,
+    uint16_t *__restrict__ x_out, const int8_t *__restrict__ CB, const float *__restrict__ NDw,
+    const int32_t *__restrict__ ZPw, const int32_t *__restrict__ O, int64_t N,
+    uint16_t *__restrict__ w_out, bool packed)
+{
+    __shared__ float s_mn[kWavesPerBlock], s_mx[kWavesPerBlock];
+    __shared__ int s_sum[kWavesPerBlock];
+    __shared__ uint16_t s_tab[kWavesPerBlock][256];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    if ((int64_t)blockIdx.x >= T) {
+        gather_w_out<true>(blockIdx.x - T, gridDim.x - T, K, n_out, CB, NDw, O, N, w_out,
+                           s_tab[wave], ZPw);
+        return;
+    }
+    const int64_t t = blockIdx.x;
+    const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
+    const int nout = x_out ? *n_out : 0;
+    const int64_t ldo = outlier_ld(nout);
+    const int64_t nchunk = K / 8;
+    uint16_t *xrow = x_out ? x_out + t * ldo : nullptr;
+    float mn = 0.0f, mx = 0.0f;
+    uint4 v[NC > 0 ? NC : 1];
+    unsigned fl[NC > 0 ? NC : 1];
+    int pre[NC > 0 ? NC : 1];
+    if constexpr (NC > 0) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int64_t c = tid + (int64_t)i * kBlock;
+            v[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
+            fl[i] = c < nchunk ? mask[c] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int64_t c = tid + (int64_t)i * kBlock;
+            pre[i] = (xrow && fl[i] != 0u) ? chunk_pre[c] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+            chunk_minmax(fl[i] ? drop_flagged(v[i], fl[i]) : v[i], mn, mx);
+    } else {
+        for (int64_t c = tid; c < nchunk; c += kBlock) {
+            const unsigned f = mask[c];
+            const uint4 w = xr[c];
+            chunk_minmax(f ? drop_flagged(w, f) : w, mn, mx);
+        }
+    }
+    wave_minmax(mn, mx);
+    if (lane == 0) {
+        s_mn[wave] = mn;
+        s_mx[wave] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        mn = __builtin_fminf(mn, s_mn[w]);
+        mx = __builtin_fmaxf(mx, s_mx[w]);
+    }
+    const ZpParams p = zp_params(mn, mx);
+    const float zpf = (float)p.zp;
+    int sum = 0;
+    auto quant = [&](uint4 w, unsigned f, int pr, int64_t c) {
+        if (f) {
+            if (xrow)
+                scatter_outliers(w, f, pr, xrow);
+            w = drop_flagged(w, f);
+        }
+        *xq_chunk(Xq, t, K, c, packed) = quant8_zp(w, p.nd, zpf, sum);
+    };
+    if constexpr (NC > 0) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int64_t c = tid + (int64_t)i * kBlock;
+            if (c < nchunk)
+                quant(v[i], fl[i], pre[i], c);
+        }
+    } else {
+        for (int64_t c = tid; c < nchunk; c += kBlock) {
+            const unsigned f = mask[c];
+            quant(xr[c], f, (xrow && f != 0u) ? chunk_pre[c] : 0, c);
+        }
+    }
+    if (x_out) {
+        for (int j = nout + tid; j < ldo; j += kBlock)
+            x_out[t * ldo + j] = 0;
+    }
+    sum = wave_sum(sum);
+    if (lane == 0)
+        s_sum[wave] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int total = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w)
+            total += s_sum[w];
+        nd_out[t] = p.nd;
+        row_zp[t] = make_int2(p.zp, total);
+    }
+}
+
 // Largest binary16 bit pattern whose value is <= thr (thr >= 0, not NaN);
 // 0x7c00 (inf) when thr >= 65504 so that no finite value exceeds it.
 unsigned threshold_bits(float thr)
@@ -806,6 +1040,56 @@ hipError_t launch_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N, int
     const int64_t blocks = (N + kWavesPerBlock - 1) / kWavesPerBlock;
     hipLaunchKernelGGL(k_quantize_weight, dim3((unsigned)blocks), dim3(kBlock), 0, s, W_t, K, N,
                        CB, SCB);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight_zp(const uint16_t *W_t, int64_t K, int64_t N, int8_t *CB,
+                                     float *ND, int32_t *ZP, int32_t *RS, hipStream_t s)
+{
+    const int64_t blocks = (N + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(k_quantize_weight_zp, dim3((unsigned)blocks), dim3(kBlock), 0, s, W_t, K,
+                       N, CB, ND, ZP, RS);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                                  int8_t *Xq, float *nd, int2 *row_zp, int32_t *O,
+                                  int32_t *n_out, uint8_t *partial, uint8_t *mask,
+                                  int32_t *chunk_pre, uint16_t *x_out, const GatherArgs &g,
+                                  bool xq_packed, hipStream_t s)
+{
+    if ((xq_packed && T > 16) || (g.w_out && !g.zp))
+        return hipErrorInvalidValue;
+    const int64_t nchunk = K / 8;
+    const int64_t rows_per = (T + kDetectSplits - 1) / kDetectSplits;
+    const dim3 det_grid((unsigned)((nchunk + 31) / 32), (unsigned)kDetectSplits);
+    hipLaunchKernelGGL(k_detect, det_grid, dim3(kDetectThreads), 0, s, X, T, K,
+                       threshold_bits(threshold), rows_per, partial);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, partial, K, mask, O, n_out,
+                       chunk_pre);
+    int64_t gather_blocks = 0;
+    if (g.w_out) {
+        gather_blocks = (g.N + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (gather_blocks > 2048)
+            gather_blocks = 2048;
+    }
+    const dim3 grid((unsigned)(T + gather_blocks));
+    const int64_t chunks_per_thread = (nchunk + kBlock - 1) / kBlock;
+#define LLMINT8_ROWQUANT_ZP(NCV)                                                              \
+    hipLaunchKernelGGL(k_rowquant_zp<NCV>, grid, dim3(kBlock), 0, s, X, T, K, mask, chunk_pre, \
+                       n_out, Xq, nd, row_zp, x_out, g.CB, g.SCB, g.zp, O, g.N, g.w_out,     \
+                       xq_packed)
+    if (chunks_per_thread <= 1)
+        LLMINT8_ROWQUANT_ZP(1);
+    else if (chunks_per_thread <= 2)
+        LLMINT8_ROWQUANT_ZP(2);
+    else if (chunks_per_thread <= 4)
+        LLMINT8_ROWQUANT_ZP(4);
+    else if (chunks_per_thread <= 8)
+        LLMINT8_ROWQUANT_ZP(8);
+    else
+        LLMINT8_ROWQUANT_ZP(0);
+#undef LLMINT8_ROWQUANT_ZP
     return hipGetLastError();
 }
 

@@ -29,6 +29,10 @@ EXPORTS = (
     "llmint8_matmul_act",
     "llmint8_matmul_path",
     "llmint8_igemm_i32",
+    "llmint8_quantize_weight_zp",
+    "llmint8_quantize_act_zp",
+    "llmint8_matmul_zp",
+    "llmint8_matmul_zp_path",
 )
 
 
@@ -64,8 +68,15 @@ def _load():
     lib.llmint8_matmul_act.argtypes = [P, I64, I64, I64, P, P, P, F, I, P, P, SZ, P]
     lib.llmint8_matmul_path.argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ, I, P, P, P]
     lib.llmint8_igemm_i32.argtypes = [P, I64, I64, I64, P, P, I, P]
+    lib.llmint8_quantize_weight_zp.argtypes = [P, I64, I64, P, P, P, P, P]
+    lib.llmint8_quantize_act_zp.argtypes = [P, I64, I64, F, P, P, P, P, P, P, SZ, P]
+    lib.llmint8_matmul_zp.argtypes = [P, I64, I64, I64, P, P, P, P, P, F, P, P, SZ, P]
+    lib.llmint8_matmul_zp_path.argtypes = [P, I64, I64, I64, P, P, P, P, P, F, P, P, SZ, I, P,
+                                           P, P]
     for fn in ("llmint8_quantize_weight", "llmint8_quantize_act", "llmint8_matmul",
-               "llmint8_matmul_act", "llmint8_matmul_path", "llmint8_igemm_i32"):
+               "llmint8_matmul_act", "llmint8_matmul_path", "llmint8_igemm_i32",
+               "llmint8_quantize_weight_zp", "llmint8_quantize_act_zp", "llmint8_matmul_zp",
+               "llmint8_matmul_zp_path"):
         getattr(lib, fn).restype = I
     _lib = lib
     return lib
@@ -234,3 +245,106 @@ def llmint8_igemm_i32(Xq, CB, C=None, path=PATH_AUTO):
            lib.llmint8_igemm_i32(Xq.data_ptr(), T, K, N, CB.data_ptr(), C.data_ptr(), int(path),
                                  _stream(Xq)))
     return C
+
+
+# ---------------------------------------------------------------------------
+# Zero-point (asymmetric) variant.
+# ---------------------------------------------------------------------------
+def llmint8_quantize_weight_zp(W_t, CB=None, ND=None, ZP=None, RS=None):
+    """W_t: fp16 [N,K].  Returns (CB int8 [N,K], ND f32 [N], ZP int32 [N], RS int32 [N])."""
+    lib = _load()
+    _dev(W_t, "W_t", _H)
+    N, K = W_t.shape
+    d = W_t.device
+    CB = torch.empty((N, K), dtype=torch.int8, device=d) if CB is None else _dev(CB, "CB", (torch.int8,))
+    ND = torch.empty((N,), dtype=torch.float32, device=d) if ND is None else _dev(ND, "ND", (torch.float32,))
+    ZP = torch.empty((N,), dtype=torch.int32, device=d) if ZP is None else _dev(ZP, "ZP", (torch.int32,))
+    RS = torch.empty((N,), dtype=torch.int32, device=d) if RS is None else _dev(RS, "RS", (torch.int32,))
+    _check("llmint8_quantize_weight_zp",
+           lib.llmint8_quantize_weight_zp(W_t.data_ptr(), K, N, CB.data_ptr(), ND.data_ptr(),
+                                          ZP.data_ptr(), RS.data_ptr(), _stream(W_t)))
+    return CB, ND, ZP, RS
+
+
+def llmint8_quantize_act_zp(X, threshold=6.0, Xq=None, nd=None, row_zp=None, outlier_idx=None,
+                            n_outliers=None, ws=None):
+    """X: fp16 [T,K].  Returns (Xq int8 [T,K], nd f32 [T], row_zp int32 [T,2] = {zp, code sum},
+    outlier_idx int32 [K], n_outliers int32 [1])."""
+    lib = _load()
+    _dev(X, "X", _H)
+    T, K = X.shape
+    d = X.device
+    Xq = torch.empty((T, K), dtype=torch.int8, device=d) if Xq is None else _dev(Xq, "Xq", (torch.int8,))
+    nd = torch.empty((T,), dtype=torch.float32, device=d) if nd is None else _dev(nd, "nd", (torch.float32,))
+    row_zp = (torch.empty((T, 2), dtype=torch.int32, device=d) if row_zp is None
+              else _dev(row_zp, "row_zp", (torch.int32,)))
+    outlier_idx = torch.empty((K,), dtype=torch.int32, device=d) if outlier_idx is None else outlier_idx
+    n_outliers = torch.empty((1,), dtype=torch.int32, device=d) if n_outliers is None else n_outliers
+    need = llmint8_quantize_act_workspace_bytes(K)
+    ws = torch.empty((need,), dtype=torch.uint8, device=d) if ws is None else ws
+    _check("llmint8_quantize_act_zp",
+           lib.llmint8_quantize_act_zp(X.data_ptr(), T, K, float(threshold), Xq.data_ptr(),
+                                       nd.data_ptr(), row_zp.data_ptr(), outlier_idx.data_ptr(),
+                                       n_outliers.data_ptr(), ws.data_ptr(),
+                                       ws.numel() * ws.element_size(), _stream(X)))
+    return Xq, nd, row_zp, outlier_idx, n_outliers
+
+
+def llmint8_matmul_zp_path(X, CB, ND, ZP, RS, threshold=6.0, bias=None, out=None, ws=None,
+                           path=PATH_AUTO, main_start=None, main_stop=None):
+    """The zero-point decomposition: X fp16 [T,K] with the output of
+    llmint8_quantize_weight_zp -> out fp16 [T,N].  path / events as
+    llmint8_matmul_path."""
+    lib = _load()
+    _dev(X, "X", _H)
+    _dev(CB, "CB", (torch.int8,))
+    _dev(ND, "ND", (torch.float32,))
+    _dev(ZP, "ZP", (torch.int32,))
+    _dev(RS, "RS", (torch.int32,))
+    T, K = X.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K or ND.shape != (N,) or ZP.shape != (N,) or RS.shape != (N,):
+        raise ValueError("shape mismatch: X %s, CB %s, ND %s, ZP %s, RS %s"
+                         % (tuple(X.shape), tuple(CB.shape), tuple(ND.shape), tuple(ZP.shape),
+                            tuple(RS.shape)))
+    if bias is not None:
+        _dev(bias, "bias", _H)
+        if bias.shape != (N,):
+            raise ValueError("bias must have shape (%d,)" % N)
+    out = torch.empty((T, N), dtype=torch.float16, device=X.device) if out is None else _dev(out, "out", _H)
+    if ws is None:
+        ws = torch.empty((llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=X.device)
+    _check("llmint8_matmul_zp_path",
+           lib.llmint8_matmul_zp_path(X.data_ptr(), T, K, N, CB.data_ptr(), ND.data_ptr(),
+                                      ZP.data_ptr(), RS.data_ptr(),
+                                      bias.data_ptr() if bias is not None else None,
+                                      float(threshold), out.data_ptr(), ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), int(path),
+                                      ctypes.c_void_p(main_start) if main_start else None,
+                                      ctypes.c_void_p(main_stop) if main_stop else None,
+                                      _stream(X)))
+    return out
+
+
+def llmint8_matmul_zp(X, CB, ND, ZP, RS, threshold=6.0, bias=None, out=None, ws=None):
+    """The zero-point decomposition (automatic kernel choice)."""
+    lib = _load()
+    _dev(X, "X", _H)
+    for t, name, dt in ((CB, "CB", torch.int8), (ND, "ND", torch.float32), (ZP, "ZP", torch.int32),
+                        (RS, "RS", torch.int32)):
+        _dev(t, name, (dt,))
+    T, K = X.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K or ND.shape != (N,) or ZP.shape != (N,) or RS.shape != (N,):
+        raise ValueError("shape mismatch: X %s, CB %s" % (tuple(X.shape), tuple(CB.shape)))
+    if bias is not None:
+        _dev(bias, "bias", _H)
+    out = torch.empty((T, N), dtype=torch.float16, device=X.device) if out is None else _dev(out, "out", _H)
+    if ws is None:
+        ws = torch.empty((llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=X.device)
+    _check("llmint8_matmul_zp",
+           lib.llmint8_matmul_zp(X.data_ptr(), T, K, N, CB.data_ptr(), ND.data_ptr(), ZP.data_ptr(),
+                                 RS.data_ptr(), bias.data_ptr() if bias is not None else None,
+                                 float(threshold), out.data_ptr(), ws.data_ptr(),
+                                 ws.numel() * ws.element_size(), _stream(X)))
+    return out

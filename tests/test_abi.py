@@ -60,9 +60,9 @@ def test_workspace_queries(lib, T):
     K, N = 4096, 16384
     ws = L.llmint8_workspace_bytes(T, K, N)
     # partial flags (16 row ranges x K/8) + mask + chunk prefixes + O + n + row
-    # scales + Xq (at least 16 rows: the decode path's fragment order) + fp16
+    # scales + zero-point row parameters + Xq (at least 16 rows: the decode path's fragment order) + fp16
     # outlier operands (worst case n = K)
-    floor = 2 * K + K // 8 + 8 * K + 4 * T + max(T, 16) * K + 2 * T * K + 2 * N * K
+    floor = 2 * K + K // 8 + 8 * K + 4 * T + 8 * T + max(T, 16) * K + 2 * T * K + 2 * N * K
     assert floor <= ws <= floor + 16 * 256
     assert L.llmint8_workspace_bytes(0, K, N) == 0
     assert L.llmint8_quantize_act_workspace_bytes(K) >= 2 * K + K // 8 + 4 * K
@@ -115,3 +115,33 @@ def test_other_entry_points_validate(lib):
     assert lib.llmint8_matmul_act(None, 4, 64, 64, P, P, None, 6.0, 1, P, P, 1 << 30, None) == 1
     assert lib.llmint8_matmul_act(P, 4, 96, 64, P, P, None, 6.0, 1, P, P, 1 << 30, None) == 2
     assert lib.llmint8_matmul_act(P, 4, 64, 64, P, P, None, 6.0, 1, P, P, 16, None) == 3
+
+
+def test_zero_point_entry_points_validate(lib):
+    # weight: null outputs, shape, and the zero-point K limit (|code + zp| <= 254)
+    assert lib.llmint8_quantize_weight_zp(P, 64, 64, P, P, P, None, None) == 1
+    assert lib.llmint8_quantize_weight_zp(P, 100, 64, P, P, P, P, None) == 2
+    assert lib.llmint8_quantize_weight_zp(P, 33344, 64, P, P, P, P, None) == 2
+    # activations: argument, shape, workspace; row_zp must be 8-byte aligned
+    assert lib.llmint8_quantize_act_zp(P, 4, 64, float("nan"), P, P, P, P, P, P, 1 << 30, None) == 1
+    assert lib.llmint8_quantize_act_zp(P, 4, 64, 6.0, P, P, P + 4, P, P, P, 1 << 30, None) == 1
+    assert lib.llmint8_quantize_act_zp(P, 4, 72, 6.0, P, P, P, P, P, P, 1 << 30, None) == 2
+    assert lib.llmint8_quantize_act_zp(P, 4, 33344, 6.0, P, P, P, P, P, P, 1 << 30, None) == 2
+    assert lib.llmint8_quantize_act_zp(P, 4, 64, 6.0, P, P, P, P, P, P, 10, None) == 3
+
+    def mm(X=P, T=8, K=64, N=64, RS=P, thr=6.0, wsb=1 << 40, path=0):
+        return lib.llmint8_matmul_zp_path(X, T, K, N, P, P, P, RS, None, thr, P, P, wsb, path,
+                                          None, None, None)
+    assert mm(X=None) == 1
+    assert mm(RS=None) == 1
+    assert mm(RS=P + 4) == 1                      # misaligned
+    assert mm(thr=-1.0) == 1
+    assert mm(path=5) == 1
+    assert mm(K=96) == 2
+    assert mm(K=33344) == 2                       # beyond the zero-point K limit
+    assert mm(K=33280, wsb=0) == 3                # the largest supported K passes the shape check
+    assert mm(T=17, path=2) == 2
+    assert mm(wsb=L.llmint8_workspace_bytes(8, 64, 64) - 1) == 3
+    assert lib.llmint8_matmul_zp(P, 4, 64, 64, P, P, P, P, None, float("nan"), P, P, 1 << 30,
+                                 None) == 1
+    assert lib.llmint8_matmul_zp(P, 4, 64, 64, P, P, P, P, None, 6.0, P, P, 16, None) == 3

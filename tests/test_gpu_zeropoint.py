@@ -1,0 +1,195 @@
+"""GPU parity of the zero-point (asymmetric) variant against the CPU oracle,
+through the C ABI.
+
+Bar: bit-exact weight codes, nd, zero points and code sums, activation codes,
+nd, zero points and code sums, outlier list and count; fp16 output within
+|d| <= 1e-3 + 2e-3*|ref| (infinities equal).  Inputs are the seeded
+generator's, skewed so that the zero points are far from 0 (ReLU rows,
+shifted rows, all-negative rows, shifted weights); expected values come only
+from the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from int8_quantized_matmul_02_amd import llmint8 as L
+from int8_quantized_matmul_02_amd import workloads
+from tests.gpu_helpers import (assert_equal_exact, assert_fp16_close, d2h, h2d, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def skewed_case(T, K, N, seed, n_dims=3, lo=8.0, hi=40.0, p=0.3):
+    """The generator's case with asymmetric rows and weights."""
+    X, W_t, dims = workloads.case(T, K, N, n_dims=min(n_dims, K // 16), lo=lo, hi=hi, p=p,
+                                  seed=seed)
+    X = X.astype(np.float32)
+    X[0::4] = np.maximum(X[0::4], 0.0)            # ReLU-like rows
+    X[1::4] += 0.75                               # shifted rows
+    X[2::4] = -np.abs(X[2::4]) - 0.1              # all-negative rows
+    if T > 5:
+        X[5] = 0.0                                # an all-zero row
+    W = W_t.astype(np.float32)
+    W[0::3] += 0.015                              # shifted weight rows
+    W[1::3] = np.abs(W[1::3])                     # non-negative weight rows
+    if N > 2:
+        W[2] = 0.0                                # an all-zero output column
+    return X.astype(np.float16), W.astype(np.float16), dims
+
+
+def oracle_rowsum(q):
+    return q.astype(np.int64).sum(axis=1).astype(np.int32)
+
+
+@pytest.mark.parametrize("N,K", [(64, 64), (192, 1088), (1024, 2048), (320, 33280)])
+def test_quantize_weight_zp_exact(N, K):
+    say("quantize_weight_zp N=%d K=%d" % (N, K))
+    _, W_t, _ = skewed_case(4, K, N, seed=N + K)
+    CB, ND, ZP, RS = L.llmint8_quantize_weight_zp(h2d(W_t))
+    CBr, NDr, ZPr = oracle.quantize_weight_zp(W_t)
+    assert_equal_exact(d2h(CB), CBr, "CB")
+    assert_equal_exact(d2h(ND), NDr, "ND")
+    assert_equal_exact(d2h(ZP), ZPr, "ZP")
+    assert_equal_exact(d2h(RS), oracle_rowsum(CBr), "RS")
+
+
+@pytest.mark.parametrize("T,K", [(1, 64), (5, 256), (16, 1088), (17, 1024), (300, 576),
+                                 (513, 4160), (1024, 16384), (3, 33280)])
+@pytest.mark.parametrize("thr", [6.0, 0.0, np.inf, 2.5])
+def test_quantize_act_zp_exact(T, K, thr):
+    say("quantize_act_zp T=%d K=%d thr=%s" % (T, K, thr))
+    X, _, _ = skewed_case(T, K, 64, seed=T * 5 + K)
+    X[T // 2, 7] = 6.0                     # exactly at the threshold: not an outlier at 6.0
+    Xq, nd, row_zp, O, n = L.llmint8_quantize_act_zp(h2d(X), thr)
+    Or = oracle.outlier_columns(X, thr)
+    Xqr, ndr, zpr = oracle.quantize_rows_zp(X, Or)
+    nn = int(d2h(n)[0])
+    assert nn == len(Or)
+    assert_equal_exact(d2h(O)[:nn], Or, "O")
+    assert_equal_exact(d2h(Xq), Xqr, "Xq")
+    assert_equal_exact(d2h(nd), ndr, "nd")
+    rz = d2h(row_zp)
+    assert_equal_exact(rz[:, 0], zpr, "zp")
+    assert_equal_exact(rz[:, 1], oracle_rowsum(Xqr), "row code sums")
+
+
+SHAPES = [
+    # (T, K, N)
+    (1, 64, 64),
+    (4, 256, 320),
+    (16, 1088, 192),
+    (17, 128, 192),
+    (100, 320, 320),
+    (300, 576, 640),
+    (513, 1024, 256),
+]
+
+
+@pytest.mark.parametrize("T,K,N", SHAPES)
+@pytest.mark.parametrize("thr", [6.0, 0.0, np.inf])
+@pytest.mark.parametrize("path", [L.PATH_AUTO, L.PATH_GEMM, L.PATH_DECODE])
+def test_matmul_zp(T, K, N, thr, path):
+    if path == L.PATH_DECODE and T > 16:
+        pytest.skip("the weight-streaming kernel takes T <= 16")
+    say("matmul_zp T=%d K=%d N=%d thr=%s path=%d" % (T, K, N, thr, path))
+    X, W_t, _ = skewed_case(T, K, N, seed=T + 3 * K + N)
+    rng = np.random.default_rng(T + K)
+    bias = (rng.standard_normal(N) * 0.5).astype(np.float16) if T % 2 else None
+    CB, ND, ZP, RS = L.llmint8_quantize_weight_zp(h2d(W_t))
+    out = L.llmint8_matmul_zp_path(h2d(X), CB, ND, ZP, RS, thr,
+                                   bias=h2d(bias) if bias is not None else None, path=path)
+    CBr, NDr, ZPr = oracle.quantize_weight_zp(W_t)
+    ref, _, _, _ = oracle.matmul_zp(X, CBr, NDr, ZPr, thr, bias=bias)
+    assert_fp16_close(d2h(out), ref, "out")
+
+
+@pytest.mark.parametrize("n_dims,T,path", [(40, 300, L.PATH_GEMM), (40, 8, L.PATH_DECODE),
+                                           (40, 8, L.PATH_GEMM), (200, 257, L.PATH_AUTO)])
+def test_matmul_zp_many_outliers(n_dims, T, path):
+    # more than 32 outlier columns: the fp16 pass of the GEMM path
+    K, N = 1024, 512
+    say("matmul_zp many outliers n_dims=%d T=%d path=%d" % (n_dims, T, path))
+    X, W_t, _ = skewed_case(T, K, N, seed=n_dims + T, n_dims=n_dims, p=0.5)
+    CB, ND, ZP, RS = L.llmint8_quantize_weight_zp(h2d(W_t))
+    out = L.llmint8_matmul_zp_path(h2d(X), CB, ND, ZP, RS, 6.0, path=path)
+    CBr, NDr, ZPr = oracle.quantize_weight_zp(W_t)
+    ref, O, _, _ = oracle.matmul_zp(X, CBr, NDr, ZPr, 6.0)
+    assert len(O) > 32
+    assert_fp16_close(d2h(out), ref, "out")
+
+
+@pytest.mark.parametrize("path", [L.PATH_GEMM, L.PATH_DECODE])
+def test_matmul_zp_int32_extreme(path):
+    # K at the zero-point limit with every shifted product at 254^2: the
+    # integer sum is 33280 * 64516 = 2,147,092,480, just inside int32, and the
+    # output is exactly 33280 (rows and weights all -1: nd = 254, zp = -127)
+    T, K, N = 4, 33280, 64
+    say("matmul_zp int32 extreme path=%d" % path)
+    X = np.full((T, K), -1.0, np.float16)
+    W_t = np.full((N, K), -1.0, np.float16)
+    CB, ND, ZP, RS = L.llmint8_quantize_weight_zp(h2d(W_t))
+    out = L.llmint8_matmul_zp_path(h2d(X), CB, ND, ZP, RS, np.inf, path=path)
+    CBr, NDr, ZPr = oracle.quantize_weight_zp(W_t)
+    assert np.all(CBr == -127) and np.all(ZPr == -127) and np.all(NDr == 254)
+    ref, _, _, _ = oracle.matmul_zp(X, CBr, NDr, ZPr, np.inf)
+    assert np.all(ref.view(np.float16) == np.float16(33280.0))
+    assert_equal_exact(d2h(out).view(np.uint16), ref, "out")
+
+
+def test_matmul_zp_matches_absmax_on_symmetric_operands():
+    # operands holding +-2^j: zero points are 0 and the variant reproduces
+    # the absmax decomposition bit for bit (pinned on the CPU), so the GPU's
+    # zero-point output is checked against the absmax oracle
+    T, K, N = 64, 512, 256
+    rng = np.random.default_rng(77)
+    X = rng.uniform(-3.9, 3.9, (T, K))
+    X[:, 0], X[:, 1] = 4.0, -4.0
+    X[::3, 30] = rng.uniform(8, 40, len(range(0, T, 3)))
+    X = X.astype(np.float16)
+    W = rng.uniform(-0.124, 0.124, (N, K))
+    W[:, 5], W[:, 6] = 0.125, -0.125
+    W = W.astype(np.float16)
+    say("matmul_zp vs absmax on symmetric operands")
+    CBz, NDz, ZPz, RSz = L.llmint8_quantize_weight_zp(h2d(W))
+    CBa, SCB = oracle.quantize_weight(W)
+    assert_equal_exact(d2h(CBz), CBa, "codes")
+    assert not d2h(ZPz).any()
+    out_z = L.llmint8_matmul_zp(h2d(X), CBz, NDz, ZPz, RSz, 6.0)
+    ref, _, _ = oracle.matmul(X, CBa, SCB, 6.0)
+    assert_fp16_close(d2h(out_z), ref, "zero-point vs the absmax oracle")
+
+
+@pytest.mark.parametrize("which", ["fc1", "decode4"])
+def test_matmul_zp_full_size_sampled(which):
+    # the benchmark workloads at full size, in the launch configuration the
+    # zero-point bench line times; sampled rows (fc1) or columns (decode)
+    if which == "fc1":
+        d = workloads.ffn_6p7b(with_fc2=False)
+        X, W_t = d["X"], d["W_t"]
+        X = np.maximum(X.astype(np.float32), -0.5).astype(np.float16)   # skew the rows
+    else:
+        d = workloads.decode_175b(4)
+        X, W_t = d["X"], d["W_t"]
+    T, K = X.shape
+    N = W_t.shape[0]
+    say("matmul_zp full size %s T=%d K=%d N=%d" % (which, T, K, N))
+    CB, ND, ZP, RS = L.llmint8_quantize_weight_zp(h2d(W_t))
+    out = d2h(L.llmint8_matmul_zp(h2d(X), CB, ND, ZP, RS, 6.0))
+    CBh, NDh, ZPh = d2h(CB), d2h(ND), d2h(ZP)
+    rng = np.random.default_rng(5)
+    if which == "fc1":
+        rows = sample_rows(T, n_random=14)
+        CBr, NDr, ZPr = oracle.quantize_weight_zp(W_t)
+        assert_equal_exact(CBh, CBr, "CB")
+        assert_equal_exact(NDh, NDr, "ND")
+        assert_equal_exact(ZPh, ZPr, "ZP")
+        ref, _, _, _ = oracle.matmul_zp(X, CBr, NDr, ZPr, 6.0, rows=rows)
+        assert_fp16_close(out[rows], ref, "out rows")
+    else:
+        cols = np.unique(np.r_[0, N - 1, rng.choice(N, 400, replace=False)])
+        CBr, NDr, ZPr = oracle.quantize_weight_zp(W_t[cols])
+        assert_equal_exact(CBh[cols], CBr, "CB sample")
+        assert_equal_exact(NDh[cols], NDr, "ND sample")
+        assert_equal_exact(ZPh[cols], ZPr, "ZP sample")
+        ref, _, _, _ = oracle.matmul_zp(X, CBr, NDr, ZPr, 6.0)
+        assert_fp16_close(out[:, cols], ref, "out cols")

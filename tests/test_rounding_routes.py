@@ -85,3 +85,63 @@ def test_reciprocal_route_declines_exact_ties():
         assert not ok.any() and not ok_fus.any(), "a tie must take the division route"
         assert np.array_equal(q_div, exact)
         assert np.array_equal(exact % 2, np.zeros_like(exact)), "ties go to even"
+
+
+# ---------------------------------------------------------------------------
+# Zero-point variant: the kernels compute the code of x from one fused
+# multiply-add, fma(x, nd, 1.5*2^23) (the exact product rounded to an integer,
+# ties to even, since 1.5*2^23 is even), minus zp (exact), clamped by an fp32
+# min at 1.5*2^23 + 127, and take it as bits - bits(1.5*2^23); the zero point
+# as fma(min', nd, 1.5*2^23) - 1.5*2^23 + 127.  (Folding zp into the addend
+# would be wrong: with an odd addend the ties go to odd.)  A fused
+# multiply-add rounds the exact x*nd + c once; that rounding is done here
+# with exact rationals.
+# ---------------------------------------------------------------------------
+from fractions import Fraction  # noqa: E402
+
+MAGIC = 12582912.0
+
+
+def fp32_round(v):
+    """Nearest fp32 value to the rational v (ties to even); v within the
+    normal range."""
+    if v == 0:
+        return 0.0
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (e - 23)          # 24 significant bits
+    q = a / ulp
+    r = round(q)                           # ties to even
+    return sign * float(r * ulp)
+
+
+def fma32(x, y, c):
+    return fp32_round(Fraction(float(x)) * Fraction(float(y)) + Fraction(float(c)))
+
+
+@pytest.mark.parametrize("seed", [21, 22, 23])
+def test_zero_point_fused_route_matches_the_oracle(seed):
+    rng = np.random.default_rng(seed)
+    kinds = [rng.standard_normal(64), np.abs(rng.standard_normal(64)) + 0.25,
+             -rng.exponential(3.0, 64), rng.uniform(-1e-3, 5e-3, 64),
+             rng.uniform(-60000, 900, 64), np.r_[[-63.5, 63.5], rng.choice([0.25, 0.75, 1.25, -0.75], 62)],
+             # nd = 2 with an odd zero point (1): the ties 0.5, 1.5, 2.5 must
+             # still go to even before the zero point is subtracted
+             np.r_[[-63.0, 64.0], rng.choice([0.25, 0.75, 1.25, -0.75, -1.25, 3.25], 62)]]
+    X = np.stack(kinds).astype(np.float16)
+    q_or, nd_or, zp_or = oracle.quantize_rows_zp(X, np.zeros(0, np.int32))
+    for t in range(X.shape[0]):
+        xs = X[t].astype(np.float32)
+        mn = np.float32(min(xs.min(), 0.0))
+        mx = np.float32(max(xs.max(), 0.0))
+        d = np.float32(mx - mn)
+        nd = np.float32(254.0) / d
+        zp = int(fma32(mn, nd, MAGIC) - MAGIC) + 127
+        assert nd == nd_or[t] and zp == zp_or[t]
+        for k in range(X.shape[1]):
+            s = min(fma32(xs[k], nd, MAGIC) - zp, MAGIC + 127.0)
+            bits = int(np.float32(s).view(np.uint32)) - int(np.float32(MAGIC).view(np.uint32))
+            assert bits == q_or[t, k], (t, k)
