@@ -263,6 +263,82 @@ def fp16_weight_step(torch, L, d, steps, warmup, dev):
             "step_TOPS": round(ops / s / 1e12, 1), "weight_quant_bytes": wbytes}
 
 
+def timed_calls(torch, plain, evented, steps, warmup, ev):
+    """timed_steps for any entry point: plain(i) is one call, evented(i, e0,
+    e1) the same call with events around its main kernel."""
+    for i in range(warmup):
+        plain(i)
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        plain(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        evented(i, pairs[i][0], pairs[i][1])
+    torch.cuda.synchronize()
+    kern = [ev.elapsed_ms(a, b) for a, b in pairs]
+    return (t1 - t0) * 1e3 / steps, float(np.mean(kern)), kern
+
+
+def zeropoint_bench(torch, L, workloads, steps, warmup, ev, dev):
+    """The zero-point (asymmetric) variant on the same workloads: fc1 (the
+    GEMM path; k_gemm with the shifted-product epilogue) and the 175B decode
+    shape at T in {1, 4, 16} (the weight-streaming kernel; two weight copies
+    rotated).  Same ops and algorithmic bytes as the absmax lines, plus the
+    per-column zp and code sums (8 B per column)."""
+    res = {}
+    d = workloads.ffn_6p7b(with_fc2=False)
+    X = torch.from_numpy(d["X"]).to(dev)
+    CB, ND, ZP, RS = L.llmint8_quantize_weight_zp(torch.from_numpy(d["W_t"]).to(dev))
+    T, K = X.shape
+    N = CB.shape[0]
+    out = torch.empty((T, N), dtype=torch.float16, device=dev)
+    ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=dev)
+    ms, kms, kern = timed_calls(
+        torch, lambda i: L.llmint8_matmul_zp(X, CB, ND, ZP, RS, 6.0, out=out, ws=ws),
+        lambda i, a, b: L.llmint8_matmul_zp_path(X, CB, ND, ZP, RS, 6.0, out=out, ws=ws,
+                                                 main_start=a, main_stop=b),
+        steps, warmup, ev)
+    ops = 2.0 * T * K * N
+    res["fc1"] = {"T": T, "K": K, "N": N, "threshold": 6.0, "step_us": round(ms * 1e3, 2),
+                  "step_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+                  "gemm_kernel_us": round(kms * 1e3, 2),
+                  "gemm_frac_int8_peak": round(ops / (kms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+    res["fc1"].update(spread_us(kern))
+    log("zero-point fc1: %.1f us/step (%.0f TOP/s), GEMM kernel %.1f us (%.1f%% of int8 peak)"
+        % (ms * 1e3, ops / ms / 1e9, kms * 1e3, 100 * ops / (kms * 1e-3) / 1e12 / INT8_PEAK_TOPS))
+    del X, CB, ND, ZP, RS, out, ws, d
+    torch.cuda.empty_cache()
+
+    d1 = workloads.decode_175b(1, with_weight=True)
+    CB, ND, ZP, RS = L.llmint8_quantize_weight_zp(torch.from_numpy(d1.pop("W_t")).to(dev))
+    CBs = [CB, CB.clone()]
+    K, N = CB.shape[1], CB.shape[0]
+    for T in (1, 4, 16):
+        dd = d1 if T == 1 else workloads.decode_175b(T, with_weight=False)
+        X = torch.from_numpy(dd["X"]).to(dev)
+        out = torch.empty((T, N), dtype=torch.float16, device=dev)
+        ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=dev)
+        ms, kms, kern = timed_calls(
+            torch, lambda i: L.llmint8_matmul_zp(X, CBs[i % 2], ND, ZP, RS, 6.0, out=out, ws=ws),
+            lambda i, a, b: L.llmint8_matmul_zp_path(X, CBs[i % 2], ND, ZP, RS, 6.0, out=out,
+                                                     ws=ws, main_start=a, main_stop=b),
+            steps, warmup, ev)
+        alg = K * N + 12 * N + T * K + 12 * T + 2 * T * N
+        res["decode_T%d" % T] = {"kernel_us": round(kms * 1e3, 2), "step_us": round(ms * 1e3, 2),
+                                 "kernel_GBs": round(alg / (kms * 1e-3) / 1e9, 1),
+                                 "frac_hbm": round(alg / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "alg_bytes": alg}
+        res["decode_T%d" % T].update(spread_us(kern))
+        log("zero-point decode T=%d: kernel %.1f us (%.0f GB/s), step %.1f us"
+            % (T, kms * 1e3, alg / kms / 1e6, ms * 1e3))
+    del CBs, CB, ND, ZP, RS
+    torch.cuda.empty_cache()
+    return res
+
+
 def configs_bench(torch, L, workloads, steps, warmup, ev, dev):
     """The method's other workloads (parity cases), each timed like the main one:
     the 1.3B up-projection, the fc2-like input (every column an outlier) and
@@ -326,6 +402,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--configs", action="store_true",
                     help="also time the other workloads (1.3B up-proj, fc2-like, attention sweep)")
+    ap.add_argument("--zeropoint", action="store_true",
+                    help="also time the zero-point variant (fc1 and the decode shape)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run one 256 MiB device-to-device copy first (a kernel of known traffic, "
                          "for scaling hardware byte counters)")
@@ -402,6 +480,8 @@ def main():
         result["decode"] = decode_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
     if args.configs:
         result["configs"] = configs_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
+    if args.zeropoint:
+        result["zeropoint"] = zeropoint_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on %d rows ..." % args.cpu_rows)
         result["cpu_baseline"] = cpu_baseline(X_h, W_h, thr, args.cpu_rows)

@@ -571,7 +571,9 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
             xo[i][s2] = outlier_frag<C>(orows, wm * (C::BM / C::WM) + i * 32 + tl, 2 * s2 + hi);
     // column factors and bias of column group j, fetched one group ahead
     v4f sn[2][4];
-    v4i zb[2][4], rb[2][4];   // zero-point variant only
+    // zero-point variant: zp and code sums of the group's columns, loaded at
+    // the start of their own group (double-buffering them too spills)
+    v4i zb[4], rb[4];
     uint2 bias[2][4];
     auto load_cols = [&](int j, int buf) {
 #pragma unroll
@@ -579,10 +581,6 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
             int64_t nc = nw + j * 32 + 8 * g + nl;
             nc = nc < N ? nc : N - 4;
             sn[buf][g] = *reinterpret_cast<const v4f *>(ep.scb + nc);
-            if constexpr (kZp) {
-                zb[buf][g] = *reinterpret_cast<const v4i *>(ep.zp_b + nc);
-                rb[buf][g] = *reinterpret_cast<const v4i *>(ep.rs_b + nc);
-            }
             if constexpr (kBias)
                 bias[buf][g] = *reinterpret_cast<const uint2 *>(ep.bias + nc);
         }
@@ -594,6 +592,15 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
         if (j + 1 < C::FN)
             load_cols(j + 1, (j + 1) % 2);
         const int cb = j % 2;
+        if constexpr (kZp) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                int64_t nc = nw + j * 32 + 8 * g + nl;
+                nc = nc < N ? nc : N - 4;
+                zb[g] = *reinterpret_cast<const v4i *>(ep.zp_b + nc);
+                rb[g] = *reinterpret_cast<const v4i *>(ep.rs_b + nc);
+            }
+        }
         v4i wo[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
@@ -604,8 +611,8 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 if constexpr (kZp)
-                    d[r] = zp_dequant(acc[i][j][r], za[i], ra[i], zb[cb][r / 4][r % 4],
-                                      rb[cb][r / 4][r % 4], at[i], sn[cb][r / 4][r % 4]);
+                    d[r] = zp_dequant(acc[i][j][r], za[i], ra[i], zb[r / 4][r % 4],
+                                      rb[r / 4][r % 4], at[i], sn[cb][r / 4][r % 4]);
                 else
                     d[r] = (float)acc[i][j][r] * (at[i] * sn[cb][r / 4][r % 4]);
             }

@@ -175,6 +175,9 @@ hipError_t launch_quantize_weight_zp(const uint16_t *W_t, int64_t K, int64_t N, 
 // zero-point quantized (nd[t]; row_zp[t] = {zp, sum of the row's K codes});
 // outlier columns hold the code of 0, -zp.  g.zp must be set when g.w_out
 // is (the outlier weight rows are then dequantized as fp16((cb+zp)/nd)).
+// Without w_out and for the shapes of quantize_act_fits_rows it is one
+// launch (the few-rows kernel), else detection, compaction and a block per
+// row.
 hipError_t launch_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K, float threshold,
                                   int8_t *Xq, float *nd, int2 *row_zp, int32_t *O,
                                   int32_t *n_out, uint8_t *partial, uint8_t *mask,

@@ -647,158 +647,6 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restric
 }
 
 // ---------------------------------------------------------------------------
-// Few rows (T <= 16, the decode regime): the whole quantization in one
-// launch of T blocks, block t quantizing row t.  The outlier set depends on
-// every row, and at these sizes each block can afford to read all of X (at
-// most 16 rows x 16384 columns): every block derives the same flags itself,
-// so no partial flags, compaction launch or workspace are needed.  A thread
-// owns the 8-column chunks c = tid, tid + 512, ... (G of them):
-//   1. it loads its chunks of every row, R rows at a time, keeps the column
-//      maxima of |x| (the flags follow from them) and row t's chunks;
-//   2. a block scan over the chunk flags in column order gives, per chunk,
-//      the number of outlier columns before it and n (block 0 also writes
-//      the ascending outlier list and n);
-//   3. the absmax of row t over the other columns (wave reductions and the 8
-//      wave maxima through LDS), then the packed int8 row and the row's
-//      outlier values in x_out.
-// The tests and the arithmetic are those of k_detect / k_compact /
-// k_rowquant, so the results are identical bit for bit.
-// ---------------------------------------------------------------------------
-constexpr int kSmallThreads = 512;
-constexpr int kSmallMaxChunks = 16 * kSmallThreads;   // G <= 16: K <= 65536
-
-template <int G>
-__global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
-    const uint16_t *__restrict__ X, int T, int K, unsigned thr_bits, int8_t *__restrict__ Xq,
-    float *__restrict__ a, int32_t *__restrict__ O, int32_t *__restrict__ n_out,
-    uint16_t *__restrict__ x_out, bool packed)
-{
-    constexpr int R = G >= 16 ? 1 : 32 / G;   // rows per batch: R*G loads in flight
-    __shared__ uint8_t s_flags[kSmallMaxChunks];
-    __shared__ int s_pre[kSmallMaxChunks];
-    __shared__ unsigned s_wmax[kSmallThreads / kWave];
-    __shared__ int s_wave_tot[kSmallThreads / kWave];
-    __shared__ int s_n;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int t = blockIdx.x;
-    const int nchunk = K / 8;
-
-    // 1. column flags over all rows; row t's chunks stay in registers
-    uint4 v[G], cm[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        v[g] = make_uint4(0u, 0u, 0u, 0u);
-        cm[g] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    for (int r0 = 0; r0 < T; r0 += R) {
-        uint4 w[R][G];
-#pragma unroll
-        for (int u = 0; u < R; ++u)
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const int r = r0 + u, c = tid + g * kSmallThreads;
-                w[u][g] = (r < T && c < nchunk)
-                              ? *reinterpret_cast<const uint4 *>(X + (int64_t)r * K + 8 * c)
-                              : make_uint4(0u, 0u, 0u, 0u);   // |0| is never above
-            }
-#pragma unroll
-        for (int u = 0; u < R; ++u)
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                cm[g] = colmax8(cm[g], w[u][g]);
-                if (r0 + u == t)
-                    v[g] = w[u][g];
-            }
-    }
-    unsigned fl[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int c = tid + g * kSmallThreads;
-        fl[g] = flags8(cm[g], thr_bits);
-        if (c < nchunk)
-            s_flags[c] = (uint8_t)fl[g];
-    }
-    __syncthreads();
-
-    // 2. outlier positions in column order (block scan)
-    const int per = (nchunk + kSmallThreads - 1) / kSmallThreads;
-    const int b0 = tid * per < nchunk ? tid * per : nchunk;
-    const int b1 = b0 + per < nchunk ? b0 + per : nchunk;
-    int cnt = 0;
-    for (int b = b0; b < b1; ++b)
-        cnt += __builtin_popcount(s_flags[b]);
-    int inc = cnt;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(inc, off, kWave);
-        if (lane >= off)
-            inc += o;
-    }
-    if (lane == kWave - 1)
-        s_wave_tot[wave] = inc;
-    // row t's absmax over the non-outlier columns
-    unsigned m = 0;
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-        m = umax(m, chunk_absmax_masked(v[g], fl[g]));
-    m = wave_max_u32(m);
-    if (lane == 0)
-        s_wmax[wave] = m;
-    __syncthreads();
-    int j = inc - cnt;
-    for (int w = 0; w < wave; ++w)
-        j += s_wave_tot[w];
-    for (int b = b0; b < b1; ++b) {
-        const unsigned mb = s_flags[b];
-        s_pre[b] = j;
-        if (t == 0) {
-            for (int i = 0; i < 8; ++i)
-                if ((mb >> i) & 1u)
-                    O[j++] = 8 * b + i;
-        } else {
-            j += __builtin_popcount(mb);
-        }
-    }
-    if (tid == kSmallThreads - 1) {
-        if (t == 0)
-            *n_out = j;
-        s_n = j;
-    }
-    unsigned amax_bits = 0;
-#pragma unroll
-    for (int w = 0; w < kSmallThreads / kWave; ++w)
-        amax_bits = umax(amax_bits, s_wmax[w]);
-    const float amax = h2f((uint16_t)amax_bits);
-    if (tid == 0)
-        a[t] = amax;
-    __syncthreads();
-
-    // 3. row t: int8 values and the gathered outlier values
-    const int n = s_n;
-    const int64_t ldo = outlier_ld(n);
-    const float r127 = amax > 0.0f ? 127.0f / amax : 0.0f;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int c = tid + g * kSmallThreads;
-        if (c >= nchunk)
-            continue;
-        const unsigned f = fl[g];
-        uint4 x = v[g];
-        if (f) {
-            if (x_out)
-                scatter_outliers(x, f, s_pre[c], x_out + t * ldo);
-            x = drop_flagged(x, f);
-        }
-        const uint2 q = quant8(x, amax, r127);
-        *xq_chunk(Xq, t, K, c, packed) = q;
-    }
-    if (x_out) {
-        for (int64_t idx = n + tid; idx < ldo; idx += kSmallThreads)
-            x_out[t * ldo + idx] = 0;
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Zero-point variant (the asymmetric quantizer of the LLM.int8() summary,
 // kurtkim.github.io, "8-bit Data Types and Quantization"): per vector the
 // range [min(min,0), max(max,0)] is mapped onto [-127, 127] by the
@@ -873,7 +721,206 @@ __device__ __forceinline__ uint2 quant8_zp(uint4 v, float nd, float zpf, int &su
     return pack_low_bytes(s);
 }
 
-// Weight: one wavefront per row n of W_t (output column n of W), over all K.
+// ---------------------------------------------------------------------------
+// Few rows (T <= 16, the decode regime): the whole quantization in one
+// launch of T blocks, block t quantizing row t.  The outlier set depends on
+// every row, and at these sizes each block can afford to read all of X (at
+// most 16 rows x 16384 columns): every block derives the same flags itself,
+// so no partial flags, compaction launch or workspace are needed.  A thread
+// owns the 8-column chunks c = tid, tid + 512, ... (G of them):
+//   1. it loads its chunks of every row, R rows at a time, keeps the column
+//      maxima of |x| (the flags follow from them) and row t's chunks;
+//   2. a block scan over the chunk flags in column order gives, per chunk,
+//      the number of outlier columns before it and n (block 0 also writes
+//      the ascending outlier list and n);
+//   3. the absmax of row t over the other columns (wave reductions and the 8
+//      wave maxima through LDS), then the packed int8 row and the row's
+//      outlier values in x_out.
+// The tests and the arithmetic are those of k_detect / k_compact /
+// k_rowquant, so the results are identical bit for bit.
+// ---------------------------------------------------------------------------
+constexpr int kSmallThreads = 512;
+constexpr int kSmallMaxChunks = 16 * kSmallThreads;   // G <= 16: K <= 65536
+
+// kZp: the zero-point variant (a receives nd, row_zp {zp, code sum}): the
+// range instead of the absmax in step 3, codes by quant8_zp, and one more
+// block reduction for the code sum.
+template <int G, bool kZp = false>
+__global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
+    const uint16_t *__restrict__ X, int T, int K, unsigned thr_bits, int8_t *__restrict__ Xq,
+    float *__restrict__ a, int32_t *__restrict__ O, int32_t *__restrict__ n_out,
+    uint16_t *__restrict__ x_out, bool packed, int2 *__restrict__ row_zp = nullptr)
+{
+    constexpr int R = G >= 16 ? 1 : 32 / G;   // rows per batch: R*G loads in flight
+    __shared__ uint8_t s_flags[kSmallMaxChunks];
+    __shared__ int s_pre[kSmallMaxChunks];
+    __shared__ unsigned s_wmax[kSmallThreads / kWave];
+    __shared__ float s_wmn[kZp ? kSmallThreads / kWave : 1];
+    __shared__ int s_wave_tot[kSmallThreads / kWave];
+    __shared__ int s_n;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int t = blockIdx.x;
+    const int nchunk = K / 8;
+
+    // 1. column flags over all rows; row t's chunks stay in registers
+    uint4 v[G], cm[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        v[g] = make_uint4(0u, 0u, 0u, 0u);
+        cm[g] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    for (int r0 = 0; r0 < T; r0 += R) {
+        uint4 w[R][G];
+#pragma unroll
+        for (int u = 0; u < R; ++u)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int r = r0 + u, c = tid + g * kSmallThreads;
+                w[u][g] = (r < T && c < nchunk)
+                              ? *reinterpret_cast<const uint4 *>(X + (int64_t)r * K + 8 * c)
+                              : make_uint4(0u, 0u, 0u, 0u);   // |0| is never above
+            }
+#pragma unroll
+        for (int u = 0; u < R; ++u)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                cm[g] = colmax8(cm[g], w[u][g]);
+                if (r0 + u == t)
+                    v[g] = w[u][g];
+            }
+    }
+    unsigned fl[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int c = tid + g * kSmallThreads;
+        fl[g] = flags8(cm[g], thr_bits);
+        if (c < nchunk)
+            s_flags[c] = (uint8_t)fl[g];
+    }
+    __syncthreads();
+
+    // 2. outlier positions in column order (block scan)
+    const int per = (nchunk + kSmallThreads - 1) / kSmallThreads;
+    const int b0 = tid * per < nchunk ? tid * per : nchunk;
+    const int b1 = b0 + per < nchunk ? b0 + per : nchunk;
+    int cnt = 0;
+    for (int b = b0; b < b1; ++b)
+        cnt += __builtin_popcount(s_flags[b]);
+    int inc = cnt;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(inc, off, kWave);
+        if (lane >= off)
+            inc += o;
+    }
+    if (lane == kWave - 1)
+        s_wave_tot[wave] = inc;
+    // row t's absmax (zero-point: range) over the non-outlier columns
+    if constexpr (kZp) {
+        float mn = 0.0f, mx = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            chunk_minmax(fl[g] ? drop_flagged(v[g], fl[g]) : v[g], mn, mx);
+        wave_minmax(mn, mx);
+        if (lane == 0) {
+            s_wmn[wave] = mn;
+            s_wmax[wave] = __builtin_bit_cast(unsigned, mx);
+        }
+    } else {
+        unsigned m = 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            m = umax(m, chunk_absmax_masked(v[g], fl[g]));
+        m = wave_max_u32(m);
+        if (lane == 0)
+            s_wmax[wave] = m;
+    }
+    __syncthreads();
+    int j = inc - cnt;
+    for (int w = 0; w < wave; ++w)
+        j += s_wave_tot[w];
+    for (int b = b0; b < b1; ++b) {
+        const unsigned mb = s_flags[b];
+        s_pre[b] = j;
+        if (t == 0) {
+            for (int i = 0; i < 8; ++i)
+                if ((mb >> i) & 1u)
+                    O[j++] = 8 * b + i;
+        } else {
+            j += __builtin_popcount(mb);
+        }
+    }
+    if (tid == kSmallThreads - 1) {
+        if (t == 0)
+            *n_out = j;
+        s_n = j;
+    }
+    float amax = 0.0f, r127 = 0.0f, zpf = 0.0f;
+    ZpParams p{0.0f, 0};
+    if constexpr (kZp) {
+        float mn = 0.0f, mx = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kSmallThreads / kWave; ++w) {
+            mn = __builtin_fminf(mn, s_wmn[w]);
+            mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, s_wmax[w]));
+        }
+        p = zp_params(mn, mx);
+        zpf = (float)p.zp;
+    } else {
+        unsigned amax_bits = 0;
+#pragma unroll
+        for (int w = 0; w < kSmallThreads / kWave; ++w)
+            amax_bits = umax(amax_bits, s_wmax[w]);
+        amax = h2f((uint16_t)amax_bits);
+        r127 = amax > 0.0f ? 127.0f / amax : 0.0f;
+        if (tid == 0)
+            a[t] = amax;
+    }
+    __syncthreads();
+
+    // 3. row t: int8 values and the gathered outlier values
+    const int n = s_n;
+    const int64_t ldo = outlier_ld(n);
+    int sum = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int c = tid + g * kSmallThreads;
+        if (c >= nchunk)
+            continue;
+        const unsigned f = fl[g];
+        uint4 x = v[g];
+        if (f) {
+            if (x_out)
+                scatter_outliers(x, f, s_pre[c], x_out + t * ldo);
+            x = drop_flagged(x, f);
+        }
+        const uint2 q = kZp ? quant8_zp(x, p.nd, zpf, sum) : quant8(x, amax, r127);
+        *xq_chunk(Xq, t, K, c, packed) = q;
+    }
+    if (x_out) {
+        for (int64_t idx = n + tid; idx < ldo; idx += kSmallThreads)
+            x_out[t * ldo + idx] = 0;
+    }
+    if constexpr (kZp) {
+        // the code sum of row t (s_wave_tot is free again: read before the
+        // last barrier)
+        sum = wave_sum(sum);
+        if (lane == 0)
+            s_wave_tot[wave] = sum;
+        __syncthreads();
+        if (tid == 0) {
+            int total = 0;
+#pragma unroll
+            for (int w = 0; w < kSmallThreads / kWave; ++w)
+                total += s_wave_tot[w];
+            a[t] = p.nd;
+            row_zp[t] = make_int2(p.zp, total);
+        }
+    }
+}
+
+// Zero-point weight quantization: one wavefront per row n of W_t (output
+// column n of W), over all K.
 __global__ __launch_bounds__(kBlock) void k_quantize_weight_zp(const uint16_t *__restrict__ W_t,
                                                                int64_t K, int64_t N,
                                                                int8_t *__restrict__ CB,
@@ -1060,6 +1107,29 @@ hipError_t launch_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K, float
 {
     if ((xq_packed && T > 16) || (g.w_out && !g.zp))
         return hipErrorInvalidValue;
+    if (!g.w_out && quantize_act_fits_rows(T, K)) {
+        // few rows: one launch (k_quant_rows in its zero-point mode)
+        const int64_t per = (K / 8 + kSmallThreads - 1) / kSmallThreads;
+        const unsigned tb = threshold_bits(threshold);
+        const dim3 grid((unsigned)T);
+#define LLMINT8_QROWS_ZP(G)                                                                    \
+    hipLaunchKernelGGL((k_quant_rows<G, true>), grid, dim3(kSmallThreads), 0, s, X, (int)T,    \
+                       (int)K, tb, Xq, nd, O, n_out, x_out, xq_packed, row_zp)
+        if (per <= 1)
+            LLMINT8_QROWS_ZP(1);
+        else if (per <= 2)
+            LLMINT8_QROWS_ZP(2);
+        else if (per <= 4)
+            LLMINT8_QROWS_ZP(4);
+        else if (per <= 8)
+            LLMINT8_QROWS_ZP(8);
+        else if (per <= 16)
+            LLMINT8_QROWS_ZP(16);
+        else
+            return hipErrorInvalidValue;
+#undef LLMINT8_QROWS_ZP
+        return hipGetLastError();
+    }
     const int64_t nchunk = K / 8;
     const int64_t rows_per = (T + kDetectSplits - 1) / kDetectSplits;
     const dim3 det_grid((unsigned)((nchunk + 31) / 32), (unsigned)kDetectSplits);

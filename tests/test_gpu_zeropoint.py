@@ -53,8 +53,11 @@ def test_quantize_weight_zp_exact(N, K):
     assert_equal_exact(d2h(RS), oracle_rowsum(CBr), "RS")
 
 
-@pytest.mark.parametrize("T,K", [(1, 64), (5, 256), (16, 1088), (17, 1024), (300, 576),
-                                 (513, 4160), (1024, 16384), (3, 33280)])
+# T <= 16 with K <= 16384 (T = 1: K <= 65536) take the one-launch kernel;
+# (3, 33280), (4, 16448) and (17, 1024) just past it, the three-kernel chain
+@pytest.mark.parametrize("T,K", [(1, 64), (5, 256), (16, 1088), (16, 16384), (1, 33280),
+                                 (4, 16448), (17, 1024), (300, 576), (513, 4160), (1024, 16384),
+                                 (3, 33280)])
 @pytest.mark.parametrize("thr", [6.0, 0.0, np.inf, 2.5])
 def test_quantize_act_zp_exact(T, K, thr):
     say("quantize_act_zp T=%d K=%d thr=%s" % (T, K, thr))
