@@ -12,7 +12,7 @@ accepted and reinterpreted.
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (worked examples printed on the pages, closed
 forms, special cases and brute force); the zero-point variant's functions by
-``tests/test_oracle_zeropoint.py``.  The one part without a pin to an
+``tests/test_oracle_zeropoint.py``, the FP8 variant's by ``tests/test_oracle_fp8.py``.  The one part without a pin to an
 independent value is the fp64 summation order of the fp16 outlier product,
 which sits far below the fp16 output tolerance.
 """
@@ -67,6 +67,13 @@ def _load():
     lib.oracle_matmul_zp.argtypes = [P, I64, I64, I64, P, P, P, P, ctypes.c_float,
                                      P, I64, P, I64, P, P, P, P, P]
     lib.oracle_matmul_zp.restype = I64
+    lib.oracle_e5m2_to_double_n.argtypes = [P, I64, P]
+    lib.oracle_double_to_e5m2_n.argtypes = [P, I64, P]
+    lib.oracle_f8_scale_exp_n.argtypes = [P, I64, P]
+    lib.oracle_quantize_weight_f8.argtypes = [P, I64, I64, P, P]
+    lib.oracle_quantize_rows_f8.argtypes = [P, I64, I64, P, I64, P, I64, P, P]
+    lib.oracle_matmul_f8.argtypes = [P, I64, I64, I64, P, P, P, ctypes.c_float,
+                                     P, I64, P, I64, P, P, P, P]
     _lib = lib
     return lib
 
@@ -288,3 +295,77 @@ def matmul_zp(X, CB, ND, ZP, threshold=6.0, bias=None, rows=None, cols=None):
     if bad:
         raise OverflowError("%d int32 overflows in the integer product" % bad)
     return out, O[: int(n[0])].copy(), nd[:nrows].copy(), zp[:nrows].copy()
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E5M2) variant.  Readings in llmint8_oracle.c: per vector a power-of-two
+# scale 2^e (the largest e with absmax * 2^e <= 57344), codes = E5M2 nearest
+# to x * 2^e, stored scale 2^-e; outlier columns are +0.
+# ---------------------------------------------------------------------------
+def e5m2_to_double(c):
+    c = np.ascontiguousarray(c, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e5m2_to_double_n(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def double_to_e5m2(v):
+    v = np.ascontiguousarray(v, np.float64)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_double_to_e5m2_n(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def f8_scale_exp(amax):
+    a = np.ascontiguousarray(amax, np.float64)
+    out = np.empty(a.shape, np.int32)
+    _load().oracle_f8_scale_exp_n(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def quantize_weight_f8(W_t):
+    """W_t: [N,K] fp16.  Returns (CB8 [N,K] uint8 E5M2 codes, SC8 [N] f32 scales 2^-e)."""
+    W_t = _bits(W_t)
+    N, K = W_t.shape
+    CB8 = np.empty((N, K), np.uint8)
+    SC8 = np.empty((N,), np.float32)
+    _load().oracle_quantize_weight_f8(_ptr(W_t), K, N, _ptr(CB8), _ptr(SC8))
+    return CB8, SC8
+
+
+def quantize_rows_f8(X, O, rows=None):
+    """Returns (Xq8 [nrows,K] uint8, sc8 [nrows] f32) for the listed rows."""
+    X = _bits(X)
+    T, K = X.shape
+    O = np.ascontiguousarray(O, np.int32)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    nrows = T if rows_arr is None else rows_arr.size
+    Xq8 = np.empty((nrows, K), np.uint8)
+    sc8 = np.empty((nrows,), np.float32)
+    _load().oracle_quantize_rows_f8(_ptr(X), T, K, _ptr(O), O.size, _ptr(rows_arr), nrows,
+                                    _ptr(Xq8), _ptr(sc8))
+    return Xq8, sc8
+
+
+def matmul_f8(X, CB8, SC8, threshold=6.0, bias=None, rows=None, cols=None):
+    """The decomposition with the non-outlier part in E5M2.  Returns
+    (out [nrows,ncols] uint16 binary16 bits, O int32, sc8 [nrows] f32)."""
+    X = _bits(X)
+    T, K = X.shape
+    CB8 = np.ascontiguousarray(CB8, np.uint8)
+    SC8 = np.ascontiguousarray(SC8, np.float32)
+    N = CB8.shape[0]
+    assert CB8.shape == (N, K) and SC8.shape == (N,)
+    b = _bits(bias) if bias is not None else None
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    cols_arr = None if cols is None else np.ascontiguousarray(cols, np.int64)
+    nrows = T if rows_arr is None else rows_arr.size
+    ncols = N if cols_arr is None else cols_arr.size
+    out = np.empty((nrows, ncols), np.uint16)
+    O = np.empty((max(K, 1),), np.int32)
+    n = np.zeros((1,), np.int64)
+    sc = np.empty((max(nrows, 1),), np.float32)
+    _load().oracle_matmul_f8(_ptr(X), T, K, N, _ptr(CB8), _ptr(SC8), _ptr(b), float(threshold),
+                             _ptr(rows_arr), nrows, _ptr(cols_arr), ncols, _ptr(out), _ptr(O),
+                             _ptr(n), _ptr(sc))
+    return out, O[: int(n[0])].copy(), sc[:nrows].copy()

@@ -36,8 +36,8 @@
  *     SCB, because only CB and SCB exist once the weight is quantized;
  *   - the output is one rounding to fp16 of the exact-as-possible (fp64)
  *     sum of the dequantized int8 part, the outlier part and the bias.
- * The zero-point (asymmetric) variant near the end of this file has its own
- * list of readings there.
+ * The zero-point (asymmetric) and FP8 variants near the end of this file
+ * have their own lists of readings there.
  *
  * fp16 values cross this interface as raw IEEE binary16 bit patterns
  * (uint16_t); the codec below is written from the bit layout.
@@ -554,6 +554,217 @@ void oracle_dequant_weight_zp_n(const int8_t *cb, const int32_t *zp, const float
 {
     for (int64_t i = 0; i < len; ++i)
         out[i] = oracle_dequant_weight_zp(cb[i], zp[i], nd[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 variant ([SUM] "Related work", 8-bit data types: floating-point 8-bit */
+/* formats with a 5-bit exponent and a 2-bit fraction are the common kind;   */
+/* "Discussion and Limitations": the Int8 findings are expected to carry     */
+/* over to FP8).  The same decomposition with the non-outlier part in E5M2.  */
+/*                                                                            */
+/* Readings (the pages give no FP8 procedure; each is listed in the design   */
+/* notes):                                                                   */
+/*   - E5M2 is the binary16 layout with a 2-bit fraction: sign, 5 exponent   */
+/*     bits with bias 15, 2 fraction bits; subnormals step 2^-16; largest    */
+/*     finite 57344;                                                         */
+/*   - vector-wise scaling as in the int8 method, by a power of two: each    */
+/*     vector is multiplied by 2^e, e the largest integer with               */
+/*     absmax * 2^e <= 57344 (e = 0 for an all-zero vector), so the scaling  */
+/*     is exact and the only rounding is to E5M2 (nearest, ties to even);    */
+/*     the stored scale is 2^-e, the factor that undoes it;                  */
+/*   - the row scale runs over the non-outlier columns, outlier columns are  */
+/*     +0 in the FP8 matrix, and the weight scale over all of K;             */
+/*   - the FP8 products are summed in fp64 here (the kernels accumulate in   */
+/*     fp32; the sum's rounding order is not fixed by the method);           */
+/*   - the outlier product uses the weight dequantized to fp16: the E5M2     */
+/*     value times its scale, rounded once to binary16.                      */
+/* ------------------------------------------------------------------------ */
+
+/* Exact value of an E5M2 code. */
+double oracle_e5m2_to_double(uint8_t c)
+{
+    int sign = (c >> 7) & 1;
+    int e = (c >> 2) & 31;
+    int f = c & 3;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -16);              /* subnormal: f/4 * 2^-14 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(4 + f), e - 17);     /* (1 + f/4) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Nearest E5M2 code to v, ties to even; |v| beyond 61440 (halfway between
+ * 57344 and 2^16) gives infinity. */
+uint8_t oracle_double_to_e5m2(double v)
+{
+    if (isnan(v))
+        return 0x7f;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return sign | 0x7c;
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;                     /* a in [2^E, 2^(E+1)) */
+    if (E < -14)
+        E = -14;                        /* subnormals share the lowest binade's spacing */
+    if (E > 15)
+        return sign | 0x7c;
+    double ulp = ldexp(1.0, E - 2);
+    double q = a / ulp;                 /* exact */
+    double r = floor(q);
+    double frac = q - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0))
+        r += 1.0;
+    if (r >= 8.0) {                     /* carried into the next binade */
+        r = 4.0;
+        E += 1;
+    }
+    if (E > 15)
+        return sign | 0x7c;
+    if (r < 4.0)                        /* only for E == -14: subnormal */
+        return sign | (uint8_t)r;
+    return sign | (uint8_t)(((E + 15) << 2) | ((int)r - 4));
+}
+
+/* The scaling exponent of a vector with absmax amax (a binary16 value):
+ * the largest e with amax * 2^e <= 57344; 0 when amax is 0. */
+int oracle_f8_scale_exp(double amax)
+{
+    if (amax == 0.0)
+        return 0;
+    int e = 0;
+    while (ldexp(amax, e) > 57344.0)
+        --e;
+    while (ldexp(amax, e + 1) <= 57344.0)
+        ++e;
+    return e;
+}
+
+/* W_t: [N,K] binary16.  CB8: [N,K] E5M2 codes, SC8: [N] scale 2^-e. */
+void oracle_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N,
+                               uint8_t *CB8, float *SC8)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint16_t *row = W_t + n * K;
+        uint16_t amax = 0;
+        for (int64_t k = 0; k < K; ++k)
+            if (half_abs_bits(row[k]) > amax)
+                amax = half_abs_bits(row[k]);
+        int e = oracle_f8_scale_exp(oracle_half_to_double(amax));
+        SC8[n] = (float)ldexp(1.0, -e);
+        for (int64_t k = 0; k < K; ++k)
+            CB8[n * K + k] = oracle_double_to_e5m2(ldexp(oracle_half_to_double(row[k]), e));
+    }
+}
+
+/* For each listed row t: the scale over the non-outlier columns, Xq8[i,k] =
+ * +0 for k in O, else the E5M2 code of X[t,k] * 2^e. */
+void oracle_quantize_rows_f8(const uint16_t *X, int64_t T, int64_t K,
+                             const int32_t *O, int64_t n,
+                             const int64_t *rows, int64_t nrows,
+                             uint8_t *Xq8, float *sc8)
+{
+    unsigned char *isout = outlier_mask(O, n, K);
+    if (rows == NULL)
+        nrows = T;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t t = rows ? rows[i] : i;
+        const uint16_t *xr = X + t * K;
+        uint16_t amax = 0;
+        for (int64_t k = 0; k < K; ++k)
+            if (!isout[k] && half_abs_bits(xr[k]) > amax)
+                amax = half_abs_bits(xr[k]);
+        int e = oracle_f8_scale_exp(oracle_half_to_double(amax));
+        sc8[i] = (float)ldexp(1.0, -e);
+        for (int64_t k = 0; k < K; ++k)
+            Xq8[i * K + k] = isout[k] ? 0 : oracle_double_to_e5m2(ldexp(oracle_half_to_double(xr[k]), e));
+    }
+    free(isout);
+}
+
+/* Dequantized fp16 weight of an E5M2 code with scale sc (a power of two):
+ * the exact product rounded once to binary16. */
+uint16_t oracle_dequant_weight_f8(uint8_t c, float sc)
+{
+    return oracle_double_to_half(oracle_e5m2_to_double(c) * (double)sc);
+}
+
+/* out[i,c] = fp16( sum_k e5m2(Xq8[t,k]) * e5m2(CB8[c,k]) * sc8[t] * SC8[c]
+ *                  + sum_{k in O} X[t,k] * Wdq8(CB8[c,k], SC8[c])  [+ bias[c]] ),
+ * the sum in fp64, rounded once.  Arguments as oracle_matmul; sc_out
+ * ([nrows]) receives the row scales. */
+void oracle_matmul_f8(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                      const uint8_t *CB8, const float *SC8, const uint16_t *bias,
+                      float threshold, const int64_t *rows, int64_t nrows,
+                      const int64_t *cols, int64_t ncols, uint16_t *out,
+                      int32_t *O_out, int64_t *n_out, float *sc_out)
+{
+    if (rows == NULL)
+        nrows = T;
+    if (cols == NULL)
+        ncols = N;
+    int32_t *O = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
+    int64_t n = oracle_outlier_columns(X, T, K, threshold, O);
+    uint8_t *Xq8 = (uint8_t *)malloc((size_t)(nrows * K > 0 ? nrows * K : 1));
+    float *sc = (float *)malloc(sizeof(float) * (size_t)(nrows > 0 ? nrows : 1));
+    oracle_quantize_rows_f8(X, T, K, O, n, rows, nrows, Xq8, sc);
+    double lut[256];
+    for (int v = 0; v < 256; ++v)
+        lut[v] = oracle_e5m2_to_double((uint8_t)v);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t t = rows ? rows[i] : i;
+        for (int64_t j = 0; j < ncols; ++j) {
+            int64_t c = cols ? cols[j] : j;
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += lut[Xq8[i * K + k]] * lut[CB8[c * K + k]];
+            double acc = s * (double)sc[i] * (double)SC8[c];
+            for (int64_t jj = 0; jj < n; ++jj) {
+                int64_t k = O[jj];
+                acc += oracle_half_to_double(X[t * K + k]) *
+                       oracle_half_to_double(oracle_dequant_weight_f8(CB8[c * K + k], SC8[c]));
+            }
+            if (bias)
+                acc += oracle_half_to_double(bias[c]);
+            out[i * ncols + j] = oracle_double_to_half(acc);
+        }
+    }
+    if (O_out)
+        memcpy(O_out, O, sizeof(int32_t) * (size_t)n);
+    if (n_out)
+        *n_out = n;
+    if (sc_out)
+        memcpy(sc_out, sc, sizeof(float) * (size_t)nrows);
+    free(O);
+    free(Xq8);
+    free(sc);
+}
+
+void oracle_e5m2_to_double_n(const uint8_t *c, int64_t len, double *out)
+{
+    for (int64_t i = 0; i < len; ++i)
+        out[i] = oracle_e5m2_to_double(c[i]);
+}
+
+void oracle_double_to_e5m2_n(const double *v, int64_t len, uint8_t *out)
+{
+    for (int64_t i = 0; i < len; ++i)
+        out[i] = oracle_double_to_e5m2(v[i]);
+}
+
+void oracle_f8_scale_exp_n(const double *a, int64_t len, int32_t *out)
+{
+    for (int64_t i = 0; i < len; ++i)
+        out[i] = oracle_f8_scale_exp(a[i]);
 }
 
 /* Number of threads the parallel loops use (for reporting the CPU baseline). */
