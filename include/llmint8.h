@@ -259,6 +259,67 @@ LLMINT8_API llmint8_status_t llmint8_matmul_zp_path(const uint16_t *X, int64_t T
                                                     hipEvent_t main_stop, hipStream_t stream);
 
 /*
+ * FP8 variant of the decomposition.  The LLM.int8() summary
+ * (kurtkim.github.io, "LLM.int8()", section "Related work", 8-bit data types)
+ * names floating-point 8-bit formats with a 5-bit exponent and a 2-bit
+ * fraction as the common kind, and its "Discussion and Limitations" expects
+ * the Int8 findings to carry over to FP8.  Here the non-outlier part is held
+ * in E5M2 (binary16's layout with a 2-bit fraction; largest finite 57344)
+ * with vector-wise power-of-two scales:
+ *
+ *   e        = largest integer with absmax * 2^e <= 57344   (0 for absmax 0)
+ *   code     = E5M2 nearest to x * 2^e, ties to even        (the scaling is exact)
+ *   scale    = 2^-e                                          (stored)
+ *   out[t,n] = fp16( sum_k e5m2(Xq8[t,k]) * e5m2(CB8[n,k]) * sc[t] * SC8[n]
+ *                    + sum_{k in O} X[t,k] * fp16(e5m2(CB8[n,k]) * SC8[n])  [+ bias[n]] )
+ *
+ * with the row absmax over the non-outlier columns (outlier columns are +0
+ * in Xq8) and the weight's over all K.  The E5M2 products are summed in fp32
+ * by the matrix cores (v_mfma_f32_32x32x64_f8f6f4; its sums of 64 products
+ * are not rounded like sequential fp32 additions), so the output is not
+ * unique to the last bit.  Shapes and conventions as llmint8_matmul.
+ */
+
+/*
+ * FP8 weight quantization, once per weight.
+ *   W_t in: fp16 [N,K];  CB8 out: E5M2 codes [N,K] (one byte each);  SC8 out: fp32 [N] scales.
+ */
+LLMINT8_API llmint8_status_t llmint8_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N,
+                                                        uint8_t *CB8, float *SC8,
+                                                        hipStream_t stream);
+
+/*
+ * FP8 activation quantization with outlier detection (as llmint8_quantize_act,
+ * same workspace query).  Xq8 out: E5M2 codes [T,K], outlier columns +0;
+ * row_scale out: fp32 [T] scales 2^-e.
+ */
+LLMINT8_API llmint8_status_t llmint8_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K,
+                                                     float threshold, uint8_t *Xq8,
+                                                     float *row_scale, int32_t *outlier_idx,
+                                                     int32_t *n_outliers, void *ws,
+                                                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The FP8 decomposition: out [T,N] fp16 from X [T,K] fp16 and the output of
+ * llmint8_quantize_weight_f8 (SC8 16-byte aligned).  Workspace:
+ * llmint8_workspace_bytes(T, K, N).
+ */
+LLMINT8_API llmint8_status_t llmint8_matmul_f8(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                               const uint8_t *CB8, const float *SC8,
+                                               const uint16_t *bias, float threshold,
+                                               uint16_t *out, void *ws, size_t ws_bytes,
+                                               hipStream_t stream);
+
+/* llmint8_matmul_f8 with the path choice and timing events of llmint8_matmul_path. */
+LLMINT8_API llmint8_status_t llmint8_matmul_f8_path(const uint16_t *X, int64_t T, int64_t K,
+                                                    int64_t N, const uint8_t *CB8,
+                                                    const float *SC8, const uint16_t *bias,
+                                                    float threshold, uint16_t *out, void *ws,
+                                                    size_t ws_bytes, int path,
+                                                    hipEvent_t main_start, hipEvent_t main_stop,
+                                                    hipStream_t stream);
+
+/*
  * The int8 product alone, C[t,n] = sum_k Xq[t,k] * CB[n,k] in int32 (LLM.int8()
  * summary, section "Int8 Matrix Multiplication with 16-bit Float Inputs and
  * Outputs"), through the same main loops as llmint8_matmul with the epilogue

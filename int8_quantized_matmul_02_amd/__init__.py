@@ -16,12 +16,16 @@ from .llmint8 import (  # noqa: F401
     llmint8_matmul,
     llmint8_matmul_act,
     llmint8_matmul_path,
+    llmint8_matmul_f8,
+    llmint8_matmul_f8_path,
     llmint8_matmul_zp,
     llmint8_matmul_zp_path,
     llmint8_quantize_act,
+    llmint8_quantize_act_f8,
     llmint8_quantize_act_workspace_bytes,
     llmint8_quantize_act_zp,
     llmint8_quantize_weight,
+    llmint8_quantize_weight_f8,
     llmint8_quantize_weight_zp,
     llmint8_status_string,
     llmint8_workspace_bytes,

@@ -305,6 +305,100 @@ llmint8_status_t llmint8_matmul_zp(const uint16_t *X, int64_t T, int64_t K, int6
                                   0, nullptr, nullptr, stream);
 }
 
+llmint8_status_t llmint8_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N, uint8_t *CB8,
+                                            float *SC8, hipStream_t stream)
+{
+    if (!W_t || !CB8 || !SC8 || !aligned16(W_t) || !aligned16(CB8))
+        return LLMINT8_ERR_INVALID_ARG;
+    llmint8_status_t st = check_shape(1, K, N);
+    if (st != LLMINT8_OK)
+        return st;
+    return launch_quantize_weight_f8(W_t, K, N, CB8, SC8, stream) == hipSuccess ? LLMINT8_OK
+                                                                                : LLMINT8_ERR_HIP;
+}
+
+llmint8_status_t llmint8_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                                         uint8_t *Xq8, float *row_scale, int32_t *outlier_idx,
+                                         int32_t *n_outliers, void *ws, size_t ws_bytes,
+                                         hipStream_t stream)
+{
+    if (!X || !Xq8 || !row_scale || !outlier_idx || !n_outliers || !ws || !aligned16(X) ||
+        !aligned16(Xq8) || !aligned16(ws) || bad_threshold(threshold))
+        return LLMINT8_ERR_INVALID_ARG;
+    llmint8_status_t st = check_shape(T, K, 64);
+    if (st != LLMINT8_OK)
+        return st;
+    if (ws_bytes < act_workspace_bytes(K))
+        return LLMINT8_ERR_WORKSPACE;
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    uint8_t *partial = base;
+    uint8_t *mask = base + align256((size_t)kDetectSplits * ((size_t)K / 8));
+    int32_t *chunk_pre = reinterpret_cast<int32_t *>(mask + align256((size_t)K / 8));
+    GatherArgs none{nullptr, nullptr, 0, nullptr};
+    none.f8 = true;
+    const hipError_t e = launch_quantize_act_f8(X, T, K, threshold, Xq8, row_scale, outlier_idx,
+                                                n_outliers, partial, mask, chunk_pre, nullptr,
+                                                none, false, stream);
+    return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
+}
+
+llmint8_status_t llmint8_matmul_f8_path(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                        const uint8_t *CB8, const float *SC8, const uint16_t *bias,
+                                        float threshold, uint16_t *out, void *ws, size_t ws_bytes,
+                                        int path, hipEvent_t main_start, hipEvent_t main_stop,
+                                        hipStream_t stream)
+{
+    if (!X || !CB8 || !SC8 || !out || !ws || !aligned16(X) || !aligned16(CB8) ||
+        !aligned16(SC8) || !aligned16(out) || !aligned16(ws) || bad_threshold(threshold) ||
+        path < 0 || path > 2)
+        return LLMINT8_ERR_INVALID_ARG;
+    llmint8_status_t st = check_shape(T, K, N);
+    if (st != LLMINT8_OK)
+        return st;
+    if (path == 2 && T > kDecodeMaxT)
+        return LLMINT8_ERR_UNSUPPORTED_SHAPE;
+    const MatmulWorkspace L = matmul_workspace_layout(T, K, N);
+    if (ws_bytes < L.total)
+        return LLMINT8_ERR_WORKSPACE;
+    const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
+
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    uint8_t *partial = base + L.partial;
+    uint8_t *mask = base + L.mask;
+    int32_t *chunk_pre = reinterpret_cast<int32_t *>(base + L.chunk_pre);
+    int32_t *O = reinterpret_cast<int32_t *>(base + L.outlier_idx);
+    int32_t *n_out = reinterpret_cast<int32_t *>(base + L.n_outliers);
+    float *sc = reinterpret_cast<float *>(base + L.row_absmax);
+    uint8_t *Xq8 = base + L.xq;
+    uint16_t *x_out = reinterpret_cast<uint16_t *>(base + L.x_out);
+    uint16_t *w_out = reinterpret_cast<uint16_t *>(base + L.w_out);
+    const int8_t *CB = reinterpret_cast<const int8_t *>(CB8);
+
+    GatherArgs g{CB, SC8, N, decode ? nullptr : w_out};
+    g.f8 = true;
+    const bool packed = decode && T >= kDecodePackedMinT;
+    const hipError_t eq = launch_quantize_act_f8(X, T, K, threshold, Xq8, sc, O, n_out, partial,
+                                                 mask, chunk_pre, x_out, g, packed, stream);
+    if (eq != hipSuccess)
+        return LLMINT8_ERR_HIP;
+    EpilogueArgs ep{sc, SC8, x_out, w_out, O, n_out, bias, out, nullptr, 0};
+    ep.f8 = true;
+    const int8_t *Xq = reinterpret_cast<const int8_t *>(Xq8);
+    const hipError_t e =
+        decode ? launch_decode(Xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
+               : launch_gemm(Xq, CB, T, K, N, ep, stream, main_start, main_stop);
+    return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
+}
+
+llmint8_status_t llmint8_matmul_f8(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                   const uint8_t *CB8, const float *SC8, const uint16_t *bias,
+                                   float threshold, uint16_t *out, void *ws, size_t ws_bytes,
+                                   hipStream_t stream)
+{
+    return llmint8_matmul_f8_path(X, T, K, N, CB8, SC8, bias, threshold, out, ws, ws_bytes, 0,
+                                  nullptr, nullptr, stream);
+}
+
 llmint8_status_t llmint8_igemm_i32(const int8_t *Xq, int64_t T, int64_t K, int64_t N,
                                    const int8_t *CB, int32_t *C, int path, hipStream_t stream)
 {

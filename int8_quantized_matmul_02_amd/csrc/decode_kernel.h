@@ -29,6 +29,7 @@
 // the bias, round once to fp16.
 #pragma once
 
+#include <type_traits>
 #include <utility>
 
 #include "internal.h"
@@ -78,9 +79,12 @@ __device__ __forceinline__ OutlierPrefetch prefetch_outliers(const int8_t *B, in
 // and the integer part is the shifted sum C + zp_b*(rs_a + K*zp_a) +
 // zp_a*rs_b, exact in wrapping 32-bit arithmetic (its true value fits int32),
 // divided by nd_a*nd_b; the outlier weights are fp16((cb + zp_b)/nd_b).
-template <bool kRawI32, bool kRelu = false, bool kZp = false>
-__device__ __forceinline__ void epilogue(const v4i acc, int lane, int64_t n, int64_t T, int64_t K,
-                                         int64_t N, const int8_t *B, const EpilogueArgs &ep,
+// FP8 variant (kF8): fp32 sums of E5M2 products, scaled by the row and
+// column scales (powers of two); the outlier weights are fp16(E5M2 * scale).
+template <bool kRawI32, bool kRelu = false, bool kZp = false, bool kF8 = false>
+__device__ __forceinline__ void epilogue(const std::conditional_t<kF8, v4f, v4i> acc, int lane,
+                                         int64_t n, int64_t T, int64_t K, int64_t N,
+                                         const int8_t *B, const EpilogueArgs &ep,
                                          const OutlierPrefetch &pre)
 {
     const int t0 = 4 * (lane / 16);
@@ -106,7 +110,7 @@ __device__ __forceinline__ void epilogue(const v4i acc, int lane, int64_t n, int
                 v[q] = (float)(int)c * (zp_inv(ep.a[t]) * ib);
             }
         } else {
-            const float sn_d = sn * (1.0f / 16129.0f);
+            const float sn_d = kF8 ? sn : sn * (1.0f / 16129.0f);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int64_t t = t0 + q < T ? t0 + q : T - 1;
@@ -127,9 +131,14 @@ __device__ __forceinline__ void epilogue(const v4i acc, int lane, int64_t n, int
                     const int o = o0 + j < pre.nout ? ep.O[o0 + j] : 0;
                     cb = B[n * K + o];
                 }
-                w[j] = o0 + j < pre.nout
-                           ? h2f(kZp ? dequant_w_zp(cb, zb, sn) : dequant_w(cb, sn))
-                           : 0.0f;
+                uint16_t wd;
+                if constexpr (kF8)
+                    wd = dequant_w_f8((unsigned)cb & 0xffu, sn);
+                else if constexpr (kZp)
+                    wd = dequant_w_zp(cb, zb, sn);
+                else
+                    wd = dequant_w(cb, sn);
+                w[j] = o0 + j < pre.nout ? h2f(wd) : 0.0f;
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -194,7 +203,7 @@ struct CfgRs {
     static_assert(kWait < 64, "vmcnt range");
 };
 
-template <class C, bool kRawI32, bool kRelu = false, bool kZp = false>
+template <class C, bool kRawI32, bool kRelu = false, bool kZp = false, bool kF8 = false>
 __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restrict__ A,
                                                            const int8_t *__restrict__ B,
                                                            int64_t T, int64_t K, int64_t N,
@@ -265,7 +274,7 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
                 a[s2] = *reinterpret_cast<const v4i *>(pa + kc + 64 * s2);
         }
     };
-    v4i acc = v4i{0, 0, 0, 0};
+    std::conditional_t<kF8, v4f, v4i> acc = {0, 0, 0, 0};
     // Fragment reads in groups of kReadGroup, each group issued before its
     // MFMAs (each MFMA waits only for its own read).  The first `skip` bytes
     // of the last stage were already summed by the previous stage: their
@@ -281,8 +290,21 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < C::kReadGroup; ++i)
-                if (64 * (s0 + i) >= skip)
-                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[s0 + i], b[i], acc, 0, 0, 0);
+                if (64 * (s0 + i) >= skip) {
+                    if constexpr (kF8) {
+                        // E5M2: two 16x16x32 MFMAs, the low and the high 8
+                        // bytes of both fragments (the same k's in both)
+                        const v4i x = a[s0 + i], y = b[i];
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf8_bf8(
+                            ((long)(unsigned)x[1] << 32) | (unsigned)x[0],
+                            ((long)(unsigned)y[1] << 32) | (unsigned)y[0], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf8_bf8(
+                            ((long)(unsigned)x[3] << 32) | (unsigned)x[2],
+                            ((long)(unsigned)y[3] << 32) | (unsigned)y[2], acc, 0, 0, 0);
+                    } else {
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[s0 + i], b[i], acc, 0, 0, 0);
+                    }
+                }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -361,7 +383,7 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
              ...);
         }(std::make_integer_sequence<int, C::kUnroll>{});
     }
-    epilogue<kRawI32, kRelu, kZp>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
+    epilogue<kRawI32, kRelu, kZp, kF8>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
 }
 
 // ---------------------------------------------------------------------------
@@ -452,10 +474,12 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_lds(const int8_t *__rest
     epilogue<kRawI32>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
 }
 
-template <class C, bool R, bool kRelu = false, bool kZp = false>
+template <class C, bool R, bool kRelu = false, bool kZp = false, bool kF8 = false>
 struct RsKernel {
-    static constexpr auto fn = k_decode_rs<C, R, kRelu, kZp>;
+    static constexpr auto fn = k_decode_rs<C, R, kRelu, kZp, kF8>;
 };
+template <class C, bool R>
+using RsKernelF8 = RsKernel<C, R, false, false, true>;
 template <class C, bool R>
 using RsKernelRelu = RsKernel<C, R, true>;
 template <class C, bool R>
@@ -497,6 +521,8 @@ hipError_t launch_rs(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, i
 {
     if (C::kSync && N % (16 * C::WAVES) != 0)
         return hipErrorInvalidValue;   // a block's wavefronts must all reach the barriers
+    if (ep.f8 && !ep.c_i32)
+        return launch_kernel<C, RsKernelF8>(Xq, CB, T, K, N, ep, s, ev0, ev1);
     if (ep.row_zp && !ep.c_i32)
         return launch_kernel<C, RsKernelZp>(Xq, CB, T, K, N, ep, s, ev0, ev1);
     if (ep.act && !ep.c_i32)

@@ -426,6 +426,130 @@ __device__ __forceinline__ void mainloop(char *smem, const Streams<C> &st, int n
     wait_vm<0>();   // the tail loads land before anyone reuses the buffers
 }
 
+// FP8 variant: v_mfma_f32_32x32x64_f8f6f4 on E5M2 codes (format 1 for both
+// operands, no block scales) with fp32 accumulators.  A 64-deep k-step
+// takes 32 bytes per lane: lane half h reads 16-byte chunks 4s + h and
+// 4s + 2 + h of the 64-byte k-step s, for A and B alike, so both operands
+// hold the same k values in the same places and the sum covers all 64.
+struct MfmaF8 {
+    typedef v16f acc_t;
+    __device__ __forceinline__ static acc_t op(v8i a, v8i b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 1, 1, 0, 0, 0, 0);
+    }
+};
+
+template <class C>
+struct Frags8 {
+    v8i a[C::FM], b[C::FN];
+};
+
+__device__ __forceinline__ v8i frag8(const char *p, int fo0, int fo1)
+{
+    const v4i lo = *reinterpret_cast<const v4i *>(p + fo0);
+    const v4i hi = *reinterpret_cast<const v4i *>(p + fo1);
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// read_one's order (a0, b0 .. b(FN-1), a1 .. a(FM-1)) for 32-byte fragments.
+template <class C>
+__device__ __forceinline__ void read_one8(Frags8<C> &f, const char *sa, const char *sb, int fo0,
+                                          int fo1, int g)
+{
+    if (g == 0)
+        f.a[0] = frag8(sa, fo0, fo1);
+    else if (g <= C::FN)
+        f.b[g - 1] = frag8(sb + (g - 1) * 32 * C::ROWB, fo0, fo1);
+    else
+        f.a[g - C::FN] = frag8(sa + (g - C::FN) * 32 * C::ROWB, fo0, fo1);
+}
+
+// kstep for the FP8 k-steps: the same groups of (load issue, fragment read,
+// MFMAs) pinned by scheduling barriers.
+template <class C, int kL0, int kNL>
+__device__ __forceinline__ void kstep8(const Frags8<C> &cur, Frags8<C> &nxt, const char *sa,
+                                       const char *sb, int fo0, int fo1,
+                                       v16f (&acc)[C::FM][C::FN], const Streams<C> &st,
+                                       char *smem, int stage, int64_t kbyte, int wave)
+{
+    constexpr int kReads = C::FM + C::FN, kMfma = C::FM * C::FN;
+    constexpr int kGroups = kReads > kNL ? kReads : kNL;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+        if (g < kNL)
+            st.issue_one(smem, stage, kbyte, wave, kL0 + g);
+        if (g < kReads)
+            read_one8<C>(nxt, sa, sb, fo0, fo1, g);
+#pragma unroll
+        for (int idx = g * kMfma / kGroups; idx < (g + 1) * kMfma / kGroups; ++idx) {
+            const int i = idx / C::FN, j = idx % C::FN;
+            acc[i][j] = MfmaF8::op(cur.b[j], cur.a[i], acc[i][j]);   // D[n][t], as k_gemm
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The pipelined main loop of `mainloop` (same stage ring, waits, barrier
+// and refill placement) over ROWB/64 FP8 k-steps per stage.
+template <class C>
+__device__ __forceinline__ void mainloop_f8(char *smem, const Streams<C> &st, int numK,
+                                            v16f (&acc)[C::FM][C::FN], int wm, int wn, int wave,
+                                            int lane)
+{
+    constexpr int kS = C::ROWB / 64;
+    const int frow = (lane & 31) * C::ROWB, h = lane >> 5, sw = C::swz(lane & 31);
+    int fo0[kS], fo1[kS];
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+        fo0[s] = frow + (((4 * s + h) ^ sw) << 4);
+        fo1[s] = frow + (((4 * s + 2 + h) ^ sw) << 4);
+    }
+    const int aoff = wm * (C::BM / C::WM) * C::ROWB;
+    const int boff = C::BM * C::ROWB + wn * (C::BN / C::WN) * C::ROWB;
+    const int64_t klast = (int64_t)(numK - 1) * C::ROWB;
+    auto kb = [&](int s) -> int64_t {
+        const int64_t k = (int64_t)s * C::ROWB;
+        return k < klast ? k : klast;
+    };
+    auto stage_a = [&](int s) { return smem + (s % C::STAGES) * C::kStageBytes + aoff; };
+    auto stage_b = [&](int s) { return smem + (s % C::STAGES) * C::kStageBytes + boff; };
+
+#pragma unroll
+    for (int s = 0; s < C::STAGES; ++s)
+        st.issue(smem, s, kb(s), wave);
+    wait_vm<(C::STAGES - 1) * C::kLoads>();   // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+
+    Frags8<C> f0, f1;
+#pragma unroll
+    for (int g = 0; g < C::FM + C::FN; ++g)
+        read_one8<C>(f0, stage_a(0), stage_b(0), fo0[0], fo1[0], g);
+    for (int kt = 0; kt < numK; ++kt) {
+#pragma unroll
+        for (int s = 0; s < kS; ++s) {
+            Frags8<C> &cur = s % 2 == 0 ? f0 : f1;
+            Frags8<C> &nxt = s % 2 == 0 ? f1 : f0;
+            if (s + 1 < kS) {
+                kstep8<C, 0, 0>(cur, nxt, stage_a(kt), stage_b(kt), fo0[s + 1], fo1[s + 1], acc,
+                                st, smem, 0, 0, wave);
+            } else {
+                wait_vm<(C::STAGES - 2) * C::kLoads>();   // stage kt+1 landed
+                __builtin_amdgcn_s_barrier();
+                const int nk = kt + 1 < numK ? kt + 1 : kt;
+                kstep8<C, 0, C::kLoads>(cur, nxt, stage_a(nk), stage_b(nk), fo0[0], fo1[0], acc,
+                                        st, smem, kt % C::STAGES, kb(kt + C::STAGES), wave);
+            }
+        }
+        // with an odd number of k-steps per stage the buffers swap roles
+        if constexpr (kS % 2 == 1) {
+            const Frags8<C> t = f0;
+            f0 = f1;
+            f1 = t;
+        }
+    }
+    wait_vm<0>();   // the tail loads land before anyone reuses the buffers
+}
+
 // The main loop for the stage shape: read-two-ahead for the int8 product
 // over 128-byte stages (the fp16 pass over many outlier columns keeps the
 // one-ahead loop: its fp32 accumulators leave no room for the third
@@ -549,8 +673,8 @@ __device__ __forceinline__ float zp_dequant(int acc, int za, int ra, int zb, int
 // wavefront has stopped reading; then the whole block tile is written out.
 // Operands come from clamped addresses and the column scales are loaded one
 // column group ahead, so no latency is paid per accumulator tile.
-template <class C, bool kBias, bool kRelu, bool kZp>
-__device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], const float (&at)[C::FM],
+template <class C, bool kBias, bool kRelu, bool kZp, class Acc = v16i>
+__device__ __forceinline__ void finish_tile(const Acc (&acc)[C::FM][C::FN], const float (&at)[C::FM],
                                             const int (&za)[C::FM], const int (&ra)[C::FM],
                                             const char *orows,
                                             char *smem, const EpilogueArgs &ep, int64_t m0,
@@ -659,8 +783,8 @@ __device__ __forceinline__ void finish_tile(const v16i (&acc)[C::FM][C::FN], con
 // there, so the two share registers) onto which the fp16 MFMAs add; then
 // the bias, one rounding, and the tile goes out through LDS like
 // finish_tile's.
-template <class C, bool kRelu, bool kZp>
-__device__ __forceinline__ void outlier_pass(const v16i (&acc)[C::FM][C::FN],
+template <class C, bool kRelu, bool kZp, class Acc = v16i>
+__device__ __forceinline__ void outlier_pass(const Acc (&acc)[C::FM][C::FN],
                                              const float (&at)[C::FM], const int (&za)[C::FM],
                                              const int (&ra)[C::FM], char *smem,
                                              const EpilogueArgs &ep, int64_t m0, int64_t n0,
@@ -744,7 +868,7 @@ __device__ __forceinline__ void outlier_pass(const v16i (&acc)[C::FM][C::FN],
     write_tile<C>(smem, ep, m0, n0, T, N, tid);
 }
 
-template <class C, bool kRawI32, bool kRelu, bool kZp = false>
+template <class C, bool kRawI32, bool kRelu, bool kZp = false, bool kF8 = false>
 __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__ A,
                                                       const int8_t *__restrict__ B, int64_t T,
                                                       int64_t K, int64_t N, EpilogueArgs ep)
@@ -770,7 +894,8 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
     if constexpr (!kRawI32)
         issue_outlier_rows<C>(orows, ep, m0, n0, T, N, wave, lane);
 
-    v16i acc[C::FM][C::FN];
+    using Acc = std::conditional_t<kF8, v16f, v16i>;
+    Acc acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -783,7 +908,10 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
         Streams<C> st;
         st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
                 n0, N, wave, lane);
-        run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+        if constexpr (kF8)
+            mainloop_f8<C>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+        else
+            run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
     }
 
     // The MFMAs compute D = CB_tile * Xq_tile^T, so a 32x32 accumulator holds
@@ -818,15 +946,17 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
             const int64_t t = tw + i * 32 + tl;
             if constexpr (kZp)
                 zp_row(ep, t < T ? t : T - 1, K, at[i], za[i], ra[i]);
+            else if constexpr (kF8)
+                at[i] = ep.a[t < T ? t : T - 1];   // the row scale 2^-e
             else
                 at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
         }
         if (ep.bias)
-            finish_tile<C, true, kRelu, kZp>(acc, at, za, ra, orows, smem, ep, m0, n0, T, N, nout,
-                                             wm, wn, lane, tid);
+            finish_tile<C, true, kRelu, kZp, Acc>(acc, at, za, ra, orows, smem, ep, m0, n0, T, N,
+                                                  nout, wm, wn, lane, tid);
         else
-            finish_tile<C, false, kRelu, kZp>(acc, at, za, ra, orows, smem, ep, m0, n0, T, N, nout,
-                                              wm, wn, lane, tid);
+            finish_tile<C, false, kRelu, kZp, Acc>(acc, at, za, ra, orows, smem, ep, m0, n0, T, N,
+                                                   nout, wm, wn, lane, tid);
     }
 }
 
@@ -836,7 +966,7 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
 // fp16 pass over the outlier columns.  A kernel of its own so that the
 // registers this path needs do not cost k_gemm's epilogue; one tile per
 // block (a persistent tile loop makes the compiler spill around it).
-template <class C, bool kRelu, bool kZp = false>
+template <class C, bool kRelu, bool kZp = false, bool kF8 = false>
 __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restrict__ A,
                                                            const int8_t *__restrict__ B,
                                                            int64_t T, int64_t K, int64_t N,
@@ -854,7 +984,8 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restr
     tile_coords(blockIdx.x, gridDim.x, ntm, ntn, C::GROUP, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
 
-    v16i acc[C::FM][C::FN];
+    using Acc = std::conditional_t<kF8, v16f, v16i>;
+    Acc acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -866,7 +997,10 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restr
         Streams<C> st;
         st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
                 n0, N, wave, lane);
-        run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+        if constexpr (kF8)
+            mainloop_f8<C>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+        else
+            run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
     }
     float at[C::FM];
     int za[C::FM], ra[C::FM];
@@ -876,11 +1010,13 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restr
         const int64_t t = tw + i * 32;
         if constexpr (kZp)
             zp_row(ep, t < T ? t : T - 1, K, at[i], za[i], ra[i]);
+        else if constexpr (kF8)
+            at[i] = ep.a[t < T ? t : T - 1];
         else
             at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
     }
-    outlier_pass<C, kRelu, kZp>(acc, at, za, ra, smem, ep, m0, n0, T, K, N, nout, wm, wn, wave,
-                                lane, tid);
+    outlier_pass<C, kRelu, kZp, Acc>(acc, at, za, ra, smem, ep, m0, n0, T, K, N, nout, wm, wn,
+                                     wave, lane, tid);
 }
 
 // The int8 GEMM (K must be a multiple of C::ROWB) with its fused epilogue
@@ -904,6 +1040,9 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
     if (ep.c_i32)
         hipLaunchKernelGGL((k_gemm<C, true, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K,
                            N, ep);
+    else if (ep.f8)
+        hipLaunchKernelGGL((k_gemm<C, false, false, false, true>), grid, dim3(C::kThreads), 0, s,
+                           Xq, CB, T, K, N, ep);
     else if (ep.row_zp)
         hipLaunchKernelGGL((k_gemm<C, false, false, true>), grid, dim3(C::kThreads), 0, s, Xq, CB,
                            T, K, N, ep);
@@ -919,7 +1058,10 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
             return e;
     }
     if (!ep.c_i32) {
-        if (ep.row_zp)
+        if (ep.f8)
+            hipLaunchKernelGGL((k_gemm_many<C, false, false, true>), grid, dim3(C::kThreads), 0, s,
+                               Xq, CB, T, K, N, ep);
+        else if (ep.row_zp)
             hipLaunchKernelGGL((k_gemm_many<C, false, true>), grid, dim3(C::kThreads), 0, s, Xq, CB,
                                T, K, N, ep);
         else if (ep.act)

@@ -8,6 +8,7 @@
 namespace llmint8 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -66,6 +67,31 @@ __device__ __forceinline__ uint16_t dequant_w_zp(int cb, int zp, float nd)
     return nd > 0.0f ? f2h((float)(cb + zp) / nd) : (uint16_t)0;
 }
 
+// FP8 (E5M2) variant.  An E5M2 code is the high byte of the binary16 with
+// the same value (same sign, exponent field and bias; 2 of the 10 fraction
+// bits), so decoding is a shift.
+__device__ __forceinline__ float e5m2_to_f(unsigned c) { return h2f((uint16_t)(c << 8)); }
+
+// The power of two 2^e that scales a vector with absmax a (an fp16 value, as
+// fp32) into E5M2's range: e is the largest integer with a * 2^e <= 57344 =
+// 1.75 * 2^15 (e = 0 for a = 0).  With a = f * 2^E, f in [1, 2): e = 15 - E
+// for f <= 1.75, else 14 - E.
+__device__ __forceinline__ int f8_scale_exp(float a)
+{
+    if (!(a > 0.0f))
+        return 0;
+    int ex;
+    const float fr = __builtin_frexpf(a, &ex);   // a = fr * 2^ex, fr in [0.5, 1)
+    return (2.0f * fr <= 1.75f ? 15 : 14) - (ex - 1);
+}
+
+// fp16 weight of E5M2 code c in a column with scale sc (a power of two): the
+// exact product rounded once.
+__device__ __forceinline__ uint16_t dequant_w_f8(unsigned c, float sc)
+{
+    return f2h(e5m2_to_f(c) * sc);
+}
+
 // 1/nd for the zero-point dequantization (0 when nd = 0).  v_rcp_f32 is
 // within 1 ulp: the dequantized value, an fp32 product rounded to fp16 at
 // the end, moves by a few fp32 ulps at most.
@@ -102,10 +128,11 @@ hipError_t launch_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N, int
 // stride.  w_out == null skips it.
 struct GatherArgs {
     const int8_t *CB;
-    const float *SCB;   // zero-point variant: nd of each column
+    const float *SCB;   // zero-point variant: nd of each column; FP8: scale 2^-e
     int64_t N;
     uint16_t *w_out;
     const int32_t *zp = nullptr;   // zero-point variant: zp of each column (else null)
+    bool f8 = false;               // FP8 variant: CB holds E5M2 codes
 };
 
 // Row ranges of the outlier detection: the partial-flag buffer holds
@@ -159,6 +186,9 @@ struct EpilogueArgs {
     const int2 *row_zp = nullptr;
     const int32_t *zp_b = nullptr;
     const int32_t *rs_b = nullptr;
+    // FP8 variant: Xq and CB hold E5M2 codes, a and scb the scales 2^-e of
+    // the rows and columns; the products are summed in fp32 by fp8 MFMAs.
+    bool f8 = false;
 };
 
 // Zero-point variant (the asymmetric quantizer of the LLM.int8() summary,
@@ -183,6 +213,21 @@ hipError_t launch_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K, float
                                   int32_t *n_out, uint8_t *partial, uint8_t *mask,
                                   int32_t *chunk_pre, uint16_t *x_out, const GatherArgs &g,
                                   bool xq_packed, hipStream_t s);
+
+// FP8 variant (E5M2, the 5-bit-exponent, 2-bit-fraction format the
+// LLM.int8() summary names under "Related work"): per vector a power-of-two
+// scale 2^e (f8_scale_exp of the absmax; the row absmax over the
+// non-outlier columns), codes = E5M2 nearest to x * 2^e (ties to even),
+// stored scale 2^-e; outlier columns are +0.  Weight: per row of W_t.
+hipError_t launch_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N, uint8_t *CB8,
+                                     float *SC8, hipStream_t s);
+// Activations: as launch_quantize_act (same kernels with the E5M2 codes;
+// sc receives the row scales 2^-e); g.f8 must be set when g.w_out is.
+hipError_t launch_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                                  uint8_t *Xq8, float *sc, int32_t *O, int32_t *n_out,
+                                  uint8_t *partial, uint8_t *mask, int32_t *chunk_pre,
+                                  uint16_t *x_out, const GatherArgs &g, bool xq_packed,
+                                  hipStream_t s);
 
 // ev0/ev1 (optional) are recorded on s right before and after the main kernel.
 hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,

@@ -121,6 +121,36 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float amax, float r)
     return pack_low_bytes(s);
 }
 
+// FP8 variant: E5M2 codes of 8 values scaled by sc = 2^e (the product is
+// exact: a power of two, and |x * 2^e| <= 57344), each rounded to the
+// nearest E5M2 value with ties to even by v_cvt_pk_bf8_f32 (two per
+// instruction, into the low or high half of a dword).
+__device__ __forceinline__ uint2 quant8_f8(uint4 v, float sc)
+{
+    unsigned w[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        int x = 0;
+        x = __builtin_amdgcn_cvt_pk_bf8_f32(h2f(half_at(v, 4 * d)) * sc,
+                                            h2f(half_at(v, 4 * d + 1)) * sc, x, false);
+        x = __builtin_amdgcn_cvt_pk_bf8_f32(h2f(half_at(v, 4 * d + 2)) * sc,
+                                            h2f(half_at(v, 4 * d + 3)) * sc, x, true);
+        w[d] = (unsigned)x;
+    }
+    return make_uint2(w[0], w[1]);
+}
+
+// The row quantization of an absmax-type kernel: int8 codes from (amax, r =
+// 127/amax), or (kF8) E5M2 codes from sc = 2^e.
+template <bool kF8>
+__device__ __forceinline__ uint2 quant8_mode(uint4 v, float amax, float r, float sc)
+{
+    if constexpr (kF8)
+        return quant8_f8(v, sc);
+    else
+        return quant8(v, amax, r);
+}
+
 // v with the halves whose flag bit is set replaced by +0.
 __device__ __forceinline__ uint4 drop_flagged(uint4 v, unsigned fl)
 {
@@ -162,6 +192,32 @@ __global__ __launch_bounds__(kBlock) void k_quantize_weight(const uint16_t *__re
     }
     if (lane == 0)
         SCB[n] = amax;
+}
+
+// FP8 variant: one wavefront per output column, the power-of-two scale of
+// the row's absmax, E5M2 codes, and the stored scale 2^-e.
+__global__ __launch_bounds__(kBlock) void k_quantize_weight_f8(const uint16_t *__restrict__ W_t,
+                                                               int64_t K, int64_t N,
+                                                               uint8_t *__restrict__ CB8,
+                                                               float *__restrict__ SC8)
+{
+    const int lane = threadIdx.x % kWave;
+    const int64_t n = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    if (n >= N)
+        return;
+    const uint4 *row = reinterpret_cast<const uint4 *>(W_t + n * K);
+    const int64_t nchunk = K / 8;
+    unsigned m = 0;
+    for (int64_t c = lane; c < nchunk; c += kWave)
+        m = umax(m, chunk_absmax(row[c]));
+    m = wave_max_u32(m);
+    const int e = f8_scale_exp(h2f((uint16_t)m));
+    const float sc = __builtin_ldexpf(1.0f, e);
+    uint2 *dst = reinterpret_cast<uint2 *>(CB8 + n * K);
+    for (int64_t c = lane; c < nchunk; c += kWave)
+        dst[c] = quant8_f8(row[c], sc);
+    if (lane == 0)
+        SC8[n] = __builtin_ldexpf(1.0f, -e);
 }
 
 // ---------------------------------------------------------------------------
@@ -345,15 +401,16 @@ __device__ __forceinline__ void scatter_outliers(uint4 v, unsigned fl, int pre,
 // One chunk of a row: outlier columns (flags fl) are 0 in the int8 row and go
 // to the compact row xrow (null: not gathered) from position pre on; the
 // others are quantized (r = 127/amax, or 0 when amax = 0).
+template <bool kF8 = false>
 __device__ __forceinline__ void quant_chunk(uint4 v, unsigned fl, float amax, float r, int pre,
-                                           uint16_t *__restrict__ xrow, uint2 *dst)
+                                           uint16_t *__restrict__ xrow, uint2 *dst, float sc = 0.0f)
 {
     if (fl) {
         if (xrow)
             scatter_outliers(v, fl, pre, xrow);
         v = drop_flagged(v, fl);
     }
-    *dst = quant8(v, amax, r);
+    *dst = quant8_mode<kF8>(v, amax, r, sc);
 }
 
 __device__ __forceinline__ unsigned chunk_absmax_masked(uint4 v, unsigned fl)
@@ -383,15 +440,22 @@ __device__ __forceinline__ uint2 *xq_chunk(int8_t *Xq, int64_t t, int64_t K, int
 // so the table is complete before any lane reads it, and the reads of one
 // row are done before the next row's table overwrites it.)  Entries of O at
 // or past n are stale: column 0 is read in their place and the value is 0.
-// Zero-point variant (kZp): SCB holds each row's nd, ZP its zp, and the
-// values are fp16((cb + zp) / nd).
-template <bool kZp>
+// kMode 0: absmax.  1, zero-point variant: SCB holds each row's nd, ZP its
+// zp, and the values are fp16((cb + zp) / nd).  2, FP8 variant: the bytes
+// are E5M2 codes and SCB the scales 2^-e.
+constexpr int kModeAbsmax = 0, kModeZp = 1, kModeF8 = 2;
+template <int kMode>
 __device__ __forceinline__ uint16_t dequant_row(int cb, float sc, int zp)
 {
-    return kZp ? dequant_w_zp(cb, zp, sc) : dequant_w(cb, sc);
+    if constexpr (kMode == kModeF8)
+        return dequant_w_f8((unsigned)cb & 0xffu, sc);
+    else if constexpr (kMode == kModeZp)
+        return dequant_w_zp(cb, zp, sc);
+    else
+        return dequant_w(cb, sc);
 }
 
-template <bool kZp = false>
+template <int kMode = kModeAbsmax>
 __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
                                              const int32_t *__restrict__ n_out,
                                              const int8_t *__restrict__ CB,
@@ -415,12 +479,12 @@ __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
         for (int64_t r = (gb * kWavesPerBlock + wave) * kRowsPerWave + lane / kGroups; r < N;
              r += nb * kWavesPerBlock * kRowsPerWave) {
             const float sc = SCB[r];
-            const int zr = kZp ? ZP[r] : 0;
+            const int zr = kMode == kModeZp ? ZP[r] : 0;
             const int8_t *cbr = CB + r * K;
             unsigned h[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const unsigned v = dequant_row<kZp>(cbr[o[e]], sc, zr);
+                const unsigned v = dequant_row<kMode>(cbr[o[e]], sc, zr);
                 h[e] = 8 * g + e < n ? v : 0u;
             }
             *reinterpret_cast<uint4 *>(w_out + r * kOutlierPad + 8 * g) =
@@ -431,9 +495,12 @@ __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
     }
     for (int64_t r = gb * kWavesPerBlock + wave; r < N; r += nb * kWavesPerBlock) {
         const float sc = SCB[r];
-        const int zr = kZp ? ZP[r] : 0;
-        for (int i = lane; i < 255; i += kWave)
-            tab[i] = dequant_row<kZp>(i - 127, sc, zr);
+        const int zr = kMode == kModeZp ? ZP[r] : 0;
+        // table index: code + 127 of an int8 code (255 entries), or the E5M2
+        // code itself (256)
+        constexpr int kBias = kMode == kModeF8 ? 0 : 127;
+        for (int i = lane; i < 256 - (kBias ? 1 : 0); i += kWave)
+            tab[i] = dequant_row<kMode>(i - kBias, sc, zr);
         const int8_t *cbr = CB + r * K;
         for (int64_t j0 = 8 * lane; j0 < ldo; j0 += 8 * kWave) {
             const int4 o0 = *reinterpret_cast<const int4 *>(O + j0);
@@ -447,13 +514,13 @@ __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int cb = (int)(int8_t)(((e < 4 ? raw.x : raw.y) >> (8 * (e & 3))) & 0xffu);
-                    h[e] = tab[(cb + 127) & 255];
+                    h[e] = tab[(cb + kBias) & 255];
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int oc = j0 + e < n ? o[e] : 0;
-                    const unsigned v = tab[(cbr[oc] + 127) & 255];
+                    const unsigned v = tab[(cbr[oc] + kBias) & 255];
                     h[e] = j0 + e < n ? v : 0u;
                 }
             }
@@ -464,7 +531,7 @@ __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
     }
 }
 
-template <int NC>
+template <int NC, bool kF8 = false>
 __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict__ X, int64_t T,
                                                      int64_t K, const uint8_t *__restrict__ mask,
                                                      const int32_t *__restrict__ chunk_pre,
@@ -481,7 +548,8 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     __shared__ uint16_t s_tab[kWavesPerBlock][256];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     if ((int64_t)blockIdx.x >= T) {
-        gather_w_out(blockIdx.x - T, gridDim.x - T, K, n_out, CB, SCB, O, N, w_out, s_tab[wave]);
+        gather_w_out<kF8 ? kModeF8 : kModeAbsmax>(blockIdx.x - T, gridDim.x - T, K, n_out, CB, SCB,
+                                                  O, N, w_out, s_tab[wave]);
         return;
     }
     const int64_t t = blockIdx.x;
@@ -521,19 +589,22 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     for (int w = 0; w < kWavesPerBlock; ++w)
         m = umax(m, s_max[w]);
     const float amax = h2f((uint16_t)m);
-    const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
+    const float r = kF8 ? 0.0f : amax > 0.0f ? 127.0f / amax : 0.0f;
+    const int e8 = kF8 ? f8_scale_exp(amax) : 0;
+    const float sc = kF8 ? __builtin_ldexpf(1.0f, e8) : 0.0f;
     if constexpr (NC > 0) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             const int64_t c = tid + (int64_t)i * kBlock;
             if (c < nchunk)
-                quant_chunk(v[i], fl[i], amax, r, pre[i], xrow, xq_chunk(Xq, t, K, c, packed));
+                quant_chunk<kF8>(v[i], fl[i], amax, r, pre[i], xrow,
+                                 xq_chunk(Xq, t, K, c, packed), sc);
         }
     } else {
         for (int64_t c = tid; c < nchunk; c += kBlock) {
             const unsigned f = mask[c];
-            quant_chunk(xr[c], f, amax, r, (xrow && f != 0u) ? chunk_pre[c] : 0, xrow,
-                        xq_chunk(Xq, t, K, c, packed));
+            quant_chunk<kF8>(xr[c], f, amax, r, (xrow && f != 0u) ? chunk_pre[c] : 0, xrow,
+                             xq_chunk(Xq, t, K, c, packed), sc);
         }
     }
     if (x_out) {
@@ -541,7 +612,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
             x_out[t * ldo + j] = 0;
     }
     if (tid == 0)
-        a[t] = amax;
+        a[t] = kF8 ? __builtin_ldexpf(1.0f, -e8) : amax;
 }
 
 // ---------------------------------------------------------------------------
@@ -570,7 +641,7 @@ __device__ __forceinline__ void step_prefix(unsigned fl, uint64_t below, int &pr
     }
 }
 
-template <int NC>
+template <int NC, bool kF8 = false>
 __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restrict__ X, int64_t T,
                                                        int64_t K, const uint8_t *__restrict__ mask,
                                                        const int32_t *__restrict__ n_out,
@@ -586,8 +657,8 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restric
     __shared__ uint16_t s_tab[kWavesPerBlock][256];
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     if ((int64_t)blockIdx.x >= row_blocks) {
-        gather_w_out(blockIdx.x - row_blocks, gridDim.x - row_blocks, K, n_out, CB, SCB, O, N,
-                     w_out, s_tab[wave]);
+        gather_w_out<kF8 ? kModeF8 : kModeAbsmax>(blockIdx.x - row_blocks, gridDim.x - row_blocks,
+                                                  K, n_out, CB, SCB, O, N, w_out, s_tab[wave]);
         return;
     }
     const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -631,19 +702,21 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restric
     }
     m = wave_max_u32(m);
     const float amax = h2f((uint16_t)m);
-    const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
+    const float r = kF8 ? 0.0f : amax > 0.0f ? 127.0f / amax : 0.0f;
+    const int e8 = kF8 ? f8_scale_exp(amax) : 0;
+    const float sc = kF8 ? __builtin_ldexpf(1.0f, e8) : 0.0f;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int64_t c = lane + (int64_t)i * kWave;
         if (c < nchunk)
-            qr[c] = quant8(v[i], amax, r);
+            qr[c] = quant8_mode<kF8>(v[i], amax, r, sc);
     }
     if (xrow) {
         for (int64_t j = nout + lane; j < ldo; j += kWave)
             xrow[j] = 0;
     }
     if (lane == 0)
-        a[t] = amax;
+        a[t] = kF8 ? __builtin_ldexpf(1.0f, -e8) : amax;
 }
 
 // ---------------------------------------------------------------------------
@@ -742,10 +815,11 @@ __device__ __forceinline__ uint2 quant8_zp(uint4 v, float nd, float zpf, int &su
 constexpr int kSmallThreads = 512;
 constexpr int kSmallMaxChunks = 16 * kSmallThreads;   // G <= 16: K <= 65536
 
-// kZp: the zero-point variant (a receives nd, row_zp {zp, code sum}): the
-// range instead of the absmax in step 3, codes by quant8_zp, and one more
-// block reduction for the code sum.
-template <int G, bool kZp = false>
+// kMode kModeZp, the zero-point variant (a receives nd, row_zp {zp, code
+// sum}): the range instead of the absmax in step 3, codes by quant8_zp, and
+// one more block reduction for the code sum.  kModeF8, the FP8 variant: the
+// absmax sets the power-of-two scale, codes by quant8_f8, a receives 2^-e.
+template <int G, int kMode = kModeAbsmax>
 __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
     const uint16_t *__restrict__ X, int T, int K, unsigned thr_bits, int8_t *__restrict__ Xq,
     float *__restrict__ a, int32_t *__restrict__ O, int32_t *__restrict__ n_out,
@@ -755,7 +829,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
     __shared__ uint8_t s_flags[kSmallMaxChunks];
     __shared__ int s_pre[kSmallMaxChunks];
     __shared__ unsigned s_wmax[kSmallThreads / kWave];
-    __shared__ float s_wmn[kZp ? kSmallThreads / kWave : 1];
+    __shared__ float s_wmn[kMode == kModeZp ? kSmallThreads / kWave : 1];
     __shared__ int s_wave_tot[kSmallThreads / kWave];
     __shared__ int s_n;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -816,7 +890,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
     if (lane == kWave - 1)
         s_wave_tot[wave] = inc;
     // row t's absmax (zero-point: range) over the non-outlier columns
-    if constexpr (kZp) {
+    if constexpr (kMode == kModeZp) {
         float mn = 0.0f, mx = 0.0f;
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -857,7 +931,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
     }
     float amax = 0.0f, r127 = 0.0f, zpf = 0.0f;
     ZpParams p{0.0f, 0};
-    if constexpr (kZp) {
+    if constexpr (kMode == kModeZp) {
         float mn = 0.0f, mx = 0.0f;
 #pragma unroll
         for (int w = 0; w < kSmallThreads / kWave; ++w) {
@@ -872,9 +946,16 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
         for (int w = 0; w < kSmallThreads / kWave; ++w)
             amax_bits = umax(amax_bits, s_wmax[w]);
         amax = h2f((uint16_t)amax_bits);
-        r127 = amax > 0.0f ? 127.0f / amax : 0.0f;
-        if (tid == 0)
-            a[t] = amax;
+        if constexpr (kMode == kModeF8) {
+            const int e8 = f8_scale_exp(amax);
+            zpf = __builtin_ldexpf(1.0f, e8);   // the FP8 scale 2^e
+            if (tid == 0)
+                a[t] = __builtin_ldexpf(1.0f, -e8);
+        } else {
+            r127 = amax > 0.0f ? 127.0f / amax : 0.0f;
+            if (tid == 0)
+                a[t] = amax;
+        }
     }
     __syncthreads();
 
@@ -894,14 +975,20 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
                 scatter_outliers(x, f, s_pre[c], x_out + t * ldo);
             x = drop_flagged(x, f);
         }
-        const uint2 q = kZp ? quant8_zp(x, p.nd, zpf, sum) : quant8(x, amax, r127);
+        uint2 q;
+        if constexpr (kMode == kModeZp)
+            q = quant8_zp(x, p.nd, zpf, sum);
+        else if constexpr (kMode == kModeF8)
+            q = quant8_f8(x, zpf);
+        else
+            q = quant8(x, amax, r127);
         *xq_chunk(Xq, t, K, c, packed) = q;
     }
     if (x_out) {
         for (int64_t idx = n + tid; idx < ldo; idx += kSmallThreads)
             x_out[t * ldo + idx] = 0;
     }
-    if constexpr (kZp) {
+    if constexpr (kMode == kModeZp) {
         // the code sum of row t (s_wave_tot is free again: read before the
         // last barrier)
         sum = wave_sum(sum);
@@ -972,8 +1059,8 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_zp(
     __shared__ uint16_t s_tab[kWavesPerBlock][256];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     if ((int64_t)blockIdx.x >= T) {
-        gather_w_out<true>(blockIdx.x - T, gridDim.x - T, K, n_out, CB, NDw, O, N, w_out,
-                           s_tab[wave], ZPw);
+        gather_w_out<kModeZp>(blockIdx.x - T, gridDim.x - T, K, n_out, CB, NDw, O, N, w_out,
+                              s_tab[wave], ZPw);
         return;
     }
     const int64_t t = blockIdx.x;
@@ -1113,7 +1200,7 @@ hipError_t launch_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K, float
         const unsigned tb = threshold_bits(threshold);
         const dim3 grid((unsigned)T);
 #define LLMINT8_QROWS_ZP(G)                                                                    \
-    hipLaunchKernelGGL((k_quant_rows<G, true>), grid, dim3(kSmallThreads), 0, s, X, (int)T,    \
+    hipLaunchKernelGGL((k_quant_rows<G, kModeZp>), grid, dim3(kSmallThreads), 0, s, X, (int)T,    \
                        (int)K, tb, Xq, nd, O, n_out, x_out, xq_packed, row_zp)
         if (per <= 1)
             LLMINT8_QROWS_ZP(1);
@@ -1197,11 +1284,14 @@ hipError_t launch_quantize_act_rows(const uint16_t *X, int64_t T, int64_t K, flo
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
-                               int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
-                               uint8_t *partial, uint8_t *mask, int32_t *chunk_pre,
-                               uint16_t *x_out, const GatherArgs &g, bool xq_packed,
-                               hipStream_t s)
+namespace {
+// Detection, compaction and the row quantization of the absmax kernels
+// (kF8: their FP8 mode).
+template <bool kF8>
+hipError_t launch_act_absmax(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                             int8_t *Xq, float *a, int32_t *O, int32_t *n_out, uint8_t *partial,
+                             uint8_t *mask, int32_t *chunk_pre, uint16_t *x_out,
+                             const GatherArgs &g, bool xq_packed, hipStream_t s)
 {
     if (xq_packed && T > 16)
         return hipErrorInvalidValue;
@@ -1226,7 +1316,8 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
         const int64_t row_blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
         const dim3 grid((unsigned)(row_blocks + gather_blocks));
 #define LLMINT8_ROWQUANT_W(NCV)                                                                  \
-    hipLaunchKernelGGL(k_rowquant_w<NCV>, grid, dim3(kBlock), 0, s, X, T, K, mask, n_out, Xq, a, \
+    hipLaunchKernelGGL((k_rowquant_w<NCV, kF8>), grid, dim3(kBlock), 0, s, X, T, K, mask, n_out, \
+                       Xq, a,                                                            \
                        x_out, g.CB, g.SCB, O, g.N, g.w_out, row_blocks)
         static_assert(kRowQuantWaveMaxK / 8 <= 8 * kWave, "rows of at most 8 chunks per lane");
         if (per <= 2)
@@ -1242,7 +1333,8 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
     const dim3 grid((unsigned)(T + gather_blocks));
     const int64_t chunks_per_thread = (nchunk + kBlock - 1) / kBlock;
 #define LLMINT8_ROWQUANT(NCV)                                                                   \
-    hipLaunchKernelGGL(k_rowquant<NCV>, grid, dim3(kBlock), 0, s, X, T, K, mask, chunk_pre, n_out, \
+    hipLaunchKernelGGL((k_rowquant<NCV, kF8>), grid, dim3(kBlock), 0, s, X, T, K, mask, chunk_pre, \
+                       n_out,                                                           \
                        Xq, a, x_out, g.CB, g.SCB, O, g.N, g.w_out, xq_packed)
     if (chunks_per_thread <= 1)
         LLMINT8_ROWQUANT(1);
@@ -1258,6 +1350,62 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
         LLMINT8_ROWQUANT(0);
 #undef LLMINT8_ROWQUANT
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                               int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
+                               uint8_t *partial, uint8_t *mask, int32_t *chunk_pre,
+                               uint16_t *x_out, const GatherArgs &g, bool xq_packed,
+                               hipStream_t s)
+{
+    return launch_act_absmax<false>(X, T, K, threshold, Xq, a, O, n_out, partial, mask, chunk_pre,
+                                    x_out, g, xq_packed, s);
+}
+
+hipError_t launch_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N, uint8_t *CB8,
+                                     float *SC8, hipStream_t s)
+{
+    const int64_t blocks = (N + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(k_quantize_weight_f8, dim3((unsigned)blocks), dim3(kBlock), 0, s, W_t, K,
+                       N, CB8, SC8);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                                  uint8_t *Xq8, float *sc, int32_t *O, int32_t *n_out,
+                                  uint8_t *partial, uint8_t *mask, int32_t *chunk_pre,
+                                  uint16_t *x_out, const GatherArgs &g, bool xq_packed,
+                                  hipStream_t s)
+{
+    if (g.w_out && !g.f8)
+        return hipErrorInvalidValue;
+    int8_t *Xq = reinterpret_cast<int8_t *>(Xq8);
+    if (!g.w_out && quantize_act_fits_rows(T, K)) {
+        // few rows: one launch (k_quant_rows in its FP8 mode)
+        const int64_t per = (K / 8 + kSmallThreads - 1) / kSmallThreads;
+        const unsigned tb = threshold_bits(threshold);
+        const dim3 grid((unsigned)T);
+#define LLMINT8_QROWS_F8(G)                                                                    \
+    hipLaunchKernelGGL((k_quant_rows<G, kModeF8>), grid, dim3(kSmallThreads), 0, s, X, (int)T, \
+                       (int)K, tb, Xq, sc, O, n_out, x_out, xq_packed, nullptr)
+        if (per <= 1)
+            LLMINT8_QROWS_F8(1);
+        else if (per <= 2)
+            LLMINT8_QROWS_F8(2);
+        else if (per <= 4)
+            LLMINT8_QROWS_F8(4);
+        else if (per <= 8)
+            LLMINT8_QROWS_F8(8);
+        else if (per <= 16)
+            LLMINT8_QROWS_F8(16);
+        else
+            return hipErrorInvalidValue;
+#undef LLMINT8_QROWS_F8
+        return hipGetLastError();
+    }
+    return launch_act_absmax<true>(X, T, K, threshold, Xq, sc, O, n_out, partial, mask, chunk_pre,
+                                   x_out, g, xq_packed, s);
 }
 
 }  // namespace llmint8

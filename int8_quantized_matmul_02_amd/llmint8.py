@@ -33,6 +33,10 @@ EXPORTS = (
     "llmint8_quantize_act_zp",
     "llmint8_matmul_zp",
     "llmint8_matmul_zp_path",
+    "llmint8_quantize_weight_f8",
+    "llmint8_quantize_act_f8",
+    "llmint8_matmul_f8",
+    "llmint8_matmul_f8_path",
 )
 
 
@@ -73,10 +77,15 @@ def _load():
     lib.llmint8_matmul_zp.argtypes = [P, I64, I64, I64, P, P, P, P, P, F, P, P, SZ, P]
     lib.llmint8_matmul_zp_path.argtypes = [P, I64, I64, I64, P, P, P, P, P, F, P, P, SZ, I, P,
                                            P, P]
+    lib.llmint8_quantize_weight_f8.argtypes = [P, I64, I64, P, P, P]
+    lib.llmint8_quantize_act_f8.argtypes = [P, I64, I64, F, P, P, P, P, P, SZ, P]
+    lib.llmint8_matmul_f8.argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ, P]
+    lib.llmint8_matmul_f8_path.argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ, I, P, P, P]
     for fn in ("llmint8_quantize_weight", "llmint8_quantize_act", "llmint8_matmul",
                "llmint8_matmul_act", "llmint8_matmul_path", "llmint8_igemm_i32",
                "llmint8_quantize_weight_zp", "llmint8_quantize_act_zp", "llmint8_matmul_zp",
-               "llmint8_matmul_zp_path"):
+               "llmint8_matmul_zp_path", "llmint8_quantize_weight_f8", "llmint8_quantize_act_f8",
+               "llmint8_matmul_f8", "llmint8_matmul_f8_path"):
         getattr(lib, fn).restype = I
     _lib = lib
     return lib
@@ -347,4 +356,91 @@ def llmint8_matmul_zp(X, CB, ND, ZP, RS, threshold=6.0, bias=None, out=None, ws=
                                  RS.data_ptr(), bias.data_ptr() if bias is not None else None,
                                  float(threshold), out.data_ptr(), ws.data_ptr(),
                                  ws.numel() * ws.element_size(), _stream(X)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E5M2) variant.
+# ---------------------------------------------------------------------------
+def llmint8_quantize_weight_f8(W_t, CB8=None, SC8=None):
+    """W_t: fp16 [N,K].  Returns (CB8 uint8 [N,K] E5M2 codes, SC8 f32 [N] scales 2^-e)."""
+    lib = _load()
+    _dev(W_t, "W_t", _H)
+    N, K = W_t.shape
+    d = W_t.device
+    CB8 = torch.empty((N, K), dtype=torch.uint8, device=d) if CB8 is None else _dev(CB8, "CB8", (torch.uint8,))
+    SC8 = torch.empty((N,), dtype=torch.float32, device=d) if SC8 is None else _dev(SC8, "SC8", (torch.float32,))
+    _check("llmint8_quantize_weight_f8",
+           lib.llmint8_quantize_weight_f8(W_t.data_ptr(), K, N, CB8.data_ptr(), SC8.data_ptr(),
+                                          _stream(W_t)))
+    return CB8, SC8
+
+
+def llmint8_quantize_act_f8(X, threshold=6.0, Xq8=None, row_scale=None, outlier_idx=None,
+                            n_outliers=None, ws=None):
+    """X: fp16 [T,K].  Returns (Xq8 uint8 [T,K], row_scale f32 [T], outlier_idx int32 [K],
+    n_outliers int32 [1])."""
+    lib = _load()
+    _dev(X, "X", _H)
+    T, K = X.shape
+    d = X.device
+    Xq8 = torch.empty((T, K), dtype=torch.uint8, device=d) if Xq8 is None else _dev(Xq8, "Xq8", (torch.uint8,))
+    row_scale = torch.empty((T,), dtype=torch.float32, device=d) if row_scale is None else row_scale
+    outlier_idx = torch.empty((K,), dtype=torch.int32, device=d) if outlier_idx is None else outlier_idx
+    n_outliers = torch.empty((1,), dtype=torch.int32, device=d) if n_outliers is None else n_outliers
+    need = llmint8_quantize_act_workspace_bytes(K)
+    ws = torch.empty((need,), dtype=torch.uint8, device=d) if ws is None else ws
+    _check("llmint8_quantize_act_f8",
+           lib.llmint8_quantize_act_f8(X.data_ptr(), T, K, float(threshold), Xq8.data_ptr(),
+                                       row_scale.data_ptr(), outlier_idx.data_ptr(),
+                                       n_outliers.data_ptr(), ws.data_ptr(),
+                                       ws.numel() * ws.element_size(), _stream(X)))
+    return Xq8, row_scale, outlier_idx, n_outliers
+
+
+def _f8_operands(X, CB8, SC8, bias, out, ws):
+    _dev(X, "X", _H)
+    _dev(CB8, "CB8", (torch.uint8,))
+    _dev(SC8, "SC8", (torch.float32,))
+    T, K = X.shape
+    N = CB8.shape[0]
+    if CB8.shape[1] != K or SC8.shape != (N,):
+        raise ValueError("shape mismatch: X %s, CB8 %s, SC8 %s"
+                         % (tuple(X.shape), tuple(CB8.shape), tuple(SC8.shape)))
+    if bias is not None:
+        _dev(bias, "bias", _H)
+        if bias.shape != (N,):
+            raise ValueError("bias must have shape (%d,)" % N)
+    out = torch.empty((T, N), dtype=torch.float16, device=X.device) if out is None else _dev(out, "out", _H)
+    if ws is None:
+        ws = torch.empty((llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=X.device)
+    return T, K, N, out, ws
+
+
+def llmint8_matmul_f8_path(X, CB8, SC8, threshold=6.0, bias=None, out=None, ws=None,
+                           path=PATH_AUTO, main_start=None, main_stop=None):
+    """The FP8 decomposition: X fp16 [T,K] with the output of
+    llmint8_quantize_weight_f8 -> out fp16 [T,N]; path / events as llmint8_matmul_path."""
+    lib = _load()
+    T, K, N, out, ws = _f8_operands(X, CB8, SC8, bias, out, ws)
+    _check("llmint8_matmul_f8_path",
+           lib.llmint8_matmul_f8_path(X.data_ptr(), T, K, N, CB8.data_ptr(), SC8.data_ptr(),
+                                      bias.data_ptr() if bias is not None else None,
+                                      float(threshold), out.data_ptr(), ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), int(path),
+                                      ctypes.c_void_p(main_start) if main_start else None,
+                                      ctypes.c_void_p(main_stop) if main_stop else None,
+                                      _stream(X)))
+    return out
+
+
+def llmint8_matmul_f8(X, CB8, SC8, threshold=6.0, bias=None, out=None, ws=None):
+    """The FP8 decomposition (automatic kernel choice)."""
+    lib = _load()
+    T, K, N, out, ws = _f8_operands(X, CB8, SC8, bias, out, ws)
+    _check("llmint8_matmul_f8",
+           lib.llmint8_matmul_f8(X.data_ptr(), T, K, N, CB8.data_ptr(), SC8.data_ptr(),
+                                 bias.data_ptr() if bias is not None else None, float(threshold),
+                                 out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                 _stream(X)))
     return out

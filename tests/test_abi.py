@@ -145,3 +145,25 @@ def test_zero_point_entry_points_validate(lib):
     assert lib.llmint8_matmul_zp(P, 4, 64, 64, P, P, P, P, None, float("nan"), P, P, 1 << 30,
                                  None) == 1
     assert lib.llmint8_matmul_zp(P, 4, 64, 64, P, P, P, P, None, 6.0, P, P, 16, None) == 3
+
+
+def test_fp8_entry_points_validate(lib):
+    assert lib.llmint8_quantize_weight_f8(P, 64, 64, P, None, None) == 1
+    assert lib.llmint8_quantize_weight_f8(P, 100, 64, P, P, None) == 2
+    assert lib.llmint8_quantize_act_f8(P, 4, 64, float("nan"), P, P, P, P, P, 1 << 30, None) == 1
+    assert lib.llmint8_quantize_act_f8(P, 4, 72, 6.0, P, P, P, P, P, 1 << 30, None) == 2
+    assert lib.llmint8_quantize_act_f8(P, 4, 64, 6.0, P, P, P, P, P, 10, None) == 3
+
+    def mm(X=P, T=8, K=64, N=64, SC8=P, thr=6.0, wsb=1 << 40, path=0):
+        return lib.llmint8_matmul_f8_path(X, T, K, N, P, SC8, None, thr, P, P, wsb, path, None,
+                                          None, None)
+    assert mm(X=None) == 1
+    assert mm(SC8=P + 4) == 1                   # misaligned
+    assert mm(thr=-1.0) == 1
+    assert mm(path=3) == 1
+    assert mm(K=96) == 2
+    assert mm(K=133184) == 2
+    assert mm(T=17, path=2) == 2
+    assert mm(wsb=L.llmint8_workspace_bytes(8, 64, 64) - 1) == 3
+    assert lib.llmint8_matmul_f8(P, 4, 64, 64, P, P, None, float("nan"), P, P, 1 << 30, None) == 1
+    assert lib.llmint8_matmul_f8(P, 4, 64, 64, P, P, None, 6.0, P, P, 16, None) == 3
