@@ -13,7 +13,10 @@ the fp16 weight stays the parameter and is quantized again on every call
 Everything computed runs in libllmint8's HIP kernels: weight quantization
 (llmint8_quantize_weight), the whole decomposition (llmint8_matmul_act), and
 an optional ReLU fused into its output rounding for the feed-forward
-expansion layers.  This module only holds the tensors, flattens leading
+expansion layers.  `quant` selects the 8-bit part's quantizer: "absmax" (the
+method's vector-wise absmax int8), or the library's two variants,
+"zeropoint" (asymmetric int8, llmint8_matmul_zp) and "fp8" (E5M2,
+llmint8_matmul_f8); the variants have no fused activation.  This module only holds the tensors, flattens leading
 dimensions into rows, and keeps one workspace buffer per device, grown as
 needed, so that steady-state calls allocate nothing but their output.
 """
@@ -22,6 +25,7 @@ import torch
 from . import llmint8 as L
 
 _ACTS = {None: L.ACT_NONE, "none": L.ACT_NONE, "relu": L.ACT_RELU}
+_QUANTS = ("absmax", "zeropoint", "fp8")
 
 
 class Linear8bitLt(torch.nn.Module):
@@ -33,8 +37,14 @@ class Linear8bitLt(torch.nn.Module):
     """
 
     def __init__(self, in_features, out_features, bias=True, has_fp16_weights=False,
-                 threshold=6.0, activation=None, device=None):
+                 threshold=6.0, activation=None, device=None, quant="absmax"):
         super().__init__()
+        if quant not in _QUANTS:
+            raise ValueError("quant must be one of %s, got %r" % (_QUANTS, quant))
+        if quant != "absmax" and _ACTS.get(activation, None) not in (L.ACT_NONE,):
+            raise ValueError("the %s variant has no fused activation" % quant)
+        if quant == "zeropoint" and in_features > 33286:
+            raise ValueError("in_features must be at most 33286 for the zero-point variant")
         if in_features % 64 or out_features % 64 or in_features <= 0 or out_features <= 0:
             raise ValueError("in_features and out_features must be positive multiples of 64, "
                              "got %d and %d" % (in_features, out_features))
@@ -49,6 +59,7 @@ class Linear8bitLt(torch.nn.Module):
         self.has_fp16_weights = has_fp16_weights
         self.threshold = float(threshold)
         self.activation = activation
+        self.quant = quant
         self.weight = torch.nn.Parameter(
             torch.empty((out_features, in_features), dtype=torch.float16, device=device),
             requires_grad=False)
@@ -59,18 +70,21 @@ class Linear8bitLt(torch.nn.Module):
                 requires_grad=False)
         else:
             self.register_parameter("bias", None)
-        self.register_buffer("CB", None)
-        self.register_buffer("SCB", None)
+        self.register_buffer("CB", None)    # int8 codes (fp8: E5M2 codes, uint8)
+        self.register_buffer("SCB", None)   # absmax: column absmax; zero-point: nd; fp8: 2^-e
+        self.register_buffer("ZP", None)    # zero-point variant: zero points and code sums
+        self.register_buffer("RS", None)
         self._ws = {}
 
     @classmethod
-    def from_linear(cls, linear, has_fp16_weights=False, threshold=6.0, activation=None):
+    def from_linear(cls, linear, has_fp16_weights=False, threshold=6.0, activation=None,
+                    quant="absmax"):
         """A Linear8bitLt holding torch.nn.Linear `linear`'s weight and bias
         (cast to fp16); quantized on the first forward call, or by
         quantize_()."""
         m = cls(linear.in_features, linear.out_features, bias=linear.bias is not None,
                 has_fp16_weights=has_fp16_weights, threshold=threshold, activation=activation,
-                device=linear.weight.device)
+                device=linear.weight.device, quant=quant)
         with torch.no_grad():
             m.weight.copy_(linear.weight.to(torch.float16))
             if linear.bias is not None:
@@ -87,10 +101,18 @@ class Linear8bitLt(torch.nn.Module):
             raise RuntimeError("Linear8bitLt: move the module to a HIP device before quantizing")
         w = self.weight.detach().contiguous()
         if self.CB is None or self.CB.device != w.device:
-            self.CB = torch.empty((self.out_features, self.in_features), dtype=torch.int8,
-                                  device=w.device)
+            dt = torch.uint8 if self.quant == "fp8" else torch.int8
+            self.CB = torch.empty((self.out_features, self.in_features), dtype=dt, device=w.device)
             self.SCB = torch.empty((self.out_features,), dtype=torch.float32, device=w.device)
-        L.llmint8_quantize_weight(w, CB=self.CB, SCB=self.SCB)
+            if self.quant == "zeropoint":
+                self.ZP = torch.empty((self.out_features,), dtype=torch.int32, device=w.device)
+                self.RS = torch.empty((self.out_features,), dtype=torch.int32, device=w.device)
+        if self.quant == "zeropoint":
+            L.llmint8_quantize_weight_zp(w, CB=self.CB, ND=self.SCB, ZP=self.ZP, RS=self.RS)
+        elif self.quant == "fp8":
+            L.llmint8_quantize_weight_f8(w, CB8=self.CB, SC8=self.SCB)
+        else:
+            L.llmint8_quantize_weight(w, CB=self.CB, SCB=self.SCB)
         if not self.has_fp16_weights:
             self.weight = None
         return self
@@ -116,12 +138,19 @@ class Linear8bitLt(torch.nn.Module):
         T = x2.shape[0]
         if T == 0:
             return x.new_empty(lead + (self.out_features,))
-        out = L.llmint8_matmul_act(x2, self.CB, self.SCB, self.threshold,
-                                   _ACTS[self.activation], bias=self.bias,
-                                   ws=self._workspace(T, x2.device))
+        ws = self._workspace(T, x2.device)
+        if self.quant == "zeropoint":
+            out = L.llmint8_matmul_zp(x2, self.CB, self.SCB, self.ZP, self.RS, self.threshold,
+                                      bias=self.bias, ws=ws)
+        elif self.quant == "fp8":
+            out = L.llmint8_matmul_f8(x2, self.CB, self.SCB, self.threshold, bias=self.bias, ws=ws)
+        else:
+            out = L.llmint8_matmul_act(x2, self.CB, self.SCB, self.threshold,
+                                       _ACTS[self.activation], bias=self.bias, ws=ws)
         return out.reshape(lead + (self.out_features,))
 
     def extra_repr(self):
         return ("in_features=%d, out_features=%d, bias=%s, has_fp16_weights=%s, threshold=%g, "
-                "activation=%s" % (self.in_features, self.out_features, self.bias is not None,
-                                   self.has_fp16_weights, self.threshold, self.activation))
+                "activation=%s, quant=%s" % (self.in_features, self.out_features,
+                                             self.bias is not None, self.has_fp16_weights,
+                                             self.threshold, self.activation, self.quant))

@@ -28,6 +28,16 @@ def test_rejects_unsupported_shapes_and_options():
     assert "has_fp16_weights=False" in repr(m)
 
 
+def test_variant_options():
+    with pytest.raises(ValueError):
+        Linear8bitLt(64, 64, quant="int4")
+    with pytest.raises(ValueError):
+        Linear8bitLt(64, 64, quant="fp8", activation="relu")
+    with pytest.raises(ValueError):
+        Linear8bitLt(33344, 64, quant="zeropoint")
+    assert "quant=fp8" in repr(Linear8bitLt(64, 64, quant="fp8"))
+
+
 def test_quantize_needs_a_device():
     m = Linear8bitLt(64, 64)
     with pytest.raises(RuntimeError):
@@ -149,3 +159,40 @@ def test_ffn_pair_chained_through_two_modules():
     C2, S2 = oracle.quantize_weight(W2)
     ref2, _, _ = oracle.matmul(h_np, C2, S2, 6.0)
     _close(y.cpu().numpy().view(np.uint16), ref2, "fc2 on fc1's output")
+
+
+@gpu
+@pytest.mark.parametrize("quant", ["zeropoint", "fp8"])
+@pytest.mark.parametrize("T", [4, 100])
+def test_variant_modules_match_their_oracles(quant, T):
+    # the module's weight buffers and output against the variant's oracle,
+    # for both kernels (T = 4: weight streaming, T = 100: tiled GEMM)
+    K, N = 320, 256
+    X, W_t, _ = workloads.case(T, K, N, n_dims=3, lo=8, hi=30, p=0.3, seed=T + 41)
+    X = (X.astype(np.float32) + 0.25).astype(np.float16)          # skewed rows
+    rng = np.random.default_rng(T)
+    bias = (rng.standard_normal(N) * 0.3).astype(np.float16)
+    lin = torch.nn.Linear(K, N, bias=True)
+    with torch.no_grad():
+        lin.weight.copy_(torch.from_numpy(W_t.astype(np.float32)))
+        lin.bias.copy_(torch.from_numpy(bias.astype(np.float32)))
+    m = Linear8bitLt.from_linear(lin.to("cuda"), quant=quant)
+    y = m(torch.from_numpy(X).cuda())
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    if quant == "zeropoint":
+        CB, ND, ZP = oracle.quantize_weight_zp(W_t)
+        assert np.array_equal(m.CB.cpu().numpy(), CB) and np.array_equal(m.ZP.cpu().numpy(), ZP)
+        ref, _, _, _ = oracle.matmul_zp(X, CB, ND, ZP, 6.0, bias=bias)
+        g, r = got.astype(np.float64), ref.view(np.float16).astype(np.float64)
+        assert np.all(np.abs(g - r) <= 1e-3 + 2e-3 * np.abs(r))
+    else:
+        CB8, SC8 = oracle.quantize_weight_f8(W_t)
+        assert np.array_equal(m.CB.cpu().numpy(), CB8) and np.array_equal(m.SCB.cpu().numpy(), SC8)
+        ref, O, sc = oracle.matmul_f8(X, CB8, SC8, 6.0, bias=bias)
+        Xq8, _ = oracle.quantize_rows_f8(X, O)
+        S = (np.abs(oracle.e5m2_to_double(Xq8)) * sc.astype(np.float64)[:, None]) @ (
+            np.abs(oracle.e5m2_to_double(CB8)) * SC8.astype(np.float64)[:, None]).T
+        g, r = got.astype(np.float64), ref.view(np.float16).astype(np.float64)
+        # the FP8 accumulation term of tests/test_gpu_fp8.py
+        assert np.all(np.abs(g - r) <= 1e-3 + 2e-3 * np.abs(r) + 2.0 ** -13 * S)
