@@ -1,4 +1,4 @@
-"""llmint8_matmul under HIP graph capture.
+"""llmint8_matmul (and the zero-point and FP8 variants) under HIP graph capture.
 
 A call enqueues kernels only (no memset, no event, no allocation or host
 synchronization once out and ws are given), so a caller can capture it.  Each
@@ -20,23 +20,38 @@ from tests.gpu_helpers import dev, h2d, say
 @pytest.mark.parametrize("T,K,N", [(1, 1024, 512), (4, 2048, 256), (16, 1088, 320),
                                    (300, 512, 512)])
 @pytest.mark.parametrize("thr", [6.0, 0.0])
-def test_matmul_graph_replay(T, K, N, thr):
-    say("graph replay T=%d K=%d N=%d thr=%s" % (T, K, N, thr))
+@pytest.mark.parametrize("variant", ["absmax", "zeropoint", "fp8"])
+def test_matmul_graph_replay(T, K, N, thr, variant):
+    say("graph replay %s T=%d K=%d N=%d thr=%s" % (variant, T, K, N, thr))
     d = dev()
     X, W_t, _ = workloads.case(T, K, N, n_dims=min(6, K // 16), lo=8, hi=60, p=0.5,
                                seed=11 * T + K + N)
     X2, _, _ = workloads.case(T, K, N, n_dims=min(6, K // 16), lo=8, hi=60, p=0.5,
                               seed=11 * T + K + N + 1)
-    CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
     bias = h2d(np.random.default_rng(5).standard_normal(N).astype(np.float16))
     Xd = h2d(X)
     out = torch.empty((T, N), dtype=torch.float16, device=d)
     ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=d)
+    if variant == "zeropoint":
+        CB, ND, ZP, RS = L.llmint8_quantize_weight_zp(h2d(W_t))
+
+        def call(x, o, w):
+            L.llmint8_matmul_zp(x, CB, ND, ZP, RS, thr, bias=bias, out=o, ws=w)
+    elif variant == "fp8":
+        CB8, SC8 = L.llmint8_quantize_weight_f8(h2d(W_t))
+
+        def call(x, o, w):
+            L.llmint8_matmul_f8(x, CB8, SC8, thr, bias=bias, out=o, ws=w)
+    else:
+        CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
+
+        def call(x, o, w):
+            L.llmint8_matmul(x, CB, SCB, thr, bias=bias, out=o, ws=w)
 
     def eager(x):
         o = torch.empty((T, N), dtype=torch.float16, device=d)
         w = torch.empty_like(ws)
-        L.llmint8_matmul(x, CB, SCB, thr, bias=bias, out=o, ws=w)
+        call(x, o, w)
         torch.cuda.synchronize()
         return o
 
@@ -47,12 +62,12 @@ def test_matmul_graph_replay(T, K, N, thr):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        L.llmint8_matmul(Xd, CB, SCB, thr, bias=bias, out=out, ws=ws)
+        call(Xd, out, ws)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        L.llmint8_matmul(Xd, CB, SCB, thr, bias=bias, out=out, ws=ws)
+        call(Xd, out, ws)
     torch.cuda.synchronize()
 
     for rep in range(3):
