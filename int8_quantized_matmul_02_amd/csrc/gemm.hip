@@ -10,12 +10,25 @@ namespace llmint8 {
 // four stages of 64 bytes; 128 KB of LDS either way.  The fp16 pass over
 // more than 32 outlier columns (rows padded to 128 bytes) runs through the
 // same ring.
+//
+// Up to K = 6144 the int8 output kernel runs with 2 x 4 wavefronts of
+// 128 x 64 instead (two per SIMD, so one issues MFMAs while the other waits
+// at a barrier or on LDS; 50 % more fragment reads per MFMA).  Measured on
+// MI355X: 242 -> 236 us at 4096 x 4096 x 16384 and 41.8 -> 40.3 us at
+// 2048 x 2048 x 8192, but 471 -> 488 us at K = 12288, where the longer main
+// loop gains less from the second wavefront than the extra LDS traffic
+// costs.  The zero-point and FP8 epilogues spill in that shape and keep four
+// wavefronts, as does the many-outlier kernel.
 using Gemm128 = gemm::Cfg<256, 256, 2, 2, 2, 4, 128>;
+using Gemm128W8 = gemm::Cfg<256, 256, 2, 4, 2, 4, 128>;
 using Gemm64 = gemm::Cfg<256, 256, 2, 2, 4, 4, 64>;
+constexpr int64_t kW8MaxK = 6144;
 
 hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
                        const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1)
 {
+    if (K % Gemm128::ROWB == 0 && K <= kW8MaxK && !ep.row_zp && !ep.f8)
+        return gemm::launch<Gemm128W8, Gemm128>(Xq, CB, T, K, N, ep, s, ev0, ev1);
     if (K % Gemm128::ROWB == 0)
         return gemm::launch<Gemm128>(Xq, CB, T, K, N, ep, s, ev0, ev1);
     return gemm::launch<Gemm64>(Xq, CB, T, K, N, ep, s, ev0, ev1);

@@ -1023,11 +1023,12 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restr
 // (and the output activation, ep.act, a template parameter of the output
 // kernels); for the output (not the raw int32 sums) also k_gemm_many, of
 // which only one does work, depending on the outlier count on the device.
-template <class C>
+template <class C, class CM = C>
 hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
                   const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
                   hipEvent_t ev1 = nullptr)
 {
+    static_assert(C::BM == CM::BM && C::BN == CM::BN && C::ROWB == CM::ROWB, "one tile grid");
     if (K % C::ROWB != 0)
         return hipErrorInvalidValue;
     const int64_t ntm = (T + C::BM - 1) / C::BM, ntn = (N + C::BN - 1) / C::BN;
@@ -1059,16 +1060,16 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
     }
     if (!ep.c_i32) {
         if (ep.f8)
-            hipLaunchKernelGGL((k_gemm_many<C, false, false, true>), grid, dim3(C::kThreads), 0, s,
+            hipLaunchKernelGGL((k_gemm_many<CM, false, false, true>), grid, dim3(CM::kThreads), 0, s,
                                Xq, CB, T, K, N, ep);
         else if (ep.row_zp)
-            hipLaunchKernelGGL((k_gemm_many<C, false, true>), grid, dim3(C::kThreads), 0, s, Xq, CB,
+            hipLaunchKernelGGL((k_gemm_many<CM, false, true>), grid, dim3(CM::kThreads), 0, s, Xq, CB,
                                T, K, N, ep);
         else if (ep.act)
-            hipLaunchKernelGGL((k_gemm_many<C, true>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K,
+            hipLaunchKernelGGL((k_gemm_many<CM, true>), grid, dim3(CM::kThreads), 0, s, Xq, CB, T, K,
                                N, ep);
         else
-            hipLaunchKernelGGL((k_gemm_many<C, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T,
+            hipLaunchKernelGGL((k_gemm_many<CM, false>), grid, dim3(CM::kThreads), 0, s, Xq, CB, T,
                                K, N, ep);
     }
     return hipGetLastError();
