@@ -13,10 +13,15 @@ The JSON line also carries:
   roofline      the GEMM kernel's own duration (HIP events recorded around its
                 launch on the stream it runs on, in a second pass of the same
                 steps right after the timed ones) against the dense int8 MFMA
-                peak;
+                peak, and beside it the measured MFMA ceiling on the
+                workload's own operands (the clock is power-managed under a
+                sustained MFMA load);
   cpu_baseline  the plain CPU oracle timed on a bounded sample of the same work;
   decode        the weight-streaming kernel at T in {1,4,16}, K=12288, N=49152
-                (604 MB of CB, two copies rotated), against HBM bandwidth.
+                (604 MB of CB, two copies rotated), against HBM bandwidth;
+  configs       the other workloads: the 1.3B-style up-projection, fc2 of the
+                FFN pair on fc1's real ReLU'd output and the pair as one step,
+                and the attention-projection sweep (--no-configs skips them).
 """
 import argparse
 import ctypes
@@ -136,6 +141,17 @@ def spread_us(kern_ms):
             "kernel_us_p90": round(float(q[2]), 2)}
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(X, W_t, thr, rows):
     import oracle
     CBh, SCBh = oracle.quantize_weight(W_t)
@@ -146,7 +162,7 @@ def cpu_baseline(X, W_t, thr, rows):
     T, K = X.shape
     N = W_t.shape[0]
     return {"value": 2.0 * rows * K * N / dt / 1e12, "unit": "TOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "rows 0..%d of X (%d of %d) against all %d output columns; the outlier set is "
                       "found from all rows; %.1f s wall" % (rows - 1, rows, T, N, dt)}
 
@@ -180,21 +196,38 @@ def decode_bench(torch, L, workloads, steps, warmup, ev, dev):
     return res
 
 
-def ffn_pair(torch, L, d, steps, warmup, dev):
-    """The 6.7B-style FFN as one step: fc1 (X [4096,4096] -> [4096,16384]) with
-    the ReLU fused into its output, then fc2 on that output ([4096,16384] ->
-    [4096,4096]), both through the decomposition at threshold 6.  Counts
-    2*T*K*N ops per layer.  Also timed with the ReLU as a separate torch pass
-    between the layers, for the cost of the unfused chain."""
+def ffn_pair(torch, L, d, steps, warmup, ev, dev, entry):
+    """The 6.7B-style FFN: fc1 (X [4096,4096] -> [4096,16384]) with the ReLU
+    fused into its output, then fc2 ([4096,16384] -> [4096,4096]) on that
+    output, both through the decomposition at threshold 6.  Returns the fc2
+    call on its own (on the ReLU'd fc1 output: most of its columns hold a
+    value above 6, so the fp16 outlier product dominates; with the fp16 MFMA
+    ceiling on fc2's own operands, X = that output and W2 in fp16) and the
+    pair as one step (2*T*K*N ops per layer), also with the ReLU as a
+    separate torch pass between the layers, for the cost of the unfused
+    chain."""
     X = torch.from_numpy(d["X"]).to(dev)
     CB1, SCB1 = L.llmint8_quantize_weight(torch.from_numpy(d["W_t"]).to(dev))
-    CB2, SCB2 = L.llmint8_quantize_weight(torch.from_numpy(d["W2_t"]).to(dev))
+    W2 = torch.from_numpy(d["W2_t"]).to(dev)
+    CB2, SCB2 = L.llmint8_quantize_weight(W2)
     T, D = X.shape
     F = CB1.shape[0]
     h = torch.empty((T, F), dtype=torch.float16, device=dev)
     y = torch.empty((T, D), dtype=torch.float16, device=dev)
     ws = torch.empty((max(L.llmint8_workspace_bytes(T, D, F), L.llmint8_workspace_bytes(T, F, D)),),
                      dtype=torch.uint8, device=dev)
+    L.llmint8_matmul_act(X, CB1, SCB1, 6.0, L.ACT_RELU, out=h, ws=ws)
+    n2 = int(L.llmint8_quantize_act(h, 6.0)[3].cpu()[0])
+    ms, kms, _ = timed_steps(torch, L, h, [CB2], SCB2, 6.0, y, ws, steps, warmup, ev)
+    fc2 = entry(T, F, D, 6.0, n2, ms, kms)
+    fc2["input"] = "the fc1 output of this workload with the ReLU fused (llmint8_matmul_act)"
+    fc2["step_frac_fp16_peak"] = round(2.0 * T * F * D / (ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4)
+    ceil16 = mfma_ceiling(torch, L, h, W2, ev)
+    fc2["fp16_mfma_ceiling_TFLOPS"] = round(ceil16, 1)
+    log("config ffn_6p7b_fc2 (on the ReLU'd fc1 output): n=%d step %.1f us (%.0f TOP/s); "
+        "fp16 MFMA ceiling on its operands %.0f TFLOP/s" % (n2, ms * 1e3, 2.0 * T * F * D / ms / 1e9,
+                                                             ceil16))
+    del W2
 
     def fused():
         L.llmint8_matmul_act(X, CB1, SCB1, 6.0, L.ACT_RELU, out=h, ws=ws)
@@ -215,19 +248,18 @@ def ffn_pair(torch, L, d, steps, warmup, dev):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 
-    n2 = int(L.llmint8_quantize_act(torch.relu(L.llmint8_matmul(X, CB1, SCB1, 6.0)), 6.0)[3].cpu()[0])
     s_f = per_step(fused)
     s_u = per_step(unfused)
     ops = 2.0 * T * D * F * 2
-    r = {"T": T, "D": D, "F": F, "threshold": 6.0, "fc2_n_outliers": n2,
-         "step_us": round(s_f * 1e6, 2), "step_TOPS": round(ops / s_f / 1e12, 1),
-         "step_frac_int8_peak": round(ops / s_f / 1e12 / INT8_PEAK_TOPS, 4),
-         "unfused_step_us": round(s_u * 1e6, 2)}
+    pair = {"T": T, "D": D, "F": F, "threshold": 6.0, "fc2_n_outliers": n2,
+            "step_us": round(s_f * 1e6, 2), "step_TOPS": round(ops / s_f / 1e12, 1),
+            "step_frac_int8_peak": round(ops / s_f / 1e12 / INT8_PEAK_TOPS, 4),
+            "unfused_step_us": round(s_u * 1e6, 2)}
     log("config ffn_6p7b_pair: fc1+ReLU+fc2 %.1f us (%.0f TOP/s), ReLU as a separate pass %.1f us"
         % (s_f * 1e6, ops / s_f / 1e12, s_u * 1e6))
     del X, CB1, SCB1, CB2, SCB2, h, y, ws
     torch.cuda.empty_cache()
-    return r
+    return {"ffn_6p7b_fc2": fc2, "ffn_6p7b_pair": pair}
 
 
 def fp16_weight_step(torch, L, d, steps, warmup, dev):
@@ -396,15 +428,45 @@ def fp8_bench(torch, L, workloads, steps, warmup, ev, dev):
     return res
 
 
+def mfma_ceiling(torch, L, A, B, ev, blocks=1024, iters=128, reps=10):
+    """The MFMA rate on A's and B's own bits (see llmint8_mfma_ceiling): 3 warm-up
+    launches, then `reps` timed back to back, each bracketed by HIP events on
+    its stream; returns ops (or flops) per second of the mean launch, in 1e12."""
+    for _ in range(3):
+        L.llmint8_mfma_ceiling(A, B, blocks, iters)
+    pairs = [(ev.create(), ev.create()) for _ in range(reps)]
+    ops = 0.0
+    for a, b in pairs:
+        _, ops = L.llmint8_mfma_ceiling(A, B, blocks, iters, start=a, stop=b)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+    return ops / (ms * 1e-3) / 1e12
+
+
 def configs_bench(torch, L, workloads, steps, warmup, ev, dev):
-    """The method's other workloads (parity cases), each timed like the main one:
-    the 1.3B up-projection, the fc2-like input (every column an outlier) and
+    """The other workloads, each timed like the main one (step = one
+    llmint8_matmul call; 2*T*K*N ops): the 1.3B-style up-projection, the
+    6.7B-style FFN pair (fc1 with the ReLU fused into its output, then fc2 on
+    that very output, so fc2 sees the outlier set a real ReLU'd fc1 output
+    has), fc1 with its weight quantized in every step (fp16 weights kept) and
     the attention-projection sweep (outlier dims n in {0,6,32,128}, threshold
-    0 and inf, T = 4095), the FFN pair fc1 -> ReLU -> fc2, and fc1 with its
-    weight quantized in every step (fp16 weights kept).  Step figures count 2*T*K*N ops for the whole call;
-    the GEMM kernel's own time is given where k_gemm does the work (up to 32
-    outlier columns)."""
+    0 and inf, T = 4095).  The GEMM kernel's own time (HIP events) is given
+    where k_gemm does the work (up to 32 outlier columns); past that the
+    work is in the many-outlier kernel and the step time is the figure."""
     res = {}
+
+    def entry(T, K, N, thr, n, ms, kms):
+        ops = 2.0 * T * K * N
+        r = {"T": T, "K": K, "N": N, "threshold": thr if np.isfinite(thr) else "inf",
+             "n_outliers": n,
+             "step_us": round(ms * 1e3, 2), "step_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+             "step_frac_int8_peak": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+        if n <= 32:
+            r["gemm_kernel_us"] = round(kms * 1e3, 2)
+            r["gemm_frac_int8_peak"] = round(ops / (kms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
+        if n == K:
+            r["step_frac_fp16_peak"] = round(ops / (ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4)
+        return r
 
     def run(name, X_h, W_h, thr):
         X = torch.from_numpy(X_h).to(dev)
@@ -417,26 +479,15 @@ def configs_bench(torch, L, workloads, steps, warmup, ev, dev):
         ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=dev)
         n = int(L.llmint8_quantize_act(X, thr)[3].cpu()[0])
         ms, kms, _ = timed_steps(torch, L, X, [CB], SCB, thr, out, ws, steps, warmup, ev)
-        ops = 2.0 * T * K * N
-        r = {"T": T, "K": K, "N": N, "threshold": thr if np.isfinite(thr) else "inf",
-             "n_outliers": n,
-             "step_us": round(ms * 1e3, 2), "step_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
-             "step_frac_int8_peak": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
-        if n <= 32:
-            r["gemm_kernel_us"] = round(kms * 1e3, 2)
-            r["gemm_frac_int8_peak"] = round(ops / (kms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
-        if n == K:
-            r["step_frac_fp16_peak"] = round(ops / (ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4)
-        res[name] = r
-        log("config %s: n=%d step %.1f us (%.0f TOP/s)" % (name, n, ms * 1e3, ops / ms / 1e9))
+        res[name] = entry(T, K, N, thr, n, ms, kms)
+        log("config %s: n=%d step %.1f us (%.0f TOP/s)" % (name, n, ms * 1e3, 2.0 * T * K * N / ms / 1e9))
         del CB, SCB, X, out, ws
         torch.cuda.empty_cache()
 
     d = workloads.up_proj_1p3b()
     run("up_proj_1p3b", d["X"], d["W_t"], 6.0)
     d = workloads.ffn_6p7b(with_fc2=True)
-    run("ffn_6p7b_fc2", workloads.ffn_6p7b_fc2_input()["X"], d["W2_t"], 6.0)
-    res["ffn_6p7b_pair"] = ffn_pair(torch, L, d, steps, warmup, dev)
+    res.update(ffn_pair(torch, L, d, steps, warmup, ev, dev, entry))
     res["ffn_6p7b_fc1_fp16_weights"] = fp16_weight_step(torch, L, d, steps, warmup, dev)
     del d
     W5 = workloads.attn_proj_sweep(0)["W_t"]
@@ -457,8 +508,10 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the CPU-oracle sample (4096 = the whole workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--configs", action="store_true",
-                    help="also time the other workloads (1.3B up-proj, fc2-like, attention sweep)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (1.3B up-proj, the FFN pair's fc2, the attention sweep)")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="timed steps per other workload (at most --steps)")
     ap.add_argument("--fp8", action="store_true",
                     help="also time the FP8 (E5M2) variant (fc1 and the decode shape)")
     ap.add_argument("--zeropoint", action="store_true",
@@ -535,10 +588,21 @@ def main():
                                       "stay out of ms_per_step)"},
     }
     result["roofline"].update(spread_us(gemm_kern))
+    Xq = L.llmint8_quantize_act(X, thr)[0]
+    ceil8 = mfma_ceiling(torch, L, Xq, CB, ev)
+    del Xq
+    result["roofline"]["ceiling"] = {
+        "kernel": "k_mfma_ceiling: v_mfma_i32_32x32x32_i8 on 16 accumulators from registers, "
+                  "nothing else in the loop, operands = 16-byte fragments of this workload's Xq and CB",
+        "achieved": round(ceil8, 1), "unit": "TOP/s", "frac_of_peak": round(ceil8 / INT8_PEAK_TOPS, 4),
+        "kernel_frac_of_ceiling": round(achieved / ceil8, 4)}
+    log("int8 MFMA ceiling on fc1's operands: %.0f TOP/s (%.1f%% of the spec peak); k_gemm at %.1f%% of it"
+        % (ceil8, 100 * ceil8 / INT8_PEAK_TOPS, 100 * achieved / ceil8))
     if not args.no_decode:
         result["decode"] = decode_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
-    if args.configs:
-        result["configs"] = configs_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
+    if not args.no_configs:
+        result["configs"] = configs_bench(torch, L, workloads, min(args.steps, args.config_steps),
+                                          min(args.warmup, 3), ev, dev)
     if args.zeropoint:
         result["zeropoint"] = zeropoint_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
     if args.fp8:

@@ -22,8 +22,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers on the current HIP device,
- *    row-major and contiguous, owned by the caller, 16-byte aligned.  Outputs
- *    must not alias inputs.  fp16 data is passed as raw IEEE binary16 bit
+ *    row-major and contiguous, owned by the caller, 16-byte aligned (the
+ *    optional bias: 8-byte aligned; row_zp: 8-byte aligned).  Outputs must
+ *    not alias inputs.  fp16 data is passed as raw IEEE binary16 bit
  *    patterns (uint16_t).
  *  - Shapes: T >= 1 (any value; a ragged last tile is handled), K and N
  *    multiples of 64, K <= 133144 (so K * 127^2 fits in int32).
@@ -32,8 +33,7 @@
  *    keeps no mutable state, so concurrent calls on different streams with
  *    separate outputs and workspaces are safe.  The work is kernel launches
  *    only (no memset, copy or event; the workspace needs no clearing), so a
- *    call made during stream capture can be replayed from a HIP graph; the
- *    timing events of llmint8_matmul_path are the one exception.
+ *    call made during stream capture can be replayed from a HIP graph.
  *  - Status codes: arguments are checked on the host before anything is
  *    enqueued, in this order: null pointers, non-positive sizes or a NaN /
  *    negative threshold -> LLMINT8_ERR_INVALID_ARG; K or N not a multiple of
@@ -70,10 +70,12 @@ typedef enum {
 /* Static, NUL-terminated description of a status code (never NULL). */
 LLMINT8_API const char *llmint8_status_string(int status);
 
-/* Bytes of workspace llmint8_matmul needs for a [T,K] x [K,N] call (the
- * worst case over all outlier counts: the fp16 outlier operands may cover
- * every column when the threshold is 0).  Pure host function; returns 0 for
- * invalid sizes. */
+/* Bytes of workspace llmint8_matmul (and its _act, _zp and _f8 forms) needs
+ * for a [T,K] x [K,N] call, the worst case over all outlier counts.  Besides
+ * the int8 activations (max(T,16) * K bytes) it holds at most
+ * (2*T + N)*min(K,1024) bytes of gathered outlier operands for T > 16
+ * (more outlier columns than fit are read in place), and 2*T*K for T <= 16
+ * (no weight operand).  Pure host function; returns 0 for invalid sizes. */
 LLMINT8_API size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N);
 
 /* Bytes of workspace llmint8_quantize_act needs for K columns. */
@@ -131,13 +133,15 @@ LLMINT8_API llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, 
  *
  *   X          in : fp16 [T,K]
  *   CB, SCB    in : from llmint8_quantize_weight, [N,K] int8 and [N] f32
- *   bias       in : fp16 [N] or NULL
+ *                   (SCB 16-byte aligned: the epilogue reads 4 scales at once)
+ *   bias       in : fp16 [N] or NULL (8-byte aligned)
  *   threshold  in : as for llmint8_quantize_act
  *   out        out: fp16 [T,N] (overflow rounds to +-inf)
  *   ws, ws_bytes  : scratch of at least llmint8_workspace_bytes(T, K, N)
  *
  * T <= 16 runs a weight-streaming kernel (the decode regime), larger T a
  * tiled MFMA GEMM; both give results that meet the same tolerance.
+ * (include/llmint8_test.h has hooks that force either and time it.)
  */
 LLMINT8_API llmint8_status_t llmint8_matmul(const uint16_t *X, int64_t T, int64_t K, int64_t N,
                                 const int8_t *CB, const float *SCB, const uint16_t *bias,
@@ -165,22 +169,6 @@ LLMINT8_API llmint8_status_t llmint8_matmul_act(const uint16_t *X, int64_t T, in
                                                 const uint16_t *bias, float threshold,
                                                 int activation, uint16_t *out, void *ws,
                                                 size_t ws_bytes, hipStream_t stream);
-
-/*
- * llmint8_matmul with the kernel choice forced and optional timing events,
- * for tests and benchmarks: path 0 = automatic, 1 = tiled GEMM, 2 =
- * weight-streaming kernel (requires T <= 16, else
- * LLMINT8_ERR_UNSUPPORTED_SHAPE).  When main_start / main_stop are non-NULL
- * they are recorded on `stream` immediately before and after the launch of
- * the main kernel (the GEMM or weight-streaming kernel), so their elapsed
- * time is that kernel's duration.  The events are created and owned by the
- * caller.
- */
-LLMINT8_API llmint8_status_t llmint8_matmul_path(const uint16_t *X, int64_t T, int64_t K, int64_t N,
-                                     const int8_t *CB, const float *SCB, const uint16_t *bias,
-                                     float threshold, uint16_t *out, void *ws, size_t ws_bytes,
-                                     int path, hipEvent_t main_start, hipEvent_t main_stop,
-                                     hipStream_t stream);
 
 /*
  * Zero-point (asymmetric) variant of the decomposition.  The LLM.int8()
@@ -249,15 +237,6 @@ LLMINT8_API llmint8_status_t llmint8_matmul_zp(const uint16_t *X, int64_t T, int
                                                uint16_t *out, void *ws, size_t ws_bytes,
                                                hipStream_t stream);
 
-/* llmint8_matmul_zp with the path choice and timing events of llmint8_matmul_path. */
-LLMINT8_API llmint8_status_t llmint8_matmul_zp_path(const uint16_t *X, int64_t T, int64_t K,
-                                                    int64_t N, const int8_t *CB, const float *ND,
-                                                    const int32_t *ZP, const int32_t *RS,
-                                                    const uint16_t *bias, float threshold,
-                                                    uint16_t *out, void *ws, size_t ws_bytes,
-                                                    int path, hipEvent_t main_start,
-                                                    hipEvent_t main_stop, hipStream_t stream);
-
 /*
  * FP8 variant of the decomposition.  The LLM.int8() summary
  * (kurtkim.github.io, "LLM.int8()", section "Related work", 8-bit data types)
@@ -309,27 +288,6 @@ LLMINT8_API llmint8_status_t llmint8_matmul_f8(const uint16_t *X, int64_t T, int
                                                const uint16_t *bias, float threshold,
                                                uint16_t *out, void *ws, size_t ws_bytes,
                                                hipStream_t stream);
-
-/* llmint8_matmul_f8 with the path choice and timing events of llmint8_matmul_path. */
-LLMINT8_API llmint8_status_t llmint8_matmul_f8_path(const uint16_t *X, int64_t T, int64_t K,
-                                                    int64_t N, const uint8_t *CB8,
-                                                    const float *SC8, const uint16_t *bias,
-                                                    float threshold, uint16_t *out, void *ws,
-                                                    size_t ws_bytes, int path,
-                                                    hipEvent_t main_start, hipEvent_t main_stop,
-                                                    hipStream_t stream);
-
-/*
- * The int8 product alone, C[t,n] = sum_k Xq[t,k] * CB[n,k] in int32 (LLM.int8()
- * summary, section "Int8 Matrix Multiplication with 16-bit Float Inputs and
- * Outputs"), through the same main loops as llmint8_matmul with the epilogue
- * storing the raw accumulators.  For exact checks of the accumulators.
- *
- *   Xq in: int8 [T,K];  CB in: int8 [N,K];  C out: int32 [T,N]
- *   path: 0 = automatic, 1 = tiled GEMM, 2 = weight-streaming (T <= 16)
- */
-LLMINT8_API llmint8_status_t llmint8_igemm_i32(const int8_t *Xq, int64_t T, int64_t K, int64_t N,
-                                   const int8_t *CB, int32_t *C, int path, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libllmint8.so")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "decode.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "decode.hip", "ceiling.hip"]
 ARCH = os.environ.get("LLMINT8_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -1,9 +1,12 @@
 // api.hip -- the C ABI: argument checks, workspace layout, kernel dispatch.
-// The operations and their sources are documented in include/llmint8.h.
+// The operations and their sources are documented in include/llmint8.h (the
+// method) and include/llmint8_test.h (test and benchmark hooks).
 
 #include <math.h>
 
-#include "../../include/llmint8.h"
+#include <atomic>
+
+#include "../../include/llmint8_test.h"
 #include "internal.h"
 
 namespace llmint8 {
@@ -14,6 +17,9 @@ constexpr int64_t kDecodeMaxT = 16;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+// The output epilogues read four column scales with one 16-byte load and four
+// bias values with one 8-byte load; the bias is optional.
+bool bias_ok(const uint16_t *bias) { return ((uintptr_t)bias & 7u) == 0; }
 
 llmint8_status_t check_shape(int64_t T, int64_t K, int64_t N)
 {
@@ -35,30 +41,99 @@ llmint8_status_t check_shape_zp(int64_t T, int64_t K, int64_t N)
 }
 }  // namespace
 
-MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N)
+MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N, bool decode)
 {
     MatmulWorkspace L;
     size_t off = 0;
     const size_t t = (size_t)T, k = (size_t)K, n = (size_t)N;
-    L.partial = off;     off += align256((size_t)kDetectSplits * (k / 8));
-    L.mask = off;        off += align256(k / 8);
-    L.chunk_pre = off;   off += align256(4 * k);   // K/8 entries used
+    // the GEMM path's gathered operands hold at most kCompactMaxLd columns
+    // (more outlier columns are read in place, see internal.h); the
+    // weight-streaming path gathers the activations of every outlier column
+    // and no weights
+    const size_t ldx = decode ? k : (k < (size_t)kCompactMaxLd ? k : (size_t)kCompactMaxLd);
+    L.mask = off;        off += detect_area_bytes(K);   // outlier flags of the 8-column chunks
+    L.groups = off;      off += align256(4 * (k / 64));
     L.outlier_idx = off; off += align256(4 * k);
-    L.n_outliers = off;  off += 256;
+    L.info = off;        off += 256;
     L.row_absmax = off;  off += align256(4 * t);   // a (zero-point variant: nd)
     L.row_zp = off;      off += align256(8 * t);   // zero-point variant: {zp, code sum}
     L.xq = off;          off += align256((t > 16 ? t : 16) * k);   // decode: 16-row fragment order
-    L.x_out = off;       off += align256(2 * t * k);
-    L.w_out = off;       off += align256(2 * n * k);
+    L.x_out = off;       off += align256(2 * t * ldx);
+    L.w_out = off;       off += decode ? 0 : align256(n * ldx);   // >= 64: kOutFew's fp16 [N,32]
     L.total = off;
     return L;
 }
 
+int compute_units()
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 size_t act_workspace_bytes(int64_t K)
 {
-    const size_t k = (size_t)K;
-    return align256((size_t)kDetectSplits * (k / 8)) + align256(k / 8) + align256(4 * k);
+    return detect_area_bytes(K);   // the outlier flags of the 8-column chunks
 }
+
+namespace {
+// The segments of a matmul call's workspace.
+struct WsPtrs {
+    uint8_t *mask;
+    int32_t *groups, *O, *info;
+    float *a;
+    int2 *row_zp;
+    int8_t *xq;
+    uint16_t *x_out;
+    void *w_out;
+};
+WsPtrs ws_ptrs(void *ws, const MatmulWorkspace &L, bool decode)
+{
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    WsPtrs p;
+    p.mask = base + L.mask;
+    p.groups = reinterpret_cast<int32_t *>(base + L.groups);
+    p.O = reinterpret_cast<int32_t *>(base + L.outlier_idx);
+    p.info = reinterpret_cast<int32_t *>(base + L.info);
+    p.a = reinterpret_cast<float *>(base + L.row_absmax);
+    p.row_zp = reinterpret_cast<int2 *>(base + L.row_zp);
+    p.xq = reinterpret_cast<int8_t *>(base + L.xq);
+    p.x_out = reinterpret_cast<uint16_t *>(base + L.x_out);
+    p.w_out = decode ? nullptr : base + L.w_out;
+    return p;
+}
+
+// The outlier summary a call's row quantization writes: the GEMM path also
+// needs the non-empty groups.
+OutlierInfoOut info_out(const WsPtrs &p, bool decode)
+{
+    OutlierInfoOut io{p.info};
+    if (!decode) {
+        io.groups = p.groups;
+        io.mask = p.mask;
+    }
+    return io;
+}
+
+// The GEMM path's dense-mode operands in the epilogue arguments.
+void dense_args(EpilogueArgs &ep, const uint16_t *X, const WsPtrs &p)
+{
+    ep.X = X;
+    ep.mask = p.mask;
+    ep.groups = p.groups;
+}
+
+}  // namespace
 
 }  // namespace llmint8
 
@@ -80,9 +155,14 @@ const char *llmint8_status_string(int status)
 
 size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N)
 {
-    if (T <= 0 || K <= 0 || N <= 0)
+    return llmint8_workspace_bytes_path(T, K, N, 0);
+}
+
+size_t llmint8_workspace_bytes_path(int64_t T, int64_t K, int64_t N, int path)
+{
+    if (T <= 0 || K <= 0 || N <= 0 || path < 0 || path > 2)
         return 0;
-    return matmul_workspace_layout(T, K, N).total;
+    return matmul_workspace_layout(T, K, N, path == 2 || (path == 0 && T <= kDecodeMaxT)).total;
 }
 
 size_t llmint8_quantize_act_workspace_bytes(int64_t K)
@@ -117,17 +197,15 @@ llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, int64_t K, f
         return st;
     if (ws_bytes < act_workspace_bytes(K))
         return LLMINT8_ERR_WORKSPACE;
-    uint8_t *base = static_cast<uint8_t *>(ws);
-    uint8_t *partial = base;
-    uint8_t *mask = base + align256((size_t)kDetectSplits * ((size_t)K / 8));
-    int32_t *chunk_pre = reinterpret_cast<int32_t *>(mask + align256((size_t)K / 8));
+    uint8_t *mask = static_cast<uint8_t *>(ws);
     const GatherArgs none{nullptr, nullptr, 0, nullptr};
     hipError_t e =
         quantize_act_fits_rows(T, K)
             ? launch_quantize_act_rows(X, T, K, threshold, Xq, row_absmax, outlier_idx,
                                        n_outliers, nullptr, false, stream)
-            : launch_quantize_act(X, T, K, threshold, Xq, row_absmax, outlier_idx, n_outliers,
-                                  partial, mask, chunk_pre, nullptr, none, false, stream);
+            : launch_quantize_act(X, T, K, threshold, Xq, row_absmax, outlier_idx,
+                                  OutlierInfoOut{n_outliers}, mask, nullptr, none, false,
+                                  stream);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 
@@ -137,47 +215,39 @@ llmint8_status_t matmul_impl(const uint16_t *X, int64_t T, int64_t K, int64_t N,
                              int activation, uint16_t *out, void *ws, size_t ws_bytes, int path,
                              hipEvent_t main_start, hipEvent_t main_stop, hipStream_t stream)
 {
-    if (!X || !CB || !SCB || !out || !ws || !aligned16(X) || !aligned16(CB) ||
-        !aligned16(out) || !aligned16(ws) || bad_threshold(threshold) || path < 0 || path > 2 ||
-        (activation != LLMINT8_ACT_NONE && activation != LLMINT8_ACT_RELU))
+    if (!X || !CB || !SCB || !out || !ws || !aligned16(X) || !aligned16(CB) || !aligned16(SCB) ||
+        !bias_ok(bias) || !aligned16(out) || !aligned16(ws) || bad_threshold(threshold) ||
+        path < 0 || path > 2 || (activation != LLMINT8_ACT_NONE && activation != LLMINT8_ACT_RELU))
         return LLMINT8_ERR_INVALID_ARG;
     llmint8_status_t st = check_shape(T, K, N);
     if (st != LLMINT8_OK)
         return st;
     if (path == 2 && T > kDecodeMaxT)
         return LLMINT8_ERR_UNSUPPORTED_SHAPE;
-    const MatmulWorkspace L = matmul_workspace_layout(T, K, N);
+    const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
+    const MatmulWorkspace L = matmul_workspace_layout(T, K, N, decode);
     if (ws_bytes < L.total)
         return LLMINT8_ERR_WORKSPACE;
-    const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
+    const WsPtrs p = ws_ptrs(ws, L, decode);
 
-    uint8_t *base = static_cast<uint8_t *>(ws);
-    uint8_t *partial = base + L.partial;
-    uint8_t *mask = base + L.mask;
-    int32_t *chunk_pre = reinterpret_cast<int32_t *>(base + L.chunk_pre);
-    int32_t *O = reinterpret_cast<int32_t *>(base + L.outlier_idx);
-    int32_t *n_out = reinterpret_cast<int32_t *>(base + L.n_outliers);
-    float *a = reinterpret_cast<float *>(base + L.row_absmax);
-    int8_t *Xq = reinterpret_cast<int8_t *>(base + L.xq);
-    uint16_t *x_out = reinterpret_cast<uint16_t *>(base + L.x_out);
-    uint16_t *w_out = reinterpret_cast<uint16_t *>(base + L.w_out);
-
-    // the GEMM path also needs the dequantized outlier weight rows; the
-    // decode path takes more than a few activation rows in fragment order
-    const GatherArgs g{CB, SCB, N, decode ? nullptr : w_out};
+    // the GEMM path also builds its outlier weight operand; the decode path
+    // takes more than a few activation rows in fragment order
+    const GatherArgs g{CB, SCB, N, p.w_out};
     const bool packed = decode && T >= kDecodePackedMinT;
     const hipError_t eq =
         decode && quantize_act_fits_rows(T, K)
-            ? launch_quantize_act_rows(X, T, K, threshold, Xq, a, O, n_out, x_out, packed, stream)
-            : launch_quantize_act(X, T, K, threshold, Xq, a, O, n_out, partial, mask, chunk_pre,
-                                  x_out, g, packed, stream);
+            ? launch_quantize_act_rows(X, T, K, threshold, p.xq, p.a, p.O, p.info, p.x_out,
+                                       packed, stream)
+            : launch_quantize_act(X, T, K, threshold, p.xq, p.a, p.O, info_out(p, decode),
+                                  p.mask, p.x_out, g, packed, stream);
     if (eq != hipSuccess)
         return LLMINT8_ERR_HIP;
-    EpilogueArgs ep{a, SCB, x_out, w_out, O, n_out, bias, out, nullptr,
+    EpilogueArgs ep{p.a, SCB, p.x_out, p.w_out, p.O, p.info, bias, out, nullptr,
                     activation == LLMINT8_ACT_RELU ? 1 : 0};
+    dense_args(ep, X, p);
     const hipError_t e =
-        decode ? launch_decode(Xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
-               : launch_gemm(Xq, CB, T, K, N, ep, stream, main_start, main_stop);
+        decode ? launch_decode(p.xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
+               : launch_gemm(p.xq, CB, T, K, N, ep, stream, main_start, main_stop);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 }  // namespace
@@ -237,14 +307,11 @@ llmint8_status_t llmint8_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K
         return st;
     if (ws_bytes < act_workspace_bytes(K))
         return LLMINT8_ERR_WORKSPACE;
-    uint8_t *base = static_cast<uint8_t *>(ws);
-    uint8_t *partial = base;
-    uint8_t *mask = base + align256((size_t)kDetectSplits * ((size_t)K / 8));
-    int32_t *chunk_pre = reinterpret_cast<int32_t *>(mask + align256((size_t)K / 8));
+    uint8_t *mask = static_cast<uint8_t *>(ws);
     const GatherArgs none{nullptr, nullptr, 0, nullptr};
     const hipError_t e = launch_quantize_act_zp(X, T, K, threshold, Xq, nd,
                                                 reinterpret_cast<int2 *>(row_zp), outlier_idx,
-                                                n_outliers, partial, mask, chunk_pre, nullptr,
+                                                OutlierInfoOut{n_outliers}, mask, nullptr,
                                                 none, false, stream);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
@@ -257,42 +324,32 @@ llmint8_status_t llmint8_matmul_zp_path(const uint16_t *X, int64_t T, int64_t K,
                                         hipStream_t stream)
 {
     if (!X || !CB || !ND || !ZP || !RS || !out || !ws || !aligned16(X) || !aligned16(CB) ||
-        !aligned16(ZP) || !aligned16(RS) || !aligned16(ND) || !aligned16(out) || !aligned16(ws) ||
-        bad_threshold(threshold) || path < 0 || path > 2)
+        !aligned16(ZP) || !aligned16(RS) || !aligned16(ND) || !bias_ok(bias) || !aligned16(out) ||
+        !aligned16(ws) || bad_threshold(threshold) || path < 0 || path > 2)
         return LLMINT8_ERR_INVALID_ARG;
     llmint8_status_t st = check_shape_zp(T, K, N);
     if (st != LLMINT8_OK)
         return st;
     if (path == 2 && T > kDecodeMaxT)
         return LLMINT8_ERR_UNSUPPORTED_SHAPE;
-    const MatmulWorkspace L = matmul_workspace_layout(T, K, N);
+    const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
+    const MatmulWorkspace L = matmul_workspace_layout(T, K, N, decode);
     if (ws_bytes < L.total)
         return LLMINT8_ERR_WORKSPACE;
-    const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
+    const WsPtrs p = ws_ptrs(ws, L, decode);
 
-    uint8_t *base = static_cast<uint8_t *>(ws);
-    uint8_t *partial = base + L.partial;
-    uint8_t *mask = base + L.mask;
-    int32_t *chunk_pre = reinterpret_cast<int32_t *>(base + L.chunk_pre);
-    int32_t *O = reinterpret_cast<int32_t *>(base + L.outlier_idx);
-    int32_t *n_out = reinterpret_cast<int32_t *>(base + L.n_outliers);
-    float *nd = reinterpret_cast<float *>(base + L.row_absmax);
-    int2 *row_zp = reinterpret_cast<int2 *>(base + L.row_zp);
-    int8_t *Xq = reinterpret_cast<int8_t *>(base + L.xq);
-    uint16_t *x_out = reinterpret_cast<uint16_t *>(base + L.x_out);
-    uint16_t *w_out = reinterpret_cast<uint16_t *>(base + L.w_out);
-
-    const GatherArgs g{CB, ND, N, decode ? nullptr : w_out, ZP};
+    const GatherArgs g{CB, ND, N, p.w_out, ZP};
     const bool packed = decode && T >= kDecodePackedMinT;
-    const hipError_t eq = launch_quantize_act_zp(X, T, K, threshold, Xq, nd, row_zp, O, n_out,
-                                                 partial, mask, chunk_pre, x_out, g, packed,
-                                                 stream);
+    const hipError_t eq = launch_quantize_act_zp(X, T, K, threshold, p.xq, p.a, p.row_zp, p.O,
+                                                 info_out(p, decode), p.mask, p.x_out, g,
+                                                 packed, stream);
     if (eq != hipSuccess)
         return LLMINT8_ERR_HIP;
-    EpilogueArgs ep{nd, ND, x_out, w_out, O, n_out, bias, out, nullptr, 0, row_zp, ZP, RS};
+    EpilogueArgs ep{p.a, ND, p.x_out, p.w_out, p.O, p.info, bias, out, nullptr, 0, p.row_zp, ZP, RS};
+    dense_args(ep, X, p);
     const hipError_t e =
-        decode ? launch_decode(Xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
-               : launch_gemm(Xq, CB, T, K, N, ep, stream, main_start, main_stop);
+        decode ? launch_decode(p.xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
+               : launch_gemm(p.xq, CB, T, K, N, ep, stream, main_start, main_stop);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 
@@ -330,14 +387,11 @@ llmint8_status_t llmint8_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K
         return st;
     if (ws_bytes < act_workspace_bytes(K))
         return LLMINT8_ERR_WORKSPACE;
-    uint8_t *base = static_cast<uint8_t *>(ws);
-    uint8_t *partial = base;
-    uint8_t *mask = base + align256((size_t)kDetectSplits * ((size_t)K / 8));
-    int32_t *chunk_pre = reinterpret_cast<int32_t *>(mask + align256((size_t)K / 8));
+    uint8_t *mask = static_cast<uint8_t *>(ws);
     GatherArgs none{nullptr, nullptr, 0, nullptr};
     none.f8 = true;
     const hipError_t e = launch_quantize_act_f8(X, T, K, threshold, Xq8, row_scale, outlier_idx,
-                                                n_outliers, partial, mask, chunk_pre, nullptr,
+                                                OutlierInfoOut{n_outliers}, mask, nullptr,
                                                 none, false, stream);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
@@ -349,44 +403,36 @@ llmint8_status_t llmint8_matmul_f8_path(const uint16_t *X, int64_t T, int64_t K,
                                         hipStream_t stream)
 {
     if (!X || !CB8 || !SC8 || !out || !ws || !aligned16(X) || !aligned16(CB8) ||
-        !aligned16(SC8) || !aligned16(out) || !aligned16(ws) || bad_threshold(threshold) ||
-        path < 0 || path > 2)
+        !aligned16(SC8) || !bias_ok(bias) || !aligned16(out) || !aligned16(ws) ||
+        bad_threshold(threshold) || path < 0 || path > 2)
         return LLMINT8_ERR_INVALID_ARG;
     llmint8_status_t st = check_shape(T, K, N);
     if (st != LLMINT8_OK)
         return st;
     if (path == 2 && T > kDecodeMaxT)
         return LLMINT8_ERR_UNSUPPORTED_SHAPE;
-    const MatmulWorkspace L = matmul_workspace_layout(T, K, N);
+    const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
+    const MatmulWorkspace L = matmul_workspace_layout(T, K, N, decode);
     if (ws_bytes < L.total)
         return LLMINT8_ERR_WORKSPACE;
-    const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
-
-    uint8_t *base = static_cast<uint8_t *>(ws);
-    uint8_t *partial = base + L.partial;
-    uint8_t *mask = base + L.mask;
-    int32_t *chunk_pre = reinterpret_cast<int32_t *>(base + L.chunk_pre);
-    int32_t *O = reinterpret_cast<int32_t *>(base + L.outlier_idx);
-    int32_t *n_out = reinterpret_cast<int32_t *>(base + L.n_outliers);
-    float *sc = reinterpret_cast<float *>(base + L.row_absmax);
-    uint8_t *Xq8 = base + L.xq;
-    uint16_t *x_out = reinterpret_cast<uint16_t *>(base + L.x_out);
-    uint16_t *w_out = reinterpret_cast<uint16_t *>(base + L.w_out);
+    const WsPtrs p = ws_ptrs(ws, L, decode);
     const int8_t *CB = reinterpret_cast<const int8_t *>(CB8);
 
-    GatherArgs g{CB, SC8, N, decode ? nullptr : w_out};
+    GatherArgs g{CB, SC8, N, p.w_out};
     g.f8 = true;
     const bool packed = decode && T >= kDecodePackedMinT;
-    const hipError_t eq = launch_quantize_act_f8(X, T, K, threshold, Xq8, sc, O, n_out, partial,
-                                                 mask, chunk_pre, x_out, g, packed, stream);
+    const hipError_t eq = launch_quantize_act_f8(X, T, K, threshold,
+                                                 reinterpret_cast<uint8_t *>(p.xq), p.a, p.O,
+                                                 info_out(p, decode), p.mask, p.x_out, g,
+                                                 packed, stream);
     if (eq != hipSuccess)
         return LLMINT8_ERR_HIP;
-    EpilogueArgs ep{sc, SC8, x_out, w_out, O, n_out, bias, out, nullptr, 0};
+    EpilogueArgs ep{p.a, SC8, p.x_out, p.w_out, p.O, p.info, bias, out, nullptr, 0};
     ep.f8 = true;
-    const int8_t *Xq = reinterpret_cast<const int8_t *>(Xq8);
+    dense_args(ep, X, p);
     const hipError_t e =
-        decode ? launch_decode(Xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
-               : launch_gemm(Xq, CB, T, K, N, ep, stream, main_start, main_stop);
+        decode ? launch_decode(p.xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
+               : launch_gemm(p.xq, CB, T, K, N, ep, stream, main_start, main_stop);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 

@@ -12,13 +12,11 @@
 // 64 lanes fetch 16 bytes from 16 different rows scatters 64-byte requests
 // over 16 DRAM pages; here every load instruction fetches 1 KB contiguous
 // from one CB row.  The MFMA, however, needs the 16 rows spread across lanes,
-// so each stage is transposed through a wavefront-private LDS buffer.  Two
-// ways to fill it:
-//   k_decode_rs   16-byte register loads, double-buffered, then ds_write
-//   k_decode_lds  direct global->LDS loads (global_load_lds)
-// The 16-byte chunks of staged row r are XOR-swizzled by r, which makes both
-// the 1 KB writes and the fragment reads (16 rows, one chunk each) hit
-// distinct LDS banks.  Every wavefront synchronizes with nothing but its own
+// so each stage is loaded into registers with 1 KB row-contiguous loads and
+// transposed through a wavefront-private LDS buffer (k_decode_rs).  The
+// 16-byte chunks of staged row r are XOR-swizzled by r, which makes both the
+// 1 KB writes and the fragment reads (16 rows, one chunk each) hit distinct
+// LDS banks.  Every wavefront synchronizes with nothing but its own
 // loads (s_waitcnt).
 //
 // The epilogue is the decomposition of the LLM.int8() summary
@@ -386,94 +384,6 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
     epilogue<kRawI32, kRelu, kZp, kF8>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
 }
 
-// ---------------------------------------------------------------------------
-// LDS-staged with direct loads: ROWBYTES of each of a wavefront's 16 CB rows
-// per stage, STAGES stages per wavefront, WAVES wavefronts per block.
-// ---------------------------------------------------------------------------
-template <int STAGES_, int ROWBYTES_, int WAVES_>
-struct CfgLds {
-    static constexpr int STAGES = STAGES_, ROWBYTES = ROWBYTES_, WAVES = WAVES_;
-    static constexpr int kThreads = 64 * WAVES;
-    static constexpr int kStageWave = 16 * ROWBYTES;
-    static constexpr int kLoads = kStageWave / 1024;    // 1 KB load instructions per stage
-    static constexpr int kSteps = ROWBYTES / 64;        // 16x16x64 MFMA k-steps per stage
-    static constexpr int kLdsBytes = WAVES * STAGES * kStageWave;
-    static_assert(ROWBYTES >= 256 && ROWBYTES % 256 == 0 && kLoads >= 1, "stage shape");
-    static_assert((STAGES - 1) * kLoads + kSteps < 64, "vmcnt range");
-};
-
-template <class C, bool kRawI32>
-__global__ __launch_bounds__(C::kThreads) void k_decode_lds(const int8_t *__restrict__ A,
-                                                            const int8_t *__restrict__ B,
-                                                            int64_t T, int64_t K, int64_t N,
-                                                            EpilogueArgs ep)
-{
-    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int64_t n0 = ((int64_t)blockIdx.x * C::WAVES + wave) * 16;
-    if (n0 >= N)
-        return;   // whole wavefront: N is a multiple of 16
-    const OutlierPrefetch pre = prefetch_outliers<kRawI32>(B, n0 + lane % 16, K, ep);
-    char *wl = smem + wave * C::STAGES * C::kStageWave;
-    const int r = lane % 16, g = lane / 16;
-    const bool arow = r < T;
-    const int8_t *pa = A + (arow ? r : 0) * K + 16 * g;
-    const int64_t nchunks = (K + C::ROWBYTES - 1) / C::ROWBYTES;
-    // Stage c holds bytes [c*ROWBYTES, (c+1)*ROWBYTES) of the wavefront's 16
-    // rows, row i at offset i*ROWBYTES, its 16-byte chunk q in slot q ^ i.
-    // Load instruction m fills the m-th KB: lane l lands at byte m*1024 + 16*l.
-    const int8_t *rowp[C::kLoads];
-    int col[C::kLoads];
-#pragma unroll
-    for (int m = 0; m < C::kLoads; ++m) {
-        const int byte = m * 1024 + 16 * lane;
-        const int row = byte / C::ROWBYTES, slot = (byte % C::ROWBYTES) / 16;
-        rowp[m] = B + (n0 + row) * K;
-        col[m] = 16 * (slot ^ (row & 15));
-    }
-    auto issue = [&](int64_t c) {
-        const int kc = (int)(c * C::ROWBYTES);
-        char *dst = wl + (c % C::STAGES) * C::kStageWave;
-#pragma unroll
-        for (int m = 0; m < C::kLoads; ++m) {
-            // past the end of a row: a harmless address inside it, never read back
-            const int off = kc + col[m] < K ? kc + col[m] : 0;
-            __builtin_amdgcn_global_load_lds((const void *)(rowp[m] + off),
-                                             (lds_void *)(dst + m * 1024), 16, 0, 0);
-        }
-    };
-    v4i acc = v4i{0, 0, 0, 0};
-    const v4i zero = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int c = 0; c < C::STAGES - 1; ++c)
-        if (c < nchunks)
-            issue(c);
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t kc = c * C::ROWBYTES;
-        const int steps = K - kc >= C::ROWBYTES ? C::kSteps : (int)((K - kc) / 64);
-        v4i a[C::kSteps];
-#pragma unroll
-        for (int s2 = 0; s2 < C::kSteps; ++s2)
-            a[s2] = (arow && s2 < steps) ? *reinterpret_cast<const v4i *>(pa + kc + 64 * s2) : zero;
-        if (c + C::STAGES - 1 < nchunks) {
-            issue(c + C::STAGES - 1);
-            // stage c landed; the newer stages and the a[] loads may still be in flight
-            wait_vm<(C::STAGES - 1) * C::kLoads + C::kSteps>();
-        } else {
-            wait_vm<C::kSteps>();   // a[] loads are the newest; everything older has landed
-        }
-        const char *src = wl + (c % C::STAGES) * C::kStageWave + r * C::ROWBYTES;
-#pragma unroll
-        for (int s2 = 0; s2 < C::kSteps; ++s2) {
-            if (s2 < steps) {
-                const v4i b = *reinterpret_cast<const v4i *>(src + (((4 * s2 + g) ^ r) * 16));
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[s2], b, acc, 0, 0, 0);
-            }
-        }
-    }
-    epilogue<kRawI32>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
-}
-
 template <class C, bool R, bool kRelu = false, bool kZp = false, bool kF8 = false>
 struct RsKernel {
     static constexpr auto fn = k_decode_rs<C, R, kRelu, kZp, kF8>;
@@ -484,11 +394,6 @@ template <class C, bool R>
 using RsKernelRelu = RsKernel<C, R, true>;
 template <class C, bool R>
 using RsKernelZp = RsKernel<C, R, false, true>;
-template <class C, bool R>
-struct LdsKernel {
-    static constexpr auto fn = k_decode_lds<C, R>;
-};
-
 // One block per C::WAVES * 16 output columns.
 template <class C, template <class, bool> class Kernel>
 hipError_t launch_kernel(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
@@ -528,14 +433,6 @@ hipError_t launch_rs(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, i
     if (ep.act && !ep.c_i32)
         return launch_kernel<C, RsKernelRelu>(Xq, CB, T, K, N, ep, s, ev0, ev1);
     return launch_kernel<C, RsKernel>(Xq, CB, T, K, N, ep, s, ev0, ev1);
-}
-
-template <class C>
-hipError_t launch_lds(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,
-                      const EpilogueArgs &ep, hipStream_t s, hipEvent_t ev0 = nullptr,
-                      hipEvent_t ev1 = nullptr)
-{
-    return launch_kernel<C, LdsKernel>(Xq, CB, T, K, N, ep, s, ev0, ev1);
 }
 
 }  // namespace

@@ -77,6 +77,17 @@ struct Cfg {
     }
 };
 
+// One 16-byte direct global->LDS load per lane through a buffer resource:
+// the lane's 16 bytes at voffset + soffset land at LDS dst + 16 * lane (dst
+// wave-uniform, passed in M0).  A plain function rather than inline builtin
+// calls in the templates below, so that the host compilation pass, which
+// has no such builtin, only ever sees this one declaration.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_void *dst,
+                                           uint32_t voffset, uint32_t soffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voffset, soffset, 0, 0);
+}
+
 // s_waitcnt vmcnt(n) with expcnt/lgkmcnt left alone (gfx9 encoding).
 template <int n>
 __device__ __forceinline__ void wait_vm()
@@ -148,19 +159,25 @@ struct Streams {
         char *sa = smem + stage * C::kStageBytes;
         char *sb = sa + C::BM * C::ROWB;
         if (j < C::kAInstr)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_void *)(sa + (wave * C::kAInstr + j) * 1024), 16, offA[j],
-                (uint32_t)kbyte, 0, 0);
+            lds_load16(ra, (lds_void *)(sa + (wave * C::kAInstr + j) * 1024), offA[j],
+                       (uint32_t)kbyte);
         else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_void *)(sb + (wave * C::kBInstr + j - C::kAInstr) * 1024), 16,
-                offB[j - C::kAInstr], (uint32_t)kbyte, 0, 0);
+            lds_load16(rb, (lds_void *)(sb + (wave * C::kBInstr + j - C::kAInstr) * 1024),
+                       offB[j - C::kAInstr], (uint32_t)kbyte);
     }
 
     __device__ __forceinline__ void issue(char *smem, int stage, int64_t kbyte, int wave) const
     {
 #pragma unroll
         for (int j = 0; j < C::kLoads; ++j)
+            issue_one(smem, stage, kbyte, wave, j);
+    }
+
+    // The A operand's loads only (the fp16 pass stages its B operand itself).
+    __device__ __forceinline__ void issue_a(char *smem, int stage, int64_t kbyte, int wave) const
+    {
+#pragma unroll
+        for (int j = 0; j < C::kAInstr; ++j)
             issue_one(smem, stage, kbyte, wave, j);
     }
 };
@@ -615,7 +632,7 @@ __device__ __forceinline__ void issue_outlier_rows(char *orows, const EpilogueAr
 {
     using R = OutlierRows<C>;
     const char *xb = reinterpret_cast<const char *>(ep.x_out);
-    const char *wb = reinterpret_cast<const char *>(ep.w_out);
+    const char *wb = static_cast<const char *>(ep.w_out);
     // every row read lies inside the workspace's x_out / w_out segments (at
     // least 2*K >= 64 bytes per row); with n = 0 their contents are unused
     const __amdgpu_buffer_rsrc_t rx = Streams<C>::rsrc(xb + m0 * R::kRowBytes, (T - m0) * R::kRowBytes);
@@ -630,8 +647,7 @@ __device__ __forceinline__ void issue_outlier_rows(char *orows, const EpilogueAr
         const int64_t lim = isx ? T - m0 : N - n0;
         const int64_t row = rr < lim ? rr : lim - 1;   // ragged: clamp
         const uint32_t off = (uint32_t)(row * R::kRowBytes + 16 * R::slot(r, lq));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(isx ? rx : rw, (lds_void *)(orows + j * 1024), 16,
-                                                 off, 0, 0, 0);
+        lds_load16(isx ? rx : rw, (lds_void *)(orows + j * 1024), off, 0);
     }
 }
 
@@ -776,20 +792,307 @@ __device__ __forceinline__ void finish_tile(const Acc (&acc)[C::FM][C::FN], cons
     write_tile<C>(smem, ep, m0, n0, T, N, tid);
 }
 
-// More than 32 outlier columns: the fp16 product runs as a second GEMM on
-// the same tile, through the same LDS pipeline, over the gathered operands
-// (x_out and w_out rows, K' = n padded to a multiple of 64 halves).  The int8
-// sums are first dequantized into fp32 accumulators (the int32 ones die
-// there, so the two share registers) onto which the fp16 MFMAs add; then
-// the bias, one rounding, and the tile goes out through LDS like
-// finish_tile's.
-template <class C, bool kRelu, bool kZp, class Acc = v16i>
+// ---------------------------------------------------------------------------
+// More than 32 outlier columns: the fp16 product as a second GEMM pass on the
+// tile, onto the dequantized int8 result, in stages of 64 outlier positions
+// (128 bytes of fp16 per operand row) through two LDS buffers.  Its operands
+// depend on the mode the row quantization chose (see internal.h):
+//   kOutCompact  A = x_out [T, ld] (fp16), B = the gathered weight codes
+//                [N, ld] (int8); stage s = positions 64s .. 64s+63;
+//   kOutDense    A = X [T, K], B = CB [N, K] themselves; stage s = the s-th
+//                non-empty 64-column group, and B's codes of the group's
+//                non-outlier columns are masked to zero (so A needs no mask).
+// A is staged by direct global->LDS loads like the int8 operands.  B goes
+// through registers: each lane loads 16 codes of a weight row, dequantizes
+// them to fp16 -- fp16(cb * fp32(SCB/127)), the correctly rounded CB*SCB/127
+// (dequant_w_r); zero-point and FP8 variants as their outlier weights -- and
+// writes them into the stage in the layout the fragment reads expect.  The
+// codes of stage s+2 are loaded while stage s is multiplied and written
+// during stage s+1, so neither operand stalls the MFMAs for long.
+// ---------------------------------------------------------------------------
+template <class C>
+using PassCfg = Cfg<C::BM, C::BN, C::WM, C::WN, 2, C::GROUP, 128>;
+
+// Dequantization parameters of one weight row (output column): absmax s =
+// fp32(SCB/127); FP8 s = the scale 2^-e; zero-point s = fp32(1/nd), zp, nd.
+struct DqRow {
+    float s;
+    int zp;
+    float nd;
+};
+
+enum { kVarAbsmax = 0, kVarZp = 1, kVarF8 = 2 };
+
+template <int kVar>
+__device__ __forceinline__ DqRow dq_row(const EpilogueArgs &ep, int64_t n)
+{
+    DqRow p{0.0f, 0, 0.0f};
+    if constexpr (kVar == kVarZp) {
+        p.nd = ep.scb[n];
+        p.zp = ep.zp_b[n];
+        p.s = p.nd > 0.0f ? 1.0f / p.nd : 0.0f;
+    } else if constexpr (kVar == kVarF8) {
+        p.s = ep.scb[n];
+    } else {
+        p.s = ep.scb[n] / 127.0f;
+    }
+    return p;
+}
+
+// 8 weight codes (bytes of w0, w1) -> 8 fp16 values; code e is kept only when
+// bit e of m8 is set (an outlier column), else 0.
+template <int kVar>
+__device__ __forceinline__ uint4 dq8(unsigned w0, unsigned w1, unsigned m8, const DqRow &p)
+{
+    unsigned h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const unsigned byte = ((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xffu;
+        uint16_t v;
+        if constexpr (kVar == kVarF8)
+            v = dequant_w_f8(byte, p.s);
+        else if constexpr (kVar == kVarZp)
+            v = dequant_w_zp_r((int)(int8_t)byte, p.zp, p.nd, p.s);
+        else
+            v = dequant_w_r((int)(int8_t)byte, p.s);
+        h[e] = ((m8 >> e) & 1u) ? v : 0u;
+    }
+    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                      h[6] | (h[7] << 16));
+}
+
+// 4 weight codes (bytes of w) -> 4 fp16 values, masked like dq8.
+template <int kVar>
+__device__ __forceinline__ uint2 dq4(unsigned w, unsigned m4, const DqRow &p)
+{
+    unsigned h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const unsigned byte = (w >> (8 * e)) & 0xffu;
+        uint16_t v;
+        if constexpr (kVar == kVarF8)
+            v = dequant_w_f8(byte, p.s);
+        else if constexpr (kVar == kVarZp)
+            v = dequant_w_zp_r((int)(int8_t)byte, p.zp, p.nd, p.s);
+        else
+            v = dequant_w_r((int)(int8_t)byte, p.s);
+        h[e] = ((m4 >> e) & 1u) ? v : 0u;
+    }
+    return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+}
+
+// The B operand of the pass: lane l loads 16 codes (positions 16 (l % 4) ..
+// of the stage) of weight row wave * kRows + 16 i + l / 4 (rows past N read
+// row N-1, never stored), dequantizes them with its row's parameters and
+// writes them to the stage's B region as 2 fp16 chunks (2 (l % 4) and the
+// next), in slot chunk ^ swz(row) like the direct-loaded operands.
+template <class C, int kVar>
+struct BStage {
+    static constexpr int kRows = C::BN / C::kWaves;   // weight rows a wavefront stages
+    static constexpr int kI = kRows / 16;              // 16-byte code loads per lane per stage
+    static constexpr int kUnits = 4 * kI;              // 4-code conversion units per stage
+    static_assert(kRows % 16 == 0, "16 rows x 4 pieces per load instruction");
+    const int8_t *tile;
+    uint32_t off[kI];
+    int row[kI], piece;
+    DqRow prm[kI];
+    v4i reg[2][kI];   // codes of two stages (by stage parity)
+
+    __device__ __forceinline__ void init(const int8_t *base, int64_t ld, int64_t n0, int64_t N,
+                                         const EpilogueArgs &ep, int wave, int lane)
+    {
+        tile = base + n0 * ld;
+        piece = lane & 3;
+#pragma unroll
+        for (int i = 0; i < kI; ++i) {
+            row[i] = wave * kRows + 16 * i + (lane >> 2);
+            const int64_t r = n0 + row[i] < N ? row[i] : N - 1 - n0;
+            off[i] = (uint32_t)(r * ld + 16 * piece);
+            prm[i] = dq_row<kVar>(ep, n0 + r);
+        }
+    }
+
+    template <int kBuf>
+    __device__ __forceinline__ void load(int col)
+    {
+#pragma unroll
+        for (int i = 0; i < kI; ++i)
+            reg[kBuf][i] = *reinterpret_cast<const v4i *>(tile + off[i] + col);
+    }
+
+    // Unit u of the stage in buffer kBuf: codes 4 (u % 4) .. of load u / 4,
+    // i.e. half u % 2 of chunk 2 * piece + (u % 4) / 2; m16: bit e set =
+    // position 16 * piece + e is an outlier column.
+    template <int kBuf>
+    __device__ __forceinline__ void store_unit(char *stage, unsigned m16, int u) const
+    {
+        const int i = u / 4, sub = u % 4;
+        const int r = row[i];
+        const uint2 h = dq4<kVar>((unsigned)reg[kBuf][i][sub], (m16 >> (4 * sub)) & 0xfu, prm[i]);
+        char *sb = stage + C::BM * C::ROWB;
+        *reinterpret_cast<uint2 *>(sb + r * C::ROWB + 16 * ((2 * piece + sub / 2) ^ C::swz(r)) +
+                                   8 * (sub % 2)) = h;
+    }
+};
+
+// One fp16 k-step of the pass: the fragment reads of the next k-step
+// interleaved with this one's MFMAs, pinned in groups like kstep's.
+// work(g) (a generic callable) runs between the g-th read and its MFMAs, so
+// VALU work can be spread over the k-step.
+template <class C, class AccArray, class Work>
+__device__ __forceinline__ void pass_kstep(const Frags<C> &cur, Frags<C> &nxt, const char *sa,
+                                           const char *sb, int fo, AccArray &acc, Work &&work)
+{
+    constexpr int kReads = C::FM + C::FN, kMfma = C::FM * C::FN;
+#pragma unroll
+    for (int g = 0; g < kReads; ++g) {
+        read_one<C>(nxt, sa, sb, fo, g);
+        work(std::integral_constant<int, 0>{}, g);
+#pragma unroll
+        for (int idx = g * kMfma / kReads; idx < (g + 1) * kMfma / kReads; ++idx) {
+            const int i = idx / C::FN, j = idx % C::FN;
+            acc[i][j] = MfmaF16F::op(cur.b[j], cur.a[i], acc[i][j]);   // D[n][t], as k_gemm
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <class C, int kVar, class AccArray>
+__device__ __forceinline__ void outlier_gemm_pass(AccArray &accf, char *smem,
+                                                  const EpilogueArgs &ep,
+                                                  const int8_t *__restrict__ CB,
+                                                  const int32_t *__restrict__ info,
+                                                  const int32_t *__restrict__ groups,
+                                                  const uint8_t *__restrict__ mask, int64_t m0,
+                                                  int64_t n0, int64_t T, int64_t K, int64_t N,
+                                                  int nout, int wm, int wn, int wave, int lane)
+{
+    using P = PassCfg<C>;
+    static_assert(P::kLdsBytes <= C::kLdsBytes, "the pass's two stages fit the ring");
+    constexpr int kBI = BStage<P, kVar>::kI;    // 16-byte code loads per lane per stage
+    // (info, groups and mask are kernel arguments the kernel does not write,
+    // so their uniform loads are scalar loads)
+    const bool dense = info[2] == kOutDense;
+    const int64_t ld = outlier_ld(nout);
+    const int nst = dense ? info[1] : (int)(ld / 64);
+    const char *abase = dense ? reinterpret_cast<const char *>(ep.X)
+                              : reinterpret_cast<const char *>(ep.x_out);
+    const int64_t lda = dense ? 2 * K : 2 * ld;
+    const int8_t *bbase = dense ? CB : static_cast<const int8_t *>(ep.w_out);
+    const int64_t ldb = dense ? K : ld;
+    // first column (position) of stage st; stages past the last repeat it
+    auto col = [&](int st) -> int {
+        st = st < nst ? st : nst - 1;
+        return dense ? 64 * groups[st] : 64 * st;
+    };
+
+    // A: direct loads into the stage's A region (the A half of Streams; its
+    // B half is not used); B: codes through registers
+    Streams<P> as;
+    as.init(abase, lda, m0, T, abase, lda, m0, T, wave, lane);
+    auto issue_a = [&](int buf, int st) {
+        const int64_t kb = 2 * (int64_t)col(st);
+        as.issue_a(smem, buf, kb, wave);
+    };
+    BStage<P, kVar> bs;
+    bs.init(bbase, ldb, n0, N, ep, wave, lane);
+    // stage st's B mask: 16 bits per lane, the outlier flags of its 16 columns
+    auto mask16 = [&](int st) -> unsigned {
+        if (!dense)
+            return 0xffffu;
+        const int q = groups[st < nst ? st : nst - 1];
+        const unsigned long long m64 =
+            *reinterpret_cast<const unsigned long long *>(mask + 8 * (int64_t)q);
+        return (unsigned)(m64 >> (16 * (lane & 3))) & 0xffffu;
+    };
+
+    const int frow = (lane & 31) * P::ROWB;
+    int fo[P::kKSteps];
+#pragma unroll
+    for (int ks = 0; ks < P::kKSteps; ++ks)
+        fo[ks] = frow + (((2 * ks + (lane >> 5)) ^ P::swz(lane & 31)) << 4);
+    const int aoff = wm * (P::BM / P::WM) * P::ROWB;
+    const int boff = P::BM * P::ROWB + wn * (P::BN / P::WN) * P::ROWB;
+    auto stage_a = [&](int buf) { return smem + buf * P::kStageBytes + aoff; };
+    auto stage_b = [&](int buf) { return smem + buf * P::kStageBytes + boff; };
+
+    auto none = [](auto, int) {};
+    // Stage s: A in LDS buffer s % 2 by direct loads, B's codes in register
+    // buffer s % 2.  Iteration kt issues B(kt+3) before its barrier and
+    // A(kt+2) after it; both land by the next iteration's barrier, and the
+    // codes of B(kt+1) are converted in iteration kt, during its MFMAs.
+    // prologue: stage 0 complete in LDS buffer 0, B(1), B(2) and A(1) in flight
+    bs.template load<0>(col(0));
+    issue_a(0, 0);
+    wait_vm<P::kAInstr>();                // B(0) landed
+    {
+        const unsigned m = mask16(0);
+#pragma unroll
+        for (int u = 0; u < BStage<P, kVar>::kUnits; ++u)
+            bs.template store_unit<0>(smem, m, u);
+    }
+    bs.template load<1>(col(1));
+    bs.template load<0>(col(2));
+    issue_a(1, 1);
+    wait_vm<2 * kBI + P::kAInstr>();      // A(0) landed
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    Frags<P> f0, f1;
+    read_frags<P>(f0, stage_a(0), stage_b(0), fo[0]);
+    constexpr int kU = BStage<P, kVar>::kUnits;
+    constexpr int kG = P::FM + P::FN;     // groups per k-step
+    static_assert(kU <= 2 * kG, "conversion units fit two k-steps");
+    // iteration kt with kt % 2 == B (compile time): stage kt in LDS buffer B,
+    // B(kt+1) converted from register buffer 1-B into LDS buffer 1-B
+    auto iter = [&](auto bc, int kt) {
+        constexpr int B = decltype(bc)::value, NB = 1 - B;
+        pass_kstep<P>(f0, f1, stage_a(B), stage_b(B), fo[1], accf, none);
+        wait_vm<kBI + P::kAInstr>();      // B(kt+1) landed; B(kt+2), A(kt+1) may be in flight
+        const unsigned m = mask16(kt + 1);
+        char *nstage = smem + NB * P::kStageBytes;   // its readers passed the last barrier
+        auto conv = [&](auto, int g, int base) {
+            const int u = base + g;
+            if (u < kU)
+                bs.template store_unit<NB>(nstage, m, u);
+        };
+        pass_kstep<P>(f1, f0, stage_a(B), stage_b(B), fo[2], accf,
+                      [&](auto z, int g) { conv(z, g, 0); });
+        pass_kstep<P>(f0, f1, stage_a(B), stage_b(B), fo[3], accf,
+                      [&](auto z, int g) { conv(z, g, kG); });
+        bs.template load<NB>(col(kt + 3));
+        wait_vm<kBI>();                   // A(kt+1) landed; B(kt+3) may be in flight
+        wait_lds();                       // stage kt read, B(kt+1) written
+        __builtin_amdgcn_s_barrier();
+        issue_a(B, kt + 2);
+        pass_kstep<P>(f1, f0, stage_a(NB), stage_b(NB), fo[0], accf, none);
+        // (the k-step above reads the first fragments of stage kt+1 from buffer
+        // NB; on the last stage they are not used)
+    };
+    int kt = 0;
+    for (; kt + 2 <= nst; kt += 2) {
+        iter(std::integral_constant<int, 0>{}, kt);
+        iter(std::integral_constant<int, 1>{}, kt + 1);
+    }
+    if (kt < nst)
+        iter(std::integral_constant<int, 0>{}, kt);
+    wait_vm<0>();   // the tail loads land before the buffers are reused
+}
+
+// More than 32 outlier columns: the int8 sums dequantized into fp32
+// accumulators (the int32 ones die there, so the two share registers), the
+// fp16 pass adding the outlier product onto them (outlier_gemm_pass), then
+// the bias, one rounding, and the tile out through LDS like finish_tile's.
+template <class C, bool kRelu, bool kZp, bool kF8, class Acc = v16i>
 __device__ __forceinline__ void outlier_pass(const Acc (&acc)[C::FM][C::FN],
                                              const float (&at)[C::FM], const int (&za)[C::FM],
                                              const int (&ra)[C::FM], char *smem,
-                                             const EpilogueArgs &ep, int64_t m0, int64_t n0,
-                                             int64_t T, int64_t K, int64_t N, int nout, int wm,
-                                             int wn, int wave, int lane, int tid)
+                                             const EpilogueArgs &ep, const int8_t *CB,
+                                             const int32_t *__restrict__ info,
+                                             const int32_t *__restrict__ groups,
+                                             const uint8_t *__restrict__ mask, int64_t m0,
+                                             int64_t n0, int64_t T, int64_t K, int64_t N,
+                                             int nout, int wm, int wn, int wave, int lane,
+                                             int tid)
 {
     const int tl = lane & 31, nl = 4 * (lane >> 5);
     const int64_t nw = n0 + wn * (C::BN / C::WN);
@@ -820,7 +1123,7 @@ __device__ __forceinline__ void outlier_pass(const Acc (&acc)[C::FM][C::FN],
                         accf[i][j][r] = (float)acc[i][j][r] * (at[i] * sn[r / 4][r % 4]);
                 }
         }
-    } else {   // the int8 part is all zeros
+    } else {   // every column an outlier: no int8 part
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -830,14 +1133,8 @@ __device__ __forceinline__ void outlier_pass(const Acc (&acc)[C::FM][C::FN],
                     accf[i][j][r] = 0.0f;
     }
     __builtin_amdgcn_s_barrier();   // every wavefront is done reading the LDS ring
-    {
-        Streams<C> st;
-        const int64_t ldo = outlier_ld(nout);   // x_out / w_out row stride in halves
-        st.init(reinterpret_cast<const char *>(ep.x_out), 2 * ldo, m0, T,
-                reinterpret_cast<const char *>(ep.w_out), 2 * ldo, n0, N, wave, lane);
-        static_assert(128 % C::ROWB == 0, "outlier rows (multiples of 128 bytes) hold whole stages");
-        run_mainloop<C, MfmaF16F>(smem, st, (int)(ldo * 2 / C::ROWB), accf, wm, wn, wave, lane);
-    }
+    outlier_gemm_pass<C, kF8 ? kVarF8 : kZp ? kVarZp : kVarAbsmax>(
+        accf, smem, ep, CB, info, groups, mask, m0, n0, T, K, N, nout, wm, wn, wave, lane);
     static_assert(C::BM * C::BN * 2 <= C::kLdsBytes, "output tile fits the LDS ring");
     __builtin_amdgcn_s_barrier();
 #pragma unroll
@@ -967,12 +1264,12 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
 // registers this path needs do not cost k_gemm's epilogue; one tile per
 // block (a persistent tile loop makes the compiler spill around it).
 template <class C, bool kRelu, bool kZp = false, bool kF8 = false>
-__global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restrict__ A,
-                                                           const int8_t *__restrict__ B,
-                                                           int64_t T, int64_t K, int64_t N,
-                                                           EpilogueArgs ep)
+__global__ __launch_bounds__(C::kThreads) void k_gemm_many(
+    const int8_t *__restrict__ A, const int8_t *__restrict__ B, int64_t T, int64_t K, int64_t N,
+    EpilogueArgs ep, const int32_t *__restrict__ info, const int32_t *__restrict__ groups,
+    const uint8_t *__restrict__ mask)
 {
-    const int nout = *ep.n_out;
+    const int nout = info[0];
     if (nout <= kOutlierPad)
         return;
     __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
@@ -980,43 +1277,49 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(const int8_t *__restr
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int ntm = (int)((T + C::BM - 1) / C::BM), ntn = (int)((N + C::BN - 1) / C::BN);
-    int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, ntm, ntn, C::GROUP, tm, tn);
-    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    // persistent: workgroup b takes tiles b, b + G, ... (G = gridDim.x, a
+    // multiple of the XCD count when below the tile count, so a tile runs on
+    // the XCD tile_coords assumes)
+    for (int tile = blockIdx.x; tile < ntm * ntn; tile += gridDim.x) {
+        int tm, tn;
+        tile_coords(tile, ntm * ntn, ntm, ntn, C::GROUP, tm, tn);
+        const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
 
-    using Acc = std::conditional_t<kF8, v16f, v16i>;
-    Acc acc[C::FM][C::FN];
+        using Acc = std::conditional_t<kF8, v16f, v16i>;
+        Acc acc[C::FM][C::FN];
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+        for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+            for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[i][j][r] = 0;
-    if (nout < K) {
-        Streams<C> st;
-        st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
-                n0, N, wave, lane);
-        if constexpr (kF8)
-            mainloop_f8<C>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
-        else
-            run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0;
+        if (nout < K) {
+            Streams<C> st;
+            st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
+                    n0, N, wave, lane);
+            if constexpr (kF8)
+                mainloop_f8<C>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+            else
+                run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+        }
+        float at[C::FM];
+        int za[C::FM], ra[C::FM];
+        const int64_t tw = m0 + wm * (C::BM / C::WM) + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            const int64_t t = tw + i * 32;
+            if constexpr (kZp)
+                zp_row(ep, t < T ? t : T - 1, K, at[i], za[i], ra[i]);
+            else if constexpr (kF8)
+                at[i] = ep.a[t < T ? t : T - 1];
+            else
+                at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
+        }
+        outlier_pass<C, kRelu, kZp, kF8, Acc>(acc, at, za, ra, smem, ep, B, info, groups, mask, m0, n0,
+                                              T, K, N, nout, wm, wn, wave, lane, tid);
+        __syncthreads();   // the output tile's LDS staging is read before the next tile's loads
     }
-    float at[C::FM];
-    int za[C::FM], ra[C::FM];
-    const int64_t tw = m0 + wm * (C::BM / C::WM) + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        const int64_t t = tw + i * 32;
-        if constexpr (kZp)
-            zp_row(ep, t < T ? t : T - 1, K, at[i], za[i], ra[i]);
-        else if constexpr (kF8)
-            at[i] = ep.a[t < T ? t : T - 1];
-        else
-            at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
-    }
-    outlier_pass<C, kRelu, kZp, Acc>(acc, at, za, ra, smem, ep, m0, n0, T, K, N, nout, wm, wn,
-                                     wave, lane, tid);
 }
 
 // The int8 GEMM (K must be a multiple of C::ROWB) with its fused epilogue
@@ -1059,18 +1362,23 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
             return e;
     }
     if (!ep.c_i32) {
+        // persistent grid: at most one workgroup per compute unit (its LDS
+        // allows no more), so a call with few outlier columns, where it
+        // exits at once, costs one dispatch round
+        const int64_t ncu = compute_units() / 8 * 8;
+        const dim3 grid_many((unsigned)(ntm * ntn <= ncu || ncu < 8 ? ntm * ntn : ncu));
         if (ep.f8)
-            hipLaunchKernelGGL((k_gemm_many<CM, false, false, true>), grid, dim3(CM::kThreads), 0, s,
-                               Xq, CB, T, K, N, ep);
+            hipLaunchKernelGGL((k_gemm_many<CM, false, false, true>), grid_many, dim3(CM::kThreads), 0, s,
+                               Xq, CB, T, K, N, ep, ep.n_out, ep.groups, ep.mask);
         else if (ep.row_zp)
-            hipLaunchKernelGGL((k_gemm_many<CM, false, true>), grid, dim3(CM::kThreads), 0, s, Xq, CB,
-                               T, K, N, ep);
+            hipLaunchKernelGGL((k_gemm_many<CM, false, true>), grid_many, dim3(CM::kThreads), 0, s, Xq, CB,
+                               T, K, N, ep, ep.n_out, ep.groups, ep.mask);
         else if (ep.act)
-            hipLaunchKernelGGL((k_gemm_many<CM, true>), grid, dim3(CM::kThreads), 0, s, Xq, CB, T, K,
-                               N, ep);
+            hipLaunchKernelGGL((k_gemm_many<CM, true>), grid_many, dim3(CM::kThreads), 0, s, Xq, CB, T, K,
+                               N, ep, ep.n_out, ep.groups, ep.mask);
         else
-            hipLaunchKernelGGL((k_gemm_many<CM, false>), grid, dim3(CM::kThreads), 0, s, Xq, CB, T,
-                               K, N, ep);
+            hipLaunchKernelGGL((k_gemm_many<CM, false>), grid_many, dim3(CM::kThreads), 0, s, Xq, CB, T,
+                               K, N, ep, ep.n_out, ep.groups, ep.mask);
     }
     return hipGetLastError();
 }

@@ -17,6 +17,27 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 constexpr int kWave = 64;
 constexpr int kOutlierPad = 32;   // outlier rows of up to 32 columns are padded to this length
 
+// How the GEMM path forms the fp16 product over the outlier columns O, chosen
+// on the device from n = |O| and the number of 64-column groups of K that hold
+// an outlier (ng), identically by every kernel that needs it:
+//   kOutFew      n <= 32: compact fp16 operands x_out [T,32] and w_out [N,32]
+//                (dequantized weights), two fp16 MFMAs per tile in k_gemm;
+//   kOutCompact  more, at most kCompactMaxLd after padding, and scattered:
+//                compact operands x_out [T,ld] (fp16) and the weight codes of
+//                the outlier columns [N,ld] (int8), dequantized by k_gemm_many
+//                as it stages them;
+//   kOutDense    otherwise (e.g. every column an outlier): k_gemm_many walks
+//                the non-empty 64-column groups of X and CB themselves, with
+//                the weight codes of non-outlier columns masked to zero, so no
+//                operand is gathered.
+// The workspace therefore holds gathered operands of at most kCompactMaxLd
+// columns: it grows with T and N, not with T*K or N*K.
+enum { kOutFew = 0, kOutCompact = 1, kOutDense = 2 };
+constexpr int64_t kCompactMaxLd = 1024;
+// The outlier-set summary in the workspace: int32 info[kInfoWords] =
+// {n, ng, mode}.
+constexpr int kInfoWords = 4;
+
 // Row stride, in halves, of the gathered outlier operands x_out [T, ld] and
 // w_out [N, ld]; the rows are zero-padded up to it.  Up to 32 outliers: 32
 // (the GEMM epilogue's two 16-deep fp16 MFMA steps); more: a multiple of 64
@@ -58,6 +79,17 @@ __device__ __forceinline__ uint16_t dequant_w(int cb, float scb)
     return f2h(((float)cb * scb) / 127.0f);
 }
 
+// The same value through r = fp32(scb / 127), computed once per column:
+// fp32(cb * r) is within 2^-23 (two roundings) of cb * scb / 127 relative to
+// it, while that value -- cb * m * 2^e / 127 for the binary16 scb = m * 2^e,
+// never a binary16 midpoint since 127 is prime -- lies at least about 2^-18
+// relative from every binary16 midpoint; so both round to the same fp16.
+// (Exhaustive check over every code and binary16 scale on the CPU.)
+__device__ __forceinline__ uint16_t dequant_w_r(int cb, float r)
+{
+    return f2h((float)cb * r);
+}
+
 // Zero-point variant: the fp16 weight fp16(fp32(cb + zp) / nd) of code cb
 // in a column with parameters (nd, zp); 0 when nd = 0 (an all-zero column).
 // cb + zp is an integer of at most 9 bits, exact in fp32; one correctly
@@ -65,6 +97,24 @@ __device__ __forceinline__ uint16_t dequant_w(int cb, float scb)
 __device__ __forceinline__ uint16_t dequant_w_zp(int cb, int zp, float nd)
 {
     return nd > 0.0f ? f2h((float)(cb + zp) / nd) : (uint16_t)0;
+}
+
+// The same value through rinv = fp32(1 / nd), computed once per column.
+// q = fp32((cb + zp) * rinv) is within 3 fp32 ulps of fp32((cb + zp) / nd)
+// (three roundings of at most 2^-24 each, relative); both round to the same
+// fp16 unless a binary16 midpoint -- an fp32 value whose low 13 bits are
+// 0x1000 in the normal binary16 range -- lies within that distance of q, or q
+// is below the normal binary16 range.  Only then is the correctly rounded
+// division taken.
+__device__ __forceinline__ uint16_t dequant_w_zp_r(int cb, int zp, float nd, float rinv)
+{
+    if (!(nd > 0.0f))
+        return 0;
+    const float m = (float)(cb + zp);
+    const float q = m * rinv;
+    const unsigned b = __builtin_bit_cast(unsigned, q) & 0x7fffffffu;
+    const bool near = b < 0x38800000u ? b != 0u : ((b & 0x1fffu) - 0x0ffbu) <= 10u;
+    return f2h(near ? m / nd : q);
 }
 
 // FP8 (E5M2) variant.  An E5M2 code is the high byte of the binary16 with
@@ -110,34 +160,73 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
     return v;
 }
 
-// Workspace segments of one llmint8_matmul call (byte offsets from the base).
+// Compute units of the current device (queried once per device).
+int compute_units();
+
+// Workspace segments of one llmint8_matmul call (byte offsets from the base);
+// decode: the weight-streaming path's layout (no gathered weight operand,
+// x_out for any outlier count).
 struct MatmulWorkspace {
-    size_t partial, mask, chunk_pre, outlier_idx, n_outliers, row_absmax, row_zp, xq, x_out, w_out,
-        total;
+    size_t mask, groups, outlier_idx, info, row_absmax, row_zp, xq, x_out, w_out, total;
 };
-MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N);
+MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N, bool decode);
 size_t act_workspace_bytes(int64_t K);
 
 // ---- launchers (each enqueues on `s`; return hipGetLastError()) ----
 hipError_t launch_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N, int8_t *CB,
                                   float *SCB, hipStream_t s);
 
-// What the row-quantization launch needs to also produce the dequantized
-// outlier weight rows for the GEMM: w_out[n, j] = fp16(CB[n,O[j]]*SCB[n]/127),
-// zero for n_outliers <= j < outlier_ld(n_outliers), which is also the row
-// stride.  w_out == null skips it.
+// What the row-quantization launch needs for the GEMM path's outlier weight
+// operand (w_out == null: not the GEMM path).  kOutFew: w_out[n, j] =
+// fp16(CB[n,O[j]]*SCB[n]/127) for j < n_outliers, zero up to 32, row stride
+// 32 halves; kOutCompact: w_out[n, j] = the code CB[n,O[j]] (int8), zero up
+// to outlier_ld(n_outliers), which is the row stride; kOutDense: nothing.
 struct GatherArgs {
     const int8_t *CB;
     const float *SCB;   // zero-point variant: nd of each column; FP8: scale 2^-e
     int64_t N;
-    uint16_t *w_out;
+    void *w_out;
     const int32_t *zp = nullptr;   // zero-point variant: zp of each column (else null)
     bool f8 = false;               // FP8 variant: CB holds E5M2 codes
 };
 
-// Row ranges of the outlier detection: the partial-flag buffer holds
-// kDetectSplits bytes per 8-column chunk (kDetectSplits * K/8 bytes).
-constexpr int kDetectSplits = 16;
+// Where the row quantization puts the outlier-set summary: info (n, ng,
+// mode; info[0] is n_out) and the ascending list of non-empty 64-column
+// groups (groups, K/64 entries).  groups null: only n and the outlier list
+// are written.
+struct OutlierInfoOut {
+    int32_t *info;
+    int32_t *groups = nullptr;
+    uint8_t *mask = nullptr;   // GEMM path: the combined flags (dense mode only)
+};
+
+// The detection area `mask` of a call (detect_area_bytes(K)): the combined
+// flags of every 8-column chunk (K/8 bytes, written by the row quantization
+// for the GEMM kernel when it reads X in place), then nr flag sets (one per
+// row range, `pitch` bytes apart) that k_detect writes and every
+// row-quantization block ORs.  nr > 1 when K is narrow, so the detection
+// launch still has about a workgroup per compute unit; each range holds at
+// least 256 rows.
+struct DetectFlags {
+    const uint8_t *parts;
+    int nr, pitch;
+};
+constexpr int kDetectMaxRanges = 8;
+__host__ __device__ inline int64_t detect_pitch(int64_t K) { return (K / 8 + 15) / 16 * 16; }
+inline size_t detect_area_bytes(int64_t K)
+{
+    const size_t a = ((size_t)K / 8 + 255) & ~(size_t)255;
+    return a + (((size_t)kDetectMaxRanges * detect_pitch(K) + 255) & ~(size_t)255);
+}
+inline DetectFlags detect_flags(uint8_t *mask, int64_t T, int64_t K)
+{
+    int nr = 1;
+    while (nr < kDetectMaxRanges && K / 64 * nr * 2 <= 256 && T >= 256 * nr * 2)
+        nr *= 2;
+    const size_t a = ((size_t)K / 8 + 255) & ~(size_t)255;
+    return DetectFlags{mask + a, nr, (int)detect_pitch(K)};
+}
+
 // The row quantization takes a wavefront per row from kRowQuantWaveMinT rows
 // on when the rows are at most kRowQuantWaveMaxK long (measured on MI355X:
 // 15 vs 20 us at 2048 x 2048, equal at 4096 x 4096); otherwise a block of
@@ -146,16 +235,21 @@ constexpr int kDetectSplits = 16;
 constexpr int64_t kRowQuantWaveMinT = 256;
 constexpr int64_t kRowQuantWaveMaxK = 4096;
 
-// Outlier detection + compaction + row quantization (+ the optional outlier
-// weight gather).  x_out (fp16 [T, outlier_ld(n)]) receives the gathered
-// outlier columns, zero-padded, when non-null.  xq_packed (T <= 16 only) writes Xq in the decode kernel's
-// fragment order [K/64][4][16][16] (16*K bytes; rows >= T are left as they
-// are) instead of row-major [T, K].
+// Outlier detection (k_detect: the flags of every 8-column chunk into the
+// detection area `mask`, see DetectFlags), then one launch that quantizes the rows and, in every block,
+// derives the outlier set from those flags itself (block 0 writes the outlier list and the
+// summary `io`), plus the GEMM path's outlier weight gather (g.w_out).
+// x_out (fp16 [T, outlier_ld(n)]) receives the gathered outlier columns,
+// zero-padded, when non-null: on the decode path (xq_packed or
+// !g.w_out) for every outlier count, on the GEMM path unless the mode is
+// kOutDense.  On the GEMM path nothing is written for a row when every
+// column is an outlier (the int8 part is then zero).  xq_packed (T <= 16
+// only) writes Xq in the decode kernel's fragment order [K/64][4][16][16]
+// (16*K bytes; rows >= T are left as they are) instead of row-major [T, K].
 hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
-                               int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
-                               uint8_t *partial, uint8_t *mask, int32_t *chunk_pre,
-                               uint16_t *x_out, const GatherArgs &g, bool xq_packed,
-                               hipStream_t s);
+                               int8_t *Xq, float *a, int32_t *O, const OutlierInfoOut &io,
+                               uint8_t *mask, uint16_t *x_out, const GatherArgs &g,
+                               bool xq_packed, hipStream_t s);
 
 // The same quantization for few rows in one launch of T blocks and without
 // workspace (each block derives the outlier set from all rows itself): one
@@ -173,9 +267,9 @@ struct EpilogueArgs {
     const float *a;          // [T] row absmax (zero-point variant: nd of each row)
     const float *scb;        // [N] (zero-point variant: nd of each column)
     const uint16_t *x_out;   // [T, outlier_ld(n)] gathered outlier activations (fp16)
-    const uint16_t *w_out;   // [N, outlier_ld(n)] dequantized outlier weights (fp16), GEMM path
+    const void *w_out;       // GEMM path: kOutFew fp16 [N,32], kOutCompact int8 codes [N,ld]
     const int32_t *O;        // [n] outlier column indices (weight-streaming path)
-    const int32_t *n_out;    // device scalar n
+    const int32_t *n_out;    // outlier-set summary {n, ng, mode} (weight-streaming path: n)
     const uint16_t *bias;    // [N] or null
     uint16_t *out;           // [T, N] fp16
     int32_t *c_i32;          // [T, N] raw accumulators (debug epilogue) or null
@@ -189,6 +283,11 @@ struct EpilogueArgs {
     // FP8 variant: Xq and CB hold E5M2 codes, a and scb the scales 2^-e of
     // the rows and columns; the products are summed in fp32 by fp8 MFMAs.
     bool f8 = false;
+    // GEMM path, kOutDense: the activations, the chunk flags and the
+    // non-empty 64-column groups
+    const uint16_t *X = nullptr;
+    const uint8_t *mask = nullptr;
+    const int32_t *groups = nullptr;
 };
 
 // Zero-point variant (the asymmetric quantizer of the LLM.int8() summary,
@@ -204,15 +303,14 @@ hipError_t launch_quantize_weight_zp(const uint16_t *W_t, int64_t K, int64_t N, 
 // Activations: as launch_quantize_act, but the non-outlier part of each row
 // zero-point quantized (nd[t]; row_zp[t] = {zp, sum of the row's K codes});
 // outlier columns hold the code of 0, -zp.  g.zp must be set when g.w_out
-// is (the outlier weight rows are then dequantized as fp16((cb+zp)/nd)).
-// Without w_out and for the shapes of quantize_act_fits_rows it is one
-// launch (the few-rows kernel), else detection, compaction and a block per
-// row.
+// is (the kOutFew outlier weight rows are then dequantized as
+// fp16((cb+zp)/nd)).  Without w_out and for the shapes of
+// quantize_act_fits_rows it is one launch (the few-rows kernel), else
+// detection and a block per row.
 hipError_t launch_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K, float threshold,
                                   int8_t *Xq, float *nd, int2 *row_zp, int32_t *O,
-                                  int32_t *n_out, uint8_t *partial, uint8_t *mask,
-                                  int32_t *chunk_pre, uint16_t *x_out, const GatherArgs &g,
-                                  bool xq_packed, hipStream_t s);
+                                  const OutlierInfoOut &io, uint8_t *mask, uint16_t *x_out,
+                                  const GatherArgs &g, bool xq_packed, hipStream_t s);
 
 // FP8 variant (E5M2, the 5-bit-exponent, 2-bit-fraction format the
 // LLM.int8() summary names under "Related work"): per vector a power-of-two
@@ -224,10 +322,9 @@ hipError_t launch_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N, 
 // Activations: as launch_quantize_act (same kernels with the E5M2 codes;
 // sc receives the row scales 2^-e); g.f8 must be set when g.w_out is.
 hipError_t launch_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float threshold,
-                                  uint8_t *Xq8, float *sc, int32_t *O, int32_t *n_out,
-                                  uint8_t *partial, uint8_t *mask, int32_t *chunk_pre,
-                                  uint16_t *x_out, const GatherArgs &g, bool xq_packed,
-                                  hipStream_t s);
+                                  uint8_t *Xq8, float *sc, int32_t *O, const OutlierInfoOut &io,
+                                  uint8_t *mask, uint16_t *x_out, const GatherArgs &g,
+                                  bool xq_packed, hipStream_t s);
 
 // ev0/ev1 (optional) are recorded on s right before and after the main kernel.
 hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,

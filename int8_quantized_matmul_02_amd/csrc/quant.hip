@@ -221,120 +221,112 @@ __global__ __launch_bounds__(kBlock) void k_quantize_weight_f8(const uint16_t *_
 }
 
 // ---------------------------------------------------------------------------
-// Outlier-column detection, in two launches and without atomics or a
-// clearing pass.  k_detect splits the rows into kDetectSplits ranges; a lane
-// keeps the running column maxima of |x| of 8 columns over its rows, the
-// flags "maximum above the threshold" are ORed over the block's row groups
-// and written as byte partial[chunk * kDetectSplits + split] (every byte is
-// written, also for empty ranges).  k_compact ORs the 16 bytes of a chunk.
-// The comparison |x| > threshold is done on binary16 bit patterns against the
-// largest binary16 value not above the threshold (computed on the host), which
-// is the same test as comparing the exact values.
+// Outlier-column detection in one launch, without atomics or a clearing
+// pass.  A block takes one 64-column slice (a 128-byte line of every row: 8
+// lanes per row, a lane owns one 8-column chunk) over one of nr row ranges;
+// each lane keeps the running maxima of |x| of its chunk over every 128th
+// row of the range (8 rows' loads in flight), and the flags "maximum above
+// the threshold" are ORed over the block into the 8 chunk bytes of the
+// slice in the range's flag set (parts + r * pitch).  The consumers OR the nr
+// sets (nr > 1 only when K is narrow: more blocks to fill the chip).  The
+// comparison |x| > threshold is done on binary16 bit patterns against the
+// largest binary16 value not above the threshold (computed on the host),
+// which is the same test as comparing the exact values.
 // ---------------------------------------------------------------------------
 constexpr int kDetectThreads = 1024;
-constexpr int kDetectRowGroups = kDetectThreads / 32;   // 32 lanes (chunks) per row group
+constexpr int kDetectRowsPerPass = kDetectThreads / 8;   // 8 lanes (one line) per row
 
 __global__ __launch_bounds__(kDetectThreads) void k_detect(const uint16_t *__restrict__ X,
-                                                           int64_t T, int64_t K,
-                                                           unsigned thr_bits, int64_t rows_per,
-                                                           uint8_t *__restrict__ partial)
+                                                           int64_t T, int64_t K, int nr,
+                                                           int pitch, unsigned thr_bits,
+                                                           uint8_t *__restrict__ parts)
 {
-    // byte rg of chunk lane c at s_bits[c * kDetectRowGroups + rg]
-    __shared__ unsigned s_bits[32 * kDetectRowGroups / 4];
-    const int c = threadIdx.x & 31, rg = threadIdx.x >> 5;
-    const int64_t col8 = (int64_t)blockIdx.x * 32 + c;    // 8-column chunk
-    const int64_t nchunk = K / 8;
-    const int64_t r0 = (int64_t)blockIdx.y * rows_per;
-    const int64_t r1 = r0 + rows_per < T ? r0 + rows_per : T;
-    unsigned bits = 0;
-    if (col8 < nchunk) {
-        constexpr int kRowsInFlight = 8;
-        uint4 cm = make_uint4(0u, 0u, 0u, 0u);
-        for (int64_t t0 = r0 + rg; t0 < r1; t0 += kRowsInFlight * kDetectRowGroups) {
-            uint4 v[kRowsInFlight];
-#pragma unroll
-            for (int u = 0; u < kRowsInFlight; ++u) {
-                const int64_t t = t0 + (int64_t)u * kDetectRowGroups;
-                v[u] = t < r1 ? *reinterpret_cast<const uint4 *>(X + t * K + col8 * 8)
-                              : make_uint4(0u, 0u, 0u, 0u);   // |0| is never above
-            }
-#pragma unroll
-            for (int u = 0; u < kRowsInFlight; ++u)
-                cm = colmax8(cm, v[u]);
-        }
-        bits = flags8(cm, thr_bits);
-    }
-    reinterpret_cast<uint8_t *>(s_bits)[c * kDetectRowGroups + rg] = (uint8_t)bits;
-    __syncthreads();
-    if (rg == 0 && col8 < nchunk) {
-        unsigned o = 0;
-#pragma unroll
-        for (int w = 0; w < kDetectRowGroups / 4; ++w)
-            o |= s_bits[c * (kDetectRowGroups / 4) + w];
-        o |= o >> 16;
-        o |= o >> 8;
-        partial[col8 * kDetectSplits + blockIdx.y] = (uint8_t)(o & 0xffu);
-    }
-}
-
-// The OR of a chunk's kDetectSplits partial bytes: its 8 outlier flags.
-__device__ __forceinline__ unsigned chunk_flags(const uint8_t *__restrict__ partial, int64_t c)
-{
-    static_assert(kDetectSplits == 16, "one 16-byte load per chunk");
-    const uint4 p = *reinterpret_cast<const uint4 *>(partial + c * kDetectSplits);
-    unsigned o = p.x | p.y | p.z | p.w;
-    o |= o >> 16;
-    o |= o >> 8;
-    return o & 0xffu;
-}
-
-constexpr int kCompactThreads = 1024;
-constexpr int kMaxChunks = 133144 / 8 + 1;   // K/8 for the largest K
-
-// One block.  Every thread ORs the partial bytes of its chunks (one 16-byte
-// load each, all independent) into an LDS flag byte; then mask[b] = the flags
-// of 8-column chunk b, the ascending outlier list O, its length n, and
-// chunk_pre[b] = the number of outlier columns before chunk b (the position
-// of its first one in O).  Each thread owns a contiguous run of chunks so a
-// block-wide exclusive scan of the per-thread counts gives the positions.
-__global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__restrict__ partial,
-                                                             int64_t K,
-                                                             uint8_t *__restrict__ mask,
-                                                             int32_t *__restrict__ O,
-                                                             int32_t *__restrict__ n_out,
-                                                             int32_t *__restrict__ chunk_pre)
-{
-    __shared__ uint8_t s_fl[kMaxChunks];
-    __shared__ int wave_tot[kCompactThreads / kWave];
+    __shared__ uint2 s_or[kDetectThreads / kWave];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    // 32-bit indexing: K <= 133144 keeps every count here far below 2^31
-    const int nchunk = (int)(K / 8);
-    constexpr int kBatch = 4;   // independent loads in flight per thread
-    for (int base = tid; base < nchunk; base += kBatch * kCompactThreads) {
-        unsigned f[kBatch];
+    const int64_t nslice = K / 64;
+    const int64_t slice = blockIdx.x % nslice;
+    const int r = (int)(blockIdx.x / nslice);
+    const int64_t rows = (T + nr - 1) / nr;
+    const int64_t t_begin = r * rows, t_end = t_begin + rows < T ? t_begin + rows : T;
+    const uint16_t *col = X + slice * 64 + 8 * (tid % 8);
+    constexpr int kRowsInFlight = 8;
+    uint4 cm = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t t0 = t_begin + tid / 8; t0 < t_end; t0 += kRowsInFlight * kDetectRowsPerPass) {
+        uint4 v[kRowsInFlight];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int c = base + u * kCompactThreads;
-            f[u] = c < nchunk ? chunk_flags(partial, c) : 0u;
+        for (int u = 0; u < kRowsInFlight; ++u) {
+            const int64_t t = t0 + (int64_t)u * kDetectRowsPerPass;
+            v[u] = t < t_end ? *reinterpret_cast<const uint4 *>(col + t * K)
+                             : make_uint4(0u, 0u, 0u, 0u);   // |0| is never above
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int c = base + u * kCompactThreads;
-            if (c < nchunk)
-                s_fl[c] = (uint8_t)f[u];
-        }
+        for (int u = 0; u < kRowsInFlight; ++u)
+            cm = colmax8(cm, v[u]);
     }
+    unsigned bits = flags8(cm, thr_bits);
+    // OR over the lanes of one chunk (equal lane % 8) in the wavefront; chunk
+    // c's byte then sits in lane c, and is shifted into place
+    bits |= __shfl_xor(bits, 8, kWave);
+    bits |= __shfl_xor(bits, 16, kWave);
+    bits |= __shfl_xor(bits, 32, kWave);
+    const int c = lane & 7;
+    unsigned lo = c < 4 ? bits << (8 * c) : 0u, hi = c < 4 ? 0u : bits << (8 * (c - 4));
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+        lo |= __shfl_xor(lo, off, kWave);
+        hi |= __shfl_xor(hi, off, kWave);
+    }
+    if (lane == 0)
+        s_or[wave] = make_uint2(lo, hi);
     __syncthreads();
-    const int per = (nchunk + kCompactThreads - 1) / kCompactThreads;
-    const int b0 = tid * per < nchunk ? tid * per : nchunk;
-    const int b1 = b0 + per < nchunk ? b0 + per : nchunk;
-    int cnt = 0;
-    for (int b = b0; b < b1; ++b) {
-        const unsigned m = s_fl[b];
-        mask[b] = (uint8_t)m;
-        cnt += __builtin_popcount(m);
+    if (tid == 0) {
+        uint2 o = make_uint2(0u, 0u);
+#pragma unroll
+        for (int w = 0; w < kDetectThreads / kWave; ++w) {
+            o.x |= s_or[w].x;
+            o.y |= s_or[w].y;
+        }
+        *reinterpret_cast<uint2 *>(parts + (int64_t)r * pitch + slice * 8) = o;
     }
-    int inc = cnt;
+}
+
+// ---------------------------------------------------------------------------
+// The outlier set from the detection flags, derived by every block of the
+// row-quantization launch itself (no compaction launch): a block copies the
+// K/8 flag bytes (from L2) into LDS and reduces them to n; the positions of
+// the outlier columns follow from a block scan of the flags' population
+// counts in column order.  Every block computes the same values; block 0 also
+// writes the outlier list and the summary for the kernels after it.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Sum over the block's kBlock threads; s_red: kWavesPerBlock ints of LDS not
+// in use by another reduction that may still be read.
+__device__ __forceinline__ int block_sum(int v, int *s_red)
+{
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    v = wave_sum(v);
+    if (lane == 0)
+        s_red[wave] = v;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w)
+        t += s_red[w];
+    return t;
+}
+
+// Exclusive prefix sum in thread order over the block; s_red as block_sum.
+__device__ __forceinline__ int block_excl_scan(int v, int *s_red)
+{
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    int inc = v;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const int o = __shfl_up(inc, off, kWave);
@@ -342,33 +334,187 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(const uint8_t *__re
             inc += o;
     }
     if (lane == kWave - 1)
-        wave_tot[wave] = inc;
+        s_red[wave] = inc;
     __syncthreads();
-    int j = inc - cnt;
-    for (int w = 0; w < wave; ++w)
-        j += wave_tot[w];
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w)
+        before += w < wave ? s_red[w] : 0;
+    return before + inc - v;
+}
+
+struct OutlierSet {
+    int n;      // |O|
+    int ng;     // non-empty 64-column groups (only computed when n > kOutlierPad)
+    int mode;   // kOutFew / kOutCompact / kOutDense
+};
+
+// The GEMM path's way of forming the outlier product (see internal.h):
+// compact while the padded outlier rows are short and not much shorter than
+// the groups that hold them would be.
+__device__ __forceinline__ int outlier_mode(int n, int ng)
+{
+    if (n <= kOutlierPad)
+        return kOutFew;
+    const int64_t ld = outlier_ld(n);
+    return (ld > kCompactMaxLd || (int64_t)ng * 64 <= ld + ld / 4) ? kOutDense : kOutCompact;
+}
+
+// All threads: s_fl[c] = the outlier flags of chunk c (bit i: column 8c+i),
+// for every chunk, the OR of the detection's flag sets (16 chunks per load);
+// returns the block-uniform summary.  s_red: 2 * kWavesPerBlock ints.  Ends
+// with the flags visible to the whole block.
+__device__ __forceinline__ OutlierSet derive_outliers(const DetectFlags &df, int nchunk,
+                                                      uint8_t *s_fl, int *s_red)
+{
+    int cnt = 0;
+    // K % 64 == 0: nchunk is a multiple of 8; whole 16-byte pieces, then a tail
+    // (the pitch is a multiple of 16)
+    for (int c = 16 * threadIdx.x; c < nchunk; c += 16 * kBlock) {
+        const uint8_t *p = df.parts + c;
+        if (c + 16 <= nchunk) {
+            uint4 f = *reinterpret_cast<const uint4 *>(p);
+            for (int r = 1; r < df.nr; ++r) {
+                const uint4 g = *reinterpret_cast<const uint4 *>(p + (int64_t)r * df.pitch);
+                f = make_uint4(f.x | g.x, f.y | g.y, f.z | g.z, f.w | g.w);
+            }
+            *reinterpret_cast<uint4 *>(s_fl + c) = f;
+            cnt += __builtin_popcount(f.x) + __builtin_popcount(f.y) + __builtin_popcount(f.z) +
+                   __builtin_popcount(f.w);
+        } else {
+            uint2 f = *reinterpret_cast<const uint2 *>(p);
+            for (int r = 1; r < df.nr; ++r) {
+                const uint2 g = *reinterpret_cast<const uint2 *>(p + (int64_t)r * df.pitch);
+                f = make_uint2(f.x | g.x, f.y | g.y);
+            }
+            *reinterpret_cast<uint2 *>(s_fl + c) = f;
+            cnt += __builtin_popcount(f.x) + __builtin_popcount(f.y);
+        }
+    }
+    OutlierSet o;
+    o.n = block_sum(cnt, s_red);   // its barrier publishes s_fl
+    o.ng = 0;
+    if (o.n > kOutlierPad) {
+        int g = 0;
+        for (int q = threadIdx.x; q < nchunk / 8; q += kBlock)
+            g += *reinterpret_cast<const uint2 *>(s_fl + 8 * q) != make_uint2(0u, 0u) ? 1 : 0;
+        o.ng = block_sum(g, s_red + kWavesPerBlock);
+    }
+    o.mode = outlier_mode(o.n, o.ng);
+    return o;
+}
+
+// All threads: from the flags, s_pre8[q] = the number of outlier columns
+// before 64-column group q (chunks 8q .. 8q+7; when s_pre8 is non-null) and
+// O[j] = the j-th outlier column for j < cap (when O is non-null; global
+// memory or LDS).  Each thread walks a contiguous run of chunks.  s_red:
+// kWavesPerBlock ints.
+__device__ __forceinline__ void outlier_positions(const uint8_t *s_fl, int nchunk, int *s_pre8,
+                                                  int32_t *O, int cap, int *s_red)
+{
+    const int per = (nchunk + kBlock - 1) / kBlock;
+    const int b0 = min((int)threadIdx.x * per, nchunk), b1 = min(b0 + per, nchunk);
+    int cnt = 0;
+    for (int b = b0; b < b1; ++b)
+        cnt += __builtin_popcount(s_fl[b]);
+    int j = block_excl_scan(cnt, s_red);
     for (int b = b0; b < b1; ++b) {
         const unsigned m = s_fl[b];
-        chunk_pre[b] = j;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if ((m >> i) & 1u)
-                O[j++] = b * 8 + i;
+        if (s_pre8 && (b & 7) == 0)
+            s_pre8[b >> 3] = j;
+        if (O) {
+            for (int i = 0; i < 8; ++i)
+                if ((m >> i) & 1u) {
+                    if (j < cap)
+                        O[j] = 8 * b + i;
+                    ++j;
+                }
+        } else {
+            j += __builtin_popcount(m);
+        }
     }
-    if (tid == kCompactThreads - 1)
-        *n_out = j;
 }
+
+// The position of chunk c's first outlier column in the compact row: the
+// group's prefix plus the flags of the group's chunks before c.
+__device__ __forceinline__ int chunk_pos(const uint8_t *s_fl, const int *s_pre8, int c)
+{
+    const int q = c >> 3;
+    const unsigned long long g = *reinterpret_cast<const unsigned long long *>(s_fl + 8 * q);
+    const unsigned long long below = (c & 7) ? (1ull << (8 * (c & 7))) - 1ull : 0ull;
+    return s_pre8[q] + __popcll(g & below);
+}
+
+// Block 0's part: the summary {n, ng, mode} and (when requested, in dense
+// mode) the combined flags and the ascending list of non-empty 64-column
+// groups.
+__device__ __forceinline__ void write_outlier_info(const uint8_t *s_fl, int nchunk,
+                                                   const OutlierSet &os, const OutlierInfoOut &io,
+                                                   int *s_red)
+{
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        io.info[0] = os.n;
+        if (io.groups) {
+            io.info[1] = os.ng;
+            io.info[2] = os.mode;
+        }
+    }
+    if (io.mask && os.mode == kOutDense) {
+        // the OR of the flag sets, for the GEMM kernel's dense mode
+        for (int c = 16 * tid; c < nchunk; c += 16 * kBlock) {
+            if (c + 16 <= nchunk)
+                *reinterpret_cast<uint4 *>(io.mask + c) = *reinterpret_cast<const uint4 *>(s_fl + c);
+            else
+                *reinterpret_cast<uint2 *>(io.mask + c) = *reinterpret_cast<const uint2 *>(s_fl + c);
+        }
+    }
+    if (io.groups && os.mode == kOutDense) {
+        const int ngrp = nchunk / 8;
+        const int per = (ngrp + kBlock - 1) / kBlock;
+        const int q0 = min(tid * per, ngrp), q1 = min(q0 + per, ngrp);
+        int cnt = 0;
+        for (int q = q0; q < q1; ++q)
+            cnt += *reinterpret_cast<const uint2 *>(s_fl + 8 * q) != make_uint2(0u, 0u) ? 1 : 0;
+        int j = block_excl_scan(cnt, s_red);
+        for (int q = q0; q < q1; ++q)
+            if (*reinterpret_cast<const uint2 *>(s_fl + 8 * q) != make_uint2(0u, 0u))
+                io.groups[j++] = q;
+    }
+}
+
+// Dynamic LDS of the row-quantization kernels: the chunk flags, then either
+// the 64-column group prefix counts (a row's gathered outlier positions) or a
+// gather block's outlier list (at most kCompactMaxLd entries): at most
+// 16.7 + 8.3 KB at the largest K.
+__host__ __device__ __forceinline__ int64_t flags_lds_bytes(int64_t nchunk)
+{
+    return (nchunk + 15) / 16 * 16;
+}
+__host__ __forceinline__ size_t rowquant_lds_bytes(int64_t K)
+{
+    const int64_t nchunk = K / 8;
+    const int64_t aux = nchunk / 8 > kCompactMaxLd ? nchunk / 8 : kCompactMaxLd;
+    return (size_t)(flags_lds_bytes(nchunk) + 4 * aux);
+}
+
+// What a row-quantization launch is for: the public activation quantizer (no
+// gathered outlier operands), the weight-streaming path (x_out for every
+// outlier count) or the GEMM path (x_out unless kOutDense; nothing at all
+// for a row when every column is an outlier).
+enum { kForAct = 0, kForDecode = 1, kForGemm = 2 };
 
 // ---------------------------------------------------------------------------
 // Row quantization: one 256-thread block per row t (so that even a handful of
-// rows keeps many lanes busy).  The row is read once into registers (NC
-// 16-byte chunks per thread; NC = 0 re-reads it from cache for very long
-// rows), its absmax over the non-outlier columns is reduced with shuffles and
-// LDS, then the int8 row is packed with outlier columns as 0, and the outlier
-// values are gathered into the compact fp16 row x_out[t, .] (row stride
-// outlier_ld(n), zero-padded): the outlier columns of chunk c start at
-// chunk_pre[c], loaded once per such chunk while the absmax is reduced.
-// Chunks without outlier columns (nearly all of them) take a branch-free path.
+// rows keeps many lanes busy).  The block first derives the outlier set (see
+// derive_outliers), then reads its row once into registers (NC 16-byte
+// chunks per thread; NC = 0 re-reads it from cache for very long rows),
+// reduces its absmax over the non-outlier columns with shuffles and LDS,
+// packs the int8 row with outlier columns as 0, and gathers the outlier
+// values into the compact fp16 row x_out[t, .] (row stride outlier_ld(n),
+// zero-padded): the outlier columns of chunk c start at the chunk's prefix
+// count.  Chunks without outlier columns (nearly all of them) take a
+// branch-free path.
 // ---------------------------------------------------------------------------
 // The 8 values of a chunk whose columns are all outliers: they sit at
 // consecutive positions p0 .. p0+7 of the compact row.
@@ -429,20 +575,17 @@ __device__ __forceinline__ uint2 *xq_chunk(int8_t *Xq, int64_t t, int64_t K, int
     return reinterpret_cast<uint2 *>(Xq + off);
 }
 
-// Dequantized outlier weight rows for the GEMM, w_out[r, j] = fp16(CB[r, O[j]]
-// * SCB[r] / 127), zero up to outlier_ld(n): blocks gb = 0 .. nb-1 of a
-// launch share the N rows.  Up to 32 outliers (one 32-half row each) a lane
-// takes one 8-column group of one row, 16 rows per wavefront, and computes
-// its at most 8 values directly.  More outliers: one wavefront per row, which
-// first tabulates the row's 255 possible values in LDS (tab, 256 entries of
-// this wavefront); each lane then gathers 8 consecutive outlier columns and
-// stores them at once.  (LDS operations of one wavefront complete in order,
-// so the table is complete before any lane reads it, and the reads of one
-// row are done before the next row's table overwrites it.)  Entries of O at
-// or past n are stale: column 0 is read in their place and the value is 0.
+// The GEMM path's outlier weight operand, built by the blocks gb = 0 .. nb-1
+// past the row blocks of a row-quantization launch, which share the N weight
+// rows (see GatherArgs).  s_O holds the first min(n, kCompactMaxLd) outlier
+// columns (LDS).  kOutFew: a lane takes one 8-column group of one row, 16
+// rows per wavefront, and dequantizes its at most 8 values.  kOutCompact: a
+// wavefront per row, a lane gathers the codes of 8 consecutive outlier
+// columns (one 8-byte load when they are 8 aligned consecutive columns) and
+// stores them at once; past n the row holds zeros.  kOutDense: nothing.
 // kMode 0: absmax.  1, zero-point variant: SCB holds each row's nd, ZP its
-// zp, and the values are fp16((cb + zp) / nd).  2, FP8 variant: the bytes
-// are E5M2 codes and SCB the scales 2^-e.
+// zp, and the kOutFew values are fp16((cb + zp) / nd).  2, FP8 variant: the
+// bytes are E5M2 codes and SCB the scales 2^-e.
 constexpr int kModeAbsmax = 0, kModeZp = 1, kModeF8 = 2;
 template <int kMode>
 __device__ __forceinline__ uint16_t dequant_row(int cb, float sc, int zp)
@@ -457,24 +600,23 @@ __device__ __forceinline__ uint16_t dequant_row(int cb, float sc, int zp)
 
 template <int kMode = kModeAbsmax>
 __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
-                                             const int32_t *__restrict__ n_out,
+                                             const OutlierSet &os, const int *s_O,
                                              const int8_t *__restrict__ CB,
-                                             const float *__restrict__ SCB,
-                                             const int32_t *__restrict__ O, int64_t N,
-                                             uint16_t *__restrict__ w_out, uint16_t *tab,
+                                             const float *__restrict__ SCB, int64_t N,
+                                             void *__restrict__ w_out,
                                              const int32_t *__restrict__ ZP = nullptr)
 {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int n = *n_out;
-    const int64_t ldo = outlier_ld(n);
-    if (ldo == kOutlierPad) {
+    const int n = os.n;
+    if (os.mode == kOutFew) {
+        uint16_t *wo = static_cast<uint16_t *>(w_out);
         constexpr int kGroups = kOutlierPad / 8, kRowsPerWave = kWave / kGroups;
         const int g = lane % kGroups;
         int o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int j = 8 * g + e;   // < 32 <= K: in bounds of O
-            o[e] = j < n ? O[j] : 0;
+            const int j = 8 * g + e;
+            o[e] = j < n ? s_O[j] : 0;
         }
         for (int64_t r = (gb * kWavesPerBlock + wave) * kRowsPerWave + lane / kGroups; r < N;
              r += nb * kWavesPerBlock * kRowsPerWave) {
@@ -487,99 +629,135 @@ __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
                 const unsigned v = dequant_row<kMode>(cbr[o[e]], sc, zr);
                 h[e] = 8 * g + e < n ? v : 0u;
             }
-            *reinterpret_cast<uint4 *>(w_out + r * kOutlierPad + 8 * g) =
+            *reinterpret_cast<uint4 *>(wo + r * kOutlierPad + 8 * g) =
                 make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                            h[6] | (h[7] << 16));
         }
         return;
     }
+    if (os.mode != kOutCompact)
+        return;
+    int8_t *wo = static_cast<int8_t *>(w_out);
+    const int64_t ldo = outlier_ld(n);   // <= kCompactMaxLd
     for (int64_t r = gb * kWavesPerBlock + wave; r < N; r += nb * kWavesPerBlock) {
-        const float sc = SCB[r];
-        const int zr = kMode == kModeZp ? ZP[r] : 0;
-        // table index: code + 127 of an int8 code (255 entries), or the E5M2
-        // code itself (256)
-        constexpr int kBias = kMode == kModeF8 ? 0 : 127;
-        for (int i = lane; i < 256 - (kBias ? 1 : 0); i += kWave)
-            tab[i] = dequant_row<kMode>(i - kBias, sc, zr);
         const int8_t *cbr = CB + r * K;
-        for (int64_t j0 = 8 * lane; j0 < ldo; j0 += 8 * kWave) {
-            const int4 o0 = *reinterpret_cast<const int4 *>(O + j0);
-            const int4 o1 = *reinterpret_cast<const int4 *>(O + j0 + 4);
-            const int o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-            unsigned h[8];
-            if (j0 + 8 <= n && o[7] == o[0] + 7 && (o[0] & 7) == 0) {
-                // 8 consecutive outlier columns (every column, at threshold 0):
-                // one 8-byte load of the weight row (8-byte aligned; K % 64 == 0)
-                const uint2 raw = *reinterpret_cast<const uint2 *>(cbr + o[0]);
+        for (int j0 = 8 * lane; j0 < ldo; j0 += 8 * kWave) {
+            unsigned b[8];
+            if (j0 + 8 <= n && s_O[j0 + 7] == s_O[j0] + 7 && (s_O[j0] & 7) == 0) {
+                const uint2 raw = *reinterpret_cast<const uint2 *>(cbr + s_O[j0]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int cb = (int)(int8_t)(((e < 4 ? raw.x : raw.y) >> (8 * (e & 3))) & 0xffu);
-                    h[e] = tab[(cb + kBias) & 255];
-                }
+                for (int e = 0; e < 8; ++e)
+                    b[e] = ((e < 4 ? raw.x : raw.y) >> (8 * (e & 3))) & 0xffu;
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int oc = j0 + e < n ? o[e] : 0;
-                    const unsigned v = tab[(cbr[oc] + kBias) & 255];
-                    h[e] = j0 + e < n ? v : 0u;
-                }
+                for (int e = 0; e < 8; ++e)
+                    b[e] = j0 + e < n ? (unsigned)(uint8_t)cbr[s_O[j0 + e]] : 0u;
             }
-            *reinterpret_cast<uint4 *>(w_out + r * ldo + j0) =
-                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                           h[6] | (h[7] << 16));
+            *reinterpret_cast<uint2 *>(wo + r * ldo + j0) =
+                make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                           b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
         }
     }
 }
 
+// The gather blocks' part of a row-quantization launch: the first outlier
+// columns into LDS, then the weight operand.  s_O: kCompactMaxLd ints.
+template <int kMode>
+__device__ __forceinline__ void gather_block(int64_t gb, int64_t nb, int64_t K, int nchunk,
+                                             const OutlierSet &os, const uint8_t *s_fl, int *s_O,
+                                             int *s_red, const int8_t *CB, const float *SCB,
+                                             int64_t N, void *w_out, const int32_t *ZP = nullptr)
+{
+    if (os.mode == kOutDense || os.n == 0)
+        return;
+    outlier_positions(s_fl, nchunk, nullptr, s_O, (int)kCompactMaxLd, s_red);
+    __syncthreads();
+    gather_w_out<kMode>(gb, nb, K, os, s_O, CB, SCB, N, w_out, ZP);
+}
+
+// The start of every row-quantization kernel: the outlier set from the
+// detection flags; block 0 writes the summary (and the outlier list, except on
+// the GEMM path, whose kernels do not read it); then, when the row's
+// outlier values are gathered, the chunk prefix counts into s_pre.  Returns
+// whether this block has a row to quantize (false on the GEMM path when
+// every column is an outlier: the int8 part is then zero and unused).
+// s_red: 4 * kWavesPerBlock ints.
+__device__ __forceinline__ bool row_prologue(const OutlierSet &os, const uint8_t *s_fl,
+                                             int nchunk, int64_t K, int use, bool gather_x,
+                                             int *s_pre8, int32_t *O, const OutlierInfoOut &io,
+                                             int *s_red)
+{
+    const bool first = blockIdx.x == 0;
+    if (use == kForGemm && os.n == K) {
+        if (first)
+            write_outlier_info(s_fl, nchunk, os, io, s_red + 3 * kWavesPerBlock);
+        return false;
+    }
+    const bool list = first && use != kForGemm;
+    if (gather_x || list)
+        outlier_positions(s_fl, nchunk, gather_x ? s_pre8 : nullptr, list ? O : nullptr, (int)K,
+                          s_red + 2 * kWavesPerBlock);
+    if (first)
+        write_outlier_info(s_fl, nchunk, os, io, s_red + 3 * kWavesPerBlock);
+    __syncthreads();   // s_pre8 complete
+    return true;
+}
+
+// Whether a row-quantization launch gathers the rows' outlier values.
+__device__ __forceinline__ bool gathers_x(const uint16_t *x_out, int use, const OutlierSet &os)
+{
+    return x_out && (use == kForDecode || (use == kForGemm && os.mode != kOutDense));
+}
+
 template <int NC, bool kF8 = false>
 __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict__ X, int64_t T,
-                                                     int64_t K, const uint8_t *__restrict__ mask,
-                                                     const int32_t *__restrict__ chunk_pre,
-                                                     const int32_t *__restrict__ n_out,
-                                                     int8_t *__restrict__ Xq,
+                                                     int64_t K, const DetectFlags df,
+                                                     int use, int32_t *__restrict__ O,
+                                                     OutlierInfoOut io, int8_t *__restrict__ Xq,
                                                      float *__restrict__ a,
                                                      uint16_t *__restrict__ x_out,
                                                      const int8_t *__restrict__ CB,
-                                                     const float *__restrict__ SCB,
-                                                     const int32_t *__restrict__ O, int64_t N,
-                                                     uint16_t *__restrict__ w_out, bool packed)
+                                                     const float *__restrict__ SCB, int64_t N,
+                                                     void *__restrict__ w_out, bool packed)
 {
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
     __shared__ unsigned s_max[kWavesPerBlock];
-    __shared__ uint16_t s_tab[kWavesPerBlock][256];
+    __shared__ int s_red[4 * kWavesPerBlock];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int nchunk = (int)(K / 8);
+    uint8_t *s_fl = s_dyn;
+    int *s_aux = reinterpret_cast<int *>(s_dyn + flags_lds_bytes(nchunk));
+    const OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
     if ((int64_t)blockIdx.x >= T) {
-        gather_w_out<kF8 ? kModeF8 : kModeAbsmax>(blockIdx.x - T, gridDim.x - T, K, n_out, CB, SCB,
-                                                  O, N, w_out, s_tab[wave]);
+        gather_block<kF8 ? kModeF8 : kModeAbsmax>(blockIdx.x - T, gridDim.x - T, K, nchunk, os,
+                                                  s_fl, s_aux, s_red + 2 * kWavesPerBlock, CB,
+                                                  SCB, N, w_out);
         return;
     }
+    const bool gx = gathers_x(x_out, use, os);
+    if (!row_prologue(os, s_fl, nchunk, K, use, gx, s_aux, O, io, s_red))
+        return;
     const int64_t t = blockIdx.x;
     const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
-    const int nout = x_out ? *n_out : 0;
+    const int nout = os.n;
     const int64_t ldo = outlier_ld(nout);
-    const int64_t nchunk = K / 8;
-    uint16_t *xrow = x_out ? x_out + t * ldo : nullptr;
+    uint16_t *xrow = gx ? x_out + t * ldo : nullptr;
     unsigned m = 0;
     uint4 v[NC > 0 ? NC : 1];
     unsigned fl[NC > 0 ? NC : 1];
-    int pre[NC > 0 ? NC : 1];
     if constexpr (NC > 0) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            const int64_t c = tid + (int64_t)i * kBlock;
+            const int c = tid + i * kBlock;
             v[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
-            fl[i] = c < nchunk ? mask[c] : 0u;
-        }
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            const int64_t c = tid + (int64_t)i * kBlock;
-            pre[i] = (xrow && fl[i] != 0u) ? chunk_pre[c] : 0;   // lands during the reduction
+            fl[i] = c < nchunk ? s_fl[c] : 0u;
         }
 #pragma unroll
         for (int i = 0; i < NC; ++i)
             m = umax(m, chunk_absmax_masked(v[i], fl[i]));
     } else {
-        for (int64_t c = tid; c < nchunk; c += kBlock)
-            m = umax(m, chunk_absmax_masked(xr[c], mask[c]));
+        for (int c = tid; c < nchunk; c += kBlock)
+            m = umax(m, chunk_absmax_masked(xr[c], s_fl[c]));
     }
     m = wave_max_u32(m);
     if (lane == 0)
@@ -595,21 +773,22 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     if constexpr (NC > 0) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            const int64_t c = tid + (int64_t)i * kBlock;
+            const int c = tid + i * kBlock;
             if (c < nchunk)
-                quant_chunk<kF8>(v[i], fl[i], amax, r, pre[i], xrow,
+                quant_chunk<kF8>(v[i], fl[i], amax, r,
+                                 (xrow && fl[i]) ? chunk_pos(s_fl, s_aux, c) : 0, xrow,
                                  xq_chunk(Xq, t, K, c, packed), sc);
         }
     } else {
-        for (int64_t c = tid; c < nchunk; c += kBlock) {
-            const unsigned f = mask[c];
-            quant_chunk<kF8>(xr[c], f, amax, r, (xrow && f != 0u) ? chunk_pre[c] : 0, xrow,
+        for (int c = tid; c < nchunk; c += kBlock) {
+            const unsigned f = s_fl[c];
+            quant_chunk<kF8>(xr[c], f, amax, r, (xrow && f) ? chunk_pos(s_fl, s_aux, c) : 0, xrow,
                              xq_chunk(Xq, t, K, c, packed), sc);
         }
     }
-    if (x_out) {
-        for (int j = nout + tid; j < ldo; j += kBlock)
-            x_out[t * ldo + j] = 0;
+    if (xrow) {
+        for (int64_t j = nout + tid; j < ldo; j += kBlock)
+            xrow[j] = 0;
     }
     if (tid == 0)
         a[t] = kF8 ? __builtin_ldexpf(1.0f, -e8) : amax;
@@ -643,41 +822,51 @@ __device__ __forceinline__ void step_prefix(unsigned fl, uint64_t below, int &pr
 
 template <int NC, bool kF8 = false>
 __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restrict__ X, int64_t T,
-                                                       int64_t K, const uint8_t *__restrict__ mask,
-                                                       const int32_t *__restrict__ n_out,
-                                                       int8_t *__restrict__ Xq,
+                                                       int64_t K,
+                                                       const DetectFlags df,
+                                                       int use, int32_t *__restrict__ O,
+                                                       OutlierInfoOut io, int8_t *__restrict__ Xq,
                                                        float *__restrict__ a,
                                                        uint16_t *__restrict__ x_out,
                                                        const int8_t *__restrict__ CB,
-                                                       const float *__restrict__ SCB,
-                                                       const int32_t *__restrict__ O, int64_t N,
-                                                       uint16_t *__restrict__ w_out,
+                                                       const float *__restrict__ SCB, int64_t N,
+                                                       void *__restrict__ w_out,
                                                        int64_t row_blocks)
 {
-    __shared__ uint16_t s_tab[kWavesPerBlock][256];
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+    __shared__ int s_red[4 * kWavesPerBlock];
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int nchunk = (int)(K / 8);
+    uint8_t *s_fl = s_dyn;
+    int *s_aux = reinterpret_cast<int *>(s_dyn + flags_lds_bytes(nchunk));
+    const OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
     if ((int64_t)blockIdx.x >= row_blocks) {
-        gather_w_out<kF8 ? kModeF8 : kModeAbsmax>(blockIdx.x - row_blocks, gridDim.x - row_blocks,
-                                                  K, n_out, CB, SCB, O, N, w_out, s_tab[wave]);
+        gather_block<kF8 ? kModeF8 : kModeAbsmax>(blockIdx.x - row_blocks,
+                                                  gridDim.x - row_blocks, K, nchunk, os, s_fl,
+                                                  s_aux, s_red + 2 * kWavesPerBlock, CB, SCB, N,
+                                                  w_out);
         return;
     }
+    const bool gx = gathers_x(x_out, use, os);
+    // positions come from ballots over the row, which a wavefront walks in order
+    if (!row_prologue(os, s_fl, nchunk, K, use, false, nullptr, O, io, s_red))
+        return;
     const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     if (t >= T)
         return;
     const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
     uint2 *qr = reinterpret_cast<uint2 *>(Xq + t * K);
-    const int64_t nchunk = K / 8;
-    const int nout = x_out ? *n_out : 0;
+    const int nout = os.n;
     const int64_t ldo = outlier_ld(nout);
-    uint16_t *xrow = x_out ? x_out + t * ldo : nullptr;
+    uint16_t *xrow = gx ? x_out + t * ldo : nullptr;
     const uint64_t below = (1ull << lane) - 1ull;
     uint4 v[NC];
     unsigned fl[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-        const int64_t c = lane + (int64_t)i * kWave;
+        const int c = lane + i * kWave;
         v[i] = c < nchunk ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
-        fl[i] = c < nchunk ? mask[c] : 0u;
+        fl[i] = c < nchunk ? s_fl[c] : 0u;
     }
     // the outlier values first, then they are zeroed in place
     if (xrow && nout > 0) {
@@ -707,7 +896,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restric
     const float sc = kF8 ? __builtin_ldexpf(1.0f, e8) : 0.0f;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-        const int64_t c = lane + (int64_t)i * kWave;
+        const int c = lane + i * kWave;
         if (c < nchunk)
             qr[c] = quant8_mode<kF8>(v[i], amax, r, sc);
     }
@@ -745,14 +934,6 @@ __device__ __forceinline__ void wave_minmax(float &mn, float &mx)
         mn = __builtin_fminf(mn, __shfl_xor(mn, off, kWave));
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, off, kWave));
     }
-}
-
-__device__ __forceinline__ int wave_sum(int v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v += __shfl_xor(v, off, kWave);
-    return v;
 }
 
 // (nd, zp) of a vector whose range [mn, mx] already contains 0:
@@ -799,7 +980,7 @@ __device__ __forceinline__ uint2 quant8_zp(uint4 v, float nd, float zpf, int &su
 // launch of T blocks, block t quantizing row t.  The outlier set depends on
 // every row, and at these sizes each block can afford to read all of X (at
 // most 16 rows x 16384 columns): every block derives the same flags itself,
-// so no partial flags, compaction launch or workspace are needed.  A thread
+// so no detection flags, separate launches or workspace are needed.  A thread
 // owns the 8-column chunks c = tid, tid + 512, ... (G of them):
 //   1. it loads its chunks of every row, R rows at a time, keeps the column
 //      maxima of |x| (the flags follow from them) and row t's chunks;
@@ -809,7 +990,7 @@ __device__ __forceinline__ uint2 quant8_zp(uint4 v, float nd, float zpf, int &su
 //   3. the absmax of row t over the other columns (wave reductions and the 8
 //      wave maxima through LDS), then the packed int8 row and the row's
 //      outlier values in x_out.
-// The tests and the arithmetic are those of k_detect / k_compact /
+// The tests and the arithmetic are those of k_detect / derive_outliers /
 // k_rowquant, so the results are identical bit for bit.
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 512;
@@ -1047,50 +1228,50 @@ __global__ __launch_bounds__(kBlock) void k_quantize_weight_zp(const uint16_t *_
 // x_out.  Extra blocks build w_out with the zero-point dequantization.
 template <int NC>
 __global__ __launch_bounds__(kBlock) void k_rowquant_zp(
-    const uint16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ mask,
-    const int32_t *__restrict__ chunk_pre, const int32_t *__restrict__ n_out,
-    int8_t *__restrict__ Xq, float *__restrict__ nd_out, int2 *__restrict__ row_zp,
-    uint16_t *__restrict__ x_out, const int8_t *__restrict__ CB, const float *__restrict__ NDw,
-    const int32_t *__restrict__ ZPw, const int32_t *__restrict__ O, int64_t N,
-    uint16_t *__restrict__ w_out, bool packed)
+    const uint16_t *__restrict__ X, int64_t T, int64_t K, const DetectFlags df,
+    int use, int32_t *__restrict__ O, OutlierInfoOut io, int8_t *__restrict__ Xq,
+    float *__restrict__ nd_out, int2 *__restrict__ row_zp, uint16_t *__restrict__ x_out,
+    const int8_t *__restrict__ CB, const float *__restrict__ NDw, const int32_t *__restrict__ ZPw,
+    int64_t N, void *__restrict__ w_out, bool packed)
 {
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
     __shared__ float s_mn[kWavesPerBlock], s_mx[kWavesPerBlock];
     __shared__ int s_sum[kWavesPerBlock];
-    __shared__ uint16_t s_tab[kWavesPerBlock][256];
+    __shared__ int s_red[4 * kWavesPerBlock];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int nchunk = (int)(K / 8);
+    uint8_t *s_fl = s_dyn;
+    int *s_aux = reinterpret_cast<int *>(s_dyn + flags_lds_bytes(nchunk));
+    const OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
     if ((int64_t)blockIdx.x >= T) {
-        gather_w_out<kModeZp>(blockIdx.x - T, gridDim.x - T, K, n_out, CB, NDw, O, N, w_out,
-                              s_tab[wave], ZPw);
+        gather_block<kModeZp>(blockIdx.x - T, gridDim.x - T, K, nchunk, os, s_fl, s_aux,
+                              s_red + 2 * kWavesPerBlock, CB, NDw, N, w_out, ZPw);
         return;
     }
+    const bool gx = gathers_x(x_out, use, os);
+    if (!row_prologue(os, s_fl, nchunk, K, use, gx, s_aux, O, io, s_red))
+        return;
     const int64_t t = blockIdx.x;
     const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
-    const int nout = x_out ? *n_out : 0;
+    const int nout = os.n;
     const int64_t ldo = outlier_ld(nout);
-    const int64_t nchunk = K / 8;
-    uint16_t *xrow = x_out ? x_out + t * ldo : nullptr;
+    uint16_t *xrow = gx ? x_out + t * ldo : nullptr;
     float mn = 0.0f, mx = 0.0f;
     uint4 v[NC > 0 ? NC : 1];
     unsigned fl[NC > 0 ? NC : 1];
-    int pre[NC > 0 ? NC : 1];
     if constexpr (NC > 0) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            const int64_t c = tid + (int64_t)i * kBlock;
+            const int c = tid + i * kBlock;
             v[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
-            fl[i] = c < nchunk ? mask[c] : 0u;
-        }
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            const int64_t c = tid + (int64_t)i * kBlock;
-            pre[i] = (xrow && fl[i] != 0u) ? chunk_pre[c] : 0;
+            fl[i] = c < nchunk ? s_fl[c] : 0u;
         }
 #pragma unroll
         for (int i = 0; i < NC; ++i)
             chunk_minmax(fl[i] ? drop_flagged(v[i], fl[i]) : v[i], mn, mx);
     } else {
-        for (int64_t c = tid; c < nchunk; c += kBlock) {
-            const unsigned f = mask[c];
+        for (int c = tid; c < nchunk; c += kBlock) {
+            const unsigned f = s_fl[c];
             const uint4 w = xr[c];
             chunk_minmax(f ? drop_flagged(w, f) : w, mn, mx);
         }
@@ -1109,10 +1290,10 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_zp(
     const ZpParams p = zp_params(mn, mx);
     const float zpf = (float)p.zp;
     int sum = 0;
-    auto quant = [&](uint4 w, unsigned f, int pr, int64_t c) {
+    auto quant = [&](uint4 w, unsigned f, int c) {
         if (f) {
             if (xrow)
-                scatter_outliers(w, f, pr, xrow);
+                scatter_outliers(w, f, chunk_pos(s_fl, s_aux, c), xrow);
             w = drop_flagged(w, f);
         }
         *xq_chunk(Xq, t, K, c, packed) = quant8_zp(w, p.nd, zpf, sum);
@@ -1120,19 +1301,17 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_zp(
     if constexpr (NC > 0) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            const int64_t c = tid + (int64_t)i * kBlock;
+            const int c = tid + i * kBlock;
             if (c < nchunk)
-                quant(v[i], fl[i], pre[i], c);
+                quant(v[i], fl[i], c);
         }
     } else {
-        for (int64_t c = tid; c < nchunk; c += kBlock) {
-            const unsigned f = mask[c];
-            quant(xr[c], f, (xrow && f != 0u) ? chunk_pre[c] : 0, c);
-        }
+        for (int c = tid; c < nchunk; c += kBlock)
+            quant(xr[c], s_fl[c], c);
     }
-    if (x_out) {
-        for (int j = nout + tid; j < ldo; j += kBlock)
-            x_out[t * ldo + j] = 0;
+    if (xrow) {
+        for (int64_t j = nout + tid; j < ldo; j += kBlock)
+            xrow[j] = 0;
     }
     sum = wave_sum(sum);
     if (lane == 0)
@@ -1166,6 +1345,30 @@ unsigned threshold_bits(float thr)
     return lo;
 }
 
+// k_detect over all rows into the flag sets of the detection area `mask`
+// (see DetectFlags); returns what the row-quantization kernels read.
+DetectFlags launch_detect(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                          uint8_t *mask, hipStream_t s)
+{
+    const DetectFlags df = detect_flags(mask, T, K);
+    const dim3 grid((unsigned)(K / 64 * df.nr));
+    hipLaunchKernelGGL(k_detect, grid, dim3(kDetectThreads), 0, s, X, T, K, df.nr, df.pitch,
+                       threshold_bits(threshold), const_cast<uint8_t *>(df.parts));
+    return df;
+}
+
+// Blocks of a row-quantization launch that build the GEMM path's outlier
+// weight operand (past the row blocks): 64 weight rows per block (kOutFew:
+// 16 rows per wavefront at once; kOutCompact: a wavefront walks 16 rows),
+// at most 1024 blocks sharing the rows.
+int64_t gather_blocks(const GatherArgs &g)
+{
+    if (!g.w_out)
+        return 0;
+    const int64_t b = (g.N + 63) / 64;
+    return b > 1024 ? 1024 : b;
+}
+
 }  // namespace
 
 hipError_t launch_quantize_weight(const uint16_t *W_t, int64_t K, int64_t N, int8_t *CB,
@@ -1188,9 +1391,8 @@ hipError_t launch_quantize_weight_zp(const uint16_t *W_t, int64_t K, int64_t N, 
 
 hipError_t launch_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K, float threshold,
                                   int8_t *Xq, float *nd, int2 *row_zp, int32_t *O,
-                                  int32_t *n_out, uint8_t *partial, uint8_t *mask,
-                                  int32_t *chunk_pre, uint16_t *x_out, const GatherArgs &g,
-                                  bool xq_packed, hipStream_t s)
+                                  const OutlierInfoOut &io, uint8_t *mask, uint16_t *x_out,
+                                  const GatherArgs &g, bool xq_packed, hipStream_t s)
 {
     if ((xq_packed && T > 16) || (g.w_out && !g.zp))
         return hipErrorInvalidValue;
@@ -1201,7 +1403,7 @@ hipError_t launch_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K, float
         const dim3 grid((unsigned)T);
 #define LLMINT8_QROWS_ZP(G)                                                                    \
     hipLaunchKernelGGL((k_quant_rows<G, kModeZp>), grid, dim3(kSmallThreads), 0, s, X, (int)T,    \
-                       (int)K, tb, Xq, nd, O, n_out, x_out, xq_packed, row_zp)
+                       (int)K, tb, Xq, nd, O, io.info, x_out, xq_packed, row_zp)
         if (per <= 1)
             LLMINT8_QROWS_ZP(1);
         else if (per <= 2)
@@ -1218,24 +1420,14 @@ hipError_t launch_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K, float
         return hipGetLastError();
     }
     const int64_t nchunk = K / 8;
-    const int64_t rows_per = (T + kDetectSplits - 1) / kDetectSplits;
-    const dim3 det_grid((unsigned)((nchunk + 31) / 32), (unsigned)kDetectSplits);
-    hipLaunchKernelGGL(k_detect, det_grid, dim3(kDetectThreads), 0, s, X, T, K,
-                       threshold_bits(threshold), rows_per, partial);
-    hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, partial, K, mask, O, n_out,
-                       chunk_pre);
-    int64_t gather_blocks = 0;
-    if (g.w_out) {
-        gather_blocks = (g.N + kWavesPerBlock - 1) / kWavesPerBlock;
-        if (gather_blocks > 2048)
-            gather_blocks = 2048;
-    }
-    const dim3 grid((unsigned)(T + gather_blocks));
+    const int use = g.w_out ? kForGemm : x_out ? kForDecode : kForAct;
+    const DetectFlags df = launch_detect(X, T, K, threshold, mask, s);
+    const dim3 grid((unsigned)(T + gather_blocks(g)));
+    const size_t lds = rowquant_lds_bytes(K);
     const int64_t chunks_per_thread = (nchunk + kBlock - 1) / kBlock;
-#define LLMINT8_ROWQUANT_ZP(NCV)                                                              \
-    hipLaunchKernelGGL(k_rowquant_zp<NCV>, grid, dim3(kBlock), 0, s, X, T, K, mask, chunk_pre, \
-                       n_out, Xq, nd, row_zp, x_out, g.CB, g.SCB, g.zp, O, g.N, g.w_out,     \
-                       xq_packed)
+#define LLMINT8_ROWQUANT_ZP(NCV)                                                               \
+    hipLaunchKernelGGL(k_rowquant_zp<NCV>, grid, dim3(kBlock), lds, s, X, T, K, df,   use, O,    \
+                       io, Xq, nd, row_zp, x_out, g.CB, g.SCB, g.zp, g.N, g.w_out, xq_packed)
     if (chunks_per_thread <= 1)
         LLMINT8_ROWQUANT_ZP(1);
     else if (chunks_per_thread <= 2)
@@ -1285,40 +1477,29 @@ hipError_t launch_quantize_act_rows(const uint16_t *X, int64_t T, int64_t K, flo
 }
 
 namespace {
-// Detection, compaction and the row quantization of the absmax kernels
-// (kF8: their FP8 mode).
+// Detection and the row quantization of the absmax kernels (kF8: their FP8
+// mode).
 template <bool kF8>
 hipError_t launch_act_absmax(const uint16_t *X, int64_t T, int64_t K, float threshold,
-                             int8_t *Xq, float *a, int32_t *O, int32_t *n_out, uint8_t *partial,
-                             uint8_t *mask, int32_t *chunk_pre, uint16_t *x_out,
-                             const GatherArgs &g, bool xq_packed, hipStream_t s)
+                             int8_t *Xq, float *a, int32_t *O, const OutlierInfoOut &io,
+                             uint8_t *mask, uint16_t *x_out, const GatherArgs &g,
+                             bool xq_packed, hipStream_t s)
 {
     if (xq_packed && T > 16)
         return hipErrorInvalidValue;
     const int64_t nchunk = K / 8;
-    const int64_t rows_per = (T + kDetectSplits - 1) / kDetectSplits;
-    const dim3 det_grid((unsigned)((nchunk + 31) / 32), (unsigned)kDetectSplits);
-    hipLaunchKernelGGL(k_detect, det_grid, dim3(kDetectThreads), 0, s, X, T, K,
-                       threshold_bits(threshold), rows_per, partial);
-    hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, partial, K, mask, O, n_out,
-                       chunk_pre);
-    // w_out blocks: one wavefront per row when many columns are outliers; with
-    // up to 32 a block covers 64 rows and the rest exit at once
-    int64_t gather_blocks = 0;
-    if (g.w_out) {
-        gather_blocks = (g.N + kWavesPerBlock - 1) / kWavesPerBlock;
-        if (gather_blocks > 2048)
-            gather_blocks = 2048;
-    }
-    if (T >= kRowQuantWaveMinT && K <= kRowQuantWaveMaxK) {
+    const int use = g.w_out ? kForGemm : x_out ? kForDecode : kForAct;
+    const DetectFlags df = launch_detect(X, T, K, threshold, mask, s);
+    const int64_t gb = gather_blocks(g);
+    const size_t lds = rowquant_lds_bytes(K);
+    if (T >= kRowQuantWaveMinT && K <= kRowQuantWaveMaxK && !xq_packed) {
         // a wavefront per row, the row in NC chunks per lane
         const int64_t per = (nchunk + kWave - 1) / kWave;
         const int64_t row_blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
-        const dim3 grid((unsigned)(row_blocks + gather_blocks));
-#define LLMINT8_ROWQUANT_W(NCV)                                                                  \
-    hipLaunchKernelGGL((k_rowquant_w<NCV, kF8>), grid, dim3(kBlock), 0, s, X, T, K, mask, n_out, \
-                       Xq, a,                                                            \
-                       x_out, g.CB, g.SCB, O, g.N, g.w_out, row_blocks)
+        const dim3 grid((unsigned)(row_blocks + gb));
+#define LLMINT8_ROWQUANT_W(NCV)                                                                \
+    hipLaunchKernelGGL((k_rowquant_w<NCV, kF8>), grid, dim3(kBlock), lds, s, X, T, K, df,        \
+                       use, O, io, Xq, a, x_out, g.CB, g.SCB, g.N, g.w_out, row_blocks)
         static_assert(kRowQuantWaveMaxK / 8 <= 8 * kWave, "rows of at most 8 chunks per lane");
         if (per <= 2)
             LLMINT8_ROWQUANT_W(2);
@@ -1330,12 +1511,11 @@ hipError_t launch_act_absmax(const uint16_t *X, int64_t T, int64_t K, float thre
         return hipGetLastError();
     }
     // fewer rows: a block per row keeps more lanes busy
-    const dim3 grid((unsigned)(T + gather_blocks));
+    const dim3 grid((unsigned)(T + gb));
     const int64_t chunks_per_thread = (nchunk + kBlock - 1) / kBlock;
-#define LLMINT8_ROWQUANT(NCV)                                                                   \
-    hipLaunchKernelGGL((k_rowquant<NCV, kF8>), grid, dim3(kBlock), 0, s, X, T, K, mask, chunk_pre, \
-                       n_out,                                                           \
-                       Xq, a, x_out, g.CB, g.SCB, O, g.N, g.w_out, xq_packed)
+#define LLMINT8_ROWQUANT(NCV)                                                                  \
+    hipLaunchKernelGGL((k_rowquant<NCV, kF8>), grid, dim3(kBlock), lds, s, X, T, K, df,          \
+                       use, O, io, Xq, a, x_out, g.CB, g.SCB, g.N, g.w_out, xq_packed)
     if (chunks_per_thread <= 1)
         LLMINT8_ROWQUANT(1);
     else if (chunks_per_thread <= 2)
@@ -1354,13 +1534,12 @@ hipError_t launch_act_absmax(const uint16_t *X, int64_t T, int64_t K, float thre
 }  // namespace
 
 hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float threshold,
-                               int8_t *Xq, float *a, int32_t *O, int32_t *n_out,
-                               uint8_t *partial, uint8_t *mask, int32_t *chunk_pre,
-                               uint16_t *x_out, const GatherArgs &g, bool xq_packed,
-                               hipStream_t s)
+                               int8_t *Xq, float *a, int32_t *O, const OutlierInfoOut &io,
+                               uint8_t *mask, uint16_t *x_out, const GatherArgs &g,
+                               bool xq_packed, hipStream_t s)
 {
-    return launch_act_absmax<false>(X, T, K, threshold, Xq, a, O, n_out, partial, mask, chunk_pre,
-                                    x_out, g, xq_packed, s);
+    return launch_act_absmax<false>(X, T, K, threshold, Xq, a, O, io, mask, x_out, g,
+                                    xq_packed, s);
 }
 
 hipError_t launch_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N, uint8_t *CB8,
@@ -1373,10 +1552,9 @@ hipError_t launch_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N, 
 }
 
 hipError_t launch_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float threshold,
-                                  uint8_t *Xq8, float *sc, int32_t *O, int32_t *n_out,
-                                  uint8_t *partial, uint8_t *mask, int32_t *chunk_pre,
-                                  uint16_t *x_out, const GatherArgs &g, bool xq_packed,
-                                  hipStream_t s)
+                                  uint8_t *Xq8, float *sc, int32_t *O, const OutlierInfoOut &io,
+                                  uint8_t *mask, uint16_t *x_out, const GatherArgs &g,
+                                  bool xq_packed, hipStream_t s)
 {
     if (g.w_out && !g.f8)
         return hipErrorInvalidValue;
@@ -1388,7 +1566,7 @@ hipError_t launch_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float
         const dim3 grid((unsigned)T);
 #define LLMINT8_QROWS_F8(G)                                                                    \
     hipLaunchKernelGGL((k_quant_rows<G, kModeF8>), grid, dim3(kSmallThreads), 0, s, X, (int)T, \
-                       (int)K, tb, Xq, sc, O, n_out, x_out, xq_packed, nullptr)
+                       (int)K, tb, Xq, sc, O, io.info, x_out, xq_packed, nullptr)
         if (per <= 1)
             LLMINT8_QROWS_F8(1);
         else if (per <= 2)
@@ -1404,8 +1582,8 @@ hipError_t launch_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float
 #undef LLMINT8_QROWS_F8
         return hipGetLastError();
     }
-    return launch_act_absmax<true>(X, T, K, threshold, Xq, sc, O, n_out, partial, mask, chunk_pre,
-                                   x_out, g, xq_packed, s);
+    return launch_act_absmax<true>(X, T, K, threshold, Xq, sc, O, io, mask, x_out, g,
+                                   xq_packed, s);
 }
 
 }  // namespace llmint8

@@ -17,12 +17,29 @@ expansion layers.  `quant` selects the 8-bit part's quantizer: "absmax" (the
 method's vector-wise absmax int8), or the library's two variants,
 "zeropoint" (asymmetric int8, llmint8_matmul_zp) and "fp8" (E5M2,
 llmint8_matmul_f8); the variants have no fused activation.  This module only holds the tensors, flattens leading
-dimensions into rows, and keeps one workspace buffer per device, grown as
-needed, so that steady-state calls allocate nothing but their output.
+dimensions into rows, and shares one workspace buffer per (device, stream)
+among all instances, grown as needed, so that steady-state calls allocate
+nothing but their output and a model needs one workspace, not one per layer.
+Calls on one stream run in order, so they may share it; calls on different
+streams get different buffers.
 """
 import torch
 
 from . import llmint8 as L
+
+# (device, stream handle) -> uint8 workspace tensor shared by every module
+_WORKSPACES = {}
+
+
+def _shared_workspace(nbytes, device):
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        # a larger buffer replaces the old one; work already enqueued on this
+        # stream keeps the old one alive through the caching allocator
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
 
 _ACTS = {None: L.ACT_NONE, "none": L.ACT_NONE, "relu": L.ACT_RELU}
 _QUANTS = ("absmax", "zeropoint", "fp8")
@@ -74,7 +91,6 @@ class Linear8bitLt(torch.nn.Module):
         self.register_buffer("SCB", None)   # absmax: column absmax; zero-point: nd; fp8: 2^-e
         self.register_buffer("ZP", None)    # zero-point variant: zero points and code sums
         self.register_buffer("RS", None)
-        self._ws = {}
 
     @classmethod
     def from_linear(cls, linear, has_fp16_weights=False, threshold=6.0, activation=None,
@@ -118,12 +134,8 @@ class Linear8bitLt(torch.nn.Module):
         return self
 
     def _workspace(self, T, device):
-        need = L.llmint8_workspace_bytes(T, self.in_features, self.out_features)
-        ws = self._ws.get(device)
-        if ws is None or ws.numel() < need:
-            ws = torch.empty((need,), dtype=torch.uint8, device=device)
-            self._ws[device] = ws
-        return ws
+        return _shared_workspace(L.llmint8_workspace_bytes(T, self.in_features, self.out_features),
+                                 device)
 
     def forward(self, x):
         if x.dtype != torch.float16:

@@ -72,3 +72,14 @@ def sample_rows(T, n_random=62, seed=1234):
     rng = np.random.default_rng(seed)
     r = rng.choice(T, size=min(T, n_random), replace=False)
     return np.unique(np.concatenate([[0, T - 1], r])).astype(np.int64)
+
+
+def tile_rows(T, tile=256, per_tile=4, seed=4321):
+    """`per_tile` seeded rows from every `tile`-row block of [0, T), plus rows
+    0 and T-1 (sorted, unique): a sample that covers every tile row of the GEMM."""
+    rng = np.random.default_rng(seed)
+    picks = [[0, T - 1]]
+    for r0 in range(0, T, tile):
+        r1 = min(T, r0 + tile)
+        picks.append(r0 + rng.choice(r1 - r0, size=min(per_tile, r1 - r0), replace=False))
+    return np.unique(np.concatenate(picks)).astype(np.int64)

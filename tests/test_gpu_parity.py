@@ -202,11 +202,11 @@ def test_stream_asynchrony_and_ordering():
     assert_fp16_close(out.cpu().numpy(), ref, "side stream")
 
 
-# One activation row with K <= 16384: the weight-streaming kernel quantizes
-# the row in every block.  Outlier counts around the 1024 columns it lists in
-# LDS (beyond them it walks the chunk flags), every column an outlier
-# (threshold 0), none (threshold inf), and K at the 16384 limit and past it
-# (where the separate quantization launch takes over).
+# One activation row: the one-launch quantization serves K up to 65536 (the
+# separate three-kernel chain takes over past it).  Outlier counts around 1024
+# and well past it (the weight-streaming epilogue walks the outlier list in
+# groups of 8), every column an outlier (threshold 0), none (threshold inf),
+# and K at and past 16384 (the limit of the few-rows kernel for T > 1).
 @pytest.mark.parametrize("K,n_dims,thr", [(8192, 1023, 6.0), (8192, 1024, 6.0), (8192, 1025, 6.0),
                                            (8192, 3000, 6.0), (16384, 6, 0.0), (16384, 6, np.inf),
                                            (12288, 6, 6.0), (16448, 6, 6.0)])
@@ -224,3 +224,134 @@ def test_one_row_decode(K, n_dims, thr, relu):
     out = L.llmint8_matmul_act(h2d(X), CB, SCB, thr, L.ACT_RELU if relu else L.ACT_NONE,
                                bias=h2d(bias))
     assert_fp16_close(d2h(out), ref, "one-row decode")
+
+
+# The tiled GEMM switches from 8 wavefronts (128 x 64 each) to 4 (128 x 128)
+# above K = 6144: both sides of the switch, each output kernel template (bias
+# on and off, ReLU on and off), up to 32 outlier columns.
+@pytest.mark.parametrize("K", [6144, 6272])
+@pytest.mark.parametrize("use_bias", [False, True])
+@pytest.mark.parametrize("relu", [False, True])
+def test_gemm_wave_shapes_around_switch(K, use_bias, relu):
+    T, N = 300, 320
+    say("gemm switch K=%d bias=%s relu=%s" % (K, use_bias, relu))
+    X, W_t, dims = workloads.case(T, K, N, n_dims=20, lo=8, hi=60, p=0.5, seed=K + 7)
+    bias = np.random.default_rng(K).standard_normal(N).astype(np.float16) if use_bias else None
+    CBr, SCBr = oracle.quantize_weight(W_t)
+    ref, Or, _ = oracle.matmul(X, CBr, SCBr, 6.0, bias=bias, relu=relu)
+    assert 0 < Or.size <= 32
+    CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
+    out = L.llmint8_matmul_act(h2d(X), CB, SCB, 6.0, L.ACT_RELU if relu else L.ACT_NONE,
+                               bias=h2d(bias) if use_bias else None)
+    assert_fp16_close(d2h(out), ref, "out")
+
+
+# Decode shapes past the few-rows kernel's K limit (2 <= T <= 16, K > 16384):
+# the three-kernel quantization writes Xq in the fragment order the
+# weight-streaming kernel reads.
+@pytest.mark.parametrize("T,K", [(4, 16448), (16, 24576)])
+@pytest.mark.parametrize("thr", [6.0, 0.0, np.inf])
+def test_decode_past_few_rows_limit(T, K, thr):
+    N = 256
+    say("decode past the few-rows limit T=%d K=%d thr=%s" % (T, K, thr))
+    X, W_t, _ = workloads.case(T, K, N, n_dims=6, lo=8, hi=60, p=1.0, seed=T + K)
+    bias = np.random.default_rng(T).standard_normal(N).astype(np.float16)
+    CBr, SCBr = oracle.quantize_weight(W_t)
+    ref, _, _ = oracle.matmul(X, CBr, SCBr, thr, bias=bias)
+    CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
+    out = L.llmint8_matmul_path(h2d(X), CB, SCB, thr, bias=h2d(bias), path=L.PATH_DECODE)
+    assert_fp16_close(d2h(out), ref, "out")
+
+
+def test_concurrent_streams():
+    """Two default-priority streams each run their own shape (a GEMM-path and a
+    weight-streaming call, with their own outputs and workspaces) at the same
+    time, several calls deep; both results against the oracle."""
+    cases = [workloads.case(1000, 1024, 768, n_dims=5, seed=21),
+             workloads.case(8, 2048, 1024, n_dims=4, seed=22)]
+    refs, ops = [], []
+    for X, W_t, _ in cases:
+        CBr, SCBr = oracle.quantize_weight(W_t)
+        refs.append(oracle.matmul(X, CBr, SCBr, 6.0)[0])
+        CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
+        ops.append((h2d(X), CB, SCB))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for s, (Xd, CB, SCB) in zip(streams, ops):
+        with torch.cuda.stream(s):
+            ws = torch.empty((L.llmint8_workspace_bytes(Xd.shape[0], Xd.shape[1], CB.shape[0]),),
+                             dtype=torch.uint8, device=Xd.device)
+            out = torch.empty((Xd.shape[0], CB.shape[0]), dtype=torch.float16, device=Xd.device)
+            outs.append((out, ws))
+    for rep in range(4):
+        for s, (Xd, CB, SCB), (out, ws) in zip(streams, ops, outs):
+            with torch.cuda.stream(s):
+                L.llmint8_matmul(Xd, CB, SCB, 6.0, out=out, ws=ws)
+    torch.cuda.synchronize()
+    for (out, _), ref, what in zip(outs, refs, ("GEMM stream", "decode stream")):
+        assert_fp16_close(out.cpu().numpy(), ref, what)
+
+
+# More than 32 outlier columns on the GEMM path: the fp16 pass reads either
+# compact gathered operands (scattered outliers, at most 1024 of them after
+# padding) or X and CB in place over the 64-column groups that hold outliers,
+# with the non-outlier columns of each group masked (clustered outliers, or
+# more than 1024).  Cases on both sides of each choice, a K whose stages are
+# 64 bytes (K % 128 != 0), ragged T and N, bias and ReLU.
+def _planted(T, K, N, cols, seed, lo=8.0, hi=60.0, p=0.6):
+    X, W_t, _ = workloads.case(T, K, N, n_dims=0, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    X = X.astype(np.float32)
+    for c in cols:
+        rows = rng.random(T) < p
+        rows[rng.integers(T)] = True      # every planted column holds an outlier
+        X[rows, c] = rng.uniform(lo, hi, rows.sum()) * np.where(rng.random(rows.sum()) < 0.5, -1, 1)
+    return X.astype(np.float16), W_t
+
+
+MANY_CASES = {
+    # name: (T, K, N, columns)
+    "compact33": (300, 4096, 320, np.arange(33) * 97 + 5),
+    "compact200": (260, 4160, 384, np.arange(200) * 20 + 3),
+    "compact1000": (300, 8192, 256, np.arange(1000) * 8 + 1),
+    "dense1030_spread": (300, 8256, 320, np.arange(1030) * 8 + 2),
+    "dense_clustered": (513, 4096, 320, np.arange(1000, 1200)),
+    "dense_partial_groups": (300, 4160, 448, np.concatenate([np.arange(64, 128), [130, 199, 4100],
+                                                            np.arange(2048, 2048 + 61)])),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MANY_CASES))
+@pytest.mark.parametrize("use_bias,relu", [(False, False), (True, True)])
+def test_many_outliers_compact_and_dense(case, use_bias, relu):
+    T, K, N, cols = MANY_CASES[case]
+    say("many outliers %s T=%d K=%d N=%d n=%d bias=%s relu=%s" % (case, T, K, N, len(cols), use_bias, relu))
+    X, W_t = _planted(T, K, N, cols, seed=len(cols) + K)
+    bias = np.random.default_rng(N).standard_normal(N).astype(np.float16) if use_bias else None
+    CBr, SCBr = oracle.quantize_weight(W_t)
+    ref, Or, _ = oracle.matmul(X, CBr, SCBr, 6.0, bias=bias, relu=relu)
+    assert Or.size == len(cols)
+    CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
+    out = L.llmint8_matmul_act(h2d(X), CB, SCB, 6.0, L.ACT_RELU if relu else L.ACT_NONE,
+                               bias=h2d(bias) if use_bias else None)
+    assert_fp16_close(d2h(out), ref, case)
+
+
+@pytest.mark.parametrize("thr", [0.0, 0.4])
+def test_nearly_every_column_an_outlier(thr):
+    """Threshold 0 with an all-zero column (n = K - 1: the int8 part still runs,
+    and the group holding that column is masked), and a threshold that leaves a
+    few small-valued columns out of the outlier set."""
+    T, K, N = 300, 1088, 320
+    say("nearly all outliers thr=%s" % thr)
+    X, W_t, _ = workloads.case(T, K, N, n_dims=0, seed=int(thr * 10) + 7)
+    X = X.astype(np.float32)
+    X[:, 100] = 0.0
+    X[:, [5, 700, 1087]] *= 0.05
+    X = X.astype(np.float16)
+    CBr, SCBr = oracle.quantize_weight(W_t)
+    ref, Or, _ = oracle.matmul(X, CBr, SCBr, thr)
+    assert K - 4 <= Or.size < K
+    CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
+    assert_fp16_close(d2h(L.llmint8_matmul(h2d(X), CB, SCB, thr)), ref, "out")

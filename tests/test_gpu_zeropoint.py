@@ -196,3 +196,42 @@ def test_matmul_zp_full_size_sampled(which):
         assert_equal_exact(ZPh[cols], ZPr, "ZP sample")
         ref, _, _, _ = oracle.matmul_zp(X, CBr, NDr, ZPr, 6.0)
         assert_fp16_close(out[:, cols], ref, "out cols")
+
+
+# Decode shapes past the few-rows kernel's K limit (2 <= T <= 16, K > 16384):
+# the three-kernel quantization in fragment order, then the weight stream.
+@pytest.mark.parametrize("T,K", [(4, 16448), (16, 24576)])
+@pytest.mark.parametrize("thr", [6.0, 0.0, np.inf])
+def test_decode_zp_past_few_rows_limit(T, K, thr):
+    N = 256
+    say("decode zp past the few-rows limit T=%d K=%d thr=%s" % (T, K, thr))
+    X, W_t, _ = skewed_case(T, K, N, seed=T + K, n_dims=6, p=1.0)
+    CB, ND, ZP, RS = L.llmint8_quantize_weight_zp(h2d(W_t))
+    out = L.llmint8_matmul_zp_path(h2d(X), CB, ND, ZP, RS, thr, path=L.PATH_DECODE)
+    CBr, NDr, ZPr = oracle.quantize_weight_zp(W_t)
+    ref, _, _, _ = oracle.matmul_zp(X, CBr, NDr, ZPr, thr)
+    assert_fp16_close(d2h(out), ref, "out")
+
+
+# More than 32 outlier columns on the GEMM path, both ways of forming the fp16
+# product: compact gathered operands (scattered outliers) and X / CB read in
+# place over the groups that hold outliers (clustered, or past 1024 columns).
+@pytest.mark.parametrize("cols", [np.arange(100) * 40 + 3, np.arange(1500, 1700),
+                                  np.arange(1040) * 4 + 1])
+def test_zp_many_outliers_compact_and_dense(cols):
+    T, K, N = 300, 4224, 320
+    say("zp many outliers n=%d" % len(cols))
+    X, W_t, _ = workloads.case(T, K, N, n_dims=0, seed=len(cols))
+    rng = np.random.default_rng(len(cols) + 1)
+    X = X.astype(np.float32)
+    for c in cols:
+        rows = rng.random(T) < 0.6
+        rows[0] = True
+        X[rows, c] = rng.uniform(8.0, 60.0, rows.sum())
+    X = X.astype(np.float16)
+    CB, ND, ZP, RS = L.llmint8_quantize_weight_zp(h2d(W_t))
+    out = L.llmint8_matmul_zp(h2d(X), CB, ND, ZP, RS, 6.0)
+    CBr, NDr, ZPr = oracle.quantize_weight_zp(W_t)
+    ref, O, _, _ = oracle.matmul_zp(X, CBr, NDr, ZPr, 6.0)
+    assert len(O) == len(cols)
+    assert_fp16_close(d2h(out), ref, "out")

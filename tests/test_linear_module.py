@@ -142,23 +142,30 @@ def test_from_linear():
 
 @gpu
 def test_ffn_pair_chained_through_two_modules():
-    """fc1 with the fused ReLU, then fc2, on a scaled-down 6.7B-style FFN (the
-    oracle runs fc2 on the GPU's own fc1 output, so each layer is judged on
-    identical inputs)."""
+    """fc1 with the fused ReLU, then fc2, on a scaled-down 6.7B-style FFN.
+    Each layer is judged on identical inputs that come from the oracle: fc1 on
+    X, fc2 on the oracle's own ReLU'd fc1 output (the same fp16 bytes go to the
+    GPU module and to the oracle).  The GPU chain fc1 -> fc2 against the oracle
+    chain is printed as end-to-end drift, not graded: the two fc2 inputs
+    differ wherever the fp16 fc1 outputs do."""
     T, D, F = 256, 512, 2048
     X, W1, _ = workloads.case(T, D, F, n_dims=6, lo=20, hi=60, p=0.75, seed=1)
     _, W2, _ = workloads.case(1, F, D, n_dims=0, seed=2)
     fc1 = _module(W1, activation="relu")
     fc2 = _module(W2)
-    h = fc1(torch.from_numpy(X).to(_dev()))
-    y = fc2(h)
-    h_np = h.cpu().numpy()
     C1, S1 = oracle.quantize_weight(W1)
-    ref1, _, _ = oracle.matmul(X, C1, S1, 6.0, relu=True)
-    _close(h_np.view(np.uint16), ref1, "fc1 + ReLU")
+    H, _, _ = oracle.matmul(X, C1, S1, 6.0, relu=True)
+    h = fc1(torch.from_numpy(X).to(_dev()))
+    _close(h.cpu().numpy().view(np.uint16), H, "fc1 + ReLU")
     C2, S2 = oracle.quantize_weight(W2)
-    ref2, _, _ = oracle.matmul(h_np, C2, S2, 6.0)
-    _close(y.cpu().numpy().view(np.uint16), ref2, "fc2 on fc1's output")
+    ref2, _, _ = oracle.matmul(H, C2, S2, 6.0)
+    y = fc2(torch.from_numpy(H.view(np.float16)).to(_dev()))
+    _close(y.cpu().numpy().view(np.uint16), ref2, "fc2 on the oracle's fc1 output")
+    chained = fc2(h).cpu().numpy().astype(np.float64)
+    r = ref2.view(np.float16).astype(np.float64)
+    print("FFN chain drift (GPU fc1 -> fc2 vs the oracle chain): max |d| %.3g, max |d|/(1e-3 + "
+          "2e-3|ref|) %.3g" % (np.abs(chained - r).max(),
+                               (np.abs(chained - r) / (1e-3 + 2e-3 * np.abs(r))).max()))
 
 
 @gpu
@@ -194,5 +201,6 @@ def test_variant_modules_match_their_oracles(quant, T):
         S = (np.abs(oracle.e5m2_to_double(Xq8)) * sc.astype(np.float64)[:, None]) @ (
             np.abs(oracle.e5m2_to_double(CB8)) * SC8.astype(np.float64)[:, None]).T
         g, r = got.astype(np.float64), ref.view(np.float16).astype(np.float64)
-        # the FP8 accumulation term of tests/test_gpu_fp8.py
-        assert np.all(np.abs(g - r) <= 1e-3 + 2e-3 * np.abs(r) + 2.0 ** -13 * S)
+        # the FP8 accumulation bound of tests/test_gpu_fp8.py
+        from tests.test_gpu_fp8 import f8_accumulation_bound
+        assert np.all(np.abs(g - r) <= 1e-3 + 2e-3 * np.abs(r) + f8_accumulation_bound(K) * S)
