@@ -64,7 +64,8 @@ typedef enum {
     LLMINT8_ERR_INVALID_ARG = 1,
     LLMINT8_ERR_UNSUPPORTED_SHAPE = 2,
     LLMINT8_ERR_WORKSPACE = 3,
-    LLMINT8_ERR_HIP = 4
+    LLMINT8_ERR_HIP = 4,
+    LLMINT8_ERR_SCRATCH = 5
 } llmint8_status_t;
 
 /* Static, NUL-terminated description of a status code (never NULL). */
@@ -147,6 +148,37 @@ LLMINT8_API llmint8_status_t llmint8_matmul(const uint16_t *X, int64_t T, int64_
                                 const int8_t *CB, const float *SCB, const uint16_t *bias,
                                 float threshold, uint16_t *out, void *ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/* Bytes of the static device scratch of llmint8_matmul_noalloc (64 MiB):
+ * a call fits when llmint8_workspace_bytes(T, K, N) is at most this, e.g.
+ * every T <= 16 call, T = 4096 x K = 4096 x N = 16384 (41 MB), or
+ * T = 2048 x K = 16384 x N = 4096 (40 MB). */
+#define LLMINT8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * llmint8_matmul without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same operation, arguments (less ws and
+ * ws_bytes), kernels and results as llmint8_matmul.
+ *
+ * The workspace is a static device array of LLMINT8_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every device it runs on until the process ends.
+ * Its device address is resolved on the first call on each device (call it
+ * once outside stream capture); the call itself allocates nothing.  The
+ * kernels need no cleared workspace, so what an earlier call left in it
+ * does not matter.  All calls on one device share the array: calls that
+ * may overlap on one device (different streams, or host threads without an
+ * ordering) race and must be serialized by the caller.
+ *
+ * Errors: as llmint8_matmul (argument and shape checks in the same order),
+ * then LLMINT8_ERR_SCRATCH when llmint8_workspace_bytes(T, K, N) exceeds
+ * LLMINT8_NOALLOC_SCRATCH_BYTES (nothing enqueued), LLMINT8_ERR_HIP when
+ * the array's address cannot be resolved or a launch fails.
+ */
+LLMINT8_API llmint8_status_t llmint8_matmul_noalloc(const uint16_t *X, int64_t T, int64_t K,
+                                                    int64_t N, const int8_t *CB, const float *SCB,
+                                                    const uint16_t *bias, float threshold,
+                                                    uint16_t *out, hipStream_t stream);
 
 /* Output activations of llmint8_matmul_act. */
 enum { LLMINT8_ACT_NONE = 0, LLMINT8_ACT_RELU = 1 };

@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/llmint8_test.h"
 #include "internal.h"
@@ -137,6 +138,48 @@ void dense_args(EpilogueArgs &ep, const uint16_t *X, const WsPtrs &p)
 
 }  // namespace llmint8
 
+// The workspace of llmint8_matmul_noalloc: one copy per device, allocated
+// when the code object is loaded on it and held until the process ends.  In
+// host code the name stands for a host-side placeholder, not for device
+// memory: kernels get the device address that device_scratch resolves.
+static __device__ __align__(256) unsigned char scratch[LLMINT8_NOALLOC_SCRATCH_BYTES];
+
+namespace llmint8 {
+namespace {
+constexpr size_t kNoAllocBytes = LLMINT8_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// This device's copy of `scratch`: its address is looked up once per device,
+// with that device current, and kept for every later call.
+hipError_t device_scratch(void **p)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    void *q = g_scratch[dev].load(std::memory_order_acquire);
+    if (!q) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        q = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!q) {
+            e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return e;
+            if (!q || ((uintptr_t)q & 255u) != 0)
+                return hipErrorInvalidSymbol;
+            g_scratch[dev].store(q, std::memory_order_release);
+        }
+    }
+    *p = q;
+    return hipSuccess;
+}
+}  // namespace
+}  // namespace llmint8
+
 using namespace llmint8;
 
 extern "C" {
@@ -149,6 +192,7 @@ const char *llmint8_status_string(int status)
     case LLMINT8_ERR_UNSUPPORTED_SHAPE: return "LLMINT8_ERR_UNSUPPORTED_SHAPE: K and N must be multiples of 64, K <= 133144 (K <= 33286 for the zero-point variant; T <= 16 for the weight-streaming path)";
     case LLMINT8_ERR_WORKSPACE: return "LLMINT8_ERR_WORKSPACE: workspace smaller than the size query";
     case LLMINT8_ERR_HIP: return "LLMINT8_ERR_HIP: a kernel launch failed";
+    case LLMINT8_ERR_SCRATCH: return "LLMINT8_ERR_SCRATCH: the call needs more workspace than the static scratch of llmint8_matmul_noalloc (LLMINT8_NOALLOC_SCRATCH_BYTES = 64 MiB)";
     default: return "LLMINT8: unknown status";
     }
 }
@@ -210,20 +254,35 @@ llmint8_status_t llmint8_quantize_act(const uint16_t *X, int64_t T, int64_t K, f
 }
 
 namespace {
+// The argument and shape checks of a matmul call, in the documented order
+// (the workspace is checked by the caller).
+llmint8_status_t matmul_check(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                              const int8_t *CB, const float *SCB, const uint16_t *bias,
+                              float threshold, int activation, const uint16_t *out, int path)
+{
+    if (!X || !CB || !SCB || !out || !aligned16(X) || !aligned16(CB) || !aligned16(SCB) ||
+        !bias_ok(bias) || !aligned16(out) || bad_threshold(threshold) || path < 0 || path > 2 ||
+        (activation != LLMINT8_ACT_NONE && activation != LLMINT8_ACT_RELU))
+        return LLMINT8_ERR_INVALID_ARG;
+    const llmint8_status_t st = check_shape(T, K, N);
+    if (st != LLMINT8_OK)
+        return st;
+    if (path == 2 && T > kDecodeMaxT)
+        return LLMINT8_ERR_UNSUPPORTED_SHAPE;
+    return LLMINT8_OK;
+}
+
 llmint8_status_t matmul_impl(const uint16_t *X, int64_t T, int64_t K, int64_t N, const int8_t *CB,
                              const float *SCB, const uint16_t *bias, float threshold,
                              int activation, uint16_t *out, void *ws, size_t ws_bytes, int path,
                              hipEvent_t main_start, hipEvent_t main_stop, hipStream_t stream)
 {
-    if (!X || !CB || !SCB || !out || !ws || !aligned16(X) || !aligned16(CB) || !aligned16(SCB) ||
-        !bias_ok(bias) || !aligned16(out) || !aligned16(ws) || bad_threshold(threshold) ||
-        path < 0 || path > 2 || (activation != LLMINT8_ACT_NONE && activation != LLMINT8_ACT_RELU))
+    if (!ws || !aligned16(ws))
         return LLMINT8_ERR_INVALID_ARG;
-    llmint8_status_t st = check_shape(T, K, N);
+    const llmint8_status_t st =
+        matmul_check(X, T, K, N, CB, SCB, bias, threshold, activation, out, path);
     if (st != LLMINT8_OK)
         return st;
-    if (path == 2 && T > kDecodeMaxT)
-        return LLMINT8_ERR_UNSUPPORTED_SHAPE;
     const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
     const MatmulWorkspace L = matmul_workspace_layout(T, K, N, decode);
     if (ws_bytes < L.total)
@@ -278,6 +337,23 @@ llmint8_status_t llmint8_matmul(const uint16_t *X, int64_t T, int64_t K, int64_t
 {
     return llmint8_matmul_path(X, T, K, N, CB, SCB, bias, threshold, out, ws, ws_bytes, 0,
                                nullptr, nullptr, stream);
+}
+
+llmint8_status_t llmint8_matmul_noalloc(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                        const int8_t *CB, const float *SCB, const uint16_t *bias,
+                                        float threshold, uint16_t *out, hipStream_t stream)
+{
+    const llmint8_status_t st =
+        matmul_check(X, T, K, N, CB, SCB, bias, threshold, LLMINT8_ACT_NONE, out, 0);
+    if (st != LLMINT8_OK)
+        return st;
+    if (llmint8_workspace_bytes(T, K, N) > kNoAllocBytes)
+        return LLMINT8_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (device_scratch(&ws) != hipSuccess)
+        return LLMINT8_ERR_HIP;
+    return matmul_impl(X, T, K, N, CB, SCB, bias, threshold, LLMINT8_ACT_NONE, out, ws,
+                       kNoAllocBytes, 0, nullptr, nullptr, stream);
 }
 
 llmint8_status_t llmint8_quantize_weight_zp(const uint16_t *W_t, int64_t K, int64_t N, int8_t *CB,

@@ -17,6 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllmint8
 _lib = None
 
 LLMINT8_OK = 0
+LLMINT8_ERR_SCRATCH = 5
 PATH_AUTO, PATH_GEMM, PATH_DECODE = 0, 1, 2
 ACT_NONE, ACT_RELU = 0, 1
 
@@ -40,6 +41,7 @@ EXPORTS = (
     "llmint8_matmul_f8",
     "llmint8_matmul_f8_path",
     "llmint8_mfma_ceiling",
+    "llmint8_matmul_noalloc",
 )
 
 
@@ -87,11 +89,13 @@ def _load():
     lib.llmint8_matmul_f8.argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ, P]
     lib.llmint8_matmul_f8_path.argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ, I, P, P, P]
     lib.llmint8_mfma_ceiling.argtypes = [P, I64, P, I64, I64, I, I, I, P, P, P, P]
+    lib.llmint8_matmul_noalloc.argtypes = [P, I64, I64, I64, P, P, P, F, P, P]
     for fn in ("llmint8_quantize_weight", "llmint8_quantize_act", "llmint8_matmul",
                "llmint8_matmul_act", "llmint8_matmul_path", "llmint8_igemm_i32",
                "llmint8_quantize_weight_zp", "llmint8_quantize_act_zp", "llmint8_matmul_zp",
                "llmint8_matmul_zp_path", "llmint8_quantize_weight_f8", "llmint8_quantize_act_f8",
-               "llmint8_matmul_f8", "llmint8_matmul_f8_path", "llmint8_mfma_ceiling"):
+               "llmint8_matmul_f8", "llmint8_matmul_f8_path", "llmint8_mfma_ceiling",
+               "llmint8_matmul_noalloc"):
         getattr(lib, fn).restype = I
     _lib = lib
     return lib
@@ -280,6 +284,25 @@ def llmint8_matmul_act(X, CB, SCB, threshold=6.0, activation=ACT_NONE, bias=None
            lib.llmint8_matmul_act(X.data_ptr(), T, K, N, CB.data_ptr(), SCB.data_ptr(), _ptr(bias),
                                   float(threshold), int(activation), out.data_ptr(), ws.data_ptr(),
                                   _nbytes(ws), _stream(X)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # LLMINT8_NOALLOC_SCRATCH_BYTES
+
+
+def llmint8_matmul_noalloc(X, CB, SCB, out, threshold=6.0, bias=None):
+    """llmint8_matmul on the library's static device scratch instead of a
+    workspace (for callers that cannot allocate; calls that overlap on one
+    device race).  `out` [T,N] fp16 is required: nothing is allocated here
+    either.  Calls whose workspace query exceeds NOALLOC_SCRATCH_BYTES raise
+    LLMInt8Error (LLMINT8_ERR_SCRATCH)."""
+    lib = _load()
+    T, K, N = _matmul_operands(X, CB, SCB, bias, (torch.int8,))
+    _arg(out, "out", _H, shape=(T, N))
+    _on_device(X=X, CB=CB, SCB=SCB, bias=bias, out=out)
+    _check("llmint8_matmul_noalloc",
+           lib.llmint8_matmul_noalloc(X.data_ptr(), T, K, N, CB.data_ptr(), SCB.data_ptr(),
+                                      _ptr(bias), float(threshold), out.data_ptr(), _stream(X)))
     return out
 
 

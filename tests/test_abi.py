@@ -54,7 +54,7 @@ def test_no_internal_symbols_exported():
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         s = L.llmint8_status_string(code)
         assert s.startswith("LLMINT8_")
     assert "unknown" in L.llmint8_status_string(99)
@@ -128,6 +128,27 @@ def test_validation_order_and_codes(lib):
     # argument errors win over shape errors, shape errors over workspace errors
     assert _matmul(lib, X=None, K=96, wsb=0) == 1
     assert _matmul(lib, K=96, wsb=0) == 2
+
+
+def test_noalloc_validates_before_touching_the_device(lib):
+    def mm(X=P, T=8, K=64, N=64, SCB=P, bias=None, thr=6.0, out=P):
+        return lib.llmint8_matmul_noalloc(X, T, K, N, P, SCB, bias, thr, out, None)
+    assert mm(X=None) == 1
+    assert mm(out=P + 8) == 1
+    assert mm(SCB=P + 4) == 1
+    assert mm(thr=float("nan")) == 1
+    assert mm(K=96) == 2
+    assert mm(T=17, K=96) == 2
+    # over the static scratch: rejected with its own code, before any HIP call
+    limit = 64 << 20
+    assert L.NOALLOC_SCRATCH_BYTES == limit
+    for T, K, N in ((4096, 16384, 16384), (8192, 8192, 4096), (4096, 12288, 12288)):
+        assert L.llmint8_workspace_bytes(T, K, N) > limit
+        assert mm(T=T, K=K, N=N) == 5
+    # sizes the header names as fitting
+    for T, K, N in ((4096, 4096, 16384), (2048, 16384, 4096), (16, 133120, 65536)):
+        assert L.llmint8_workspace_bytes(T, K, N) <= limit, (T, K, N)
+    assert "static scratch" in L.llmint8_status_string(5)
 
 
 def test_other_entry_points_validate(lib):
