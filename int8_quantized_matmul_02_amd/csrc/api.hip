@@ -65,23 +65,6 @@ MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N, bool de
     return L;
 }
 
-int compute_units()
-{
-    constexpr int kMaxDevices = 64;
-    static std::atomic<int> cached[kMaxDevices];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return 256;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 size_t act_workspace_bytes(int64_t K)
 {
     return detect_area_bytes(K);   // the outlier flags of the 8-column chunks

@@ -88,6 +88,15 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_void *d
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voffset, soffset, 0, 0);
 }
 
+// One 16-byte load per lane into registers through a buffer resource (lane
+// offset voffset, wave-uniform soffset); a plain function for the same
+// reason as lds_load16.
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                          uint32_t soffset)
+{
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0));
+}
+
 // s_waitcnt vmcnt(n) with expcnt/lgkmcnt left alone (gfx9 encoding).
 template <int n>
 __device__ __forceinline__ void wait_vm()
@@ -881,6 +890,36 @@ __device__ __forceinline__ uint2 dq4(unsigned w, unsigned m4, const DqRow &p)
     return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
 }
 
+// The byte mask of 4 codes from their 4 outlier flags (bit e -> byte e).
+__device__ __forceinline__ unsigned byte_mask4(unsigned m4)
+{
+    return ((m4 * 0x00204081u) & 0x01010101u) * 0xffu;
+}
+
+// dq4 for the variants whose code 0 dequantizes to +0 (absmax, FP8): the
+// codes of non-outlier columns are cleared first (bytemask), so the masking
+// costs one instruction per 4 codes, and the halves are built in place
+// (v_fma_mixlo / v_fma_mixhi: one instruction per value after the int8
+// conversion).
+template <int kVar>
+__device__ __forceinline__ uint2 dq4m(unsigned w, unsigned bytemask, const DqRow &p)
+{
+    typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+    w &= bytemask;
+    h2v h[2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const unsigned byte = (w >> (8 * e)) & 0xffu;
+        float v;
+        if constexpr (kVar == kVarF8)
+            v = e5m2_to_f(byte) * p.s;
+        else
+            v = (float)(int)(int8_t)byte * p.s;
+        h[e / 2][e % 2] = (_Float16)v;
+    }
+    return make_uint2(__builtin_bit_cast(unsigned, h[0]), __builtin_bit_cast(unsigned, h[1]));
+}
+
 // The B operand of the pass: lane l loads 16 codes (positions 16 (l % 4) ..
 // of the stage) of weight row wave * kRows + 16 i + l / 4 (rows past N read
 // row N-1, never stored), dequantizes them with its row's parameters and
@@ -892,7 +931,7 @@ struct BStage {
     static constexpr int kI = kRows / 16;              // 16-byte code loads per lane per stage
     static constexpr int kUnits = 4 * kI;              // 4-code conversion units per stage
     static_assert(kRows % 16 == 0, "16 rows x 4 pieces per load instruction");
-    const int8_t *tile;
+    __amdgpu_buffer_rsrc_t tile;   // the tile's rows n0 .. N-1
     uint32_t off[kI];
     int row[kI], piece;
     DqRow prm[kI];
@@ -901,7 +940,7 @@ struct BStage {
     __device__ __forceinline__ void init(const int8_t *base, int64_t ld, int64_t n0, int64_t N,
                                          const EpilogueArgs &ep, int wave, int lane)
     {
-        tile = base + n0 * ld;
+        tile = Streams<C>::rsrc(reinterpret_cast<const char *>(base + n0 * ld), (N - n0) * ld);
         piece = lane & 3;
 #pragma unroll
         for (int i = 0; i < kI; ++i) {
@@ -917,18 +956,25 @@ struct BStage {
     {
 #pragma unroll
         for (int i = 0; i < kI; ++i)
-            reg[kBuf][i] = *reinterpret_cast<const v4i *>(tile + off[i] + col);
+            reg[kBuf][i] = buf_load16(tile, off[i], (uint32_t)col);
     }
 
     // Unit u of the stage in buffer kBuf: codes 4 (u % 4) .. of load u / 4,
     // i.e. half u % 2 of chunk 2 * piece + (u % 4) / 2; m16: bit e set =
     // position 16 * piece + e is an outlier column.
+    // bm: the byte masks of the lane's 4 code words (byte_mask4 of m16's
+    // nibbles), used by the variants whose code 0 is +0
     template <int kBuf>
-    __device__ __forceinline__ void store_unit(char *stage, unsigned m16, int u) const
+    __device__ __forceinline__ void store_unit(char *stage, unsigned m16, const unsigned (&bm)[4],
+                                               int u) const
     {
         const int i = u / 4, sub = u % 4;
         const int r = row[i];
-        const uint2 h = dq4<kVar>((unsigned)reg[kBuf][i][sub], (m16 >> (4 * sub)) & 0xfu, prm[i]);
+        uint2 h;
+        if constexpr (kVar == kVarZp)
+            h = dq4<kVar>((unsigned)reg[kBuf][i][sub], (m16 >> (4 * sub)) & 0xfu, prm[i]);
+        else
+            h = dq4m<kVar>((unsigned)reg[kBuf][i][sub], bm[sub], prm[i]);
         char *sb = stage + C::BM * C::ROWB;
         *reinterpret_cast<uint2 *>(sb + r * C::ROWB + 16 * ((2 * piece + sub / 2) ^ C::swz(r)) +
                                    8 * (sub % 2)) = h;
@@ -1025,11 +1071,18 @@ __device__ __forceinline__ void outlier_gemm_pass(AccArray &accf, char *smem,
     bs.template load<0>(col(0));
     issue_a(0, 0);
     wait_vm<P::kAInstr>();                // B(0) landed
+    auto masks = [&](unsigned m, unsigned (&bm)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            bm[q] = byte_mask4((m >> (4 * q)) & 0xfu);
+    };
     {
         const unsigned m = mask16(0);
+        unsigned bm[4];
+        masks(m, bm);
 #pragma unroll
         for (int u = 0; u < BStage<P, kVar>::kUnits; ++u)
-            bs.template store_unit<0>(smem, m, u);
+            bs.template store_unit<0>(smem, m, bm, u);
     }
     bs.template load<1>(col(1));
     bs.template load<0>(col(2));
@@ -1041,24 +1094,29 @@ __device__ __forceinline__ void outlier_gemm_pass(AccArray &accf, char *smem,
     read_frags<P>(f0, stage_a(0), stage_b(0), fo[0]);
     constexpr int kU = BStage<P, kVar>::kUnits;
     constexpr int kG = P::FM + P::FN;     // groups per k-step
-    static_assert(kU <= 2 * kG, "conversion units fit two k-steps");
+    static_assert(kU <= 3 * kG, "conversion units fit three k-steps");
     // iteration kt with kt % 2 == B (compile time): stage kt in LDS buffer B,
     // B(kt+1) converted from register buffer 1-B into LDS buffer 1-B
     auto iter = [&](auto bc, int kt) {
         constexpr int B = decltype(bc)::value, NB = 1 - B;
-        pass_kstep<P>(f0, f1, stage_a(B), stage_b(B), fo[1], accf, none);
         wait_vm<kBI + P::kAInstr>();      // B(kt+1) landed; B(kt+2), A(kt+1) may be in flight
         const unsigned m = mask16(kt + 1);
+        unsigned bm[4];
+        masks(m, bm);
         char *nstage = smem + NB * P::kStageBytes;   // its readers passed the last barrier
+        // the conversion units spread evenly over the groups of three k-steps
         auto conv = [&](auto, int g, int base) {
-            const int u = base + g;
-            if (u < kU)
-                bs.template store_unit<NB>(nstage, m, u);
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (u * 3 * kG / kU == base + g)
+                    bs.template store_unit<NB>(nstage, m, bm, u);
         };
-        pass_kstep<P>(f1, f0, stage_a(B), stage_b(B), fo[2], accf,
+        pass_kstep<P>(f0, f1, stage_a(B), stage_b(B), fo[1], accf,
                       [&](auto z, int g) { conv(z, g, 0); });
-        pass_kstep<P>(f0, f1, stage_a(B), stage_b(B), fo[3], accf,
+        pass_kstep<P>(f1, f0, stage_a(B), stage_b(B), fo[2], accf,
                       [&](auto z, int g) { conv(z, g, kG); });
+        pass_kstep<P>(f0, f1, stage_a(B), stage_b(B), fo[3], accf,
+                      [&](auto z, int g) { conv(z, g, 2 * kG); });
         bs.template load<NB>(col(kt + 3));
         wait_vm<kBI>();                   // A(kt+1) landed; B(kt+3) may be in flight
         wait_lds();                       // stage kt read, B(kt+1) written
@@ -1277,49 +1335,43 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int ntm = (int)((T + C::BM - 1) / C::BM), ntn = (int)((N + C::BN - 1) / C::BN);
-    // persistent: workgroup b takes tiles b, b + G, ... (G = gridDim.x, a
-    // multiple of the XCD count when below the tile count, so a tile runs on
-    // the XCD tile_coords assumes)
-    for (int tile = blockIdx.x; tile < ntm * ntn; tile += gridDim.x) {
-        int tm, tn;
-        tile_coords(tile, ntm * ntn, ntm, ntn, C::GROUP, tm, tn);
-        const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, ntm, ntn, C::GROUP, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
 
-        using Acc = std::conditional_t<kF8, v16f, v16i>;
-        Acc acc[C::FM][C::FN];
+    using Acc = std::conditional_t<kF8, v16f, v16i>;
+    Acc acc[C::FM][C::FN];
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j)
+        for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    acc[i][j][r] = 0;
-        if (nout < K) {
-            Streams<C> st;
-            st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
-                    n0, N, wave, lane);
-            if constexpr (kF8)
-                mainloop_f8<C>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
-            else
-                run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
-        }
-        float at[C::FM];
-        int za[C::FM], ra[C::FM];
-        const int64_t tw = m0 + wm * (C::BM / C::WM) + (lane & 31);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-            const int64_t t = tw + i * 32;
-            if constexpr (kZp)
-                zp_row(ep, t < T ? t : T - 1, K, at[i], za[i], ra[i]);
-            else if constexpr (kF8)
-                at[i] = ep.a[t < T ? t : T - 1];
-            else
-                at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
-        }
-        outlier_pass<C, kRelu, kZp, kF8, Acc>(acc, at, za, ra, smem, ep, B, info, groups, mask, m0, n0,
-                                              T, K, N, nout, wm, wn, wave, lane, tid);
-        __syncthreads();   // the output tile's LDS staging is read before the next tile's loads
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0;
+    if (nout < K) {
+        Streams<C> st;
+        st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
+                n0, N, wave, lane);
+        if constexpr (kF8)
+            mainloop_f8<C>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+        else
+            run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
     }
+    float at[C::FM];
+    int za[C::FM], ra[C::FM];
+    const int64_t tw = m0 + wm * (C::BM / C::WM) + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const int64_t t = tw + i * 32;
+        if constexpr (kZp)
+            zp_row(ep, t < T ? t : T - 1, K, at[i], za[i], ra[i]);
+        else if constexpr (kF8)
+            at[i] = ep.a[t < T ? t : T - 1];
+        else
+            at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
+    }
+    outlier_pass<C, kRelu, kZp, kF8, Acc>(acc, at, za, ra, smem, ep, B, info, groups, mask, m0, n0,
+                                          T, K, N, nout, wm, wn, wave, lane, tid);
 }
 
 // The int8 GEMM (K must be a multiple of C::ROWB) with its fused epilogue
@@ -1362,22 +1414,17 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
             return e;
     }
     if (!ep.c_i32) {
-        // persistent grid: at most one workgroup per compute unit (its LDS
-        // allows no more), so a call with few outlier columns, where it
-        // exits at once, costs one dispatch round
-        const int64_t ncu = compute_units() / 8 * 8;
-        const dim3 grid_many((unsigned)(ntm * ntn <= ncu || ncu < 8 ? ntm * ntn : ncu));
         if (ep.f8)
-            hipLaunchKernelGGL((k_gemm_many<CM, false, false, true>), grid_many, dim3(CM::kThreads), 0, s,
+            hipLaunchKernelGGL((k_gemm_many<CM, false, false, true>), grid, dim3(CM::kThreads), 0, s,
                                Xq, CB, T, K, N, ep, ep.n_out, ep.groups, ep.mask);
         else if (ep.row_zp)
-            hipLaunchKernelGGL((k_gemm_many<CM, false, true>), grid_many, dim3(CM::kThreads), 0, s, Xq, CB,
+            hipLaunchKernelGGL((k_gemm_many<CM, false, true>), grid, dim3(CM::kThreads), 0, s, Xq, CB,
                                T, K, N, ep, ep.n_out, ep.groups, ep.mask);
         else if (ep.act)
-            hipLaunchKernelGGL((k_gemm_many<CM, true>), grid_many, dim3(CM::kThreads), 0, s, Xq, CB, T, K,
+            hipLaunchKernelGGL((k_gemm_many<CM, true>), grid, dim3(CM::kThreads), 0, s, Xq, CB, T, K,
                                N, ep, ep.n_out, ep.groups, ep.mask);
         else
-            hipLaunchKernelGGL((k_gemm_many<CM, false>), grid_many, dim3(CM::kThreads), 0, s, Xq, CB, T,
+            hipLaunchKernelGGL((k_gemm_many<CM, false>), grid, dim3(CM::kThreads), 0, s, Xq, CB, T,
                                K, N, ep, ep.n_out, ep.groups, ep.mask);
     }
     return hipGetLastError();

@@ -160,9 +160,6 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
     return v;
 }
 
-// Compute units of the current device (queried once per device).
-int compute_units();
-
 // Workspace segments of one llmint8_matmul call (byte offsets from the base);
 // decode: the weight-streaming path's layout (no gathered weight operand,
 // x_out for any outlier count).
