@@ -1223,14 +1223,13 @@ __device__ __forceinline__ void outlier_pass(const Acc (&acc)[C::FM][C::FN],
     write_tile<C>(smem, ep, m0, n0, T, N, tid);
 }
 
-template <class C, bool kRawI32, bool kRelu, bool kZp = false, bool kF8 = false>
-__global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__ A,
-                                                      const int8_t *__restrict__ B, int64_t T,
-                                                      int64_t K, int64_t N, EpilogueArgs ep)
+// One tile of the int8 GEMM with the up-to-32-outlier epilogue (or the raw
+// int32 store); smem: the ring, then (output path) the tile's outlier rows.
+template <class C, bool kRawI32, bool kRelu, bool kZp, bool kF8>
+__device__ __forceinline__ void gemm_tile(char *smem, const int8_t *__restrict__ A,
+                                          const int8_t *__restrict__ B, int64_t T, int64_t K,
+                                          int64_t N, const EpilogueArgs &ep)
 {
-    // the ring, then (output path) the tile's outlier rows
-    __shared__ __attribute__((aligned(1024)))
-    char smem[C::kLdsBytes + (kRawI32 ? 0 : OutlierRows<C>::kBytes)];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -1315,22 +1314,22 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
     }
 }
 
-// More than 32 outlier columns (k_gemm returns at once then, and this kernel
-// does otherwise): per tile the int8 GEMM (skipped when every column is an
+// More than 32 outlier columns (k_gemm returns at once then, and this path
+// runs otherwise): per tile the int8 GEMM (skipped when every column is an
 // outlier, e.g. threshold 0, since Xq is then all zeros), then the fused
-// fp16 pass over the outlier columns.  A kernel of its own so that the
-// registers this path needs do not cost k_gemm's epilogue; one tile per
-// block (a persistent tile loop makes the compiler spill around it).
-template <class C, bool kRelu, bool kZp = false, bool kF8 = false>
-__global__ __launch_bounds__(C::kThreads) void k_gemm_many(
-    const int8_t *__restrict__ A, const int8_t *__restrict__ B, int64_t T, int64_t K, int64_t N,
-    EpilogueArgs ep, const int32_t *__restrict__ info, const int32_t *__restrict__ groups,
-    const uint8_t *__restrict__ mask)
+// fp16 pass over the outlier columns.  A kernel of its own (k_gemm_many)
+// where k_gemm runs another tile shape, so that the registers this path
+// needs do not cost k_gemm's epilogue; one launch with k_gemm (k_gemm_both)
+// where both run the same shape; one tile per block (a persistent tile loop
+// makes the compiler spill around it).  smem is the ring.
+template <class C, bool kRelu, bool kZp, bool kF8>
+__device__ __forceinline__ void many_tile(char *smem, const int8_t *__restrict__ A,
+                                          const int8_t *__restrict__ B, int64_t T, int64_t K,
+                                          int64_t N, const EpilogueArgs &ep,
+                                          const int32_t *__restrict__ info,
+                                          const int32_t *__restrict__ groups,
+                                          const uint8_t *__restrict__ mask, int nout)
 {
-    const int nout = info[0];
-    if (nout <= kOutlierPad)
-        return;
-    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -1374,6 +1373,46 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(
                                           T, K, N, nout, wm, wn, wave, lane, tid);
 }
 
+template <class C, bool kRawI32, bool kRelu, bool kZp = false, bool kF8 = false>
+__global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__ A,
+                                                      const int8_t *__restrict__ B, int64_t T,
+                                                      int64_t K, int64_t N, EpilogueArgs ep)
+{
+    __shared__ __attribute__((aligned(1024)))
+    char smem[C::kLdsBytes + (kRawI32 ? 0 : OutlierRows<C>::kBytes)];
+    gemm_tile<C, kRawI32, kRelu, kZp, kF8>(smem, A, B, T, K, N, ep);
+}
+
+template <class C, bool kRelu, bool kZp = false, bool kF8 = false>
+__global__ __launch_bounds__(C::kThreads) void k_gemm_many(
+    const int8_t *__restrict__ A, const int8_t *__restrict__ B, int64_t T, int64_t K, int64_t N,
+    EpilogueArgs ep, const int32_t *__restrict__ info, const int32_t *__restrict__ groups,
+    const uint8_t *__restrict__ mask)
+{
+    const int nout = info[0];
+    if (nout <= kOutlierPad)
+        return;
+    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
+    many_tile<C, kRelu, kZp, kF8>(smem, A, B, T, K, N, ep, info, groups, mask, nout);
+}
+
+// Both output paths in one launch, the path chosen per call from the outlier
+// count on the device: when both run in the same tile shape (and so the same
+// register budget), this saves the second, idle launch.
+template <class C, bool kRelu>
+__global__ __launch_bounds__(C::kThreads) void k_gemm_both(
+    const int8_t *__restrict__ A, const int8_t *__restrict__ B, int64_t T, int64_t K, int64_t N,
+    EpilogueArgs ep, const int32_t *__restrict__ info, const int32_t *__restrict__ groups,
+    const uint8_t *__restrict__ mask)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes + OutlierRows<C>::kBytes];
+    const int nout = info[0];
+    if (nout > kOutlierPad)
+        many_tile<C, kRelu, false, false>(smem, A, B, T, K, N, ep, info, groups, mask, nout);
+    else
+        gemm_tile<C, false, kRelu, false, false>(smem, A, B, T, K, N, ep);
+}
+
 // The int8 GEMM (K must be a multiple of C::ROWB) with its fused epilogue
 // (and the output activation, ep.act, a template parameter of the output
 // kernels); for the output (not the raw int32 sums) also k_gemm_many, of
@@ -1392,6 +1431,25 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
         const hipError_t e = hipEventRecord(ev0, s);
         if (e != hipSuccess)
             return e;
+    }
+    // absmax output with both paths in the same 128-byte-stage shape: one
+    // launch (measured: 261 -> 259 us at 4096 x 4096 x 16384, 53.4 -> 52.0 us at
+    // 2048 x 2048 x 8192; the 64-byte-stage shape spills more combined)
+    if constexpr (std::is_same_v<C, CM> && C::ROWB == 128) {
+        if (!ep.c_i32 && !ep.f8 && !ep.row_zp) {
+            if (ep.act)
+                hipLaunchKernelGGL((k_gemm_both<C, true>), grid, dim3(C::kThreads), 0, s, Xq, CB,
+                                   T, K, N, ep, ep.n_out, ep.groups, ep.mask);
+            else
+                hipLaunchKernelGGL((k_gemm_both<C, false>), grid, dim3(C::kThreads), 0, s, Xq,
+                                   CB, T, K, N, ep, ep.n_out, ep.groups, ep.mask);
+            if (ev1) {
+                const hipError_t e = hipEventRecord(ev1, s);
+                if (e != hipSuccess)
+                    return e;
+            }
+            return hipGetLastError();
+        }
     }
     if (ep.c_i32)
         hipLaunchKernelGGL((k_gemm<C, true, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K,
