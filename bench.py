@@ -577,7 +577,8 @@ def main():
         "config": {"workload": "6.7B-style FFN fc1: X[4096,4096] fp16, 6 outlier dims +-U(20,60) in 75% "
                                "of rows, W[4096,16384] int8 CB+SCB, threshold 6.0",
                    "T": T, "K": K, "N": N, "threshold": thr, "n_outliers": n_outliers},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm (int8 MFMA GEMM + fused epilogue)",
+        "roofline": {"bound": "mfma", "kernel": "k_gemm_both (int8 MFMA GEMM + fused epilogue; "
+                                                 "its many-outlier path is idle at 6 outlier columns)",
                      "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                      "frac": round(achieved / INT8_PEAK_TOPS, 4),
                      "traffic": profiled_traffic("k_gemm_ffn_6p7b_fc1.txt"),
