@@ -382,6 +382,11 @@ int64_t oracle_matmul(const uint16_t *X, int64_t T, int64_t K, int64_t N,
 /*   - the fp16 outlier product uses the weight dequantized as               */
 /*     fp16(fp32(CB + zp) / nd) (one fp32 division, then one rounding to     */
 /*     fp16; 0 when nd = 0).                                                 */
+/* Parity unpinned: the last bit of d and nd.  The pages fix no precision    */
+/* for them; fp32 is a reading, and the pins that recompute d and nd in      */
+/* numpy fp32 check this code against that reading, not the reading against */
+/* the pages.  Everything downstream of nd (codes, zp, code sums, products)  */
+/* is pinned against exact rationals and closed forms.                       */
 /* ------------------------------------------------------------------------ */
 
 /* Exact product of an fp32 scale and an fp16 value (24 + 11 significant bits
