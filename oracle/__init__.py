@@ -74,6 +74,13 @@ def _load():
     lib.oracle_quantize_rows_f8.argtypes = [P, I64, I64, P, I64, P, I64, P, P]
     lib.oracle_matmul_f8.argtypes = [P, I64, I64, I64, P, P, P, ctypes.c_float,
                                      P, I64, P, I64, P, P, P, P]
+    lib.oracle_e4m3_to_double_n.argtypes = [P, I64, P]
+    lib.oracle_double_to_e4m3_n.argtypes = [P, I64, P]
+    lib.oracle_f8_scale_exp_fmt_n.argtypes = [P, I64, P, ctypes.c_int]
+    lib.oracle_quantize_weight_f8_fmt.argtypes = [P, I64, I64, P, P, ctypes.c_int]
+    lib.oracle_quantize_rows_f8_fmt.argtypes = [P, I64, I64, P, I64, P, I64, P, P, ctypes.c_int]
+    lib.oracle_matmul_f8_fmt.argtypes = [P, I64, I64, I64, P, P, P, ctypes.c_float,
+                                         P, I64, P, I64, P, P, P, P, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -316,24 +323,49 @@ def double_to_e5m2(v):
     return out
 
 
-def f8_scale_exp(amax):
-    a = np.ascontiguousarray(amax, np.float64)
-    out = np.empty(a.shape, np.int32)
-    _load().oracle_f8_scale_exp_n(_ptr(a), a.size, _ptr(out))
+def e4m3_to_double(c):
+    c = np.ascontiguousarray(c, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e4m3_to_double_n(_ptr(c), c.size, _ptr(out))
     return out
 
 
-def quantize_weight_f8(W_t):
-    """W_t: [N,K] fp16.  Returns (CB8 [N,K] uint8 E5M2 codes, SC8 [N] f32 scales 2^-e)."""
+def double_to_e4m3(v):
+    v = np.ascontiguousarray(v, np.float64)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_double_to_e4m3_n(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+# FP8 formats: E5M2 (the pages' kind) and E4M3 (largest finite 448)
+F8_FORMATS = {"e5m2": 1, "e4m3": 2}
+
+
+def f8_to_double(c, fmt="e5m2"):
+    return e4m3_to_double(c) if fmt == "e4m3" else e5m2_to_double(c)
+
+
+def f8_scale_exp(amax, fmt="e5m2"):
+    a = np.ascontiguousarray(amax, np.float64)
+    out = np.empty(a.shape, np.int32)
+    if fmt == "e5m2":
+        _load().oracle_f8_scale_exp_n(_ptr(a), a.size, _ptr(out))
+    else:
+        _load().oracle_f8_scale_exp_fmt_n(_ptr(a), a.size, _ptr(out), F8_FORMATS[fmt])
+    return out
+
+
+def quantize_weight_f8(W_t, fmt="e5m2"):
+    """W_t: [N,K] fp16.  Returns (CB8 [N,K] uint8 codes of the format, SC8 [N] f32 scales 2^-e)."""
     W_t = _bits(W_t)
     N, K = W_t.shape
     CB8 = np.empty((N, K), np.uint8)
     SC8 = np.empty((N,), np.float32)
-    _load().oracle_quantize_weight_f8(_ptr(W_t), K, N, _ptr(CB8), _ptr(SC8))
+    _load().oracle_quantize_weight_f8_fmt(_ptr(W_t), K, N, _ptr(CB8), _ptr(SC8), F8_FORMATS[fmt])
     return CB8, SC8
 
 
-def quantize_rows_f8(X, O, rows=None):
+def quantize_rows_f8(X, O, rows=None, fmt="e5m2"):
     """Returns (Xq8 [nrows,K] uint8, sc8 [nrows] f32) for the listed rows."""
     X = _bits(X)
     T, K = X.shape
@@ -342,14 +374,15 @@ def quantize_rows_f8(X, O, rows=None):
     nrows = T if rows_arr is None else rows_arr.size
     Xq8 = np.empty((nrows, K), np.uint8)
     sc8 = np.empty((nrows,), np.float32)
-    _load().oracle_quantize_rows_f8(_ptr(X), T, K, _ptr(O), O.size, _ptr(rows_arr), nrows,
-                                    _ptr(Xq8), _ptr(sc8))
+    _load().oracle_quantize_rows_f8_fmt(_ptr(X), T, K, _ptr(O), O.size, _ptr(rows_arr), nrows,
+                                        _ptr(Xq8), _ptr(sc8), F8_FORMATS[fmt])
     return Xq8, sc8
 
 
-def matmul_f8(X, CB8, SC8, threshold=6.0, bias=None, rows=None, cols=None):
-    """The decomposition with the non-outlier part in E5M2.  Returns
-    (out [nrows,ncols] uint16 binary16 bits, O int32, sc8 [nrows] f32)."""
+def matmul_f8(X, CB8, SC8, threshold=6.0, bias=None, rows=None, cols=None, fmt="e5m2"):
+    """The decomposition with the non-outlier part in FP8 (E5M2, or E4M3 with
+    fmt="e4m3").  Returns (out [nrows,ncols] uint16 binary16 bits, O int32,
+    sc8 [nrows] f32)."""
     X = _bits(X)
     T, K = X.shape
     CB8 = np.ascontiguousarray(CB8, np.uint8)
@@ -365,7 +398,7 @@ def matmul_f8(X, CB8, SC8, threshold=6.0, bias=None, rows=None, cols=None):
     O = np.empty((max(K, 1),), np.int32)
     n = np.zeros((1,), np.int64)
     sc = np.empty((max(nrows, 1),), np.float32)
-    _load().oracle_matmul_f8(_ptr(X), T, K, N, _ptr(CB8), _ptr(SC8), _ptr(b), float(threshold),
-                             _ptr(rows_arr), nrows, _ptr(cols_arr), ncols, _ptr(out), _ptr(O),
-                             _ptr(n), _ptr(sc))
+    _load().oracle_matmul_f8_fmt(_ptr(X), T, K, N, _ptr(CB8), _ptr(SC8), _ptr(b),
+                                 float(threshold), _ptr(rows_arr), nrows, _ptr(cols_arr), ncols,
+                                 _ptr(out), _ptr(O), _ptr(n), _ptr(sc), F8_FORMATS[fmt])
     return out, O[: int(n[0])].copy(), sc[:nrows].copy()

@@ -651,9 +651,107 @@ int oracle_f8_scale_exp(double amax)
     return e;
 }
 
+/* ------------------------------------------------------------------------ */
+/* E4M3, the other common 8-bit floating-point format (4 exponent bits with  */
+/* bias 7, 3 fraction bits, the "fn" layout: no infinities, S.1111.111 is    */
+/* NaN, largest finite 1.75 * 2^8 = 448, subnormals step 2^-9).  The pages   */
+/* name only the 5-bit-exponent kind; the E4M3 form of the variant takes     */
+/* every reading of the E5M2 one with this format in its place (the scale    */
+/* targets 448).                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Exact value of an E4M3 code. */
+double oracle_e4m3_to_double(uint8_t c)
+{
+    int sign = (c >> 7) & 1;
+    int e = (c >> 3) & 15;
+    int f = c & 7;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -9);               /* subnormal: f/8 * 2^-6 */
+    else if (e == 15 && f == 7)
+        v = NAN;
+    else
+        v = ldexp((double)(8 + f), e - 10);     /* (1 + f/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* Nearest E4M3 code to v, ties to even; a value that rounds above 448
+ * (|v| > 464, past the tie with the next step, which goes to the even 448)
+ * has no code and gives NaN. */
+uint8_t oracle_double_to_e4m3(double v)
+{
+    if (isnan(v))
+        return 0x7f;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return sign | 0x7f;
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;                     /* a in [2^E, 2^(E+1)) */
+    if (E < -6)
+        E = -6;                         /* subnormals share the lowest binade's spacing */
+    if (E > 8)
+        return sign | 0x7f;
+    double ulp = ldexp(1.0, E - 3);
+    double q = a / ulp;                 /* exact */
+    double r = floor(q);
+    double frac = q - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0))
+        r += 1.0;
+    if (r >= 16.0) {                    /* carried into the next binade */
+        r = 8.0;
+        E += 1;
+    }
+    if (E > 8 || (E == 8 && r > 14.0))  /* beyond 448 */
+        return sign | 0x7f;
+    if (r < 8.0)                        /* only for E == -6: subnormal */
+        return sign | (uint8_t)r;
+    return sign | (uint8_t)(((E + 7) << 3) | ((int)r - 8));
+}
+
+/* Format codes of the FP8 functions below: 1 = E5M2, 2 = E4M3. */
+static double f8_value(uint8_t c, int fmt)
+{
+    return fmt == 2 ? oracle_e4m3_to_double(c) : oracle_e5m2_to_double(c);
+}
+
+static uint8_t f8_code(double v, int fmt)
+{
+    return fmt == 2 ? oracle_double_to_e4m3(v) : oracle_double_to_e5m2(v);
+}
+
+/* The scaling exponent in format fmt: the largest e with amax * 2^e at most
+ * the format's largest finite value (57344 or 448); 0 when amax is 0. */
+int oracle_f8_scale_exp_fmt(double amax, int fmt)
+{
+    if (fmt != 2)
+        return oracle_f8_scale_exp(amax);
+    if (amax == 0.0)
+        return 0;
+    int e = 0;
+    while (ldexp(amax, e) > 448.0)
+        --e;
+    while (ldexp(amax, e + 1) <= 448.0)
+        ++e;
+    return e;
+}
+
 /* W_t: [N,K] binary16.  CB8: [N,K] E5M2 codes, SC8: [N] scale 2^-e. */
+void oracle_quantize_weight_f8_fmt(const uint16_t *W_t, int64_t K, int64_t N,
+                                   uint8_t *CB8, float *SC8, int fmt);
 void oracle_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N,
                                uint8_t *CB8, float *SC8)
+{
+    oracle_quantize_weight_f8_fmt(W_t, K, N, CB8, SC8, 1);
+}
+
+/* The same in format fmt (codes of that format, scale 2^-e for its e). */
+void oracle_quantize_weight_f8_fmt(const uint16_t *W_t, int64_t K, int64_t N,
+                                   uint8_t *CB8, float *SC8, int fmt)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
@@ -662,19 +760,19 @@ void oracle_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N,
         for (int64_t k = 0; k < K; ++k)
             if (half_abs_bits(row[k]) > amax)
                 amax = half_abs_bits(row[k]);
-        int e = oracle_f8_scale_exp(oracle_half_to_double(amax));
+        int e = oracle_f8_scale_exp_fmt(oracle_half_to_double(amax), fmt);
         SC8[n] = (float)ldexp(1.0, -e);
         for (int64_t k = 0; k < K; ++k)
-            CB8[n * K + k] = oracle_double_to_e5m2(ldexp(oracle_half_to_double(row[k]), e));
+            CB8[n * K + k] = f8_code(ldexp(oracle_half_to_double(row[k]), e), fmt);
     }
 }
 
 /* For each listed row t: the scale over the non-outlier columns, Xq8[i,k] =
- * +0 for k in O, else the E5M2 code of X[t,k] * 2^e. */
-void oracle_quantize_rows_f8(const uint16_t *X, int64_t T, int64_t K,
-                             const int32_t *O, int64_t n,
-                             const int64_t *rows, int64_t nrows,
-                             uint8_t *Xq8, float *sc8)
+ * +0 for k in O, else the code (format fmt) of X[t,k] * 2^e. */
+void oracle_quantize_rows_f8_fmt(const uint16_t *X, int64_t T, int64_t K,
+                                 const int32_t *O, int64_t n,
+                                 const int64_t *rows, int64_t nrows,
+                                 uint8_t *Xq8, float *sc8, int fmt)
 {
     unsigned char *isout = outlier_mask(O, n, K);
     if (rows == NULL)
@@ -687,12 +785,21 @@ void oracle_quantize_rows_f8(const uint16_t *X, int64_t T, int64_t K,
         for (int64_t k = 0; k < K; ++k)
             if (!isout[k] && half_abs_bits(xr[k]) > amax)
                 amax = half_abs_bits(xr[k]);
-        int e = oracle_f8_scale_exp(oracle_half_to_double(amax));
+        int e = oracle_f8_scale_exp_fmt(oracle_half_to_double(amax), fmt);
         sc8[i] = (float)ldexp(1.0, -e);
         for (int64_t k = 0; k < K; ++k)
-            Xq8[i * K + k] = isout[k] ? 0 : oracle_double_to_e5m2(ldexp(oracle_half_to_double(xr[k]), e));
+            Xq8[i * K + k] = isout[k] ? 0 : f8_code(ldexp(oracle_half_to_double(xr[k]), e), fmt);
     }
     free(isout);
+}
+
+/* E5M2 rows (the original form). */
+void oracle_quantize_rows_f8(const uint16_t *X, int64_t T, int64_t K,
+                             const int32_t *O, int64_t n,
+                             const int64_t *rows, int64_t nrows,
+                             uint8_t *Xq8, float *sc8)
+{
+    oracle_quantize_rows_f8_fmt(X, T, K, O, n, rows, nrows, Xq8, sc8, 1);
 }
 
 /* Dequantized fp16 weight of an E5M2 code with scale sc (a power of two):
@@ -702,15 +809,38 @@ uint16_t oracle_dequant_weight_f8(uint8_t c, float sc)
     return oracle_double_to_half(oracle_e5m2_to_double(c) * (double)sc);
 }
 
+/* The same for a code of format fmt. */
+uint16_t oracle_dequant_weight_f8_fmt(uint8_t c, float sc, int fmt)
+{
+    return oracle_double_to_half(f8_value(c, fmt) * (double)sc);
+}
+
 /* out[i,c] = fp16( sum_k e5m2(Xq8[t,k]) * e5m2(CB8[c,k]) * sc8[t] * SC8[c]
  *                  + sum_{k in O} X[t,k] * Wdq8(CB8[c,k], SC8[c])  [+ bias[c]] ),
  * the sum in fp64, rounded once.  Arguments as oracle_matmul; sc_out
  * ([nrows]) receives the row scales. */
+void oracle_matmul_f8_fmt(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                          const uint8_t *CB8, const float *SC8, const uint16_t *bias,
+                          float threshold, const int64_t *rows, int64_t nrows,
+                          const int64_t *cols, int64_t ncols, uint16_t *out,
+                          int32_t *O_out, int64_t *n_out, float *sc_out, int fmt);
 void oracle_matmul_f8(const uint16_t *X, int64_t T, int64_t K, int64_t N,
                       const uint8_t *CB8, const float *SC8, const uint16_t *bias,
                       float threshold, const int64_t *rows, int64_t nrows,
                       const int64_t *cols, int64_t ncols, uint16_t *out,
                       int32_t *O_out, int64_t *n_out, float *sc_out)
+{
+    oracle_matmul_f8_fmt(X, T, K, N, CB8, SC8, bias, threshold, rows, nrows, cols, ncols, out,
+                         O_out, n_out, sc_out, 1);
+}
+
+/* The same in format fmt (1 = E5M2, 2 = E4M3): codes and the dequantized
+ * outlier weights of that format. */
+void oracle_matmul_f8_fmt(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                          const uint8_t *CB8, const float *SC8, const uint16_t *bias,
+                          float threshold, const int64_t *rows, int64_t nrows,
+                          const int64_t *cols, int64_t ncols, uint16_t *out,
+                          int32_t *O_out, int64_t *n_out, float *sc_out, int fmt)
 {
     if (rows == NULL)
         nrows = T;
@@ -720,10 +850,10 @@ void oracle_matmul_f8(const uint16_t *X, int64_t T, int64_t K, int64_t N,
     int64_t n = oracle_outlier_columns(X, T, K, threshold, O);
     uint8_t *Xq8 = (uint8_t *)malloc((size_t)(nrows * K > 0 ? nrows * K : 1));
     float *sc = (float *)malloc(sizeof(float) * (size_t)(nrows > 0 ? nrows : 1));
-    oracle_quantize_rows_f8(X, T, K, O, n, rows, nrows, Xq8, sc);
+    oracle_quantize_rows_f8_fmt(X, T, K, O, n, rows, nrows, Xq8, sc, fmt);
     double lut[256];
     for (int v = 0; v < 256; ++v)
-        lut[v] = oracle_e5m2_to_double((uint8_t)v);
+        lut[v] = f8_value((uint8_t)v, fmt);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < nrows; ++i) {
         int64_t t = rows ? rows[i] : i;
@@ -736,7 +866,7 @@ void oracle_matmul_f8(const uint16_t *X, int64_t T, int64_t K, int64_t N,
             for (int64_t jj = 0; jj < n; ++jj) {
                 int64_t k = O[jj];
                 acc += oracle_half_to_double(X[t * K + k]) *
-                       oracle_half_to_double(oracle_dequant_weight_f8(CB8[c * K + k], SC8[c]));
+                       oracle_half_to_double(oracle_dequant_weight_f8_fmt(CB8[c * K + k], SC8[c], fmt));
             }
             if (bias)
                 acc += oracle_half_to_double(bias[c]);
@@ -770,6 +900,24 @@ void oracle_f8_scale_exp_n(const double *a, int64_t len, int32_t *out)
 {
     for (int64_t i = 0; i < len; ++i)
         out[i] = oracle_f8_scale_exp(a[i]);
+}
+
+void oracle_e4m3_to_double_n(const uint8_t *c, int64_t len, double *out)
+{
+    for (int64_t i = 0; i < len; ++i)
+        out[i] = oracle_e4m3_to_double(c[i]);
+}
+
+void oracle_double_to_e4m3_n(const double *v, int64_t len, uint8_t *out)
+{
+    for (int64_t i = 0; i < len; ++i)
+        out[i] = oracle_double_to_e4m3(v[i]);
+}
+
+void oracle_f8_scale_exp_fmt_n(const double *a, int64_t len, int32_t *out, int fmt)
+{
+    for (int64_t i = 0; i < len; ++i)
+        out[i] = oracle_f8_scale_exp_fmt(a[i], fmt);
 }
 
 /* Number of threads the parallel loops use (for reporting the CPU baseline). */
