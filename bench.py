@@ -372,23 +372,27 @@ def zeropoint_bench(torch, L, workloads, steps, warmup, ev, dev):
     return res
 
 
-def fp8_bench(torch, L, workloads, steps, warmup, ev, dev):
-    """The FP8 (E5M2) variant on the same workloads: fc1 (the GEMM path,
-    v_mfma_f32_32x32x64_f8f6f4; roofline: the dense fp8 peak, 5.0 PFLOP/s)
-    and the 175B decode shape at T in {1, 4, 16} (two weight copies rotated;
-    the same algorithmic bytes as the int8 weight stream)."""
+def fp8_bench(torch, L, workloads, steps, warmup, ev, dev, fmt="f8"):
+    """The FP8 variant (fmt "f8": E5M2, "e4m3": E4M3) on the same workloads:
+    fc1 (the GEMM path, v_mfma_f32_32x32x64_f8f6f4; roofline: the dense fp8
+    peak, 5.0 PFLOP/s) and the 175B decode shape at T in {1, 4, 16} (two
+    weight copies rotated; the same algorithmic bytes as the int8 weight
+    stream)."""
+    qw = getattr(L, "llmint8_quantize_weight_" + fmt)
+    mm = getattr(L, "llmint8_matmul_" + fmt)
+    mmp = getattr(L, "llmint8_matmul_%s_path" % fmt)
+    tag = "fp8" if fmt == "f8" else fmt
     res = {}
     d = workloads.ffn_6p7b(with_fc2=False)
     X = torch.from_numpy(d["X"]).to(dev)
-    CB8, SC8 = L.llmint8_quantize_weight_f8(torch.from_numpy(d["W_t"]).to(dev))
+    CB8, SC8 = qw(torch.from_numpy(d["W_t"]).to(dev))
     T, K = X.shape
     N = CB8.shape[0]
     out = torch.empty((T, N), dtype=torch.float16, device=dev)
     ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=dev)
     ms, kms, kern = timed_calls(
-        torch, lambda i: L.llmint8_matmul_f8(X, CB8, SC8, 6.0, out=out, ws=ws),
-        lambda i, a, b: L.llmint8_matmul_f8_path(X, CB8, SC8, 6.0, out=out, ws=ws,
-                                                 main_start=a, main_stop=b),
+        torch, lambda i: mm(X, CB8, SC8, 6.0, out=out, ws=ws),
+        lambda i, a, b: mmp(X, CB8, SC8, 6.0, out=out, ws=ws, main_start=a, main_stop=b),
         steps, warmup, ev)
     ops = 2.0 * T * K * N
     res["fc1"] = {"T": T, "K": K, "N": N, "threshold": 6.0, "step_us": round(ms * 1e3, 2),
@@ -396,13 +400,13 @@ def fp8_bench(torch, L, workloads, steps, warmup, ev, dev):
                   "gemm_kernel_us": round(kms * 1e3, 2),
                   "gemm_frac_fp8_peak": round(ops / (kms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
     res["fc1"].update(spread_us(kern))
-    log("fp8 fc1: %.1f us/step (%.0f TFLOP/s), GEMM kernel %.1f us (%.1f%% of the fp8 peak)"
-        % (ms * 1e3, ops / ms / 1e9, kms * 1e3, 100 * ops / (kms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS))
+    log("%s fc1: %.1f us/step (%.0f TFLOP/s), GEMM kernel %.1f us (%.1f%% of the fp8 peak)"
+        % (tag, ms * 1e3, ops / ms / 1e9, kms * 1e3, 100 * ops / (kms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS))
     del X, CB8, SC8, out, ws, d
     torch.cuda.empty_cache()
 
     d1 = workloads.decode_175b(1, with_weight=True)
-    CB8, SC8 = L.llmint8_quantize_weight_f8(torch.from_numpy(d1.pop("W_t")).to(dev))
+    CB8, SC8 = qw(torch.from_numpy(d1.pop("W_t")).to(dev))
     CBs = [CB8, CB8.clone()]
     K, N = CB8.shape[1], CB8.shape[0]
     for T in (1, 4, 16):
@@ -411,9 +415,9 @@ def fp8_bench(torch, L, workloads, steps, warmup, ev, dev):
         out = torch.empty((T, N), dtype=torch.float16, device=dev)
         ws = torch.empty((L.llmint8_workspace_bytes(T, K, N),), dtype=torch.uint8, device=dev)
         ms, kms, kern = timed_calls(
-            torch, lambda i: L.llmint8_matmul_f8(X, CBs[i % 2], SC8, 6.0, out=out, ws=ws),
-            lambda i, a, b: L.llmint8_matmul_f8_path(X, CBs[i % 2], SC8, 6.0, out=out, ws=ws,
-                                                     main_start=a, main_stop=b),
+            torch, lambda i: mm(X, CBs[i % 2], SC8, 6.0, out=out, ws=ws),
+            lambda i, a, b: mmp(X, CBs[i % 2], SC8, 6.0, out=out, ws=ws, main_start=a,
+                                main_stop=b),
             steps, warmup, ev)
         alg = K * N + 4 * N + T * K + 4 * T + 2 * T * N
         res["decode_T%d" % T] = {"kernel_us": round(kms * 1e3, 2), "step_us": round(ms * 1e3, 2),
@@ -421,8 +425,8 @@ def fp8_bench(torch, L, workloads, steps, warmup, ev, dev):
                                  "frac_hbm": round(alg / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                  "alg_bytes": alg}
         res["decode_T%d" % T].update(spread_us(kern))
-        log("fp8 decode T=%d: kernel %.1f us (%.0f GB/s), step %.1f us"
-            % (T, kms * 1e3, alg / kms / 1e6, ms * 1e3))
+        log("%s decode T=%d: kernel %.1f us (%.0f GB/s), step %.1f us"
+            % (tag, T, kms * 1e3, alg / kms / 1e6, ms * 1e3))
     del CBs, CB8, SC8
     torch.cuda.empty_cache()
     return res
@@ -513,7 +517,7 @@ def main():
     ap.add_argument("--config-steps", type=int, default=20,
                     help="timed steps per other workload (at most --steps)")
     ap.add_argument("--fp8", action="store_true",
-                    help="also time the FP8 (E5M2) variant (fc1 and the decode shape)")
+                    help="also time the FP8 variant, E5M2 and E4M3 (fc1 and the decode shape)")
     ap.add_argument("--zeropoint", action="store_true",
                     help="also time the zero-point variant (fc1 and the decode shape)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -608,6 +612,8 @@ def main():
         result["zeropoint"] = zeropoint_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
     if args.fp8:
         result["fp8"] = fp8_bench(torch, L, workloads, args.steps, args.warmup, ev, dev)
+        result["fp8_e4m3"] = fp8_bench(torch, L, workloads, args.steps, args.warmup, ev, dev,
+                                       fmt="e4m3")
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on %d rows ..." % args.cpu_rows)
         result["cpu_baseline"] = cpu_baseline(X_h, W_h, thr, args.cpu_rows)

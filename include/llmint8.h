@@ -321,6 +321,32 @@ LLMINT8_API llmint8_status_t llmint8_matmul_f8(const uint16_t *X, int64_t T, int
                                                uint16_t *out, void *ws, size_t ws_bytes,
                                                hipStream_t stream);
 
+/*
+ * The same FP8 variant in E4M3, the other 8-bit float format of the matrix
+ * cores (4 exponent bits with bias 7, 3 fraction bits, no infinities; largest
+ * finite 448, smallest subnormal 2^-9).  The page names only the 5-bit
+ * exponent kind; this form keeps every convention of the E5M2 one above with
+ * E4M3 in its place: e is the largest integer with absmax * 2^e <= 448,
+ * codes are the E4M3 values nearest to x * 2^e (ties to even), scales 2^-e,
+ * outlier columns +0, and the products are summed in fp32 by
+ * v_mfma_f32_32x32x64_f8f6f4 (format E4M3 for both operands).  Arguments,
+ * alignment, workspace and errors exactly as the _f8 functions; CB8 and Xq8
+ * hold E4M3 codes.
+ */
+LLMINT8_API llmint8_status_t llmint8_quantize_weight_e4m3(const uint16_t *W_t, int64_t K,
+                                                          int64_t N, uint8_t *CB8, float *SC8,
+                                                          hipStream_t stream);
+LLMINT8_API llmint8_status_t llmint8_quantize_act_e4m3(const uint16_t *X, int64_t T, int64_t K,
+                                                       float threshold, uint8_t *Xq8,
+                                                       float *row_scale, int32_t *outlier_idx,
+                                                       int32_t *n_outliers, void *ws,
+                                                       size_t ws_bytes, hipStream_t stream);
+LLMINT8_API llmint8_status_t llmint8_matmul_e4m3(const uint16_t *X, int64_t T, int64_t K,
+                                                 int64_t N, const uint8_t *CB8, const float *SC8,
+                                                 const uint16_t *bias, float threshold,
+                                                 uint16_t *out, void *ws, size_t ws_bytes,
+                                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,15 @@ LLMINT8_API llmint8_status_t llmint8_matmul_f8_path(const uint16_t *X, int64_t T
                                                     hipEvent_t main_start, hipEvent_t main_stop,
                                                     hipStream_t stream);
 
+/* llmint8_matmul_e4m3 with the path choice and timing events of llmint8_matmul_path. */
+LLMINT8_API llmint8_status_t llmint8_matmul_e4m3_path(const uint16_t *X, int64_t T, int64_t K,
+                                                      int64_t N, const uint8_t *CB8,
+                                                      const float *SC8, const uint16_t *bias,
+                                                      float threshold, uint16_t *out, void *ws,
+                                                      size_t ws_bytes, int path,
+                                                      hipEvent_t main_start, hipEvent_t main_stop,
+                                                      hipStream_t stream);
+
 /*
  * The int8 product alone, C[t,n] = sum_k Xq[t,k] * CB[n,k] in int32 (LLM.int8()
  * summary, section "Int8 Matrix Multiplication with 16-bit Float Inputs and

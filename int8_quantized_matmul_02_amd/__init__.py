@@ -13,6 +13,8 @@ from .llmint8 import (  # noqa: F401
     PATH_GEMM,
     LLMInt8Error,
     llmint8_igemm_i32,
+    llmint8_matmul_e4m3,
+    llmint8_matmul_e4m3_path,
     llmint8_matmul,
     llmint8_matmul_act,
     llmint8_matmul_path,
@@ -21,10 +23,12 @@ from .llmint8 import (  # noqa: F401
     llmint8_matmul_zp,
     llmint8_matmul_zp_path,
     llmint8_quantize_act,
+    llmint8_quantize_act_e4m3,
     llmint8_quantize_act_f8,
     llmint8_quantize_act_workspace_bytes,
     llmint8_quantize_act_zp,
     llmint8_quantize_weight,
+    llmint8_quantize_weight_e4m3,
     llmint8_quantize_weight_f8,
     llmint8_quantize_weight_zp,
     llmint8_status_string,

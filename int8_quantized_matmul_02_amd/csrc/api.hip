@@ -421,22 +421,25 @@ llmint8_status_t llmint8_matmul_zp(const uint16_t *X, int64_t T, int64_t K, int6
                                   0, nullptr, nullptr, stream);
 }
 
-llmint8_status_t llmint8_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N, uint8_t *CB8,
-                                            float *SC8, hipStream_t stream)
+namespace {
+// The FP8 entry points of both formats (fmt kF8E5M2 or kF8E4M3).
+llmint8_status_t quantize_weight_fp8(const uint16_t *W_t, int64_t K, int64_t N, uint8_t *CB8,
+                                     float *SC8, int fmt, hipStream_t stream)
 {
     if (!W_t || !CB8 || !SC8 || !aligned16(W_t) || !aligned16(CB8))
         return LLMINT8_ERR_INVALID_ARG;
     llmint8_status_t st = check_shape(1, K, N);
     if (st != LLMINT8_OK)
         return st;
-    return launch_quantize_weight_f8(W_t, K, N, CB8, SC8, stream) == hipSuccess ? LLMINT8_OK
-                                                                                : LLMINT8_ERR_HIP;
+    return launch_quantize_weight_f8(W_t, K, N, CB8, SC8, fmt, stream) == hipSuccess
+               ? LLMINT8_OK
+               : LLMINT8_ERR_HIP;
 }
 
-llmint8_status_t llmint8_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float threshold,
-                                         uint8_t *Xq8, float *row_scale, int32_t *outlier_idx,
-                                         int32_t *n_outliers, void *ws, size_t ws_bytes,
-                                         hipStream_t stream)
+llmint8_status_t quantize_act_fp8(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                                  uint8_t *Xq8, float *row_scale, int32_t *outlier_idx,
+                                  int32_t *n_outliers, void *ws, size_t ws_bytes, int fmt,
+                                  hipStream_t stream)
 {
     if (!X || !Xq8 || !row_scale || !outlier_idx || !n_outliers || !ws || !aligned16(X) ||
         !aligned16(Xq8) || !aligned16(ws) || bad_threshold(threshold))
@@ -448,18 +451,18 @@ llmint8_status_t llmint8_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K
         return LLMINT8_ERR_WORKSPACE;
     uint8_t *mask = static_cast<uint8_t *>(ws);
     GatherArgs none{nullptr, nullptr, 0, nullptr};
-    none.f8 = true;
+    none.f8 = fmt;
     const hipError_t e = launch_quantize_act_f8(X, T, K, threshold, Xq8, row_scale, outlier_idx,
                                                 OutlierInfoOut{n_outliers}, mask, nullptr,
-                                                none, false, stream);
+                                                none, false, fmt, stream);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
 }
 
-llmint8_status_t llmint8_matmul_f8_path(const uint16_t *X, int64_t T, int64_t K, int64_t N,
-                                        const uint8_t *CB8, const float *SC8, const uint16_t *bias,
-                                        float threshold, uint16_t *out, void *ws, size_t ws_bytes,
-                                        int path, hipEvent_t main_start, hipEvent_t main_stop,
-                                        hipStream_t stream)
+llmint8_status_t matmul_fp8_path(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                 const uint8_t *CB8, const float *SC8, const uint16_t *bias,
+                                 float threshold, uint16_t *out, void *ws, size_t ws_bytes,
+                                 int path, hipEvent_t main_start, hipEvent_t main_stop, int fmt,
+                                 hipStream_t stream)
 {
     if (!X || !CB8 || !SC8 || !out || !ws || !aligned16(X) || !aligned16(CB8) ||
         !aligned16(SC8) || !bias_ok(bias) || !aligned16(out) || !aligned16(ws) ||
@@ -478,21 +481,47 @@ llmint8_status_t llmint8_matmul_f8_path(const uint16_t *X, int64_t T, int64_t K,
     const int8_t *CB = reinterpret_cast<const int8_t *>(CB8);
 
     GatherArgs g{CB, SC8, N, p.w_out};
-    g.f8 = true;
+    g.f8 = fmt;
     const bool packed = decode && T >= kDecodePackedMinT;
     const hipError_t eq = launch_quantize_act_f8(X, T, K, threshold,
                                                  reinterpret_cast<uint8_t *>(p.xq), p.a, p.O,
                                                  info_out(p, decode), p.mask, p.x_out, g,
-                                                 packed, stream);
+                                                 packed, fmt, stream);
     if (eq != hipSuccess)
         return LLMINT8_ERR_HIP;
     EpilogueArgs ep{p.a, SC8, p.x_out, p.w_out, p.O, p.info, bias, out, nullptr, 0};
-    ep.f8 = true;
+    ep.f8 = fmt;
     dense_args(ep, X, p);
     const hipError_t e =
         decode ? launch_decode(p.xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
                : launch_gemm(p.xq, CB, T, K, N, ep, stream, main_start, main_stop);
     return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP;
+}
+}  // namespace
+
+llmint8_status_t llmint8_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N, uint8_t *CB8,
+                                            float *SC8, hipStream_t stream)
+{
+    return quantize_weight_fp8(W_t, K, N, CB8, SC8, kF8E5M2, stream);
+}
+
+llmint8_status_t llmint8_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float threshold,
+                                         uint8_t *Xq8, float *row_scale, int32_t *outlier_idx,
+                                         int32_t *n_outliers, void *ws, size_t ws_bytes,
+                                         hipStream_t stream)
+{
+    return quantize_act_fp8(X, T, K, threshold, Xq8, row_scale, outlier_idx, n_outliers, ws,
+                            ws_bytes, kF8E5M2, stream);
+}
+
+llmint8_status_t llmint8_matmul_f8_path(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                        const uint8_t *CB8, const float *SC8, const uint16_t *bias,
+                                        float threshold, uint16_t *out, void *ws, size_t ws_bytes,
+                                        int path, hipEvent_t main_start, hipEvent_t main_stop,
+                                        hipStream_t stream)
+{
+    return matmul_fp8_path(X, T, K, N, CB8, SC8, bias, threshold, out, ws, ws_bytes, path,
+                           main_start, main_stop, kF8E5M2, stream);
 }
 
 llmint8_status_t llmint8_matmul_f8(const uint16_t *X, int64_t T, int64_t K, int64_t N,
@@ -502,6 +531,41 @@ llmint8_status_t llmint8_matmul_f8(const uint16_t *X, int64_t T, int64_t K, int6
 {
     return llmint8_matmul_f8_path(X, T, K, N, CB8, SC8, bias, threshold, out, ws, ws_bytes, 0,
                                   nullptr, nullptr, stream);
+}
+
+llmint8_status_t llmint8_quantize_weight_e4m3(const uint16_t *W_t, int64_t K, int64_t N,
+                                              uint8_t *CB8, float *SC8, hipStream_t stream)
+{
+    return quantize_weight_fp8(W_t, K, N, CB8, SC8, kF8E4M3, stream);
+}
+
+llmint8_status_t llmint8_quantize_act_e4m3(const uint16_t *X, int64_t T, int64_t K,
+                                           float threshold, uint8_t *Xq8, float *row_scale,
+                                           int32_t *outlier_idx, int32_t *n_outliers, void *ws,
+                                           size_t ws_bytes, hipStream_t stream)
+{
+    return quantize_act_fp8(X, T, K, threshold, Xq8, row_scale, outlier_idx, n_outliers, ws,
+                            ws_bytes, kF8E4M3, stream);
+}
+
+llmint8_status_t llmint8_matmul_e4m3_path(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                          const uint8_t *CB8, const float *SC8,
+                                          const uint16_t *bias, float threshold, uint16_t *out,
+                                          void *ws, size_t ws_bytes, int path,
+                                          hipEvent_t main_start, hipEvent_t main_stop,
+                                          hipStream_t stream)
+{
+    return matmul_fp8_path(X, T, K, N, CB8, SC8, bias, threshold, out, ws, ws_bytes, path,
+                           main_start, main_stop, kF8E4M3, stream);
+}
+
+llmint8_status_t llmint8_matmul_e4m3(const uint16_t *X, int64_t T, int64_t K, int64_t N,
+                                     const uint8_t *CB8, const float *SC8, const uint16_t *bias,
+                                     float threshold, uint16_t *out, void *ws, size_t ws_bytes,
+                                     hipStream_t stream)
+{
+    return llmint8_matmul_e4m3_path(X, T, K, N, CB8, SC8, bias, threshold, out, ws, ws_bytes, 0,
+                                    nullptr, nullptr, stream);
 }
 
 llmint8_status_t llmint8_igemm_i32(const int8_t *Xq, int64_t T, int64_t K, int64_t N,

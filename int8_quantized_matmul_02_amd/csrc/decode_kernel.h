@@ -77,10 +77,12 @@ __device__ __forceinline__ OutlierPrefetch prefetch_outliers(const int8_t *B, in
 // and the integer part is the shifted sum C + zp_b*(rs_a + K*zp_a) +
 // zp_a*rs_b, exact in wrapping 32-bit arithmetic (its true value fits int32),
 // divided by nd_a*nd_b; the outlier weights are fp16((cb + zp_b)/nd_b).
-// FP8 variant (kF8): fp32 sums of E5M2 products, scaled by the row and
-// column scales (powers of two); the outlier weights are fp16(E5M2 * scale).
-template <bool kRawI32, bool kRelu = false, bool kZp = false, bool kF8 = false>
-__device__ __forceinline__ void epilogue(const std::conditional_t<kF8, v4f, v4i> acc, int lane,
+// FP8 variant (kF8, the format): fp32 sums of the FP8 products, scaled by
+// the row and column scales (powers of two); the outlier weights are
+// fp16(code value * scale).
+template <bool kRawI32, bool kRelu = false, bool kZp = false, int kF8 = kF8None>
+__device__ __forceinline__ void epilogue(const std::conditional_t<kF8 != kF8None, v4f, v4i> acc,
+                                         int lane,
                                          int64_t n, int64_t T, int64_t K, int64_t N,
                                          const int8_t *B, const EpilogueArgs &ep,
                                          const OutlierPrefetch &pre)
@@ -130,8 +132,8 @@ __device__ __forceinline__ void epilogue(const std::conditional_t<kF8, v4f, v4i>
                     cb = B[n * K + o];
                 }
                 uint16_t wd;
-                if constexpr (kF8)
-                    wd = dequant_w_f8((unsigned)cb & 0xffu, sn);
+                if constexpr (kF8 != kF8None)
+                    wd = dequant_w_f8<kF8>((unsigned)cb & 0xffu, sn);
                 else if constexpr (kZp)
                     wd = dequant_w_zp(cb, zb, sn);
                 else
@@ -201,7 +203,18 @@ struct CfgRs {
     static_assert(kWait < 64, "vmcnt range");
 };
 
-template <class C, bool kRawI32, bool kRelu = false, bool kZp = false, bool kF8 = false>
+// One 16x16x32 FP8 MFMA on 8-byte fragments of format kFmt (fp8 = E4M3,
+// bf8 = E5M2), fp32 accumulators.
+template <int kFmt>
+__device__ __forceinline__ v4f mfma_f8_16(long a, long b, v4f c)
+{
+    if constexpr (kFmt == kF8E4M3)
+        return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf8_bf8(a, b, c, 0, 0, 0);
+}
+
+template <class C, bool kRawI32, bool kRelu = false, bool kZp = false, int kF8 = kF8None>
 __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restrict__ A,
                                                            const int8_t *__restrict__ B,
                                                            int64_t T, int64_t K, int64_t N,
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
                 a[s2] = *reinterpret_cast<const v4i *>(pa + kc + 64 * s2);
         }
     };
-    std::conditional_t<kF8, v4f, v4i> acc = {0, 0, 0, 0};
+    std::conditional_t<kF8 != kF8None, v4f, v4i> acc = {0, 0, 0, 0};
     // Fragment reads in groups of kReadGroup, each group issued before its
     // MFMAs (each MFMA waits only for its own read).  The first `skip` bytes
     // of the last stage were already summed by the previous stage: their
@@ -289,16 +302,14 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
 #pragma unroll
             for (int i = 0; i < C::kReadGroup; ++i)
                 if (64 * (s0 + i) >= skip) {
-                    if constexpr (kF8) {
-                        // E5M2: two 16x16x32 MFMAs, the low and the high 8
+                    if constexpr (kF8 != kF8None) {
+                        // FP8: two 16x16x32 MFMAs, the low and the high 8
                         // bytes of both fragments (the same k's in both)
                         const v4i x = a[s0 + i], y = b[i];
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf8_bf8(
-                            ((long)(unsigned)x[1] << 32) | (unsigned)x[0],
-                            ((long)(unsigned)y[1] << 32) | (unsigned)y[0], acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf8_bf8(
-                            ((long)(unsigned)x[3] << 32) | (unsigned)x[2],
-                            ((long)(unsigned)y[3] << 32) | (unsigned)y[2], acc, 0, 0, 0);
+                        acc = mfma_f8_16<kF8>(((long)(unsigned)x[1] << 32) | (unsigned)x[0],
+                                              ((long)(unsigned)y[1] << 32) | (unsigned)y[0], acc);
+                        acc = mfma_f8_16<kF8>(((long)(unsigned)x[3] << 32) | (unsigned)x[2],
+                                              ((long)(unsigned)y[3] << 32) | (unsigned)y[2], acc);
                     } else {
                         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[s0 + i], b[i], acc, 0, 0, 0);
                     }
@@ -384,12 +395,14 @@ __global__ __launch_bounds__(C::kThreads) void k_decode_rs(const int8_t *__restr
     epilogue<kRawI32, kRelu, kZp, kF8>(acc, lane, n0 + lane % 16, T, K, N, B, ep, pre);
 }
 
-template <class C, bool R, bool kRelu = false, bool kZp = false, bool kF8 = false>
+template <class C, bool R, bool kRelu = false, bool kZp = false, int kF8 = kF8None>
 struct RsKernel {
     static constexpr auto fn = k_decode_rs<C, R, kRelu, kZp, kF8>;
 };
 template <class C, bool R>
-using RsKernelF8 = RsKernel<C, R, false, false, true>;
+using RsKernelF8 = RsKernel<C, R, false, false, kF8E5M2>;
+template <class C, bool R>
+using RsKernelF8E4 = RsKernel<C, R, false, false, kF8E4M3>;
 template <class C, bool R>
 using RsKernelRelu = RsKernel<C, R, true>;
 template <class C, bool R>
@@ -426,6 +439,8 @@ hipError_t launch_rs(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, i
 {
     if (C::kSync && N % (16 * C::WAVES) != 0)
         return hipErrorInvalidValue;   // a block's wavefronts must all reach the barriers
+    if (ep.f8 == kF8E4M3 && !ep.c_i32)
+        return launch_kernel<C, RsKernelF8E4>(Xq, CB, T, K, N, ep, s, ev0, ev1);
     if (ep.f8 && !ep.c_i32)
         return launch_kernel<C, RsKernelF8>(Xq, CB, T, K, N, ep, s, ev0, ev1);
     if (ep.row_zp && !ep.c_i32)

@@ -452,16 +452,19 @@ __device__ __forceinline__ void mainloop(char *smem, const Streams<C> &st, int n
     wait_vm<0>();   // the tail loads land before anyone reuses the buffers
 }
 
-// FP8 variant: v_mfma_f32_32x32x64_f8f6f4 on E5M2 codes (format 1 for both
-// operands, no block scales) with fp32 accumulators.  A 64-deep k-step
+// FP8 variant: v_mfma_f32_32x32x64_f8f6f4 on FP8 codes (the instruction's
+// format 0 is E4M3, 1 is E5M2; the same for both operands, no block scales)
+// with fp32 accumulators.  A 64-deep k-step
 // takes 32 bytes per lane: lane half h reads 16-byte chunks 4s + h and
 // 4s + 2 + h of the 64-byte k-step s, for A and B alike, so both operands
 // hold the same k values in the same places and the sum covers all 64.
+template <int kFmt>
 struct MfmaF8 {
     typedef v16f acc_t;
+    static constexpr int kCode = kFmt == kF8E4M3 ? 0 : 1;
     __device__ __forceinline__ static acc_t op(v8i a, v8i b, acc_t c)
     {
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 1, 1, 0, 0, 0, 0);
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kCode, kCode, 0, 0, 0, 0);
     }
 };
 
@@ -492,7 +495,7 @@ __device__ __forceinline__ void read_one8(Frags8<C> &f, const char *sa, const ch
 
 // kstep for the FP8 k-steps: the same groups of (load issue, fragment read,
 // MFMAs) pinned by scheduling barriers.
-template <class C, int kL0, int kNL>
+template <class C, int kFmt, int kL0, int kNL>
 __device__ __forceinline__ void kstep8(const Frags8<C> &cur, Frags8<C> &nxt, const char *sa,
                                        const char *sb, int fo0, int fo1,
                                        v16f (&acc)[C::FM][C::FN], const Streams<C> &st,
@@ -509,15 +512,16 @@ __device__ __forceinline__ void kstep8(const Frags8<C> &cur, Frags8<C> &nxt, con
 #pragma unroll
         for (int idx = g * kMfma / kGroups; idx < (g + 1) * kMfma / kGroups; ++idx) {
             const int i = idx / C::FN, j = idx % C::FN;
-            acc[i][j] = MfmaF8::op(cur.b[j], cur.a[i], acc[i][j]);   // D[n][t], as k_gemm
+            acc[i][j] = MfmaF8<kFmt>::op(cur.b[j], cur.a[i], acc[i][j]);   // D[n][t], as k_gemm
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // The pipelined main loop of `mainloop` (same stage ring, waits, barrier
-// and refill placement) over ROWB/64 FP8 k-steps per stage.
-template <class C>
+// and refill placement) over ROWB/64 FP8 k-steps per stage (codes of
+// format kFmt).
+template <class C, int kFmt>
 __device__ __forceinline__ void mainloop_f8(char *smem, const Streams<C> &st, int numK,
                                             v16f (&acc)[C::FM][C::FN], int wm, int wn, int wave,
                                             int lane)
@@ -556,13 +560,13 @@ __device__ __forceinline__ void mainloop_f8(char *smem, const Streams<C> &st, in
             Frags8<C> &cur = s % 2 == 0 ? f0 : f1;
             Frags8<C> &nxt = s % 2 == 0 ? f1 : f0;
             if (s + 1 < kS) {
-                kstep8<C, 0, 0>(cur, nxt, stage_a(kt), stage_b(kt), fo0[s + 1], fo1[s + 1], acc,
+                kstep8<C, kFmt, 0, 0>(cur, nxt, stage_a(kt), stage_b(kt), fo0[s + 1], fo1[s + 1], acc,
                                 st, smem, 0, 0, wave);
             } else {
                 wait_vm<(C::STAGES - 2) * C::kLoads>();   // stage kt+1 landed
                 __builtin_amdgcn_s_barrier();
                 const int nk = kt + 1 < numK ? kt + 1 : kt;
-                kstep8<C, 0, C::kLoads>(cur, nxt, stage_a(nk), stage_b(nk), fo0[0], fo1[0], acc,
+                kstep8<C, kFmt, 0, C::kLoads>(cur, nxt, stage_a(nk), stage_b(nk), fo0[0], fo1[0], acc,
                                         st, smem, kt % C::STAGES, kb(kt + C::STAGES), wave);
             }
         }
@@ -830,7 +834,12 @@ struct DqRow {
     float nd;
 };
 
-enum { kVarAbsmax = 0, kVarZp = 1, kVarF8 = 2 };
+// kVarF8: E5M2 codes, kVarF8E4: E4M3 codes.
+enum { kVarAbsmax = 0, kVarZp = 1, kVarF8 = 2, kVarF8E4 = 3 };
+constexpr int var_f8(int var)
+{
+    return var == kVarF8 ? kF8E5M2 : var == kVarF8E4 ? kF8E4M3 : kF8None;
+}
 
 template <int kVar>
 __device__ __forceinline__ DqRow dq_row(const EpilogueArgs &ep, int64_t n)
@@ -840,7 +849,7 @@ __device__ __forceinline__ DqRow dq_row(const EpilogueArgs &ep, int64_t n)
         p.nd = ep.scb[n];
         p.zp = ep.zp_b[n];
         p.s = p.nd > 0.0f ? 1.0f / p.nd : 0.0f;
-    } else if constexpr (kVar == kVarF8) {
+    } else if constexpr (var_f8(kVar) != kF8None) {
         p.s = ep.scb[n];
     } else {
         p.s = ep.scb[n] / 127.0f;
@@ -858,8 +867,8 @@ __device__ __forceinline__ uint4 dq8(unsigned w0, unsigned w1, unsigned m8, cons
     for (int e = 0; e < 8; ++e) {
         const unsigned byte = ((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xffu;
         uint16_t v;
-        if constexpr (kVar == kVarF8)
-            v = dequant_w_f8(byte, p.s);
+        if constexpr (var_f8(kVar) != kF8None)
+            v = dequant_w_f8<var_f8(kVar)>(byte, p.s);
         else if constexpr (kVar == kVarZp)
             v = dequant_w_zp_r((int)(int8_t)byte, p.zp, p.nd, p.s);
         else
@@ -879,8 +888,8 @@ __device__ __forceinline__ uint2 dq4(unsigned w, unsigned m4, const DqRow &p)
     for (int e = 0; e < 4; ++e) {
         const unsigned byte = (w >> (8 * e)) & 0xffu;
         uint16_t v;
-        if constexpr (kVar == kVarF8)
-            v = dequant_w_f8(byte, p.s);
+        if constexpr (var_f8(kVar) != kF8None)
+            v = dequant_w_f8<var_f8(kVar)>(byte, p.s);
         else if constexpr (kVar == kVarZp)
             v = dequant_w_zp_r((int)(int8_t)byte, p.zp, p.nd, p.s);
         else
@@ -911,8 +920,8 @@ __device__ __forceinline__ uint2 dq4m(unsigned w, unsigned bytemask, const DqRow
     for (int e = 0; e < 4; ++e) {
         const unsigned byte = (w >> (8 * e)) & 0xffu;
         float v;
-        if constexpr (kVar == kVarF8)
-            v = e5m2_to_f(byte) * p.s;
+        if constexpr (var_f8(kVar) != kF8None)
+            v = f8_to_f<var_f8(kVar)>(byte) * p.s;
         else
             v = (float)(int)(int8_t)byte * p.s;
         h[e / 2][e % 2] = (_Float16)v;
@@ -1140,7 +1149,7 @@ __device__ __forceinline__ void outlier_gemm_pass(AccArray &accf, char *smem,
 // accumulators (the int32 ones die there, so the two share registers), the
 // fp16 pass adding the outlier product onto them (outlier_gemm_pass), then
 // the bias, one rounding, and the tile out through LDS like finish_tile's.
-template <class C, bool kRelu, bool kZp, bool kF8, class Acc = v16i>
+template <class C, bool kRelu, bool kZp, int kF8, class Acc = v16i>
 __device__ __forceinline__ void outlier_pass(const Acc (&acc)[C::FM][C::FN],
                                              const float (&at)[C::FM], const int (&za)[C::FM],
                                              const int (&ra)[C::FM], char *smem,
@@ -1191,7 +1200,7 @@ __device__ __forceinline__ void outlier_pass(const Acc (&acc)[C::FM][C::FN],
                     accf[i][j][r] = 0.0f;
     }
     __builtin_amdgcn_s_barrier();   // every wavefront is done reading the LDS ring
-    outlier_gemm_pass<C, kF8 ? kVarF8 : kZp ? kVarZp : kVarAbsmax>(
+    outlier_gemm_pass<C, kF8 == kF8E4M3 ? kVarF8E4 : kF8 ? kVarF8 : kZp ? kVarZp : kVarAbsmax>(
         accf, smem, ep, CB, info, groups, mask, m0, n0, T, K, N, nout, wm, wn, wave, lane);
     static_assert(C::BM * C::BN * 2 <= C::kLdsBytes, "output tile fits the LDS ring");
     __builtin_amdgcn_s_barrier();
@@ -1225,7 +1234,7 @@ __device__ __forceinline__ void outlier_pass(const Acc (&acc)[C::FM][C::FN],
 
 // One tile of the int8 GEMM with the up-to-32-outlier epilogue (or the raw
 // int32 store); smem: the ring, then (output path) the tile's outlier rows.
-template <class C, bool kRawI32, bool kRelu, bool kZp, bool kF8>
+template <class C, bool kRawI32, bool kRelu, bool kZp, int kF8>
 __device__ __forceinline__ void gemm_tile(char *smem, const int8_t *__restrict__ A,
                                           const int8_t *__restrict__ B, int64_t T, int64_t K,
                                           int64_t N, const EpilogueArgs &ep)
@@ -1248,7 +1257,7 @@ __device__ __forceinline__ void gemm_tile(char *smem, const int8_t *__restrict__
     if constexpr (!kRawI32)
         issue_outlier_rows<C>(orows, ep, m0, n0, T, N, wave, lane);
 
-    using Acc = std::conditional_t<kF8, v16f, v16i>;
+    using Acc = std::conditional_t<kF8 != kF8None, v16f, v16i>;
     Acc acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -1262,8 +1271,8 @@ __device__ __forceinline__ void gemm_tile(char *smem, const int8_t *__restrict__
         Streams<C> st;
         st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
                 n0, N, wave, lane);
-        if constexpr (kF8)
-            mainloop_f8<C>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+        if constexpr (kF8 != kF8None)
+            mainloop_f8<C, kF8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
         else
             run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
     }
@@ -1300,7 +1309,7 @@ __device__ __forceinline__ void gemm_tile(char *smem, const int8_t *__restrict__
             const int64_t t = tw + i * 32 + tl;
             if constexpr (kZp)
                 zp_row(ep, t < T ? t : T - 1, K, at[i], za[i], ra[i]);
-            else if constexpr (kF8)
+            else if constexpr (kF8 != kF8None)
                 at[i] = ep.a[t < T ? t : T - 1];   // the row scale 2^-e
             else
                 at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
@@ -1322,7 +1331,7 @@ __device__ __forceinline__ void gemm_tile(char *smem, const int8_t *__restrict__
 // needs do not cost k_gemm's epilogue; one launch with k_gemm (k_gemm_both)
 // where both run the same shape; one tile per block (a persistent tile loop
 // makes the compiler spill around it).  smem is the ring.
-template <class C, bool kRelu, bool kZp, bool kF8>
+template <class C, bool kRelu, bool kZp, int kF8>
 __device__ __forceinline__ void many_tile(char *smem, const int8_t *__restrict__ A,
                                           const int8_t *__restrict__ B, int64_t T, int64_t K,
                                           int64_t N, const EpilogueArgs &ep,
@@ -1338,7 +1347,7 @@ __device__ __forceinline__ void many_tile(char *smem, const int8_t *__restrict__
     tile_coords(blockIdx.x, gridDim.x, ntm, ntn, C::GROUP, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
 
-    using Acc = std::conditional_t<kF8, v16f, v16i>;
+    using Acc = std::conditional_t<kF8 != kF8None, v16f, v16i>;
     Acc acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -1351,8 +1360,8 @@ __device__ __forceinline__ void many_tile(char *smem, const int8_t *__restrict__
         Streams<C> st;
         st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(B), K,
                 n0, N, wave, lane);
-        if constexpr (kF8)
-            mainloop_f8<C>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+        if constexpr (kF8 != kF8None)
+            mainloop_f8<C, kF8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
         else
             run_mainloop<C, MfmaI8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
     }
@@ -1364,7 +1373,7 @@ __device__ __forceinline__ void many_tile(char *smem, const int8_t *__restrict__
         const int64_t t = tw + i * 32;
         if constexpr (kZp)
             zp_row(ep, t < T ? t : T - 1, K, at[i], za[i], ra[i]);
-        else if constexpr (kF8)
+        else if constexpr (kF8 != kF8None)
             at[i] = ep.a[t < T ? t : T - 1];
         else
             at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
@@ -1373,7 +1382,7 @@ __device__ __forceinline__ void many_tile(char *smem, const int8_t *__restrict__
                                           T, K, N, nout, wm, wn, wave, lane, tid);
 }
 
-template <class C, bool kRawI32, bool kRelu, bool kZp = false, bool kF8 = false>
+template <class C, bool kRawI32, bool kRelu, bool kZp = false, int kF8 = kF8None>
 __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__ A,
                                                       const int8_t *__restrict__ B, int64_t T,
                                                       int64_t K, int64_t N, EpilogueArgs ep)
@@ -1383,7 +1392,7 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(const int8_t *__restrict__
     gemm_tile<C, kRawI32, kRelu, kZp, kF8>(smem, A, B, T, K, N, ep);
 }
 
-template <class C, bool kRelu, bool kZp = false, bool kF8 = false>
+template <class C, bool kRelu, bool kZp = false, int kF8 = kF8None>
 __global__ __launch_bounds__(C::kThreads) void k_gemm_many(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, int64_t T, int64_t K, int64_t N,
     EpilogueArgs ep, const int32_t *__restrict__ info, const int32_t *__restrict__ groups,
@@ -1454,9 +1463,12 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
     if (ep.c_i32)
         hipLaunchKernelGGL((k_gemm<C, true, false>), grid, dim3(C::kThreads), 0, s, Xq, CB, T, K,
                            N, ep);
+    else if (ep.f8 == kF8E4M3)
+        hipLaunchKernelGGL((k_gemm<C, false, false, false, kF8E4M3>), grid, dim3(C::kThreads), 0,
+                           s, Xq, CB, T, K, N, ep);
     else if (ep.f8)
-        hipLaunchKernelGGL((k_gemm<C, false, false, false, true>), grid, dim3(C::kThreads), 0, s,
-                           Xq, CB, T, K, N, ep);
+        hipLaunchKernelGGL((k_gemm<C, false, false, false, kF8E5M2>), grid, dim3(C::kThreads), 0,
+                           s, Xq, CB, T, K, N, ep);
     else if (ep.row_zp)
         hipLaunchKernelGGL((k_gemm<C, false, false, true>), grid, dim3(C::kThreads), 0, s, Xq, CB,
                            T, K, N, ep);
@@ -1472,9 +1484,12 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
             return e;
     }
     if (!ep.c_i32) {
-        if (ep.f8)
-            hipLaunchKernelGGL((k_gemm_many<CM, false, false, true>), grid, dim3(CM::kThreads), 0, s,
-                               Xq, CB, T, K, N, ep, ep.n_out, ep.groups, ep.mask);
+        if (ep.f8 == kF8E4M3)
+            hipLaunchKernelGGL((k_gemm_many<CM, false, false, kF8E4M3>), grid, dim3(CM::kThreads),
+                               0, s, Xq, CB, T, K, N, ep, ep.n_out, ep.groups, ep.mask);
+        else if (ep.f8)
+            hipLaunchKernelGGL((k_gemm_many<CM, false, false, kF8E5M2>), grid, dim3(CM::kThreads),
+                               0, s, Xq, CB, T, K, N, ep, ep.n_out, ep.groups, ep.mask);
         else if (ep.row_zp)
             hipLaunchKernelGGL((k_gemm_many<CM, false, true>), grid, dim3(CM::kThreads), 0, s, Xq, CB,
                                T, K, N, ep, ep.n_out, ep.groups, ep.mask);

@@ -117,29 +117,51 @@ __device__ __forceinline__ uint16_t dequant_w_zp_r(int cb, int zp, float nd, flo
     return f2h(near ? m / nd : q);
 }
 
-// FP8 (E5M2) variant.  An E5M2 code is the high byte of the binary16 with
+// FP8 variant.  Formats: E5M2 (5 exponent bits with bias 15, 2 fraction
+// bits, largest finite 57344) and E4M3 (4 exponent bits with bias 7, 3
+// fraction bits, no infinities, largest finite 448, subnormal step 2^-9);
+// kF8None selects the int8 path wherever a format parameter appears.
+enum { kF8None = 0, kF8E5M2 = 1, kF8E4M3 = 2 };
+
+// Value of an FP8 code.  An E5M2 code is the high byte of the binary16 with
 // the same value (same sign, exponent field and bias; 2 of the 10 fraction
-// bits), so decoding is a shift.
-__device__ __forceinline__ float e5m2_to_f(unsigned c) { return h2f((uint16_t)(c << 8)); }
+// bits), so decoding is a shift.  E4M3: a normal code (exponent field e > 0)
+// is the fp32 with exponent field e + 120 and the 3 fraction bits on top of
+// its fraction; a subnormal one is f * 2^-9, exact in fp32.
+template <int kFmt>
+__device__ __forceinline__ float f8_to_f(unsigned c)
+{
+    if constexpr (kFmt == kF8E4M3) {
+        const unsigned e = (c >> 3) & 15u, f = c & 7u;
+        const float mag = e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (f << 20))
+                            : (float)f * 0.001953125f;
+        return (c & 0x80u) ? -mag : mag;
+    } else {
+        return h2f((uint16_t)(c << 8));
+    }
+}
 
 // The power of two 2^e that scales a vector with absmax a (an fp16 value, as
-// fp32) into E5M2's range: e is the largest integer with a * 2^e <= 57344 =
-// 1.75 * 2^15 (e = 0 for a = 0).  With a = f * 2^E, f in [1, 2): e = 15 - E
-// for f <= 1.75, else 14 - E.
+// fp32) into the format's range: e is the largest integer with a * 2^e <=
+// 1.75 * 2^M, M = 15 (E5M2, 57344) or 8 (E4M3, 448); e = 0 for a = 0.  With
+// a = f * 2^E, f in [1, 2): e = M - E for f <= 1.75, else M - 1 - E.
+template <int kFmt>
 __device__ __forceinline__ int f8_scale_exp(float a)
 {
+    constexpr int M = kFmt == kF8E4M3 ? 8 : 15;
     if (!(a > 0.0f))
         return 0;
     int ex;
     const float fr = __builtin_frexpf(a, &ex);   // a = fr * 2^ex, fr in [0.5, 1)
-    return (2.0f * fr <= 1.75f ? 15 : 14) - (ex - 1);
+    return (2.0f * fr <= 1.75f ? M : M - 1) - (ex - 1);
 }
 
-// fp16 weight of E5M2 code c in a column with scale sc (a power of two): the
+// fp16 weight of FP8 code c in a column with scale sc (a power of two): the
 // exact product rounded once.
+template <int kFmt>
 __device__ __forceinline__ uint16_t dequant_w_f8(unsigned c, float sc)
 {
-    return f2h(e5m2_to_f(c) * sc);
+    return f2h(f8_to_f<kFmt>(c) * sc);
 }
 
 // 1/nd for the zero-point dequantization (0 when nd = 0).  v_rcp_f32 is
@@ -184,7 +206,7 @@ struct GatherArgs {
     int64_t N;
     void *w_out;
     const int32_t *zp = nullptr;   // zero-point variant: zp of each column (else null)
-    bool f8 = false;               // FP8 variant: CB holds E5M2 codes
+    int f8 = kF8None;              // FP8 variant: the format of CB's codes
 };
 
 // Where the row quantization puts the outlier-set summary: info (n, ng,
@@ -277,9 +299,10 @@ struct EpilogueArgs {
     const int2 *row_zp = nullptr;
     const int32_t *zp_b = nullptr;
     const int32_t *rs_b = nullptr;
-    // FP8 variant: Xq and CB hold E5M2 codes, a and scb the scales 2^-e of
-    // the rows and columns; the products are summed in fp32 by fp8 MFMAs.
-    bool f8 = false;
+    // FP8 variant (f8 = kF8E5M2 or kF8E4M3): Xq and CB hold codes of that
+    // format, a and scb the scales 2^-e of the rows and columns; the
+    // products are summed in fp32 by fp8 MFMAs.
+    int f8 = kF8None;
     // GEMM path, kOutDense: the activations, the chunk flags and the
     // non-empty 64-column groups
     const uint16_t *X = nullptr;
@@ -309,19 +332,20 @@ hipError_t launch_quantize_act_zp(const uint16_t *X, int64_t T, int64_t K, float
                                   const OutlierInfoOut &io, uint8_t *mask, uint16_t *x_out,
                                   const GatherArgs &g, bool xq_packed, hipStream_t s);
 
-// FP8 variant (E5M2, the 5-bit-exponent, 2-bit-fraction format the
-// LLM.int8() summary names under "Related work"): per vector a power-of-two
-// scale 2^e (f8_scale_exp of the absmax; the row absmax over the
-// non-outlier columns), codes = E5M2 nearest to x * 2^e (ties to even),
-// stored scale 2^-e; outlier columns are +0.  Weight: per row of W_t.
+// FP8 variant (fmt kF8E5M2: the 5-bit-exponent, 2-bit-fraction format the
+// LLM.int8() summary names under "Related work"; kF8E4M3: the 4-bit-exponent
+// one): per vector a power-of-two scale 2^e (f8_scale_exp of the absmax; the
+// row absmax over the non-outlier columns), codes = the format's value
+// nearest to x * 2^e (ties to even), stored scale 2^-e; outlier columns are
+// +0.  Weight: per row of W_t.
 hipError_t launch_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N, uint8_t *CB8,
-                                     float *SC8, hipStream_t s);
-// Activations: as launch_quantize_act (same kernels with the E5M2 codes;
-// sc receives the row scales 2^-e); g.f8 must be set when g.w_out is.
+                                     float *SC8, int fmt, hipStream_t s);
+// Activations: as launch_quantize_act (same kernels with the FP8 codes;
+// sc receives the row scales 2^-e); g.f8 must equal fmt when g.w_out is set.
 hipError_t launch_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float threshold,
                                   uint8_t *Xq8, float *sc, int32_t *O, const OutlierInfoOut &io,
                                   uint8_t *mask, uint16_t *x_out, const GatherArgs &g,
-                                  bool xq_packed, hipStream_t s);
+                                  bool xq_packed, int fmt, hipStream_t s);
 
 // ev0/ev1 (optional) are recorded on s right before and after the main kernel.
 hipError_t launch_gemm(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int64_t N,

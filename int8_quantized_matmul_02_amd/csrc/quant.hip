@@ -121,32 +121,43 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float amax, float r)
     return pack_low_bytes(s);
 }
 
-// FP8 variant: E5M2 codes of 8 values scaled by sc = 2^e (the product is
-// exact: a power of two, and |x * 2^e| <= 57344), each rounded to the
-// nearest E5M2 value with ties to even by v_cvt_pk_bf8_f32 (two per
-// instruction, into the low or high half of a dword).
+// FP8 variant: codes of 8 values scaled by sc = 2^e (the product is exact:
+// a power of two, and |x * 2^e| is at most the format's largest finite
+// value), each rounded to the nearest value of the format with ties to even
+// by v_cvt_pk_bf8_f32 (E5M2) or v_cvt_pk_fp8_f32 (E4M3), two per
+// instruction, into the low or high half of a dword.
+template <int kFmt, bool kHi>
+__device__ __forceinline__ int cvt_pk_f8(float a, float b, int old)
+{
+    if constexpr (kFmt == kF8E4M3)
+        return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, kHi);
+    else
+        return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, kHi);
+}
+
+template <int kFmt>
 __device__ __forceinline__ uint2 quant8_f8(uint4 v, float sc)
 {
     unsigned w[2];
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
         int x = 0;
-        x = __builtin_amdgcn_cvt_pk_bf8_f32(h2f(half_at(v, 4 * d)) * sc,
-                                            h2f(half_at(v, 4 * d + 1)) * sc, x, false);
-        x = __builtin_amdgcn_cvt_pk_bf8_f32(h2f(half_at(v, 4 * d + 2)) * sc,
-                                            h2f(half_at(v, 4 * d + 3)) * sc, x, true);
+        x = cvt_pk_f8<kFmt, false>(h2f(half_at(v, 4 * d)) * sc, h2f(half_at(v, 4 * d + 1)) * sc,
+                                   x);
+        x = cvt_pk_f8<kFmt, true>(h2f(half_at(v, 4 * d + 2)) * sc,
+                                  h2f(half_at(v, 4 * d + 3)) * sc, x);
         w[d] = (unsigned)x;
     }
     return make_uint2(w[0], w[1]);
 }
 
 // The row quantization of an absmax-type kernel: int8 codes from (amax, r =
-// 127/amax), or (kF8) E5M2 codes from sc = 2^e.
-template <bool kF8>
+// 127/amax), or (kF8, a format) FP8 codes from sc = 2^e.
+template <int kF8>
 __device__ __forceinline__ uint2 quant8_mode(uint4 v, float amax, float r, float sc)
 {
-    if constexpr (kF8)
-        return quant8_f8(v, sc);
+    if constexpr (kF8 != kF8None)
+        return quant8_f8<kF8>(v, sc);
     else
         return quant8(v, amax, r);
 }
@@ -195,7 +206,8 @@ __global__ __launch_bounds__(kBlock) void k_quantize_weight(const uint16_t *__re
 }
 
 // FP8 variant: one wavefront per output column, the power-of-two scale of
-// the row's absmax, E5M2 codes, and the stored scale 2^-e.
+// the row's absmax, codes of format kFmt, and the stored scale 2^-e.
+template <int kFmt>
 __global__ __launch_bounds__(kBlock) void k_quantize_weight_f8(const uint16_t *__restrict__ W_t,
                                                                int64_t K, int64_t N,
                                                                uint8_t *__restrict__ CB8,
@@ -211,11 +223,11 @@ __global__ __launch_bounds__(kBlock) void k_quantize_weight_f8(const uint16_t *_
     for (int64_t c = lane; c < nchunk; c += kWave)
         m = umax(m, chunk_absmax(row[c]));
     m = wave_max_u32(m);
-    const int e = f8_scale_exp(h2f((uint16_t)m));
+    const int e = f8_scale_exp<kFmt>(h2f((uint16_t)m));
     const float sc = __builtin_ldexpf(1.0f, e);
     uint2 *dst = reinterpret_cast<uint2 *>(CB8 + n * K);
     for (int64_t c = lane; c < nchunk; c += kWave)
-        dst[c] = quant8_f8(row[c], sc);
+        dst[c] = quant8_f8<kFmt>(row[c], sc);
     if (lane == 0)
         SC8[n] = __builtin_ldexpf(1.0f, -e);
 }
@@ -547,7 +559,7 @@ __device__ __forceinline__ void scatter_outliers(uint4 v, unsigned fl, int pre,
 // One chunk of a row: outlier columns (flags fl) are 0 in the int8 row and go
 // to the compact row xrow (null: not gathered) from position pre on; the
 // others are quantized (r = 127/amax, or 0 when amax = 0).
-template <bool kF8 = false>
+template <int kF8 = kF8None>
 __device__ __forceinline__ void quant_chunk(uint4 v, unsigned fl, float amax, float r, int pre,
                                            uint16_t *__restrict__ xrow, uint2 *dst, float sc = 0.0f)
 {
@@ -584,14 +596,23 @@ __device__ __forceinline__ uint2 *xq_chunk(int8_t *Xq, int64_t t, int64_t K, int
 // columns (one 8-byte load when they are 8 aligned consecutive columns) and
 // stores them at once; past n the row holds zeros.  kOutDense: nothing.
 // kMode 0: absmax.  1, zero-point variant: SCB holds each row's nd, ZP its
-// zp, and the kOutFew values are fp16((cb + zp) / nd).  2, FP8 variant: the
-// bytes are E5M2 codes and SCB the scales 2^-e.
-constexpr int kModeAbsmax = 0, kModeZp = 1, kModeF8 = 2;
+// zp, and the kOutFew values are fp16((cb + zp) / nd).  2 and 3, FP8
+// variant: the bytes are E5M2 (2) or E4M3 (3) codes and SCB the scales 2^-e.
+constexpr int kModeAbsmax = 0, kModeZp = 1, kModeF8 = 2, kModeF8E4 = 3;
+// The FP8 format of a mode (kF8None for the int8 modes), and back.
+constexpr int mode_f8(int mode)
+{
+    return mode == kModeF8 ? kF8E5M2 : mode == kModeF8E4 ? kF8E4M3 : kF8None;
+}
+constexpr int f8_mode(int fmt)
+{
+    return fmt == kF8E5M2 ? kModeF8 : fmt == kF8E4M3 ? kModeF8E4 : kModeAbsmax;
+}
 template <int kMode>
 __device__ __forceinline__ uint16_t dequant_row(int cb, float sc, int zp)
 {
-    if constexpr (kMode == kModeF8)
-        return dequant_w_f8((unsigned)cb & 0xffu, sc);
+    if constexpr (mode_f8(kMode) != kF8None)
+        return dequant_w_f8<mode_f8(kMode)>((unsigned)cb & 0xffu, sc);
     else if constexpr (kMode == kModeZp)
         return dequant_w_zp(cb, zp, sc);
     else
@@ -709,7 +730,7 @@ __device__ __forceinline__ bool gathers_x(const uint16_t *x_out, int use, const 
     return x_out && (use == kForDecode || (use == kForGemm && os.mode != kOutDense));
 }
 
-template <int NC, bool kF8 = false>
+template <int NC, int kF8 = kF8None>
 __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict__ X, int64_t T,
                                                      int64_t K, const DetectFlags df,
                                                      int use, int32_t *__restrict__ O,
@@ -729,7 +750,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     int *s_aux = reinterpret_cast<int *>(s_dyn + flags_lds_bytes(nchunk));
     const OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
     if ((int64_t)blockIdx.x >= T) {
-        gather_block<kF8 ? kModeF8 : kModeAbsmax>(blockIdx.x - T, gridDim.x - T, K, nchunk, os,
+        gather_block<f8_mode(kF8)>(blockIdx.x - T, gridDim.x - T, K, nchunk, os,
                                                   s_fl, s_aux, s_red + 2 * kWavesPerBlock, CB,
                                                   SCB, N, w_out);
         return;
@@ -768,7 +789,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
         m = umax(m, s_max[w]);
     const float amax = h2f((uint16_t)m);
     const float r = kF8 ? 0.0f : amax > 0.0f ? 127.0f / amax : 0.0f;
-    const int e8 = kF8 ? f8_scale_exp(amax) : 0;
+    const int e8 = kF8 ? f8_scale_exp<kF8>(amax) : 0;
     const float sc = kF8 ? __builtin_ldexpf(1.0f, e8) : 0.0f;
     if constexpr (NC > 0) {
 #pragma unroll
@@ -820,7 +841,7 @@ __device__ __forceinline__ void step_prefix(unsigned fl, uint64_t below, int &pr
     }
 }
 
-template <int NC, bool kF8 = false>
+template <int NC, int kF8 = kF8None>
 __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restrict__ X, int64_t T,
                                                        int64_t K,
                                                        const DetectFlags df,
@@ -841,7 +862,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restric
     int *s_aux = reinterpret_cast<int *>(s_dyn + flags_lds_bytes(nchunk));
     const OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
     if ((int64_t)blockIdx.x >= row_blocks) {
-        gather_block<kF8 ? kModeF8 : kModeAbsmax>(blockIdx.x - row_blocks,
+        gather_block<f8_mode(kF8)>(blockIdx.x - row_blocks,
                                                   gridDim.x - row_blocks, K, nchunk, os, s_fl,
                                                   s_aux, s_red + 2 * kWavesPerBlock, CB, SCB, N,
                                                   w_out);
@@ -892,7 +913,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restric
     m = wave_max_u32(m);
     const float amax = h2f((uint16_t)m);
     const float r = kF8 ? 0.0f : amax > 0.0f ? 127.0f / amax : 0.0f;
-    const int e8 = kF8 ? f8_scale_exp(amax) : 0;
+    const int e8 = kF8 ? f8_scale_exp<kF8>(amax) : 0;
     const float sc = kF8 ? __builtin_ldexpf(1.0f, e8) : 0.0f;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
@@ -999,7 +1020,8 @@ constexpr int kSmallMaxChunks = 16 * kSmallThreads;   // G <= 16: K <= 65536
 // kMode kModeZp, the zero-point variant (a receives nd, row_zp {zp, code
 // sum}): the range instead of the absmax in step 3, codes by quant8_zp, and
 // one more block reduction for the code sum.  kModeF8, the FP8 variant: the
-// absmax sets the power-of-two scale, codes by quant8_f8, a receives 2^-e.
+// absmax sets the power-of-two scale, codes by quant8_f8, a receives 2^-e
+// (kModeF8: E5M2 codes, kModeF8E4: E4M3).
 template <int G, int kMode = kModeAbsmax>
 __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
     const uint16_t *__restrict__ X, int T, int K, unsigned thr_bits, int8_t *__restrict__ Xq,
@@ -1127,8 +1149,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
         for (int w = 0; w < kSmallThreads / kWave; ++w)
             amax_bits = umax(amax_bits, s_wmax[w]);
         amax = h2f((uint16_t)amax_bits);
-        if constexpr (kMode == kModeF8) {
-            const int e8 = f8_scale_exp(amax);
+        if constexpr (mode_f8(kMode) != kF8None) {
+            const int e8 = f8_scale_exp<mode_f8(kMode)>(amax);
             zpf = __builtin_ldexpf(1.0f, e8);   // the FP8 scale 2^e
             if (tid == 0)
                 a[t] = __builtin_ldexpf(1.0f, -e8);
@@ -1159,8 +1181,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
         uint2 q;
         if constexpr (kMode == kModeZp)
             q = quant8_zp(x, p.nd, zpf, sum);
-        else if constexpr (kMode == kModeF8)
-            q = quant8_f8(x, zpf);
+        else if constexpr (mode_f8(kMode) != kF8None)
+            q = quant8_f8<mode_f8(kMode)>(x, zpf);
         else
             q = quant8(x, amax, r127);
         *xq_chunk(Xq, t, K, c, packed) = q;
@@ -1478,8 +1500,8 @@ hipError_t launch_quantize_act_rows(const uint16_t *X, int64_t T, int64_t K, flo
 
 namespace {
 // Detection and the row quantization of the absmax kernels (kF8: their FP8
-// mode).
-template <bool kF8>
+// mode of that format).
+template <int kF8>
 hipError_t launch_act_absmax(const uint16_t *X, int64_t T, int64_t K, float threshold,
                              int8_t *Xq, float *a, int32_t *O, const OutlierInfoOut &io,
                              uint8_t *mask, uint16_t *x_out, const GatherArgs &g,
@@ -1538,25 +1560,31 @@ hipError_t launch_quantize_act(const uint16_t *X, int64_t T, int64_t K, float th
                                uint8_t *mask, uint16_t *x_out, const GatherArgs &g,
                                bool xq_packed, hipStream_t s)
 {
-    return launch_act_absmax<false>(X, T, K, threshold, Xq, a, O, io, mask, x_out, g,
+    return launch_act_absmax<kF8None>(X, T, K, threshold, Xq, a, O, io, mask, x_out, g,
                                     xq_packed, s);
 }
 
 hipError_t launch_quantize_weight_f8(const uint16_t *W_t, int64_t K, int64_t N, uint8_t *CB8,
-                                     float *SC8, hipStream_t s)
+                                     float *SC8, int fmt, hipStream_t s)
 {
     const int64_t blocks = (N + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(k_quantize_weight_f8, dim3((unsigned)blocks), dim3(kBlock), 0, s, W_t, K,
-                       N, CB8, SC8);
+    if (fmt == kF8E4M3)
+        hipLaunchKernelGGL(k_quantize_weight_f8<kF8E4M3>, dim3((unsigned)blocks), dim3(kBlock), 0,
+                           s, W_t, K, N, CB8, SC8);
+    else if (fmt == kF8E5M2)
+        hipLaunchKernelGGL(k_quantize_weight_f8<kF8E5M2>, dim3((unsigned)blocks), dim3(kBlock), 0,
+                           s, W_t, K, N, CB8, SC8);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t launch_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float threshold,
                                   uint8_t *Xq8, float *sc, int32_t *O, const OutlierInfoOut &io,
                                   uint8_t *mask, uint16_t *x_out, const GatherArgs &g,
-                                  bool xq_packed, hipStream_t s)
+                                  bool xq_packed, int fmt, hipStream_t s)
 {
-    if (g.w_out && !g.f8)
+    if ((fmt != kF8E5M2 && fmt != kF8E4M3) || (g.w_out && g.f8 != fmt))
         return hipErrorInvalidValue;
     int8_t *Xq = reinterpret_cast<int8_t *>(Xq8);
     if (!g.w_out && quantize_act_fits_rows(T, K)) {
@@ -1565,8 +1593,12 @@ hipError_t launch_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float
         const unsigned tb = threshold_bits(threshold);
         const dim3 grid((unsigned)T);
 #define LLMINT8_QROWS_F8(G)                                                                    \
-    hipLaunchKernelGGL((k_quant_rows<G, kModeF8>), grid, dim3(kSmallThreads), 0, s, X, (int)T, \
-                       (int)K, tb, Xq, sc, O, io.info, x_out, xq_packed, nullptr)
+    if (fmt == kF8E4M3)                                                                        \
+        hipLaunchKernelGGL((k_quant_rows<G, kModeF8E4>), grid, dim3(kSmallThreads), 0, s, X,   \
+                           (int)T, (int)K, tb, Xq, sc, O, io.info, x_out, xq_packed, nullptr); \
+    else                                                                                       \
+        hipLaunchKernelGGL((k_quant_rows<G, kModeF8>), grid, dim3(kSmallThreads), 0, s, X,     \
+                           (int)T, (int)K, tb, Xq, sc, O, io.info, x_out, xq_packed, nullptr)
         if (per <= 1)
             LLMINT8_QROWS_F8(1);
         else if (per <= 2)
@@ -1582,8 +1614,11 @@ hipError_t launch_quantize_act_f8(const uint16_t *X, int64_t T, int64_t K, float
 #undef LLMINT8_QROWS_F8
         return hipGetLastError();
     }
-    return launch_act_absmax<true>(X, T, K, threshold, Xq, sc, O, io, mask, x_out, g,
-                                   xq_packed, s);
+    if (fmt == kF8E4M3)
+        return launch_act_absmax<kF8E4M3>(X, T, K, threshold, Xq, sc, O, io, mask, x_out, g,
+                                          xq_packed, s);
+    return launch_act_absmax<kF8E5M2>(X, T, K, threshold, Xq, sc, O, io, mask, x_out, g,
+                                      xq_packed, s);
 }
 
 }  // namespace llmint8

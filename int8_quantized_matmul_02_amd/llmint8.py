@@ -40,6 +40,10 @@ EXPORTS = (
     "llmint8_quantize_act_f8",
     "llmint8_matmul_f8",
     "llmint8_matmul_f8_path",
+    "llmint8_quantize_weight_e4m3",
+    "llmint8_quantize_act_e4m3",
+    "llmint8_matmul_e4m3",
+    "llmint8_matmul_e4m3_path",
     "llmint8_mfma_ceiling",
     "llmint8_matmul_noalloc",
 )
@@ -84,18 +88,23 @@ def _load():
     lib.llmint8_matmul_zp.argtypes = [P, I64, I64, I64, P, P, P, P, P, F, P, P, SZ, P]
     lib.llmint8_matmul_zp_path.argtypes = [P, I64, I64, I64, P, P, P, P, P, F, P, P, SZ, I, P,
                                            P, P]
-    lib.llmint8_quantize_weight_f8.argtypes = [P, I64, I64, P, P, P]
-    lib.llmint8_quantize_act_f8.argtypes = [P, I64, I64, F, P, P, P, P, P, SZ, P]
-    lib.llmint8_matmul_f8.argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ, P]
-    lib.llmint8_matmul_f8_path.argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ, I, P, P, P]
+    for f8 in ("f8", "e4m3"):
+        getattr(lib, "llmint8_quantize_weight_" + f8).argtypes = [P, I64, I64, P, P, P]
+        getattr(lib, "llmint8_quantize_act_" + f8).argtypes = [P, I64, I64, F, P, P, P, P, P, SZ,
+                                                               P]
+        getattr(lib, "llmint8_matmul_" + f8).argtypes = [P, I64, I64, I64, P, P, P, F, P, P, SZ,
+                                                         P]
+        getattr(lib, "llmint8_matmul_%s_path" % f8).argtypes = [P, I64, I64, I64, P, P, P, F, P,
+                                                                P, SZ, I, P, P, P]
     lib.llmint8_mfma_ceiling.argtypes = [P, I64, P, I64, I64, I, I, I, P, P, P, P]
     lib.llmint8_matmul_noalloc.argtypes = [P, I64, I64, I64, P, P, P, F, P, P]
     for fn in ("llmint8_quantize_weight", "llmint8_quantize_act", "llmint8_matmul",
                "llmint8_matmul_act", "llmint8_matmul_path", "llmint8_igemm_i32",
                "llmint8_quantize_weight_zp", "llmint8_quantize_act_zp", "llmint8_matmul_zp",
                "llmint8_matmul_zp_path", "llmint8_quantize_weight_f8", "llmint8_quantize_act_f8",
-               "llmint8_matmul_f8", "llmint8_matmul_f8_path", "llmint8_mfma_ceiling",
-               "llmint8_matmul_noalloc"):
+               "llmint8_matmul_f8", "llmint8_matmul_f8_path", "llmint8_quantize_weight_e4m3",
+               "llmint8_quantize_act_e4m3", "llmint8_matmul_e4m3", "llmint8_matmul_e4m3_path",
+               "llmint8_mfma_ceiling", "llmint8_matmul_noalloc"):
         getattr(lib, fn).restype = I
     _lib = lib
     return lib
@@ -429,10 +438,10 @@ def llmint8_matmul_zp(X, CB, ND, ZP, RS, threshold=6.0, bias=None, out=None, ws=
 
 
 # ---------------------------------------------------------------------------
-# FP8 (E5M2) variant.
+# FP8 variant: E5M2 (the _f8 functions) and E4M3 (the _e4m3 functions), the
+# same arguments; the format only changes which library symbols are called.
 # ---------------------------------------------------------------------------
-def llmint8_quantize_weight_f8(W_t, CB8=None, SC8=None):
-    """W_t: fp16 [N,K].  Returns (CB8 uint8 [N,K] E5M2 codes, SC8 f32 [N] scales 2^-e)."""
+def _quantize_weight_fp8(fmt, W_t, CB8, SC8):
     lib = _load()
     _arg(W_t, "W_t", _H)
     N, K = W_t.shape
@@ -440,16 +449,13 @@ def llmint8_quantize_weight_f8(W_t, CB8=None, SC8=None):
     CB8 = _new_or(CB8, "CB8", (torch.uint8,), (N, K), d)
     SC8 = _new_or(SC8, "SC8", (torch.float32,), (N,), d)
     _on_device(W_t=W_t, CB8=CB8, SC8=SC8)
-    _check("llmint8_quantize_weight_f8",
-           lib.llmint8_quantize_weight_f8(W_t.data_ptr(), K, N, CB8.data_ptr(), SC8.data_ptr(),
-                                          _stream(W_t)))
+    fn = "llmint8_quantize_weight_" + fmt
+    _check(fn, getattr(lib, fn)(W_t.data_ptr(), K, N, CB8.data_ptr(), SC8.data_ptr(),
+                                _stream(W_t)))
     return CB8, SC8
 
 
-def llmint8_quantize_act_f8(X, threshold=6.0, Xq8=None, row_scale=None, outlier_idx=None,
-                            n_outliers=None, ws=None):
-    """X: fp16 [T,K].  Returns (Xq8 uint8 [T,K], row_scale f32 [T], outlier_idx int32 [K],
-    n_outliers int32 [1])."""
+def _quantize_act_fp8(fmt, X, threshold, Xq8, row_scale, outlier_idx, n_outliers, ws):
     lib = _load()
     _arg(X, "X", _H)
     T, K = X.shape
@@ -460,11 +466,11 @@ def llmint8_quantize_act_f8(X, threshold=6.0, Xq8=None, row_scale=None, outlier_
     n_outliers = _new_or(n_outliers, "n_outliers", (torch.int32,), (1,), d, min_numel=1)
     ws = _ws(ws, llmint8_quantize_act_workspace_bytes(K), d)
     _on_device(X=X, Xq8=Xq8, row_scale=row_scale, outlier_idx=outlier_idx, n_outliers=n_outliers, ws=ws)
-    _check("llmint8_quantize_act_f8",
-           lib.llmint8_quantize_act_f8(X.data_ptr(), T, K, float(threshold), Xq8.data_ptr(),
-                                       row_scale.data_ptr(), outlier_idx.data_ptr(),
-                                       n_outliers.data_ptr(), ws.data_ptr(),
-                                       ws.numel() * ws.element_size(), _stream(X)))
+    fn = "llmint8_quantize_act_" + fmt
+    _check(fn, getattr(lib, fn)(X.data_ptr(), T, K, float(threshold), Xq8.data_ptr(),
+                                row_scale.data_ptr(), outlier_idx.data_ptr(),
+                                n_outliers.data_ptr(), ws.data_ptr(),
+                                ws.numel() * ws.element_size(), _stream(X)))
     return Xq8, row_scale, outlier_idx, n_outliers
 
 
@@ -475,28 +481,74 @@ def _f8_operands(X, CB8, SC8, bias, out, ws, path=PATH_AUTO):
     return T, K, N, out, ws
 
 
+def _matmul_fp8_path(fmt, X, CB8, SC8, threshold, bias, out, ws, path, main_start, main_stop):
+    lib = _load()
+    T, K, N, out, ws = _f8_operands(X, CB8, SC8, bias, out, ws, path)
+    _on_device(X=X, CB8=CB8, SC8=SC8, bias=bias, out=out, ws=ws)
+    fn = "llmint8_matmul_%s_path" % fmt
+    _check(fn, getattr(lib, fn)(X.data_ptr(), T, K, N, CB8.data_ptr(), SC8.data_ptr(),
+                                _ptr(bias), float(threshold), out.data_ptr(), ws.data_ptr(),
+                                _nbytes(ws), int(path), _ev(main_start), _ev(main_stop),
+                                _stream(X)))
+    return out
+
+
+def _matmul_fp8(fmt, X, CB8, SC8, threshold, bias, out, ws):
+    lib = _load()
+    T, K, N, out, ws = _f8_operands(X, CB8, SC8, bias, out, ws)
+    _on_device(X=X, CB8=CB8, SC8=SC8, bias=bias, out=out, ws=ws)
+    fn = "llmint8_matmul_" + fmt
+    _check(fn, getattr(lib, fn)(X.data_ptr(), T, K, N, CB8.data_ptr(), SC8.data_ptr(),
+                                _ptr(bias), float(threshold), out.data_ptr(), ws.data_ptr(),
+                                _nbytes(ws), _stream(X)))
+    return out
+
+
+def llmint8_quantize_weight_f8(W_t, CB8=None, SC8=None):
+    """W_t: fp16 [N,K].  Returns (CB8 uint8 [N,K] E5M2 codes, SC8 f32 [N] scales 2^-e)."""
+    return _quantize_weight_fp8("f8", W_t, CB8, SC8)
+
+
+def llmint8_quantize_act_f8(X, threshold=6.0, Xq8=None, row_scale=None, outlier_idx=None,
+                            n_outliers=None, ws=None):
+    """X: fp16 [T,K].  Returns (Xq8 uint8 [T,K] E5M2 codes, row_scale f32 [T], outlier_idx
+    int32 [K], n_outliers int32 [1])."""
+    return _quantize_act_fp8("f8", X, threshold, Xq8, row_scale, outlier_idx, n_outliers, ws)
+
+
 def llmint8_matmul_f8_path(X, CB8, SC8, threshold=6.0, bias=None, out=None, ws=None,
                            path=PATH_AUTO, main_start=None, main_stop=None):
     """The FP8 decomposition: X fp16 [T,K] with the output of
     llmint8_quantize_weight_f8 -> out fp16 [T,N]; path / events as llmint8_matmul_path."""
-    lib = _load()
-    T, K, N, out, ws = _f8_operands(X, CB8, SC8, bias, out, ws, path)
-    _on_device(X=X, CB8=CB8, SC8=SC8, bias=bias, out=out, ws=ws)
-    _check("llmint8_matmul_f8_path",
-           lib.llmint8_matmul_f8_path(X.data_ptr(), T, K, N, CB8.data_ptr(), SC8.data_ptr(),
-                                      _ptr(bias), float(threshold), out.data_ptr(), ws.data_ptr(),
-                                      _nbytes(ws), int(path), _ev(main_start), _ev(main_stop),
-                                      _stream(X)))
-    return out
+    return _matmul_fp8_path("f8", X, CB8, SC8, threshold, bias, out, ws, path, main_start,
+                            main_stop)
 
 
 def llmint8_matmul_f8(X, CB8, SC8, threshold=6.0, bias=None, out=None, ws=None):
     """The FP8 decomposition (automatic kernel choice)."""
-    lib = _load()
-    T, K, N, out, ws = _f8_operands(X, CB8, SC8, bias, out, ws)
-    _on_device(X=X, CB8=CB8, SC8=SC8, bias=bias, out=out, ws=ws)
-    _check("llmint8_matmul_f8",
-           lib.llmint8_matmul_f8(X.data_ptr(), T, K, N, CB8.data_ptr(), SC8.data_ptr(),
-                                 _ptr(bias), float(threshold), out.data_ptr(), ws.data_ptr(),
-                                 _nbytes(ws), _stream(X)))
-    return out
+    return _matmul_fp8("f8", X, CB8, SC8, threshold, bias, out, ws)
+
+
+def llmint8_quantize_weight_e4m3(W_t, CB8=None, SC8=None):
+    """W_t: fp16 [N,K].  Returns (CB8 uint8 [N,K] E4M3 codes, SC8 f32 [N] scales 2^-e)."""
+    return _quantize_weight_fp8("e4m3", W_t, CB8, SC8)
+
+
+def llmint8_quantize_act_e4m3(X, threshold=6.0, Xq8=None, row_scale=None, outlier_idx=None,
+                              n_outliers=None, ws=None):
+    """X: fp16 [T,K].  Returns (Xq8 uint8 [T,K] E4M3 codes, row_scale f32 [T], outlier_idx
+    int32 [K], n_outliers int32 [1])."""
+    return _quantize_act_fp8("e4m3", X, threshold, Xq8, row_scale, outlier_idx, n_outliers, ws)
+
+
+def llmint8_matmul_e4m3_path(X, CB8, SC8, threshold=6.0, bias=None, out=None, ws=None,
+                             path=PATH_AUTO, main_start=None, main_stop=None):
+    """The E4M3 decomposition: X fp16 [T,K] with the output of
+    llmint8_quantize_weight_e4m3 -> out fp16 [T,N]; path / events as llmint8_matmul_path."""
+    return _matmul_fp8_path("e4m3", X, CB8, SC8, threshold, bias, out, ws, path, main_start,
+                            main_stop)
+
+
+def llmint8_matmul_e4m3(X, CB8, SC8, threshold=6.0, bias=None, out=None, ws=None):
+    """The E4M3 decomposition (automatic kernel choice)."""
+    return _matmul_fp8("e4m3", X, CB8, SC8, threshold, bias, out, ws)

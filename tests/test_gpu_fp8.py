@@ -1,8 +1,8 @@
-"""GPU parity of the FP8 (E5M2) variant against the CPU oracle, through the C
-ABI.
+"""GPU parity of the FP8 variant, in E5M2 (the _f8 entry points) and E4M3
+(the _e4m3 ones), against the CPU oracle, through the C ABI.
 
-Bar: bit-exact E5M2 codes and scales of weights and activations, outlier
-list and count.  The E5M2 products are summed by the matrix cores and in
+Bar: bit-exact FP8 codes and scales of weights and activations, outlier
+list and count.  The FP8 products are summed by the matrix cores and in
 fp64 by the oracle; that sum is not unique, and the fp8 MFMAs do not round it
 like sequential fp32 additions, so the bound gamma_K * S of an fp32
 summation does not cover them.  Their summation, characterized on MI355X with
@@ -15,7 +15,9 @@ result truncated to fp32.  So one instruction's error is below
 |accumulator|), and a length-K sum of s instructions (s = K/64 for the tiled
 GEMM's 64-deep steps, K/32 for the weight stream's 32-deep ones) errs by at
 most E = (7 * 2^-13 + 11 * 2^-24 * ceil(K/32)) * S, S = sum_k |x^ * w^| over
-the quantized part (the dequantized E5M2 values).  The fp16 output is
+the quantized part (the dequantized FP8 values).  The same probes with E4M3
+operands (products 1 and 2^-s, s <= 18, the format's range) show the same
+group alignment, so the bound serves both formats.  The fp16 output is
 compared within 1e-3 + 2e-3*|ref| + E; the structure (scales, outlier
 product, bias) is checked bit for bit by the exactly representable cases,
 whose sums the matrix cores form exactly.
@@ -30,19 +32,28 @@ from tests.gpu_helpers import assert_equal_exact, d2h, h2d, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
+# the library's entry points of each FP8 format (the oracle's format names)
+API = {
+    "e5m2": dict(qw=L.llmint8_quantize_weight_f8, qa=L.llmint8_quantize_act_f8,
+                 mm=L.llmint8_matmul_f8, mmp=L.llmint8_matmul_f8_path),
+    "e4m3": dict(qw=L.llmint8_quantize_weight_e4m3, qa=L.llmint8_quantize_act_e4m3,
+                 mm=L.llmint8_matmul_e4m3, mmp=L.llmint8_matmul_e4m3_path),
+}
+FMTS = pytest.mark.parametrize("fmt", ["e5m2", "e4m3"])
+
 
 def f8_accumulation_bound(K):
-    """Relative bound (to S) of the matrix cores' E5M2 summation over K terms
+    """Relative bound (to S) of the matrix cores' FP8 summation over K terms
     (module docstring)."""
     return 7.0 * 2.0 ** -13 + 11.0 * 2.0 ** -24 * -(-K // 32)
 
 
-def assert_f8_close(got, ref, X, CB8r, SC8r, thr, rows=None, what="out"):
+def assert_f8_close(got, ref, X, CB8r, SC8r, thr, rows=None, what="out", fmt="e5m2"):
     """assert_fp16_close with the FP8 accumulation term E = bound(K) * S added."""
     O = oracle.outlier_columns(X, thr)
-    Xq, sc = oracle.quantize_rows_f8(X, O, rows=rows)
-    a = np.abs(oracle.e5m2_to_double(Xq)) * sc.astype(np.float64)[:, None]
-    b = np.abs(oracle.e5m2_to_double(CB8r)) * SC8r.astype(np.float64)[:, None]
+    Xq, sc = oracle.quantize_rows_f8(X, O, rows=rows, fmt=fmt)
+    a = np.abs(oracle.f8_to_double(Xq, fmt)) * sc.astype(np.float64)[:, None]
+    b = np.abs(oracle.f8_to_double(CB8r, fmt)) * SC8r.astype(np.float64)[:, None]
     S = a @ b.T
     g = got.view(np.float16).astype(np.float64)
     r = ref.view(np.float16).astype(np.float64)
@@ -69,12 +80,13 @@ def f8_case(T, K, N, seed, n_dims=3, lo=8.0, hi=40.0, p=0.3):
     return X.astype(np.float16), W.astype(np.float16), dims
 
 
+@FMTS
 @pytest.mark.parametrize("N,K", [(64, 64), (192, 1088), (1024, 2048)])
-def test_quantize_weight_f8_exact(N, K):
-    say("quantize_weight_f8 N=%d K=%d" % (N, K))
+def test_quantize_weight_f8_exact(N, K, fmt):
+    say("quantize_weight %s N=%d K=%d" % (fmt, N, K))
     _, W_t, _ = f8_case(4, K, N, seed=N + K)
-    CB8, SC8 = L.llmint8_quantize_weight_f8(h2d(W_t))
-    CBr, SCr = oracle.quantize_weight_f8(W_t)
+    CB8, SC8 = API[fmt]["qw"](h2d(W_t))
+    CBr, SCr = oracle.quantize_weight_f8(W_t, fmt)
     assert_equal_exact(d2h(CB8), CBr, "CB8")
     assert_equal_exact(d2h(SC8), SCr, "SC8")
 
@@ -84,12 +96,13 @@ def test_quantize_weight_f8_exact(N, K):
 @pytest.mark.parametrize("T,K", [(1, 64), (5, 256), (16, 1088), (1, 33280), (4, 16448),
                                  (17, 1024), (300, 576), (513, 4160), (1024, 4096)])
 @pytest.mark.parametrize("thr", [6.0, 0.0, np.inf])
-def test_quantize_act_f8_exact(T, K, thr):
-    say("quantize_act_f8 T=%d K=%d thr=%s" % (T, K, thr))
+@FMTS
+def test_quantize_act_f8_exact(T, K, thr, fmt):
+    say("quantize_act %s T=%d K=%d thr=%s" % (fmt, T, K, thr))
     X, _, _ = f8_case(T, K, 64, seed=T * 3 + K)
-    Xq8, sc, O, n = L.llmint8_quantize_act_f8(h2d(X), thr)
+    Xq8, sc, O, n = API[fmt]["qa"](h2d(X), thr)
     Or = oracle.outlier_columns(X, thr)
-    Xqr, scr = oracle.quantize_rows_f8(X, Or)
+    Xqr, scr = oracle.quantize_rows_f8(X, Or, fmt=fmt)
     nn = int(d2h(n)[0])
     assert nn == len(Or)
     assert_equal_exact(d2h(O)[:nn], Or, "O")
@@ -112,60 +125,71 @@ SHAPES = [
 @pytest.mark.parametrize("T,K,N", SHAPES)
 @pytest.mark.parametrize("thr", [6.0, 0.0, np.inf])
 @pytest.mark.parametrize("path", [L.PATH_AUTO, L.PATH_GEMM, L.PATH_DECODE])
-def test_matmul_f8(T, K, N, thr, path):
+@FMTS
+def test_matmul_f8(T, K, N, thr, path, fmt):
     if path == L.PATH_DECODE and T > 16:
         pytest.skip("the weight-streaming kernel takes T <= 16")
-    say("matmul_f8 T=%d K=%d N=%d thr=%s path=%d" % (T, K, N, thr, path))
+    say("matmul %s T=%d K=%d N=%d thr=%s path=%d" % (fmt, T, K, N, thr, path))
     X, W_t, _ = f8_case(T, K, N, seed=T + 5 * K + N)
     rng = np.random.default_rng(T + K)
     bias = (rng.standard_normal(N) * 0.5).astype(np.float16) if T % 2 else None
-    CB8, SC8 = L.llmint8_quantize_weight_f8(h2d(W_t))
-    out = L.llmint8_matmul_f8_path(h2d(X), CB8, SC8, thr,
-                                   bias=h2d(bias) if bias is not None else None, path=path)
-    CBr, SCr = oracle.quantize_weight_f8(W_t)
-    ref, _, _ = oracle.matmul_f8(X, CBr, SCr, thr, bias=bias)
-    assert_f8_close(d2h(out), ref, X, CBr, SCr, thr)
+    CB8, SC8 = API[fmt]["qw"](h2d(W_t))
+    out = API[fmt]["mmp"](h2d(X), CB8, SC8, thr, bias=h2d(bias) if bias is not None else None,
+                          path=path)
+    CBr, SCr = oracle.quantize_weight_f8(W_t, fmt)
+    ref, _, _ = oracle.matmul_f8(X, CBr, SCr, thr, bias=bias, fmt=fmt)
+    assert_f8_close(d2h(out), ref, X, CBr, SCr, thr, fmt=fmt)
 
 
 @pytest.mark.parametrize("n_dims,T,path", [(40, 300, L.PATH_GEMM), (40, 8, L.PATH_DECODE),
                                            (200, 257, L.PATH_AUTO)])
-def test_matmul_f8_many_outliers(n_dims, T, path):
+@FMTS
+def test_matmul_f8_many_outliers(n_dims, T, path, fmt):
     K, N = 1024, 512
-    say("matmul_f8 many outliers n_dims=%d T=%d path=%d" % (n_dims, T, path))
+    say("matmul %s many outliers n_dims=%d T=%d path=%d" % (fmt, n_dims, T, path))
     X, W_t, _ = f8_case(T, K, N, seed=n_dims + T, n_dims=n_dims, p=0.5)
-    CB8, SC8 = L.llmint8_quantize_weight_f8(h2d(W_t))
-    out = L.llmint8_matmul_f8_path(h2d(X), CB8, SC8, 6.0, path=path)
-    CBr, SCr = oracle.quantize_weight_f8(W_t)
-    ref, O, _ = oracle.matmul_f8(X, CBr, SCr, 6.0)
+    CB8, SC8 = API[fmt]["qw"](h2d(W_t))
+    out = API[fmt]["mmp"](h2d(X), CB8, SC8, 6.0, path=path)
+    CBr, SCr = oracle.quantize_weight_f8(W_t, fmt)
+    ref, O, _ = oracle.matmul_f8(X, CBr, SCr, 6.0, fmt=fmt)
     assert len(O) > 32
-    assert_f8_close(d2h(out), ref, X, CBr, SCr, 6.0)
+    assert_f8_close(d2h(out), ref, X, CBr, SCr, 6.0, fmt=fmt)
 
 
 @pytest.mark.parametrize("path,n_out", [(L.PATH_GEMM, 1), (L.PATH_DECODE, 1), (L.PATH_GEMM, 40),
                                         (L.PATH_DECODE, 40)])
-def test_matmul_f8_exact_on_representable_inputs(path, n_out):
-    # entries of at most 3 significant bits, products summed exactly in fp32
-    # (every partial sum is a multiple of 2^-8 below 2^15): the output is the
-    # exact product rounded once, bit for bit
+@FMTS
+def test_matmul_f8_exact_on_representable_inputs(path, n_out, fmt):
+    # entries of at most 3 (E5M2) or 4 (E4M3) significant bits, products
+    # summed exactly in fp32 (every partial sum is a multiple of 2^-10 below
+    # 2^15, and the scaled products of a group of eight lie within 13 bits of
+    # its largest): the output is the exact product rounded once, bit for bit
     rng = np.random.default_rng(31)
     T, K, N = 12 if path == L.PATH_DECODE else 40, 512, 128
-    X = rng.choice([-3.0, -1.5, -1.0, -0.5, 0.0, 0.25, 0.75, 1.0, 2.0, 3.5], (T, K))
+    if fmt == "e4m3":
+        xs = [-3.0, -1.875, -1.0, -0.5, 0.0, 0.25, 0.9375, 1.0, 2.0, 3.5]
+        ws = [-0.375, -0.25, -0.234375, 0.0, 0.0625, 0.125, 0.1875, 0.25]
+    else:
+        xs = [-3.0, -1.5, -1.0, -0.5, 0.0, 0.25, 0.75, 1.0, 2.0, 3.5]
+        ws = [-0.375, -0.25, -0.125, 0.0, 0.0625, 0.125, 0.1875, 0.25]
+    X = rng.choice(xs, (T, K))
     X[:, 0] = 3.5
     X[::2, 17:17 + n_out] = 24.0          # outlier columns (40: the GEMM path's fp16 pass)
-    W = rng.choice([-0.375, -0.25, -0.125, 0.0, 0.0625, 0.125, 0.1875, 0.25], (N, K))
+    W = rng.choice(ws, (N, K))
     W[:, 1] = 0.375
-    say("matmul_f8 representable path=%d n_out=%d" % (path, n_out))
-    CB8, SC8 = L.llmint8_quantize_weight_f8(h2d(W.astype(np.float16)))
-    out = L.llmint8_matmul_f8_path(h2d(X.astype(np.float16)), CB8, SC8, 6.0, path=path)
+    say("matmul %s representable path=%d n_out=%d" % (fmt, path, n_out))
+    CB8, SC8 = API[fmt]["qw"](h2d(W.astype(np.float16)))
+    out = API[fmt]["mmp"](h2d(X.astype(np.float16)), CB8, SC8, 6.0, path=path)
     exact = (X @ W.T).astype(np.float16).view(np.uint16)
-    CBr, SCr = oracle.quantize_weight_f8(W.astype(np.float16))
-    ref, _, _ = oracle.matmul_f8(X.astype(np.float16), CBr, SCr, 6.0)
+    CBr, SCr = oracle.quantize_weight_f8(W.astype(np.float16), fmt)
+    ref, _, _ = oracle.matmul_f8(X.astype(np.float16), CBr, SCr, 6.0, fmt=fmt)
     assert np.array_equal(ref, exact)
     assert_equal_exact(d2h(out).view(np.uint16), exact, "out")
 
 
 @pytest.mark.parametrize("which", ["fc1", "decode4"])
-def test_matmul_f8_full_size_sampled(which):
+@FMTS
+def test_matmul_f8_full_size_sampled(which, fmt):
     if which == "fc1":
         d = workloads.ffn_6p7b(with_fc2=False)
     else:
@@ -173,41 +197,42 @@ def test_matmul_f8_full_size_sampled(which):
     X, W_t = d["X"], d["W_t"]
     T, K = X.shape
     N = W_t.shape[0]
-    say("matmul_f8 full size %s T=%d K=%d N=%d" % (which, T, K, N))
-    CB8, SC8 = L.llmint8_quantize_weight_f8(h2d(W_t))
-    out = d2h(L.llmint8_matmul_f8(h2d(X), CB8, SC8, 6.0))
+    say("matmul %s full size %s T=%d K=%d N=%d" % (fmt, which, T, K, N))
+    CB8, SC8 = API[fmt]["qw"](h2d(W_t))
+    out = d2h(API[fmt]["mm"](h2d(X), CB8, SC8, 6.0))
     CBh, SCh = d2h(CB8), d2h(SC8)
     rng = np.random.default_rng(6)
     if which == "fc1":
         rows = sample_rows(T, n_random=14)
-        CBr, SCr = oracle.quantize_weight_f8(W_t)
+        CBr, SCr = oracle.quantize_weight_f8(W_t, fmt)
         assert_equal_exact(CBh, CBr, "CB8")
         assert_equal_exact(SCh, SCr, "SC8")
-        ref, _, _ = oracle.matmul_f8(X, CBr, SCr, 6.0, rows=rows)
-        assert_f8_close(out[rows], ref, X, CBr, SCr, 6.0, rows=rows, what="out rows")
+        ref, _, _ = oracle.matmul_f8(X, CBr, SCr, 6.0, rows=rows, fmt=fmt)
+        assert_f8_close(out[rows], ref, X, CBr, SCr, 6.0, rows=rows, what="out rows", fmt=fmt)
     else:
         cols = np.unique(np.r_[0, N - 1, rng.choice(N, 400, replace=False)])
-        CBr, SCr = oracle.quantize_weight_f8(W_t[cols])
+        CBr, SCr = oracle.quantize_weight_f8(W_t[cols], fmt)
         assert_equal_exact(CBh[cols], CBr, "CB8 sample")
         assert_equal_exact(SCh[cols], SCr, "SC8 sample")
-        ref, _, _ = oracle.matmul_f8(X, CBr, SCr, 6.0)
+        ref, _, _ = oracle.matmul_f8(X, CBr, SCr, 6.0, fmt=fmt)
         assert_f8_close(np.ascontiguousarray(out[:, cols]), ref, X, CBr, SCr, 6.0,
-                        what="out cols")
+                        what="out cols", fmt=fmt)
 
 
 # Decode shapes past the few-rows kernel's K limit (2 <= T <= 16, K > 16384):
 # the three-kernel quantization in fragment order, then the weight stream.
 @pytest.mark.parametrize("T,K", [(4, 16448), (16, 24576)])
 @pytest.mark.parametrize("thr", [6.0, 0.0, np.inf])
-def test_decode_f8_past_few_rows_limit(T, K, thr):
+@FMTS
+def test_decode_f8_past_few_rows_limit(T, K, thr, fmt):
     N = 256
-    say("decode f8 past the few-rows limit T=%d K=%d thr=%s" % (T, K, thr))
+    say("decode %s past the few-rows limit T=%d K=%d thr=%s" % (fmt, T, K, thr))
     X, W_t, _ = f8_case(T, K, N, seed=T + K, n_dims=6, p=1.0)
-    CB8, SC8 = L.llmint8_quantize_weight_f8(h2d(W_t))
-    out = L.llmint8_matmul_f8_path(h2d(X), CB8, SC8, thr, path=L.PATH_DECODE)
-    CBr, SCr = oracle.quantize_weight_f8(W_t)
-    ref, _, _ = oracle.matmul_f8(X, CBr, SCr, thr)
-    assert_f8_close(d2h(out), ref, X, CBr, SCr, thr)
+    CB8, SC8 = API[fmt]["qw"](h2d(W_t))
+    out = API[fmt]["mmp"](h2d(X), CB8, SC8, thr, path=L.PATH_DECODE)
+    CBr, SCr = oracle.quantize_weight_f8(W_t, fmt)
+    ref, _, _ = oracle.matmul_f8(X, CBr, SCr, thr, fmt=fmt)
+    assert_f8_close(d2h(out), ref, X, CBr, SCr, thr, fmt=fmt)
 
 
 # More than 32 outlier columns on the GEMM path, both ways of forming the fp16
@@ -215,9 +240,10 @@ def test_decode_f8_past_few_rows_limit(T, K, thr):
 # place over the groups that hold outliers (clustered, or past 1024 columns).
 @pytest.mark.parametrize("cols", [np.arange(100) * 40 + 3, np.arange(1500, 1700),
                                   np.arange(1040) * 4 + 1])
-def test_f8_many_outliers_compact_and_dense(cols):
+@FMTS
+def test_f8_many_outliers_compact_and_dense(cols, fmt):
     T, K, N = 300, 4224, 320
-    say("f8 many outliers n=%d" % len(cols))
+    say("%s many outliers n=%d" % (fmt, len(cols)))
     X, W_t, _ = workloads.case(T, K, N, n_dims=0, seed=len(cols))
     rng = np.random.default_rng(len(cols) + 1)
     X = X.astype(np.float32)
@@ -226,9 +252,9 @@ def test_f8_many_outliers_compact_and_dense(cols):
         rows[0] = True
         X[rows, c] = rng.uniform(8.0, 60.0, rows.sum())
     X = X.astype(np.float16)
-    CB8, SC8 = L.llmint8_quantize_weight_f8(h2d(W_t))
-    out = L.llmint8_matmul_f8(h2d(X), CB8, SC8, 6.0)
-    CBr, SCr = oracle.quantize_weight_f8(W_t)
-    ref, O, _ = oracle.matmul_f8(X, CBr, SCr, 6.0)
+    CB8, SC8 = API[fmt]["qw"](h2d(W_t))
+    out = API[fmt]["mm"](h2d(X), CB8, SC8, 6.0)
+    CBr, SCr = oracle.quantize_weight_f8(W_t, fmt)
+    ref, O, _ = oracle.matmul_f8(X, CBr, SCr, 6.0, fmt=fmt)
     assert len(O) == len(cols)
-    assert_f8_close(d2h(out), ref, X, CBr, SCr, 6.0)
+    assert_f8_close(d2h(out), ref, X, CBr, SCr, 6.0, fmt=fmt)
