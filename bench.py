@@ -88,6 +88,7 @@ class HipEvents:
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.made = []
 
     def create(self):
@@ -97,6 +98,11 @@ class HipEvents:
             raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
         self.made.append(e.value)
         return e.value
+
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -111,15 +117,21 @@ class HipEvents:
         self.made = []
 
 
-def timed_steps(torch, L, X, CBs, SCB, thr, out, ws, steps, warmup, ev):
+def timed_steps(torch, L, X, CBs, SCB, thr, out, ws, steps, warmup, ev, extra=None):
     """`warmup` untimed steps, `steps` timed ones (plain llmint8_matmul calls), then
     `steps` more with HIP events recorded around the main kernel on its stream.
     An event record between two kernels holds the second back by a few
     microseconds, so the events stay out of the timed steps.  Returns
-    (ms per step, mean main-kernel ms, per-launch main-kernel ms)."""
+    (ms per step, mean main-kernel ms, per-launch main-kernel ms).  With a
+    dict `extra`, the second pass also records an event before each call:
+    extra["step_ms"] and extra["pre_ms"] get each call's time from it to the
+    end of the main kernel and to its start (the quantization kernels plus
+    the one event record's gap), in the same pass as the kernel times."""
     for i in range(warmup):
         L.llmint8_matmul(X, CBs[i % len(CBs)], SCB, thr, out=out, ws=ws)
     pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    pre = [ev.create() for _ in range(steps)] if extra is not None else None
+    stream = torch.cuda.current_stream(X.device).cuda_stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -127,10 +139,15 @@ def timed_steps(torch, L, X, CBs, SCB, thr, out, ws, steps, warmup, ev):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(steps):
+        if pre is not None:
+            ev.record(pre[i], stream)
         L.llmint8_matmul_path(X, CBs[i % len(CBs)], SCB, thr, out=out, ws=ws, path=L.PATH_AUTO,
                               main_start=pairs[i][0], main_stop=pairs[i][1])
     torch.cuda.synchronize()
     kern = [ev.elapsed_ms(a, b) for a, b in pairs]
+    if pre is not None:
+        extra["step_ms"] = [ev.elapsed_ms(p, b) for p, (a, b) in zip(pre, pairs)]
+        extra["pre_ms"] = [ev.elapsed_ms(p, a) for p, (a, b) in zip(pre, pairs)]
     return (t1 - t0) * 1e3 / steps, float(np.mean(kern)), kern
 
 
@@ -557,8 +574,9 @@ def main():
     _, _, _, n_out = L.llmint8_quantize_act(X, thr)
     n_outliers = int(n_out.cpu()[0])
 
+    same_pass = {}
     ms, gemm_ms, gemm_kern = timed_steps(torch, L, X, [CB], SCB, thr, out, ws, args.steps,
-                                         args.warmup, ev)
+                                         args.warmup, ev, extra=same_pass)
     ops = 2.0 * T * K * N
     value = ops / (ms * 1e-3) / 1e12
     achieved = ops / (gemm_ms * 1e-3) / 1e12
@@ -593,6 +611,14 @@ def main():
                                       "stay out of ms_per_step)"},
     }
     result["roofline"].update(spread_us(gemm_kern))
+    med = lambda v: round(float(np.median(np.asarray(v) * 1e3)), 2)
+    result["roofline"]["same_pass"] = {
+        "step_us_median": med(same_pass["step_ms"]),
+        "before_kernel_us_median": med(same_pass["pre_ms"]),
+        "note": "event before each call to the end / start of k_gemm_both, in the pass that "
+                "times the kernel: the quantization kernels and one event record's gap come "
+                "before the kernel; the plain steps of ms_per_step ran earlier, at another "
+                "point of the clock's power management"}
     Xq = L.llmint8_quantize_act(X, thr)[0]
     ceil8 = mfma_ceiling(torch, L, Xq, CB, ev)
     del Xq
