@@ -15,8 +15,9 @@ Everything computed runs in libllmint8's HIP kernels: weight quantization
 an optional ReLU fused into its output rounding for the feed-forward
 expansion layers.  `quant` selects the 8-bit part's quantizer: "absmax" (the
 method's vector-wise absmax int8), or the library's two variants,
-"zeropoint" (asymmetric int8, llmint8_matmul_zp) and "fp8" (E5M2,
-llmint8_matmul_f8); the variants have no fused activation.  This module only holds the tensors, flattens leading
+"zeropoint" (asymmetric int8, llmint8_matmul_zp), "fp8" (E5M2,
+llmint8_matmul_f8) and "fp8_e4m3" (E4M3, llmint8_matmul_e4m3); the variants
+have no fused activation.  This module only holds the tensors, flattens leading
 dimensions into rows, and shares one workspace buffer per (device, stream)
 among all instances, grown as needed, so that steady-state calls allocate
 nothing but their output and a model needs one workspace, not one per layer.
@@ -42,7 +43,9 @@ def _shared_workspace(nbytes, device):
     return ws
 
 _ACTS = {None: L.ACT_NONE, "none": L.ACT_NONE, "relu": L.ACT_RELU}
-_QUANTS = ("absmax", "zeropoint", "fp8")
+_QUANTS = ("absmax", "zeropoint", "fp8", "fp8_e4m3")
+# the FP8 quantizers: the binding's function-name suffix of each format
+_FP8 = {"fp8": "f8", "fp8_e4m3": "e4m3"}
 
 
 class Linear8bitLt(torch.nn.Module):
@@ -87,7 +90,7 @@ class Linear8bitLt(torch.nn.Module):
                 requires_grad=False)
         else:
             self.register_parameter("bias", None)
-        self.register_buffer("CB", None)    # int8 codes (fp8: E5M2 codes, uint8)
+        self.register_buffer("CB", None)    # int8 codes (fp8 / fp8_e4m3: E5M2 / E4M3 codes, uint8)
         self.register_buffer("SCB", None)   # absmax: column absmax; zero-point: nd; fp8: 2^-e
         self.register_buffer("ZP", None)    # zero-point variant: zero points and code sums
         self.register_buffer("RS", None)
@@ -117,7 +120,7 @@ class Linear8bitLt(torch.nn.Module):
             raise RuntimeError("Linear8bitLt: move the module to a HIP device before quantizing")
         w = self.weight.detach().contiguous()
         if self.CB is None or self.CB.device != w.device:
-            dt = torch.uint8 if self.quant == "fp8" else torch.int8
+            dt = torch.uint8 if self.quant in _FP8 else torch.int8
             self.CB = torch.empty((self.out_features, self.in_features), dtype=dt, device=w.device)
             self.SCB = torch.empty((self.out_features,), dtype=torch.float32, device=w.device)
             if self.quant == "zeropoint":
@@ -125,8 +128,8 @@ class Linear8bitLt(torch.nn.Module):
                 self.RS = torch.empty((self.out_features,), dtype=torch.int32, device=w.device)
         if self.quant == "zeropoint":
             L.llmint8_quantize_weight_zp(w, CB=self.CB, ND=self.SCB, ZP=self.ZP, RS=self.RS)
-        elif self.quant == "fp8":
-            L.llmint8_quantize_weight_f8(w, CB8=self.CB, SC8=self.SCB)
+        elif self.quant in _FP8:
+            getattr(L, "llmint8_quantize_weight_" + _FP8[self.quant])(w, CB8=self.CB, SC8=self.SCB)
         else:
             L.llmint8_quantize_weight(w, CB=self.CB, SCB=self.SCB)
         if not self.has_fp16_weights:
@@ -154,8 +157,9 @@ class Linear8bitLt(torch.nn.Module):
         if self.quant == "zeropoint":
             out = L.llmint8_matmul_zp(x2, self.CB, self.SCB, self.ZP, self.RS, self.threshold,
                                       bias=self.bias, ws=ws)
-        elif self.quant == "fp8":
-            out = L.llmint8_matmul_f8(x2, self.CB, self.SCB, self.threshold, bias=self.bias, ws=ws)
+        elif self.quant in _FP8:
+            out = getattr(L, "llmint8_matmul_" + _FP8[self.quant])(
+                x2, self.CB, self.SCB, self.threshold, bias=self.bias, ws=ws)
         else:
             out = L.llmint8_matmul_act(x2, self.CB, self.SCB, self.threshold,
                                        _ACTS[self.activation], bias=self.bias, ws=ws)

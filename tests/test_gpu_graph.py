@@ -20,7 +20,7 @@ from tests.gpu_helpers import dev, h2d, say
 @pytest.mark.parametrize("T,K,N", [(1, 1024, 512), (4, 2048, 256), (16, 1088, 320),
                                    (300, 512, 512)])
 @pytest.mark.parametrize("thr", [6.0, 0.0])
-@pytest.mark.parametrize("variant", ["absmax", "zeropoint", "fp8"])
+@pytest.mark.parametrize("variant", ["absmax", "zeropoint", "fp8", "fp8_e4m3"])
 def test_matmul_graph_replay(T, K, N, thr, variant):
     say("graph replay %s T=%d K=%d N=%d thr=%s" % (variant, T, K, N, thr))
     d = dev()
@@ -42,6 +42,11 @@ def test_matmul_graph_replay(T, K, N, thr, variant):
 
         def call(x, o, w):
             L.llmint8_matmul_f8(x, CB8, SC8, thr, bias=bias, out=o, ws=w)
+    elif variant == "fp8_e4m3":
+        CB8, SC8 = L.llmint8_quantize_weight_e4m3(h2d(W_t))
+
+        def call(x, o, w):
+            L.llmint8_matmul_e4m3(x, CB8, SC8, thr, bias=bias, out=o, ws=w)
     else:
         CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
 

@@ -36,6 +36,9 @@ def test_variant_options():
     with pytest.raises(ValueError):
         Linear8bitLt(33344, 64, quant="zeropoint")
     assert "quant=fp8" in repr(Linear8bitLt(64, 64, quant="fp8"))
+    with pytest.raises(ValueError):
+        Linear8bitLt(64, 64, quant="fp8_e4m3", activation="relu")
+    assert "quant=fp8_e4m3" in repr(Linear8bitLt(64, 64, quant="fp8_e4m3"))
 
 
 def test_quantize_needs_a_device():
@@ -169,7 +172,7 @@ def test_ffn_pair_chained_through_two_modules():
 
 
 @gpu
-@pytest.mark.parametrize("quant", ["zeropoint", "fp8"])
+@pytest.mark.parametrize("quant", ["zeropoint", "fp8", "fp8_e4m3"])
 @pytest.mark.parametrize("T", [4, 100])
 def test_variant_modules_match_their_oracles(quant, T):
     # the module's weight buffers and output against the variant's oracle,
@@ -194,12 +197,13 @@ def test_variant_modules_match_their_oracles(quant, T):
         g, r = got.astype(np.float64), ref.view(np.float16).astype(np.float64)
         assert np.all(np.abs(g - r) <= 1e-3 + 2e-3 * np.abs(r))
     else:
-        CB8, SC8 = oracle.quantize_weight_f8(W_t)
+        fmt = "e4m3" if quant == "fp8_e4m3" else "e5m2"
+        CB8, SC8 = oracle.quantize_weight_f8(W_t, fmt)
         assert np.array_equal(m.CB.cpu().numpy(), CB8) and np.array_equal(m.SCB.cpu().numpy(), SC8)
-        ref, O, sc = oracle.matmul_f8(X, CB8, SC8, 6.0, bias=bias)
-        Xq8, _ = oracle.quantize_rows_f8(X, O)
-        S = (np.abs(oracle.e5m2_to_double(Xq8)) * sc.astype(np.float64)[:, None]) @ (
-            np.abs(oracle.e5m2_to_double(CB8)) * SC8.astype(np.float64)[:, None]).T
+        ref, O, sc = oracle.matmul_f8(X, CB8, SC8, 6.0, bias=bias, fmt=fmt)
+        Xq8, _ = oracle.quantize_rows_f8(X, O, fmt=fmt)
+        S = (np.abs(oracle.f8_to_double(Xq8, fmt)) * sc.astype(np.float64)[:, None]) @ (
+            np.abs(oracle.f8_to_double(CB8, fmt)) * SC8.astype(np.float64)[:, None]).T
         g, r = got.astype(np.float64), ref.view(np.float16).astype(np.float64)
         # the FP8 accumulation bound of tests/test_gpu_fp8.py
         from tests.test_gpu_fp8 import f8_accumulation_bound
