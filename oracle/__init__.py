@@ -234,9 +234,9 @@ def matmul(X, CB, SCB, threshold=6.0, bias=None, rows=None, cols=None, relu=Fals
 # ---------------------------------------------------------------------------
 # Zero-point (asymmetric) vector-wise variant.  The readings of the page's
 # garbled zero-point formulas are stated in llmint8_oracle.c; in short, per
-# vector: range [min(min,0), max(max,0)], d = fp32(max' - min'),
-# nd = fp32(254/d), zp = RNE(nd*min') + 127, code = min(RNE(nd*x) - zp, 127),
-# and x ~= (code + zp) / nd.
+# vector: range [min(min,0), max(max,0)], d = max' - min', nd = 254/d exact,
+# zp = RNE(nd*min') + 127, code = RNE(nd*x) - zp (exact rationals rounded,
+# ties to even), x ~= (code + zp) / nd; the stored nd is the nearest fp32.
 # ---------------------------------------------------------------------------
 def dequant_weight_zp(cb, zp, nd):
     """Binary16 value of fp32((cb + zp) / nd), element-wise (0 where nd = 0)."""

@@ -372,59 +372,91 @@ int64_t oracle_matmul(const uint16_t *X, int64_t T, int64_t K, int64_t N,
 /*   - the range always contains 0: min' = min(min, 0), max' = max(max, 0),  */
 /*     so zp fits the page's int16 (it lies in [-127, 127]), the value 0 has */
 /*     an exact code (-zp), and every |A_i8 + zp| <= 254;                    */
-/*   - d = fp32(max' - min') and nd = fp32(254 / d), each rounded once;      */
-/*     d = 0 (an all-zero vector) gives nd = 0, zp = 0 and codes 0;          */
-/*   - zp = RNE(nd * min') + 127 and A_i8 = min(RNE(nd * x) - zp, 127), both */
-/*     roundings of the exact product nd * x (ties to even); the clamp only  */
-/*     acts when fp32 rounding makes RNE(nd*max') - RNE(nd*min') = 255;      */
+/*   - nd = 254 / (max' - min') is the exact rational, as round(127 x / a)   */
+/*     is in the absmax variant: the page fixes no precision, so nothing is  */
+/*     rounded before the codes; d = max' - min' = 0 (an all-zero vector)    */
+/*     gives nd = 0, zp = 0 and codes 0;                                     */
+/*   - zp = RNE(nd * min') + 127 and A_i8 = RNE(nd * x) - zp, roundings of   */
+/*     the exact rationals to the nearest integer, ties to even; then        */
+/*     A_i8 + zp runs from RNE(nd * min') to RNE(nd * min' + 254) =          */
+/*     RNE(nd * min') + 254, so every code lies in [-127, 127] with no clamp; */
+/*   - what is stored for dequantization (ND of a weight column, nd of an    */
+/*     activation row) is the fp32 value nearest to the exact nd;            */
 /*   - outlier columns hold the code of 0, -zp, so that A_i8 + zp_a = 0      */
 /*     there and they add nothing to the integer product;                    */
-/*   - the fp16 outlier product uses the weight dequantized as               */
-/*     fp16(fp32(CB + zp) / nd) (one fp32 division, then one rounding to     */
-/*     fp16; 0 when nd = 0).                                                 */
-/* Parity unpinned: the last bit of d and nd.  The pages fix no precision    */
-/* for them; fp32 is a reading, and the pins that recompute d and nd in      */
-/* numpy fp32 check this code against that reading, not the reading against */
-/* the pages.  Everything downstream of nd (codes, zp, code sums, products)  */
-/* is pinned against exact rationals and closed forms.                       */
+/*   - the fp16 outlier product uses the weight dequantized from the stored  */
+/*     values as fp16(fp32(CB + zp) / ND) (one fp32 division, then one       */
+/*     rounding to fp16; 0 when ND = 0).                                     */
+/* fp16 values are integer multiples of 2^-24, so with X = x * 2^24 and      */
+/* D = d * 2^24 (integers, |X| < 2^40, D < 2^41) every rational here is a    */
+/* quotient of integers: nd * x = 254 X / D.                                 */
 /* ------------------------------------------------------------------------ */
 
-/* Exact product of an fp32 scale and an fp16 value (24 + 11 significant bits
- * fit fp64's 53), rounded to the nearest integer with ties to even (rint in
- * the default rounding mode). */
-static int64_t rne_product(float nd, double x)
+/* x * 2^24 as an integer (exact for every binary16 value). */
+static int64_t fixed24(double x)
 {
-    return (int64_t)rint((double)nd * x);
+    return (int64_t)ldexp(x, 24);
+}
+
+/* num / den rounded to the nearest integer, ties to even (den > 0). */
+static int64_t rne_ratio(int64_t num, int64_t den)
+{
+    int64_t q = num / den, r = num % den;     /* C division truncates toward 0 */
+    if (r < 0) {                              /* make it floor: 0 <= r < den */
+        q -= 1;
+        r += den;
+    }
+    if (2 * r > den || (2 * r == den && (q & 1)))
+        q += 1;
+    return q;
+}
+
+/* The fp32 value nearest to 254 * 2^24 / D (ties to even), D > 0: the
+ * quotient scaled by a power of two into [2^23, 2^24), rounded as an
+ * integer. */
+static float nearest_f32_nd(int64_t D)
+{
+    unsigned __int128 num = (unsigned __int128)254 << 24, den = (unsigned __int128)D;
+    int e = 0;                                 /* value = (num / den) * 2^-e */
+    while (num / den >= ((unsigned __int128)1 << 24)) {
+        den <<= 1;                             /* halves the quotient */
+        --e;
+    }
+    while (num / den < ((unsigned __int128)1 << 23)) {
+        num <<= 1;                             /* doubles the quotient */
+        ++e;
+    }
+    unsigned __int128 q = num / den, r = num % den;
+    if (2 * r > den || (2 * r == den && (q & 1)))
+        q += 1;
+    return (float)ldexp((double)(uint64_t)q, -e);
 }
 
 /* The zero-point parameters of one vector from its smallest and largest
- * value (binary16, already widened to double) with 0 added to the range. */
-static void zp_params(double vmin, double vmax, float *nd, int32_t *zp)
+ * value (binary16, already widened to double) with 0 added to the range:
+ * D = (max' - min') * 2^24, the stored nd and zp. */
+static void zp_params(double vmin, double vmax, int64_t *D, float *nd, int32_t *zp)
 {
     if (vmin > 0.0)
         vmin = 0.0;
     if (vmax < 0.0)
         vmax = 0.0;
-    float d = (float)vmax - (float)vmin;      /* one fp32 rounding */
-    if (d == 0.0f) {
+    *D = fixed24(vmax) - fixed24(vmin);
+    if (*D == 0) {
         *nd = 0.0f;
         *zp = 0;
         return;
     }
-    float n = 254.0f / d;                     /* one fp32 division */
-    *nd = n;
-    *zp = (int32_t)(rne_product(n, vmin) + 127);
+    *nd = nearest_f32_nd(*D);
+    *zp = (int32_t)(rne_ratio(254 * fixed24(vmin), *D) + 127);
 }
 
-/* Code of value x in a vector with parameters (nd, zp). */
-static int8_t zp_code(float nd, int32_t zp, double x)
+/* Code of value x in a vector with parameters (D, zp). */
+static int8_t zp_code(int64_t D, int32_t zp, double x)
 {
-    if (nd == 0.0f)
+    if (D == 0)
         return 0;
-    int64_t q = rne_product(nd, x) - zp;
-    if (q > 127)
-        q = 127;
-    return (int8_t)q;
+    return (int8_t)(rne_ratio(254 * fixed24(x), D) - zp);
 }
 
 /* Dequantized fp16 weight of code cb in a column with parameters (nd, zp). */
@@ -451,9 +483,10 @@ void oracle_quantize_weight_zp(const uint16_t *W_t, int64_t K, int64_t N,
             if (v > vmax)
                 vmax = v;
         }
-        zp_params(vmin, vmax, &ND[n], &ZP[n]);
+        int64_t D;
+        zp_params(vmin, vmax, &D, &ND[n], &ZP[n]);
         for (int64_t k = 0; k < K; ++k)
-            CB[n * K + k] = zp_code(ND[n], ZP[n], oracle_half_to_double(row[k]));
+            CB[n * K + k] = zp_code(D, ZP[n], oracle_half_to_double(row[k]));
     }
 }
 
@@ -482,10 +515,11 @@ void oracle_quantize_rows_zp(const uint16_t *X, int64_t T, int64_t K,
             if (v > vmax)
                 vmax = v;
         }
-        zp_params(vmin, vmax, &nd[i], &zp[i]);
+        int64_t D;
+        zp_params(vmin, vmax, &D, &nd[i], &zp[i]);
         for (int64_t k = 0; k < K; ++k)
             Xq[i * K + k] = isout[k] ? (int8_t)(-zp[i])
-                                     : zp_code(nd[i], zp[i], oracle_half_to_double(xr[k]));
+                                     : zp_code(D, zp[i], oracle_half_to_double(xr[k]));
     }
     free(isout);
 }

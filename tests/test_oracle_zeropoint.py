@@ -29,9 +29,25 @@ def widened(X):
     return np.asarray(X, np.float16).astype(np.float64)
 
 
-def exact_shifted(nd, x):
-    """RNE of the exact product nd*x (nd an fp32 value, x an fp16 value)."""
-    return round(Fraction(float(nd)) * Fraction(float(x)))   # round() on a Fraction: ties to even
+def exact_params(row):
+    """(d, nd, zp) of one vector from exact rationals: the range with 0 added,
+    nd = 254/d, zp = RNE(nd*min') + 127 (round() on a Fraction: ties to even)."""
+    xs = widened(row)
+    mn, mx = min(xs.min(), 0.0), max(xs.max(), 0.0)
+    d = Fraction(mx) - Fraction(mn)
+    if d == 0:
+        return d, Fraction(0), 0
+    nd = 254 / d
+    return d, nd, round(nd * Fraction(mn)) + 127
+
+
+def nearest_f32(v):
+    """The fp32 value nearest to the positive rational v, ties to even: the
+    best of numpy's float32 of float(v) and its two neighbours."""
+    c = np.float32(float(v))
+    cands = [c, np.nextafter(c, np.float32(np.inf)), np.nextafter(c, np.float32(0))]
+    return min(cands, key=lambda f: (abs(Fraction(float(f)) - v),
+                                     int(np.float32(f).view(np.uint32)) & 1))
 
 
 def test_relu_row_uses_the_whole_code_range():
@@ -90,18 +106,74 @@ def test_codes_are_exact_rational_roundings(seed):
     q, nd, zp = oracle.quantize_rows_zp(X, NO_O)
     Xd = widened(X)
     for t in range(X.shape[0]):
-        vmin = min(Xd[t].min(), 0.0)
-        vmax = max(Xd[t].max(), 0.0)
-        d = np.float32(vmax) - np.float32(vmin)          # numpy fp32: IEEE, one rounding
+        d, ndx, zpx = exact_params(X[t])
         if d == 0:
             assert nd[t] == 0 and zp[t] == 0 and not q[t].any()
             continue
-        assert nd[t] == np.float32(254.0) / d
-        assert zp[t] == exact_shifted(nd[t], vmin) + 127
+        assert nd[t] == nearest_f32(ndx)
+        assert zp[t] == zpx
         for k in range(X.shape[1]):
-            want = exact_shifted(nd[t], Xd[t, k]) - int(zp[t])
-            assert q[t, k] == min(want, 127), (t, k)
+            assert q[t, k] == round(ndx * Fraction(Xd[t, k])) - zpx, (t, k)
     assert np.abs(q.astype(np.int32)).max() <= 127
+
+
+# Ranges [-lo, hi] (binary16 values) whose 254/d, rounded to fp64 first, lands
+# exactly on the midpoint between two fp32 values while the exact quotient
+# lies above it, so that rounding the fp64 quotient to fp32 gives the lower
+# neighbour instead of the nearest; found by a search over binary16 pairs.
+MIDPOINT_RANGES = [(7112.0, 889), (14224.0, 1778)]     # (hi, bits of lo)
+
+
+def test_stored_nd_is_not_a_double_rounding():
+    for hi, lo_bits in MIDPOINT_RANGES:
+        lo = float(np.array([lo_bits], np.uint16).view(np.float16)[0])
+        row = f16([hi, -lo, 1.0])
+        q, nd, zp = oracle.quantize_rows_zp(row[None, :], NO_O)
+        d, ndx, zpx = exact_params(row)
+        via_fp64 = np.float32(254.0 / (hi + lo))
+        assert nd[0] == nearest_f32(ndx) and nd[0] != via_fp64
+
+
+def _random_rows(seed, rows=120, K=256):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((rows, K)) * rng.uniform(0.01, 100, (rows, 1))
+    X[::3] = np.abs(X[::3])
+    return f16(X)
+
+
+def test_codes_follow_the_exact_nd_not_a_rounded_one():
+    # rounding nd to fp32 before the products (the natural fp32 shortcut)
+    # moves some codes by one; the oracle must give the exact-rational code
+    # there too.  The seeded rows hold such cases, and the test requires them.
+    X = _random_rows(1)
+    q, nd, zp = oracle.quantize_rows_zp(X, NO_O)
+    Xd = widened(X)
+    moved = 0
+    for t in range(X.shape[0]):
+        d, ndx, zpx = exact_params(X[t])
+        mn, mx = min(Xd[t].min(), 0.0), max(Xd[t].max(), 0.0)
+        nd32 = Fraction(float(np.float32(254.0) / (np.float32(mx) - np.float32(mn))))
+        zp32 = round(nd32 * Fraction(mn)) + 127
+        for k in range(X.shape[1]):
+            exact = round(ndx * Fraction(Xd[t, k])) - zpx
+            shortcut = min(round(nd32 * Fraction(Xd[t, k])) - zp32, 127)
+            assert q[t, k] == exact, (t, k)
+            moved += shortcut != exact
+    assert moved >= 1
+
+
+def test_stored_nd_is_the_nearest_fp32():
+    # vectors whose range d has many significant bits (a large and a tiny
+    # end), so 254/d is far from any short binary fraction
+    rng = np.random.default_rng(7)
+    for _ in range(300):
+        hi = float(np.float16(rng.uniform(1, 60000)))
+        lo = -float(np.float16(rng.uniform(0, 1) * 2.0 ** -int(rng.integers(0, 24))))
+        row = f16([hi, lo, 0.5 * hi])
+        q, nd, zp = oracle.quantize_rows_zp(row[None, :], NO_O)
+        d, ndx, zpx = exact_params(row)
+        assert nd[0] == nearest_f32(ndx) and zp[0] == zpx
+        assert q[0, 0] == 127 and q[0, 1] == -127
 
 
 @pytest.mark.parametrize("seed", [3, 4])
@@ -110,15 +182,16 @@ def test_reconstruction_error_is_half_a_step(seed):
     q, nd, zp = oracle.quantize_rows_zp(X, NO_O)
     Xd = widened(X)
     for t in range(X.shape[0]):
-        if nd[t] == 0:
+        d, ndx, zpx = exact_params(X[t])
+        if d == 0:
             continue
-        xhat = (q[t].astype(np.float64) + zp[t]) / np.float64(nd[t])
-        step = 1.0 / np.float64(nd[t])
-        err = np.abs(Xd[t] - xhat)
-        # half a step, plus the fp32 rounding of nd (relative 2^-24 of |x|*nd)
-        assert np.all(err <= 0.5 * step * (1 + 1e-6) + np.abs(Xd[t]) * 2.0 ** -23), t
+        step = 1 / ndx
+        for k in range(X.shape[1]):
+            # x is within half a step of its dequantized value, exactly
+            assert abs(Fraction(Xd[t, k]) - (int(q[t, k]) + zpx) * step) <= step / 2, (t, k)
         # the range is covered: its ends take the extreme codes
         assert q[t].min() == -127 or Xd[t].min() > 0
+        assert q[t].max() == 127 or Xd[t].max() < 0
 
 
 def test_outlier_columns_hold_the_code_of_zero():
@@ -226,13 +299,11 @@ def test_negating_the_input_negates_the_output():
     CB, ND, ZP = oracle.quantize_weight_zp(W)
     out_p, O_p, nd_p, zp_p = oracle.matmul_zp(X, CB, ND, ZP, threshold=6.0)
     out_n, O_n, nd_n, zp_n = oracle.matmul_zp(-X, CB, ND, ZP, threshold=6.0)
-    # no code of either input was clamped, so the shifted codes negate exactly
-    for Xs, nd, zp, O in ((X, nd_p, zp_p, O_p), (-X, nd_n, zp_n, O_n)):
-        Xq, _, _ = oracle.quantize_rows_zp(Xs, O)
-        keep = np.ones(K, bool)
-        keep[O] = False
-        assert np.array_equal(_shifted(Xq, zp)[:, keep],
-                              np.rint(nd.astype(np.float64)[:, None] * widened(Xs))[:, keep])
+    # the range of -x is the range of x mirrored (same d), and rounding to
+    # nearest even is odd-symmetric, so the shifted codes negate exactly
+    Xq_p, _, _ = oracle.quantize_rows_zp(X, O_p)
+    Xq_n, _, _ = oracle.quantize_rows_zp(-X, O_n)
+    assert np.array_equal(_shifted(Xq_n, zp_n), -_shifted(Xq_p, zp_p))
     assert np.array_equal(O_p, O_n) and np.array_equal(nd_p, nd_n)
     assert np.array_equal(out_n, out_p ^ np.uint16(0x8000))
 
