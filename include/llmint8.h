@@ -214,12 +214,16 @@ LLMINT8_API llmint8_status_t llmint8_matmul_act(const uint16_t *X, int64_t T, in
  * W, over all K):
  *
  *   min' = min(min, 0), max' = max(max, 0)     (0 joins every range)
- *   d    = fp32(max' - min'),  nd = fp32(254 / d)   (d = 0: nd = 0, zp = 0)
+ *   d    = max' - min',  nd = 254 / d              (exact; d = 0: nd = 0, zp = 0)
  *   zp   = RNE(nd * min') + 127                     (in [-127, 127])
- *   code = min(RNE(nd * x) - zp, 127)               (in [-127, 127])
+ *   code = RNE(nd * x) - zp                         (in [-127, 127])
  *
- * RNE rounds the exact product nd*x to the nearest integer, ties to even;
- * code + zp = RNE(nd*x) is the page's shifted value and x ~= (code + zp)/nd.
+ * RNE rounds the exact rational nd*x = 254x/d to the nearest integer, ties
+ * to even (the page fixes no precision, so nothing is rounded before the
+ * codes, as in the absmax variant); code + zp = RNE(nd*x) is the page's
+ * shifted value and x ~= (code + zp)/nd.  What ND[n] and the activation
+ * rows' nd[t] store is the fp32 value nearest to the exact nd; the
+ * dequantization below uses those stored values.
  * Outlier columns of X (as for llmint8_matmul) hold the code of 0, -zp, so
  * they add nothing to the integer sum, and
  *

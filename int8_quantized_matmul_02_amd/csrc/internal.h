@@ -312,9 +312,10 @@ struct EpilogueArgs {
 
 // Zero-point variant (the asymmetric quantizer of the LLM.int8() summary,
 // "8-bit Data Types and Quantization"): per vector, range [min(min,0),
-// max(max,0)], d = fp32(max' - min'), nd = fp32(254/d), zp = RNE(nd*min') +
-// 127, code = min(RNE(nd*x) - zp, 127) (roundings of the exact product);
-// d = 0 gives nd = 0, zp = 0, codes 0.  Weight: per row of W_t over all K,
+// max(max,0)], d = max' - min', nd = 254/d (exact), zp = RNE(nd*min') + 127,
+// code = RNE(nd*x) - zp (roundings of the exact rationals, ties to even); the
+// stored nd is the fp32 value nearest to it; d = 0 gives nd = 0, zp = 0,
+// codes 0.  Weight: per row of W_t over all K,
 // with RS[n] the sum of the row's codes.  K <= kMaxKZp keeps the shifted
 // product sum_k (A+zp_a)(B+zp_b), |A+zp| <= 254, inside int32.
 constexpr int64_t kMaxKZp = 33286;

@@ -957,41 +957,87 @@ __device__ __forceinline__ void wave_minmax(float &mn, float &mx)
     }
 }
 
-// (nd, zp) of a vector whose range [mn, mx] already contains 0:
-// d = fp32(mx - mn) and nd = fp32(254/d), each rounded once (the division is
-// IEEE-correct: the library is built with correctly rounded fp32 division);
-// zp = RNE(nd*mn) + 127, the product rounded exactly once by the fused
-// multiply-add with kRoundMagic (|nd*mn| <= 254.0001, so the sum sits where
-// the fp32 spacing is 1).  d = 0 gives (0, 0).
+// RNE(254 x / d), the exact rational rounded to the nearest integer with ties
+// to even, for a binary16 value x (as fp32) and d = max' - min' > 0 of its
+// vector (exact in fp64), with r = 254/d correctly rounded in fp64.
+// y = x*r is within 2^-52 |254 x / d| <= 2^-44 of the rational (two fp64
+// roundings), while a rational that is not a tie lies at least 2^-42 from
+// every half-integer: 254x/d - (k + 1/2) = (508x - (2k+1) d) / (2d), the
+// numerator a nonzero multiple of 2^-24 (binary16 granularity) and d < 2^17.
+// So floor(y) + (frac > 1/2) is the answer unless frac is within 2^-40 of
+// 1/2; there the sign of 508x - (2k+1) d decides, computed exactly by one
+// fused multiply-add (508x has 18 significant bits, (2k+1) d at most 50, and
+// their difference is a multiple of 2^-24 below 2^27).
+__device__ __forceinline__ int rne254(float x, double d, double r)
+{
+    const double xd = (double)x;
+    const double y = xd * r;
+    const double k = __builtin_floor(y);
+    const double f = y - k;                    // exact
+    int q = (int)k + (f > 0.5 ? 1 : 0);
+    if (__builtin_fabs(f - 0.5) < 0x1p-40) {
+        const double e = __builtin_fma(-(2.0 * k + 1.0), d, 508.0 * xd);
+        q = (int)k + (e > 0.0 ? 1 : e < 0.0 ? 0 : ((int)k & 1));
+    }
+    return q;
+}
+
+// The fp32 value nearest to 254/d (ties to even), from r = 254/d correctly
+// rounded in fp64: fp32(r) is that value unless r lies within 2^-52 r of
+// the midpoint between two fp32 values (the exact quotient is within
+// 2^-53 r of r and could then sit on the midpoint's other side); there the
+// sign of mid*d - 254, exact in one fused multiply-add, picks the side.
+__device__ __forceinline__ float nearest_f32_254_over(double d, double r)
+{
+    const float f = (float)r;
+    const double fd = (double)f;
+    if (fd == r)
+        return f;
+    const unsigned fb = __builtin_bit_cast(unsigned, f);
+    const float g = __builtin_bit_cast(float, r > fd ? fb + 1u : fb - 1u);   // r > 0
+    const double mid = 0.5 * (fd + (double)g);                              // exact
+    if (__builtin_fabs(r - mid) > 0x1p-52 * r)
+        return f;
+    const float lo = __builtin_fminf(f, g), hi = __builtin_fmaxf(f, g);
+    const double e = __builtin_fma(mid, d, -254.0);
+    if (e > 0.0)
+        return lo;
+    if (e < 0.0)
+        return hi;
+    return (__builtin_bit_cast(unsigned, lo) & 1u) ? hi : lo;
+}
+
+// (nd, zp) of a vector whose range [mn, mx] (binary16 values as fp32)
+// already contains 0: nd = 254/d, d = mx - mn, is kept exact for the codes
+// (d exact in fp64, r = 254/d in fp64, rne254 rounds the rationals), and the
+// stored nd is its nearest fp32 value; zp = RNE(254 mn / d) + 127.  d = 0
+// gives nd = 0, zp = 0 (and codes 0).
 struct ZpParams {
+    double d, r;
     float nd;
     int zp;
 };
 __device__ __forceinline__ ZpParams zp_params(float mn, float mx)
 {
-    const float d = mx - mn;
-    if (!(d > 0.0f))
-        return ZpParams{0.0f, 0};
-    const float nd = 254.0f / d;
-    const float s = __builtin_fmaf(mn, nd, kRoundMagic);
-    return ZpParams{nd, (int)(s - kRoundMagic) + 127};
+    const double d = (double)mx - (double)mn;
+    if (!(d > 0.0))
+        return ZpParams{0.0, 0.0, 0.0f, 0};
+    const double r = 254.0 / d;
+    return ZpParams{d, r, nearest_f32_254_over(d, r), rne254(mn, d, r) + 127};
 }
 
-// Codes of 8 values, min(RNE(nd*x) - zp, 127): one fused multiply-add per
-// value with the addend kRoundMagic rounds the exact product to an integer
-// (ties to even, kRoundMagic being even; an odd addend such as
-// kRoundMagic - zp would send ties to odd), then zp (zpf, an integer, so the
-// subtraction is exact within [2^23, 2^24)) is subtracted, the clamp is an
-// fp32 min, and the code is the low byte.  The codes' sum is added to *sum
-// (bits(kRoundMagic + q) - bits(kRoundMagic) = q).
-__device__ __forceinline__ uint2 quant8_zp(uint4 v, float nd, float zpf, int &sum)
+// Codes of 8 values, RNE(254 x / d) - zp: RNE(254 x / d) runs from
+// RNE(254 mn / d) = zp - 127 to RNE(254 mn / d + 254) = zp + 127, so every
+// code lies in [-127, 127].  The codes' sum is added to *sum; d = 0 gives
+// codes 0.
+__device__ __forceinline__ uint2 quant8_zp(uint4 v, const ZpParams &p, int &sum)
 {
     float s[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        s[i] = __builtin_fminf(__builtin_fmaf(h2f(half_at(v, i)), nd, kRoundMagic) - zpf,
-                               kRoundMagic + 127.0f);
-        sum += (int)(__builtin_bit_cast(unsigned, s[i]) - __builtin_bit_cast(unsigned, kRoundMagic));
+        const int q = p.d > 0.0 ? rne254(h2f(half_at(v, i)), p.d, p.r) - p.zp : 0;
+        sum += q;
+        s[i] = __builtin_bit_cast(float, q);   // pack_low_bytes takes the low byte of each word
     }
     return pack_low_bytes(s);
 }
@@ -1133,7 +1179,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
         s_n = j;
     }
     float amax = 0.0f, r127 = 0.0f, zpf = 0.0f;
-    ZpParams p{0.0f, 0};
+    ZpParams p{0.0, 0.0, 0.0f, 0};
     if constexpr (kMode == kModeZp) {
         float mn = 0.0f, mx = 0.0f;
 #pragma unroll
@@ -1142,7 +1188,6 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
             mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, s_wmax[w]));
         }
         p = zp_params(mn, mx);
-        zpf = (float)p.zp;
     } else {
         unsigned amax_bits = 0;
 #pragma unroll
@@ -1180,7 +1225,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_quant_rows(
         }
         uint2 q;
         if constexpr (kMode == kModeZp)
-            q = quant8_zp(x, p.nd, zpf, sum);
+            q = quant8_zp(x, p, sum);
         else if constexpr (mode_f8(kMode) != kF8None)
             q = quant8_f8<mode_f8(kMode)>(x, zpf);
         else
@@ -1229,11 +1274,10 @@ __global__ __launch_bounds__(kBlock) void k_quantize_weight_zp(const uint16_t *_
         chunk_minmax(row[c], mn, mx);
     wave_minmax(mn, mx);
     const ZpParams p = zp_params(mn, mx);
-    const float zpf = (float)p.zp;
     uint2 *dst = reinterpret_cast<uint2 *>(CB + n * K);
     int sum = 0;
     for (int64_t c = lane; c < nchunk; c += kWave)
-        dst[c] = quant8_zp(row[c], p.nd, zpf, sum);
+        dst[c] = quant8_zp(row[c], p, sum);
     sum = wave_sum(sum);
     if (lane == 0) {
         ND[n] = p.nd;
@@ -1310,7 +1354,6 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_zp(
         mx = __builtin_fmaxf(mx, s_mx[w]);
     }
     const ZpParams p = zp_params(mn, mx);
-    const float zpf = (float)p.zp;
     int sum = 0;
     auto quant = [&](uint4 w, unsigned f, int c) {
         if (f) {
@@ -1318,7 +1361,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_zp(
                 scatter_outliers(w, f, chunk_pos(s_fl, s_aux, c), xrow);
             w = drop_flagged(w, f);
         }
-        *xq_chunk(Xq, t, K, c, packed) = quant8_zp(w, p.nd, zpf, sum);
+        *xq_chunk(Xq, t, K, c, packed) = quant8_zp(w, p, sum);
     };
     if constexpr (NC > 0) {
 #pragma unroll

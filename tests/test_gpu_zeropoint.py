@@ -76,6 +76,51 @@ def test_quantize_act_zp_exact(T, K, thr):
     assert_equal_exact(rz[:, 1], oracle_rowsum(Xqr), "row code sums")
 
 
+def exact_rational_rows(R, K, seed):
+    """Rows that separate the exact-rational codes from shortcuts: ranges whose
+    254/d rounded to fp64 sits on an fp32 midpoint (the stored nd must still
+    be the nearest fp32), exact ties (d = 127: nd = 2, even and odd zero
+    points), and rows of wide dynamic range where rounding nd to fp32 before
+    the products moves codes."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for hi, lo_bits in ((7112.0, 889), (14224.0, 1778)):
+        lo = float(np.array([lo_bits], np.uint16).view(np.float16)[0])
+        r = rng.uniform(0, hi, K)
+        r[0], r[1] = hi, -lo
+        rows.append(r)
+    for lo, hi in ((-63.5, 63.5), (-63.0, 64.0)):
+        r = rng.choice([0.25, 0.75, 1.25, -0.75, -1.25, 3.25], K)
+        r[0], r[1] = lo, hi
+        rows.append(r)
+    while len(rows) < R:
+        r = rng.standard_normal(K) * rng.uniform(0.01, 100)
+        rows.append(np.abs(r) if len(rows) % 3 == 0 else r)
+    return np.stack(rows[:R]).astype(np.float16)
+
+
+# every row of each case goes through the kernel that the shape selects:
+# the one-launch few-rows kernel (T <= 16), the block-per-row kernel, and the
+# weight quantizer
+@pytest.mark.parametrize("T", [16, 64])
+def test_zp_codes_are_exact_rational_roundings(T):
+    K = 256
+    say("zp exact-rational rows T=%d K=%d" % (T, K))
+    X = exact_rational_rows(T, K, seed=T)
+    Xq, nd, row_zp, O, n = L.llmint8_quantize_act_zp(h2d(X), np.inf)
+    Xqr, ndr, zpr = oracle.quantize_rows_zp(X, np.zeros(0, np.int32))
+    assert_equal_exact(d2h(Xq), Xqr, "Xq")
+    assert_equal_exact(d2h(nd), ndr, "nd")
+    assert_equal_exact(d2h(row_zp)[:, 0], zpr, "zp")
+    W_t = exact_rational_rows(64, K, seed=T + 1)          # N must be a multiple of 64
+    CB, ND, ZP, RS = L.llmint8_quantize_weight_zp(h2d(W_t))
+    CBr, NDr, ZPr = oracle.quantize_weight_zp(W_t)
+    assert_equal_exact(d2h(CB), CBr, "CB")
+    assert_equal_exact(d2h(ND), NDr, "ND")
+    assert_equal_exact(d2h(ZP), ZPr, "ZP")
+    assert_equal_exact(d2h(RS), oracle_rowsum(CBr), "RS")
+
+
 SHAPES = [
     # (T, K, N)
     (1, 64, 64),

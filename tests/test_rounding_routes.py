@@ -88,60 +88,106 @@ def test_reciprocal_route_declines_exact_ties():
 
 
 # ---------------------------------------------------------------------------
-# Zero-point variant: the kernels compute the code of x from one fused
-# multiply-add, fma(x, nd, 1.5*2^23) (the exact product rounded to an integer,
-# ties to even, since 1.5*2^23 is even), minus zp (exact), clamped by an fp32
-# min at 1.5*2^23 + 127, and take it as bits - bits(1.5*2^23); the zero point
-# as fma(min', nd, 1.5*2^23) - 1.5*2^23 + 127.  (Folding zp into the addend
-# would be wrong: with an odd addend the ties go to odd.)  A fused
-# multiply-add rounds the exact x*nd + c once; that rounding is done here
-# with exact rationals.
+# Zero-point variant: the kernels round the exact rational 254 x / d
+# (d = max' - min', exact in fp64) as floor(y) + (frac(y) > 1/2) with
+# y = x * fp64(254/d), and decide a fraction within 2^-40 of 1/2 by the sign
+# of 508 x - (2k + 1) d (one exact fused multiply-add on the GPU, exact
+# integers here).  The stored nd is fp32(fp64(254/d)) unless fp64(254/d) lies
+# within 2^-52 of the midpoint between two fp32 values, where the sign of
+# mid * d - 254 picks the side.  numpy's float64 and float32 arithmetic is
+# IEEE round-to-nearest-even, as the GPU's is.
 # ---------------------------------------------------------------------------
 from fractions import Fraction  # noqa: E402
 
-MAGIC = 12582912.0
+NEAR_HALF = 2.0 ** -40
 
 
-def fp32_round(v):
-    """Nearest fp32 value to the rational v (ties to even); v within the
-    normal range."""
-    if v == 0:
-        return 0.0
-    sign = -1 if v < 0 else 1
-    a = abs(v)
-    e = a.numerator.bit_length() - a.denominator.bit_length()
-    if Fraction(2) ** e > a:
-        e -= 1
-    ulp = Fraction(2) ** (e - 23)          # 24 significant bits
-    q = a / ulp
-    r = round(q)                           # ties to even
-    return sign * float(r * ulp)
+def rne254_route(x, d, r, hits):
+    xd = np.float64(x)
+    y = xd * r
+    k = np.floor(y)
+    f = y - k
+    q = int(k) + (1 if f > 0.5 else 0)
+    if abs(f - 0.5) < NEAR_HALF:
+        hits.append(1)
+        e = Fraction(508) * Fraction(float(xd)) - (2 * int(k) + 1) * Fraction(float(d))
+        q = int(k) + (1 if e > 0 else 0 if e < 0 else (int(k) & 1))
+    return q
 
 
-def fma32(x, y, c):
-    return fp32_round(Fraction(float(x)) * Fraction(float(y)) + Fraction(float(c)))
+def nearest_nd_route(d, r):
+    f = np.float32(r)
+    fd = np.float64(f)
+    if fd == r:
+        return f
+    fb = int(f.view(np.uint32))
+    g = np.array([fb + 1 if r > fd else fb - 1], np.uint32).view(np.float32)[0]
+    mid = 0.5 * (fd + np.float64(g))
+    if abs(r - mid) > 2.0 ** -52 * r:
+        return f
+    lo, hi = min(f, g), max(f, g)
+    e = Fraction(float(mid)) * Fraction(float(d)) - 254
+    if e > 0:
+        return lo
+    if e < 0:
+        return hi
+    return hi if int(lo.view(np.uint32)) & 1 else lo
+
+
+def zp_route(row, hits):
+    xs = row.astype(np.float32)
+    mn, mx = min(xs.min(), np.float32(0)), max(xs.max(), np.float32(0))
+    d = np.float64(mx) - np.float64(mn)
+    if d == 0:
+        return np.float32(0), 0, [0] * len(xs)
+    r = np.float64(254.0) / d
+    zp = rne254_route(mn, d, r, hits) + 127
+    return nearest_nd_route(d, r), zp, [rne254_route(x, d, r, hits) - zp for x in xs]
 
 
 @pytest.mark.parametrize("seed", [21, 22, 23])
-def test_zero_point_fused_route_matches_the_oracle(seed):
+def test_zero_point_route_matches_the_oracle(seed):
     rng = np.random.default_rng(seed)
     kinds = [rng.standard_normal(64), np.abs(rng.standard_normal(64)) + 0.25,
              -rng.exponential(3.0, 64), rng.uniform(-1e-3, 5e-3, 64),
-             rng.uniform(-60000, 900, 64), np.r_[[-63.5, 63.5], rng.choice([0.25, 0.75, 1.25, -0.75], 62)],
-             # nd = 2 with an odd zero point (1): the ties 0.5, 1.5, 2.5 must
-             # still go to even before the zero point is subtracted
+             rng.uniform(-60000, 900, 64), rng.uniform(-2.0 ** -20, 3.0, 64),
+             # exact ties: d = 127 gives nd = 2, so 0.25, 0.75, 1.25 scale to
+             # 0.5, 1.5, 2.5; with the zero point odd (min' = -63) as well
+             np.r_[[-63.5, 63.5], rng.choice([0.25, 0.75, 1.25, -0.75], 62)],
              np.r_[[-63.0, 64.0], rng.choice([0.25, 0.75, 1.25, -0.75, -1.25, 3.25], 62)]]
+    kinds += [rng.standard_normal(64) * rng.uniform(0.01, 100) for _ in range(24)]
     X = np.stack(kinds).astype(np.float16)
     q_or, nd_or, zp_or = oracle.quantize_rows_zp(X, np.zeros(0, np.int32))
+    hits = []
     for t in range(X.shape[0]):
-        xs = X[t].astype(np.float32)
-        mn = np.float32(min(xs.min(), 0.0))
-        mx = np.float32(max(xs.max(), 0.0))
-        d = np.float32(mx - mn)
-        nd = np.float32(254.0) / d
-        zp = int(fma32(mn, nd, MAGIC) - MAGIC) + 127
-        assert nd == nd_or[t] and zp == zp_or[t]
-        for k in range(X.shape[1]):
-            s = min(fma32(xs[k], nd, MAGIC) - zp, MAGIC + 127.0)
-            bits = int(np.float32(s).view(np.uint32)) - int(np.float32(MAGIC).view(np.uint32))
-            assert bits == q_or[t, k], (t, k)
+        nd, zp, codes = zp_route(X[t], hits)
+        assert nd == nd_or[t] and zp == zp_or[t], t
+        assert codes == q_or[t].astype(int).tolist(), t
+    assert len(hits) >= 60          # the exact tie branch ran (the tie rows)
+
+
+def test_nearest_nd_route_at_fp32_midpoints():
+    # fp64 values d for which fp64(254/d) lands on, or next to, the midpoint
+    # between two fp32 values: there fp32(fp64(254/d)) can be a double
+    # rounding, and the route must still give the fp32 value nearest to the
+    # exact quotient
+    rng = np.random.default_rng(31)
+    checked = 0
+    for _ in range(400):
+        f = np.float32(rng.uniform(0.002, 2.0 ** 31))
+        g = np.nextafter(f, np.float32(np.inf))
+        mid = 0.5 * (np.float64(f) + np.float64(g))
+        d0 = np.float64(254.0) / mid
+        for step in range(-3, 4):
+            d = d0
+            for _ in range(abs(step)):
+                d = np.nextafter(d, np.inf if step > 0 else 0.0)
+            r = np.float64(254.0) / d
+            exact = Fraction(254) / Fraction(float(d))
+            cands = [np.float32(r), np.nextafter(np.float32(r), np.float32(np.inf)),
+                     np.nextafter(np.float32(r), np.float32(0))]
+            want = min(cands, key=lambda v: (abs(Fraction(float(v)) - exact),
+                                             int(v.view(np.uint32)) & 1))
+            assert nearest_nd_route(d, r) == want
+            checked += abs(r - mid) <= 2.0 ** -52 * r
+    assert checked >= 100           # the midpoint branch ran
