@@ -76,7 +76,11 @@ LLMINT8_API const char *llmint8_status_string(int status);
  * the int8 activations (max(T,16) * K bytes) it holds at most
  * (2*T + N)*min(K,1024) bytes of gathered outlier operands for T > 16
  * (more outlier columns than fit are read in place), and 2*T*K for T <= 16
- * (no weight operand).  Pure host function; returns 0 for invalid sizes. */
+ * (no weight operand); for T >= 512 and K <= 65536 also
+ * N*min(K/4 rounded down to 128, 4096) bytes for the weight codes of the
+ * non-outlier columns, which the int8 product runs over alone when at least
+ * three quarters of the columns are outliers.  Pure host function; returns 0
+ * for invalid sizes. */
 LLMINT8_API size_t llmint8_workspace_bytes(int64_t T, int64_t K, int64_t N);
 
 /* Bytes of workspace llmint8_quantize_act needs for K columns. */
@@ -150,9 +154,11 @@ LLMINT8_API llmint8_status_t llmint8_matmul(const uint16_t *X, int64_t T, int64_
                                 hipStream_t stream);
 
 /* Bytes of the static device scratch of llmint8_matmul_noalloc (64 MiB):
- * a call fits when llmint8_workspace_bytes(T, K, N) is at most this, e.g.
- * every T <= 16 call, T = 4096 x K = 4096 x N = 16384 (41 MB), or
- * T = 2048 x K = 16384 x N = 4096 (40 MB). */
+ * a call fits when llmint8_workspace_bytes(T, K, N), less the optional
+ * segment for the non-outlier weight codes (N*min(K/4 rounded down to 128,
+ * 4096) bytes for T >= 512, K <= 65536), is at most this, e.g. every
+ * T <= 16 call, T = 4096 x K = 4096 x N = 16384 (42 MB, 59 MB with the
+ * optional segment), or T = 2048 x K = 16384 x N = 4096 (40 MB). */
 #define LLMINT8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /*
@@ -170,10 +176,14 @@ LLMINT8_API llmint8_status_t llmint8_matmul(const uint16_t *X, int64_t T, int64_
  * may overlap on one device (different streams, or host threads without an
  * ordering) race and must be serialized by the caller.
  *
+ * When the array holds the workspace but not its optional segment for the
+ * non-outlier weight codes, the call runs without it: the int8 product then
+ * runs over all of K, with the same result.
+ *
  * Errors: as llmint8_matmul (argument and shape checks in the same order),
- * then LLMINT8_ERR_SCRATCH when llmint8_workspace_bytes(T, K, N) exceeds
- * LLMINT8_NOALLOC_SCRATCH_BYTES (nothing enqueued), LLMINT8_ERR_HIP when
- * the array's address cannot be resolved or a launch fails.
+ * then LLMINT8_ERR_SCRATCH when the workspace less that optional segment
+ * exceeds LLMINT8_NOALLOC_SCRATCH_BYTES (nothing enqueued), LLMINT8_ERR_HIP
+ * when the array's address cannot be resolved or a launch fails.
  */
 LLMINT8_API llmint8_status_t llmint8_matmul_noalloc(const uint16_t *X, int64_t T, int64_t K,
                                                     int64_t N, const int8_t *CB, const float *SCB,

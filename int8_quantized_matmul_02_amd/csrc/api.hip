@@ -61,6 +61,11 @@ MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N, bool de
     L.xq = off;          off += align256((t > 16 ? t : 16) * k);   // decode: 16-row fragment order
     L.x_out = off;       off += align256(2 * t * ldx);
     L.w_out = off;       off += decode ? 0 : align256(n * ldx);   // >= 64: kOutFew's fp16 [N,32]
+    // the kept-column mode's weight operand [N, kc], last so that a call can
+    // run without it (see llmint8_matmul_noalloc)
+    L.kept = off;
+    if (!decode && T >= kKeptMinT && K <= kKeptMaxK)
+        off += align256(n * (size_t)kept_cap(K));
     L.total = off;
     return L;
 }
@@ -80,6 +85,7 @@ struct WsPtrs {
     int8_t *xq;
     uint16_t *x_out;
     void *w_out;
+    int8_t *kept;   // null: no kept-column segment
 };
 WsPtrs ws_ptrs(void *ws, const MatmulWorkspace &L, bool decode)
 {
@@ -94,6 +100,7 @@ WsPtrs ws_ptrs(void *ws, const MatmulWorkspace &L, bool decode)
     p.xq = reinterpret_cast<int8_t *>(base + L.xq);
     p.x_out = reinterpret_cast<uint16_t *>(base + L.x_out);
     p.w_out = decode ? nullptr : base + L.w_out;
+    p.kept = L.total > L.kept ? reinterpret_cast<int8_t *>(base + L.kept) : nullptr;
     return p;
 }
 
@@ -258,7 +265,8 @@ llmint8_status_t matmul_check(const uint16_t *X, int64_t T, int64_t K, int64_t N
 llmint8_status_t matmul_impl(const uint16_t *X, int64_t T, int64_t K, int64_t N, const int8_t *CB,
                              const float *SCB, const uint16_t *bias, float threshold,
                              int activation, uint16_t *out, void *ws, size_t ws_bytes, int path,
-                             hipEvent_t main_start, hipEvent_t main_stop, hipStream_t stream)
+                             hipEvent_t main_start, hipEvent_t main_stop, hipStream_t stream,
+                             bool with_kept = true)
 {
     if (!ws || !aligned16(ws))
         return LLMINT8_ERR_INVALID_ARG;
@@ -267,14 +275,18 @@ llmint8_status_t matmul_impl(const uint16_t *X, int64_t T, int64_t K, int64_t N,
     if (st != LLMINT8_OK)
         return st;
     const bool decode = path == 2 || (path == 0 && T <= kDecodeMaxT);
-    const MatmulWorkspace L = matmul_workspace_layout(T, K, N, decode);
+    MatmulWorkspace L = matmul_workspace_layout(T, K, N, decode);
+    if (!with_kept)
+        L.total = L.kept;   // no kept-column segment: the int8 part runs over all K
     if (ws_bytes < L.total)
         return LLMINT8_ERR_WORKSPACE;
     const WsPtrs p = ws_ptrs(ws, L, decode);
 
-    // the GEMM path also builds its outlier weight operand; the decode path
-    // takes more than a few activation rows in fragment order
-    const GatherArgs g{CB, SCB, N, p.w_out};
+    // the GEMM path also builds its outlier weight operand (and, with many
+    // outlier columns, the kept-column operand); the decode path takes more
+    // than a few activation rows in fragment order
+    GatherArgs g{CB, SCB, N, p.w_out};
+    g.cb_kept = p.kept;
     const bool packed = decode && T >= kDecodePackedMinT;
     const hipError_t eq =
         decode && quantize_act_fits_rows(T, K)
@@ -287,6 +299,7 @@ llmint8_status_t matmul_impl(const uint16_t *X, int64_t T, int64_t K, int64_t N,
     EpilogueArgs ep{p.a, SCB, p.x_out, p.w_out, p.O, p.info, bias, out, nullptr,
                     activation == LLMINT8_ACT_RELU ? 1 : 0};
     dense_args(ep, X, p);
+    ep.cb_kept = p.kept;
     const hipError_t e =
         decode ? launch_decode(p.xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
                : launch_gemm(p.xq, CB, T, K, N, ep, stream, main_start, main_stop);
@@ -330,13 +343,16 @@ llmint8_status_t llmint8_matmul_noalloc(const uint16_t *X, int64_t T, int64_t K,
         matmul_check(X, T, K, N, CB, SCB, bias, threshold, LLMINT8_ACT_NONE, out, 0);
     if (st != LLMINT8_OK)
         return st;
-    if (llmint8_workspace_bytes(T, K, N) > kNoAllocBytes)
+    // the kept-column segment is optional: without room for it the int8
+    // part runs over all of K
+    const MatmulWorkspace L = matmul_workspace_layout(T, K, N, T <= kDecodeMaxT);
+    if (L.kept > kNoAllocBytes)
         return LLMINT8_ERR_SCRATCH;
     void *ws = nullptr;
     if (device_scratch(&ws) != hipSuccess)
         return LLMINT8_ERR_HIP;
     return matmul_impl(X, T, K, N, CB, SCB, bias, threshold, LLMINT8_ACT_NONE, out, ws,
-                       kNoAllocBytes, 0, nullptr, nullptr, stream);
+                       kNoAllocBytes, 0, nullptr, nullptr, stream, L.total <= kNoAllocBytes);
 }
 
 llmint8_status_t llmint8_quantize_weight_zp(const uint16_t *W_t, int64_t K, int64_t N, int8_t *CB,

@@ -35,8 +35,39 @@ constexpr int kOutlierPad = 32;   // outlier rows of up to 32 columns are padded
 enum { kOutFew = 0, kOutCompact = 1, kOutDense = 2 };
 constexpr int64_t kCompactMaxLd = 1024;
 // The outlier-set summary in the workspace: int32 info[kInfoWords] =
-// {n, ng, mode}.
+// {n, ng, mode, kc} (kc: see kept_ld).
 constexpr int kInfoWords = 4;
+
+// Kept-column mode of the GEMM path's int8 part (absmax variant): when most
+// columns are outliers, the int8 product runs over the kept (non-outlier)
+// columns alone, compacted in column order.  The row quantization writes
+// each row's kept codes to the start of its Xq row (row stride K),
+// zero-padded to kc = the kept count rounded up to 128 bytes, and its gather
+// blocks write the kept codes of every weight row to cb_kept [N, kc]; every
+// product of an outlier column is 0 in the int8 sum, so the sum is unchanged.
+// Chosen on the device when kc <= kept_cap(K) (a quarter of K, at most
+// kKeptMaxLd: the int8 work falls at least fourfold, and the workspace
+// segment stays at most N * min(K/4, 4096) bytes), for launches of at least
+// kKeptMinT rows (with fewer rows the int8 work saved does not repay reading
+// CB once more) and K <= kKeptMaxK (the row quantization's LDS, which grows
+// with K, stays small).
+constexpr int64_t kKeptMaxLd = 4096;
+constexpr int64_t kKeptMinT = 512;
+constexpr int64_t kKeptMaxK = 65536;
+__host__ __device__ __forceinline__ int64_t kept_cap(int64_t K)
+{
+    const int64_t h = K / 4 / 128 * 128;
+    return h < kKeptMaxLd ? h : kKeptMaxLd;
+}
+// kc for n outlier columns out of K; 0: the int8 part runs over all of K
+// (few outliers), or not at all (n = K).
+__host__ __device__ __forceinline__ int64_t kept_ld(int64_t K, int n)
+{
+    if (n <= kOutlierPad || n >= K)
+        return 0;
+    const int64_t kc = (K - n + 127) / 128 * 128;
+    return kc <= kept_cap(K) ? kc : 0;
+}
 
 // Row stride, in halves, of the gathered outlier operands x_out [T, ld] and
 // w_out [N, ld]; the rows are zero-padded up to it.  Up to 32 outliers: 32
@@ -186,7 +217,7 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
 // decode: the weight-streaming path's layout (no gathered weight operand,
 // x_out for any outlier count).
 struct MatmulWorkspace {
-    size_t mask, groups, outlier_idx, info, row_absmax, row_zp, xq, x_out, w_out, total;
+    size_t mask, groups, outlier_idx, info, row_absmax, row_zp, xq, x_out, w_out, kept, total;
 };
 MatmulWorkspace matmul_workspace_layout(int64_t T, int64_t K, int64_t N, bool decode);
 size_t act_workspace_bytes(int64_t K);
@@ -207,6 +238,7 @@ struct GatherArgs {
     void *w_out;
     const int32_t *zp = nullptr;   // zero-point variant: zp of each column (else null)
     int f8 = kF8None;              // FP8 variant: the format of CB's codes
+    int8_t *cb_kept = nullptr;     // kept-column mode's weight operand [N, kc] (null: off)
 };
 
 // Where the row quantization puts the outlier-set summary: info (n, ng,
@@ -308,6 +340,8 @@ struct EpilogueArgs {
     const uint16_t *X = nullptr;
     const uint8_t *mask = nullptr;
     const int32_t *groups = nullptr;
+    // kept-column mode (info[3] = kc > 0): the weight rows' kept codes [N, kc]
+    const int8_t *cb_kept = nullptr;
 };
 
 // Zero-point variant (the asymmetric quantizer of the LLM.int8() summary,

@@ -359,6 +359,7 @@ struct OutlierSet {
     int n;      // |O|
     int ng;     // non-empty 64-column groups (only computed when n > kOutlierPad)
     int mode;   // kOutFew / kOutCompact / kOutDense
+    int kc;     // kept-column mode's int8 width (0: off; see kept_ld)
 };
 
 // The GEMM path's way of forming the outlier product (see internal.h):
@@ -413,6 +414,7 @@ __device__ __forceinline__ OutlierSet derive_outliers(const DetectFlags &df, int
         o.ng = block_sum(g, s_red + kWavesPerBlock);
     }
     o.mode = outlier_mode(o.n, o.ng);
+    o.kc = 0;   // the row kernels that support the kept-column mode set it
     return o;
 }
 
@@ -470,6 +472,7 @@ __device__ __forceinline__ void write_outlier_info(const uint8_t *s_fl, int nchu
         if (io.groups) {
             io.info[1] = os.ng;
             io.info[2] = os.mode;
+            io.info[3] = os.kc;
         }
     }
     if (io.mask && os.mode == kOutDense) {
@@ -498,16 +501,21 @@ __device__ __forceinline__ void write_outlier_info(const uint8_t *s_fl, int nchu
 // Dynamic LDS of the row-quantization kernels: the chunk flags, then either
 // the 64-column group prefix counts (a row's gathered outlier positions) or a
 // gather block's outlier list (at most kCompactMaxLd entries): at most
-// 16.7 + 8.3 KB at the largest K.
+// 16.7 + 8.3 KB at the largest K.  Launches that may take the kept-column
+// mode add a region for one compacted row of kept_cap(K) bytes (a row block
+// builds its own row there, then its weight rows one after another).
 __host__ __device__ __forceinline__ int64_t flags_lds_bytes(int64_t nchunk)
 {
     return (nchunk + 15) / 16 * 16;
 }
-__host__ __forceinline__ size_t rowquant_lds_bytes(int64_t K)
+__host__ __device__ __forceinline__ int64_t aux_lds_bytes(int64_t nchunk)
+{
+    return 4 * (nchunk / 8 > kCompactMaxLd ? nchunk / 8 : kCompactMaxLd);
+}
+__host__ __forceinline__ size_t rowquant_lds_bytes(int64_t K, bool kept = false)
 {
     const int64_t nchunk = K / 8;
-    const int64_t aux = nchunk / 8 > kCompactMaxLd ? nchunk / 8 : kCompactMaxLd;
-    return (size_t)(flags_lds_bytes(nchunk) + 4 * aux);
+    return (size_t)(flags_lds_bytes(nchunk) + aux_lds_bytes(nchunk) + (kept ? kept_cap(K) : 0));
 }
 
 // What a row-quantization launch is for: the public activation quantizer (no
@@ -560,15 +568,25 @@ __device__ __forceinline__ void scatter_outliers(uint4 v, unsigned fl, int pre,
 // to the compact row xrow (null: not gathered) from position pre on; the
 // others are quantized (r = 127/amax, or 0 when amax = 0).
 template <int kF8 = kF8None>
-__device__ __forceinline__ void quant_chunk(uint4 v, unsigned fl, float amax, float r, int pre,
-                                           uint16_t *__restrict__ xrow, uint2 *dst, float sc = 0.0f)
+__device__ __forceinline__ uint2 quant_chunk(uint4 v, unsigned fl, float amax, float r, int pre,
+                                            uint16_t *__restrict__ xrow, float sc = 0.0f)
 {
     if (fl) {
         if (xrow)
             scatter_outliers(v, fl, pre, xrow);
         v = drop_flagged(v, fl);
     }
-    *dst = quant8_mode<kF8>(v, amax, r, sc);
+    return quant8_mode<kF8>(v, amax, r, sc);
+}
+
+// Kept-column mode: the codes of a chunk's kept columns (flags clear), in
+// column order, into the compacted row s_row from position kpos on.
+__device__ __forceinline__ void put_kept(uint2 q, unsigned fl, int kpos, uint8_t *s_row)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (!((fl >> i) & 1u))
+            s_row[kpos++] = (uint8_t)(((i < 4 ? q.x : q.y) >> (8 * (i & 3))) & 0xffu);
 }
 
 __device__ __forceinline__ unsigned chunk_absmax_masked(uint4 v, unsigned fl)
@@ -681,6 +699,77 @@ __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
     }
 }
 
+// Kept-column mode's weight operand, one row per call of a 256-thread
+// block: dst[j] = cbr[k_j] for the m kept columns k_0 < k_1 < ... of the row
+// cbr, zero up to kc.  The block reads the row in rounds of 16 KB (each
+// wavefront 4 KB: four coalesced 1 KB pieces, 16 bytes per lane, all in
+// flight), places each lane's kept bytes at its prefix count (lanes, then
+// pieces, then wavefronts, i.e. column order) in the compacted row s_row in
+// LDS, and stores s_row in 16-byte pieces.  s_red: kWavesPerBlock ints.  (A
+// gather of single bytes through a kept-column list was bound by load
+// latency: 180 us at N = 4096.)
+__device__ __forceinline__ void kept_weight_row(const int8_t *__restrict__ cbr, int64_t K, int kc,
+                                                int m, const uint8_t *s_fl, uint8_t *s_row,
+                                                int *s_red, int8_t *__restrict__ dst)
+{
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    constexpr int kPieces = 4;
+    constexpr int64_t kRound = (int64_t)kBlock * 16 * kPieces;
+    int base = 0;
+    for (int64_t c0 = 0; c0 < K; c0 += kRound) {
+        uint4 v[kPieces];
+        unsigned keep[kPieces];
+#pragma unroll
+        for (int q = 0; q < kPieces; ++q) {
+            // K % 64 == 0: a lane's 16 columns lie wholly inside or outside
+            const int64_t col = c0 + (int64_t)(wave * kPieces + q) * 16 * kWave + 16 * lane;
+            v[q] = col < K ? *reinterpret_cast<const uint4 *>(cbr + col) : make_uint4(0u, 0u, 0u, 0u);
+            keep[q] = col < K ? ~((unsigned)s_fl[col / 8] | ((unsigned)s_fl[col / 8 + 1] << 8)) & 0xffffu
+                              : 0u;
+        }
+        int pre[kPieces], wtot = 0;
+#pragma unroll
+        for (int q = 0; q < kPieces; ++q) {
+            const int cnt = __builtin_popcount(keep[q]);
+            int inc = cnt;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int o = __shfl_up(inc, off, kWave);
+                if (lane >= off)
+                    inc += o;
+            }
+            pre[q] = wtot + inc - cnt;
+            wtot += __shfl(inc, kWave - 1, kWave);
+        }
+        if (lane == 0)
+            s_red[wave] = wtot;
+        __syncthreads();
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+            before += w < wave ? s_red[w] : 0;
+            tot += s_red[w];
+        }
+        __syncthreads();   // s_red is written again in the next round
+#pragma unroll
+        for (int q = 0; q < kPieces; ++q) {
+            int p = base + before + pre[q];
+            const unsigned w4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if ((keep[q] >> i) & 1u)
+                    s_row[p++] = (uint8_t)(w4[i / 4] >> (8 * (i % 4)));
+        }
+        base += tot;
+    }
+    for (int j = m + tid; j < kc; j += kBlock)
+        s_row[j] = 0;
+    __syncthreads();
+    for (int j = tid; j < kc / 16; j += kBlock)
+        reinterpret_cast<uint4 *>(dst)[j] = reinterpret_cast<const uint4 *>(s_row)[j];
+    __syncthreads();   // s_row is written again by the next row
+}
+
 // The gather blocks' part of a row-quantization launch: the first outlier
 // columns into LDS, then the weight operand.  s_O: kCompactMaxLd ints.
 template <int kMode>
@@ -706,9 +795,8 @@ __device__ __forceinline__ void gather_block(int64_t gb, int64_t nb, int64_t K, 
 __device__ __forceinline__ bool row_prologue(const OutlierSet &os, const uint8_t *s_fl,
                                              int nchunk, int64_t K, int use, bool gather_x,
                                              int *s_pre8, int32_t *O, const OutlierInfoOut &io,
-                                             int *s_red)
+                                             int *s_red, bool first)
 {
-    const bool first = blockIdx.x == 0;
     if (use == kForGemm && os.n == K) {
         if (first)
             write_outlier_info(s_fl, nchunk, os, io, s_red + 3 * kWavesPerBlock);
@@ -739,7 +827,8 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
                                                      uint16_t *__restrict__ x_out,
                                                      const int8_t *__restrict__ CB,
                                                      const float *__restrict__ SCB, int64_t N,
-                                                     void *__restrict__ w_out, bool packed)
+                                                     void *__restrict__ w_out, bool packed,
+                                                     int8_t *__restrict__ cb_kept)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
     __shared__ unsigned s_max[kWavesPerBlock];
@@ -748,17 +837,25 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     const int nchunk = (int)(K / 8);
     uint8_t *s_fl = s_dyn;
     int *s_aux = reinterpret_cast<int *>(s_dyn + flags_lds_bytes(nchunk));
-    const OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
-    if ((int64_t)blockIdx.x >= T) {
-        gather_block<f8_mode(kF8)>(blockIdx.x - T, gridDim.x - T, K, nchunk, os,
-                                                  s_fl, s_aux, s_red + 2 * kWavesPerBlock, CB,
-                                                  SCB, N, w_out);
+    // kept-column mode (cb_kept non-null only for launches with its LDS
+    // region): the row block's compacted row, then its wavefronts' compacted
+    // weight rows
+    uint8_t *s_kept = s_dyn + flags_lds_bytes(nchunk) + aux_lds_bytes(nchunk);
+    OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
+    if (cb_kept)
+        os.kc = (int)kept_ld(K, os.n);
+    // the gather blocks come first
+    const int64_t gb = (int64_t)gridDim.x - T;
+    if ((int64_t)blockIdx.x < gb) {
+        gather_block<f8_mode(kF8)>(blockIdx.x, gb, K, nchunk, os, s_fl, s_aux,
+                                   s_red + 2 * kWavesPerBlock, CB, SCB, N, w_out);
         return;
     }
+    const int64_t t = (int64_t)blockIdx.x - gb;
     const bool gx = gathers_x(x_out, use, os);
-    if (!row_prologue(os, s_fl, nchunk, K, use, gx, s_aux, O, io, s_red))
+    const bool kept = os.kc > 0;
+    if (!row_prologue(os, s_fl, nchunk, K, use, gx || kept, s_aux, O, io, s_red, t == 0))
         return;
-    const int64_t t = blockIdx.x;
     const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
     const int nout = os.n;
     const int64_t ldo = outlier_ld(nout);
@@ -791,25 +888,47 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     const float r = kF8 ? 0.0f : amax > 0.0f ? 127.0f / amax : 0.0f;
     const int e8 = kF8 ? f8_scale_exp<kF8>(amax) : 0;
     const float sc = kF8 ? __builtin_ldexpf(1.0f, e8) : 0.0f;
+    // the chunk's codes to Xq, or in the kept-column mode its kept codes to
+    // the compacted row (column 8c is preceded by 8c - pre kept columns)
+    auto put = [&](uint4 x, unsigned f, int c) {
+        const int pre = ((xrow && f) || kept) ? chunk_pos(s_fl, s_aux, c) : 0;
+        const uint2 q = quant_chunk<kF8>(x, f, amax, r, pre, xrow, sc);
+        if (kept)
+            put_kept(q, f, 8 * c - pre, s_kept);
+        else
+            *xq_chunk(Xq, t, K, c, packed) = q;
+    };
     if constexpr (NC > 0) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             const int c = tid + i * kBlock;
             if (c < nchunk)
-                quant_chunk<kF8>(v[i], fl[i], amax, r,
-                                 (xrow && fl[i]) ? chunk_pos(s_fl, s_aux, c) : 0, xrow,
-                                 xq_chunk(Xq, t, K, c, packed), sc);
+                put(v[i], fl[i], c);
         }
     } else {
-        for (int c = tid; c < nchunk; c += kBlock) {
-            const unsigned f = s_fl[c];
-            quant_chunk<kF8>(xr[c], f, amax, r, (xrow && f) ? chunk_pos(s_fl, s_aux, c) : 0, xrow,
-                             xq_chunk(Xq, t, K, c, packed), sc);
-        }
+        for (int c = tid; c < nchunk; c += kBlock)
+            put(xr[c], s_fl[c], c);
     }
     if (xrow) {
         for (int64_t j = nout + tid; j < ldo; j += kBlock)
             xrow[j] = 0;
+    }
+    if (kept) {
+        // zero padding up to kc, then the compacted row to the start of
+        // Xq's row t
+        for (int j = (int)K - nout + tid; j < os.kc; j += kBlock)
+            s_kept[j] = 0;
+        __syncthreads();
+        uint4 *dst = reinterpret_cast<uint4 *>(Xq + t * K);
+        for (int j = tid; j < os.kc / 16; j += kBlock)
+            dst[j] = reinterpret_cast<const uint4 *>(s_kept)[j];
+        // the kept weight operand: row block t builds weight rows t, t + T,
+        // t + 2T, ... (the row blocks share the N rows evenly, and no extra
+        // blocks sit idle when the mode is not taken)
+        __syncthreads();
+        for (int64_t r = t; r < N; r += T)
+            kept_weight_row(CB + r * K, K, os.kc, (int)K - nout, s_fl, s_kept, s_red,
+                            cb_kept + r * os.kc);
     }
     if (tid == 0)
         a[t] = kF8 ? __builtin_ldexpf(1.0f, -e8) : amax;
@@ -870,7 +989,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restric
     }
     const bool gx = gathers_x(x_out, use, os);
     // positions come from ballots over the row, which a wavefront walks in order
-    if (!row_prologue(os, s_fl, nchunk, K, use, false, nullptr, O, io, s_red))
+    if (!row_prologue(os, s_fl, nchunk, K, use, false, nullptr, O, io, s_red, blockIdx.x == 0))
         return;
     const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     if (t >= T)
@@ -1315,7 +1434,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_zp(
         return;
     }
     const bool gx = gathers_x(x_out, use, os);
-    if (!row_prologue(os, s_fl, nchunk, K, use, gx, s_aux, O, io, s_red))
+    if (!row_prologue(os, s_fl, nchunk, K, use, gx, s_aux, O, io, s_red, blockIdx.x == 0))
         return;
     const int64_t t = blockIdx.x;
     const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
@@ -1575,12 +1694,17 @@ hipError_t launch_act_absmax(const uint16_t *X, int64_t T, int64_t K, float thre
 #undef LLMINT8_ROWQUANT_W
         return hipGetLastError();
     }
-    // fewer rows: a block per row keeps more lanes busy
+    // fewer rows: a block per row keeps more lanes busy; the kept-column mode
+    // of the int8 part is taken here (absmax, enough rows, K in range)
+    const bool kept = g.cb_kept && kF8 == kF8None && use == kForGemm && T >= kKeptMinT &&
+                      K <= kKeptMaxK;
+    int8_t *cb_kept = kept ? g.cb_kept : nullptr;
+    const size_t lds_rows = rowquant_lds_bytes(K, kept);
     const dim3 grid((unsigned)(T + gb));
     const int64_t chunks_per_thread = (nchunk + kBlock - 1) / kBlock;
 #define LLMINT8_ROWQUANT(NCV)                                                                  \
-    hipLaunchKernelGGL((k_rowquant<NCV, kF8>), grid, dim3(kBlock), lds, s, X, T, K, df,          \
-                       use, O, io, Xq, a, x_out, g.CB, g.SCB, g.N, g.w_out, xq_packed)
+    hipLaunchKernelGGL((k_rowquant<NCV, kF8>), grid, dim3(kBlock), lds_rows, s, X, T, K, df,     \
+                       use, O, io, Xq, a, x_out, g.CB, g.SCB, g.N, g.w_out, xq_packed, cb_kept)
     if (chunks_per_thread <= 1)
         LLMINT8_ROWQUANT(1);
     else if (chunks_per_thread <= 2)

@@ -71,10 +71,13 @@ def test_workspace_queries(lib, T, K):
     # outlier summary + row scales + zero-point row parameters + Xq (at least
     # 16 rows: the decode path's fragment order) + gathered fp16 activations +
     # (GEMM path) gathered weight codes; the gathered operands hold at most
-    # min(K, 1024) columns on the GEMM path, so nothing grows with N * K
+    # min(K, 1024) columns on the GEMM path, and the kept-column operand (GEMM
+    # path, T >= 512, K <= 65536) min(K/4 rounded down to 128, 4096) columns,
+    # so nothing grows with N * K
     det = K // 8 + 8 * ((K // 8 + 15) // 16 * 16)
     common = det + K // 16 + 4 * K + 4 * T + 8 * T + max(T, 16) * K
-    gemm_floor = common + 2 * T * min(K, 1024) + min(K, 1024) * N
+    kept = min(K // 4 // 128 * 128, 4096) * N if T >= 512 and K <= 65536 else 0
+    gemm_floor = common + 2 * T * min(K, 1024) + min(K, 1024) * N + kept
     assert gemm_floor <= gemm <= gemm_floor + 16 * 256
     dec = L.llmint8_workspace_bytes_path(T, K, N, L.PATH_DECODE) if T <= 16 else None
     if T <= 16:

@@ -338,13 +338,48 @@ def test_many_outliers_compact_and_dense(case, use_bias, relu):
     assert_fp16_close(d2h(out), ref, case)
 
 
+# Kept-column mode of the int8 part: with T >= 512 rows and the kept
+# (non-outlier) columns rounded up to 128 at most a quarter of K, the int8
+# product runs over the compacted kept columns only.  Cases at the quarter
+# (kc = K/4) and one column past it, one row short of 512, a ragged T, a K
+# whose stages are 64 bytes, and a wider K.
+KEPT_CASES = {
+    # name: (T, K, N, number of outlier columns, drawn at random)
+    "kept_at_cap": (512, 1024, 320, 768),
+    "kept_past_cap": (512, 1024, 256, 767),
+    "kept_one_row_short": (511, 1024, 320, 800),
+    "kept_ragged_T": (600, 2048, 256, 1600),
+    "kept_k64_stages": (512, 1088, 256, 900),
+    "kept_wide": (1024, 4096, 512, 3500),
+}
+
+
+@pytest.mark.parametrize("case", sorted(KEPT_CASES))
+@pytest.mark.parametrize("use_bias,relu", [(False, False), (True, True)])
+def test_kept_column_mode(case, use_bias, relu):
+    T, K, N, n = KEPT_CASES[case]
+    say("kept columns %s T=%d K=%d N=%d n=%d bias=%s relu=%s" % (case, T, K, N, n, use_bias, relu))
+    cols = np.sort(np.random.default_rng(K + n).choice(K, n, replace=False))
+    X, W_t = _planted(T, K, N, cols, seed=n + K)
+    bias = np.random.default_rng(N).standard_normal(N).astype(np.float16) if use_bias else None
+    CBr, SCBr = oracle.quantize_weight(W_t)
+    ref, Or, _ = oracle.matmul(X, CBr, SCBr, 6.0, bias=bias, relu=relu)
+    assert Or.size == n
+    CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
+    out = L.llmint8_matmul_act(h2d(X), CB, SCB, 6.0, L.ACT_RELU if relu else L.ACT_NONE,
+                               bias=h2d(bias) if use_bias else None)
+    assert_fp16_close(d2h(out), ref, case)
+
+
+@pytest.mark.parametrize("T", [300, 512])
 @pytest.mark.parametrize("thr", [0.0, 0.4])
-def test_nearly_every_column_an_outlier(thr):
+def test_nearly_every_column_an_outlier(thr, T):
     """Threshold 0 with an all-zero column (n = K - 1: the int8 part still runs,
     and the group holding that column is masked), and a threshold that leaves a
-    few small-valued columns out of the outlier set."""
-    T, K, N = 300, 1088, 320
-    say("nearly all outliers thr=%s" % thr)
+    few small-valued columns out of the outlier set; with 512 rows the int8
+    part takes the kept-column mode (at most 4 kept columns)."""
+    K, N = 1088, 320
+    say("nearly all outliers T=%d thr=%s" % (T, thr))
     X, W_t, _ = workloads.case(T, K, N, n_dims=0, seed=int(thr * 10) + 7)
     X = X.astype(np.float32)
     X[:, 100] = 0.0

@@ -36,6 +36,8 @@ CASES = {
                               (70, 1024, 256, np.array([5, 77, 300, 301, 640, 1000]), 6.0, False)],
     "gemm_dense_then_all": [(300, 8256, 320, np.arange(1030) * 8 + 2, 6.0, False),
                             (40, 2048, 192, np.array([], dtype=np.int64), 0.0, True)],
+    "gemm_kept_then_kept": [(600, 2048, 256, np.arange(1600) + 300, 6.0, True),
+                            (512, 1024, 320, np.arange(800) + 100, 6.0, False)],
     "decode_then_decode": [(16, 4096, 512, np.array([9, 1000, 4095]), 6.0, True),
                            (3, 1024, 256, np.array([1, 2]), 6.0, False)],
     "fc1_size_then_up_proj_size": [(4096, 4096, 16384, np.array([11, 900, 2048, 3000, 3001, 4000]),
