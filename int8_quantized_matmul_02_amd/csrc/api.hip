@@ -498,6 +498,7 @@ llmint8_status_t matmul_fp8_path(const uint16_t *X, int64_t T, int64_t K, int64_
 
     GatherArgs g{CB, SC8, N, p.w_out};
     g.f8 = fmt;
+    g.cb_kept = p.kept;
     const bool packed = decode && T >= kDecodePackedMinT;
     const hipError_t eq = launch_quantize_act_f8(X, T, K, threshold,
                                                  reinterpret_cast<uint8_t *>(p.xq), p.a, p.O,
@@ -508,6 +509,7 @@ llmint8_status_t matmul_fp8_path(const uint16_t *X, int64_t T, int64_t K, int64_
     EpilogueArgs ep{p.a, SC8, p.x_out, p.w_out, p.O, p.info, bias, out, nullptr, 0};
     ep.f8 = fmt;
     dense_args(ep, X, p);
+    ep.cb_kept = p.kept;
     const hipError_t e =
         decode ? launch_decode(p.xq, CB, T, K, N, ep, packed, stream, main_start, main_stop)
                : launch_gemm(p.xq, CB, T, K, N, ep, stream, main_start, main_stop);

@@ -1357,12 +1357,13 @@ __device__ __forceinline__ void many_tile(char *smem, const int8_t *__restrict__
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0;
     if (nout < K) {
-        // kept-column mode (absmax; info[3] = kc > 0): the int8 product over
-        // the kc compacted kept columns, at the start of each Xq row and in
-        // ep.cb_kept [N, kc]; the outlier columns' products are all 0
+        // kept-column mode (absmax and FP8; info[3] = kc > 0): the 8-bit
+        // product over the kc compacted kept columns, at the start of each Xq
+        // row and in ep.cb_kept [N, kc]; the outlier columns' products are all
+        // 0 (int8 code 0, FP8 code +0)
         int64_t kk = K;
         const int8_t *Bk = B;
-        if constexpr (!kZp && kF8 == kF8None) {
+        if constexpr (!kZp) {
             const int kc = info[3];
             if (kc > 0) {
                 kk = kc;
@@ -1373,7 +1374,7 @@ __device__ __forceinline__ void many_tile(char *smem, const int8_t *__restrict__
         st.init(reinterpret_cast<const char *>(A), K, m0, T, reinterpret_cast<const char *>(Bk),
                 kk, n0, N, wave, lane);
         if constexpr (kF8 != kF8None)
-            mainloop_f8<C, kF8>(smem, st, (int)(K / C::ROWB), acc, wm, wn, wave, lane);
+            mainloop_f8<C, kF8>(smem, st, (int)(kk / C::ROWB), acc, wm, wn, wave, lane);
         else
             run_mainloop<C, MfmaI8>(smem, st, (int)(kk / C::ROWB), acc, wm, wn, wave, lane);
     }

@@ -38,7 +38,8 @@ constexpr int64_t kCompactMaxLd = 1024;
 // {n, ng, mode, kc} (kc: see kept_ld).
 constexpr int kInfoWords = 4;
 
-// Kept-column mode of the GEMM path's int8 part (absmax variant): when most
+// Kept-column mode of the GEMM path's 8-bit part (absmax and FP8 variants;
+// the zero-point variant's unrolled sum runs over all K): when most
 // columns are outliers, the int8 product runs over the kept (non-outlier)
 // columns alone, compacted in column order.  The row quantization writes
 // each row's kept codes to the start of its Xq row (row stride K),

@@ -1695,9 +1695,8 @@ hipError_t launch_act_absmax(const uint16_t *X, int64_t T, int64_t K, float thre
         return hipGetLastError();
     }
     // fewer rows: a block per row keeps more lanes busy; the kept-column mode
-    // of the int8 part is taken here (absmax, enough rows, K in range)
-    const bool kept = g.cb_kept && kF8 == kF8None && use == kForGemm && T >= kKeptMinT &&
-                      K <= kKeptMaxK;
+    // of the 8-bit part is taken here (absmax and FP8, enough rows, K in range)
+    const bool kept = g.cb_kept && use == kForGemm && T >= kKeptMinT && K <= kKeptMaxK;
     int8_t *cb_kept = kept ? g.cb_kept : nullptr;
     const size_t lds_rows = rowquant_lds_bytes(K, kept);
     const dim3 grid((unsigned)(T + gb));

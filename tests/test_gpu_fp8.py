@@ -258,3 +258,56 @@ def test_f8_many_outliers_compact_and_dense(cols, fmt):
     ref, O, _ = oracle.matmul_f8(X, CBr, SCr, 6.0, fmt=fmt)
     assert len(O) == len(cols)
     assert_f8_close(d2h(out), ref, X, CBr, SCr, 6.0, fmt=fmt)
+
+
+# Kept-column mode (T >= 512, three quarters or more of the columns
+# outliers): the FP8 product over the compacted kept columns.  The fp32 sums
+# of the matrix cores group the products differently than over all of K, so
+# the output is held to the same accumulation bound; inputs whose every
+# partial sum is exact must still give the exact product bit for bit.
+@pytest.mark.parametrize("T", [512, 600])
+@FMTS
+def test_f8_kept_column_mode(T, fmt):
+    K, N, n = 2048, 256, 1600
+    say("%s kept columns T=%d K=%d N=%d n=%d" % (fmt, T, K, N, n))
+    cols = np.sort(np.random.default_rng(T).choice(K, n, replace=False))
+    X, W_t, _ = workloads.case(T, K, N, n_dims=0, seed=T + 3)
+    rng = np.random.default_rng(T + 4)
+    X = X.astype(np.float32)
+    for c in cols:
+        rows = rng.random(T) < 0.5
+        rows[0] = True
+        X[rows, c] = rng.uniform(8.0, 60.0, rows.sum()) * np.where(rng.random(rows.sum()) < 0.5, -1, 1)
+    X = X.astype(np.float16)
+    CB8, SC8 = API[fmt]["qw"](h2d(W_t))
+    out = API[fmt]["mm"](h2d(X), CB8, SC8, 6.0)
+    CBr, SCr = oracle.quantize_weight_f8(W_t, fmt)
+    ref, O, _ = oracle.matmul_f8(X, CBr, SCr, 6.0, fmt=fmt)
+    assert len(O) == n
+    assert_f8_close(d2h(out), ref, X, CBr, SCr, 6.0, fmt=fmt)
+
+
+@FMTS
+def test_f8_kept_column_mode_exact_on_representable_inputs(fmt):
+    rng = np.random.default_rng(33)
+    T, K, N, n_out = 512, 512, 128, 400        # 112 kept columns: kc = 128 = K/4
+    if fmt == "e4m3":
+        xs = [-3.0, -1.875, -1.0, -0.5, 0.0, 0.25, 0.9375, 1.0, 2.0, 3.5]
+        ws = [-0.375, -0.25, -0.234375, 0.0, 0.0625, 0.125, 0.1875, 0.25]
+    else:
+        xs = [-3.0, -1.5, -1.0, -0.5, 0.0, 0.25, 0.75, 1.0, 2.0, 3.5]
+        ws = [-0.375, -0.25, -0.125, 0.0, 0.0625, 0.125, 0.1875, 0.25]
+    X = rng.choice(xs, (T, K))
+    X[:, 0] = 3.5
+    out_cols = np.sort(rng.choice(np.arange(1, K), n_out, replace=False))
+    X[::2, out_cols] = 24.0
+    W = rng.choice(ws, (N, K))
+    W[:, 1] = 0.375
+    say("%s kept columns, representable inputs" % fmt)
+    CB8, SC8 = API[fmt]["qw"](h2d(W.astype(np.float16)))
+    out = API[fmt]["mm"](h2d(X.astype(np.float16)), CB8, SC8, 6.0)
+    exact = (X @ W.T).astype(np.float16).view(np.uint16)
+    CBr, SCr = oracle.quantize_weight_f8(W.astype(np.float16), fmt)
+    ref, O, _ = oracle.matmul_f8(X.astype(np.float16), CBr, SCr, 6.0, fmt=fmt)
+    assert len(O) == n_out and np.array_equal(ref, exact)
+    assert_equal_exact(d2h(out).view(np.uint16), exact, "out")

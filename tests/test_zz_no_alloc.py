@@ -64,6 +64,27 @@ def test_noalloc_matches_matmul_on_two_calls(case):
         assert_equal_exact(bits(got), bits(ref), "%s call %d" % (case, i))
 
 
+def test_noalloc_runs_without_the_kept_segment_when_it_does_not_fit():
+    # 4096 x 8192 x 8192: the workspace fits the scratch only without its
+    # kept-column segment, so the no-allocation call runs the int8 part over
+    # all of K while llmint8_matmul (full workspace) takes the kept-column
+    # mode (7000 of 8192 columns are outliers); the integer sums are the
+    # same, so the outputs must agree bit for bit
+    T, K, N = 4096, 8192, 8192
+    cols = np.sort(np.random.default_rng(5).choice(K, 7000, replace=False))
+    say("noalloc without the kept segment T=%d K=%d N=%d n_planted=%d" % (T, K, N, len(cols)))
+    assert L.llmint8_workspace_bytes(T, K, N) > L.NOALLOC_SCRATCH_BYTES
+    X, W_t = _planted(T, K, N, cols, seed=11)
+    Xd = h2d(X)
+    CB, SCB = L.llmint8_quantize_weight(h2d(W_t))
+    out_n = torch.full((T, N), float("nan"), dtype=torch.float16, device=Xd.device)
+    L.llmint8_matmul_noalloc(Xd, CB, SCB, out_n, 6.0)
+    out_r = L.llmint8_matmul(Xd, CB, SCB, 6.0)
+    got, ref = d2h(out_n), d2h(out_r)
+    assert not np.isnan(got.astype(np.float32)).any(), "output not fully written"
+    assert_equal_exact(bits(got), bits(ref), "kept segment left out")
+
+
 def test_noalloc_rejects_a_call_beyond_the_scratch():
     T, K, N = 4096, 16384, 16384
     say("noalloc over the limit T=%d K=%d N=%d" % (T, K, N))
