@@ -18,7 +18,7 @@ from tests.gpu_helpers import dev, h2d, say
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("T,K,N", [(1, 1024, 512), (4, 2048, 256), (16, 1088, 320),
-                                   (300, 512, 512)])
+                                   (300, 512, 512), (512, 512, 256)])
 @pytest.mark.parametrize("thr", [6.0, 0.0])
 @pytest.mark.parametrize("variant", ["absmax", "zeropoint", "fp8", "fp8_e4m3"])
 def test_matmul_graph_replay(T, K, N, thr, variant):
@@ -28,6 +28,11 @@ def test_matmul_graph_replay(T, K, N, thr, variant):
                                seed=11 * T + K + N)
     X2, _, _ = workloads.case(T, K, N, n_dims=min(6, K // 16), lo=8, hi=60, p=0.5,
                               seed=11 * T + K + N + 1)
+    if T >= 512:
+        # one all-zero column: at threshold 0 the other 511 are outliers and
+        # the absmax and FP8 forms take the kept-column mode (one kept column)
+        X[:, 5] = 0
+        X2[:, 5] = 0
     bias = h2d(np.random.default_rng(5).standard_normal(N).astype(np.float16))
     Xd = h2d(X)
     out = torch.empty((T, N), dtype=torch.float16, device=d)
