@@ -838,8 +838,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     uint8_t *s_fl = s_dyn;
     int *s_aux = reinterpret_cast<int *>(s_dyn + flags_lds_bytes(nchunk));
     // kept-column mode (cb_kept non-null only for launches with its LDS
-    // region): the row block's compacted row, then its wavefronts' compacted
-    // weight rows
+    // region): the row block's compacted row, then its compacted weight rows
     uint8_t *s_kept = s_dyn + flags_lds_bytes(nchunk) + aux_lds_bytes(nchunk);
     OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
     if (cb_kept)
