@@ -43,15 +43,15 @@ constexpr int kInfoWords = 4;
 // columns are outliers, the int8 product runs over the kept (non-outlier)
 // columns alone, compacted in column order.  The row quantization writes
 // each row's kept codes to the start of its Xq row (row stride K),
-// zero-padded to kc = the kept count rounded up to 128 bytes, and its gather
-// blocks write the kept codes of every weight row to cb_kept [N, kc]; every
-// product of an outlier column is 0 in the int8 sum, so the sum is unchanged.
+// zero-padded to kc = the kept count rounded up to 128 bytes, and its row
+// blocks write the kept codes of every weight row to cb_kept [N, kc] (both
+// through one list of the kept columns per block); every product of an
+// outlier column is 0 in the int8 sum, so the sum is unchanged.
 // Chosen on the device when kc <= kept_cap(K) (a quarter of K, at most
 // kKeptMaxLd: the int8 work falls at least fourfold, and the workspace
 // segment stays at most N * min(K/4, 4096) bytes), for launches of at least
 // kKeptMinT rows (with fewer rows the int8 work saved does not repay reading
-// CB once more) and K <= kKeptMaxK (the row quantization's LDS, which grows
-// with K, stays small).
+// CB once more) and K <= kKeptMaxK (the list's 16-bit column indices).
 constexpr int64_t kKeptMaxLd = 4096;
 constexpr int64_t kKeptMinT = 512;
 constexpr int64_t kKeptMaxK = 65536;
@@ -258,7 +258,9 @@ struct OutlierInfoOut {
 // row range, `pitch` bytes apart) that k_detect writes and every
 // row-quantization block ORs.  nr > 1 when K is narrow, so the detection
 // launch still has about a workgroup per compute unit; each range holds at
-// least 256 rows.
+// least 256 rows.  (More ranges for wider K, 8 at K = 12288, left the
+// detection as fast and slowed the row quantization, whose every block ORs
+// the nr sets.)
 struct DetectFlags {
     const uint8_t *parts;
     int nr, pitch;

@@ -265,11 +265,13 @@ __global__ __launch_bounds__(kDetectThreads) void k_detect(const uint16_t *__res
     uint4 cm = make_uint4(0u, 0u, 0u, 0u);
     for (int64_t t0 = t_begin + tid / 8; t0 < t_end; t0 += kRowsInFlight * kDetectRowsPerPass) {
         uint4 v[kRowsInFlight];
+        // a row past the range re-reads row t0, which leaves the maximum as
+        // it is; the loads are unconditional, so all of them are in flight
+        // at once (a load under a condition is waited for inside it)
 #pragma unroll
         for (int u = 0; u < kRowsInFlight; ++u) {
             const int64_t t = t0 + (int64_t)u * kDetectRowsPerPass;
-            v[u] = t < t_end ? *reinterpret_cast<const uint4 *>(col + t * K)
-                             : make_uint4(0u, 0u, 0u, 0u);   // |0| is never above
+            v[u] = *reinterpret_cast<const uint4 *>(col + (t < t_end ? t : t0) * K);
         }
 #pragma unroll
         for (int u = 0; u < kRowsInFlight; ++u)
@@ -502,8 +504,7 @@ __device__ __forceinline__ void write_outlier_info(const uint8_t *s_fl, int nchu
 // the 64-column group prefix counts (a row's gathered outlier positions) or a
 // gather block's outlier list (at most kCompactMaxLd entries): at most
 // 16.7 + 8.3 KB at the largest K.  Launches that may take the kept-column
-// mode add a region for one compacted row of kept_cap(K) bytes (a row block
-// builds its own row there, then its weight rows one after another).
+// mode add the list of kept columns: kept_cap(K) 16-bit entries.
 __host__ __device__ __forceinline__ int64_t flags_lds_bytes(int64_t nchunk)
 {
     return (nchunk + 15) / 16 * 16;
@@ -515,7 +516,7 @@ __host__ __device__ __forceinline__ int64_t aux_lds_bytes(int64_t nchunk)
 __host__ __forceinline__ size_t rowquant_lds_bytes(int64_t K, bool kept = false)
 {
     const int64_t nchunk = K / 8;
-    return (size_t)(flags_lds_bytes(nchunk) + aux_lds_bytes(nchunk) + (kept ? kept_cap(K) : 0));
+    return (size_t)(flags_lds_bytes(nchunk) + aux_lds_bytes(nchunk) + (kept ? 2 * kept_cap(K) : 0));
 }
 
 // What a row-quantization launch is for: the public activation quantizer (no
@@ -577,16 +578,6 @@ __device__ __forceinline__ uint2 quant_chunk(uint4 v, unsigned fl, float amax, f
         v = drop_flagged(v, fl);
     }
     return quant8_mode<kF8>(v, amax, r, sc);
-}
-
-// Kept-column mode: the codes of a chunk's kept columns (flags clear), in
-// column order, into the compacted row s_row from position kpos on.
-__device__ __forceinline__ void put_kept(uint2 q, unsigned fl, int kpos, uint8_t *s_row)
-{
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        if (!((fl >> i) & 1u))
-            s_row[kpos++] = (uint8_t)(((i < 4 ? q.x : q.y) >> (8 * (i & 3))) & 0xffu);
 }
 
 __device__ __forceinline__ unsigned chunk_absmax_masked(uint4 v, unsigned fl)
@@ -699,75 +690,63 @@ __device__ __forceinline__ void gather_w_out(int64_t gb, int64_t nb, int64_t K,
     }
 }
 
-// Kept-column mode's weight operand, one row per call of a 256-thread
-// block: dst[j] = cbr[k_j] for the m kept columns k_0 < k_1 < ... of the row
-// cbr, zero up to kc.  The block reads the row in rounds of 16 KB (each
-// wavefront 4 KB: four coalesced 1 KB pieces, 16 bytes per lane, all in
-// flight), places each lane's kept bytes at its prefix count (lanes, then
-// pieces, then wavefronts, i.e. column order) in the compacted row s_row in
-// LDS, and stores s_row in 16-byte pieces.  s_red: kWavesPerBlock ints.  (A
-// gather of single bytes through a kept-column list was bound by load
-// latency: 180 us at N = 4096.)
-__device__ __forceinline__ void kept_weight_row(const int8_t *__restrict__ cbr, int64_t K, int kc,
-                                                int m, const uint8_t *s_fl, uint8_t *s_row,
-                                                int *s_red, int8_t *__restrict__ dst)
+// Kept-column mode: the kept (non-outlier) columns of the row set, in column
+// order, into the LDS list s_list (16-bit column indices; K <= kKeptMaxK):
+// chunk c's kept columns start at position 8c - (outlier columns before c),
+// and a lane walks the clear bits of each of its chunks' flags.  The list
+// serves the block's activation row and its weight rows alike, so each of
+// them is compacted by gathering 8 listed columns per thread (a per-byte
+// placement of every kept code cost ~2200 instructions per wavefront at
+// 4096 x 16384).  The m kept columns are followed by column 0 up to kc, so
+// that the gathers below load unconditionally (a load under a condition is
+// waited for inside it) and zero those entries after the load.  s_pre8: the
+// 64-column group prefix counts.
+__device__ __forceinline__ void kept_list(const uint8_t *s_fl, const int *s_pre8, int nchunk,
+                                          int m, int kc, uint16_t *s_list)
 {
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    constexpr int kPieces = 4;
-    constexpr int64_t kRound = (int64_t)kBlock * 16 * kPieces;
-    int base = 0;
-    for (int64_t c0 = 0; c0 < K; c0 += kRound) {
-        uint4 v[kPieces];
-        unsigned keep[kPieces];
-#pragma unroll
-        for (int q = 0; q < kPieces; ++q) {
-            // K % 64 == 0: a lane's 16 columns lie wholly inside or outside
-            const int64_t col = c0 + (int64_t)(wave * kPieces + q) * 16 * kWave + 16 * lane;
-            v[q] = col < K ? *reinterpret_cast<const uint4 *>(cbr + col) : make_uint4(0u, 0u, 0u, 0u);
-            keep[q] = col < K ? ~((unsigned)s_fl[col / 8] | ((unsigned)s_fl[col / 8 + 1] << 8)) & 0xffffu
-                              : 0u;
+    for (int c = threadIdx.x; c < nchunk; c += kBlock) {
+        unsigned km = ~(unsigned)s_fl[c] & 0xffu;
+        if (km == 0u)
+            continue;
+        int p = 8 * c - chunk_pos(s_fl, s_pre8, c);
+        while (km) {
+            s_list[p++] = (uint16_t)(8 * c + __builtin_ctz(km));
+            km &= km - 1u;
         }
-        int pre[kPieces], wtot = 0;
-#pragma unroll
-        for (int q = 0; q < kPieces; ++q) {
-            const int cnt = __builtin_popcount(keep[q]);
-            int inc = cnt;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const int o = __shfl_up(inc, off, kWave);
-                if (lane >= off)
-                    inc += o;
-            }
-            pre[q] = wtot + inc - cnt;
-            wtot += __shfl(inc, kWave - 1, kWave);
-        }
-        if (lane == 0)
-            s_red[wave] = wtot;
-        __syncthreads();
-        int before = 0, tot = 0;
-#pragma unroll
-        for (int w = 0; w < kWavesPerBlock; ++w) {
-            before += w < wave ? s_red[w] : 0;
-            tot += s_red[w];
-        }
-        __syncthreads();   // s_red is written again in the next round
-#pragma unroll
-        for (int q = 0; q < kPieces; ++q) {
-            int p = base + before + pre[q];
-            const unsigned w4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if ((keep[q] >> i) & 1u)
-                    s_row[p++] = (uint8_t)(w4[i / 4] >> (8 * (i % 4)));
-        }
-        base += tot;
     }
-    for (int j = m + tid; j < kc; j += kBlock)
-        s_row[j] = 0;
-    __syncthreads();
-    for (int j = tid; j < kc / 16; j += kBlock)
-        reinterpret_cast<uint4 *>(dst)[j] = reinterpret_cast<const uint4 *>(s_row)[j];
-    __syncthreads();   // s_row is written again by the next row
+    for (int j = m + (int)threadIdx.x; j < kc; j += kBlock)
+        s_list[j] = 0;
+}
+
+// 8 consecutive entries j0 .. j0+7 of a compacted row: the listed columns of
+// row src (fp16 values or int8 codes), 0 past the m kept columns.
+__device__ __forceinline__ uint4 kept_gather_h(const uint16_t *__restrict__ src,
+                                               const uint16_t *s_list, int j0, int m)
+{
+    unsigned h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        h[e] = src[s_list[j0 + e]];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        h[e] = j0 + e < m ? h[e] : 0u;
+    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                      h[6] | (h[7] << 16));
+}
+
+__device__ __forceinline__ uint2 kept_gather_b(const int8_t *__restrict__ src,
+                                               const uint16_t *s_list, int j0, int m)
+{
+    const uint8_t *u = reinterpret_cast<const uint8_t *>(src);
+    unsigned b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        b[e] = u[s_list[j0 + e]];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        b[e] = j0 + e < m ? b[e] : 0u;
+    return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                      b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
 }
 
 // The gather blocks' part of a row-quantization launch: the first outlier
@@ -838,8 +817,9 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     uint8_t *s_fl = s_dyn;
     int *s_aux = reinterpret_cast<int *>(s_dyn + flags_lds_bytes(nchunk));
     // kept-column mode (cb_kept non-null only for launches with its LDS
-    // region): the row block's compacted row, then its compacted weight rows
-    uint8_t *s_kept = s_dyn + flags_lds_bytes(nchunk) + aux_lds_bytes(nchunk);
+    // region): the list of kept columns
+    uint16_t *s_list =
+        reinterpret_cast<uint16_t *>(s_dyn + flags_lds_bytes(nchunk) + aux_lds_bytes(nchunk));
     OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
     if (cb_kept)
         os.kc = (int)kept_ld(K, os.n);
@@ -853,20 +833,33 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     const int64_t t = (int64_t)blockIdx.x - gb;
     const bool gx = gathers_x(x_out, use, os);
     const bool kept = os.kc > 0;
+    const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
+    // Row t's loads go out before the prologue's scans and barriers, so that
+    // their latency runs under them (nothing is loaded when the row has no
+    // int8 part: every column an outlier on the GEMM path).
+    uint4 v[NC > 0 ? NC : 1];
+    if constexpr (NC > 0) {
+        if (!(use == kForGemm && os.n == K)) {
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                const int c = tid + i * kBlock;
+                v[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
     if (!row_prologue(os, s_fl, nchunk, K, use, gx || kept, s_aux, O, io, s_red, t == 0))
         return;
-    const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
+    if (kept)   // the list is complete at the absmax's barrier
+        kept_list(s_fl, s_aux, nchunk, (int)K - os.n, os.kc, s_list);
     const int nout = os.n;
     const int64_t ldo = outlier_ld(nout);
     uint16_t *xrow = gx ? x_out + t * ldo : nullptr;
     unsigned m = 0;
-    uint4 v[NC > 0 ? NC : 1];
     unsigned fl[NC > 0 ? NC : 1];
     if constexpr (NC > 0) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             const int c = tid + i * kBlock;
-            v[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
             fl[i] = c < nchunk ? s_fl[c] : 0u;
         }
 #pragma unroll
@@ -887,47 +880,57 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     const float r = kF8 ? 0.0f : amax > 0.0f ? 127.0f / amax : 0.0f;
     const int e8 = kF8 ? f8_scale_exp<kF8>(amax) : 0;
     const float sc = kF8 ? __builtin_ldexpf(1.0f, e8) : 0.0f;
-    // the chunk's codes to Xq, or in the kept-column mode its kept codes to
-    // the compacted row (column 8c is preceded by 8c - pre kept columns)
-    auto put = [&](uint4 x, unsigned f, int c) {
-        const int pre = ((xrow && f) || kept) ? chunk_pos(s_fl, s_aux, c) : 0;
-        const uint2 q = quant_chunk<kF8>(x, f, amax, r, pre, xrow, sc);
-        if (kept)
-            put_kept(q, f, 8 * c - pre, s_kept);
-        else
-            *xq_chunk(Xq, t, K, c, packed) = q;
-    };
-    if constexpr (NC > 0) {
+    if (kept) {
+        // the row's outlier values (compact mode with few kept columns, small K)
+        if (xrow) {
+            if constexpr (NC > 0) {
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            const int c = tid + i * kBlock;
-            if (c < nchunk)
-                put(v[i], fl[i], c);
+                for (int i = 0; i < NC; ++i) {
+                    const int c = tid + i * kBlock;
+                    if (c < nchunk && fl[i])
+                        scatter_outliers(v[i], fl[i], chunk_pos(s_fl, s_aux, c), xrow);
+                }
+            } else {
+                for (int c = tid; c < nchunk; c += kBlock)
+                    if (s_fl[c])
+                        scatter_outliers(xr[c], s_fl[c], chunk_pos(s_fl, s_aux, c), xrow);
+            }
         }
+        // the kept codes, zero-padded to kc, at the start of Xq's row t; then
+        // the kept weight operand: row block t builds weight rows t, t + T,
+        // t + 2T, ... (the row blocks share the N rows evenly, and no extra
+        // blocks sit idle when the mode is not taken); both gather through
+        // the list (the rows are in cache: row t was just read)
+        const int mk = (int)K - nout;
+        const uint16_t *xt = X + t * K;
+        for (int j0 = 8 * tid; j0 < os.kc; j0 += 8 * kBlock)
+            *reinterpret_cast<uint2 *>(Xq + t * K + j0) =
+                quant8_mode<kF8>(kept_gather_h(xt, s_list, j0, mk), amax, r, sc);
+        for (int64_t rr = t; rr < N; rr += T)
+            for (int j0 = 8 * tid; j0 < os.kc; j0 += 8 * kBlock)
+                *reinterpret_cast<uint2 *>(cb_kept + rr * os.kc + j0) =
+                    kept_gather_b(CB + rr * K, s_list, j0, mk);
     } else {
-        for (int c = tid; c < nchunk; c += kBlock)
-            put(xr[c], s_fl[c], c);
+        // the chunk's codes to Xq (and its outlier values to the compact row)
+        auto put = [&](uint4 x, unsigned f, int c) {
+            const int pre = (xrow && f) ? chunk_pos(s_fl, s_aux, c) : 0;
+            *xq_chunk(Xq, t, K, c, packed) = quant_chunk<kF8>(x, f, amax, r, pre, xrow, sc);
+        };
+        if constexpr (NC > 0) {
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                const int c = tid + i * kBlock;
+                if (c < nchunk)
+                    put(v[i], fl[i], c);
+            }
+        } else {
+            for (int c = tid; c < nchunk; c += kBlock)
+                put(xr[c], s_fl[c], c);
+        }
     }
     if (xrow) {
         for (int64_t j = nout + tid; j < ldo; j += kBlock)
             xrow[j] = 0;
-    }
-    if (kept) {
-        // zero padding up to kc, then the compacted row to the start of
-        // Xq's row t
-        for (int j = (int)K - nout + tid; j < os.kc; j += kBlock)
-            s_kept[j] = 0;
-        __syncthreads();
-        uint4 *dst = reinterpret_cast<uint4 *>(Xq + t * K);
-        for (int j = tid; j < os.kc / 16; j += kBlock)
-            dst[j] = reinterpret_cast<const uint4 *>(s_kept)[j];
-        // the kept weight operand: row block t builds weight rows t, t + T,
-        // t + 2T, ... (the row blocks share the N rows evenly, and no extra
-        // blocks sit idle when the mode is not taken)
-        __syncthreads();
-        for (int64_t r = t; r < N; r += T)
-            kept_weight_row(CB + r * K, K, os.kc, (int)K - nout, s_fl, s_kept, s_red,
-                            cb_kept + r * os.kc);
     }
     if (tid == 0)
         a[t] = kF8 ? __builtin_ldexpf(1.0f, -e8) : amax;
@@ -939,26 +942,12 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
 // c = lane + 64 i, so every load instruction reads 1 KB of the row).  The
 // absmax is a wave reduction (no LDS, no block barrier), outlier columns are
 // zeroed before the absmax and the pack, so chunks with and without outliers
-// take the same arithmetic, and the outlier values go to the compact row of
-// x_out at positions from a wavefront prefix count of the flags (ballots), so
-// no per-chunk position table is read.  Extra blocks build w_out as
-// k_rowquant's.
+// take the same arithmetic.  On the GEMM path with short outlier rows the
+// block lists the outlier columns once in LDS and each wavefront copies its
+// row's values from that list (a per-chunk scatter cost hundreds of
+// instructions per row for a handful of values).  Extra blocks build w_out
+// as k_rowquant's.
 // ---------------------------------------------------------------------------
-// Outlier columns before this lane's chunk within one 64-chunk step of a
-// wavefront (lanes below it), and in the whole step: per flag bit, a ballot
-// and its masked population count.
-__device__ __forceinline__ void step_prefix(unsigned fl, uint64_t below, int &pre, int &tot)
-{
-    pre = 0;
-    tot = 0;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const uint64_t m = __ballot((fl >> b) & 1u);
-        pre += __popcll(m & below);
-        tot += __popcll(m);
-    }
-}
-
 template <int NC, int kF8 = kF8None>
 __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restrict__ X, int64_t T,
                                                        int64_t K,
@@ -987,39 +976,46 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restric
         return;
     }
     const bool gx = gathers_x(x_out, use, os);
-    // positions come from ballots over the row, which a wavefront walks in order
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
+    // the row's loads go out before the prologue and the outlier list, so
+    // that their latency runs under them (none when the row has no int8
+    // part: every column an outlier on the GEMM path)
+    uint4 v[NC];
+    if (t < T && !(use == kForGemm && os.n == K)) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int c = lane + i * kWave;
+            v[i] = c < nchunk ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
     if (!row_prologue(os, s_fl, nchunk, K, use, false, nullptr, O, io, s_red, blockIdx.x == 0))
         return;
-    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    // The outlier columns' positions (at most kCompactMaxLd: the gathered
+    // rows exist only in the modes with short outlier rows), once per block
+    // into LDS; each wavefront then copies its row's outlier values to the
+    // compact row with one 2-byte load per entry (the row is in cache).
+    const int nout = os.n;
+    if (gx && nout > 0) {
+        outlier_positions(s_fl, nchunk, nullptr, s_aux, (int)kCompactMaxLd,
+                          s_red + 2 * kWavesPerBlock);
+        __syncthreads();
+    }
     if (t >= T)
         return;
-    const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
     uint2 *qr = reinterpret_cast<uint2 *>(Xq + t * K);
-    const int nout = os.n;
     const int64_t ldo = outlier_ld(nout);
-    uint16_t *xrow = gx ? x_out + t * ldo : nullptr;
-    const uint64_t below = (1ull << lane) - 1ull;
-    uint4 v[NC];
+    if (gx) {
+        const uint16_t *xt = X + t * K;
+        uint16_t *xrow = x_out + t * ldo;
+        for (int64_t j = lane; j < ldo; j += kWave)
+            xrow[j] = j < nout ? xt[s_aux[j]] : (uint16_t)0;
+    }
     unsigned fl[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = lane + i * kWave;
-        v[i] = c < nchunk ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
         fl[i] = c < nchunk ? s_fl[c] : 0u;
-    }
-    // the outlier values first, then they are zeroed in place
-    if (xrow && nout > 0) {
-        int base = 0;
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            if (__ballot(fl[i] != 0u) == 0ull)
-                continue;
-            int pre, tot;
-            step_prefix(fl[i], below, pre, tot);
-            if (fl[i])
-                scatter_outliers(v[i], fl[i], base + pre, xrow);
-            base += tot;
-        }
     }
     unsigned m = 0;
 #pragma unroll
@@ -1038,10 +1034,6 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restric
         const int c = lane + i * kWave;
         if (c < nchunk)
             qr[c] = quant8_mode<kF8>(v[i], amax, r, sc);
-    }
-    if (xrow) {
-        for (int64_t j = nout + lane; j < ldo; j += kWave)
-            xrow[j] = 0;
     }
     if (lane == 0)
         a[t] = kF8 ? __builtin_ldexpf(1.0f, -e8) : amax;
@@ -1675,8 +1667,10 @@ hipError_t launch_act_absmax(const uint16_t *X, int64_t T, int64_t K, float thre
     const DetectFlags df = launch_detect(X, T, K, threshold, mask, s);
     const int64_t gb = gather_blocks(g);
     const size_t lds = rowquant_lds_bytes(K);
-    if (T >= kRowQuantWaveMinT && K <= kRowQuantWaveMaxK && !xq_packed) {
-        // a wavefront per row, the row in NC chunks per lane
+    if (T >= kRowQuantWaveMinT && K <= kRowQuantWaveMaxK && !xq_packed && use != kForDecode) {
+        // a wavefront per row, the row in NC chunks per lane (its outlier
+        // gather lists at most kCompactMaxLd columns: the GEMM path's modes
+        // with gathered rows)
         const int64_t per = (nchunk + kWave - 1) / kWave;
         const int64_t row_blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
         const dim3 grid((unsigned)(row_blocks + gb));

@@ -342,7 +342,9 @@ def test_many_outliers_compact_and_dense(case, use_bias, relu):
 # (non-outlier) columns rounded up to 128 at most a quarter of K, the int8
 # product runs over the compacted kept columns only.  Cases at the quarter
 # (kc = K/4) and one column past it, one row short of 512, a ragged T, a K
-# whose stages are 64 bytes, and a wider K.
+# whose stages are 64 bytes, a wider K, more weight rows than rows (a row
+# block builds several compacted weight rows), and a K past one 16 KB round
+# of the weight-row compaction (a second, partial round).
 KEPT_CASES = {
     # name: (T, K, N, number of outlier columns, drawn at random)
     "kept_at_cap": (512, 1024, 320, 768),
@@ -351,6 +353,8 @@ KEPT_CASES = {
     "kept_ragged_T": (600, 2048, 256, 1600),
     "kept_k64_stages": (512, 1088, 256, 900),
     "kept_wide": (1024, 4096, 512, 3500),
+    "kept_n_past_t": (512, 1024, 1280, 800),
+    "kept_two_rounds": (512, 17408, 128, 14000),
 }
 
 
