@@ -1234,7 +1234,13 @@ __device__ __forceinline__ void outlier_pass(const Acc (&acc)[C::FM][C::FN],
 
 // One tile of the int8 GEMM with the up-to-32-outlier epilogue (or the raw
 // int32 store); smem: the ring, then (output path) the tile's outlier rows.
-template <class C, bool kRawI32, bool kRelu, bool kZp, int kF8>
+// kBiasSel: -1 picks the epilogue with or without the bias per call (ep.bias);
+// 0 / 1 compile only the one without / with it.  A kernel with both epilogues
+// has the compiler hoist the accumulators' int-to-float conversions, which
+// both begin with, above the branch, where they outlive the registers free
+// there and spill (measured on the 2 x 4 wavefront shape: 52 bytes per lane,
+// reloaded inside the epilogue behind full memory waits).
+template <class C, bool kRawI32, bool kRelu, bool kZp, int kF8, int kBiasSel = -1>
 __device__ __forceinline__ void gemm_tile(char *smem, const int8_t *__restrict__ A,
                                           const int8_t *__restrict__ B, int64_t T, int64_t K,
                                           int64_t N, const EpilogueArgs &ep)
@@ -1314,9 +1320,9 @@ __device__ __forceinline__ void gemm_tile(char *smem, const int8_t *__restrict__
             else
                 at[i] = ep.a[t < T ? t : T - 1] * (1.0f / 16129.0f);
         }
-        if (ep.bias)
-            finish_tile<C, true, kRelu, kZp, Acc>(acc, at, za, ra, orows, smem, ep, m0, n0, T, N,
-                                                  nout, wm, wn, lane, tid);
+        if (kBiasSel == 1 || (kBiasSel < 0 && ep.bias))
+            finish_tile<C, kBiasSel != 0, kRelu, kZp, Acc>(acc, at, za, ra, orows, smem, ep, m0,
+                                                           n0, T, N, nout, wm, wn, lane, tid);
         else
             finish_tile<C, false, kRelu, kZp, Acc>(acc, at, za, ra, orows, smem, ep, m0, n0, T, N,
                                                    nout, wm, wn, lane, tid);
@@ -1420,8 +1426,9 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_many(
 
 // Both output paths in one launch, the path chosen per call from the outlier
 // count on the device: when both run in the same tile shape (and so the same
-// register budget), this saves the second, idle launch.
-template <class C, bool kRelu>
+// register budget), this saves the second, idle launch.  One kernel per bias
+// choice (see gemm_tile's kBiasSel).
+template <class C, bool kRelu, bool kBias>
 __global__ __launch_bounds__(C::kThreads) void k_gemm_both(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, int64_t T, int64_t K, int64_t N,
     EpilogueArgs ep, const int32_t *__restrict__ info, const int32_t *__restrict__ groups,
@@ -1432,7 +1439,7 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_both(
     if (nout > kOutlierPad)
         many_tile<C, kRelu, false, false>(smem, A, B, T, K, N, ep, info, groups, mask, nout);
     else
-        gemm_tile<C, false, kRelu, false, false>(smem, A, B, T, K, N, ep);
+        gemm_tile<C, false, kRelu, false, false, kBias ? 1 : 0>(smem, A, B, T, K, N, ep);
 }
 
 // The int8 GEMM (K must be a multiple of C::ROWB) with its fused epilogue
@@ -1459,12 +1466,18 @@ hipError_t launch(const int8_t *Xq, const int8_t *CB, int64_t T, int64_t K, int6
     // 2048 x 2048 x 8192; the 64-byte-stage shape spills more combined)
     if constexpr (std::is_same_v<C, CM> && C::ROWB == 128) {
         if (!ep.c_i32 && !ep.f8 && !ep.row_zp) {
-            if (ep.act)
-                hipLaunchKernelGGL((k_gemm_both<C, true>), grid, dim3(C::kThreads), 0, s, Xq, CB,
-                                   T, K, N, ep, ep.n_out, ep.groups, ep.mask);
-            else
-                hipLaunchKernelGGL((k_gemm_both<C, false>), grid, dim3(C::kThreads), 0, s, Xq,
+            if (ep.act && ep.bias)
+                hipLaunchKernelGGL((k_gemm_both<C, true, true>), grid, dim3(C::kThreads), 0, s, Xq,
                                    CB, T, K, N, ep, ep.n_out, ep.groups, ep.mask);
+            else if (ep.act)
+                hipLaunchKernelGGL((k_gemm_both<C, true, false>), grid, dim3(C::kThreads), 0, s,
+                                   Xq, CB, T, K, N, ep, ep.n_out, ep.groups, ep.mask);
+            else if (ep.bias)
+                hipLaunchKernelGGL((k_gemm_both<C, false, true>), grid, dim3(C::kThreads), 0, s,
+                                   Xq, CB, T, K, N, ep, ep.n_out, ep.groups, ep.mask);
+            else
+                hipLaunchKernelGGL((k_gemm_both<C, false, false>), grid, dim3(C::kThreads), 0, s,
+                                   Xq, CB, T, K, N, ep, ep.n_out, ep.groups, ep.mask);
             if (ev1) {
                 const hipError_t e = hipEventRecord(ev1, s);
                 if (e != hipSuccess)
