@@ -379,13 +379,53 @@ __device__ __forceinline__ int outlier_mode(int n, int ng)
 // for every chunk, the OR of the detection's flag sets (16 chunks per load);
 // returns the block-uniform summary.  s_red: 2 * kWavesPerBlock ints.  Ends
 // with the flags visible to the whole block.
+// between(): the caller's own loads (its rows), issued after the flag loads
+// and before their use, so that the two latencies overlap (memory loads
+// complete in issue order, so waiting for the flags does not wait for the
+// rows).  First pass: thread i loads 16-byte piece i / nr of set i % nr
+// (nr is a power of two, so a piece's nr loads sit in adjacent lanes of one
+// wavefront and are ORed by lane exchanges); pieces * nr <= kBlock whenever
+// nr > 1 (detect_flags), and with nr = 1 pieces past kBlock follow in a
+// loop.  The first pass's load is unconditional (threads past the flags
+// re-read piece 0 of set 0), so it is in flight with the caller's loads.
+struct NoLoads {
+    __device__ void operator()() const {}
+};
+template <class Between = NoLoads>
 __device__ __forceinline__ OutlierSet derive_outliers(const DetectFlags &df, int nchunk,
-                                                      uint8_t *s_fl, int *s_red)
+                                                      uint8_t *s_fl, int *s_red,
+                                                      Between &&between = Between{})
 {
     int cnt = 0;
+    {
+        const int nr = df.nr, q = (int)threadIdx.x / nr, r = (int)threadIdx.x % nr;
+        const int c = 16 * q;
+        const bool act = c < nchunk;
+        uint4 f = *reinterpret_cast<const uint4 *>(df.parts + (act ? (int64_t)r * df.pitch + c : 0));
+        __builtin_amdgcn_sched_barrier(0);
+        between();
+        __builtin_amdgcn_sched_barrier(0);
+        for (int off = 1; off < nr; off <<= 1) {
+            f.x |= __shfl_xor(f.x, off, kWave);
+            f.y |= __shfl_xor(f.y, off, kWave);
+            f.z |= __shfl_xor(f.z, off, kWave);
+            f.w |= __shfl_xor(f.w, off, kWave);
+        }
+        if (act && r == 0) {
+            if (c + 16 > nchunk) {   // K % 64 == 0: an 8-byte tail
+                f.z = 0u;
+                f.w = 0u;
+                *reinterpret_cast<uint2 *>(s_fl + c) = make_uint2(f.x, f.y);
+            } else {
+                *reinterpret_cast<uint4 *>(s_fl + c) = f;
+            }
+            cnt += __builtin_popcount(f.x) + __builtin_popcount(f.y) + __builtin_popcount(f.z) +
+                   __builtin_popcount(f.w);
+        }
+    }
     // K % 64 == 0: nchunk is a multiple of 8; whole 16-byte pieces, then a tail
     // (the pitch is a multiple of 16)
-    for (int c = 16 * threadIdx.x; c < nchunk; c += 16 * kBlock) {
+    for (int c = 16 * (threadIdx.x + kBlock); c < nchunk; c += 16 * kBlock) {
         const uint8_t *p = df.parts + c;
         if (c + 16 <= nchunk) {
             uint4 f = *reinterpret_cast<const uint4 *>(p);
@@ -967,28 +1007,35 @@ __global__ __launch_bounds__(kBlock) void k_rowquant_w(const uint16_t *__restric
     const int nchunk = (int)(K / 8);
     uint8_t *s_fl = s_dyn;
     int *s_aux = reinterpret_cast<int *>(s_dyn + flags_lds_bytes(nchunk));
-    const OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
     if ((int64_t)blockIdx.x >= row_blocks) {
+        const OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
         gather_block<f8_mode(kF8)>(blockIdx.x - row_blocks,
                                                   gridDim.x - row_blocks, K, nchunk, os, s_fl,
                                                   s_aux, s_red + 2 * kWavesPerBlock, CB, SCB, N,
                                                   w_out);
         return;
     }
-    const bool gx = gathers_x(x_out, use, os);
     const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
-    // the row's loads go out before the prologue and the outlier list, so
-    // that their latency runs under them (none when the row has no int8
-    // part: every column an outlier on the GEMM path)
+    // The row's loads go out with the flag loads, so that their latency runs
+    // under the flags' and the prologue.  They are unconditional (a wavefront
+    // past the last row re-reads row T-1, chunks past the row re-read chunk
+    // 0, both unused): a load under a condition would make the flags' use
+    // wait for it too.  When every column is an outlier on the GEMM path the
+    // row is loaded and not used.
+    const uint4 *xr = reinterpret_cast<const uint4 *>(X + (t < T ? t : T - 1) * K);
     uint4 v[NC];
-    if (t < T && !(use == kForGemm && os.n == K)) {
+    const OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red, [&]() {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             const int c = lane + i * kWave;
-            v[i] = c < nchunk ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+            v[i] = xr[c < nchunk ? c : 0];
         }
-    }
+    });
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+        if (lane + i * kWave >= nchunk)
+            v[i] = make_uint4(0u, 0u, 0u, 0u);
+    const bool gx = gathers_x(x_out, use, os);
     if (!row_prologue(os, s_fl, nchunk, K, use, false, nullptr, O, io, s_red, blockIdx.x == 0))
         return;
     // The outlier columns' positions (at most kCompactMaxLd: the gathered
