@@ -384,10 +384,12 @@ __device__ __forceinline__ int outlier_mode(int n, int ng)
 // complete in issue order, so waiting for the flags does not wait for the
 // rows).  First pass: thread i loads 16-byte piece i / nr of set i % nr
 // (nr is a power of two, so a piece's nr loads sit in adjacent lanes of one
-// wavefront and are ORed by lane exchanges); pieces * nr <= kBlock whenever
-// nr > 1 (detect_flags), and with nr = 1 pieces past kBlock follow in a
-// loop.  The first pass's load is unconditional (threads past the flags
-// re-read piece 0 of set 0), so it is in flight with the caller's loads.
+// wavefront and are ORed by lane exchanges), pieces 0 .. kBlock/nr - 1; a
+// loop takes the pieces past those, a thread per piece ORing the nr sets
+// itself (detect_flags keeps pieces * nr <= kBlock / 2 when nr > 1, so the
+// loop runs only for nr = 1 and K > 32768).  The first pass's load is
+// unconditional (threads past the flags re-read piece 0 of set 0), so it is
+// in flight with the caller's loads.
 struct NoLoads {
     __device__ void operator()() const {}
 };
@@ -425,7 +427,7 @@ __device__ __forceinline__ OutlierSet derive_outliers(const DetectFlags &df, int
     }
     // K % 64 == 0: nchunk is a multiple of 8; whole 16-byte pieces, then a tail
     // (the pitch is a multiple of 16)
-    for (int c = 16 * (threadIdx.x + kBlock); c < nchunk; c += 16 * kBlock) {
+    for (int c = 16 * ((int)threadIdx.x + kBlock / df.nr); c < nchunk; c += 16 * kBlock) {
         const uint8_t *p = df.parts + c;
         if (c + 16 <= nchunk) {
             uint4 f = *reinterpret_cast<const uint4 *>(p);
