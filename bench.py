@@ -117,6 +117,32 @@ class HipEvents:
         self.made = []
 
 
+# Wall time of untimed calls of a step before its warmup steps (--settle-ms).
+# The GPU's power manager answers a sudden sustained MFMA load with a dip:
+# fc1 GEMMs run at ~245 us for about ten calls, slow to 300-325 us, and
+# settle near 255 us after about sixty (measured: 280.5 us per step timed
+# right after 10 warmup steps, 258.1 after 60, 255.9 after 200, and 258.2
+# over 500 steps timed from the start).  Settling first makes the timed steps
+# and the kernel-event pass after them see the same, sustained clock.
+SETTLE_MS = 40.0
+
+
+def settle(torch, fn):
+    """Untimed calls of fn (batches of 8, each synchronized) for SETTLE_MS of
+    wall time; returns the number of calls."""
+    n = 0
+    if SETTLE_MS <= 0:
+        return n
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
 def timed_steps(torch, L, X, CBs, SCB, thr, out, ws, steps, warmup, ev, extra=None):
     """`warmup` untimed steps, `steps` timed ones (plain llmint8_matmul calls), then
     `steps` more with HIP events recorded around the main kernel on its stream.
@@ -127,6 +153,7 @@ def timed_steps(torch, L, X, CBs, SCB, thr, out, ws, steps, warmup, ev, extra=No
     extra["step_ms"] and extra["pre_ms"] get each call's time from it to the
     end of the main kernel and to its start (the quantization kernels plus
     the one event record's gap), in the same pass as the kernel times."""
+    settle(torch, lambda: L.llmint8_matmul(X, CBs[0], SCB, thr, out=out, ws=ws))
     for i in range(warmup):
         L.llmint8_matmul(X, CBs[i % len(CBs)], SCB, thr, out=out, ws=ws)
     pairs = [(ev.create(), ev.create()) for _ in range(steps)]
@@ -256,6 +283,7 @@ def ffn_pair(torch, L, d, steps, warmup, ev, dev, entry):
         L.llmint8_matmul(h, CB2, SCB2, 6.0, out=y, ws=ws)
 
     def per_step(fn):
+        settle(torch, fn)
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -295,6 +323,7 @@ def fp16_weight_step(torch, L, d, steps, warmup, dev):
         L.llmint8_quantize_weight(W, CB=CB, SCB=SCB)
         L.llmint8_matmul(X, CB, SCB, 6.0, out=out, ws=ws)
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -316,6 +345,7 @@ def fp16_weight_step(torch, L, d, steps, warmup, dev):
 def timed_calls(torch, plain, evented, steps, warmup, ev):
     """timed_steps for any entry point: plain(i) is one call, evented(i, e0,
     e1) the same call with events around its main kernel."""
+    settle(torch, lambda: plain(0))
     for i in range(warmup):
         plain(i)
     pairs = [(ev.create(), ev.create()) for _ in range(steps)]
@@ -453,6 +483,7 @@ def mfma_ceiling(torch, L, A, B, ev, blocks=1024, iters=128, reps=10):
     """The MFMA rate on A's and B's own bits (see llmint8_mfma_ceiling): 3 warm-up
     launches, then `reps` timed back to back, each bracketed by HIP events on
     its stream; returns ops (or flops) per second of the mean launch, in 1e12."""
+    settle(torch, lambda: L.llmint8_mfma_ceiling(A, B, blocks, iters))
     for _ in range(3):
         L.llmint8_mfma_ceiling(A, B, blocks, iters)
     pairs = [(ev.create(), ev.create()) for _ in range(reps)]
@@ -522,6 +553,7 @@ def configs_bench(torch, L, workloads, steps, warmup, ev, dev):
 
 
 def main():
+    global SETTLE_MS
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -537,10 +569,14 @@ def main():
                     help="also time the FP8 variant, E5M2 and E4M3 (fc1 and the decode shape)")
     ap.add_argument("--zeropoint", action="store_true",
                     help="also time the zero-point variant (fc1 and the decode shape)")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="wall time of untimed calls of each timed step before its warmup steps "
+                         "(lets the power-managed clock settle; 0: none)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run one 256 MiB device-to-device copy first (a kernel of known traffic, "
                          "for scaling hardware byte counters)")
     args = ap.parse_args()
+    SETTLE_MS = args.settle_ms
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -590,6 +626,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": SETTLE_MS,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -608,7 +645,9 @@ def main():
                      "kernel_us": round(gemm_ms * 1e3, 2), "ops_per_launch": ops,
                      "kernel_timing": "HIP events around the kernel on its stream, in a second pass of "
                                       "the same steps (event records add a few us per step, so they "
-                                      "stay out of ms_per_step)"},
+                                      "stay out of ms_per_step); before the warmup steps, untimed "
+                                      "calls for settle_ms of wall time let the power-managed "
+                                      "clock settle, so both passes see the sustained clock"},
     }
     result["roofline"].update(spread_us(gemm_kern))
     med = lambda v: round(float(np.median(np.asarray(v) * 1e3)), 2)
@@ -617,8 +656,7 @@ def main():
         "before_kernel_us_median": med(same_pass["pre_ms"]),
         "note": "event before each call to the end / start of k_gemm_both, in the pass that "
                 "times the kernel: the quantization kernels and one event record's gap come "
-                "before the kernel; the plain steps of ms_per_step ran earlier, at another "
-                "point of the clock's power management"}
+                "before the kernel; the plain steps of ms_per_step ran just before it"}
     Xq = L.llmint8_quantize_act(X, thr)[0]
     ceil8 = mfma_ceiling(torch, L, Xq, CB, ev)
     del Xq
