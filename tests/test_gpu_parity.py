@@ -44,11 +44,14 @@ def test_quantize_weight_exact(N, K):
 # Few rows take the one-launch kernel (T = 1 with K <= 65536, (1, 65536) at
 # the limit; T <= 16 with K <= 16384, (4, 16384) and (16, 16384) at it); the
 # rest, (1, 65600), (4, 16448), (16, 16448) and (17, 1024) just past, the
-# three-kernel chain.
+# three-kernel chain.  (2048, 1088) and (2304, 576) have the detection split
+# into 8 row ranges with an 8-byte tail of flags per range (K % 128 = 64),
+# which the row kernels' blocks OR across lanes.
 @pytest.mark.parametrize("T,K", [(1, 64), (16, 256), (100, 320), (513, 1024), (2000, 2048),
                                  (1, 133120), (1, 65536), (1, 65600), (2, 12288), (3, 1088),
                                  (4, 16384), (4, 16448), (9, 12288), (16, 16384), (16, 16448),
-                                 (17, 1024), (1027, 640), (1024, 16384), (1024, 16448)])
+                                 (17, 1024), (1027, 640), (1024, 16384), (1024, 16448),
+                                 (2048, 1088), (2304, 576)])
 @pytest.mark.parametrize("thr", [6.0, 0.0, np.inf, 2.5])
 def test_quantize_act_exact(T, K, thr):
     say("quantize_act T=%d K=%d thr=%s" % (T, K, thr))
