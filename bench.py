@@ -9,6 +9,10 @@ once before timing, as the method does when the weight is loaded),
 threshold 6.0.  Inputs are seeded and synthetic and resident in HBM before the
 timed region.
 
+Before its warmup steps, each timed loop runs untimed calls of its step for
+settle_ms (40 ms) of wall time, so that the power-managed clock has settled
+(a sustained MFMA load first drives it through a ~15 ms dip).
+
 The JSON line also carries:
   roofline      the GEMM kernel's own duration (HIP events recorded around its
                 launch on the stream it runs on, in a second pass of the same
