@@ -849,7 +849,7 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
                                                      const int8_t *__restrict__ CB,
                                                      const float *__restrict__ SCB, int64_t N,
                                                      void *__restrict__ w_out, bool packed,
-                                                     int8_t *__restrict__ cb_kept)
+                                                     int8_t *__restrict__ cb_kept, bool early)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
     __shared__ unsigned s_max[kWavesPerBlock];
@@ -862,33 +862,46 @@ __global__ __launch_bounds__(kBlock) void k_rowquant(const uint16_t *__restrict_
     // region): the list of kept columns
     uint16_t *s_list =
         reinterpret_cast<uint16_t *>(s_dyn + flags_lds_bytes(nchunk) + aux_lds_bytes(nchunk));
-    OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
-    if (cb_kept)
-        os.kc = (int)kept_ld(K, os.n);
     // the gather blocks come first
     const int64_t gb = (int64_t)gridDim.x - T;
     if ((int64_t)blockIdx.x < gb) {
+        OutlierSet os = derive_outliers(df, nchunk, s_fl, s_red);
         gather_block<f8_mode(kF8)>(blockIdx.x, gb, K, nchunk, os, s_fl, s_aux,
                                    s_red + 2 * kWavesPerBlock, CB, SCB, N, w_out);
         return;
     }
     const int64_t t = (int64_t)blockIdx.x - gb;
-    const bool gx = gathers_x(x_out, use, os);
-    const bool kept = os.kc > 0;
     const uint4 *xr = reinterpret_cast<const uint4 *>(X + t * K);
     // Row t's loads go out before the prologue's scans and barriers, so that
-    // their latency runs under them (nothing is loaded when the row has no
-    // int8 part: every column an outlier on the GEMM path).
+    // their latency runs under them.  With `early` (the host's guess that the
+    // row has an int8 part: threshold > 0) they go out with the flag loads,
+    // unconditionally (chunks past the row re-read chunk 0, zeroed after), so
+    // that the flags' wait leaves them in flight; otherwise after the flags,
+    // and not at all when every column is an outlier on the GEMM path.
     uint4 v[NC > 0 ? NC : 1];
-    if constexpr (NC > 0) {
-        if (!(use == kForGemm && os.n == K)) {
+    auto load_row = [&]() {
+        if constexpr (NC > 0) {
 #pragma unroll
             for (int i = 0; i < NC; ++i) {
                 const int c = tid + i * kBlock;
-                v[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
+                v[i] = xr[c < nchunk ? c : 0];
             }
         }
+    };
+    OutlierSet os = early ? derive_outliers(df, nchunk, s_fl, s_red, load_row)
+                          : derive_outliers(df, nchunk, s_fl, s_red);
+    if (!early && !(use == kForGemm && os.n == K))
+        load_row();
+    if constexpr (NC > 0) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+            if (tid + i * kBlock >= nchunk)
+                v[i] = make_uint4(0u, 0u, 0u, 0u);
     }
+    if (cb_kept)
+        os.kc = (int)kept_ld(K, os.n);
+    const bool gx = gathers_x(x_out, use, os);
+    const bool kept = os.kc > 0;
     if (!row_prologue(os, s_fl, nchunk, K, use, gx || kept, s_aux, O, io, s_red, t == 0))
         return;
     if (kept)   // the list is complete at the absmax's barrier
@@ -1745,7 +1758,8 @@ hipError_t launch_act_absmax(const uint16_t *X, int64_t T, int64_t K, float thre
     const int64_t chunks_per_thread = (nchunk + kBlock - 1) / kBlock;
 #define LLMINT8_ROWQUANT(NCV)                                                                  \
     hipLaunchKernelGGL((k_rowquant<NCV, kF8>), grid, dim3(kBlock), lds_rows, s, X, T, K, df,     \
-                       use, O, io, Xq, a, x_out, g.CB, g.SCB, g.N, g.w_out, xq_packed, cb_kept)
+                       use, O, io, Xq, a, x_out, g.CB, g.SCB, g.N, g.w_out, xq_packed, cb_kept,   \
+                       threshold > 0.0f)
     if (chunks_per_thread <= 1)
         LLMINT8_ROWQUANT(1);
     else if (chunks_per_thread <= 2)
