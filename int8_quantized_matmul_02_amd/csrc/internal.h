@@ -256,11 +256,14 @@ struct OutlierInfoOut {
 // flags of every 8-column chunk (K/8 bytes, written by the row quantization
 // for the GEMM kernel when it reads X in place), then nr flag sets (one per
 // row range, `pitch` bytes apart) that k_detect writes and every
-// row-quantization block ORs.  nr > 1 when K is narrow, so the detection
-// launch still has about a workgroup per compute unit; each range holds at
-// least 256 rows.  (More ranges for wider K, 8 at K = 12288, left the
-// detection as fast and slowed the row quantization, whose every block ORs
-// the nr sets.)
+// row-quantization block ORs.  nr (a power of two, at most
+// kDetectMaxRanges, each range of at least 256 rows) is the first that
+// minimizes the busiest compute unit's share of the launch's K/64 * nr
+// blocks, each over 1/nr of a 64-column slice's rows: a block streams its
+// rows at the rate its compute unit's outstanding misses allow, so the
+// launch runs at the pace of the CU with the most rows (K = 4096: 4 ranges;
+// 2048: 8; 12288: 4, where one range left a quarter of the CUs idle; 16384:
+// 1).
 struct DetectFlags {
     const uint8_t *parts;
     int nr, pitch;
@@ -274,9 +277,18 @@ inline size_t detect_area_bytes(int64_t K)
 }
 inline DetectFlags detect_flags(uint8_t *mask, int64_t T, int64_t K)
 {
+    constexpr int64_t kCUs = 256;
+    const int64_t slices = K / 64;
     int nr = 1;
-    while (nr < kDetectMaxRanges && K / 64 * nr * 2 <= 256 && T >= 256 * nr * 2)
-        nr *= 2;
+    int64_t best_num = (slices + kCUs - 1) / kCUs, best_den = 1;   // busiest CU: num/den slices
+    for (int c = 2; c <= kDetectMaxRanges && T >= 256 * (int64_t)c; c *= 2) {
+        const int64_t num = (slices * c + kCUs - 1) / kCUs;
+        if (num * best_den < best_num * c) {
+            best_num = num;
+            best_den = c;
+            nr = c;
+        }
+    }
     const size_t a = ((size_t)K / 8 + 255) & ~(size_t)255;
     return DetectFlags{mask + a, nr, (int)detect_pitch(K)};
 }

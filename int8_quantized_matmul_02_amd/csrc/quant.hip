@@ -382,14 +382,14 @@ __device__ __forceinline__ int outlier_mode(int n, int ng)
 // between(): the caller's own loads (its rows), issued after the flag loads
 // and before their use, so that the two latencies overlap (memory loads
 // complete in issue order, so waiting for the flags does not wait for the
-// rows).  First pass: thread i loads 16-byte piece i / nr of set i % nr
-// (nr is a power of two, so a piece's nr loads sit in adjacent lanes of one
-// wavefront and are ORed by lane exchanges), pieces 0 .. kBlock/nr - 1; a
-// loop takes the pieces past those, a thread per piece ORing the nr sets
-// itself (detect_flags keeps pieces * nr <= kBlock / 2 when nr > 1, so the
-// loop runs only for nr = 1 and K > 32768).  The first pass's load is
-// unconditional (threads past the flags re-read piece 0 of set 0), so it is
-// in flight with the caller's loads.
+// rows).  First pass: thread i loads 16-byte pieces i / nr and
+// i / nr + kBlock / nr of set i % nr (nr is a power of two, so a piece's nr
+// loads sit in adjacent lanes of one wavefront and are ORed by lane
+// exchanges), pieces 0 .. 2 kBlock/nr - 1; a loop takes the pieces past
+// those, a thread per piece ORing the nr sets itself (at the shapes measured
+// it runs only for nr = 1 and K > 65536).  The first pass's loads are
+// unconditional (threads past the flags re-read piece 0 of set 0), so they
+// are in flight with the caller's loads.
 struct NoLoads {
     __device__ void operator()() const {}
 };
@@ -399,35 +399,48 @@ __device__ __forceinline__ OutlierSet derive_outliers(const DetectFlags &df, int
                                                       Between &&between = Between{})
 {
     int cnt = 0;
+    constexpr int kFirst = 2;   // pieces per thread in the first pass
     {
-        const int nr = df.nr, q = (int)threadIdx.x / nr, r = (int)threadIdx.x % nr;
-        const int c = 16 * q;
-        const bool act = c < nchunk;
-        uint4 f = *reinterpret_cast<const uint4 *>(df.parts + (act ? (int64_t)r * df.pitch + c : 0));
+        const int nr = df.nr, r = (int)threadIdx.x % nr;
+        uint4 f[kFirst];
+        int c[kFirst];
+#pragma unroll
+        for (int k = 0; k < kFirst; ++k) {
+            c[k] = 16 * ((int)threadIdx.x / nr + k * (kBlock / nr));
+            const bool act = c[k] < nchunk;
+            f[k] = *reinterpret_cast<const uint4 *>(df.parts +
+                                                    (act ? (int64_t)r * df.pitch + c[k] : 0));
+        }
         __builtin_amdgcn_sched_barrier(0);
         between();
         __builtin_amdgcn_sched_barrier(0);
         for (int off = 1; off < nr; off <<= 1) {
-            f.x |= __shfl_xor(f.x, off, kWave);
-            f.y |= __shfl_xor(f.y, off, kWave);
-            f.z |= __shfl_xor(f.z, off, kWave);
-            f.w |= __shfl_xor(f.w, off, kWave);
-        }
-        if (act && r == 0) {
-            if (c + 16 > nchunk) {   // K % 64 == 0: an 8-byte tail
-                f.z = 0u;
-                f.w = 0u;
-                *reinterpret_cast<uint2 *>(s_fl + c) = make_uint2(f.x, f.y);
-            } else {
-                *reinterpret_cast<uint4 *>(s_fl + c) = f;
+#pragma unroll
+            for (int k = 0; k < kFirst; ++k) {
+                f[k].x |= __shfl_xor(f[k].x, off, kWave);
+                f[k].y |= __shfl_xor(f[k].y, off, kWave);
+                f[k].z |= __shfl_xor(f[k].z, off, kWave);
+                f[k].w |= __shfl_xor(f[k].w, off, kWave);
             }
-            cnt += __builtin_popcount(f.x) + __builtin_popcount(f.y) + __builtin_popcount(f.z) +
-                   __builtin_popcount(f.w);
+        }
+#pragma unroll
+        for (int k = 0; k < kFirst; ++k) {
+            if (c[k] < nchunk && r == 0) {
+                if (c[k] + 16 > nchunk) {   // K % 64 == 0: an 8-byte tail
+                    f[k].z = 0u;
+                    f[k].w = 0u;
+                    *reinterpret_cast<uint2 *>(s_fl + c[k]) = make_uint2(f[k].x, f[k].y);
+                } else {
+                    *reinterpret_cast<uint4 *>(s_fl + c[k]) = f[k];
+                }
+                cnt += __builtin_popcount(f[k].x) + __builtin_popcount(f[k].y) +
+                       __builtin_popcount(f[k].z) + __builtin_popcount(f[k].w);
+            }
         }
     }
     // K % 64 == 0: nchunk is a multiple of 8; whole 16-byte pieces, then a tail
     // (the pitch is a multiple of 16)
-    for (int c = 16 * ((int)threadIdx.x + kBlock / df.nr); c < nchunk; c += 16 * kBlock) {
+    for (int c = 16 * ((int)threadIdx.x + kFirst * kBlock / df.nr); c < nchunk; c += 16 * kBlock) {
         const uint8_t *p = df.parts + c;
         if (c + 16 <= nchunk) {
             uint4 f = *reinterpret_cast<const uint4 *>(p);
